@@ -1,0 +1,129 @@
+"""CPU oracle for the selective scan (TEST INFRASTRUCTURE ONLY).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
+leg may import this package.  The product library never uses it.
+
+``scan_fwd``  -- Mamba-1 selective scan, plain sequential fp64 recurrence
+                 (mssm_oracle.c: oracle_scan_fwd).  Pinned by the tests in
+                 tests/test_oracle_pins.py: LTI == convolution, delta -> 0 keeps
+                 the state, geometric closed form, brute-force unrolled sum,
+                 chaining, reset at large delta, linearity/causality, gate and
+                 skip special cases.
+``ssd_fwd``   -- Mamba-2 scalar-A multi-head form, its own sequential loop
+                 (mssm_oracle.c: oracle_ssd_fwd).  Pinned by: equality with the
+                 Mamba-1 oracle under head broadcast, the geometric closed form
+                 with scalar A, a brute-force unrolled sum, chaining.
+Both take the already-rounded inputs the GPU receives (bf16 bit patterns are
+decoded by the C code's own codec) and return fp64 results.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mssm_oracle.c")
+_LIB = os.path.join(_HERE, "libmssm_oracle.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (IEEE fp64, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + f".tmp{os.getpid()}"
+        subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-std=c99", "-o", tmp, _SRC, "-lm", "-lpthread"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def load_library(path: Optional[str] = None):
+    """Load (and bind) an oracle shared library; the default one is built on demand."""
+    lib = ctypes.CDLL(path or build())
+    p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.oracle_scan_fwd.restype = i32
+    lib.oracle_scan_fwd.argtypes = [i64, i64, i64, i64, i32, p, p, p, p, p, p, p, p, i64, i64, p, p, i32]
+    lib.oracle_ssd_fwd.restype = i32
+    lib.oracle_ssd_fwd.argtypes = [i64, i64, i64, i64, i64, i64, i32, p, p, p, p, p, p, p, p, i64, i64, p, p, i32]
+    return lib
+
+
+def _get():
+    global _lib
+    if _lib is None:
+        _lib = load_library()
+    return _lib
+
+
+def _io_code(a: np.ndarray) -> int:
+    if a.dtype == np.uint16:
+        return 1
+    if a.dtype == np.float32:
+        return 0
+    raise TypeError(f"io arrays must be float32 or uint16 (bf16 bits), got {a.dtype}")
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a: Optional[np.ndarray], dtype=None) -> Optional[np.ndarray]:
+    if a is None:
+        return None
+    return np.ascontiguousarray(a, dtype=dtype) if dtype is not None else np.ascontiguousarray(a)
+
+
+def default_threads() -> int:
+    return max(1, len(os.sched_getaffinity(0)))
+
+
+def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, c0: int = 0, c1: Optional[int] = None,
+             nthreads: Optional[int] = None, lib=None):
+    """Mamba-1 selective scan. x/delta/z [Bsz, L, Dm]; B/C [Bsz, L, N]; A [Dm, N]; D [Dm]; h0 [Bsz, Dm, N].
+
+    Returns (out [Bsz, L, c1-c0] fp64, final_state [Bsz, c1-c0, N] fp64) for channels [c0, c1).
+    """
+    x, delta, B, C, z = _c(x), _c(delta), _c(B), _c(C), _c(z)
+    io = _io_code(x)
+    for t in (delta, B, C) + ((z,) if z is not None else ()):
+        if _io_code(t) != io:
+            raise TypeError("x, delta, B, C, z must share one dtype")
+    A, D, h0 = _c(A, np.float32), _c(D, np.float32), _c(h0, np.float32)
+    bsz, L, dm = x.shape
+    N = A.shape[1]
+    c1 = dm if c1 is None else c1
+    nc = c1 - c0
+    out = np.empty((bsz, L, nc), dtype=np.float64)
+    fin = np.empty((bsz, nc, N), dtype=np.float64)
+    rc = (lib or _get()).oracle_scan_fwd(bsz, L, dm, N, io, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                                         _ptr(D), _ptr(z), _ptr(h0), c0, c1, _ptr(out), _ptr(fin),
+                                         nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_scan_fwd rejected its arguments")
+    return out, fin
+
+
+def ssd_fwd(x, delta, A, B, C, D=None, z=None, h0=None, hd0: int = 0, hd1: Optional[int] = None,
+            nthreads: Optional[int] = None, lib=None):
+    """Mamba-2 scalar-A form. x/z [Bsz, L, H, P]; delta [Bsz, L, H]; B/C [Bsz, L, G, N]; A/D [H].
+
+    Returns (out [Bsz, L, hd1-hd0, P] fp64, final_state [Bsz, hd1-hd0, P, N] fp64) for heads [hd0, hd1).
+    """
+    x, delta, B, C, z = _c(x), _c(delta), _c(B), _c(C), _c(z)
+    io = _io_code(x)
+    A, D, h0 = _c(A, np.float32), _c(D, np.float32), _c(h0, np.float32)
+    bsz, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    hd1 = H if hd1 is None else hd1
+    nh = hd1 - hd0
+    out = np.empty((bsz, L, nh, P), dtype=np.float64)
+    fin = np.empty((bsz, nh, P, N), dtype=np.float64)
+    rc = (lib or _get()).oracle_ssd_fwd(bsz, L, H, P, N, G, io, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                                        _ptr(D), _ptr(z), _ptr(h0), hd0, hd1, _ptr(out), _ptr(fin),
+                                        nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_ssd_fwd rejected its arguments")
+    return out, fin

@@ -1,0 +1,221 @@
+/*
+ * CPU oracle for the selective-scan forward pass.  TEST INFRASTRUCTURE ONLY:
+ * nothing in the product library links or calls this file; only the tests,
+ * the smoke check and the benchmark's CPU-baseline leg use it.
+ *
+ * Plain, slow, sequential fp64 recurrences written straight from the
+ * definitions.  No blocking, no chunking, no reordering: one (batch, channel)
+ * row (Mamba-1) or one (batch, head) pair (Mamba-2 form) is walked step by
+ * step in time.  Threads split independent rows only.
+ *
+ * Sources (page title + section):
+ *  - "Mamba-2 y state-space models", 4.1: the recurrence h_t = A h_{t-1} + B x_t
+ *    and the readout y_t = C h_t.
+ *  - "P20 - Mamba", 5 (minimal maths): the selective SSM makes the recurrence
+ *    and readout parameters depend on the current token.
+ *  - "03 - Modelos de espacio de estados", "El mecanismo selectivo de Mamba":
+ *    B, C and the step delta are per token; "Discretizacion": zero-order hold
+ *    with A diagonal, so exp(delta*A) is taken elementwise; "Parallel scan":
+ *    h_t = Abar_t h_{t-1} + Bbar_t x_t.
+ *  - "Mamba-3" (blog), introduction: in Mamba-2 the transition is a scalar
+ *    times the identity, so each head has one scalar A.
+ *  - "Mamba-2 y state-space models", 4.3 notes: Mamba-2 organises the state
+ *    in heads of size headdim.
+ * Readings where the pages are silent or garbled:
+ *  - Bbar x = delta * B * x (Euler step for the input, zero-order hold for A).
+ *  - A is a fixed parameter (negative reals), delta arrives final.
+ *  - out = (C.h + D*x) * silu(z), silu(z) = z / (1 + exp(-z)); D and z optional.
+ *  - y_t reads the state after step t; h_{-1} = h0 (zero when absent).
+ *  - Mamba-2 form: head h reads group g = h / (H / G) of B and C; D per head.
+ *
+ * Parity status of each function is stated in the oracle's Python wrapper.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define IO_F32 0
+#define IO_BF16 1
+
+/* bf16 bit pattern -> value (the upper half of an fp32) */
+static double bf16_value(uint16_t bits) {
+    uint32_t u = ((uint32_t)bits) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static double load_io(const void* p, int io, int64_t i) {
+    if (io == IO_BF16) return bf16_value(((const uint16_t*)p)[i]);
+    return (double)((const float*)p)[i];
+}
+
+static double silu(double v) { return v / (1.0 + exp(-v)); }
+
+/* ------------------------------------------------------------------------- */
+/* Mamba-1 selective scan                                                     */
+/* ------------------------------------------------------------------------- */
+typedef struct {
+    int64_t Bsz, L, D, N;
+    int io;
+    const void *x, *delta, *Bm, *Cm, *z;
+    const float *A, *Dv, *h0;
+    int64_t c0, c1;          /* channel range [c0, c1) */
+    double *out, *final_state;
+    int64_t row_begin, row_end;  /* rows = b * (c1 - c0) + (c - c0) */
+} scan_job;
+
+static void scan_row(const scan_job* j, int64_t b, int64_t c, double* h) {
+    const int64_t N = j->N, D = j->D, L = j->L, nc = j->c1 - j->c0;
+    for (int64_t n = 0; n < N; ++n) h[n] = j->h0 ? (double)j->h0[(b * D + c) * N + n] : 0.0;
+    for (int64_t t = 0; t < L; ++t) {
+        const int64_t i = (b * L + t) * D + c;      /* [B, L, D] */
+        const int64_t r = (b * L + t) * N;          /* [B, L, N] */
+        const double d = load_io(j->delta, j->io, i);
+        const double u = load_io(j->x, j->io, i);
+        double acc = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+            const double dA = exp(d * (double)j->A[c * N + n]);
+            const double dBx = d * load_io(j->Bm, j->io, r + n) * u;
+            h[n] = dA * h[n] + dBx;
+            acc += load_io(j->Cm, j->io, r + n) * h[n];
+        }
+        double y = acc + (j->Dv ? (double)j->Dv[c] * u : 0.0);
+        if (j->z) y *= silu(load_io(j->z, j->io, i));
+        j->out[(b * L + t) * nc + (c - j->c0)] = y;
+    }
+    if (j->final_state)
+        for (int64_t n = 0; n < N; ++n) j->final_state[(b * nc + (c - j->c0)) * N + n] = h[n];
+}
+
+static void* scan_worker(void* arg) {
+    const scan_job* j = (const scan_job*)arg;
+    const int64_t nc = j->c1 - j->c0;
+    double* h = (double*)malloc(sizeof(double) * (size_t)j->N);
+    for (int64_t row = j->row_begin; row < j->row_end; ++row)
+        scan_row(j, row / nc, j->c0 + row % nc, h);
+    free(h);
+    return NULL;
+}
+
+/*
+ * out [Bsz, L, c1-c0] fp64; final_state [Bsz, c1-c0, N] fp64 (nullable).
+ * x, delta, z: [Bsz, L, D]; Bm, Cm: [Bsz, L, N] in io dtype; A [D, N], Dv [D],
+ * h0 [Bsz, D, N] fp32 (Dv, z, h0 nullable).  Returns 0, or -1 on bad sizes.
+ */
+int oracle_scan_fwd(int64_t Bsz, int64_t L, int64_t D, int64_t N, int io,
+                    const void* x, const void* delta, const float* A, const void* Bm, const void* Cm,
+                    const float* Dv, const void* z, const float* h0, int64_t c0, int64_t c1,
+                    double* out, double* final_state, int nthreads) {
+    if (Bsz < 0 || L < 0 || D <= 0 || N <= 0 || c0 < 0 || c1 > D || c1 < c0) return -1;
+    if (io != IO_F32 && io != IO_BF16) return -1;
+    const int64_t rows = Bsz * (c1 - c0);
+    if (rows == 0) return 0;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > rows) nthreads = (int)rows;
+    scan_job* jobs = (scan_job*)calloc((size_t)nthreads, sizeof(scan_job));
+    pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+    for (int k = 0; k < nthreads; ++k) {
+        scan_job* j = &jobs[k];
+        j->Bsz = Bsz; j->L = L; j->D = D; j->N = N; j->io = io;
+        j->x = x; j->delta = delta; j->Bm = Bm; j->Cm = Cm; j->z = z;
+        j->A = A; j->Dv = Dv; j->h0 = h0; j->c0 = c0; j->c1 = c1;
+        j->out = out; j->final_state = final_state;
+        j->row_begin = rows * k / nthreads;
+        j->row_end = rows * (k + 1) / nthreads;
+    }
+    for (int k = 1; k < nthreads; ++k) pthread_create(&th[k], NULL, scan_worker, &jobs[k]);
+    scan_worker(&jobs[0]);
+    for (int k = 1; k < nthreads; ++k) pthread_join(th[k], NULL);
+    free(jobs);
+    free(th);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Mamba-2 scalar-A multi-head form (its own loop, not a call into the above) */
+/* ------------------------------------------------------------------------- */
+typedef struct {
+    int64_t Bsz, L, H, P, N, G;
+    int io;
+    const void *x, *delta, *Bm, *Cm, *z;
+    const float *A, *Dv, *h0;
+    int64_t hd0, hd1;        /* head range [hd0, hd1) */
+    double *out, *final_state;
+    int64_t pair_begin, pair_end;   /* pairs = b * (hd1 - hd0) + (h - hd0) */
+} ssd_job;
+
+static void ssd_pair(const ssd_job* j, int64_t b, int64_t hd, double* S) {
+    const int64_t H = j->H, P = j->P, N = j->N, L = j->L, G = j->G, nh = j->hd1 - j->hd0;
+    const int64_t g = hd / (H / G);
+    for (int64_t p = 0; p < P; ++p)
+        for (int64_t n = 0; n < N; ++n)
+            S[p * N + n] = j->h0 ? (double)j->h0[((b * H + hd) * P + p) * N + n] : 0.0;
+    for (int64_t t = 0; t < L; ++t) {
+        const double d = load_io(j->delta, j->io, (b * L + t) * H + hd);
+        const double a = exp(d * (double)j->A[hd]);          /* scalar decay for the whole head */
+        const int64_t r = ((b * L + t) * G + g) * N;           /* [B, L, G, N] */
+        for (int64_t p = 0; p < P; ++p) {
+            const int64_t i = ((b * L + t) * H + hd) * P + p;  /* [B, L, H, P] */
+            const double u = load_io(j->x, j->io, i);
+            double acc = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                S[p * N + n] = a * S[p * N + n] + d * load_io(j->Bm, j->io, r + n) * u;
+                acc += load_io(j->Cm, j->io, r + n) * S[p * N + n];
+            }
+            double y = acc + (j->Dv ? (double)j->Dv[hd] * u : 0.0);
+            if (j->z) y *= silu(load_io(j->z, j->io, i));
+            j->out[((b * L + t) * nh + (hd - j->hd0)) * P + p] = y;
+        }
+    }
+    if (j->final_state)
+        for (int64_t p = 0; p < P; ++p)
+            for (int64_t n = 0; n < N; ++n)
+                j->final_state[((b * nh + (hd - j->hd0)) * P + p) * N + n] = S[p * N + n];
+}
+
+static void* ssd_worker(void* arg) {
+    const ssd_job* j = (const ssd_job*)arg;
+    const int64_t nh = j->hd1 - j->hd0;
+    double* S = (double*)malloc(sizeof(double) * (size_t)(j->P * j->N));
+    for (int64_t k = j->pair_begin; k < j->pair_end; ++k) ssd_pair(j, k / nh, j->hd0 + k % nh, S);
+    free(S);
+    return NULL;
+}
+
+/*
+ * out [Bsz, L, hd1-hd0, P] fp64; final_state [Bsz, hd1-hd0, P, N] fp64 (nullable).
+ * x, z: [Bsz, L, H, P]; delta [Bsz, L, H]; Bm, Cm [Bsz, L, G, N] in io dtype;
+ * A [H], Dv [H], h0 [Bsz, H, P, N] fp32 (Dv, z, h0 nullable).
+ */
+int oracle_ssd_fwd(int64_t Bsz, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int io,
+                   const void* x, const void* delta, const float* A, const void* Bm, const void* Cm,
+                   const float* Dv, const void* z, const float* h0, int64_t hd0, int64_t hd1,
+                   double* out, double* final_state, int nthreads) {
+    if (Bsz < 0 || L < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0 || H % G != 0) return -1;
+    if (hd0 < 0 || hd1 > H || hd1 < hd0) return -1;
+    if (io != IO_F32 && io != IO_BF16) return -1;
+    const int64_t pairs = Bsz * (hd1 - hd0);
+    if (pairs == 0) return 0;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > pairs) nthreads = (int)pairs;
+    ssd_job* jobs = (ssd_job*)calloc((size_t)nthreads, sizeof(ssd_job));
+    pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+    for (int k = 0; k < nthreads; ++k) {
+        ssd_job* j = &jobs[k];
+        j->Bsz = Bsz; j->L = L; j->H = H; j->P = P; j->N = N; j->G = G; j->io = io;
+        j->x = x; j->delta = delta; j->Bm = Bm; j->Cm = Cm; j->z = z;
+        j->A = A; j->Dv = Dv; j->h0 = h0; j->hd0 = hd0; j->hd1 = hd1;
+        j->out = out; j->final_state = final_state;
+        j->pair_begin = pairs * k / nthreads;
+        j->pair_end = pairs * (k + 1) / nthreads;
+    }
+    for (int k = 1; k < nthreads; ++k) pthread_create(&th[k], NULL, ssd_worker, &jobs[k]);
+    ssd_worker(&jobs[0]);
+    for (int k = 1; k < nthreads; ++k) pthread_join(th[k], NULL);
+    free(jobs);
+    free(th);
+    return 0;
+}

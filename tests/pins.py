@@ -1,0 +1,364 @@
+"""Pins for the CPU oracle: results the pages and the mathematics fix, computed
+without the recurrence (closed forms, convolution, explicit products).
+
+Each pin takes an oracle library handle (``lib``) so the mutation tests can
+run the same pins against deliberately broken builds of the oracle.  A pin
+raises AssertionError when the oracle disagrees.
+
+Passages (page title, section):
+  LTI == convolution   "P20 - Mamba" 5 (fixed A, B, C: a convolution with a
+                       long kernel); "Mamba-2 y state-space models" 4.1
+                       (parallelisable via a convolution).
+  delta -> 0           "03 - Modelos de espacio de estados", "El mecanismo
+                       selectivo": a closed gate keeps the state.
+  large delta          same section: an open gate lets the state absorb the
+                       new input (the old state is forgotten).
+  geometric form       scalar A ("Mamba-3" introduction) with constant inputs.
+  unrolled sum         "Parallel scan": the recurrence h_t = Abar_t h_{t-1} +
+                       Bbar_t x_t unrolled into a sum of products.
+  chaining             the fixed-size state is the whole memory
+                       ("Mamba-2 y state-space models" 4.3 notes).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+from workloads import bf16_bits_to_f32, f32_to_bf16_bits
+
+
+def _silu(v):
+    return v / (1.0 + np.exp(-v))
+
+
+def _close(got, want, rtol, what):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    scale = max(float(np.max(np.abs(want))) if want.size else 0.0, 1e-300)
+    err = float(np.max(np.abs(got - want))) if want.size else 0.0
+    assert err <= rtol * scale, f"{what}: max abs err {err:.3e} > {rtol:.1e} * {scale:.3e}"
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _neg_A(rng, d, n):
+    # distinct, channel-dependent negative values (so an index mix-up shows)
+    return -(rng.uniform(0.2, 2.5, size=(d, n))).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# Mamba-1 pins
+# ---------------------------------------------------------------------------
+def pin_lti_convolution(lib, seed=1):
+    """Constant delta per channel and constant B, C: y = conv(x, K), K_k = sum_n C_n (e^{d A})^k d B_n."""
+    rng = _rng(seed)
+    bsz, L, d, n = 2, 96, 3, 5
+    A = _neg_A(rng, d, n)
+    dc = rng.uniform(0.05, 0.6, size=d).astype(np.float32)
+    beta = rng.standard_normal(n).astype(np.float32)
+    gamma = rng.standard_normal(n).astype(np.float32)
+    x = rng.standard_normal((bsz, L, d)).astype(np.float32)
+    delta = np.broadcast_to(dc, (bsz, L, d)).copy()
+    B = np.broadcast_to(beta, (bsz, L, n)).copy()
+    C = np.broadcast_to(gamma, (bsz, L, n)).copy()
+    out, _ = oracle.scan_fwd(x, delta, A, B, C, lib=lib)
+    k = np.arange(L, dtype=np.float64)[:, None, None]                       # [L, 1, 1]
+    dc64, beta64, gamma64 = dc.astype(np.float64), beta.astype(np.float64), gamma.astype(np.float64)
+    decay = np.exp(dc64[:, None] * A.astype(np.float64))                   # [d, n]
+    K = np.sum(gamma64[None, None, :] * decay[None] ** k * (dc64[:, None] * beta64[None, :])[None], axis=-1)  # [L, d]
+    want = np.empty((bsz, L, d))
+    for b in range(bsz):
+        for c in range(d):
+            want[b, :, c] = np.convolve(x[b, :, c].astype(np.float64), K[:, c])[:L]
+    _close(out, want, 1e-12, "LTI convolution")
+
+
+def pin_delta_zero(lib, seed=2):
+    """delta == 0: the state is untouched (bitwise) and y_t = C_t . h0 + D x_t, gated."""
+    rng = _rng(seed)
+    bsz, L, d, n = 2, 33, 4, 3
+    A = _neg_A(rng, d, n)
+    x = rng.standard_normal((bsz, L, d)).astype(np.float32)
+    z = rng.standard_normal((bsz, L, d)).astype(np.float32)
+    B = rng.standard_normal((bsz, L, n)).astype(np.float32)
+    C = rng.standard_normal((bsz, L, n)).astype(np.float32)
+    D = rng.standard_normal(d).astype(np.float32)
+    h0 = rng.standard_normal((bsz, d, n)).astype(np.float32)
+    delta = np.zeros((bsz, L, d), np.float32)
+    out, fin = oracle.scan_fwd(x, delta, A, B, C, D, z, h0, lib=lib)
+    assert np.array_equal(fin, h0.astype(np.float64)), "delta=0 must leave the state unchanged"
+    y = np.einsum("bln,bdn->bld", C.astype(np.float64), h0.astype(np.float64)) + D.astype(np.float64) * x.astype(np.float64)
+    _close(out, y * _silu(z.astype(np.float64)), 1e-13, "delta=0 readout")
+
+
+def pin_geometric(lib, seed=3):
+    """Scalar A, constant delta/x/B/C: h_t = a^{t+1} h0 + d B u (1 - a^{t+1}) / (1 - a)."""
+    rng = _rng(seed)
+    bsz, L, d, n = 1, 57, 3, 4
+    alpha, dl, u = np.float32(-0.7), np.float32(0.3), np.float32(1.3)
+    A = np.full((d, n), alpha, np.float32)
+    beta = rng.standard_normal(n).astype(np.float32)
+    gamma = rng.standard_normal(n).astype(np.float32)
+    D = rng.standard_normal(d).astype(np.float32)
+    z = rng.standard_normal((bsz, L, d)).astype(np.float32)
+    h0 = rng.standard_normal((bsz, d, n)).astype(np.float32)
+    x = np.full((bsz, L, d), u, np.float32)
+    delta = np.full((bsz, L, d), dl, np.float32)
+    B = np.broadcast_to(beta, (bsz, L, n)).copy()
+    C = np.broadcast_to(gamma, (bsz, L, n)).copy()
+    out, fin = oracle.scan_fwd(x, delta, A, B, C, D, z, h0, lib=lib)
+    a = np.exp(np.float64(dl) * np.float64(alpha))
+    p = a ** np.arange(1, L + 1, dtype=np.float64)                           # a^{t+1}
+    h = p[None, :, None, None] * h0[:, None].astype(np.float64) + \
+        (np.float64(dl) * beta.astype(np.float64) * np.float64(u))[None, None, None, :] * \
+        ((1 - p) / (1 - a))[None, :, None, None]                              # [b, L, d, n]
+    y = np.einsum("bldn,n->bld", h, gamma.astype(np.float64)) + D.astype(np.float64) * np.float64(u)
+    _close(out, y * _silu(z.astype(np.float64)), 1e-12, "geometric closed form")
+    _close(fin, h[:, -1], 1e-12, "geometric final state")
+
+
+def bruteforce_scan(x, delta, A, B, C, D=None, z=None, h0=None):
+    """y_t = sum_n C_t[n] (prod_{r<=t} e^{d_r A}) h0[n] + sum_{s<=t} sum_n C_t[n] (prod_{s<r<=t} e^{d_r A}) d_s B_s[n] x_s."""
+    x, delta, A, B, C = (np.asarray(v, np.float64) for v in (x, delta, A, B, C))
+    bsz, L, d = x.shape
+    n = A.shape[1]
+    out = np.zeros((bsz, L, d))
+    for b in range(bsz):
+        for c in range(d):
+            for t in range(L):
+                tot = 0.0
+                for m in range(n):
+                    if h0 is not None:
+                        prod = 1.0
+                        for r in range(0, t + 1):
+                            prod *= np.exp(delta[b, r, c] * A[c, m])
+                        tot += C[b, t, m] * prod * float(h0[b, c, m])
+                    for s in range(t + 1):
+                        prod = 1.0
+                        for r in range(s + 1, t + 1):
+                            prod *= np.exp(delta[b, r, c] * A[c, m])
+                        tot += C[b, t, m] * prod * delta[b, s, c] * B[b, s, m] * x[b, s, c]
+                if D is not None:
+                    tot += float(D[c]) * x[b, t, c]
+                if z is not None:
+                    tot *= _silu(float(z[b, t, c]))
+                out[b, t, c] = tot
+    return out
+
+
+def pin_bruteforce(lib, seed=4):
+    rng = _rng(seed)
+    bsz, L, d, n = 2, 24, 3, 4
+    A = _neg_A(rng, d, n)
+    x = rng.standard_normal((bsz, L, d)).astype(np.float32)
+    delta = rng.uniform(0.01, 0.8, size=(bsz, L, d)).astype(np.float32)
+    B = rng.standard_normal((bsz, L, n)).astype(np.float32)
+    C = rng.standard_normal((bsz, L, n)).astype(np.float32)
+    D = rng.standard_normal(d).astype(np.float32)
+    z = rng.standard_normal((bsz, L, d)).astype(np.float32)
+    h0 = rng.standard_normal((bsz, d, n)).astype(np.float32)
+    out, _ = oracle.scan_fwd(x, delta, A, B, C, D, z, h0, lib=lib)
+    _close(out, bruteforce_scan(x, delta, A, B, C, D, z, h0), 1e-12, "brute-force unrolled sum")
+
+
+def pin_chaining(lib, seed=5):
+    """scan(x)[L1:] == scan(x[L1:], h0 = final(scan(x[:L1]))), and the finals agree."""
+    rng = _rng(seed)
+    bsz, L, d, n, L1 = 2, 70, 3, 4, 29
+    A = _neg_A(rng, d, n)
+    x = rng.standard_normal((bsz, L, d)).astype(np.float32)
+    delta = rng.uniform(0.01, 0.5, size=(bsz, L, d)).astype(np.float32)
+    B = rng.standard_normal((bsz, L, n)).astype(np.float32)
+    C = rng.standard_normal((bsz, L, n)).astype(np.float32)
+    D = rng.standard_normal(d).astype(np.float32)
+    z = rng.standard_normal((bsz, L, d)).astype(np.float32)
+    full, fin = oracle.scan_fwd(x, delta, A, B, C, D, z, lib=lib)
+    _, mid = oracle.scan_fwd(x[:, :L1], delta[:, :L1], A, B[:, :L1], C[:, :L1], D, z[:, :L1], lib=lib)
+    # the state is handed over in fp32 (the carrier type); compare with a matching tolerance
+    tail, fin2 = oracle.scan_fwd(x[:, L1:], delta[:, L1:], A, B[:, L1:], C[:, L1:], D, z[:, L1:],
+                                 mid.astype(np.float32), lib=lib)
+    _close(tail, full[:, L1:], 1e-6, "chaining output")
+    _close(fin2, fin, 1e-6, "chaining final state")
+
+
+def pin_reset(lib, seed=6):
+    """delta = 200, A <= -1: the old state is wiped (e^{-200}), h_t = d B_t x_t."""
+    rng = _rng(seed)
+    bsz, L, d, n = 1, 20, 3, 4
+    A = -(1.0 + rng.uniform(0, 3, size=(d, n))).astype(np.float32)
+    x = rng.standard_normal((bsz, L, d)).astype(np.float32)
+    delta = np.full((bsz, L, d), 200.0, np.float32)
+    B = rng.standard_normal((bsz, L, n)).astype(np.float32)
+    C = rng.standard_normal((bsz, L, n)).astype(np.float32)
+    D = rng.standard_normal(d).astype(np.float32)
+    h0 = rng.standard_normal((bsz, d, n)).astype(np.float32)
+    out, _ = oracle.scan_fwd(x, delta, A, B, C, D, None, h0, lib=lib)
+    cb = np.sum(C.astype(np.float64) * B.astype(np.float64), axis=-1)        # [b, L]
+    want = 200.0 * x.astype(np.float64) * cb[:, :, None] + D.astype(np.float64) * x.astype(np.float64)
+    _close(out, want, 1e-13, "reset at large delta")
+
+
+def pin_linearity_causality(lib, seed=7):
+    rng = _rng(seed)
+    bsz, L, d, n = 2, 40, 3, 4
+    A = _neg_A(rng, d, n)
+    x1 = rng.standard_normal((bsz, L, d)).astype(np.float32)
+    x2 = rng.standard_normal((bsz, L, d)).astype(np.float32)
+    delta = rng.uniform(0.01, 0.5, size=(bsz, L, d)).astype(np.float32)
+    B = rng.standard_normal((bsz, L, n)).astype(np.float32)
+    C = rng.standard_normal((bsz, L, n)).astype(np.float32)
+    D = rng.standard_normal(d).astype(np.float32)
+    a, b = 0.75, -1.5
+    y1, _ = oracle.scan_fwd(x1, delta, A, B, C, D, lib=lib)
+    y2, _ = oracle.scan_fwd(x2, delta, A, B, C, D, lib=lib)
+    x12 = (a * x1.astype(np.float64) + b * x2.astype(np.float64))
+    # inputs are fp32: a*x1 + b*x2 is computed exactly in fp64 and passed through fp32 -> small rounding
+    y12, _ = oracle.scan_fwd(x12.astype(np.float32), delta, A, B, C, D, lib=lib)
+    _close(y12, a * y1 + b * y2, 1e-6, "linearity in x")
+    t0 = 17
+    xp = x1.copy()
+    xp[:, t0] += np.float32(3.0)
+    yp, _ = oracle.scan_fwd(xp, delta, A, B, C, D, lib=lib)
+    assert np.array_equal(yp[:, :t0], y1[:, :t0]), "outputs before t0 must not depend on x[t0]"
+    assert not np.array_equal(yp[:, t0], y1[:, t0]), "output at t0 must depend on x[t0]"
+
+
+def pin_gate_skip(lib, seed=8):
+    rng = _rng(seed)
+    bsz, L, d, n = 2, 30, 3, 4
+    A = _neg_A(rng, d, n)
+    x = rng.standard_normal((bsz, L, d)).astype(np.float32)
+    delta = rng.uniform(0.01, 0.5, size=(bsz, L, d)).astype(np.float32)
+    B = rng.standard_normal((bsz, L, n)).astype(np.float32)
+    C = rng.standard_normal((bsz, L, n)).astype(np.float32)
+    D = rng.standard_normal(d).astype(np.float32)
+    z = rng.standard_normal((bsz, L, d)).astype(np.float32)
+    out, _ = oracle.scan_fwd(x, delta, A, B, C, D, np.zeros_like(z), lib=lib)
+    assert np.all(out == 0.0), "z == 0 gates the output to exactly 0"
+    want = D.astype(np.float64) * x.astype(np.float64) * _silu(z.astype(np.float64))
+    out, _ = oracle.scan_fwd(x, delta, A, B, np.zeros_like(C), D, z, lib=lib)
+    _close(out, want, 1e-14, "C == 0 leaves D x silu(z)")
+    out, _ = oracle.scan_fwd(x, delta, A, np.zeros_like(B), C, D, z, lib=lib)
+    _close(out, want, 1e-14, "B == 0, h0 == 0 leaves D x silu(z)")
+    out_noD, _ = oracle.scan_fwd(x, delta, A, B, C, None, None, lib=lib)
+    out_D, _ = oracle.scan_fwd(x, delta, A, B, C, D, None, lib=lib)
+    _close(out_D - out_noD, D.astype(np.float64) * x.astype(np.float64), 1e-12, "skip term D x")
+
+
+def pin_bf16_codec(lib, seed=9):
+    """bf16 inputs are read exactly: oracle(bf16 bits) == oracle(same values as fp32)."""
+    rng = _rng(seed)
+    bsz, L, d, n = 2, 25, 3, 4
+    A = _neg_A(rng, d, n)
+    mk = lambda *s: f32_to_bf16_bits(rng.standard_normal(s).astype(np.float32))
+    x, z = mk(bsz, L, d), mk(bsz, L, d)
+    delta = f32_to_bf16_bits(rng.uniform(0.01, 0.5, size=(bsz, L, d)).astype(np.float32))
+    B, C = mk(bsz, L, n), mk(bsz, L, n)
+    D = rng.standard_normal(d).astype(np.float32)
+    ob, fb = oracle.scan_fwd(x, delta, A, B, C, D, z, lib=lib)
+    f = bf16_bits_to_f32
+    of, ff = oracle.scan_fwd(f(x), f(delta), A, f(B), f(C), D, f(z), lib=lib)
+    assert np.array_equal(ob, of) and np.array_equal(fb, ff), "bf16 decode must be exact"
+
+
+# ---------------------------------------------------------------------------
+# Mamba-2 (scalar A per head) pins
+# ---------------------------------------------------------------------------
+def _ssd_case(rng, bsz=2, L=37, H=4, P=3, N=5, G=2, with_dz=True, with_h0=True):
+    x = rng.standard_normal((bsz, L, H, P)).astype(np.float32)
+    delta = rng.uniform(0.01, 0.6, size=(bsz, L, H)).astype(np.float32)
+    A = -(rng.uniform(0.3, 3.0, size=H)).astype(np.float32)
+    B = rng.standard_normal((bsz, L, G, N)).astype(np.float32)
+    C = rng.standard_normal((bsz, L, G, N)).astype(np.float32)
+    D = rng.standard_normal(H).astype(np.float32) if with_dz else None
+    z = rng.standard_normal((bsz, L, H, P)).astype(np.float32) if with_dz else None
+    h0 = rng.standard_normal((bsz, H, P, N)).astype(np.float32) if with_h0 else None
+    return x, delta, A, B, C, D, z, h0
+
+
+def pin_ssd_equals_broadcast_scan(lib, seed=11):
+    """The scalar-A head form is the diagonal scan with A and delta broadcast over the head's P channels."""
+    rng = _rng(seed)
+    x, delta, A, B, C, D, z, h0 = _ssd_case(rng)
+    bsz, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    out, fin = oracle.ssd_fwd(x, delta, A, B, C, D, z, h0, lib=lib)
+    hpg = H // G
+    for g in range(G):
+        hs = slice(g * hpg, (g + 1) * hpg)
+        xe = x[:, :, hs, :].reshape(bsz, L, hpg * P)
+        de = np.repeat(delta[:, :, hs], P, axis=2)
+        Ae = np.repeat(np.repeat(A[hs], P)[:, None], N, axis=1)
+        De = np.repeat(D[hs], P)
+        ze = z[:, :, hs, :].reshape(bsz, L, hpg * P)
+        h0e = h0[:, hs].reshape(bsz, hpg * P, N)
+        ye, fe = oracle.scan_fwd(xe, de, Ae, B[:, :, g], C[:, :, g], De, ze, h0e, lib=lib)
+        _close(out[:, :, hs, :].reshape(bsz, L, hpg * P), ye, 1e-13, f"SSD == broadcast scan (group {g})")
+        _close(fin[:, hs].reshape(bsz, hpg * P, N), fe, 1e-13, f"SSD final == broadcast scan (group {g})")
+
+
+def pin_ssd_geometric(lib, seed=12):
+    rng = _rng(seed)
+    bsz, L, H, P, N, G = 1, 45, 2, 3, 4, 1
+    dl, u = np.float32(0.25), np.float32(-0.8)
+    A = np.array([-0.5, -1.7], np.float32)
+    beta = rng.standard_normal(N).astype(np.float32)
+    gamma = rng.standard_normal(N).astype(np.float32)
+    x = np.full((bsz, L, H, P), u, np.float32)
+    delta = np.full((bsz, L, H), dl, np.float32)
+    B = np.broadcast_to(beta, (bsz, L, G, N)).copy()
+    C = np.broadcast_to(gamma, (bsz, L, G, N)).copy()
+    h0 = rng.standard_normal((bsz, H, P, N)).astype(np.float32)
+    out, fin = oracle.ssd_fwd(x, delta, A, B, C, None, None, h0, lib=lib)
+    for h in range(H):
+        a = np.exp(np.float64(dl) * np.float64(A[h]))
+        p = a ** np.arange(1, L + 1, dtype=np.float64)
+        hs = p[:, None, None] * h0[0, h][None].astype(np.float64) + \
+            (np.float64(dl) * np.float64(u) * beta.astype(np.float64))[None, None, :] * ((1 - p) / (1 - a))[:, None, None]
+        y = np.einsum("lpn,n->lp", hs, gamma.astype(np.float64))
+        _close(out[0, :, h, :], y, 1e-12, "SSD geometric closed form")
+        _close(fin[0, h], hs[-1], 1e-12, "SSD geometric final")
+
+
+def pin_ssd_bruteforce(lib, seed=13):
+    rng = _rng(seed)
+    x, delta, A, B, C, D, z, h0 = _ssd_case(rng, bsz=1, L=16, H=2, P=2, N=3, G=1)
+    out, _ = oracle.ssd_fwd(x, delta, A, B, C, D, z, h0, lib=lib)
+    x64, d64, B64, C64 = (v.astype(np.float64) for v in (x, delta, B, C))
+    bsz, L, H, P = x.shape
+    want = np.zeros_like(out)
+    for h in range(H):
+        ell = d64[0, :, h] * np.float64(A[h])                     # log-decay per step
+        for t in range(L):
+            for p in range(P):
+                tot = np.float64(0.0)
+                for s in range(-1, t + 1):
+                    w = np.exp(np.sum(ell[s + 1:t + 1]))          # decay from after s up to t
+                    if s < 0:
+                        tot += w * np.dot(C64[0, t, 0], h0[0, h, p].astype(np.float64))
+                    else:
+                        tot += w * np.dot(C64[0, t, 0], B64[0, s, 0]) * d64[0, s, h] * x64[0, s, h, p]
+                tot += np.float64(D[h]) * x64[0, t, h, p]
+                tot *= _silu(np.float64(z[0, t, h, p]))
+                want[0, t, h, p] = tot
+    _close(out, want, 1e-11, "SSD brute-force unrolled sum")
+
+
+def pin_ssd_chaining(lib, seed=14):
+    rng = _rng(seed)
+    x, delta, A, B, C, D, z, _ = _ssd_case(rng, L=50, with_h0=False)
+    L1 = 21
+    full, fin = oracle.ssd_fwd(x, delta, A, B, C, D, z, lib=lib)
+    _, mid = oracle.ssd_fwd(x[:, :L1], delta[:, :L1], A, B[:, :L1], C[:, :L1], D, z[:, :L1], lib=lib)
+    tail, fin2 = oracle.ssd_fwd(x[:, L1:], delta[:, L1:], A, B[:, L1:], C[:, L1:], D, z[:, L1:],
+                                mid.astype(np.float32), lib=lib)
+    _close(tail, full[:, L1:], 1e-6, "SSD chaining output")
+    _close(fin2, fin, 1e-6, "SSD chaining final")
+
+
+SCAN_PINS = [pin_lti_convolution, pin_delta_zero, pin_geometric, pin_bruteforce, pin_chaining, pin_reset,
+             pin_linearity_causality, pin_gate_skip, pin_bf16_codec]
+SSD_PINS = [pin_ssd_equals_broadcast_scan, pin_ssd_geometric, pin_ssd_bruteforce, pin_ssd_chaining]
+ALL_PINS = SCAN_PINS + SSD_PINS

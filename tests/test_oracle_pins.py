@@ -1,0 +1,66 @@
+"""The CPU oracle against what the pages and the mathematics fix (no GPU)."""
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+import pins
+
+ORACLE_SRC = os.path.join(os.path.dirname(oracle.__file__), "mssm_oracle.c")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return oracle.load_library()
+
+
+@pytest.mark.parametrize("pin", pins.ALL_PINS, ids=lambda p: p.__name__)
+def test_pin(lib, pin):
+    pin(lib)
+
+
+# Plausible mistakes, planted in a copy of the oracle source on the CPU.
+# Each one must make at least one pin fail.
+MUTANTS = {
+    "decay_sign": ("exp(d * (double)j->A[c * N + n])", "exp(-d * (double)j->A[c * N + n])"),
+    "decay_without_delta": ("exp(d * (double)j->A[c * N + n])", "exp((double)j->A[c * N + n])"),
+    "input_without_delta": ("const double dBx = d * load_io(j->Bm", "const double dBx = load_io(j->Bm"),
+    "A_transposed": ("j->A[c * N + n]", "j->A[(n * D + c) % (D * N)]"),
+    "readout_before_update": (
+        "h[n] = dA * h[n] + dBx;\n            acc += load_io(j->Cm, j->io, r + n) * h[n];",
+        "acc += load_io(j->Cm, j->io, r + n) * h[n];\n            h[n] = dA * h[n] + dBx;"),
+    "B_for_C": ("acc += load_io(j->Cm, j->io, r + n) * h[n];", "acc += load_io(j->Bm, j->io, r + n) * h[n];"),
+    "skip_dropped": ("(j->Dv ? (double)j->Dv[c] * u : 0.0)", "0.0"),
+    "gate_sigmoid_not_silu": ("return v / (1.0 + exp(-v));", "return 1.0 / (1.0 + exp(-v));"),
+    "h0_ignored": ("j->h0 ? (double)j->h0[(b * D + c) * N + n] : 0.0", "0.0"),
+    "bf16_halfulp": ("uint32_t u = ((uint32_t)bits) << 16;", "uint32_t u = (((uint32_t)bits) << 16) | 0x8000u;"),
+    "C_index_off_by_one_t": ("const int64_t r = (b * L + t) * N;", "const int64_t r = (b * L + (t > 0 ? t - 1 : 0)) * N;"),
+    "ssd_group_index": ("const int64_t g = hd / (H / G);", "const int64_t g = hd % G;"),
+    "ssd_decay_sign": ("exp(d * (double)j->A[hd])", "exp(-d * (double)j->A[hd])"),
+    "ssd_input_without_delta": ("a * S[p * N + n] + d * load_io(j->Bm", "a * S[p * N + n] + load_io(j->Bm"),
+    "ssd_h0_layout": ("j->h0[((b * H + hd) * P + p) * N + n]", "j->h0[((b * H + hd) * N + (n % P)) * P + (p % N)]"),
+    "ssd_skip_dropped": ("(j->Dv ? (double)j->Dv[hd] * u : 0.0)", "0.0"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name):
+    old, new = MUTANTS[name]
+    src = open(ORACLE_SRC).read()
+    assert src.count(old) >= 1, f"mutation anchor not found: {old!r}"
+    with tempfile.TemporaryDirectory() as d:
+        path = os.path.join(d, "mutant.c")
+        so = os.path.join(d, "libmutant.so")
+        with open(path, "w") as f:
+            f.write(src.replace(old, new))
+        subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-std=c99", "-o", so, path, "-lm", "-lpthread"])
+        lib = oracle.load_library(so)
+        failed = []
+        for pin in pins.ALL_PINS:
+            try:
+                pin(lib)
+            except AssertionError:
+                failed.append(pin.__name__)
+        assert failed, f"no pin caught mutant {name}"

@@ -1,0 +1,262 @@
+"""Seeded synthetic inputs for the selective-scan workloads.
+
+This module is shared by the CPU oracle side (tests) and the GPU side (tests,
+bench).  It holds the input recipe only -- shapes, value distributions and the
+bf16 rounding of inputs -- and none of the scan's arithmetic.
+
+Recipe (the workloads the pages describe, made concrete):
+  * Mamba-1 selective scan (page "03 - Modelos de espacio de estados",
+    sections "El mecanismo selectivo de Mamba" and "Discretizacion"): per-token
+    step size delta, per-token B and C shared across channels, fixed diagonal
+    negative A per (channel, state).
+  * Mamba-2 scalar-A multi-head form (page "Mamba-2 y state-space models",
+    section 4.2; page "Mamba-3", introduction: the transition is a scalar
+    times the identity): per-(token, head) delta, scalar A per head, B/C per
+    (token, group).
+
+Distributions: x, z, B, C ~ N(0, 1); D ~ N(0, 1) per channel;
+delta = softplus(0.5 * N(0, 1) - 2) evaluated in fp32; S4D-real A[c, n] =
+-(n + 1); "A = -exp(log k)" evaluated in fp32; SSD A[h] = -exp(U(log 1, log 16)).
+
+Random streams: tensor `k` of workload `cfg_id` is drawn in blocks of
+``BLOCK`` elements; block `j` comes from numpy PCG64 seeded with
+SeedSequence([ROOT_SEED + cfg_id, k, j]).  Values are drawn in fp32 and
+rounded to bf16 (round-to-nearest-even) where the workload's I/O is bf16.
+Blocks make generation streamable and deterministic for any size.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+ROOT_SEED = 1700
+BLOCK = 1 << 22
+
+# tensor ids (fixed order of the per-tensor streams)
+T_X, T_DELTA, T_Z, T_B, T_C, T_D, T_A, T_H0 = range(8)
+
+F32 = "f32"
+BF16 = "bf16"
+
+
+@dataclasses.dataclass(frozen=True)
+class ScanConfig:
+    """Mamba-1 selective scan workload: x/delta/z [B, L, D], B/C [B, L, N], A [D, N]."""
+    name: str
+    cfg_id: int
+    batch: int
+    seqlen: int
+    dim: int
+    dstate: int
+    io: str                 # "f32" or "bf16"
+    a_kind: str             # "s4d_real" (-(n+1)) or "exp_log" (-exp(log k) in fp32)
+    has_D: bool = True
+    has_z: bool = True
+    return_final: bool = True
+
+    @property
+    def updates(self) -> int:
+        return self.batch * self.seqlen * self.dim * self.dstate
+
+    def algorithmic_bytes(self) -> int:
+        """Every input read once, every output written once."""
+        e = 2 if self.io == BF16 else 4
+        bld = self.batch * self.seqlen * self.dim
+        bln = self.batch * self.seqlen * self.dstate
+        n = bld * e * 2                     # x, delta
+        n += bld * e if self.has_z else 0   # z
+        n += bln * e * 2                    # B, C
+        n += self.dim * self.dstate * 4     # A (fp32)
+        n += self.dim * 4 if self.has_D else 0
+        n += bld * e                        # out
+        n += self.batch * self.dim * self.dstate * 4 if self.return_final else 0
+        return n
+
+
+@dataclasses.dataclass(frozen=True)
+class SSDConfig:
+    """Mamba-2 scalar-A multi-head workload: x/z [B, L, H, P], delta [B, L, H], B/C [B, L, G, N]."""
+    name: str
+    cfg_id: int
+    batch: int
+    seqlen: int
+    nheads: int
+    headdim: int
+    dstate: int
+    ngroups: int
+    chunk: int
+    io: str = BF16
+    has_D: bool = False
+    has_z: bool = False
+    return_final: bool = True
+
+    @property
+    def updates(self) -> int:
+        return self.batch * self.seqlen * self.nheads * self.headdim * self.dstate
+
+    def algorithmic_bytes(self) -> int:
+        e = 2 if self.io == BF16 else 4
+        blhp = self.batch * self.seqlen * self.nheads * self.headdim
+        n = blhp * e                                            # x
+        n += self.batch * self.seqlen * self.nheads * e         # delta
+        n += 2 * self.batch * self.seqlen * self.ngroups * self.dstate * e  # B, C
+        n += self.nheads * 4                                    # A
+        n += self.nheads * 4 if self.has_D else 0
+        n += blhp * e if self.has_z else 0
+        n += blhp * e                                           # out
+        n += self.batch * self.nheads * self.headdim * self.dstate * 4 if self.return_final else 0
+        return n
+
+
+# The five workloads.  Index 0 is the small fp32 case; index 1 is the
+# 130M-like layer the throughput figure is quoted on.
+CONFIGS = {
+    1: ScanConfig("mamba1_tiny_f32", 1, 1, 256, 64, 16, F32, "s4d_real", return_final=True),
+    2: ScanConfig("mamba1_130m_layer_bf16", 2, 8, 2048, 1536, 16, BF16, "exp_log", return_final=False),
+    3: ScanConfig("mamba1_2p8b_layer_bf16", 3, 4, 8192, 5120, 16, BF16, "s4d_real", return_final=True),
+    4: SSDConfig("mamba2_ssd_bf16", 4, 8, 4096, 32, 64, 128, 1, 256),
+    5: ScanConfig("mamba1_long_1m_bf16", 5, 1, 1 << 20, 2048, 16, BF16, "s4d_real", return_final=True),
+}
+
+
+# ----------------------------------------------------------------------------
+# fp32 -> bf16 (round to nearest even), as raw uint16 bit patterns
+# ----------------------------------------------------------------------------
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bf16 (RNE); returns uint16 bit patterns. Inputs are finite."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# blocked, seeded streams
+# ----------------------------------------------------------------------------
+def _stream(cfg_id: int, tensor: int, block: int, seed_base: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed_base + cfg_id, tensor, block])))
+
+
+def normal_f32(cfg_id: int, tensor: int, n: int, seed_base: int = ROOT_SEED) -> np.ndarray:
+    out = np.empty(n, dtype=np.float32)
+    for j, s in enumerate(range(0, n, BLOCK)):
+        e = min(n, s + BLOCK)
+        _stream(cfg_id, tensor, j, seed_base).standard_normal(e - s, dtype=np.float32, out=out[s:e])
+    return out
+
+
+def uniform_f32(cfg_id: int, tensor: int, n: int, lo: float, hi: float, seed_base: int = ROOT_SEED) -> np.ndarray:
+    out = np.empty(n, dtype=np.float32)
+    for j, s in enumerate(range(0, n, BLOCK)):
+        e = min(n, s + BLOCK)
+        g = _stream(cfg_id, tensor, j, seed_base)
+        out[s:e] = g.random(e - s, dtype=np.float32) * np.float32(hi - lo) + np.float32(lo)
+    return out
+
+
+def softplus_delta_f32(cfg_id: int, n: int, seed_base: int = ROOT_SEED) -> np.ndarray:
+    """delta = softplus(0.5 * N(0,1) - 2), all in fp32 (blockwise to bound memory)."""
+    out = normal_f32(cfg_id, T_DELTA, n, seed_base)
+    for s in range(0, n, BLOCK):
+        v = out[s:s + BLOCK]
+        v *= np.float32(0.5)
+        v -= np.float32(2.0)
+        np.log1p(np.exp(v), out=v)
+    return out
+
+
+def _io(a: np.ndarray, io: str) -> np.ndarray:
+    return f32_to_bf16_bits(a) if io == BF16 else a
+
+
+def s4d_real_A(dim: int, dstate: int) -> np.ndarray:
+    return -np.tile(np.arange(1, dstate + 1, dtype=np.float32), (dim, 1))
+
+
+def exp_log_A(dim: int, dstate: int) -> np.ndarray:
+    k = np.arange(1, dstate + 1, dtype=np.float32)
+    a = -np.exp(np.log(k))          # fp32 arithmetic throughout
+    return np.tile(a.astype(np.float32), (dim, 1))
+
+
+@dataclasses.dataclass
+class ScanInputs:
+    """Host arrays. Tensors in io dtype are uint16 (bf16 bits) or float32."""
+    x: np.ndarray
+    delta: np.ndarray
+    A: np.ndarray
+    B: np.ndarray
+    C: np.ndarray
+    D: Optional[np.ndarray]
+    z: Optional[np.ndarray]
+    h0: Optional[np.ndarray]
+    io: str
+
+
+def make_scan_inputs(cfg: ScanConfig, seed_base: int = ROOT_SEED, with_h0: bool = False) -> ScanInputs:
+    b, l, d, n = cfg.batch, cfg.seqlen, cfg.dim, cfg.dstate
+    cid = cfg.cfg_id
+    x = _io(normal_f32(cid, T_X, b * l * d, seed_base), cfg.io).reshape(b, l, d)
+    delta = _io(softplus_delta_f32(cid, b * l * d, seed_base), cfg.io).reshape(b, l, d)
+    z = _io(normal_f32(cid, T_Z, b * l * d, seed_base), cfg.io).reshape(b, l, d) if cfg.has_z else None
+    Bm = _io(normal_f32(cid, T_B, b * l * n, seed_base), cfg.io).reshape(b, l, n)
+    Cm = _io(normal_f32(cid, T_C, b * l * n, seed_base), cfg.io).reshape(b, l, n)
+    D = normal_f32(cid, T_D, d, seed_base) if cfg.has_D else None
+    if cfg.a_kind == "s4d_real":
+        A = s4d_real_A(d, n)
+    elif cfg.a_kind == "exp_log":
+        A = exp_log_A(d, n)
+    else:
+        raise ValueError(cfg.a_kind)
+    h0 = normal_f32(cid, T_H0, b * d * n, seed_base).reshape(b, d, n) if with_h0 else None
+    return ScanInputs(x, delta, np.ascontiguousarray(A), Bm, Cm, D, z, h0, cfg.io)
+
+
+@dataclasses.dataclass
+class SSDInputs:
+    x: np.ndarray       # [B, L, H, P]
+    delta: np.ndarray   # [B, L, H]
+    A: np.ndarray       # [H] fp32
+    B: np.ndarray       # [B, L, G, N]
+    C: np.ndarray       # [B, L, G, N]
+    D: Optional[np.ndarray]
+    z: Optional[np.ndarray]
+    h0: Optional[np.ndarray]   # [B, H, P, N] fp32
+    io: str
+
+
+def make_ssd_inputs(cfg: SSDConfig, seed_base: int = ROOT_SEED, with_D: Optional[bool] = None,
+                    with_z: Optional[bool] = None, with_h0: bool = False) -> SSDInputs:
+    b, l, h, p, n, g = cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups
+    cid = cfg.cfg_id
+    with_D = cfg.has_D if with_D is None else with_D
+    with_z = cfg.has_z if with_z is None else with_z
+    x = _io(normal_f32(cid, T_X, b * l * h * p, seed_base), cfg.io).reshape(b, l, h, p)
+    delta = _io(softplus_delta_f32(cid, b * l * h, seed_base), cfg.io).reshape(b, l, h)
+    Bm = _io(normal_f32(cid, T_B, b * l * g * n, seed_base), cfg.io).reshape(b, l, g, n)
+    Cm = _io(normal_f32(cid, T_C, b * l * g * n, seed_base), cfg.io).reshape(b, l, g, n)
+    u = uniform_f32(cid, T_A, h, float(np.log(np.float32(1.0))), float(np.log(np.float32(16.0))), seed_base)
+    A = (-np.exp(u)).astype(np.float32)
+    D = normal_f32(cid, T_D, h, seed_base) if with_D else None
+    z = _io(normal_f32(cid, T_Z, b * l * h * p, seed_base), cfg.io).reshape(b, l, h, p) if with_z else None
+    h0 = normal_f32(cid, T_H0, b * h * p * n, seed_base).reshape(b, h, p, n) if with_h0 else None
+    return SSDInputs(x, delta, A, Bm, Cm, D, z, h0, cfg.io)
+
+
+def scan_config(batch: int, seqlen: int, dim: int, dstate: int, io: str = F32, a_kind: str = "s4d_real",
+                has_D: bool = True, has_z: bool = True, cfg_id: int = 100) -> ScanConfig:
+    """An ad-hoc Mamba-1 workload with the standard distributions (for tests)."""
+    return ScanConfig(f"scan_b{batch}_l{seqlen}_d{dim}_n{dstate}_{io}", cfg_id, batch, seqlen, dim, dstate, io,
+                      a_kind, has_D, has_z, True)
+
+
+def ssd_config(batch: int, seqlen: int, nheads: int, headdim: int, dstate: int, ngroups: int = 1,
+               chunk: int = 64, io: str = BF16, has_D: bool = False, has_z: bool = False,
+               cfg_id: int = 200) -> SSDConfig:
+    return SSDConfig(f"ssd_b{batch}_l{seqlen}_h{nheads}_p{headdim}_n{dstate}_g{ngroups}", cfg_id, batch, seqlen,
+                     nheads, headdim, dstate, ngroups, chunk, io, has_D, has_z, True)

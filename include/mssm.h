@@ -1,0 +1,147 @@
+/*
+ * mssm.h -- C ABI of the MI355X (gfx950) selective-scan library (libmssm.so).
+ *
+ * Two forward operations:
+ *
+ *  1. mssm_selective_scan_fwd -- the Mamba-1 selective scan.  Defined by the
+ *     linear state recurrence h_t = A h_{t-1} + B x_t with readout y_t = C h_t
+ *     ("Mamba-2 y state-space models", 4.1), made selective -- B, C and the
+ *     step delta depend on the token ("03 - Modelos de espacio de estados",
+ *     "El mecanismo selectivo de Mamba"; "P20 - Mamba", 5) -- and discretised
+ *     by zero-order hold with a diagonal A, so that exp(delta * A) is taken
+ *     elementwise ("03 - ...", "Discretizacion").  Per (batch b, channel c,
+ *     state n) and time t:
+ *         h[n]     = exp(delta[b,t,c] * A[c,n]) * h[n] + delta[b,t,c] * B[b,t,n] * x[b,t,c]
+ *         y[b,t,c] = sum_n C[b,t,n] * h[n] + D[c] * x[b,t,c]
+ *         out      = y * silu(z[b,t,c]),   silu(v) = v / (1 + exp(-v))
+ *     with h = h0[b,c,:] (or 0) before t = 0.  The input term delta*B*x is
+ *     the Euler step for B (the pages' own ZOH formula for Bbar was lost);
+ *     D and z are optional.
+ *
+ *  2. mssm_ssd_fwd -- the Mamba-2 multi-head form, whose transition is a
+ *     scalar times the identity ("Mamba-3" blog, introduction) on a state
+ *     organised in heads of size headdim ("Mamba-2 y state-space models",
+ *     4.2 and 4.3 notes).  Per (b, head h, p < headdim, n) with group
+ *     g = h / (nheads / ngroups):
+ *         S[p,n]     = exp(delta[b,t,h] * A[h]) * S[p,n] + delta[b,t,h] * B[b,t,g,n] * x[b,t,h,p]
+ *         y[b,t,h,p] = sum_n C[b,t,g,n] * S[p,n] + D[h] * x[b,t,h,p],   out = y * silu(z)
+ *     Computed chunk by chunk with matrix-core contractions (the
+ *     attention-like "SSD" form of "Mamba-2 y state-space models", 4.2);
+ *     the result does not depend on the chunk length except by rounding.
+ *
+ * Conventions shared by every entry point:
+ *  - Every data pointer is a DEVICE pointer owned by the caller.  The library
+ *    never allocates, frees or keeps a pointer after returning, and never
+ *    synchronises: work is enqueued on `stream` (a hipStream_t passed as
+ *    void*; NULL = the null stream) and the call returns at once.
+ *  - Tensors are dense, row-major and contiguous (last index fastest).
+ *    x, delta, B, C, z and out share io_dtype; A, D, h0 and final_state are
+ *    always fp32.  fp32 results are rounded to bf16 to nearest-even.
+ *  - Accumulation and state are fp32 whatever io_dtype is.
+ *  - `out` and `final_state` must not alias any input or each other.
+ *  - Errors: a negative mssm_status.  All argument checks run on the host
+ *    before anything is enqueued; on error nothing is enqueued and outputs
+ *    are untouched.  MSSM_ERR_HIP means a launch failed; the HIP error text
+ *    of the calling thread's last failure is returned by
+ *    mssm_last_error_detail().
+ *  - Thread-safe: no mutable global state (apart from that per-thread error
+ *    text).  Calls on different streams may overlap.
+ */
+#ifndef MSSM_H
+#define MSSM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSSM_ABI_VERSION 1
+
+typedef enum {
+    MSSM_OK = 0,
+    MSSM_ERR_INVALID_ARG = -1,   /* null required pointer, size <= 0, size overflow, aliasing */
+    MSSM_ERR_UNSUPPORTED = -2,   /* dtype, dstate outside 1..256, nheads % ngroups != 0, bad chunk */
+    MSSM_ERR_MISALIGNED = -3,    /* a pointer not aligned to its element size */
+    MSSM_ERR_WORKSPACE = -4,     /* workspace missing or smaller than the size query asks */
+    MSSM_ERR_HIP = -5            /* a HIP launch failed (see mssm_last_error_detail) */
+} mssm_status;
+
+typedef enum { MSSM_F32 = 0, MSSM_BF16 = 1 } mssm_dtype;
+
+/* Mamba-1 selective scan problem.
+ *   x, delta, z, out : [batch, seqlen, dim]      (io_dtype)
+ *   B, C             : [batch, seqlen, dstate]   (io_dtype; shared by all channels)
+ *   A                : [dim, dstate] fp32 (the values of A, normally negative)
+ *   D                : [dim] fp32, nullable
+ *   h0, final_state  : [batch, dim, dstate] fp32, nullable
+ * split_seq   : number of sequence chunks scanned in parallel with an exact
+ *               inter-chunk state carry (0 = library's choice, else 1..4096).
+ * split_state : lanes that share one channel's dstate states (0 = library's
+ *               choice, else 1, 2, 4, 8 or 16).
+ * dstate must be 1..256. */
+typedef struct {
+    int64_t batch, seqlen, dim, dstate;
+    int32_t io_dtype;   /* mssm_dtype */
+    int32_t split_seq;
+    int32_t split_state;
+    uint32_t flags;     /* reserved, must be 0 */
+} mssm_scan_desc;
+
+/* Mamba-2 scalar-A multi-head problem.
+ *   x, z, out        : [batch, seqlen, nheads, headdim]   (io_dtype)
+ *   delta            : [batch, seqlen, nheads]             (io_dtype)
+ *   B, C             : [batch, seqlen, ngroups, dstate]    (io_dtype)
+ *   A, D             : [nheads] fp32 (D nullable)
+ *   h0, final_state  : [batch, nheads, headdim, dstate] fp32, nullable
+ * chunk: time-chunk length of the matrix form: 0 (library's choice), 32, 64,
+ * 128 or 256.  io_dtype must be MSSM_BF16 (the matrix cores take bf16
+ * operands).  headdim must be a multiple of 16 and at most 256; dstate a
+ * multiple of 16 and at most 256. */
+typedef struct {
+    int64_t batch, seqlen, nheads, headdim, dstate, ngroups, chunk;
+    int32_t io_dtype;
+    uint32_t flags;     /* reserved, must be 0 */
+} mssm_ssd_desc;
+
+/* Selective scan forward.  workspace: device memory of at least
+ * mssm_selective_scan_workspace_size(desc) bytes (may be NULL when that size
+ * is 0), 256-byte aligned, reusable once the stream has passed this call. */
+int mssm_selective_scan_fwd(const mssm_scan_desc* desc,
+                            const void* x, const void* delta, const float* A,
+                            const void* B, const void* C, const float* D, const void* z,
+                            const float* h0, void* out, float* final_state,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace mssm_selective_scan_fwd needs for this problem (0 when
+ * the sequence is not split).  Returns 0 for an invalid descriptor too. */
+size_t mssm_selective_scan_workspace_size(const mssm_scan_desc* desc);
+
+/* Mamba-2 scalar-A multi-head forward.  Same ownership, stream and error rules
+ * as mssm_selective_scan_fwd. */
+int mssm_ssd_fwd(const mssm_ssd_desc* desc,
+                 const void* x, const void* delta, const float* A,
+                 const void* B, const void* C, const float* D, const void* z,
+                 const float* h0, void* out, float* final_state,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+size_t mssm_ssd_workspace_size(const mssm_ssd_desc* desc);
+
+/* The plan the library would use for a selective-scan descriptor:
+ * writes the sequence-chunk count and lanes-per-channel; returns a status. */
+int mssm_selective_scan_plan(const mssm_scan_desc* desc, int32_t* split_seq, int32_t* split_state);
+
+/* Static text for a status code (never NULL). */
+const char* mssm_status_string(int status);
+
+/* Text of the calling thread's last MSSM_ERR_HIP failure ("" if none). */
+const char* mssm_last_error_detail(void);
+
+int mssm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSSM_H */

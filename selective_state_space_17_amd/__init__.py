@@ -1,0 +1,227 @@
+"""MI355X (gfx950) selective scan: thin Python binding of libmssm.so.
+
+Every step of the computation runs in the library's HIP kernels; this module
+only checks tensors, allocates outputs and workspace with torch (device memory
+and streams are all torch is used for) and forwards raw pointers through the C
+ABI declared in include/mssm.h.  There is no fallback path: if the library is
+missing, importing this package raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmssm.so")
+
+MSSM_OK = 0
+MSSM_ERR_INVALID_ARG = -1
+MSSM_ERR_UNSUPPORTED = -2
+MSSM_ERR_MISALIGNED = -3
+MSSM_ERR_WORKSPACE = -4
+MSSM_ERR_HIP = -5
+MSSM_F32 = 0
+MSSM_BF16 = 1
+
+
+class ScanDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("dim", ctypes.c_int64),
+                ("dstate", ctypes.c_int64), ("io_dtype", ctypes.c_int32), ("split_seq", ctypes.c_int32),
+                ("split_state", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+class SSDDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
+                ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
+                ("chunk", ctypes.c_int64), ("io_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+# every exported symbol and its ctypes signature (checked against include/mssm.h by the tests)
+_P, _SZ, _I = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+SIGNATURES = {
+    "mssm_selective_scan_fwd": (_I, [ctypes.POINTER(ScanDesc)] + [_P] * 10 + [_P, _SZ, _P]),
+    "mssm_selective_scan_workspace_size": (_SZ, [ctypes.POINTER(ScanDesc)]),
+    "mssm_selective_scan_plan": (_I, [ctypes.POINTER(ScanDesc), ctypes.POINTER(ctypes.c_int32),
+                                      ctypes.POINTER(ctypes.c_int32)]),
+    "mssm_ssd_fwd": (_I, [ctypes.POINTER(SSDDesc)] + [_P] * 10 + [_P, _SZ, _P]),
+    "mssm_ssd_workspace_size": (_SZ, [ctypes.POINTER(SSDDesc)]),
+    "mssm_status_string": (ctypes.c_char_p, [_I]),
+    "mssm_last_error_detail": (ctypes.c_char_p, []),
+    "mssm_abi_version": (_I, []),
+}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m selective_state_space_17_amd.build` "
+                          "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+class MssmError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        detail = lib.mssm_last_error_detail().decode() if status == MSSM_ERR_HIP else ""
+        msg = f"{what}: {lib.mssm_status_string(status).decode()} ({status})"
+        super().__init__(msg + (f": {detail}" if detail else ""))
+        self.status = status
+
+
+def abi_version() -> int:
+    return lib.mssm_abi_version()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _check_gpu(name, t, dtype, shape):
+    torch = _torch()
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _io_code(dtype) -> int:
+    torch = _torch()
+    if dtype == torch.float32:
+        return MSSM_F32
+    if dtype == torch.bfloat16:
+        return MSSM_BF16
+    raise TypeError(f"io dtype must be float32 or bfloat16, got {dtype}")
+
+
+def _stream_handle(stream) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def scan_desc(batch, seqlen, dim, dstate, io_dtype, split_seq=0, split_state=0) -> ScanDesc:
+    return ScanDesc(batch, seqlen, dim, dstate, io_dtype, split_seq, split_state, 0)
+
+
+def selective_scan_plan(batch: int, seqlen: int, dim: int, dstate: int, io_dtype: int = MSSM_BF16,
+                        split_seq: int = 0, split_state: int = 0) -> Tuple[int, int]:
+    """(sequence chunks, lanes per channel) the library picks for this problem."""
+    d = scan_desc(batch, seqlen, dim, dstate, io_dtype, split_seq, split_state)
+    k, g = ctypes.c_int32(0), ctypes.c_int32(0)
+    st = lib.mssm_selective_scan_plan(ctypes.byref(d), ctypes.byref(k), ctypes.byref(g))
+    if st != MSSM_OK:
+        raise MssmError(st, "mssm_selective_scan_plan")
+    return k.value, g.value
+
+
+def selective_scan_workspace_size(batch, seqlen, dim, dstate, io_dtype=MSSM_BF16, split_seq=0, split_state=0) -> int:
+    d = scan_desc(batch, seqlen, dim, dstate, io_dtype, split_seq, split_state)
+    return lib.mssm_selective_scan_workspace_size(ctypes.byref(d))
+
+
+def selective_scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, return_final_state: bool = False,
+                       split_seq: int = 0, split_state: int = 0, out=None, final_state=None, workspace=None,
+                       stream=None):
+    """Mamba-1 selective scan forward (mssm_selective_scan_fwd).
+
+    x, delta, z: [batch, seqlen, dim]; B, C: [batch, seqlen, dstate] (float32 or bfloat16, all alike);
+    A: [dim, dstate] float32; D: [dim] float32; h0: [batch, dim, dstate] float32.
+    Returns out (and final_state [batch, dim, dstate] float32 when requested).
+    """
+    torch = _torch()
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, seqlen, dim]")
+    bsz, L, dm = x.shape
+    if A.dim() != 2 or A.shape[0] != dm:
+        raise ValueError("A must be [dim, dstate]")
+    N = A.shape[1]
+    io = _io_code(x.dtype)
+    for name, t, shape in (("x", x, (bsz, L, dm)), ("delta", delta, (bsz, L, dm)), ("z", z, (bsz, L, dm)),
+                           ("B", B, (bsz, L, N)), ("C", C, (bsz, L, N))):
+        _check_gpu(name, t, x.dtype, shape)
+    _check_gpu("A", A, torch.float32, (dm, N))
+    _check_gpu("D", D, torch.float32, (dm,))
+    _check_gpu("h0", h0, torch.float32, (bsz, dm, N))
+    if out is None:
+        out = torch.empty_like(x)
+    _check_gpu("out", out, x.dtype, (bsz, L, dm))
+    if return_final_state and final_state is None:
+        final_state = torch.empty((bsz, dm, N), dtype=torch.float32, device=x.device)
+    _check_gpu("final_state", final_state, torch.float32, (bsz, dm, N))
+    d = scan_desc(bsz, L, dm, N, io, split_seq, split_state)
+    ws_bytes = lib.mssm_selective_scan_workspace_size(ctypes.byref(d))
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    st = lib.mssm_selective_scan_fwd(ctypes.byref(d), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                     _ptr(z), _ptr(h0), _ptr(out), _ptr(final_state),
+                                     _ptr(workspace) if ws_bytes else None,
+                                     workspace.numel() if (ws_bytes and workspace is not None) else 0,
+                                     _stream_handle(stream))
+    if st != MSSM_OK:
+        raise MssmError(st, "mssm_selective_scan_fwd")
+    return (out, final_state) if return_final_state else out
+
+
+def ssd_desc(batch, seqlen, nheads, headdim, dstate, ngroups, chunk=0, io_dtype=MSSM_BF16) -> SSDDesc:
+    return SSDDesc(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, io_dtype, 0)
+
+
+def ssd_workspace_size(batch, seqlen, nheads, headdim, dstate, ngroups, chunk=0) -> int:
+    d = ssd_desc(batch, seqlen, nheads, headdim, dstate, ngroups, chunk)
+    return lib.mssm_ssd_workspace_size(ctypes.byref(d))
+
+
+def ssd_fwd(x, delta, A, B, C, D=None, z=None, h0=None, chunk: int = 0, return_final_state: bool = False,
+            out=None, final_state=None, workspace=None, stream=None):
+    """Mamba-2 scalar-A multi-head forward (mssm_ssd_fwd).
+
+    x, z: [batch, seqlen, nheads, headdim] bfloat16; delta: [batch, seqlen, nheads] bfloat16;
+    B, C: [batch, seqlen, ngroups, dstate] bfloat16; A, D: [nheads] float32;
+    h0: [batch, nheads, headdim, dstate] float32.
+    """
+    torch = _torch()
+    if x.dim() != 4 or B.dim() != 4:
+        raise ValueError("x must be [batch, seqlen, nheads, headdim] and B [batch, seqlen, ngroups, dstate]")
+    bsz, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    io = _io_code(x.dtype)
+    for name, t, shape in (("x", x, (bsz, L, H, P)), ("z", z, (bsz, L, H, P)), ("delta", delta, (bsz, L, H)),
+                           ("B", B, (bsz, L, G, N)), ("C", C, (bsz, L, G, N))):
+        _check_gpu(name, t, x.dtype, shape)
+    _check_gpu("A", A, torch.float32, (H,))
+    _check_gpu("D", D, torch.float32, (H,))
+    _check_gpu("h0", h0, torch.float32, (bsz, H, P, N))
+    if out is None:
+        out = torch.empty_like(x)
+    _check_gpu("out", out, x.dtype, (bsz, L, H, P))
+    if return_final_state and final_state is None:
+        final_state = torch.empty((bsz, H, P, N), dtype=torch.float32, device=x.device)
+    _check_gpu("final_state", final_state, torch.float32, (bsz, H, P, N))
+    d = ssd_desc(bsz, L, H, P, N, G, chunk, io)
+    ws_bytes = lib.mssm_ssd_workspace_size(ctypes.byref(d))
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    st = lib.mssm_ssd_fwd(ctypes.byref(d), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                          _ptr(h0), _ptr(out), _ptr(final_state), _ptr(workspace) if ws_bytes else None,
+                          workspace.numel() if (ws_bytes and workspace is not None) else 0, _stream_handle(stream))
+    if st != MSSM_OK:
+        raise MssmError(st, "mssm_ssd_fwd")
+    return (out, final_state) if return_final_state else out

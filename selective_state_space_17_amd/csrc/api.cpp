@@ -1,0 +1,289 @@
+// C-ABI front end of libmssm: argument checks, planning, dispatch.
+// Every check runs on the host before anything is enqueued.
+#include "../../include/mssm.h"
+
+#include <cmath>
+#include <cstring>
+#include <limits>
+
+#include "internal.h"
+
+namespace {
+
+thread_local char g_err[256] = "";
+
+void set_err(hipError_t e) {
+  const char* s = hipGetErrorString(e);
+  std::strncpy(g_err, s ? s : "unknown HIP error", sizeof(g_err) - 1);
+  g_err[sizeof(g_err) - 1] = '\0';
+}
+
+constexpr int64_t kSimds = 256 * 4;   // MI355X: 256 CUs x 4 SIMDs
+
+bool mul_ok(int64_t a, int64_t b, int64_t* r) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > std::numeric_limits<int64_t>::max() / a) return false;
+  *r = a * b;
+  return true;
+}
+
+bool aligned(const void* p, size_t a) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;
+};
+Range rng(const void* p, int64_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return {a, a + static_cast<uintptr_t>(bytes)};
+}
+bool overlap(const void* p, int64_t pb, const void* q, int64_t qb) {
+  if (p == nullptr || q == nullptr || pb <= 0 || qb <= 0) return false;
+  const Range a = rng(p, pb), b = rng(q, qb);
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+// --------------------------------------------------------------------------
+// Mamba-1 planning
+// --------------------------------------------------------------------------
+int states_per_lane(int G, int64_t N) {
+  const int64_t need = (N + G - 1) / G;
+  return need <= 4 ? 4 : (need <= 8 ? 8 : 16);
+}
+
+int ilog2(int v) {
+  int r = 0;
+  while ((1 << (r + 1)) <= v) ++r;
+  return r;
+}
+
+// Estimated kernel time in VALU issue slots per lane (smaller is better).
+double scan_cost(const mssm_scan_desc& d, int G, int K) {
+  const int npl = states_per_lane(G, d.dstate);
+  const int64_t cpw = 64 / G;
+  const int64_t groups = d.batch * ((d.dim + cpw - 1) / cpw);
+  const double slots_step = npl * 6.0 + ilog2(G) + 14.0;   // 6 slots per state update + per-step epilogue
+  const int64_t chunk = (d.seqlen + K - 1) / K;
+  // pass 2 rescans until the carried-in state has decayed (about 800 steps for
+  // softplus-distributed deltas and |A| >= 1); bounded by the chunk length
+  const double steps = static_cast<double>(chunk) + (K > 1 ? std::min<double>(chunk, 800.0) : 0.0);
+  const int64_t waves = groups * K;
+  const int64_t per_simd = (waves + kSimds - 1) / kSimds;
+  const double eff = per_simd <= 1 ? 0.85 : (per_simd == 2 ? 0.93 : 0.97);
+  return steps * slots_step * static_cast<double>(per_simd) / eff + (K > 1 ? 2e4 : 0.0);
+}
+
+int validate_scan_desc(const mssm_scan_desc* d) {
+  if (d == nullptr) return MSSM_ERR_INVALID_ARG;
+  if (d->batch < 0 || d->seqlen < 0 || d->dim <= 0 || d->dstate <= 0) return MSSM_ERR_INVALID_ARG;
+  if (d->flags != 0) return MSSM_ERR_INVALID_ARG;
+  if (d->io_dtype != MSSM_F32 && d->io_dtype != MSSM_BF16) return MSSM_ERR_UNSUPPORTED;
+  if (d->dstate > 256) return MSSM_ERR_UNSUPPORTED;
+  if (d->split_seq < 0 || d->split_seq > 4096) return MSSM_ERR_INVALID_ARG;
+  if (d->split_state != 0 && !mssm::scan_supported_G(d->split_state, d->dstate)) return MSSM_ERR_UNSUPPORTED;
+  const int64_t es = d->io_dtype == MSSM_BF16 ? 2 : 4;
+  int64_t t = 0;
+  if (!mul_ok(d->batch, d->seqlen, &t) || !mul_ok(t, d->dim, &t) || !mul_ok(t, es, &t)) return MSSM_ERR_INVALID_ARG;
+  if (!mul_ok(d->batch, d->seqlen, &t) || !mul_ok(t, d->dstate, &t) || !mul_ok(t, es, &t)) return MSSM_ERR_INVALID_ARG;
+  if (!mul_ok(d->batch, d->dim, &t) || !mul_ok(t, d->dstate, &t) || !mul_ok(t, 4 * 4096, &t)) return MSSM_ERR_INVALID_ARG;
+  return MSSM_OK;
+}
+
+int plan_scan(const mssm_scan_desc& d, int* K_out, int* G_out) {
+  int bestK = 1, bestG = 0;
+  double best = std::numeric_limits<double>::infinity();
+  const int Gs[] = {1, 2, 4, 8, 16};
+  for (int G : Gs) {
+    if (!mssm::scan_supported_G(G, d.dstate)) continue;
+    if (d.split_state != 0 && G != d.split_state) continue;
+    if (d.split_seq != 0) {
+      const int K = static_cast<int>(std::min<int64_t>(d.split_seq, std::max<int64_t>(d.seqlen, 1)));
+      const double c = scan_cost(d, G, K);
+      if (c < best) { best = c; bestK = K; bestG = G; }
+      continue;
+    }
+    for (int K = 1; K <= 4096; K *= 2) {
+      if (K > 1 && d.seqlen / K < 256) break;
+      const double c = scan_cost(d, G, K);
+      if (c < best) { best = c; bestK = K; bestG = G; }
+    }
+  }
+  if (bestG == 0) return MSSM_ERR_UNSUPPORTED;
+  // the grid is 1-D: batch * K * channel-groups blocks
+  const int64_t cpw = 64 / bestG;
+  const int64_t blocks = d.batch * bestK * ((d.dim + cpw - 1) / cpw);
+  if (blocks > std::numeric_limits<int32_t>::max()) return MSSM_ERR_UNSUPPORTED;
+  *K_out = bestK;
+  *G_out = bestG;
+  return MSSM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mssm_abi_version(void) { return MSSM_ABI_VERSION; }
+
+const char* mssm_status_string(int status) {
+  switch (status) {
+    case MSSM_OK: return "ok";
+    case MSSM_ERR_INVALID_ARG: return "invalid argument";
+    case MSSM_ERR_UNSUPPORTED: return "unsupported problem";
+    case MSSM_ERR_MISALIGNED: return "misaligned pointer";
+    case MSSM_ERR_WORKSPACE: return "workspace missing or too small";
+    case MSSM_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char* mssm_last_error_detail(void) { return g_err; }
+
+int mssm_selective_scan_plan(const mssm_scan_desc* desc, int32_t* split_seq, int32_t* split_state) {
+  const int v = validate_scan_desc(desc);
+  if (v != MSSM_OK) return v;
+  if (split_seq == nullptr || split_state == nullptr) return MSSM_ERR_INVALID_ARG;
+  int K = 1, G = 1;
+  const int r = plan_scan(*desc, &K, &G);
+  if (r != MSSM_OK) return r;
+  *split_seq = K;
+  *split_state = G;
+  return MSSM_OK;
+}
+
+size_t mssm_selective_scan_workspace_size(const mssm_scan_desc* desc) {
+  if (validate_scan_desc(desc) != MSSM_OK) return 0;
+  int K = 1, G = 1;
+  if (plan_scan(*desc, &K, &G) != MSSM_OK) return 0;
+  return mssm::scan_workspace_bytes(desc->batch, desc->dim, desc->dstate, K);
+}
+
+int mssm_selective_scan_fwd(const mssm_scan_desc* desc, const void* x, const void* delta, const float* A,
+                            const void* B, const void* C, const float* D, const void* z, const float* h0, void* out,
+                            float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
+  const int v = validate_scan_desc(desc);
+  if (v != MSSM_OK) return v;
+  const mssm_scan_desc& d = *desc;
+  if (d.batch == 0) return MSSM_OK;
+  const int64_t es = d.io_dtype == MSSM_BF16 ? 2 : 4;
+  const int64_t n_bld = d.batch * d.seqlen * d.dim;
+  const int64_t n_bln = d.batch * d.seqlen * d.dstate;
+  const bool has_steps = n_bld > 0;
+  if (A == nullptr) return MSSM_ERR_INVALID_ARG;
+  if (has_steps && (x == nullptr || delta == nullptr || B == nullptr || C == nullptr || out == nullptr))
+    return MSSM_ERR_INVALID_ARG;
+  if (!aligned(x, es) || !aligned(delta, es) || !aligned(B, es) || !aligned(C, es) || !aligned(z, es) ||
+      !aligned(out, es) || !aligned(A, 4) || !aligned(D, 4) || !aligned(h0, 4) || !aligned(final_state, 4))
+    return MSSM_ERR_MISALIGNED;
+  // outputs must not alias inputs or each other
+  const int64_t b_io = n_bld * es, b_bc = n_bln * es;
+  const int64_t b_st = d.batch * d.dim * d.dstate * 4;
+  const void* ins[] = {x, delta, B, C, z, A, D, h0};
+  const int64_t inb[] = {b_io, b_io, b_bc, b_bc, b_io, d.dim * d.dstate * 4, d.dim * 4, b_st};
+  for (int i = 0; i < 8; ++i) {
+    if (overlap(out, b_io, ins[i], inb[i])) return MSSM_ERR_INVALID_ARG;
+    if (overlap(final_state, b_st, ins[i], inb[i])) return MSSM_ERR_INVALID_ARG;
+  }
+  if (overlap(out, b_io, final_state, b_st)) return MSSM_ERR_INVALID_ARG;
+
+  int K = 1, G = 1;
+  const int pr = plan_scan(d, &K, &G);
+  if (pr != MSSM_OK) return pr;
+  const size_t need = mssm::scan_workspace_bytes(d.batch, d.dim, d.dstate, K);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need) return MSSM_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return MSSM_ERR_MISALIGNED;
+    if (overlap(workspace, static_cast<int64_t>(need), out, b_io) ||
+        overlap(workspace, static_cast<int64_t>(need), final_state, b_st))
+      return MSSM_ERR_INVALID_ARG;
+  }
+
+  mssm::ScanArgs a{};
+  a.x = x; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.h0 = h0;
+  a.out = out; a.final_state = final_state; a.workspace = workspace;
+  a.batch = d.batch; a.L = d.seqlen; a.dim = d.dim; a.N = d.dstate;
+  a.io = d.io_dtype; a.K = K; a.G = G;
+  const hipError_t e = mssm::scan_launch(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    set_err(e);
+    return MSSM_ERR_HIP;
+  }
+  return MSSM_OK;
+}
+
+// --------------------------------------------------------------------------
+// Mamba-2 scalar-A multi-head form
+// --------------------------------------------------------------------------
+static int validate_ssd_desc(const mssm_ssd_desc* d, int64_t* Q) {
+  if (d == nullptr) return MSSM_ERR_INVALID_ARG;
+  if (d->batch < 0 || d->seqlen < 0 || d->nheads <= 0 || d->headdim <= 0 || d->dstate <= 0 || d->ngroups <= 0)
+    return MSSM_ERR_INVALID_ARG;
+  if (d->flags != 0) return MSSM_ERR_INVALID_ARG;
+  if (d->io_dtype != MSSM_BF16) return MSSM_ERR_UNSUPPORTED;
+  if (d->nheads % d->ngroups != 0) return MSSM_ERR_UNSUPPORTED;
+  if (d->headdim % 16 != 0 || d->headdim > 256 || d->dstate % 16 != 0 || d->dstate > 256) return MSSM_ERR_UNSUPPORTED;
+  const int64_t q = d->chunk == 0 ? 64 : d->chunk;
+  if (q != 32 && q != 64 && q != 128 && q != 256) return MSSM_ERR_UNSUPPORTED;
+  int64_t t = 0;
+  if (!mul_ok(d->batch, d->seqlen, &t) || !mul_ok(t, d->nheads, &t) || !mul_ok(t, d->headdim, &t) ||
+      !mul_ok(t, 2, &t))
+    return MSSM_ERR_INVALID_ARG;
+  if (!mul_ok(d->batch, d->seqlen, &t) || !mul_ok(t, d->ngroups, &t) || !mul_ok(t, d->dstate, &t) ||
+      !mul_ok(t, 2, &t))
+    return MSSM_ERR_INVALID_ARG;
+  if (!mul_ok(d->batch, d->nheads, &t) || !mul_ok(t, d->headdim, &t) || !mul_ok(t, d->dstate, &t) ||
+      !mul_ok(t, 4, &t))
+    return MSSM_ERR_INVALID_ARG;
+  *Q = q;
+  return MSSM_OK;
+}
+
+size_t mssm_ssd_workspace_size(const mssm_ssd_desc* desc) {
+  int64_t Q = 0;
+  if (validate_ssd_desc(desc, &Q) != MSSM_OK) return 0;
+  return mssm::ssd_workspace_bytes(desc->batch, desc->seqlen, desc->nheads, desc->headdim, desc->dstate,
+                                   desc->ngroups, Q);
+}
+
+int mssm_ssd_fwd(const mssm_ssd_desc* desc, const void* x, const void* delta, const float* A, const void* B,
+                 const void* C, const float* D, const void* z, const float* h0, void* out, float* final_state,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  int64_t Q = 0;
+  const int v = validate_ssd_desc(desc, &Q);
+  if (v != MSSM_OK) return v;
+  const mssm_ssd_desc& d = *desc;
+  if (d.batch == 0) return MSSM_OK;
+  const int64_t n_x = d.batch * d.seqlen * d.nheads * d.headdim;
+  const int64_t n_d = d.batch * d.seqlen * d.nheads;
+  const int64_t n_bc = d.batch * d.seqlen * d.ngroups * d.dstate;
+  const int64_t b_st = d.batch * d.nheads * d.headdim * d.dstate * 4;
+  const bool has_steps = n_x > 0;
+  if (A == nullptr) return MSSM_ERR_INVALID_ARG;
+  if (has_steps && (x == nullptr || delta == nullptr || B == nullptr || C == nullptr || out == nullptr))
+    return MSSM_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(z, 16) || !aligned(out, 16) || !aligned(B, 16) || !aligned(C, 16) ||
+      !aligned(delta, 2) || !aligned(A, 4) || !aligned(D, 4) || !aligned(h0, 16) || !aligned(final_state, 16))
+    return MSSM_ERR_MISALIGNED;
+  const void* ins[] = {x, delta, B, C, z, A, D, h0};
+  const int64_t inb[] = {n_x * 2, n_d * 2, n_bc * 2, n_bc * 2, n_x * 2, d.nheads * 4, d.nheads * 4, b_st};
+  for (int i = 0; i < 8; ++i) {
+    if (overlap(out, n_x * 2, ins[i], inb[i])) return MSSM_ERR_INVALID_ARG;
+    if (overlap(final_state, b_st, ins[i], inb[i])) return MSSM_ERR_INVALID_ARG;
+  }
+  if (overlap(out, n_x * 2, final_state, b_st)) return MSSM_ERR_INVALID_ARG;
+  const size_t need = mssm::ssd_workspace_bytes(d.batch, d.seqlen, d.nheads, d.headdim, d.dstate, d.ngroups, Q);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need) return MSSM_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return MSSM_ERR_MISALIGNED;
+  }
+  mssm::SSDArgs a{};
+  a.x = x; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.h0 = h0;
+  a.out = out; a.final_state = final_state; a.workspace = workspace;
+  a.batch = d.batch; a.L = d.seqlen; a.H = d.nheads; a.P = d.headdim; a.N = d.dstate; a.G = d.ngroups; a.Q = Q;
+  const hipError_t e = mssm::ssd_launch(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    set_err(e);
+    return MSSM_ERR_HIP;
+  }
+  return MSSM_OK;
+}
+
+}  // extern "C"

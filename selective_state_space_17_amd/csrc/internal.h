@@ -1,0 +1,65 @@
+// Internal declarations shared by the C-ABI front end and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mssm {
+
+// ---------------------------------------------------------------------------
+// Mamba-1 selective scan
+// ---------------------------------------------------------------------------
+struct ScanArgs {
+  const void* x;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;       // nullable
+  const void* z;        // nullable
+  const float* h0;      // nullable
+  void* out;
+  float* final_state;   // nullable
+  void* workspace;
+  int64_t batch, L, dim, N;
+  int io;               // 0 fp32, 1 bf16
+  int K;                // sequence chunks
+  int G;                // lanes per channel
+};
+
+// Workspace layout for K > 1 (all fp32 / int32, 256-byte aligned blocks):
+//   hend [batch][K][dim][N]  state at each chunk's end (chunk 0: true; others: from zero)
+//   hin  [batch][K][dim][N]  true state entering each chunk
+//   S    [batch][K][dim]     sum of delta over each chunk
+//   neg  [batch][K][dim]     chunk contained a negative delta
+size_t scan_workspace_bytes(int64_t batch, int64_t dim, int64_t N, int K);
+
+// Enqueue the scan; returns hipSuccess or the launch error.
+hipError_t scan_launch(const ScanArgs& a, hipStream_t stream);
+
+// lanes-per-channel values the kernels are built for
+bool scan_supported_G(int G, int64_t N);
+
+// ---------------------------------------------------------------------------
+// Mamba-2 scalar-A multi-head (SSD) form
+// ---------------------------------------------------------------------------
+struct SSDArgs {
+  const void* x;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;
+  const void* z;
+  const float* h0;
+  void* out;
+  float* final_state;
+  void* workspace;
+  int64_t batch, L, H, P, N, G, Q;
+};
+
+size_t ssd_workspace_bytes(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q);
+hipError_t ssd_launch(const SSDArgs& a, hipStream_t stream);
+
+}  // namespace mssm

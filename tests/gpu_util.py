@@ -1,0 +1,57 @@
+"""Helpers for the GPU parity tests: host<->device copies and the tolerance rule.
+
+Tolerance (both forms): an element passes iff |g - r| <= rtol * max(|r|, rms(r)),
+rms over the compared tensor; rtol = 1e-4 for fp32 I/O and 2e-2 for bf16 I/O
+with fp32 state.  The rms floor keeps the rule well-posed where the silu gate
+drives outputs to ~0.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+from workloads import bf16_bits_to_f32
+
+RTOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def dev(a):
+    import torch
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(a).cuda()
+
+
+def host64(t) -> np.ndarray:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return bf16_bits_to_f32(t.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+    return t.detach().cpu().numpy().astype(np.float64)
+
+
+def check(got: np.ndarray, ref: np.ndarray, rtol: float, what: str) -> dict:
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, f"{what}: shape {got.shape} vs {ref.shape}"
+    assert np.all(np.isfinite(got)), f"{what}: non-finite GPU values"
+    if ref.size == 0:
+        return {"max_rel": 0.0, "normwise": 0.0}
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    scale = np.maximum(np.abs(ref), rms)
+    err = np.abs(got - ref)
+    bad = err > rtol * scale
+    rel = float(np.max(err / np.where(scale > 0, scale, 1.0)))
+    nw = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+    if bad.any():
+        i = np.unravel_index(np.argmax(err / np.where(scale > 0, scale, 1.0)), ref.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())}/{ref.size} elements out of tolerance {rtol}; "
+                             f"worst at {i}: got {got[i]!r} ref {ref[i]!r}; max rel {rel:.3e}, normwise {nw:.3e}")
+    return {"max_rel": rel, "normwise": nw}

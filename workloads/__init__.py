@@ -27,6 +27,8 @@ Blocks make generation streamable and deterministic for any size.
 from __future__ import annotations
 
 import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
 from typing import Optional
 
 import numpy as np
@@ -142,36 +144,73 @@ def _stream(cfg_id: int, tensor: int, block: int, seed_base: int) -> np.random.G
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed_base + cfg_id, tensor, block])))
 
 
-def normal_f32(cfg_id: int, tensor: int, n: int, seed_base: int = ROOT_SEED) -> np.ndarray:
-    out = np.empty(n, dtype=np.float32)
+def _blocks(n: int):
     for j, s in enumerate(range(0, n, BLOCK)):
-        e = min(n, s + BLOCK)
-        _stream(cfg_id, tensor, j, seed_base).standard_normal(e - s, dtype=np.float32, out=out[s:e])
+        yield j, s, min(n, s + BLOCK)
+
+
+_WORKERS = max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _for_blocks(n: int, fn) -> None:
+    """Run fn(j, s, e) for every block (independent streams, so order does not matter)."""
+    blocks = list(_blocks(n))
+    if len(blocks) <= 1:
+        for blk in blocks:
+            fn(*blk)
+        return
+    with ThreadPoolExecutor(max_workers=_WORKERS) as ex:
+        list(ex.map(lambda blk: fn(*blk), blocks))
+
+
+def _alloc(n: int, io: str) -> np.ndarray:
+    return np.empty(n, dtype=np.uint16 if io == BF16 else np.float32)
+
+
+def _store(out: np.ndarray, s: int, e: int, v: np.ndarray) -> None:
+    out[s:e] = f32_to_bf16_bits(v) if out.dtype == np.uint16 else v
+
+
+def normal(cfg_id: int, tensor: int, n: int, io: str = F32, seed_base: int = ROOT_SEED) -> np.ndarray:
+    """N(0,1) drawn in fp32, stored in io dtype (bf16 bits rounded to nearest even)."""
+    out = _alloc(n, io)
+
+    def fill(j, s, e):
+        _store(out, s, e, _stream(cfg_id, tensor, j, seed_base).standard_normal(e - s, dtype=np.float32))
+
+    _for_blocks(n, fill)
     return out
+
+
+def normal_f32(cfg_id: int, tensor: int, n: int, seed_base: int = ROOT_SEED) -> np.ndarray:
+    return normal(cfg_id, tensor, n, F32, seed_base)
 
 
 def uniform_f32(cfg_id: int, tensor: int, n: int, lo: float, hi: float, seed_base: int = ROOT_SEED) -> np.ndarray:
     out = np.empty(n, dtype=np.float32)
-    for j, s in enumerate(range(0, n, BLOCK)):
-        e = min(n, s + BLOCK)
+    for j, s, e in _blocks(n):
         g = _stream(cfg_id, tensor, j, seed_base)
         out[s:e] = g.random(e - s, dtype=np.float32) * np.float32(hi - lo) + np.float32(lo)
     return out
 
 
-def softplus_delta_f32(cfg_id: int, n: int, seed_base: int = ROOT_SEED) -> np.ndarray:
-    """delta = softplus(0.5 * N(0,1) - 2), all in fp32 (blockwise to bound memory)."""
-    out = normal_f32(cfg_id, T_DELTA, n, seed_base)
-    for s in range(0, n, BLOCK):
-        v = out[s:s + BLOCK]
+def softplus_delta(cfg_id: int, n: int, io: str = F32, seed_base: int = ROOT_SEED) -> np.ndarray:
+    """delta = softplus(0.5 * N(0,1) - 2), evaluated in fp32, stored in io dtype."""
+    out = _alloc(n, io)
+
+    def fill(j, s, e):
+        v = _stream(cfg_id, T_DELTA, j, seed_base).standard_normal(e - s, dtype=np.float32)
         v *= np.float32(0.5)
         v -= np.float32(2.0)
         np.log1p(np.exp(v), out=v)
+        _store(out, s, e, v)
+
+    _for_blocks(n, fill)
     return out
 
 
-def _io(a: np.ndarray, io: str) -> np.ndarray:
-    return f32_to_bf16_bits(a) if io == BF16 else a
+def softplus_delta_f32(cfg_id: int, n: int, seed_base: int = ROOT_SEED) -> np.ndarray:
+    return softplus_delta(cfg_id, n, F32, seed_base)
 
 
 def s4d_real_A(dim: int, dstate: int) -> np.ndarray:
@@ -201,11 +240,11 @@ class ScanInputs:
 def make_scan_inputs(cfg: ScanConfig, seed_base: int = ROOT_SEED, with_h0: bool = False) -> ScanInputs:
     b, l, d, n = cfg.batch, cfg.seqlen, cfg.dim, cfg.dstate
     cid = cfg.cfg_id
-    x = _io(normal_f32(cid, T_X, b * l * d, seed_base), cfg.io).reshape(b, l, d)
-    delta = _io(softplus_delta_f32(cid, b * l * d, seed_base), cfg.io).reshape(b, l, d)
-    z = _io(normal_f32(cid, T_Z, b * l * d, seed_base), cfg.io).reshape(b, l, d) if cfg.has_z else None
-    Bm = _io(normal_f32(cid, T_B, b * l * n, seed_base), cfg.io).reshape(b, l, n)
-    Cm = _io(normal_f32(cid, T_C, b * l * n, seed_base), cfg.io).reshape(b, l, n)
+    x = normal(cid, T_X, b * l * d, cfg.io, seed_base).reshape(b, l, d)
+    delta = softplus_delta(cid, b * l * d, cfg.io, seed_base).reshape(b, l, d)
+    z = normal(cid, T_Z, b * l * d, cfg.io, seed_base).reshape(b, l, d) if cfg.has_z else None
+    Bm = normal(cid, T_B, b * l * n, cfg.io, seed_base).reshape(b, l, n)
+    Cm = normal(cid, T_C, b * l * n, cfg.io, seed_base).reshape(b, l, n)
     D = normal_f32(cid, T_D, d, seed_base) if cfg.has_D else None
     if cfg.a_kind == "s4d_real":
         A = s4d_real_A(d, n)
@@ -236,14 +275,14 @@ def make_ssd_inputs(cfg: SSDConfig, seed_base: int = ROOT_SEED, with_D: Optional
     cid = cfg.cfg_id
     with_D = cfg.has_D if with_D is None else with_D
     with_z = cfg.has_z if with_z is None else with_z
-    x = _io(normal_f32(cid, T_X, b * l * h * p, seed_base), cfg.io).reshape(b, l, h, p)
-    delta = _io(softplus_delta_f32(cid, b * l * h, seed_base), cfg.io).reshape(b, l, h)
-    Bm = _io(normal_f32(cid, T_B, b * l * g * n, seed_base), cfg.io).reshape(b, l, g, n)
-    Cm = _io(normal_f32(cid, T_C, b * l * g * n, seed_base), cfg.io).reshape(b, l, g, n)
+    x = normal(cid, T_X, b * l * h * p, cfg.io, seed_base).reshape(b, l, h, p)
+    delta = softplus_delta(cid, b * l * h, cfg.io, seed_base).reshape(b, l, h)
+    Bm = normal(cid, T_B, b * l * g * n, cfg.io, seed_base).reshape(b, l, g, n)
+    Cm = normal(cid, T_C, b * l * g * n, cfg.io, seed_base).reshape(b, l, g, n)
     u = uniform_f32(cid, T_A, h, float(np.log(np.float32(1.0))), float(np.log(np.float32(16.0))), seed_base)
     A = (-np.exp(u)).astype(np.float32)
     D = normal_f32(cid, T_D, h, seed_base) if with_D else None
-    z = _io(normal_f32(cid, T_Z, b * l * h * p, seed_base), cfg.io).reshape(b, l, h, p) if with_z else None
+    z = normal(cid, T_Z, b * l * h * p, cfg.io, seed_base).reshape(b, l, h, p) if with_z else None
     h0 = normal_f32(cid, T_H0, b * h * p * n, seed_base).reshape(b, h, p, n) if with_h0 else None
     return SSDInputs(x, delta, A, Bm, Cm, D, z, h0, cfg.io)
 

@@ -1,0 +1,264 @@
+"""Throughput of the selective-scan forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+
+A step is one full forward pass (the whole hot path) over one batch of the
+workload, with inputs already resident in HBM.  The default workload is the
+Mamba-1 130M-like layer (batch 8, L 2048, d_inner 1536, d_state 16, bf16 I/O,
+fp32 state).  Prints one JSON line on stdout; progress goes to stderr.
+
+Inputs rotate over several resident copies so that consecutive steps never
+read data the 256 MB memory-side cache still holds from the previous step.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0                      # MI355X HBM3E
+# VALU issue rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (packed fp32 is not used)
+PEAK_VALU_TSLOT = 256 * 4 * 16 * 2.4e9 / 1e12
+PEAK_BF16_MFMA_TFLOPS = 2500.0
+# algorithmic VALU issue slots: per state update mul + exp2 (half rate: 2 slots) + mul + FMA + FMA;
+# per (b, t, c): delta*x, D*x + y, and the silu gate (mul, exp2, add, rcp, 2 mul) = 10
+SLOTS_PER_UPDATE = 6.0
+SLOTS_PER_STEP_CHANNEL = 10.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "selective_state_space_17_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".cpp", ".h")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM bytes per launch from committed rocprofv3 counters, if taken on the current kernels."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    t = json.load(open(path))
+    if t.get("source_digest") != source_digest():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def dev(a):
+    import numpy as np
+    import torch
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(a).cuda()
+
+
+def cpu_baseline_scan(inp, cfg):
+    import oracle
+    threads = oracle.default_threads()
+    # bounded sample: whole batch and sequence, channels up to ~4e9 updates (10-30 s of oracle work)
+    per_ch = cfg.batch * cfg.seqlen * cfg.dstate
+    nc = int(min(cfg.dim, max(1, 4e9 // per_ch)))
+    t = time.perf_counter()
+    oracle.scan_fwd(inp.x, inp.delta, inp.A, inp.B, inp.C, inp.D, inp.z, None, c0=0, c1=nc, nthreads=threads)
+    dt = time.perf_counter() - t
+    return {"value": per_ch * nc / dt, "unit": "state-updates/s", "cores": threads, "kind": "oracle",
+            "sample": f"channels 0..{nc} of {cfg.dim}, all batches and steps ({per_ch * nc:.3e} updates, "
+                      f"{dt:.2f} s, fp64 sequential recurrence)"}
+
+
+def cpu_baseline_ssd(inp, cfg):
+    import oracle
+    threads = oracle.default_threads()
+    per_head = cfg.batch * cfg.seqlen * cfg.headdim * cfg.dstate
+    nh = int(min(cfg.nheads, max(1, 4e9 // per_head)))
+    t = time.perf_counter()
+    oracle.ssd_fwd(inp.x, inp.delta, inp.A, inp.B, inp.C, inp.D, inp.z, None, hd0=0, hd1=nh, nthreads=threads)
+    dt = time.perf_counter() - t
+    return {"value": per_head * nh / dt, "unit": "state-updates/s", "cores": threads, "kind": "oracle",
+            "sample": f"heads 0..{nh} of {cfg.nheads}, all batches and steps ({per_head * nh:.3e} updates, "
+                      f"{dt:.2f} s, fp64 sequential recurrence)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, help="workload id (1-5); 2 is the one the metric is quoted on")
+    ap.add_argument("--sets", type=int, default=0, help="resident input copies to rotate over (0: auto)")
+    ap.add_argument("--chunk", type=int, default=0, help="SSD time-chunk length (0: the workload's)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB 5 times (scales the HBM byte counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the path is not sharded across GPUs in this build", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {n} bytes 5 times (reads {n}, writes {n} per copy)")
+        return
+
+    import selective_state_space_17_amd as M
+    import workloads as W
+
+    cfg = W.CONFIGS[args.config]
+    is_ssd = isinstance(cfg, W.SSDConfig)
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    alg_bytes = cfg.algorithmic_bytes()
+    sets = args.sets or max(1, min(8, int(np.ceil(768e6 / alg_bytes))))
+    log(f"workload {cfg.name}: {cfg.updates:.3e} updates, {alg_bytes / 1e6:.1f} MB algorithmic, {sets} input set(s)")
+
+    t = time.perf_counter()
+    if is_ssd:
+        chunk = args.chunk or cfg.chunk
+        host = [W.make_ssd_inputs(cfg, seed_base=W.ROOT_SEED + 1000 * i) for i in range(sets)]
+        ins = [dict(x=dev(h.x), delta=dev(h.delta), A=dev(h.A), B=dev(h.B), C=dev(h.C), D=dev(h.D), z=dev(h.z))
+               for h in host]
+        outs = [(torch.empty_like(i["x"]),
+                 torch.empty((cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate), dtype=torch.float32, device="cuda"))
+                for i in ins]
+        ws_n = M.ssd_workspace_size(cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups, chunk)
+        ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+
+        def step(i):
+            a, (o, f) = ins[i % sets], outs[i % sets]
+            M.ssd_fwd(a["x"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], None, chunk=chunk,
+                      out=o, final_state=f, return_final_state=True, workspace=ws if ws_n else None)
+        plan = {"chunk": chunk}
+    else:
+        host = [W.make_scan_inputs(cfg, seed_base=W.ROOT_SEED + 1000 * i) for i in range(sets)]
+        ins = [dict(x=dev(h.x), delta=dev(h.delta), A=dev(h.A), B=dev(h.B), C=dev(h.C), D=dev(h.D), z=dev(h.z))
+               for h in host]
+        outs = [(torch.empty_like(i["x"]),
+                 torch.empty((cfg.batch, cfg.dim, cfg.dstate), dtype=torch.float32, device="cuda")
+                 if cfg.return_final else None) for i in ins]
+        io = M.MSSM_BF16 if cfg.io == W.BF16 else M.MSSM_F32
+        K, G = M.selective_scan_plan(cfg.batch, cfg.seqlen, cfg.dim, cfg.dstate, io)
+        ws_n = M.selective_scan_workspace_size(cfg.batch, cfg.seqlen, cfg.dim, cfg.dstate, io)
+        ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+
+        def step(i):
+            a, (o, f) = ins[i % sets], outs[i % sets]
+            M.selective_scan_fwd(a["x"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], None,
+                                 out=o, final_state=f, return_final_state=f is not None,
+                                 workspace=ws if ws_n else None)
+        plan = {"split_seq": K, "split_state": G}
+    del host[1:]
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.perf_counter() - t:.1f}s; plan {plan}")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done")
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(args.warmup + i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = [a.elapsed_time(b) for a, b in ev]
+    ms = float(np.mean(step_ms))
+    log(f"timed {args.steps} steps: wall {wall * 1e3 / args.steps:.3f} ms/step, events mean {ms:.3f} "
+        f"median {float(np.median(step_ms)):.3f} min {min(step_ms):.3f} ms")
+
+    upd_s = cfg.updates / (wall / args.steps)
+    kern_s = ms * 1e-3
+    hbm = {"achieved": alg_bytes / kern_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+           "frac": alg_bytes / kern_s / 1e9 / PEAK_HBM_GBS}
+    traffic = load_traffic(cfg.name)
+    if is_ssd:
+        Q = plan["chunk"]
+        # matrix-core work of the chunked form per launch: causal intra-chunk Q*Q*P/2,
+        # chunk-state readout and update 2*N*P per step and head, C.B^T Q*N per step and group
+        macs = cfg.batch * cfg.seqlen * (cfg.nheads * (Q * cfg.headdim / 2 + 2 * cfg.dstate * cfg.headdim)
+                                         + cfg.ngroups * Q * cfg.dstate)
+        mf = {"achieved": 2 * macs / kern_s / 1e12, "peak": PEAK_BF16_MFMA_TFLOPS, "unit": "TFLOP/s"}
+        mf["frac"] = mf["achieved"] / mf["peak"]
+        bound = "hbm" if hbm["frac"] >= mf["frac"] else "mfma"
+        roof = dict(hbm if bound == "hbm" else mf)
+        roof["bound"] = bound
+        roof["other"] = mf if bound == "hbm" else hbm
+    else:
+        slots = cfg.updates * SLOTS_PER_UPDATE + cfg.batch * cfg.seqlen * cfg.dim * SLOTS_PER_STEP_CHANNEL
+        alu = {"achieved": slots / kern_s / 1e12, "peak": PEAK_VALU_TSLOT, "unit": "Tslot/s"}
+        alu["frac"] = alu["achieved"] / alu["peak"]
+        bound = "alu" if alu["frac"] >= hbm["frac"] else "hbm"
+        roof = dict(alu if bound == "alu" else hbm)
+        roof["bound"] = bound
+        roof["other"] = hbm if bound == "alu" else alu
+    roof["traffic"] = traffic
+    roof = {k: roof[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic", "other")}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        h = host[0]
+        cpu = cpu_baseline_ssd(h, cfg) if is_ssd else cpu_baseline_scan(h, cfg)
+        log(f"cpu baseline: {cpu}")
+
+    conf = {"workload": cfg.name, "batch": cfg.batch, "seqlen": cfg.seqlen}
+    if is_ssd:
+        conf.update(nheads=cfg.nheads, headdim=cfg.headdim, d_state=cfg.dstate, ngroups=cfg.ngroups,
+                    chunk=plan["chunk"], io="bf16")
+    else:
+        conf.update(d_inner=cfg.dim, d_state=cfg.dstate, io=cfg.io, D=cfg.has_D, z_gate=cfg.has_z,
+                    final_state=cfg.return_final, **plan)
+    conf["input_sets"] = sets
+    line = {
+        "metric": "selective-scan state updates/s (B*L*d_inner*N), 1 GPU",
+        "value": upd_s,
+        "unit": "state-updates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": conf,
+        "hbm_gbs": alg_bytes / (wall / args.steps) / 1e9,
+        "kernel_ms": ms,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -59,8 +59,8 @@ int ilog2(int v) {
 // Estimated kernel time in VALU issue slots per lane (smaller is better).
 double scan_cost(const mssm_scan_desc& d, int G, int K) {
   const int npl = states_per_lane(G, d.dstate);
-  const int64_t cpw = 64 / G;
-  const int64_t groups = d.batch * ((d.dim + cpw - 1) / cpw);
+  const int64_t cpb = 256 / G;                               // channels per 4-wave block
+  const int64_t groups = d.batch * ((d.dim + cpb - 1) / cpb) * 4;   // waves per chunk
   const double slots_step = npl * 6.0 + ilog2(G) + 14.0;   // 6 slots per state update + per-step epilogue
   const int64_t chunk = (d.seqlen + K - 1) / K;
   // pass 2 rescans until the carried-in state has decayed (about 800 steps for
@@ -109,8 +109,8 @@ int plan_scan(const mssm_scan_desc& d, int* K_out, int* G_out) {
   }
   if (bestG == 0) return MSSM_ERR_UNSUPPORTED;
   // the grid is 1-D: batch * K * channel-groups blocks
-  const int64_t cpw = 64 / bestG;
-  const int64_t blocks = d.batch * bestK * ((d.dim + cpw - 1) / cpw);
+  const int64_t cpb = 256 / bestG;
+  const int64_t blocks = d.batch * bestK * ((d.dim + cpb - 1) / cpb);
   if (blocks > std::numeric_limits<int32_t>::max()) return MSSM_ERR_UNSUPPORTED;
   *K_out = bestK;
   *G_out = bestG;

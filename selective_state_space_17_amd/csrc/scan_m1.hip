@@ -8,18 +8,26 @@
 // the exponential is elementwise), "Parallel scan" (the recurrence is
 // associative, which is what lets the sequence be split below).
 //
-// Mapping onto the chip.  One wave (64 lanes) owns CPW = 64/G channels of
-// one batch row and one time chunk; G lanes share a channel, each holding
-// NPL of its states in fp32 VGPRs.  Per time tile of T steps the wave
-// prefetches x/delta/z (and B/C, shared by all channels) with 16-byte
-// global loads one tile ahead, stages them in its own LDS, then walks the
-// tile step by step: per state one multiply for the exponent, one exp2
-// (A is pre-scaled by log2 e), one multiply for delta*x*B, one FMA for the
-// recurrence and one FMA for the readout.  The G partial readouts are summed
-// with DPP row operations; outputs are staged in LDS and written back with
-// 16-byte stores.  The kernels are VALU/transcendental bound (exp2 issues at
-// half rate on gfx950), so everything else is kept off the VALU where it can
-// be: B and C come from LDS as broadcast reads, the reduction rides on DPP.
+// Mapping onto the chip.  A block of 4 waves owns CPB = 256/G channels of one
+// batch row and one time chunk; G lanes share a channel, each holding NPL of
+// its states in fp32 VGPRs.  The path is VALU/transcendental bound (exp2
+// issues at half rate on gfx950), so per state update the lane issues only
+// the five unavoidable operations: a multiply for the exponent (A is
+// pre-scaled by log2 e), exp2, a multiply for delta*x*B, an FMA for the
+// recurrence and an FMA for the readout.  Everything per (t, c) -- bf16
+// widening, delta*x, the silu gate, D*x -- is computed once per element when a
+// time tile is staged (global -> registers one tile ahead with 16-byte loads,
+// then into fp32 LDS arrays), not once per lane; outputs are collected in LDS
+// and written back with 16-byte stores.
+//
+// B and C (shared by all channels of a batch row) reach the lanes in two ways:
+//  - dstate <= 16 ("fast" path): one VGPR per step holds the 16 values across
+//    each 16-lane row and every state reads its value through a DPP operand
+//    (row_newbcast for one lane per channel, quad_perm broadcasts for 2 or 4
+//    lanes per channel; the lane layout puts a state group on one quad), so
+//    B rides on v_mul_f32_dpp and C on v_fmac_f32_dpp at no extra cost;
+//  - larger dstate ("generic" path): per-lane 16-byte LDS reads.
+// The G partial readouts are summed with DPP row rotations/permutations.
 //
 // Sequence split (K > 1 chunks), exact up to fp32 rounding:
 //   pass 1  every chunk scans from a zero state (chunk 0 from h0), writes its
@@ -41,6 +49,10 @@ namespace {
 
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr int kWave = 64;
+constexpr int kWaves = 4;      // waves per block
+constexpr int kThreads = kWave * kWaves;
+
+using u32x4 = unsigned int __attribute__((ext_vector_type(4)));   // native 128-bit register tuple
 
 template <int IO> struct IoType;
 template <> struct IoType<0> { using T = float; };
@@ -59,37 +71,44 @@ template <int CTRL> __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
 }
 
-// Sum over each group of G consecutive lanes; every lane of the group gets the total.
-template <int G> __device__ __forceinline__ float group_sum(float v) {
-  if constexpr (G >= 2) v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
-  if constexpr (G >= 4) v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
-  if constexpr (G >= 8) v += dpp<0x141>(v);   // row_half_mirror
-  if constexpr (G >= 16) v += dpp<0x140>(v);  // row_mirror
-  return v;
-}
-
 __device__ __forceinline__ float exp2_hw(float v) { return __builtin_amdgcn_exp2f(v); }
+
+__device__ __forceinline__ float silu_gate(float z) {
+  return z * __builtin_amdgcn_rcpf(1.f + exp2_hw(-z * kLog2e));
+}
 
 // modes
 constexpr int kSingle = 0;   // whole sequence in one chunk: h0 -> final_state
 constexpr int kChunk = 1;    // pass 1 of a split sequence
 constexpr int kFixup = 2;    // pass 2 of a split sequence
 
-template <int IO, int G, int NPL, bool VEC>
+// DPP controls
+constexpr int kRowRor8 = 0x128;
+constexpr int kRowRor4 = 0x124;
+constexpr int kQuadSwap1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+constexpr int quad_bcast(int j) { return j | (j << 2) | (j << 4) | (j << 6); }   // quad_perm [j,j,j,j]
+constexpr int row_newbcast(int j) { return 0x150 + j; }
+
+template <int IO, int G, int NPL, bool VEC, bool FAST>
 struct Geometry {
   using T = typename IoType<IO>::T;
   static constexpr int ES = sizeof(T);
   static constexpr int CPW = kWave / G;                          // channels per wave
-  static constexpr int NP = G * NPL;                             // padded state count
-  static constexpr int RB = CPW * ES;                            // bytes per tile row (one step)
-  static constexpr int LPR = VEC ? (RB / 16 > 0 ? RB / 16 : 1) : 1;  // lanes per row for 16-byte loads
-  static constexpr int RPI = VEC ? kWave / LPR : 1;              // rows per load instruction
-  static constexpr int TG = G == 1 ? 16 : (G == 2 ? 32 : 64);
-  static constexpr int TCAP = 4096 / NP < 8 ? 8 : 4096 / NP;     // keeps the fp32 B/C tiles <= 16 KB each
-  static constexpr int STEPS = TG < TCAP ? TG : TCAP;            // steps per tile
-  static constexpr bool VEC_OK = RB % 16 == 0 && kWave % LPR == 0 && STEPS % RPI == 0;
-  static constexpr int NIT = VEC ? STEPS / RPI : (STEPS * CPW + kWave - 1) / kWave;  // x/delta/z loads per lane
+  static constexpr int CPB = kWaves * CPW;                       // channels per block
+  static constexpr int NP = FAST ? 16 : G * NPL;                 // padded state count
+  static constexpr int RB = CPB * ES;                            // bytes per tile row (one step)
+  static constexpr int LPR = VEC ? (RB / 16 > 0 ? RB / 16 : 1) : 1;  // threads per row for 16-byte loads
+  static constexpr int RPI = VEC ? (kThreads / LPR > 0 ? kThreads / LPR : 1) : 1;  // rows per load instruction
+  static constexpr int TWANT = 4096 / CPB < 32 ? 4096 / CPB : 32;  // <= 32 unrolled steps, operand tiles <= 64 KB
+  static constexpr int TCAP = 4096 / NP < 8 ? 8 : 4096 / NP;    // B/C tiles stay <= 16 KB each
+  static constexpr int STEPS = TWANT < TCAP ? TWANT : TCAP;      // steps per tile
+  static constexpr bool VEC_OK = RB % 16 == 0 && kThreads % LPR == 0 && STEPS % RPI == 0;
+  static constexpr int NIT = VEC ? STEPS / RPI : (STEPS * CPB + kThreads - 1) / kThreads;  // loads per thread
   static constexpr int EPC = 16 / ES;                            // elements per 16-byte chunk
+  static constexpr int EPT = VEC ? EPC : 1;                      // channels a staging thread holds
 };
 
 struct KernelParams {
@@ -110,32 +129,139 @@ struct KernelParams {
   int64_t batch, L, dim, N;
   int64_t chunk_len;
   int K;
-  int ngroups;          // channel groups (waves) per (batch, chunk)
+  int ngroups;          // channel groups (blocks) per (batch, chunk)
   int chunk_offset;     // fix-up pass starts at chunk 1
+  int bc_shift;         // log2(N / elements-per-16-bytes) for 16-byte B/C loads
 };
 
-template <int IO, int G, int NPL, bool VEC, int MODE>
-__global__ __launch_bounds__(kWave) void scan_kernel(KernelParams p) {
-  using Geo = Geometry<IO, G, NPL, VEC>;
+// Readout for the fast path: a0 + a1 = sum_j C_j * h_j with C_j taken from the
+// lane holding it through a DPP operand (v_mul/v_fmac_f32_dpp); two partial
+// sums keep the dependent chain short.  s_nop 1 covers the VALU-write ->
+// DPP-read hazard on the C register.
+template <int G> struct FastReadout;
+
+template <> struct FastReadout<1> {   // one VGPR, C[n] in lane n of each row: row_newbcast:n
+  static __device__ __forceinline__ void run(float& a0, float& a1, float c, const float (&h)[16]) {
+    asm("s_nop 1\n\t"
+        "v_mul_f32_dpp %0, %2, %3 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %1, %2, %4 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %2, %5 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %2, %6 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %2, %7 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %2, %8 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %2, %9 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %2, %10 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %2, %11 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %2, %12 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %2, %13 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %2, %14 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %2, %15 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %2, %16 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %2, %17 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %2, %18 row_newbcast:15 row_mask:0xf bank_mask:0xf"
+        : "=&v"(a0), "=&v"(a1)
+        : "v"(c), "v"(h[0]), "v"(h[1]), "v"(h[2]), "v"(h[3]), "v"(h[4]), "v"(h[5]), "v"(h[6]), "v"(h[7]),
+          "v"(h[8]), "v"(h[9]), "v"(h[10]), "v"(h[11]), "v"(h[12]), "v"(h[13]), "v"(h[14]), "v"(h[15]));
+  }
+};
+
+template <> struct FastReadout<2> {   // two VGPRs, quad position p holds C[8g + 4v + p]: quad_perm [p,p,p,p]
+  static __device__ __forceinline__ void run(float& a0, float& a1, float c0, float c1, const float (&h)[8]) {
+    asm("s_nop 1\n\t"
+        "v_mul_f32_dpp %0, %2, %4 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %1, %2, %5 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %2, %6 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %2, %7 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %3, %8 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %3, %9 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %3, %10 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %3, %11 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf"
+        : "=&v"(a0), "=&v"(a1)
+        : "v"(c0), "v"(c1), "v"(h[0]), "v"(h[1]), "v"(h[2]), "v"(h[3]), "v"(h[4]), "v"(h[5]), "v"(h[6]),
+          "v"(h[7]));
+  }
+};
+
+template <> struct FastReadout<4> {   // one VGPR, quad position p holds C[4g + p]
+  static __device__ __forceinline__ void run(float& a0, float& a1, float c, const float (&h)[4]) {
+    asm("s_nop 1\n\t"
+        "v_mul_f32_dpp %0, %2, %3 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %1, %2, %4 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %2, %5 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %2, %6 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf"
+        : "=&v"(a0), "=&v"(a1)
+        : "v"(c), "v"(h[0]), "v"(h[1]), "v"(h[2]), "v"(h[3]));
+  }
+};
+
+// B_j for state j of the lane's state group, through a DPP operand
+template <int G, int J> __device__ __forceinline__ float fast_b(float b0, float b1) {
+  if constexpr (G == 1) return dpp<row_newbcast(J)>(b0);
+  else if constexpr (G == 2) return J < 4 ? dpp<quad_bcast(J & 3)>(b0) : dpp<quad_bcast(J & 3)>(b1);
+  else return dpp<quad_bcast(J)>(b0);
+}
+
+template <int G, int J, int NPL>
+__device__ __forceinline__ void fast_updates(float (&h)[NPL], const float (&A2)[NPL], float d, float du, float b0,
+                                             float b1) {
+  const float dA = exp2_hw(d * A2[J]);
+  h[J] = __builtin_fmaf(dA, h[J], du * fast_b<G, J>(b0, b1));
+  if constexpr (J + 1 < NPL) fast_updates<G, J + 1, NPL>(h, A2, d, du, b0, b1);
+}
+
+// Sum of the G partial readouts of a channel (every lane of the group gets it).
+template <int G, bool FAST> __device__ __forceinline__ float reduce_groups(float v) {
+  if constexpr (FAST) {
+    // state groups sit on different quads (G=4) or quad pairs (G=2) of a row
+    if constexpr (G >= 2) v += dpp<kRowRor8>(v);
+    if constexpr (G >= 4) v += dpp<kRowRor4>(v);
+  } else {
+    // generic layout: the G lanes of a channel are consecutive
+    if constexpr (G >= 2) v += dpp<kQuadSwap1>(v);
+    if constexpr (G >= 4) v += dpp<kQuadSwap2>(v);
+    if constexpr (G >= 8) v += dpp<kRowHalfMirror>(v);
+    if constexpr (G >= 16) v += dpp<kRowMirror>(v);
+  }
+  return v;
+}
+
+template <int IO, int G, int NPL, bool VEC, bool FAST, int MODE>
+__global__ __launch_bounds__(kThreads) void scan_kernel(KernelParams p) {
+  using Geo = Geometry<IO, G, NPL, VEC, FAST>;
   static_assert(!VEC || Geo::VEC_OK, "tile geometry");
+  static_assert(!FAST || (G * NPL == 16 && (G == 1 || G == 2 || G == 4)), "fast path layout");
   using T = typename Geo::T;
-  constexpr int CPW = Geo::CPW, NP = Geo::NP, TT = Geo::STEPS, NIT = Geo::NIT;
-  constexpr int EPC = Geo::EPC;
-  // B/C tile: TT*N contiguous elements; 16-byte chunks when vectorised
-  constexpr int BC_MAX_ELEMS = TT * NP;
-  constexpr int NITB = VEC ? (BC_MAX_ELEMS * (int)sizeof(T) + 16 * kWave - 1) / (16 * kWave)
-                           : (BC_MAX_ELEMS + kWave - 1) / kWave;
+  constexpr int CPW = Geo::CPW, CPB = Geo::CPB, NP = Geo::NP, TT = Geo::STEPS, NIT = Geo::NIT;
+  constexpr int EPC = Geo::EPC, EPT = Geo::EPT;
+  constexpr int NITB = VEC ? (TT * NP * static_cast<int>(sizeof(T)) + 16 * kThreads - 1) / (16 * kThreads)
+                           : (TT * NP + kThreads - 1) / kThreads;
 
-  __shared__ __attribute__((aligned(16))) T xs[TT * CPW];
-  __shared__ __attribute__((aligned(16))) T ds[TT * CPW];
-  __shared__ __attribute__((aligned(16))) T zs[TT * CPW];
-  __shared__ __attribute__((aligned(16))) T ys[TT * CPW];
-  __shared__ __attribute__((aligned(16))) float Bs[TT * NP];
-  __shared__ __attribute__((aligned(16))) float Cs[TT * NP];
+  // per-(t, c) operands, fp32, with one spare row so a step can always read one ahead
+  __shared__ __attribute__((aligned(16))) float Dl[(TT + 1) * CPB];   // delta
+  __shared__ __attribute__((aligned(16))) float Ul[(TT + 1) * CPB];   // delta * x
+  __shared__ __attribute__((aligned(16))) float Gl[(TT + 1) * CPB];   // silu(z) (1 without z)
+  __shared__ __attribute__((aligned(16))) float Yl[(TT + 1) * CPB];   // silu(z) * D * x
+  __shared__ __attribute__((aligned(16))) T ys[TT * CPB];            // outputs of the previous tile
+  __shared__ __attribute__((aligned(16))) float Bs[(TT + 1) * NP];
+  __shared__ __attribute__((aligned(16))) float Cs[(TT + 1) * NP];
 
-  const int lane = threadIdx.x;
-  const int ch = lane / G;
-  const int g = lane % G;
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = tid / kWave;
+  // lane -> (channel within the wave, state group)
+  int chw, g;
+  if constexpr (FAST && G == 2) {
+    const int r = lane >> 4, q = (lane >> 2) & 3, pp = lane & 3;
+    g = q >> 1;
+    chw = 8 * r + 4 * (q & 1) + pp;
+  } else if constexpr (FAST && G == 4) {
+    g = (lane >> 2) & 3;
+    chw = 4 * (lane >> 4) + (lane & 3);
+  } else {
+    chw = lane / G;
+    g = lane % G;
+  }
+  const int chb = wave * CPW + chw;   // channel within the block
 
   // block -> (batch, chunk, channel group)
   int bid = blockIdx.x;
@@ -146,21 +272,23 @@ __global__ __launch_bounds__(kWave) void scan_kernel(KernelParams p) {
   const int64_t b = bid / nchunks_here;
 
   const int64_t dim = p.dim, N = p.N, L = p.L;
-  const int64_t c0 = static_cast<int64_t>(cg) * CPW;
-  const int64_t c = c0 + ch;
+  const int64_t c0 = static_cast<int64_t>(cg) * CPB;
+  const int64_t c = c0 + chb;
   const bool cvalid = c < dim;
   const int64_t t_begin = static_cast<int64_t>(k) * p.chunk_len;
   const int64_t t_end = t_begin + p.chunk_len < L ? t_begin + p.chunk_len : L;
 
   const T* __restrict__ xg = static_cast<const T*>(p.x);
   const T* __restrict__ dg = static_cast<const T*>(p.delta);
-  const T* __restrict__ zg = static_cast<const T*>(p.z);
+  // without z the z loads read x (values unused) so the load stream has no branches
+  const T* __restrict__ zg = static_cast<const T*>(p.z != nullptr ? p.z : p.x);
   const T* __restrict__ Bg = static_cast<const T*>(p.B);
   const T* __restrict__ Cg = static_cast<const T*>(p.C);
   T* __restrict__ yg = static_cast<T*>(p.out);
   const bool has_z = p.z != nullptr;
+  const int Ni = static_cast<int>(N);
 
-  // per-lane constants and state
+  // states of this lane: n = g*NPL + j
   float A2[NPL], h[NPL];
   float amax = -INFINITY;     // largest (least negative) exponent slope among real states
   float hmax = 0.f;           // largest |h_in| among real states (fix-up)
@@ -181,9 +309,7 @@ __global__ __launch_bounds__(kWave) void scan_kernel(KernelParams p) {
       hmax = fmaxf(hmax, fabsf(h_init));
     }
   }
-  const float Dc = (p.D != nullptr && cvalid) ? p.D[c] : 0.f;
 
-  bool fix_done = false;
   bool never_exit = false;
   if constexpr (MODE == kFixup) {
     // a channel whose chunk saw a negative delta cannot use the decay bound
@@ -192,110 +318,146 @@ __global__ __launch_bounds__(kWave) void scan_kernel(KernelParams p) {
   float S = 0.f;       // running sum of delta over this chunk
   int negseen = 0;
 
-  // zero the padded B/C columns once (never overwritten by loads)
-  if (NP > N) {
-    for (int e = lane; e < TT * NP; e += kWave) {
-      if ((e % NP) >= N) { Bs[e] = 0.f; Cs[e] = 0.f; }
+  // staging threads: the channels they widen are fixed for the whole kernel
+  const int rin = VEC ? tid / Geo::LPR : 0;
+  const int seg = VEC ? tid % Geo::LPR : 0;
+  const int scol = VEC ? seg * EPC : tid % CPB;    // first channel (within block) of this thread
+  float Dreg[EPT];
+#pragma unroll
+  for (int q = 0; q < EPT; ++q) {
+    const int64_t cc = c0 + scol + q;
+    Dreg[q] = (p.D != nullptr && cc < dim) ? p.D[cc] : 0.f;
+  }
+
+  // zero the padded B/C columns and the spare rows once (loads never write them)
+  for (int e = tid; e < (TT + 1) * NP; e += kThreads) {
+    if ((e % NP) >= Ni || e >= TT * NP) {
+      Bs[e] = 0.f;
+      Cs[e] = 0.f;
     }
+  }
+  for (int e = tid; e < CPB; e += kThreads) {
+    Dl[TT * CPB + e] = 0.f;
+    Ul[TT * CPB + e] = 0.f;
+    Gl[TT * CPB + e] = 0.f;
+    Yl[TT * CPB + e] = 0.f;
   }
 
   // ------------------------------------------------------------------
-  // prefetch registers
+  // tile prefetch registers, filled one (long) tile ahead of use
   // ------------------------------------------------------------------
-  using Chunk = typename std::conditional<VEC, uint4, T>::type;
+  using Chunk = typename std::conditional<VEC, u32x4, T>::type;
   Chunk xr[NIT], dr[NIT], zr[NIT];
   Chunk br[NITB], cr[NITB];
 
+  // Loads are unconditional: out-of-range rows/channels/chunks are clamped to
+  // in-range addresses; their values land in LDS rows or channels that are
+  // never used.
   auto issue_loads = [&](int64_t t0) {
-    const int64_t nvalid = (t_end - t0) < TT ? (t_end - t0) : TT;
+    const int nvalid = static_cast<int>((t_end - t0) < TT ? (t_end - t0) : TT);
     if constexpr (VEC) {
-      const int rin = lane / Geo::LPR, seg = lane % Geo::LPR;
-      const int64_t cc = c0 + static_cast<int64_t>(seg) * EPC;
+      const int64_t cc = (c0 + scol) < dim ? (c0 + scol) : (dim - EPC);
 #pragma unroll
       for (int i = 0; i < NIT; ++i) {
         const int r = i * Geo::RPI + rin;
-        const bool ok = r < nvalid && cc < dim;
-        const int64_t off = ((b * L + t0 + r) * dim + cc);
-        xr[i] = ok ? *reinterpret_cast<const uint4*>(xg + off) : uint4{0, 0, 0, 0};
-        dr[i] = ok ? *reinterpret_cast<const uint4*>(dg + off) : uint4{0, 0, 0, 0};
-        if (has_z) zr[i] = ok ? *reinterpret_cast<const uint4*>(zg + off) : uint4{0, 0, 0, 0};
+        const int rr = r < nvalid ? r : nvalid - 1;
+        const int64_t off = (b * L + t0 + rr) * dim + cc;
+        xr[i] = *reinterpret_cast<const u32x4*>(xg + off);
+        dr[i] = *reinterpret_cast<const u32x4*>(dg + off);
+        zr[i] = *reinterpret_cast<const u32x4*>(zg + off);
       }
-      const int64_t nbc = nvalid * N;    // valid elements of the flattened [steps x N] B/C tile
+      // the [steps x N] B/C tile is contiguous in memory: 16-byte chunks
+      const int nchunks = (nvalid * Ni) / EPC;
       const int64_t base = (b * L + t0) * N;
 #pragma unroll
       for (int i = 0; i < NITB; ++i) {
-        const int64_t e = (static_cast<int64_t>(i) * kWave + lane) * EPC;
-        const bool ok = e < nbc;
-        br[i] = ok ? *reinterpret_cast<const uint4*>(Bg + base + e) : uint4{0, 0, 0, 0};
-        cr[i] = ok ? *reinterpret_cast<const uint4*>(Cg + base + e) : uint4{0, 0, 0, 0};
+        const int ci = i * kThreads + tid;
+        const int cci = ci < nchunks ? ci : nchunks - 1;
+        br[i] = *reinterpret_cast<const u32x4*>(Bg + base + static_cast<int64_t>(cci) * EPC);
+        cr[i] = *reinterpret_cast<const u32x4*>(Cg + base + static_cast<int64_t>(cci) * EPC);
       }
     } else {
+      const int64_t cc = (c0 + scol) < dim ? (c0 + scol) : (dim - 1);
 #pragma unroll
       for (int i = 0; i < NIT; ++i) {
-        const int e = i * kWave + lane;
-        const int r = e / CPW, col = e % CPW;
-        const bool ok = e < TT * CPW && r < nvalid && c0 + col < dim;
-        const int64_t off = (b * L + t0 + r) * dim + c0 + col;
-        xr[i] = ok ? xg[off] : T(0);
-        dr[i] = ok ? dg[off] : T(0);
-        if (has_z) zr[i] = ok ? zg[off] : T(0);
+        const int e = i * kThreads + tid;
+        const int r = e / CPB;
+        const int rr = r < nvalid ? r : nvalid - 1;
+        const int64_t off = (b * L + t0 + rr) * dim + cc;
+        xr[i] = xg[off];
+        dr[i] = dg[off];
+        zr[i] = zg[off];
       }
-      const int64_t nbc = nvalid * N;
+      const int nbc = nvalid * Ni;
       const int64_t base = (b * L + t0) * N;
 #pragma unroll
       for (int i = 0; i < NITB; ++i) {
-        const int64_t e = static_cast<int64_t>(i) * kWave + lane;
-        const bool ok = e < nbc;
-        br[i] = ok ? Bg[base + e] : T(0);
-        cr[i] = ok ? Cg[base + e] : T(0);
+        const int e = i * kThreads + tid;
+        const int ee = e < nbc ? e : nbc - 1;
+        br[i] = Bg[base + ee];
+        cr[i] = Cg[base + ee];
       }
     }
   };
 
+  // widen one element and compute its per-(t, c) operands
+  auto stage_one = [&](int idx, T xv, T dv, T zv, float Dv) {
+    const float d = to_f32(dv), u = to_f32(xv);
+    const float gz = has_z ? silu_gate(to_f32(zv)) : 1.f;
+    Dl[idx] = d;
+    Ul[idx] = d * u;
+    Gl[idx] = gz;
+    Yl[idx] = gz * (Dv * u);
+  };
+
   auto stage_to_lds = [&](int64_t t0) {
-    const int64_t nvalid = (t_end - t0) < TT ? (t_end - t0) : TT;
+    const int nvalid = static_cast<int>((t_end - t0) < TT ? (t_end - t0) : TT);
+    // Register fences: the prefetched values become usable only here, so the
+    // compiler cannot start consuming them (and wait for them) right after the
+    // loads are issued, a tile early.
+#pragma unroll
+    for (int i = 0; i < NIT; ++i) asm volatile("" : "+v"(xr[i]), "+v"(dr[i]), "+v"(zr[i]));
+#pragma unroll
+    for (int i = 0; i < NITB; ++i) asm volatile("" : "+v"(br[i]), "+v"(cr[i]));
     if constexpr (VEC) {
-      const int rin = lane / Geo::LPR, seg = lane % Geo::LPR;
 #pragma unroll
       for (int i = 0; i < NIT; ++i) {
-        const int r = i * Geo::RPI + rin;
-        const int idx = r * CPW + seg * EPC;
-        *reinterpret_cast<uint4*>(&xs[idx]) = xr[i];
-        *reinterpret_cast<uint4*>(&ds[idx]) = dr[i];
-        if (has_z) *reinterpret_cast<uint4*>(&zs[idx]) = zr[i];
+        const int idx = (i * Geo::RPI + rin) * CPB + scol;
+        const T* xv = reinterpret_cast<const T*>(&xr[i]);
+        const T* dv = reinterpret_cast<const T*>(&dr[i]);
+        const T* zv = reinterpret_cast<const T*>(&zr[i]);
+#pragma unroll
+        for (int q = 0; q < EPC; ++q) stage_one(idx + q, xv[q], dv[q], has_z ? zv[q] : T(0), Dreg[q]);
       }
-      const int64_t nbc = nvalid * N;
+      const int nchunks = (nvalid * Ni) / EPC;
+      const int cmask = (1 << p.bc_shift) - 1;
 #pragma unroll
       for (int i = 0; i < NITB; ++i) {
-        const int64_t e = (static_cast<int64_t>(i) * kWave + lane) * EPC;
-        if (e < nbc) {
+        const int ci = i * kThreads + tid;
+        if (ci < nchunks) {
+          const int r = ci >> p.bc_shift;           // a chunk never straddles two steps
+          const int n0 = (ci & cmask) * EPC;
           const T* bv = reinterpret_cast<const T*>(&br[i]);
           const T* cv = reinterpret_cast<const T*>(&cr[i]);
 #pragma unroll
           for (int q = 0; q < EPC; ++q) {
-            const int64_t ee = e + q;
-            const int r = static_cast<int>(ee / N), n = static_cast<int>(ee % N);
-            Bs[r * NP + n] = to_f32(bv[q]);
-            Cs[r * NP + n] = to_f32(cv[q]);
+            Bs[r * NP + n0 + q] = to_f32(bv[q]);
+            Cs[r * NP + n0 + q] = to_f32(cv[q]);
           }
         }
       }
     } else {
 #pragma unroll
       for (int i = 0; i < NIT; ++i) {
-        const int e = i * kWave + lane;
-        if (e < TT * CPW) {
-          xs[e] = xr[i];
-          ds[e] = dr[i];
-          if (has_z) zs[e] = zr[i];
-        }
+        const int e = i * kThreads + tid;
+        if (e < TT * CPB) stage_one(e, xr[i], dr[i], has_z ? zr[i] : T(0), Dreg[0]);
       }
-      const int64_t nbc = nvalid * N;
+      const int nbc = nvalid * Ni;
 #pragma unroll
       for (int i = 0; i < NITB; ++i) {
-        const int64_t e = static_cast<int64_t>(i) * kWave + lane;
+        const int e = i * kThreads + tid;
         if (e < nbc) {
-          const int r = static_cast<int>(e / N), n = static_cast<int>(e % N);
+          const int r = e / Ni, n = e - r * Ni;
           Bs[r * NP + n] = to_f32(br[i]);
           Cs[r * NP + n] = to_f32(cr[i]);
         }
@@ -304,72 +466,137 @@ __global__ __launch_bounds__(kWave) void scan_kernel(KernelParams p) {
   };
 
   auto store_tile = [&](int64_t t0) {
-    const int64_t nvalid = (t_end - t0) < TT ? (t_end - t0) : TT;
+    const int nvalid = static_cast<int>((t_end - t0) < TT ? (t_end - t0) : TT);
     if constexpr (VEC) {
-      const int rin = lane / Geo::LPR, seg = lane % Geo::LPR;
-      const int64_t cc = c0 + static_cast<int64_t>(seg) * EPC;
+      const int64_t cc = c0 + scol;
 #pragma unroll
       for (int i = 0; i < NIT; ++i) {
         const int r = i * Geo::RPI + rin;
         if (r < nvalid && cc < dim) {
-          const uint4 v = *reinterpret_cast<const uint4*>(&ys[r * CPW + seg * EPC]);
+          const uint4 v = *reinterpret_cast<const uint4*>(&ys[r * CPB + scol]);
           *reinterpret_cast<uint4*>(yg + (b * L + t0 + r) * dim + cc) = v;
         }
       }
     } else {
 #pragma unroll
       for (int i = 0; i < NIT; ++i) {
-        const int e = i * kWave + lane;
-        const int r = e / CPW, col = e % CPW;
-        if (e < TT * CPW && r < nvalid && c0 + col < dim) yg[(b * L + t0 + r) * dim + c0 + col] = ys[e];
+        const int e = i * kThreads + tid;
+        const int r = e / CPB;
+        if (e < TT * CPB && r < nvalid && c0 + scol < dim) yg[(b * L + t0 + r) * dim + c0 + scol] = ys[e];
       }
     }
   };
 
   // ------------------------------------------------------------------
-  // time loop
+  // per-step work
+  // ------------------------------------------------------------------
+  struct Ops {
+    float d, du, gz, yd;
+    float b0, b1, c0, c1;           // fast path: B/C registers
+    float4 bq[FAST ? 1 : NPL / 4];  // generic path: this lane's B/C values
+    float4 cq[FAST ? 1 : NPL / 4];
+  };
+  // where this lane reads its B/C register(s) in a Bs row (fast path)
+  int boff0 = 0, boff1 = 0;
+  if constexpr (FAST) {
+    if constexpr (G == 1) {
+      boff0 = lane & 15;
+    } else if constexpr (G == 2) {
+      boff0 = 8 * g + (lane & 3);
+      boff1 = boff0 + 4;
+    } else {
+      boff0 = 4 * g + (lane & 3);
+    }
+  }
+
+  auto load_step = [&](int s, Ops& v) {
+    v.d = Dl[s * CPB + chb];
+    v.du = Ul[s * CPB + chb];
+    v.gz = Gl[s * CPB + chb];
+    v.yd = Yl[s * CPB + chb];
+    if constexpr (FAST) {
+      v.b0 = Bs[s * NP + boff0];
+      v.c0 = Cs[s * NP + boff0];
+      if constexpr (G == 2) {
+        v.b1 = Bs[s * NP + boff1];
+        v.c1 = Cs[s * NP + boff1];
+      }
+    } else {
+      const float4* bp = reinterpret_cast<const float4*>(&Bs[s * NP + g * NPL]);
+      const float4* cp = reinterpret_cast<const float4*>(&Cs[s * NP + g * NPL]);
+#pragma unroll
+      for (int q = 0; q < NPL / 4; ++q) {
+        v.bq[q] = bp[q];
+        v.cq[q] = cp[q];
+      }
+    }
+  };
+
+  auto do_step = [&](int s, const Ops& v) {
+    float a0 = 0.f, a1 = 0.f;
+    if constexpr (FAST) {
+      fast_updates<G, 0, NPL>(h, A2, v.d, v.du, v.b0, G == 2 ? v.b1 : v.b0);
+      if constexpr (G == 2) FastReadout<2>::run(a0, a1, v.c0, v.c1, h);
+      else FastReadout<G>::run(a0, a1, v.c0, h);
+    } else {
+#pragma unroll
+      for (int q = 0; q < NPL / 4; ++q) {
+        const float bb[4] = {v.bq[q].x, v.bq[q].y, v.bq[q].z, v.bq[q].w};
+        const float cc4[4] = {v.cq[q].x, v.cq[q].y, v.cq[q].z, v.cq[q].w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = q * 4 + r;
+          const float dA = exp2_hw(v.d * A2[j]);
+          h[j] = __builtin_fmaf(dA, h[j], v.du * bb[r]);
+          if (r & 1) a1 = __builtin_fmaf(cc4[r], h[j], a1);
+          else a0 = __builtin_fmaf(cc4[r], h[j], a0);
+        }
+      }
+    }
+    const float acc = reduce_groups<G, FAST>(a0 + a1);
+    ys[s * CPB + chb] = from_f32<T>(__builtin_fmaf(acc, v.gz, v.yd));
+    if constexpr (MODE != kSingle) {
+      S += v.d;
+      negseen |= (v.d < 0.f);
+    }
+  };
+
+  // ------------------------------------------------------------------
+  // time loop.  Per tile: stage it (waits for its loads), write the previous
+  // tile's outputs from ys (other LDS arrays than the staging writes), barrier,
+  // issue the next tile's loads, compute (writes ys), barrier.  Both the
+  // stores and the loads thus precede the next wait by a whole tile.
   // ------------------------------------------------------------------
   if (t_begin < t_end) issue_loads(t_begin);
   int64_t prev_t0 = -1;
   for (int64_t t0 = t_begin; t0 < t_end; t0 += TT) {
     const int ns = (t_end - t0) < TT ? static_cast<int>(t_end - t0) : TT;
     stage_to_lds(t0);
-    __syncthreads();
     if (prev_t0 >= 0) store_tile(prev_t0);
+    __syncthreads();
     if (t0 + TT < t_end) issue_loads(t0 + TT);
 
-    for (int s = 0; s < ns; ++s) {
-      const float d = to_f32(ds[s * CPW + ch]);
-      const float u = to_f32(xs[s * CPW + ch]);
-      const float du = d * u;
-      const float4* bp = reinterpret_cast<const float4*>(&Bs[s * NP + g * NPL]);
-      const float4* cp = reinterpret_cast<const float4*>(&Cs[s * NP + g * NPL]);
-      float acc = 0.f;
+    if (ns == TT) {
+      // full tile: fully unrolled, operands read one step ahead (row TT is the spare zero row)
+      Ops cur, nxt;
+      load_step(0, cur);
 #pragma unroll
-      for (int q = 0; q < NPL / 4; ++q) {
-        const float4 bq = bp[q];
-        const float4 cq = cp[q];
-        const float bb[4] = {bq.x, bq.y, bq.z, bq.w};
-        const float cc4[4] = {cq.x, cq.y, cq.z, cq.w};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = q * 4 + r;
-          const float dA = exp2_hw(d * A2[j]);
-          h[j] = __builtin_fmaf(dA, h[j], du * bb[r]);
-          acc = __builtin_fmaf(cc4[r], h[j], acc);
-        }
+      for (int s = 0; s < TT; ++s) {
+        load_step(s + 1, nxt);
+        do_step(s, cur);
+        cur = nxt;
       }
-      acc = group_sum<G>(acc);
-      float y = __builtin_fmaf(Dc, u, acc);
-      if (has_z) {
-        const float zz = to_f32(zs[s * CPW + ch]);
-        y *= zz * __builtin_amdgcn_rcpf(1.f + exp2_hw(-zz * kLog2e));
+    } else {
+      Ops va, vb;
+      load_step(0, va);
+      int s = 0;
+      for (; s + 1 < ns; s += 2) {
+        load_step(s + 1, vb);
+        do_step(s, va);
+        load_step(s + 2, va);     // row s + 2 <= ns < TT: loaded, never used
+        do_step(s + 1, vb);
       }
-      ys[s * CPW + ch] = from_f32<T>(y);
-      if constexpr (MODE != kSingle) {
-        S += d;
-        negseen |= (d < 0.f);
-      }
+      if (s < ns) do_step(s, va);
     }
     __syncthreads();
     prev_t0 = t0;
@@ -378,14 +605,10 @@ __global__ __launch_bounds__(kWave) void scan_kernel(KernelParams p) {
       // carried-in part bounded by exp2(amax * S) * hmax; done once it would be 0 in fp32
       const bool lane_done = !cvalid || hmax == 0.f ||
                              (!never_exit && amax < 0.f && amax * S + __log2f(hmax) < -150.f);
-      if (__all(lane_done)) {
-        fix_done = true;
-        break;
-      }
+      if (__syncthreads_and(lane_done)) break;
     }
   }
   if (prev_t0 >= 0) store_tile(prev_t0);
-  (void)fix_done;
 
   // ------------------------------------------------------------------
   // chunk results
@@ -433,17 +656,17 @@ __global__ __launch_bounds__(256) void carry_kernel(KernelParams p) {
 
 size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
-template <int IO, int G, int NPL, bool VEC>
+template <int IO, int G, int NPL, bool VEC, bool FAST>
 hipError_t launch_cfg(const KernelParams& kp, int64_t batch, hipStream_t stream) {
-  const dim3 block(kWave);
+  const dim3 block(kThreads);
   if (kp.K == 1) {
     const dim3 grid(static_cast<unsigned>(batch * kp.ngroups));
-    hipLaunchKernelGGL((scan_kernel<IO, G, NPL, VEC, kSingle>), grid, block, 0, stream, kp);
+    hipLaunchKernelGGL((scan_kernel<IO, G, NPL, VEC, FAST, kSingle>), grid, block, 0, stream, kp);
     return hipGetLastError();
   }
   {
     const dim3 grid(static_cast<unsigned>(batch * kp.K * kp.ngroups));
-    hipLaunchKernelGGL((scan_kernel<IO, G, NPL, VEC, kChunk>), grid, block, 0, stream, kp);
+    hipLaunchKernelGGL((scan_kernel<IO, G, NPL, VEC, FAST, kChunk>), grid, block, 0, stream, kp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -458,36 +681,44 @@ hipError_t launch_cfg(const KernelParams& kp, int64_t batch, hipStream_t stream)
     KernelParams kf = kp;
     kf.chunk_offset = 1;
     const dim3 grid(static_cast<unsigned>(batch * (kp.K - 1) * kp.ngroups));
-    hipLaunchKernelGGL((scan_kernel<IO, G, NPL, VEC, kFixup>), grid, block, 0, stream, kf);
+    hipLaunchKernelGGL((scan_kernel<IO, G, NPL, VEC, FAST, kFixup>), grid, block, 0, stream, kf);
     return hipGetLastError();
   }
 }
 
-template <int IO, int G, int NPL>
+template <int IO, int G, int NPL, bool FAST>
 hipError_t launch_vec(const KernelParams& kp, bool vec, int64_t batch, hipStream_t stream) {
-  if constexpr (Geometry<IO, G, NPL, true>::VEC_OK) {
-    if (vec) return launch_cfg<IO, G, NPL, true>(kp, batch, stream);
+  if constexpr (Geometry<IO, G, NPL, true, FAST>::VEC_OK) {
+    if (vec) return launch_cfg<IO, G, NPL, true, FAST>(kp, batch, stream);
   }
-  return launch_cfg<IO, G, NPL, false>(kp, batch, stream);
+  return launch_cfg<IO, G, NPL, false, FAST>(kp, batch, stream);
 }
 
 template <int IO, int G>
-hipError_t launch_npl(const KernelParams& kp, int npl, bool vec, int64_t batch, hipStream_t stream) {
+hipError_t launch_generic(const KernelParams& kp, int npl, bool vec, int64_t batch, hipStream_t stream) {
   switch (npl) {
-    case 4: return launch_vec<IO, G, 4>(kp, vec, batch, stream);
-    case 8: return launch_vec<IO, G, 8>(kp, vec, batch, stream);
-    default: return launch_vec<IO, G, 16>(kp, vec, batch, stream);
+    case 4: return launch_vec<IO, G, 4, false>(kp, vec, batch, stream);
+    case 8: return launch_vec<IO, G, 8, false>(kp, vec, batch, stream);
+    default: return launch_vec<IO, G, 16, false>(kp, vec, batch, stream);
   }
 }
 
 template <int IO>
 hipError_t launch_io(const KernelParams& kp, int G, int npl, bool vec, int64_t batch, hipStream_t stream) {
+  if (kp.N <= 16) {
+    switch (G) {
+      case 1: return launch_vec<IO, 1, 16, true>(kp, vec, batch, stream);
+      case 2: return launch_vec<IO, 2, 8, true>(kp, vec, batch, stream);
+      case 4: return launch_vec<IO, 4, 4, true>(kp, vec, batch, stream);
+      case 8: return launch_vec<IO, 8, 4, false>(kp, vec, batch, stream);
+      default: return launch_vec<IO, 16, 4, false>(kp, vec, batch, stream);
+    }
+  }
   switch (G) {
-    case 1: return launch_npl<IO, 1>(kp, npl, vec, batch, stream);
-    case 2: return launch_npl<IO, 2>(kp, npl, vec, batch, stream);
-    case 4: return launch_npl<IO, 4>(kp, npl, vec, batch, stream);
-    case 8: return launch_npl<IO, 8>(kp, npl, vec, batch, stream);
-    default: return launch_npl<IO, 16>(kp, npl, vec, batch, stream);
+    case 2: return launch_vec<IO, 2, 16, false>(kp, vec, batch, stream);
+    case 4: return launch_generic<IO, 4>(kp, npl < 8 ? 8 : npl, vec, batch, stream);
+    case 8: return launch_generic<IO, 8>(kp, npl, vec, batch, stream);
+    default: return launch_generic<IO, 16>(kp, npl, vec, batch, stream);
   }
 }
 
@@ -519,8 +750,8 @@ hipError_t scan_launch(const ScanArgs& a, hipStream_t stream) {
   kp.chunk_len = (a.L + a.K - 1) / a.K;
   kp.chunk_offset = 0;
   const int G = a.G;
-  const int cpw = kWave / G;
-  kp.ngroups = static_cast<int>((a.dim + cpw - 1) / cpw);
+  const int cpb = kThreads / G;
+  kp.ngroups = static_cast<int>((a.dim + cpb - 1) / cpb);
   if (a.K > 1) {
     char* ws = static_cast<char*>(a.workspace);
     const size_t st = static_cast<size_t>(a.batch) * a.K * a.dim * a.N * sizeof(float);
@@ -531,9 +762,14 @@ hipError_t scan_launch(const ScanArgs& a, hipStream_t stream) {
     kp.neg = reinterpret_cast<int*>(ws + 2 * align256(st) + align256(sc));
   }
   const int npl = states_per_lane(G, a.N);
-  const size_t es = a.io == 1 ? 2 : 4;
+  const int64_t es = a.io == 1 ? 2 : 4;
   auto al16 = [](const void* q) { return q == nullptr || (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
-  const bool vec = (a.dim * es) % 16 == 0 && (a.N * es) % 16 == 0 && al16(a.x) && al16(a.delta) && al16(a.z) &&
+  // 16-byte B/C loads need N / (elements per 16 bytes) to be a power of two
+  const int64_t bc_chunks = (a.N * es) / 16;
+  const bool bc_pow2 = (a.N * es) % 16 == 0 && bc_chunks > 0 && (bc_chunks & (bc_chunks - 1)) == 0;
+  kp.bc_shift = 0;
+  while (bc_pow2 && (int64_t{1} << kp.bc_shift) < bc_chunks) ++kp.bc_shift;
+  const bool vec = (a.dim * es) % 16 == 0 && bc_pow2 && al16(a.x) && al16(a.delta) && al16(a.z) &&
                    al16(a.B) && al16(a.C) && al16(a.out);
   if (a.io == 1) return launch_io<1>(kp, G, npl, vec, a.batch, stream);
   return launch_io<0>(kp, G, npl, vec, a.batch, stream);

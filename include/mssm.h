@@ -62,7 +62,7 @@ extern "C" {
 typedef enum {
     MSSM_OK = 0,
     MSSM_ERR_INVALID_ARG = -1,   /* null required pointer, size <= 0, size overflow, aliasing */
-    MSSM_ERR_UNSUPPORTED = -2,   /* dtype, dstate outside 1..256, nheads % ngroups != 0, bad chunk */
+    MSSM_ERR_UNSUPPORTED = -2,   /* dtype, dstate/headdim outside the supported set, nheads % ngroups != 0, bad chunk */
     MSSM_ERR_MISALIGNED = -3,    /* a pointer not aligned to its element size */
     MSSM_ERR_WORKSPACE = -4,     /* workspace missing or smaller than the size query asks */
     MSSM_ERR_HIP = -5            /* a HIP launch failed (see mssm_last_error_detail) */
@@ -95,10 +95,12 @@ typedef struct {
  *   B, C             : [batch, seqlen, ngroups, dstate]    (io_dtype)
  *   A, D             : [nheads] fp32 (D nullable)
  *   h0, final_state  : [batch, nheads, headdim, dstate] fp32, nullable
- * chunk: time-chunk length of the matrix form: 0 (library's choice), 32, 64,
- * 128 or 256.  io_dtype must be MSSM_BF16 (the matrix cores take bf16
- * operands).  headdim must be a multiple of 16 and at most 256; dstate a
- * multiple of 16 and at most 256. */
+ * chunk: time-chunk length of the matrix form: 0 (library's choice), 64, 128
+ * or 256; a chunk longer than 64 steps is evaluated as consecutive 64-step
+ * blocks with the state carried between them (the same algebra, so only
+ * rounding differs).  io_dtype must be MSSM_BF16 (the matrix cores take bf16
+ * operands).  headdim must be a multiple of 64; dstate a multiple of 16 and
+ * at most 128.  The state never leaves the chip between blocks. */
 typedef struct {
     int64_t batch, seqlen, nheads, headdim, dstate, ngroups, chunk;
     int32_t io_dtype;

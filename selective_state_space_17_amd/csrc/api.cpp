@@ -219,9 +219,9 @@ static int validate_ssd_desc(const mssm_ssd_desc* d, int64_t* Q) {
   if (d->flags != 0) return MSSM_ERR_INVALID_ARG;
   if (d->io_dtype != MSSM_BF16) return MSSM_ERR_UNSUPPORTED;
   if (d->nheads % d->ngroups != 0) return MSSM_ERR_UNSUPPORTED;
-  if (d->headdim % 16 != 0 || d->headdim > 256 || d->dstate % 16 != 0 || d->dstate > 256) return MSSM_ERR_UNSUPPORTED;
+  if (d->headdim % 64 != 0 || d->dstate % 16 != 0 || d->dstate > 128) return MSSM_ERR_UNSUPPORTED;
   const int64_t q = d->chunk == 0 ? 64 : d->chunk;
-  if (q != 32 && q != 64 && q != 128 && q != 256) return MSSM_ERR_UNSUPPORTED;
+  if (q != 64 && q != 128 && q != 256) return MSSM_ERR_UNSUPPORTED;
   int64_t t = 0;
   if (!mul_ok(d->batch, d->seqlen, &t) || !mul_ok(t, d->nheads, &t) || !mul_ok(t, d->headdim, &t) ||
       !mul_ok(t, 2, &t))

@@ -1,10 +1,393 @@
-// Mamba-2 scalar-A multi-head (SSD) form -- placeholder until the matrix-core kernel lands.
+// Mamba-2 scalar-A multi-head ("SSD") forward for gfx950 (MI355X).
+//
+// Per (batch b, head h, headdim p, state n) with group g = h / (H / G):
+//   S[p,n] <- exp(delta_t A_h) S[p,n] + delta_t B[t,g,n] x[t,h,p]
+//   y[t,h,p] = sum_n C[t,g,n] S[p,n] (+ D_h x) (* silu(z))
+// The transition is a scalar times the identity ("Mamba-3" blog,
+// introduction), so within a block of Q steps the recurrence unrolls into
+// matrix products ("Mamba-2 y state-space models", 4.2: the selective SSM
+// written as matmuls).  With l_t = delta_t A_h and the inclusive in-block sum
+// s_t = sum_{r<=t} l_r:
+//   y_t   = exp(s_t) C_t . S_in  +  sum_{s<=t} (C_t . B_s) exp(s_t - s_s) delta_s x_s
+//   S_out = exp(s_Q) S_in + sum_s exp(s_Q - s_s) delta_s x_s (x) B_s
+// One workgroup (4 waves) owns one (b, h, 64-wide headdim slice) and walks
+// the sequence in 64-step blocks; its fp32 state stays in MFMA accumulators
+// the whole time (never written to HBM).  Per block:
+//   G  = C . B^T            (64 x 64, K = N)      v_mfma_f32_16x16x32_bf16
+//   M  = G o exp2(s_t - s_s) o delta_s, causal    VALU, bf16 into LDS
+//   Y  = exp2(s_t) (C . S^T) + M . X              (64 x 64, K = N then 64)
+//   S  = exp2(s_Q) S + Xw^T . B                   (64 x N, K = 64)
+// x, B and C enter the matrix cores exactly (they are bf16 inputs).  The three
+// computed operands -- the state copy S, the decayed mask M and the weighted
+// inputs Xw -- are each split into a bf16 pair hi + lo (hi = bf16(v),
+// lo = bf16(v - hi)), so the products see ~16 mantissa bits and the result
+// stays at fp32-state accuracy; the state itself stays fp32 in the
+// accumulators.  Exponents use base 2 with A pre-scaled by log2 e.
+// A chunk length of 128 or 256 steps is evaluated as 2 or 4 consecutive
+// 64-step blocks with the state carried between them (the same algebra).
+#include <type_traits>
+
 #include "internal.h"
 
 namespace mssm {
+namespace {
+
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr int kWave = 64;
+constexpr int kThreads = 256;
+constexpr int QB = 64;     // steps per block
+constexpr int PB = 64;     // headdim slice per workgroup
+constexpr int PAD = 8;     // bf16 padding per LDS row (keeps 16-byte reads conflict-free)
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf2f(uint16_t v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
+__device__ __forceinline__ uint16_t f2bf(float v) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v)); }
+__device__ __forceinline__ float exp2_hw(float v) { return __builtin_amdgcn_exp2f(v); }
+// v = hi + lo with both parts bf16 (about 16 significant bits together)
+__device__ __forceinline__ void split_bf(float v, uint16_t& hi, uint16_t& lo) {
+  hi = f2bf(v);
+  lo = f2bf(v - bf2f(hi));
+}
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 8 consecutive bf16 from LDS (16-byte aligned)
+__device__ __forceinline__ bf16x8 lds8(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+struct SSDParams {
+  const uint16_t* x;
+  const uint16_t* delta;
+  const float* A;
+  const uint16_t* B;
+  const uint16_t* C;
+  const float* D;
+  const uint16_t* z;
+  const float* h0;
+  uint16_t* out;
+  float* final_state;
+  int64_t batch, L, H, P, N, G;
+  int nps;   // headdim slices per head (P / 64)
+};
+
+// MFMA fragment layout (16x16x32): A row / B column = lane % 16, k = 8 * (lane / 16) + q;
+// accumulator element v of a lane is row 4 * (lane / 16) + v, column lane % 16.
+template <int NP>
+__global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
+  constexpr int NS = NP + PAD;        // row stride of [*, NP] arrays
+  constexpr int QS = QB + PAD;        // row stride of [*, 64] arrays
+  constexpr int NT = NP / 16;         // 16-wide state tiles
+  constexpr int CPR = NP / 8;         // 16-byte chunks per padded B/C row
+
+  __shared__ __attribute__((aligned(16))) uint16_t Cs[QB * NS];    // C block  [t][n]
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[QB * NS];    // B block  [s][n]
+  __shared__ __attribute__((aligned(16))) uint16_t BT[NP * QS];    // B block  [n][s]
+  __shared__ __attribute__((aligned(16))) uint16_t XT[PB * QS];    // x block  [p][s]
+  __shared__ __attribute__((aligned(16))) uint16_t Ms[2][QB * QS];  // decayed causal C.B^T [t][s], hi/lo
+  __shared__ __attribute__((aligned(16))) uint16_t Xw[2][PB * QS];  // exp2(s_Q - s_s) delta_s x_s [p][s], hi/lo
+  __shared__ __attribute__((aligned(16))) uint16_t Sb[2][PB * NS];  // state [p][n], hi/lo
+  __shared__ float dls[QB];   // delta
+  __shared__ float css[QB];   // inclusive sum of delta * A * log2 e
+
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int w = tid / kWave;
+  const int lr = lane % 16;         // fragment row / column
+  const int lk = 8 * (lane / 16);   // fragment k offset
+  const int lq = 4 * (lane / 16);   // accumulator row offset
+
+  // block -> (b, g, head within group, headdim slice); all blocks of one (b, g)
+  // share an XCD when batch*groups is a multiple of 8 (B/C then stay in that L2)
+  const int64_t BG = p.batch * p.G;
+  const int64_t wid = blockIdx.x;
+  const int64_t pair = wid % BG;
+  const int64_t member = wid / BG;
+  const int64_t b = pair / p.G, g = pair % p.G;
+  const int64_t hpg = p.H / p.G;
+  const int64_t h = g * hpg + member / p.nps;
+  const int64_t p0 = (member % p.nps) * PB;
+  const int64_t L = p.L, H = p.H, P = p.P, N = p.N, G = p.G;
+  const float a2 = p.A[h] * kLog2e;
+  const float Dh = p.D != nullptr ? p.D[h] : 0.f;
+  const int Ni = static_cast<int>(N);
+  const int cpr = Ni / 8;             // 16-byte chunks per B/C row in memory
+
+  // zero the padded state columns of C/B/B^T/S (never written afterwards)
+  for (int e = tid; e < QB * NS; e += kThreads) {
+    if ((e % NS) >= Ni) { Cs[e] = 0; Bs[e] = 0; }
+  }
+  for (int e = tid; e < NP * QS; e += kThreads) {
+    if (e / QS >= Ni) BT[e] = 0;
+  }
+
+  // ---- state: wave w owns headdim rows [16w, 16w+16) x all NP columns ----
+  f32x4 S[NT];
+#pragma unroll
+  for (int c = 0; c < NT; ++c) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t pp = p0 + 16 * w + lq + v, n = 16 * c + lr;
+      S[c][v] = (p.h0 != nullptr && n < N) ? p.h0[((b * H + h) * P + pp) * N + n] : 0.f;
+    }
+  }
+  auto write_state_bf16 = [&]() {
+#pragma unroll
+    for (int c = 0; c < NT; ++c)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int e = (16 * w + lq + v) * NS + 16 * c + lr;
+        split_bf(S[c][v], Sb[0][e], Sb[1][e]);
+      }
+  };
+  write_state_bf16();
+
+  // ---- prefetch registers for one block ----
+  constexpr int BCL = (QB * CPR + kThreads - 1) / kThreads;   // B (and C) 16-byte loads per thread
+  constexpr int XL = QB * (PB / 8) / kThreads;                 // x loads per thread (2)
+  u32x4 breg[BCL], creg[BCL], xreg[XL];
+  uint16_t dreg = 0;
+
+  auto issue_loads = [&](int64_t t0, int nvalid) {
+    // B, C: rows of N bf16 (group g)
+#pragma unroll
+    for (int i = 0; i < BCL; ++i) {
+      const int ci = i * kThreads + tid;
+      int r = ci / cpr, c8 = ci - (ci / cpr) * cpr;
+      if (ci >= QB * cpr) { r = 0; c8 = 0; }
+      const int rr = r < nvalid ? r : nvalid - 1;
+      const int64_t off = ((b * L + t0 + rr) * G + g) * N + 8 * c8;
+      breg[i] = *reinterpret_cast<const u32x4*>(p.B + off);
+      creg[i] = *reinterpret_cast<const u32x4*>(p.C + off);
+    }
+#pragma unroll
+    for (int i = 0; i < XL; ++i) {
+      const int ci = i * kThreads + tid;
+      const int r = ci / (PB / 8), c8 = ci % (PB / 8);
+      const int rr = r < nvalid ? r : nvalid - 1;
+      xreg[i] = *reinterpret_cast<const u32x4*>(p.x + ((b * L + t0 + rr) * H + h) * P + p0 + 8 * c8);
+    }
+    if (tid < QB) {
+      const int rr = tid < nvalid ? tid : nvalid - 1;
+      dreg = p.delta[(b * L + t0 + rr) * H + h];
+    }
+  };
+
+  auto stage = [&](int nvalid) {
+#pragma unroll
+    for (int i = 0; i < BCL; ++i) asm volatile("" : "+v"(breg[i]), "+v"(creg[i]));
+#pragma unroll
+    for (int i = 0; i < XL; ++i) asm volatile("" : "+v"(xreg[i]));
+#pragma unroll
+    for (int i = 0; i < BCL; ++i) {
+      const int ci = i * kThreads + tid;
+      if (ci < QB * cpr) {
+        const int r = ci / cpr, c8 = ci - (ci / cpr) * cpr;
+        const bool ok = r < nvalid;
+        const u32x4 bv = ok ? breg[i] : u32x4{0, 0, 0, 0};
+        const u32x4 cv = ok ? creg[i] : u32x4{0, 0, 0, 0};
+        *reinterpret_cast<u32x4*>(&Bs[r * NS + 8 * c8]) = bv;
+        *reinterpret_cast<u32x4*>(&Cs[r * NS + 8 * c8]) = cv;
+        const uint16_t* be = reinterpret_cast<const uint16_t*>(&bv);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) BT[(8 * c8 + q) * QS + r] = be[q];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < XL; ++i) {
+      const int ci = i * kThreads + tid;
+      const int r = ci / (PB / 8), c8 = ci % (PB / 8);
+      const u32x4 xv = r < nvalid ? xreg[i] : u32x4{0, 0, 0, 0};
+      const uint16_t* xe = reinterpret_cast<const uint16_t*>(&xv);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) XT[(8 * c8 + q) * QS + r] = xe[q];
+    }
+    if (tid < QB) dls[tid] = tid < nvalid ? bf2f(dreg) : 0.f;
+  };
+
+  // ---- block loop ----
+  const int64_t nblocks = (L + QB - 1) / QB;
+  if (nblocks > 0) issue_loads(0, static_cast<int>(L < QB ? L : QB));
+  for (int64_t blk = 0; blk < nblocks; ++blk) {
+    const int64_t t0 = blk * QB;
+    const int nvalid = static_cast<int>((L - t0) < QB ? (L - t0) : QB);
+    stage(nvalid);
+    __syncthreads();
+    if (blk + 1 < nblocks) {
+      const int64_t t1 = t0 + QB;
+      issue_loads(t1, static_cast<int>((L - t1) < QB ? (L - t1) : QB));
+    }
+    // inclusive in-block sum of delta * A * log2 e (wave 0)
+    if (w == 0) {
+      float v = dls[lane] * a2;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const float u = __shfl_up(v, off, kWave);
+        if (lane >= off) v += u;
+      }
+      css[lane] = v;
+    }
+    __syncthreads();
+    const float cs_end = css[QB - 1];
+
+    // G = C . B^T for t-tile w (4 s-tiles), then M = decayed causal G -> LDS
+    {
+      f32x4 Gacc[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) Gacc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k0 = 0; k0 < NP; k0 += 32) {
+        const bf16x8 a = lds8(&Cs[(16 * w + lr) * NS + k0 + lk]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          if (c <= w) Gacc[c] = mfma16(a, lds8(&Bs[(16 * c + lr) * NS + k0 + lk]), Gacc[c]);
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int s = 16 * c + lr;
+        const float css_s = css[s], dl_s = dls[s];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int t = 16 * w + lq + v;
+          const float m = (c <= w && s <= t) ? Gacc[c][v] * exp2_hw(css[t] - css_s) * dl_s : 0.f;
+          split_bf(m, Ms[0][t * QS + s], Ms[1][t * QS + s]);
+        }
+      }
+    }
+    // Xw[p][s] = exp2(s_Q - s_s) delta_s x[s][p]
+#pragma unroll
+    for (int i = 0; i < PB * QB / kThreads; ++i) {
+      const int e = i * kThreads + tid;
+      const int pp = e / QB, s = e % QB;
+      const float wgt = exp2_hw(cs_end - css[s]) * dls[s];
+      split_bf(wgt * bf2f(XT[pp * QS + s]), Xw[0][pp * QS + s], Xw[1][pp * QS + s]);
+    }
+    __syncthreads();
+
+    // Y for t-tile w, 4 headdim tiles
+    {
+      f32x4 Y[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) Y[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k0 = 0; k0 < NP; k0 += 32) {
+        const bf16x8 a = lds8(&Cs[(16 * w + lr) * NS + k0 + lk]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          Y[c] = mfma16(a, lds8(&Sb[0][(16 * c + lr) * NS + k0 + lk]), Y[c]);
+          Y[c] = mfma16(a, lds8(&Sb[1][(16 * c + lr) * NS + k0 + lk]), Y[c]);
+        }
+      }
+      float rs[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) rs[v] = exp2_hw(css[16 * w + lq + v]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) Y[c][v] *= rs[v];
+#pragma unroll
+      for (int s0 = 0; s0 < QB; s0 += 32) {
+        if (s0 <= 16 * w + 15) {
+          const bf16x8 ah = lds8(&Ms[0][(16 * w + lr) * QS + s0 + lk]);
+          const bf16x8 al = lds8(&Ms[1][(16 * w + lr) * QS + s0 + lk]);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const bf16x8 bx = lds8(&XT[(16 * c + lr) * QS + s0 + lk]);
+            Y[c] = mfma16(ah, bx, Y[c]);
+            Y[c] = mfma16(al, bx, Y[c]);
+          }
+        }
+      }
+      // epilogue: + D x, * silu(z), store
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int pl = 16 * c + lr;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int t = 16 * w + lq + v;
+          if (t < nvalid) {
+            const int64_t o = ((b * L + t0 + t) * H + h) * P + p0 + pl;
+            float y = Y[c][v] + Dh * bf2f(XT[pl * QS + t]);
+            if (p.z != nullptr) {
+              const float zz = bf2f(p.z[o]);
+              y *= zz * __builtin_amdgcn_rcpf(1.f + exp2_hw(-zz * kLog2e));
+            }
+            p.out[o] = f2bf(y);
+          }
+        }
+      }
+    }
+
+    // state: S = exp2(s_Q) S + Xw^T B  (rows 16w.. of headdim, all NP columns)
+    {
+      const float dec = exp2_hw(cs_end);
+#pragma unroll
+      for (int c = 0; c < NT; ++c)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) S[c][v] *= dec;
+#pragma unroll
+      for (int s0 = 0; s0 < QB; s0 += 32) {
+        const bf16x8 ah = lds8(&Xw[0][(16 * w + lr) * QS + s0 + lk]);
+        const bf16x8 al = lds8(&Xw[1][(16 * w + lr) * QS + s0 + lk]);
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+          const bf16x8 bb = lds8(&BT[(16 * c + lr) * QS + s0 + lk]);
+          S[c] = mfma16(ah, bb, S[c]);
+          S[c] = mfma16(al, bb, S[c]);
+        }
+      }
+    }
+    __syncthreads();      // every wave is done with this block's LDS (including the old Sb)
+    write_state_bf16();
+  }
+
+  if (p.final_state != nullptr) {
+#pragma unroll
+    for (int c = 0; c < NT; ++c)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t pp = p0 + 16 * w + lq + v, n = 16 * c + lr;
+        if (n < N) p.final_state[((b * H + h) * P + pp) * N + n] = S[c][v];
+      }
+  }
+}
+
+template <int NP>
+hipError_t launch_np(const SSDParams& sp, hipStream_t stream) {
+  const int64_t blocks = sp.batch * sp.H * sp.nps;
+  hipLaunchKernelGGL(ssd_kernel<NP>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream, sp);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool ssd_supported(int64_t P, int64_t N) { return P % PB == 0 && P > 0 && N % 16 == 0 && N > 0 && N <= 128; }
 
 size_t ssd_workspace_bytes(int64_t, int64_t, int64_t, int64_t, int64_t, int64_t, int64_t) { return 0; }
 
-hipError_t ssd_launch(const SSDArgs&, hipStream_t) { return hipErrorNotSupported; }
+hipError_t ssd_launch(const SSDArgs& a, hipStream_t stream) {
+  SSDParams sp{};
+  sp.x = static_cast<const uint16_t*>(a.x);
+  sp.delta = static_cast<const uint16_t*>(a.delta);
+  sp.A = a.A;
+  sp.B = static_cast<const uint16_t*>(a.B);
+  sp.C = static_cast<const uint16_t*>(a.C);
+  sp.D = a.D;
+  sp.z = static_cast<const uint16_t*>(a.z);
+  sp.h0 = a.h0;
+  sp.out = static_cast<uint16_t*>(a.out);
+  sp.final_state = a.final_state;
+  sp.batch = a.batch; sp.L = a.L; sp.H = a.H; sp.P = a.P; sp.N = a.N; sp.G = a.G;
+  sp.nps = static_cast<int>(a.P / PB);
+  if (a.N <= 32) return launch_np<32>(sp, stream);
+  if (a.N <= 64) return launch_np<64>(sp, stream);
+  return launch_np<128>(sp, stream);
+}
 
 }  // namespace mssm

@@ -88,7 +88,9 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t Cs[QB * NS];    // C block  [t][n]
   __shared__ __attribute__((aligned(16))) uint16_t Bs[QB * NS];    // B block  [s][n]
   __shared__ __attribute__((aligned(16))) uint16_t BT[NP * QS];    // B block  [n][s]
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[QB * QS];    // x block  [s][p]
   __shared__ __attribute__((aligned(16))) uint16_t XT[PB * QS];    // x block  [p][s]
+  __shared__ __attribute__((aligned(16))) uint16_t Ys[QB * QS];    // outputs of the previous block [t][p]
   __shared__ __attribute__((aligned(16))) uint16_t Ms[2][QB * QS];  // decayed causal C.B^T [t][s], hi/lo
   __shared__ __attribute__((aligned(16))) uint16_t Xw[2][PB * QS];  // exp2(s_Q - s_s) delta_s x_s [p][s], hi/lo
   __shared__ __attribute__((aligned(16))) uint16_t Sb[2][PB * NS];  // state [p][n], hi/lo
@@ -121,9 +123,6 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
   // zero the padded state columns of C/B/B^T/S (never written afterwards)
   for (int e = tid; e < QB * NS; e += kThreads) {
     if ((e % NS) >= Ni) { Cs[e] = 0; Bs[e] = 0; }
-  }
-  for (int e = tid; e < NP * QS; e += kThreads) {
-    if (e / QS >= Ni) BT[e] = 0;
   }
 
   // ---- state: wave w owns headdim rows [16w, 16w+16) x all NP columns ----
@@ -178,6 +177,7 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
     }
   };
 
+  // registers -> LDS, row-major (16-byte writes); rows past the end are zero
   auto stage = [&](int nvalid) {
 #pragma unroll
     for (int i = 0; i < BCL; ++i) asm volatile("" : "+v"(breg[i]), "+v"(creg[i]));
@@ -189,25 +189,52 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
       if (ci < QB * cpr) {
         const int r = ci / cpr, c8 = ci - (ci / cpr) * cpr;
         const bool ok = r < nvalid;
-        const u32x4 bv = ok ? breg[i] : u32x4{0, 0, 0, 0};
-        const u32x4 cv = ok ? creg[i] : u32x4{0, 0, 0, 0};
-        *reinterpret_cast<u32x4*>(&Bs[r * NS + 8 * c8]) = bv;
-        *reinterpret_cast<u32x4*>(&Cs[r * NS + 8 * c8]) = cv;
-        const uint16_t* be = reinterpret_cast<const uint16_t*>(&bv);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) BT[(8 * c8 + q) * QS + r] = be[q];
+        *reinterpret_cast<u32x4*>(&Bs[r * NS + 8 * c8]) = ok ? breg[i] : u32x4{0, 0, 0, 0};
+        *reinterpret_cast<u32x4*>(&Cs[r * NS + 8 * c8]) = ok ? creg[i] : u32x4{0, 0, 0, 0};
       }
     }
 #pragma unroll
     for (int i = 0; i < XL; ++i) {
       const int ci = i * kThreads + tid;
       const int r = ci / (PB / 8), c8 = ci % (PB / 8);
-      const u32x4 xv = r < nvalid ? xreg[i] : u32x4{0, 0, 0, 0};
-      const uint16_t* xe = reinterpret_cast<const uint16_t*>(&xv);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) XT[(8 * c8 + q) * QS + r] = xe[q];
+      *reinterpret_cast<u32x4*>(&Xs[r * QS + 8 * c8]) = r < nvalid ? xreg[i] : u32x4{0, 0, 0, 0};
     }
     if (tid < QB) dls[tid] = tid < nvalid ? bf2f(dreg) : 0.f;
+  };
+
+  // transposed copies for the operands that need a column as k: consecutive
+  // lanes read consecutive columns (conflict-free) and write 16-byte rows
+  auto transpose = [&]() {
+#pragma unroll
+    for (int i = 0; i < NP * (QB / 8) / kThreads; ++i) {
+      const int j = i * kThreads + tid;
+      const int n = j % NP, s8 = j / NP;
+      uint16_t v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = Bs[(8 * s8 + q) * NS + n];
+      *reinterpret_cast<u32x4*>(&BT[n * QS + 8 * s8]) = __builtin_bit_cast(u32x4, v);
+    }
+#pragma unroll
+    for (int i = 0; i < PB * (QB / 8) / kThreads; ++i) {
+      const int j = i * kThreads + tid;
+      const int pp = j % PB, s8 = j / PB;
+      uint16_t v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = Xs[(8 * s8 + q) * QS + pp];
+      *reinterpret_cast<u32x4*>(&XT[pp * QS + 8 * s8]) = __builtin_bit_cast(u32x4, v);
+    }
+  };
+
+  // outputs of a finished block, 16-byte stores
+  auto store_block = [&](int64_t t0, int nvalid) {
+#pragma unroll
+    for (int i = 0; i < XL; ++i) {
+      const int ci = i * kThreads + tid;
+      const int r = ci / (PB / 8), c8 = ci % (PB / 8);
+      if (r < nvalid)
+        *reinterpret_cast<u32x4*>(p.out + ((b * L + t0 + r) * H + h) * P + p0 + 8 * c8) =
+            *reinterpret_cast<const u32x4*>(&Ys[r * QS + 8 * c8]);
+    }
   };
 
   // ---- block loop ----
@@ -217,11 +244,13 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
     const int64_t t0 = blk * QB;
     const int nvalid = static_cast<int>((L - t0) < QB ? (L - t0) : QB);
     stage(nvalid);
+    if (blk > 0) store_block(t0 - QB, QB);     // every block but the last is full
     __syncthreads();
     if (blk + 1 < nblocks) {
       const int64_t t1 = t0 + QB;
       issue_loads(t1, static_cast<int>((L - t1) < QB ? (L - t1) : QB));
     }
+    transpose();
     // inclusive in-block sum of delta * A * log2 e (wave 0)
     if (w == 0) {
       float v = dls[lane] * a2;
@@ -311,15 +340,12 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int t = 16 * w + lq + v;
-          if (t < nvalid) {
-            const int64_t o = ((b * L + t0 + t) * H + h) * P + p0 + pl;
-            float y = Y[c][v] + Dh * bf2f(XT[pl * QS + t]);
-            if (p.z != nullptr) {
-              const float zz = bf2f(p.z[o]);
-              y *= zz * __builtin_amdgcn_rcpf(1.f + exp2_hw(-zz * kLog2e));
-            }
-            p.out[o] = f2bf(y);
+          float y = Y[c][v] + Dh * bf2f(Xs[t * QS + pl]);
+          if (p.z != nullptr && t < nvalid) {
+            const float zz = bf2f(p.z[((b * L + t0 + t) * H + h) * P + p0 + pl]);
+            y *= zz * __builtin_amdgcn_rcpf(1.f + exp2_hw(-zz * kLog2e));
           }
+          Ys[t * QS + pl] = f2bf(y);
         }
       }
     }
@@ -345,6 +371,11 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
     }
     __syncthreads();      // every wave is done with this block's LDS (including the old Sb)
     write_state_bf16();
+  }
+
+  if (nblocks > 0) {
+    const int64_t tl = (nblocks - 1) * QB;
+    store_block(tl, static_cast<int>(L - tl));
   }
 
   if (p.final_state != nullptr) {

@@ -155,6 +155,8 @@ def main():
     ap.add_argument("--config", type=int, default=2, help="workload id (1-5); 2 is the one the metric is quoted on")
     ap.add_argument("--sets", type=int, default=0, help="resident input copies to rotate over (0: auto)")
     ap.add_argument("--chunk", type=int, default=0, help="SSD time-chunk length (0: the workload's)")
+    ap.add_argument("--split-seq", type=int, default=0, help="force the sequence-chunk count (0: the planner's)")
+    ap.add_argument("--split-state", type=int, default=0, help="force lanes per channel (0: the planner's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB 5 times (scales the HBM byte counters)")
@@ -225,15 +227,17 @@ def main():
                  torch.empty((cfg.batch, cfg.dim, cfg.dstate), dtype=torch.float32, device="cuda")
                  if cfg.return_final else None) for i in ins]
         io = M.MSSM_BF16 if cfg.io == W.BF16 else M.MSSM_F32
-        K, G = M.selective_scan_plan(cfg.batch, cfg.seqlen, cfg.dim, cfg.dstate, io)
-        ws_n = M.selective_scan_workspace_size(cfg.batch, cfg.seqlen, cfg.dim, cfg.dstate, io)
+        K, G = M.selective_scan_plan(cfg.batch, cfg.seqlen, cfg.dim, cfg.dstate, io,
+                                     split_seq=args.split_seq, split_state=args.split_state)
+        ws_n = M.selective_scan_workspace_size(cfg.batch, cfg.seqlen, cfg.dim, cfg.dstate, io,
+                                               split_seq=K, split_state=G)
         ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
 
         def step(i):
             a, (o, f) = ins[i % sets], outs[i % sets]
             M.selective_scan_fwd(a["x"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], None,
                                  out=o, final_state=f, return_final_state=f is not None,
-                                 workspace=ws if ws_n else None)
+                                 split_seq=K, split_state=G, workspace=ws if ws_n else None)
         plan = {"split_seq": K, "split_state": G}
     del host[1:]
     torch.cuda.synchronize()

@@ -56,6 +56,10 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run `python -m selective_state_space_17_amd.build` "
                           "(or __graft_entry__.build()) first")
+    # The library's HIP runtime dependency must resolve to the copy torch ships:
+    # two HIP runtimes in one process leave the second without a device.  Load
+    # torch first so libamdhip64 is already present when the library is opened.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)

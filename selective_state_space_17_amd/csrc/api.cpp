@@ -61,7 +61,10 @@ double scan_cost(const mssm_scan_desc& d, int G, int K) {
   const int npl = states_per_lane(G, d.dstate);
   const int64_t cpb = 256 / G;                               // channels per 4-wave block
   const int64_t groups = d.batch * ((d.dim + cpb - 1) / cpb) * 4;   // waves per chunk
-  const double slots_step = npl * 6.0 + ilog2(G) + 14.0;   // 6 slots per state update + per-step epilogue
+  // 6 slots per state update + per-step epilogue; with 16 lanes per channel and
+  // dstate 16 (one state per lane) the readout sum is a 16-step LDS transpose
+  // and the per-(t, c) staging is spread over 16 lanes: about 11 slots per step
+  const double slots_step = (G == 16 && d.dstate == 16) ? 11.0 : npl * 6.0 + ilog2(G) + 14.0;
   const int64_t chunk = (d.seqlen + K - 1) / K;
   // pass 2 rescans until the carried-in state has decayed (about 800 steps for
   // softplus-distributed deltas and |A| >= 1); bounded by the chunk length

@@ -636,6 +636,279 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(KernelParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// One state per lane ("wide" layout), dstate == 16.
+//
+// A 16-lane row of a wave is one channel and lane n of the row holds its state
+// n, so a problem has 16 lanes per channel and fills the chip with several
+// waves per SIMD even where batch * dim is small.  Per step a lane issues five
+// VALU operations and nothing else: delta and delta*x of step s come from lane
+// s of its row (row_newbcast:s, folded by the compiler into v_mul_f32_dpp),
+// B_n and C_n are the lane's own registers (read from transposed LDS copies,
+// 16-byte reads covering 4 steps).  The readout's sum over the 16 states runs
+// once per 16 steps: each lane parks its 16 products C_n h_n in LDS and reads
+// back the 16 products of one step (a transpose), so lane j of a row finishes
+// step j, applies the gate and writes the output.  Steps past the end of the
+// sequence are staged with delta = 0, which leaves the state unchanged exactly
+// (exp2(0) = 1, delta*x = 0).
+// ---------------------------------------------------------------------------
+namespace wide {
+constexpr int CPB = 16;            // channels per block (one per 16-lane row)
+constexpr int TT = 64;             // steps per tile (4 groups of 16)
+constexpr int QS = TT + 1;         // float4 row stride of the per-(c, t) operands (spreads banks)
+constexpr int BS = TT + 4;         // float row stride of the transposed B/C tiles
+constexpr int PS = 20;             // float stride between one lane's 16 products
+constexpr int PR = 16 * PS + 16;   // float stride between rows of the product buffer
+}  // namespace wide
+
+using u32x2 = unsigned int __attribute__((ext_vector_type(2)));
+
+template <int S> __device__ __forceinline__ float row_bcast(float v) { return dpp<row_newbcast(S)>(v); }
+
+// 16 recurrence steps of one lane: its state h, exponent slope a2, the step
+// operands q (delta, delta*x held by lane s of the row for step s), B_n and
+// C_n per step; products C_n h_n land in pr.
+template <int S>
+__device__ __forceinline__ void wide_steps(float& h, float a2, float qd, float qu, const float (&Bv)[16],
+                                           const float (&Cv)[16], float (&pr)[16]) {
+  const float dA = exp2_hw(row_bcast<S>(qd) * a2);
+  h = __builtin_fmaf(dA, h, row_bcast<S>(qu) * Bv[S]);
+  pr[S] = Cv[S] * h;
+  if constexpr (S + 1 < 16) wide_steps<S + 1>(h, a2, qd, qu, Bv, Cv, pr);
+}
+
+__device__ __forceinline__ float row_sum(float v) {
+  v += dpp<0x128>(v);   // row_ror:8
+  v += dpp<0x124>(v);   // row_ror:4
+  v += dpp<0x122>(v);   // row_ror:2
+  v += dpp<0x121>(v);   // row_ror:1
+  return v;
+}
+
+template <int IO, int MODE>
+__global__ __launch_bounds__(kThreads) void wide_kernel(KernelParams p) {
+  using namespace wide;
+  using T = typename IoType<IO>::T;
+  // a staging thread moves 4 channels (or 4 states of B/C) of one step
+  using Chunk = typename std::conditional<IO == 1, u32x2, u32x4>::type;
+
+  __shared__ __attribute__((aligned(16))) float4 Qs[CPB * QS];      // {delta, delta*x, silu(z), silu(z)*D*x} [c][t]
+  __shared__ __attribute__((aligned(16))) float Bt[16 * BS];        // B [n][t]
+  __shared__ __attribute__((aligned(16))) float Ct[16 * BS];        // C [n][t]
+  __shared__ __attribute__((aligned(16))) float Pb[kThreads / 16 * PR];   // per-row products [row][n][s]
+  __shared__ __attribute__((aligned(16))) T ys[TT * CPB];           // outputs of the previous tile [t][c]
+
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int row = tid / 16;            // channel within the block (4 rows per wave)
+  const int n = lane % 16;             // state of this lane; also the step it finishes in a group
+
+  // block -> (batch, chunk, channel group); 4 consecutive channel groups (one
+  // 128-byte line of a bf16 row) run on one XCD, whose L2 then serves them all
+  const int64_t nb = gridDim.x;
+  const int64_t bid = blockIdx.x;
+  int64_t lin = bid;
+  if (bid < (nb / 32) * 32) {
+    const int64_t xcd = bid % 8, rr = bid / 8;
+    lin = ((rr / 4) * 8 + xcd) * 4 + rr % 4;
+  }
+  const int cg = static_cast<int>(lin % p.ngroups);
+  const int64_t rest = lin / p.ngroups;
+  const int nchunks_here = (MODE == kFixup) ? p.K - 1 : p.K;
+  const int k = static_cast<int>(rest % nchunks_here) + p.chunk_offset;
+  const int64_t b = rest / nchunks_here;
+
+  const int64_t dim = p.dim, L = p.L;
+  const int64_t c0 = static_cast<int64_t>(cg) * CPB;
+  const int64_t c = c0 + row;
+  const bool cvalid = c < dim;
+  const int64_t cl = cvalid ? c : dim - 1;
+  const int64_t t_begin = static_cast<int64_t>(k) * p.chunk_len;
+  const int64_t t_end = t_begin + p.chunk_len < L ? t_begin + p.chunk_len : L;
+
+  const T* __restrict__ xg = static_cast<const T*>(p.x);
+  const T* __restrict__ dg = static_cast<const T*>(p.delta);
+  const T* __restrict__ zg = static_cast<const T*>(p.z != nullptr ? p.z : p.x);
+  const T* __restrict__ Bg = static_cast<const T*>(p.B);
+  const T* __restrict__ Cg = static_cast<const T*>(p.C);
+  T* __restrict__ yg = static_cast<T*>(p.out);
+  const bool has_z = p.z != nullptr;
+
+  const float a2 = p.A[cl * 16 + n] * kLog2e;
+  float h = 0.f;
+  if constexpr (MODE == kFixup) {
+    h = p.hin[((b * p.K + k) * dim + cl) * 16 + n];
+  } else {
+    if (p.h0 != nullptr && (MODE == kSingle || k == 0)) h = p.h0[(b * dim + cl) * 16 + n];
+  }
+  const float h_in = h;
+  bool never_exit = false;
+  if constexpr (MODE == kFixup) never_exit = p.neg[(b * p.K + k) * dim + cl] != 0;
+  float S = 0.f;         // this lane's share of the chunk's delta sum (the steps it stages)
+  float negseen = 0.f;   // 1 once a negative delta was seen among those steps
+
+  // staging: thread -> (step ts, 4 channels / states from 4*q4)
+  const int ts = tid / 4, q4 = tid % 4;
+  const int64_t sc = (c0 + 4 * q4) < dim ? (c0 + 4 * q4) : (dim - 4);   // dim % 4 == 0
+  float Dreg[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) Dreg[q] = p.D != nullptr ? p.D[sc + q] : 0.f;
+
+  Chunk xr, dr, zr, br, cr;
+  auto issue_loads = [&](int64_t t0) {
+    const int nvalid = static_cast<int>((t_end - t0) < TT ? (t_end - t0) : TT);
+    const int rr = ts < nvalid ? ts : nvalid - 1;
+    const int64_t row_t = b * L + t0 + rr;
+    xr = *reinterpret_cast<const Chunk*>(xg + row_t * dim + sc);
+    dr = *reinterpret_cast<const Chunk*>(dg + row_t * dim + sc);
+    zr = *reinterpret_cast<const Chunk*>(zg + row_t * dim + sc);
+    br = *reinterpret_cast<const Chunk*>(Bg + row_t * 16 + 4 * q4);
+    cr = *reinterpret_cast<const Chunk*>(Cg + row_t * 16 + 4 * q4);
+  };
+
+  auto stage = [&](int64_t t0) {
+    const int nvalid = static_cast<int>((t_end - t0) < TT ? (t_end - t0) : TT);
+    asm volatile("" : "+v"(xr), "+v"(dr), "+v"(zr), "+v"(br), "+v"(cr));
+    const T* xv = reinterpret_cast<const T*>(&xr);
+    const T* dv = reinterpret_cast<const T*>(&dr);
+    const T* zv = reinterpret_cast<const T*>(&zr);
+    const T* bv = reinterpret_cast<const T*>(&br);
+    const T* cv = reinterpret_cast<const T*>(&cr);
+    const bool ok = ts < nvalid;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float d = to_f32(dv[q]), u = to_f32(xv[q]);
+      const float gz = has_z ? silu_gate(to_f32(zv[q])) : 1.f;
+      const float4 v = ok ? float4{d, d * u, gz, gz * (Dreg[q] * u)} : float4{0.f, 0.f, 0.f, 0.f};
+      Qs[(4 * q4 + q) * QS + ts] = v;
+      Bt[(4 * q4 + q) * BS + ts] = to_f32(bv[q]);
+      Ct[(4 * q4 + q) * BS + ts] = to_f32(cv[q]);
+    }
+  };
+
+  auto store_tile = [&](int64_t t0) {
+    const int nvalid = static_cast<int>((t_end - t0) < TT ? (t_end - t0) : TT);
+    // TT rows of 16 channels: 16 / (16 / sizeof(T)) 16-byte pieces per row
+    constexpr int PPR = CPB * static_cast<int>(sizeof(T)) / 16;
+    for (int e = tid; e < TT * PPR; e += kThreads) {
+      const int rrow = e / PPR, piece = e % PPR;
+      const int64_t cc = c0 + piece * (16 / static_cast<int>(sizeof(T)));
+      if (rrow < nvalid && cc < dim)
+        *reinterpret_cast<u32x4*>(yg + (b * L + t0 + rrow) * dim + cc) =
+            *reinterpret_cast<const u32x4*>(&ys[rrow * CPB + piece * (16 / static_cast<int>(sizeof(T)))]);
+    }
+  };
+
+  float* const Prow = &Pb[row * PR];
+
+  // operands of one 16-step group: q = {delta, delta*x, silu(z), silu(z)*D*x}
+  // of step t16 + n, and B_n, C_n of the 16 steps
+  struct GroupOps {
+    float4 q;
+    float Bv[16], Cv[16];
+  };
+  auto load_ops = [&](int t16, GroupOps& o) {
+    o.q = Qs[row * QS + t16 + n];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 bb = *reinterpret_cast<const float4*>(&Bt[n * BS + t16 + 4 * i]);
+      const float4 cc = *reinterpret_cast<const float4*>(&Ct[n * BS + t16 + 4 * i]);
+      o.Bv[4 * i] = bb.x; o.Bv[4 * i + 1] = bb.y; o.Bv[4 * i + 2] = bb.z; o.Bv[4 * i + 3] = bb.w;
+      o.Cv[4 * i] = cc.x; o.Cv[4 * i + 1] = cc.y; o.Cv[4 * i + 2] = cc.z; o.Cv[4 * i + 3] = cc.w;
+    }
+  };
+  // transpose through LDS: lane n parks its 16 products, then reads the 16
+  // products of step n (issued here, summed later so the LDS latency overlaps
+  // the next group's arithmetic)
+  auto park_and_fetch = [&](const float (&pr)[16], float (&rd)[16]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<float4*>(&Prow[n * PS + 4 * i]) = float4{pr[4 * i], pr[4 * i + 1], pr[4 * i + 2], pr[4 * i + 3]};
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int m = 0; m < 16; ++m) rd[m] = Prow[m * PS + n];
+    __builtin_amdgcn_wave_barrier();
+  };
+  auto finish = [&](int t16, const float4& q, const float (&rd)[16]) {
+    const float y = ((rd[0] + rd[1]) + (rd[2] + rd[3]) + ((rd[4] + rd[5]) + (rd[6] + rd[7]))) +
+                    ((rd[8] + rd[9]) + (rd[10] + rd[11]) + ((rd[12] + rd[13]) + (rd[14] + rd[15])));
+    ys[(t16 + n) * CPB + row] = from_f32<T>(__builtin_fmaf(y, q.z, q.w));
+    if constexpr (MODE != kSingle) {
+      S += q.x;
+      negseen = q.x < 0.f ? 1.f : negseen;
+    }
+  };
+  // one group start to finish (tail tiles)
+  auto group = [&](int t16) {
+    GroupOps o;
+    float pr[16], rd[16];
+    load_ops(t16, o);
+    wide_steps<0>(h, a2, o.q.x, o.q.y, o.Bv, o.Cv, pr);
+    park_and_fetch(pr, rd);
+    finish(t16, o.q, rd);
+  };
+  // a full tile, software-pipelined: group g+1's operands are read before
+  // group g's steps, group g-1's sum after them
+  auto full_tile = [&]() {
+    GroupOps o[2];
+    float pr[16], rd[16];
+    float4 qprev;
+    load_ops(0, o[0]);
+#pragma unroll
+    for (int g = 0; g < TT / 16; ++g) {
+      if (g + 1 < TT / 16) load_ops(16 * (g + 1), o[(g + 1) & 1]);
+      wide_steps<0>(h, a2, o[g & 1].q.x, o[g & 1].q.y, o[g & 1].Bv, o[g & 1].Cv, pr);
+      if (g > 0) finish(16 * (g - 1), qprev, rd);
+      park_and_fetch(pr, rd);
+      qprev = o[g & 1].q;
+    }
+    finish(TT - 16, qprev, rd);
+  };
+
+  if (t_begin < t_end) issue_loads(t_begin);
+  int64_t prev_t0 = -1;
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += TT) {
+    const int ns = (t_end - t0) < TT ? static_cast<int>(t_end - t0) : TT;
+    stage(t0);
+    if (prev_t0 >= 0) store_tile(prev_t0);
+    __syncthreads();
+    if (t0 + TT < t_end) issue_loads(t0 + TT);
+    if (ns == TT) {
+      full_tile();
+    } else {
+      for (int t16 = 0; t16 < ns; t16 += 16) group(t16);
+    }
+    __syncthreads();
+    prev_t0 = t0;
+    if constexpr (MODE == kFixup) {
+      // state n's carried-in part is exp2(a2 * sum(delta)) * h_in; done once it is 0 in fp32
+      const float Srow = row_sum(S);
+      const bool lane_done = !cvalid || h_in == 0.f ||
+                             (!never_exit && a2 < 0.f && a2 * Srow + __log2f(fabsf(h_in)) < -150.f);
+      if (__syncthreads_and(lane_done)) break;
+    }
+  }
+  if (prev_t0 >= 0) store_tile(prev_t0);
+
+  if constexpr (MODE == kSingle) {
+    if (p.final_state != nullptr && cvalid) p.final_state[(b * dim + c) * 16 + n] = h;
+  } else if constexpr (MODE == kChunk) {
+    const float Srow = row_sum(S);
+    float ng = negseen;
+    ng = fmaxf(ng, dpp<0x128>(ng));
+    ng = fmaxf(ng, dpp<0x124>(ng));
+    ng = fmaxf(ng, dpp<0x122>(ng));
+    ng = fmaxf(ng, dpp<0x121>(ng));
+    if (cvalid) {
+      p.hend[((b * p.K + k) * dim + c) * 16 + n] = h;
+      if (n == 0) {
+        p.S[(b * p.K + k) * dim + c] = Srow;
+        p.neg[(b * p.K + k) * dim + c] = ng > 0.f ? 1 : 0;
+      }
+    }
+  }
+}
+
 // carry across chunks: one thread per (b, c, n)
 __global__ __launch_bounds__(256) void carry_kernel(KernelParams p) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -686,6 +959,37 @@ hipError_t launch_cfg(const KernelParams& kp, int64_t batch, hipStream_t stream)
   }
 }
 
+// the same three launches for the one-state-per-lane kernel
+template <int IO>
+hipError_t launch_wide(const KernelParams& kp, int64_t batch, hipStream_t stream) {
+  const dim3 block(kThreads);
+  if (kp.K == 1) {
+    const dim3 grid(static_cast<unsigned>(batch * kp.ngroups));
+    hipLaunchKernelGGL((wide_kernel<IO, kSingle>), grid, block, 0, stream, kp);
+    return hipGetLastError();
+  }
+  {
+    const dim3 grid(static_cast<unsigned>(batch * kp.K * kp.ngroups));
+    hipLaunchKernelGGL((wide_kernel<IO, kChunk>), grid, block, 0, stream, kp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    const int64_t total = batch * kp.dim * kp.N;
+    const dim3 grid(static_cast<unsigned>((total + 255) / 256));
+    hipLaunchKernelGGL(carry_kernel, grid, dim3(256), 0, stream, kp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    KernelParams kf = kp;
+    kf.chunk_offset = 1;
+    const dim3 grid(static_cast<unsigned>(batch * (kp.K - 1) * kp.ngroups));
+    hipLaunchKernelGGL((wide_kernel<IO, kFixup>), grid, block, 0, stream, kf);
+    return hipGetLastError();
+  }
+}
+
 template <int IO, int G, int NPL, bool FAST>
 hipError_t launch_vec(const KernelParams& kp, bool vec, int64_t batch, hipStream_t stream) {
   if constexpr (Geometry<IO, G, NPL, true, FAST>::VEC_OK) {
@@ -705,6 +1009,7 @@ hipError_t launch_generic(const KernelParams& kp, int npl, bool vec, int64_t bat
 
 template <int IO>
 hipError_t launch_io(const KernelParams& kp, int G, int npl, bool vec, int64_t batch, hipStream_t stream) {
+  if (G == 16 && kp.N == 16 && vec) return launch_wide<IO>(kp, batch, stream);
   if (kp.N <= 16) {
     switch (G) {
       case 1: return launch_vec<IO, 1, 16, true>(kp, vec, batch, stream);

@@ -73,7 +73,7 @@ def test_every_lane_split(M, G, io):
 
 
 @pytest.mark.parametrize("K", [2, 3, 7, 64])
-@pytest.mark.parametrize("G", [1, 4])
+@pytest.mark.parametrize("G", [1, 4, 16])
 def test_sequence_split(M, K, G):
     cfg = W.scan_config(2, 3001, 64, 16, io="bf16", cfg_id=402)
     inp = W.make_scan_inputs(cfg, with_h0=True)
@@ -81,14 +81,37 @@ def test_sequence_split(M, K, G):
     compare(M, inp, "bf16", f"K={K} G={G}", split_seq=K, split_state=G)
 
 
-def test_sequence_split_fp32_slow_decay(M):
+# one state per lane (16 lanes per channel): ragged lengths, partial channel groups, both I/O types,
+# single pass and sequence split
+WIDE = [
+    (1, 1, 16, "f32"),
+    (2, 17, 40, "bf16"),
+    (1, 65, 36, "f32"),
+    (3, 1000, 48, "bf16"),
+    (1, 64, 16, "bf16"),
+    (2, 129, 1536, "bf16"),
+]
+
+
+@pytest.mark.parametrize("K", [1, 3])
+@pytest.mark.parametrize("case", WIDE, ids=lambda c: "b{}_l{}_d{}_{}".format(*c))
+def test_one_state_per_lane(M, case, K):
+    b, l, d, io = case
+    cfg = W.scan_config(b, l, d, 16, io=io, cfg_id=420 + l + d)
+    inp = W.make_scan_inputs(cfg, with_h0=True)
+    say("one state per lane", case, K)
+    compare(M, inp, io, f"wide {case} K={K}", split_seq=K, split_state=16)
+
+
+@pytest.mark.parametrize("G", [1, 16])
+def test_sequence_split_fp32_slow_decay(M, G):
     # small |A| and small delta: the carried-in state survives whole chunks, so the
     # rescan pass must cover them completely
     cfg = W.scan_config(1, 2000, 64, 16, io="f32", cfg_id=403)
     inp = W.make_scan_inputs(cfg, with_h0=True)
     inp.A[:] = -0.01
     inp.delta[:] = np.float32(0.01)
-    compare(M, inp, "f32", "slow decay K=5", split_seq=5, split_state=1)
+    compare(M, inp, "f32", f"slow decay K=5 G={G}", split_seq=5, split_state=G)
 
 
 def test_chunk_invariance(M):
@@ -123,15 +146,15 @@ def test_determinism_and_causality(M):
     import torch
     cfg = W.scan_config(2, 2500, 64, 16, io="bf16", cfg_id=406)
     inp = W.make_scan_inputs(cfg, with_h0=True)
-    for K in (1, 4):
-        o1, f1 = run_gpu(M, inp, split_seq=K, split_state=1)
-        o2, f2 = run_gpu(M, inp, split_seq=K, split_state=1)
+    for K, G in ((1, 1), (4, 1), (1, 16), (4, 16)):
+        o1, f1 = run_gpu(M, inp, split_seq=K, split_state=G)
+        o2, f2 = run_gpu(M, inp, split_seq=K, split_state=G)
         assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(f1, f2), "run-to-run bitwise"
         t0 = 1777
         x2 = inp.x.copy()
         x2[:, t0] = W.f32_to_bf16_bits(W.bf16_bits_to_f32(x2[:, t0]) + np.float32(1.0))
         p = W.ScanInputs(x2, inp.delta, inp.A, inp.B, inp.C, inp.D, inp.z, inp.h0, "bf16")
-        o3, _ = run_gpu(M, p, split_seq=K, split_state=1)
+        o3, _ = run_gpu(M, p, split_seq=K, split_state=G)
         assert torch.equal(o3[:, :t0].view(torch.int16), o1[:, :t0].view(torch.int16)), f"K={K}: outputs before t0 changed"
         assert not (o3[:, t0] == o1[:, t0]).all()
 
@@ -142,9 +165,9 @@ def test_pins_on_gpu(M):
     inp = W.make_scan_inputs(cfg, with_h0=True)
     # delta == 0 leaves the state bitwise unchanged, also across a sequence split
     z0 = W.ScanInputs(inp.x, np.zeros_like(inp.delta), inp.A, inp.B, inp.C, inp.D, inp.z, inp.h0, "f32")
-    for K in (1, 3):
-        _, f = run_gpu(M, z0, split_seq=K, split_state=1)
-        assert np.array_equal(f.cpu().numpy(), inp.h0), f"delta=0 must keep h0 (K={K})"
+    for K, G in ((1, 1), (3, 1), (1, 16), (3, 16)):
+        _, f = run_gpu(M, z0, split_seq=K, split_state=G)
+        assert np.array_equal(f.cpu().numpy(), inp.h0), f"delta=0 must keep h0 (K={K}, G={G})"
     # z == 0 gates everything to exactly 0
     g0 = W.ScanInputs(inp.x, inp.delta, inp.A, inp.B, inp.C, inp.D, np.zeros_like(inp.z), inp.h0, "f32")
     o, _ = run_gpu(M, g0)

@@ -10,19 +10,31 @@
 // s_t = sum_{r<=t} l_r:
 //   y_t   = exp(s_t) C_t . S_in  +  sum_{s<=t} (C_t . B_s) exp(s_t - s_s) delta_s x_s
 //   S_out = exp(s_Q) S_in + sum_s exp(s_Q - s_s) delta_s x_s (x) B_s
-// One workgroup (4 waves) owns one (b, h, 64-wide headdim slice) and walks
-// the sequence in 64-step blocks; its fp32 state stays in MFMA accumulators
-// the whole time (never written to HBM).  Per block:
-//   G  = C . B^T            (64 x 64, K = N)      v_mfma_f32_16x16x32_bf16
-//   M  = G o exp2(s_t - s_s) o delta_s, causal    VALU, bf16 into LDS
-//   Y  = exp2(s_t) (C . S^T) + M . X              (64 x 64, K = N then 64)
-//   S  = exp2(s_Q) S + Xw^T . B                   (64 x N, K = 64)
+//
+// One workgroup (8 waves) owns one (b, h, 64-wide headdim slice) and walks the
+// sequence in 64-step blocks.  Wave w holds headdim rows 16*(w%4).. of the
+// state for one half of the states (n < NP/2 or n >= NP/2), transposed,
+// S^T[n, p], in MFMA accumulators for the whole sequence; the state is never
+// written to memory except as final_state.  Per block (v_mfma_f32_16x16x32_bf16
+// throughout; base-2 exponents, A pre-scaled by log2 e):
+//   G^T = B . C^T         (s x t, K = N; the 10 causal 16x16 tiles dealt out
+//                          over the waves)
+//   M   = G o exp2(s_t - s_s) o delta_s  ->  LDS, bf16 hi/lo pair, [t][s]
+//   Y^T = exp2(s_t) (S . C^T) + X^T . M^T (p x t; each wave of a pair reads
+//                          out its half of the states and the pair adds the
+//                          two partial sums through LDS)
+//   S^T = exp2(s_Q) S^T + B^T . Xw        (n x p, K = s)
+// An MFMA sums over its 32 k slots in any order.  Every operand here lists
+// its k values in the accumulator's row order -- lane group q (lane / 16) of a
+// 32-wide k block holds k = 4q..4q+3 and 16+4q..16+4q+3 -- so a pair of
+// 16x16 state accumulators is directly an operand fragment, and the LDS
+// copies of B, C, x and M are stored with their k axis permuted the same way
+// so that each fragment is one 16-byte read (row strides keep those reads
+// free of bank conflicts).
 // x, B and C enter the matrix cores exactly (they are bf16 inputs).  The three
-// computed operands -- the state copy S, the decayed mask M and the weighted
-// inputs Xw -- are each split into a bf16 pair hi + lo (hi = bf16(v),
-// lo = bf16(v - hi)), so the products see ~16 mantissa bits and the result
-// stays at fp32-state accuracy; the state itself stays fp32 in the
-// accumulators.  Exponents use base 2 with A pre-scaled by log2 e.
+// computed operands -- the state, the decayed mask M and the weighted inputs
+// Xw -- are each split into hi = bf16(v), lo = bf16(v - hi), so the products
+// see about 16 significant bits and the result keeps fp32-state accuracy.
 // A chunk length of 128 or 256 steps is evaluated as 2 or 4 consecutive
 // 64-step blocks with the state carried between them (the same algebra).
 #include <type_traits>
@@ -34,22 +46,37 @@ namespace {
 
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr int kWave = 64;
-constexpr int kThreads = 256;
+constexpr int kWaves = 8;
+constexpr int kThreads = kWave * kWaves;
 constexpr int QB = 64;     // steps per block
 constexpr int PB = 64;     // headdim slice per workgroup
-constexpr int PAD = 8;     // bf16 padding per LDS row (keeps 16-byte reads conflict-free)
+constexpr int PAD = 8;     // bf16 padding per LDS row: row strides of 4 (mod 8) dwords
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ float bf2f(uint16_t v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
-__device__ __forceinline__ uint16_t f2bf(float v) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v)); }
 __device__ __forceinline__ float exp2_hw(float v) { return __builtin_amdgcn_exp2f(v); }
-// v = hi + lo with both parts bf16 (about 16 significant bits together)
-__device__ __forceinline__ void split_bf(float v, uint16_t& hi, uint16_t& lo) {
-  hi = f2bf(v);
-  lo = f2bf(v - bf2f(hi));
+// two floats -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+__device__ __forceinline__ float lo_f(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_f(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// 8 floats -> bf16 hi/lo fragments (v = hi + lo to about 16 significant bits)
+__device__ __forceinline__ void split8(const float (&v)[8], bf16x8& hi, bf16x8& lo) {
+  u32x4 h, l;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[i] = pack2(v[2 * i], v[2 * i + 1]);
+    l[i] = pack2(v[2 * i] - lo_f(h[i]), v[2 * i + 1] - hi_f(h[i]));
+  }
+  hi = __builtin_bit_cast(bf16x8, h);
+  lo = __builtin_bit_cast(bf16x8, l);
 }
 
 __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
@@ -57,8 +84,20 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const 
 }
 
 // 8 consecutive bf16 from LDS (16-byte aligned)
-__device__ __forceinline__ bf16x8 lds8(const uint16_t* p) {
+__device__ __forceinline__ bf16x8 frag(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+// k-axis permutation inside a 32-wide block: natural k -> stored position.
+// Stored positions 8q..8q+7 hold k = 4q..4q+3 and 16+4q..16+4q+3.
+__device__ __forceinline__ int kpos(int k) {
+  const int r = k & 31;
+  return (k & ~31) + (r < 16 ? 8 * (r >> 2) + (r & 3) : 8 * ((r - 16) >> 2) + 4 + (r & 3));
+}
+// stored position -> natural k
+__device__ __forceinline__ int knat(int pos) {
+  const int r = pos & 31, q = r >> 3, j = r & 7;
+  return (pos & ~31) + (j < 4 ? 4 * q + j : 16 + 4 * q + (j - 4));
 }
 
 struct SSDParams {
@@ -76,33 +115,39 @@ struct SSDParams {
   int nps;   // headdim slices per head (P / 64)
 };
 
-// MFMA fragment layout (16x16x32): A row / B column = lane % 16, k = 8 * (lane / 16) + q;
-// accumulator element v of a lane is row 4 * (lane / 16) + v, column lane % 16.
+// MFMA 16x16x32 lane layout: A row / B column = lane % 16 with the k slots of
+// lane group lane / 16 as above; accumulator element v of a lane is row
+// 4 * (lane / 16) + v, column lane % 16.
 template <int NP>
 __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
-  constexpr int NS = NP + PAD;        // row stride of [*, NP] arrays
-  constexpr int QS = QB + PAD;        // row stride of [*, 64] arrays
-  constexpr int NT = NP / 16;         // 16-wide state tiles
-  constexpr int CPR = NP / 8;         // 16-byte chunks per padded B/C row
+  static_assert(NP % 64 == 0, "each wave of a pair holds whole 32-wide k blocks of the state");
+  constexpr int NS = NP + PAD;        // row stride of [*, NP] arrays (bf16)
+  constexpr int QS = QB + PAD;        // row stride of [*, 64] arrays (bf16)
+  constexpr int NTH = NP / 32;        // 16-row state tiles per wave (half of the states)
+  constexpr int NKH = NP / 64;        // 32-wide k blocks per half
 
-  __shared__ __attribute__((aligned(16))) uint16_t Cs[QB * NS];    // C block  [t][n]
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[QB * NS];    // B block  [s][n]
-  __shared__ __attribute__((aligned(16))) uint16_t BT[NP * QS];    // B block  [n][s]
-  __shared__ __attribute__((aligned(16))) uint16_t Xs[QB * QS];    // x block  [s][p]
-  __shared__ __attribute__((aligned(16))) uint16_t XT[PB * QS];    // x block  [p][s]
-  __shared__ __attribute__((aligned(16))) uint16_t Ys[QB * QS];    // outputs of the previous block [t][p]
-  __shared__ __attribute__((aligned(16))) uint16_t Ms[2][QB * QS];  // decayed causal C.B^T [t][s], hi/lo
-  __shared__ __attribute__((aligned(16))) uint16_t Xw[2][PB * QS];  // exp2(s_Q - s_s) delta_s x_s [p][s], hi/lo
-  __shared__ __attribute__((aligned(16))) uint16_t Sb[2][PB * NS];  // state [p][n], hi/lo
-  __shared__ float dls[QB];   // delta
-  __shared__ float css[QB];   // inclusive sum of delta * A * log2 e
+  __shared__ __attribute__((aligned(16))) uint16_t Cs[QB * NS];       // C      [t][kpos(n)]
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[QB * NS];       // B      [s][kpos(n)]
+  __shared__ __attribute__((aligned(16))) uint16_t BT[NP * QS];       // B      [n][kpos(s)]
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[QB * QS];       // x      [s][p]
+  __shared__ __attribute__((aligned(16))) uint16_t XT[PB * QS];       // x      [p][kpos(s)]
+  __shared__ __attribute__((aligned(16))) uint16_t Zs[QB * QS];       // z      [t][p]
+  __shared__ __attribute__((aligned(16))) uint16_t Ys[QB * QS];       // outputs of the previous block [t][p]
+  __shared__ __attribute__((aligned(16))) uint16_t Ms[2][QB * QS];    // decayed causal mask [t][kpos(s)], hi/lo
+  __shared__ __attribute__((aligned(16))) f32x4 Xc[kWaves * 2 * kWave];  // partial readouts handed to the pair partner
+  __shared__ __attribute__((aligned(16))) float css[QB];              // inclusive sum of delta * A * log2 e
+  __shared__ __attribute__((aligned(16))) float dls[QB];              // delta
+  __shared__ __attribute__((aligned(16))) float wls[QB];              // exp2(s_Q - s_s) * delta_s
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int w = tid / kWave;
-  const int lr = lane % 16;         // fragment row / column
-  const int lk = 8 * (lane / 16);   // fragment k offset
-  const int lq = 4 * (lane / 16);   // accumulator row offset
+  const int pt = w % 4;              // headdim tile of this wave
+  const int nh = w / 4;              // half of the states it holds
+  const int lc = lane % 16;          // fragment row / column
+  const int lg = lane / 16;          // lane group
+  const int l8 = 8 * lg;             // fragment offset in a stored 32-block
+  const int lq = 4 * lg;             // accumulator row offset
 
   // block -> (b, g, head within group, headdim slice); all blocks of one (b, g)
   // share an XCD when batch*groups is a multiple of 8 (B/C then stay in that L2)
@@ -117,125 +162,187 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
   const int64_t L = p.L, H = p.H, P = p.P, N = p.N, G = p.G;
   const float a2 = p.A[h] * kLog2e;
   const float Dh = p.D != nullptr ? p.D[h] : 0.f;
+  const bool has_z = p.z != nullptr;
   const int Ni = static_cast<int>(N);
   const int cpr = Ni / 8;             // 16-byte chunks per B/C row in memory
 
-  // zero the padded state columns of C/B/B^T/S (never written afterwards)
-  for (int e = tid; e < QB * NS; e += kThreads) {
-    if ((e % NS) >= Ni) { Cs[e] = 0; Bs[e] = 0; }
-  }
+  // B/C columns past N stay zero; so do the mask tiles above the diagonal
+  // (read as part of 32-wide k blocks, never computed)
+  for (int e = tid; e < QB * NS; e += kThreads) { Cs[e] = 0; Bs[e] = 0; }
+  for (int e = tid; e < 2 * QB * QS; e += kThreads) (&Ms[0][0])[e] = 0;
+  __syncthreads();   // before any staging write lands on a zeroed element
 
-  // ---- state: wave w owns headdim rows [16w, 16w+16) x all NP columns ----
-  f32x4 S[NT];
+  // ---- state S^T: columns p = 16 pt + lc, rows n = NP/2 nh + 16 i + lq + v ----
+  const int64_t prow = p0 + 16 * pt + lc;
+  const int nbase = (NP / 2) * nh;
+  f32x4 S[NTH];
 #pragma unroll
-  for (int c = 0; c < NT; ++c) {
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t pp = p0 + 16 * w + lq + v, n = 16 * c + lr;
-      S[c][v] = (p.h0 != nullptr && n < N) ? p.h0[((b * H + h) * P + pp) * N + n] : 0.f;
+  for (int i = 0; i < NTH; ++i) {
+    const int n0 = nbase + 16 * i + lq;
+    if (p.h0 != nullptr && n0 < Ni) {
+      const float4 v = *reinterpret_cast<const float4*>(&p.h0[((b * H + h) * P + prow) * N + n0]);
+      S[i] = f32x4{v.x, v.y, v.z, v.w};
+    } else {
+      S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
-  auto write_state_bf16 = [&]() {
-#pragma unroll
-    for (int c = 0; c < NT; ++c)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int e = (16 * w + lq + v) * NS + 16 * c + lr;
-        split_bf(S[c][v], Sb[0][e], Sb[1][e]);
-      }
-  };
-  write_state_bf16();
 
-  // ---- prefetch registers for one block ----
-  constexpr int BCL = (QB * CPR + kThreads - 1) / kThreads;   // B (and C) 16-byte loads per thread
-  constexpr int XL = QB * (PB / 8) / kThreads;                 // x loads per thread (2)
-  u32x4 breg[BCL], creg[BCL], xreg[XL];
+  // ---- global -> registers, one block ahead ----
+  // pointers to step 0 of this (b, g) / (b, h, slice); per-thread offsets are loop invariant
+  const uint16_t* const Bg = p.B + (b * L * G + g) * N;
+  const uint16_t* const Cg = p.C + (b * L * G + g) * N;
+  const uint16_t* const xg = p.x + (b * L * H + h) * P + p0;
+  const uint16_t* const zg = (has_z ? p.z : p.x) + (b * L * H + h) * P + p0;
+  const uint16_t* const dg = p.delta + b * L * H + h;
+  const int bc_row = static_cast<int>(G * N);   // elements between consecutive steps
+  const int x_row = static_cast<int>(H * P);
+  constexpr int BCL = (QB * NP / 8 + kThreads - 1) / kThreads;   // B (and C) 16-byte loads per thread
+  int bc_r[BCL], bc_c[BCL];
+#pragma unroll
+  for (int i = 0; i < BCL; ++i) {
+    const int ci = i * kThreads + tid;
+    const bool live = ci < QB * cpr;
+    bc_r[i] = live ? ci / cpr : -1;
+    bc_c[i] = live ? 8 * (ci % cpr) : 0;
+  }
+  const int x_r = tid / (PB / 8), x_c = 8 * (tid % (PB / 8));   // one 16-byte x (and z) piece per thread
+  u32x4 breg[BCL], creg[BCL], xreg, zreg;
   uint16_t dreg = 0;
 
   auto issue_loads = [&](int64_t t0, int nvalid) {
-    // B, C: rows of N bf16 (group g)
+    const int64_t tb = t0;
 #pragma unroll
     for (int i = 0; i < BCL; ++i) {
-      const int ci = i * kThreads + tid;
-      int r = ci / cpr, c8 = ci - (ci / cpr) * cpr;
-      if (ci >= QB * cpr) { r = 0; c8 = 0; }
-      const int rr = r < nvalid ? r : nvalid - 1;
-      const int64_t off = ((b * L + t0 + rr) * G + g) * N + 8 * c8;
-      breg[i] = *reinterpret_cast<const u32x4*>(p.B + off);
-      creg[i] = *reinterpret_cast<const u32x4*>(p.C + off);
+      const int r = bc_r[i] < 0 ? 0 : (bc_r[i] < nvalid ? bc_r[i] : nvalid - 1);
+      const int64_t off = (tb + r) * bc_row + bc_c[i];
+      breg[i] = *reinterpret_cast<const u32x4*>(Bg + off);
+      creg[i] = *reinterpret_cast<const u32x4*>(Cg + off);
     }
-#pragma unroll
-    for (int i = 0; i < XL; ++i) {
-      const int ci = i * kThreads + tid;
-      const int r = ci / (PB / 8), c8 = ci % (PB / 8);
-      const int rr = r < nvalid ? r : nvalid - 1;
-      xreg[i] = *reinterpret_cast<const u32x4*>(p.x + ((b * L + t0 + rr) * H + h) * P + p0 + 8 * c8);
-    }
-    if (tid < QB) {
-      const int rr = tid < nvalid ? tid : nvalid - 1;
-      dreg = p.delta[(b * L + t0 + rr) * H + h];
-    }
+    const int r = x_r < nvalid ? x_r : nvalid - 1;
+    const int64_t off = (tb + r) * x_row + x_c;
+    xreg = *reinterpret_cast<const u32x4*>(xg + off);
+    zreg = *reinterpret_cast<const u32x4*>(zg + off);
+    if (tid < QB) dreg = dg[(tb + (tid < nvalid ? tid : nvalid - 1)) * H];
   };
 
-  // registers -> LDS, row-major (16-byte writes); rows past the end are zero
+  // registers -> LDS (rows past the end are zero); wave 0 also forms the block's decay sums
   auto stage = [&](int nvalid) {
 #pragma unroll
     for (int i = 0; i < BCL; ++i) asm volatile("" : "+v"(breg[i]), "+v"(creg[i]));
-#pragma unroll
-    for (int i = 0; i < XL; ++i) asm volatile("" : "+v"(xreg[i]));
+    asm volatile("" : "+v"(xreg), "+v"(zreg));
 #pragma unroll
     for (int i = 0; i < BCL; ++i) {
-      const int ci = i * kThreads + tid;
-      if (ci < QB * cpr) {
-        const int r = ci / cpr, c8 = ci - (ci / cpr) * cpr;
-        const bool ok = r < nvalid;
-        *reinterpret_cast<u32x4*>(&Bs[r * NS + 8 * c8]) = ok ? breg[i] : u32x4{0, 0, 0, 0};
-        *reinterpret_cast<u32x4*>(&Cs[r * NS + 8 * c8]) = ok ? creg[i] : u32x4{0, 0, 0, 0};
+      if (bc_r[i] >= 0) {
+        const bool ok = bc_r[i] < nvalid;
+        const u32x4 bv = ok ? breg[i] : u32x4{0, 0, 0, 0};
+        const u32x4 cv = ok ? creg[i] : u32x4{0, 0, 0, 0};
+        // 8 consecutive n = two aligned groups of 4, each contiguous once permuted
+        const int o = bc_r[i] * NS;
+        const int k0 = kpos(bc_c[i]), k1 = kpos(bc_c[i] + 4);
+        *reinterpret_cast<u32x2*>(&Bs[o + k0]) = u32x2{bv[0], bv[1]};
+        *reinterpret_cast<u32x2*>(&Bs[o + k1]) = u32x2{bv[2], bv[3]};
+        *reinterpret_cast<u32x2*>(&Cs[o + k0]) = u32x2{cv[0], cv[1]};
+        *reinterpret_cast<u32x2*>(&Cs[o + k1]) = u32x2{cv[2], cv[3]};
       }
     }
-#pragma unroll
-    for (int i = 0; i < XL; ++i) {
-      const int ci = i * kThreads + tid;
-      const int r = ci / (PB / 8), c8 = ci % (PB / 8);
-      *reinterpret_cast<u32x4*>(&Xs[r * QS + 8 * c8]) = r < nvalid ? xreg[i] : u32x4{0, 0, 0, 0};
+    {
+      const bool ok = x_r < nvalid;
+      *reinterpret_cast<u32x4*>(&Xs[x_r * QS + x_c]) = ok ? xreg : u32x4{0, 0, 0, 0};
+      if (has_z) *reinterpret_cast<u32x4*>(&Zs[x_r * QS + x_c]) = zreg;
     }
-    if (tid < QB) dls[tid] = tid < nvalid ? bf2f(dreg) : 0.f;
+    if (w == 0) {
+      const float d = lane < nvalid ? __uint_as_float(static_cast<uint32_t>(dreg) << 16) : 0.f;
+      float v = d * a2;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const float u = __shfl_up(v, off, kWave);
+        if (lane >= off) v += u;
+      }
+      const float cs_end = __shfl(v, kWave - 1, kWave);
+      css[lane] = v;
+      dls[lane] = d;
+      wls[lane] = exp2_hw(cs_end - v) * d;
+    }
   };
 
-  // transposed copies for the operands that need a column as k: consecutive
-  // lanes read consecutive columns (conflict-free) and write 16-byte rows
+  // B^T and x^T with the step axis permuted: a thread reads 2 adjacent columns
+  // of 8 consecutive rows (4-byte reads) and writes 2 rows of 8 steps
   auto transpose = [&]() {
+    auto one = [&](const uint16_t* src, int sstride, int c2, int rg, uint16_t* dst, int ra, int rb) {
+      uint32_t v[8];
 #pragma unroll
-    for (int i = 0; i < NP * (QB / 8) / kThreads; ++i) {
-      const int j = i * kThreads + tid;
-      const int n = j % NP, s8 = j / NP;
-      uint16_t v[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) v[q] = Bs[(8 * s8 + q) * NS + n];
-      *reinterpret_cast<u32x4*>(&BT[n * QS + 8 * s8]) = __builtin_bit_cast(u32x4, v);
+      for (int q = 0; q < 8; ++q) v[q] = *reinterpret_cast<const uint32_t*>(&src[(8 * rg + q) * sstride + c2]);
+      // low halves -> row ra, high halves -> row rb; steps 8rg..8rg+3 and 8rg+4..8rg+7
+      // land on two groups of 4 stored positions
+      const u32x2 a0 = {__builtin_amdgcn_perm(v[1], v[0], 0x05040100u), __builtin_amdgcn_perm(v[3], v[2], 0x05040100u)};
+      const u32x2 a1 = {__builtin_amdgcn_perm(v[5], v[4], 0x05040100u), __builtin_amdgcn_perm(v[7], v[6], 0x05040100u)};
+      const u32x2 b0 = {__builtin_amdgcn_perm(v[1], v[0], 0x07060302u), __builtin_amdgcn_perm(v[3], v[2], 0x07060302u)};
+      const u32x2 b1 = {__builtin_amdgcn_perm(v[5], v[4], 0x07060302u), __builtin_amdgcn_perm(v[7], v[6], 0x07060302u)};
+      const int s0 = kpos(8 * rg), s1 = kpos(8 * rg + 4);
+      *reinterpret_cast<u32x2*>(&dst[ra * QS + s0]) = a0;
+      *reinterpret_cast<u32x2*>(&dst[ra * QS + s1]) = a1;
+      *reinterpret_cast<u32x2*>(&dst[rb * QS + s0]) = b0;
+      *reinterpret_cast<u32x2*>(&dst[rb * QS + s1]) = b1;
+    };
+    // B: NP/2 stored column pairs x 8 row groups
+    for (int j = tid; j < (NP / 2) * 8; j += kThreads) {
+      const int cp = j % (NP / 2), rg = j / (NP / 2);
+      const int n = knat(2 * cp);   // stored pair (2cp, 2cp+1) holds natural n, n+1
+      one(Bs, NS, 2 * cp, rg, BT, n, n + 1);
     }
-#pragma unroll
-    for (int i = 0; i < PB * (QB / 8) / kThreads; ++i) {
-      const int j = i * kThreads + tid;
-      const int pp = j % PB, s8 = j / PB;
-      uint16_t v[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) v[q] = Xs[(8 * s8 + q) * QS + pp];
-      *reinterpret_cast<u32x4*>(&XT[pp * QS + 8 * s8]) = __builtin_bit_cast(u32x4, v);
+    // x: 32 column pairs x 8 row groups
+    for (int j = tid; j < (PB / 2) * 8; j += kThreads) {
+      const int cp = j % (PB / 2), rg = j / (PB / 2);
+      one(Xs, QS, 2 * cp, rg, XT, 2 * cp, 2 * cp + 1);
     }
   };
 
   // outputs of a finished block, 16-byte stores
+  uint16_t* const yg = p.out + (b * L * H + h) * P + p0;
   auto store_block = [&](int64_t t0, int nvalid) {
-#pragma unroll
-    for (int i = 0; i < XL; ++i) {
-      const int ci = i * kThreads + tid;
-      const int r = ci / (PB / 8), c8 = ci % (PB / 8);
-      if (r < nvalid)
-        *reinterpret_cast<u32x4*>(p.out + ((b * L + t0 + r) * H + h) * P + p0 + 8 * c8) =
-            *reinterpret_cast<const u32x4*>(&Ys[r * QS + 8 * c8]);
-    }
+    if (tid < QB * PB / 8 && x_r < nvalid)
+      *reinterpret_cast<u32x4*>(yg + (t0 + x_r) * x_row + x_c) = *reinterpret_cast<const u32x4*>(&Ys[x_r * QS + x_c]);
   };
+
+  // G^T tile (s-tile i, t-tile j) -> M[t][kpos(s)] hi/lo, 4 consecutive s per lane (8-byte writes)
+  auto mask_tile = [&](int i, int j) {
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k0 = 0; k0 < NP; k0 += 32)
+      acc = mfma16(frag(&Bs[(16 * i + lc) * NS + k0 + l8]), frag(&Cs[(16 * j + lc) * NS + k0 + l8]), acc);
+    const int t = 16 * j + lc;
+    const int s0 = 16 * i + lq;
+    const float ct = css[t];
+    const float4 cs4 = *reinterpret_cast<const float4*>(&css[s0]);
+    const float4 dl4 = *reinterpret_cast<const float4*>(&dls[s0]);
+    float m[4] = {acc[0] * exp2_hw(ct - cs4.x) * dl4.x, acc[1] * exp2_hw(ct - cs4.y) * dl4.y,
+                  acc[2] * exp2_hw(ct - cs4.z) * dl4.z, acc[3] * exp2_hw(ct - cs4.w) * dl4.w};
+    if (i == j) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) m[v] = (s0 + v <= t) ? m[v] : 0.f;
+    }
+    const uint32_t h01 = pack2(m[0], m[1]), h23 = pack2(m[2], m[3]);
+    const uint32_t l01 = pack2(m[0] - lo_f(h01), m[1] - hi_f(h01));
+    const uint32_t l23 = pack2(m[2] - lo_f(h23), m[3] - hi_f(h23));
+    const int sp = kpos(s0);
+    *reinterpret_cast<u32x2*>(&Ms[0][t * QS + sp]) = u32x2{h01, h23};
+    *reinterpret_cast<u32x2*>(&Ms[1][t * QS + sp]) = u32x2{l01, l23};
+  };
+
+  // causal mask tile of this wave besides (0,0) / (0,1) for waves 0 and 1
+  int mi = 3, mj = 3;
+  switch (w) {
+    case 0: mi = 1; mj = 1; break;
+    case 1: mi = 0; mj = 2; break;
+    case 2: mi = 1; mj = 2; break;
+    case 3: mi = 2; mj = 2; break;
+    case 4: mi = 0; mj = 3; break;
+    case 5: mi = 1; mj = 3; break;
+    case 6: mi = 2; mj = 3; break;
+    default: break;
+  }
+
+  const int partner = w ^ 4;   // the wave holding the other half of the states
 
   // ---- block loop ----
   const int64_t nblocks = (L + QB - 1) / QB;
@@ -251,126 +358,112 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
       issue_loads(t1, static_cast<int>((L - t1) < QB ? (L - t1) : QB));
     }
     transpose();
-    // inclusive in-block sum of delta * A * log2 e (wave 0)
-    if (w == 0) {
-      float v = dls[lane] * a2;
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const float u = __shfl_up(v, off, kWave);
-        if (lane >= off) v += u;
-      }
-      css[lane] = v;
-    }
-    __syncthreads();
-    const float cs_end = css[QB - 1];
-
-    // G = C . B^T for t-tile w (4 s-tiles), then M = decayed causal G -> LDS
-    {
-      f32x4 Gacc[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) Gacc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k0 = 0; k0 < NP; k0 += 32) {
-        const bf16x8 a = lds8(&Cs[(16 * w + lr) * NS + k0 + lk]);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          if (c <= w) Gacc[c] = mfma16(a, lds8(&Bs[(16 * c + lr) * NS + k0 + lk]), Gacc[c]);
-        }
-      }
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int s = 16 * c + lr;
-        const float css_s = css[s], dl_s = dls[s];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int t = 16 * w + lq + v;
-          const float m = (c <= w && s <= t) ? Gacc[c][v] * exp2_hw(css[t] - css_s) * dl_s : 0.f;
-          split_bf(m, Ms[0][t * QS + s], Ms[1][t * QS + s]);
-        }
-      }
-    }
-    // Xw[p][s] = exp2(s_Q - s_s) delta_s x[s][p]
-#pragma unroll
-    for (int i = 0; i < PB * QB / kThreads; ++i) {
-      const int e = i * kThreads + tid;
-      const int pp = e / QB, s = e % QB;
-      const float wgt = exp2_hw(cs_end - css[s]) * dls[s];
-      split_bf(wgt * bf2f(XT[pp * QS + s]), Xw[0][pp * QS + s], Xw[1][pp * QS + s]);
-    }
+    // the 10 causal tiles (i <= j): waves 0 and 1 take two, the others one
+    if (w < 2) mask_tile(0, w);
+    mask_tile(mi, mj);
     __syncthreads();
 
-    // Y for t-tile w, 4 headdim tiles
-    {
-      f32x4 Y[4];
+    // state fragments of this wave's half (operand A of the readout: rows p, k = n)
+    bf16x8 sh[NKH], sl[NKH];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) Y[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k0 = 0; k0 < NP; k0 += 32) {
-        const bf16x8 a = lds8(&Cs[(16 * w + lr) * NS + k0 + lk]);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          Y[c] = mfma16(a, lds8(&Sb[0][(16 * c + lr) * NS + k0 + lk]), Y[c]);
-          Y[c] = mfma16(a, lds8(&Sb[1][(16 * c + lr) * NS + k0 + lk]), Y[c]);
-        }
-      }
-      float rs[4];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) rs[v] = exp2_hw(css[16 * w + lq + v]);
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) Y[c][v] *= rs[v];
-#pragma unroll
-      for (int s0 = 0; s0 < QB; s0 += 32) {
-        if (s0 <= 16 * w + 15) {
-          const bf16x8 ah = lds8(&Ms[0][(16 * w + lr) * QS + s0 + lk]);
-          const bf16x8 al = lds8(&Ms[1][(16 * w + lr) * QS + s0 + lk]);
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const bf16x8 bx = lds8(&XT[(16 * c + lr) * QS + s0 + lk]);
-            Y[c] = mfma16(ah, bx, Y[c]);
-            Y[c] = mfma16(al, bx, Y[c]);
-          }
-        }
-      }
-      // epilogue: + D x, * silu(z), store
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int pl = 16 * c + lr;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int t = 16 * w + lq + v;
-          float y = Y[c][v] + Dh * bf2f(Xs[t * QS + pl]);
-          if (p.z != nullptr && t < nvalid) {
-            const float zz = bf2f(p.z[((b * L + t0 + t) * H + h) * P + p0 + pl]);
-            y *= zz * __builtin_amdgcn_rcpf(1.f + exp2_hw(-zz * kLog2e));
-          }
-          Ys[t * QS + pl] = f2bf(y);
-        }
-      }
+    for (int m = 0; m < NKH; ++m) {
+      const float v[8] = {S[2 * m][0], S[2 * m][1], S[2 * m][2], S[2 * m][3],
+                          S[2 * m + 1][0], S[2 * m + 1][1], S[2 * m + 1][2], S[2 * m + 1][3]};
+      split8(v, sh[m], sl[m]);
     }
+    // x^T fragments of this wave's rows (operand A of X^T M^T; operand B of the update once weighted)
+    bf16x8 xf[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) xf[m] = frag(&XT[(16 * pt + lc) * QS + 32 * m + l8]);
 
-    // state: S = exp2(s_Q) S + Xw^T B  (rows 16w.. of headdim, all NP columns)
-    {
-      const float dec = exp2_hw(cs_end);
+    // partial Y^T tiles (rows p = 16pt + lq + v, column t = 16j + lc), the hand-over of
+    // the partner's two tiles and the state update; the half nh is a compile-time
+    // constant inside so that tile indices never need run-time selection
+    f32x4 Y[4];
+    auto readout = [&](auto half) {
+      constexpr int NH = decltype(half)::value;
+      constexpr int JA = NH == 0 ? 0 : 1, JB = NH == 0 ? 3 : 2;    // tiles this wave finishes
+      constexpr int JO0 = NH == 0 ? 1 : 0, JO1 = NH == 0 ? 2 : 3;  // tiles the partner finishes
+      constexpr int NB = (NP / 2) * NH;
 #pragma unroll
-      for (int c = 0; c < NT; ++c)
+      for (int j = 0; j < 4; ++j) {
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int v = 0; v < 4; ++v) S[c][v] *= dec;
+        for (int m = 0; m < NKH; ++m) {
+          const bf16x8 cf = frag(&Cs[(16 * j + lc) * NS + NB + 32 * m + l8]);
+          acc = mfma16(sh[m], cf, acc);
+          acc = mfma16(sl[m], cf, acc);
+        }
+        const float e = exp2_hw(css[16 * j + lc]);
 #pragma unroll
-      for (int s0 = 0; s0 < QB; s0 += 32) {
-        const bf16x8 ah = lds8(&Xw[0][(16 * w + lr) * QS + s0 + lk]);
-        const bf16x8 al = lds8(&Xw[1][(16 * w + lr) * QS + s0 + lk]);
+        for (int v = 0; v < 4; ++v) acc[v] *= e;
+        if (j == JA || j == JB) {
 #pragma unroll
-        for (int c = 0; c < NT; ++c) {
-          const bf16x8 bb = lds8(&BT[(16 * c + lr) * QS + s0 + lk]);
-          S[c] = mfma16(ah, bb, S[c]);
-          S[c] = mfma16(al, bb, S[c]);
+          for (int m = 0; m < 2; ++m) {
+            if (32 * m <= 16 * j + 15) {
+              acc = mfma16(xf[m], frag(&Ms[0][(16 * j + lc) * QS + 32 * m + l8]), acc);
+              acc = mfma16(xf[m], frag(&Ms[1][(16 * j + lc) * QS + 32 * m + l8]), acc);
+            }
+          }
+        }
+        Y[j] = acc;
+      }
+      Xc[(w * 2 + 0) * kWave + lane] = Y[JO0];
+      Xc[(w * 2 + 1) * kWave + lane] = Y[JO1];
+
+      // state update of this half: S^T = exp2(s_Q) S^T + B^T Xw  (K = s)
+      const float dec = exp2_hw(css[QB - 1]);
+#pragma unroll
+      for (int i = 0; i < NTH; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) S[i][v] *= dec;
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const float4 w0 = *reinterpret_cast<const float4*>(&wls[32 * m + lq]);
+        const float4 w1 = *reinterpret_cast<const float4*>(&wls[32 * m + 16 + lq]);
+        const u32x4 xr = __builtin_bit_cast(u32x4, xf[m]);
+        const float xw[8] = {lo_f(xr[0]) * w0.x, hi_f(xr[0]) * w0.y, lo_f(xr[1]) * w0.z, hi_f(xr[1]) * w0.w,
+                             lo_f(xr[2]) * w1.x, hi_f(xr[2]) * w1.y, lo_f(xr[3]) * w1.z, hi_f(xr[3]) * w1.w};
+        bf16x8 xh, xl;
+        split8(xw, xh, xl);
+#pragma unroll
+        for (int i = 0; i < NTH; ++i) {
+          const bf16x8 bf = frag(&BT[(NB + 16 * i + lc) * QS + 32 * m + l8]);
+          S[i] = mfma16(bf, xh, S[i]);
+          S[i] = mfma16(bf, xl, S[i]);
         }
       }
-    }
-    __syncthreads();      // every wave is done with this block's LDS (including the old Sb)
-    write_state_bf16();
+    };
+    if (nh == 0) readout(std::integral_constant<int, 0>{});
+    else readout(std::integral_constant<int, 1>{});
+    __syncthreads();
+
+    // finish two t-tiles: own partial + partner's, then + D x, * silu(z)
+    auto finish = [&](auto half) {
+      constexpr int NH = decltype(half)::value;
+      constexpr int JA = NH == 0 ? 0 : 1, JB = NH == 0 ? 3 : 2;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int j = k == 0 ? JA : JB;
+        const f32x4 o = Xc[(partner * 2 + k) * kWave + lane];
+        const int t = 16 * j + lc;
+        const int pl = 16 * pt + lq;
+        const u32x2 xv = *reinterpret_cast<const u32x2*>(&Xs[t * QS + pl]);
+        const f32x4 yj = Y[k == 0 ? JA : JB];
+        float y[4] = {yj[0] + o[0] + Dh * lo_f(xv[0]), yj[1] + o[1] + Dh * hi_f(xv[0]),
+                      yj[2] + o[2] + Dh * lo_f(xv[1]), yj[3] + o[3] + Dh * hi_f(xv[1])};
+        if (has_z) {
+          const u32x2 zv = *reinterpret_cast<const u32x2*>(&Zs[t * QS + pl]);
+          const float zz[4] = {lo_f(zv[0]), hi_f(zv[0]), lo_f(zv[1]), hi_f(zv[1])};
+#pragma unroll
+          for (int v = 0; v < 4; ++v) y[v] *= zz[v] * __builtin_amdgcn_rcpf(1.f + exp2_hw(-zz[v] * kLog2e));
+        }
+        *reinterpret_cast<u32x2*>(&Ys[t * QS + pl]) = u32x2{pack2(y[0], y[1]), pack2(y[2], y[3])};
+      }
+    };
+    if (nh == 0) finish(std::integral_constant<int, 0>{});
+    else finish(std::integral_constant<int, 1>{});
+    __syncthreads();      // every wave is done with this block's LDS
   }
 
   if (nblocks > 0) {
@@ -380,12 +473,12 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
 
   if (p.final_state != nullptr) {
 #pragma unroll
-    for (int c = 0; c < NT; ++c)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int64_t pp = p0 + 16 * w + lq + v, n = 16 * c + lr;
-        if (n < N) p.final_state[((b * H + h) * P + pp) * N + n] = S[c][v];
-      }
+    for (int i = 0; i < NTH; ++i) {
+      const int n0 = nbase + 16 * i + lq;
+      if (n0 < Ni)
+        *reinterpret_cast<float4*>(&p.final_state[((b * H + h) * P + prow) * N + n0]) =
+            float4{S[i][0], S[i][1], S[i][2], S[i][3]};
+    }
   }
 }
 
@@ -416,7 +509,6 @@ hipError_t ssd_launch(const SSDArgs& a, hipStream_t stream) {
   sp.final_state = a.final_state;
   sp.batch = a.batch; sp.L = a.L; sp.H = a.H; sp.P = a.P; sp.N = a.N; sp.G = a.G;
   sp.nps = static_cast<int>(a.P / PB);
-  if (a.N <= 32) return launch_np<32>(sp, stream);
   if (a.N <= 64) return launch_np<64>(sp, stream);
   return launch_np<128>(sp, stream);
 }

@@ -100,7 +100,8 @@ typedef struct {
  * blocks with the state carried between them (the same algebra, so only
  * rounding differs).  io_dtype must be MSSM_BF16 (the matrix cores take bf16
  * operands).  headdim must be a multiple of 64; dstate a multiple of 16 and
- * at most 128.  The state never leaves the chip between blocks. */
+ * at most 128; nheads * headdim and ngroups * dstate below 2^24.  The state
+ * never leaves the chip between blocks. */
 typedef struct {
     int64_t batch, seqlen, nheads, headdim, dstate, ngroups, chunk;
     int32_t io_dtype;

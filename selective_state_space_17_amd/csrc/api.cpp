@@ -223,6 +223,8 @@ static int validate_ssd_desc(const mssm_ssd_desc* d, int64_t* Q) {
   if (d->io_dtype != MSSM_BF16) return MSSM_ERR_UNSUPPORTED;
   if (d->nheads % d->ngroups != 0) return MSSM_ERR_UNSUPPORTED;
   if (d->headdim % 64 != 0 || d->dstate % 16 != 0 || d->dstate > 128) return MSSM_ERR_UNSUPPORTED;
+  // per-step row strides are formed with 24-bit multiplies inside a 64-step block
+  if (d->nheads > (1 << 24) / d->headdim || d->ngroups > (1 << 24) / d->dstate) return MSSM_ERR_UNSUPPORTED;
   const int64_t q = d->chunk == 0 ? 64 : d->chunk;
   if (q != 64 && q != 128 && q != 256) return MSSM_ERR_UNSUPPORTED;
   int64_t t = 0;

@@ -88,6 +88,12 @@ __device__ __forceinline__ bf16x8 frag(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
 
+// DPP-moved copy of v (lanes outside the row mask, or whose source lane is out
+// of range, read 0)
+template <int CTRL, int ROW_MASK> __device__ __forceinline__ float dppf(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xf, true));
+}
+
 // k-axis permutation inside a 32-wide block: natural k -> stored position.
 // Stored positions 8q..8q+7 hold k = 4q..4q+3 and 16+4q..16+4q+3.
 __device__ __forceinline__ int kpos(int k) {
@@ -129,10 +135,10 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t Cs[QB * NS];       // C      [t][kpos(n)]
   __shared__ __attribute__((aligned(16))) uint16_t Bs[QB * NS];       // B      [s][kpos(n)]
   __shared__ __attribute__((aligned(16))) uint16_t BT[NP * QS];       // B      [n][kpos(s)]
-  __shared__ __attribute__((aligned(16))) uint16_t Xs[QB * QS];       // x      [s][p]
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[2][QB * QS];    // x      [s][p], double-buffered
   __shared__ __attribute__((aligned(16))) uint16_t XT[PB * QS];       // x      [p][kpos(s)]
-  __shared__ __attribute__((aligned(16))) uint16_t Zs[QB * QS];       // z      [t][p]
-  __shared__ __attribute__((aligned(16))) uint16_t Ys[QB * QS];       // outputs of the previous block [t][p]
+  __shared__ __attribute__((aligned(16))) uint16_t Zs[2][QB * QS];    // z      [t][p], double-buffered
+  __shared__ __attribute__((aligned(16))) uint16_t Ys[2][QB * QS];    // outputs [t][p], double-buffered
   __shared__ __attribute__((aligned(16))) uint16_t Ms[2][QB * QS];    // decayed causal mask [t][kpos(s)], hi/lo
   __shared__ __attribute__((aligned(16))) f32x4 Xc[kWaves * 2 * kWave];  // partial readouts handed to the pair partner
   __shared__ __attribute__((aligned(16))) float css[QB];              // inclusive sum of delta * A * log2 e
@@ -194,114 +200,143 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
   const uint16_t* const xg = p.x + (b * L * H + h) * P + p0;
   const uint16_t* const zg = (has_z ? p.z : p.x) + (b * L * H + h) * P + p0;
   const uint16_t* const dg = p.delta + b * L * H + h;
-  const int bc_row = static_cast<int>(G * N);   // elements between consecutive steps
-  const int x_row = static_cast<int>(H * P);
-  constexpr int BCL = (QB * NP / 8 + kThreads - 1) / kThreads;   // B (and C) 16-byte loads per thread
-  int bc_r[BCL], bc_c[BCL];
+  const int64_t bc_row = G * N;   // elements between consecutive steps
+  const int64_t x_row = H * P;
+  // B: thread -> (row pair rp, 8-wide chunk cb); a pair of rows lets the thread
+  // write the transposed copy B^T with 4-byte stores (two steps per store)
+  const int rp = tid % 32, cb = tid / 32;
+  const bool b_live = cb < cpr;
+  // C: thread -> (row, chunk), consecutive threads along a row
+  constexpr int CL = (QB * NP / 8 + kThreads - 1) / kThreads;
+  int c_r[CL], c_c[CL];
 #pragma unroll
-  for (int i = 0; i < BCL; ++i) {
+  for (int i = 0; i < CL; ++i) {
     const int ci = i * kThreads + tid;
     const bool live = ci < QB * cpr;
-    bc_r[i] = live ? ci / cpr : -1;
-    bc_c[i] = live ? 8 * (ci % cpr) : 0;
+    c_r[i] = live ? ci / cpr : -1;
+    c_c[i] = live ? 8 * (ci % cpr) : 0;
   }
-  const int x_r = tid / (PB / 8), x_c = 8 * (tid % (PB / 8));   // one 16-byte x (and z) piece per thread
-  u32x4 breg[BCL], creg[BCL], xreg, zreg;
+  // x (waves 0-3) and z (waves 4-7): thread -> (row pair xp, chunk xc)
+  const int xi = tid % 256, xp = xi % 32, xc = xi / 32;
+  const bool is_x = tid < 256;
+  const uint16_t* const vg = is_x ? xg : zg;
+  u32x4 b0reg, b1reg, creg[CL], v0reg, v1reg;
   uint16_t dreg = 0;
 
-  auto issue_loads = [&](int64_t t0, int nvalid) {
-    const int64_t tb = t0;
+  // element offsets from step 0 of a block (rows past the end of the sequence,
+  // in the last block only, are clamped to its last row)
+  auto offsets = [&](int nvalid, int (&ob)[2], int (&oc)[CL], int (&ov)[2]) {
+    auto rc = [&](int r) { return r < nvalid ? r : nvalid - 1; };
+    const int bcol = b_live ? 8 * cb : 0;
+    ob[0] = __umul24(rc(2 * rp), static_cast<int>(bc_row)) + bcol;
+    ob[1] = __umul24(rc(2 * rp + 1), static_cast<int>(bc_row)) + bcol;
 #pragma unroll
-    for (int i = 0; i < BCL; ++i) {
-      const int r = bc_r[i] < 0 ? 0 : (bc_r[i] < nvalid ? bc_r[i] : nvalid - 1);
-      const int64_t off = (tb + r) * bc_row + bc_c[i];
-      breg[i] = *reinterpret_cast<const u32x4*>(Bg + off);
-      creg[i] = *reinterpret_cast<const u32x4*>(Cg + off);
+    for (int i = 0; i < CL; ++i) oc[i] = __umul24(rc(c_r[i] < 0 ? 0 : c_r[i]), static_cast<int>(bc_row)) + c_c[i];
+    ov[0] = __umul24(rc(2 * xp), static_cast<int>(x_row)) + 8 * xc;
+    ov[1] = __umul24(rc(2 * xp + 1), static_cast<int>(x_row)) + 8 * xc;
+  };
+  int fb[2], fc[CL], fv[2];   // offsets of a full block
+  offsets(QB, fb, fc, fv);
+  auto issue_loads = [&](int64_t t0, int nvalid) {
+    int ob[2], oc[CL], ov[2];
+    if (nvalid == QB) {
+      ob[0] = fb[0]; ob[1] = fb[1]; ov[0] = fv[0]; ov[1] = fv[1];
+#pragma unroll
+      for (int i = 0; i < CL; ++i) oc[i] = fc[i];
+    } else {
+      offsets(nvalid, ob, oc, ov);
     }
-    const int r = x_r < nvalid ? x_r : nvalid - 1;
-    const int64_t off = (tb + r) * x_row + x_c;
-    xreg = *reinterpret_cast<const u32x4*>(xg + off);
-    zreg = *reinterpret_cast<const u32x4*>(zg + off);
-    if (tid < QB) dreg = dg[(tb + (tid < nvalid ? tid : nvalid - 1)) * H];
+    const uint16_t* const bt = Bg + t0 * bc_row;
+    const uint16_t* const ct = Cg + t0 * bc_row;
+    const uint16_t* const vt = vg + t0 * x_row;
+    b0reg = *reinterpret_cast<const u32x4*>(bt + ob[0]);
+    b1reg = *reinterpret_cast<const u32x4*>(bt + ob[1]);
+#pragma unroll
+    for (int i = 0; i < CL; ++i) creg[i] = *reinterpret_cast<const u32x4*>(ct + oc[i]);
+    v0reg = *reinterpret_cast<const u32x4*>(vt + ov[0]);
+    v1reg = *reinterpret_cast<const u32x4*>(vt + ov[1]);
+    if (tid < QB) dreg = dg[(t0 + (tid < nvalid ? tid : nvalid - 1)) * H];
   };
 
-  // registers -> LDS (rows past the end are zero); wave 0 also forms the block's decay sums
-  auto stage = [&](int nvalid) {
+  // registers -> LDS (rows past the end are zero), with the transposed copies of
+  // B and x; wave 0 also forms the block's decay sums
+  auto stage = [&](int nvalid, int buf) {
+    asm volatile("" : "+v"(b0reg), "+v"(b1reg), "+v"(v0reg), "+v"(v1reg));
 #pragma unroll
-    for (int i = 0; i < BCL; ++i) asm volatile("" : "+v"(breg[i]), "+v"(creg[i]));
-    asm volatile("" : "+v"(xreg), "+v"(zreg));
+    for (int i = 0; i < CL; ++i) asm volatile("" : "+v"(creg[i]));
+    if (nvalid < QB) {   // rows past the end of the sequence must read as zero
+      const u32x4 zero = {0, 0, 0, 0};
+      if (2 * rp >= nvalid) b0reg = zero;
+      if (2 * rp + 1 >= nvalid) b1reg = zero;
 #pragma unroll
-    for (int i = 0; i < BCL; ++i) {
-      if (bc_r[i] >= 0) {
-        const bool ok = bc_r[i] < nvalid;
-        const u32x4 bv = ok ? breg[i] : u32x4{0, 0, 0, 0};
-        const u32x4 cv = ok ? creg[i] : u32x4{0, 0, 0, 0};
-        // 8 consecutive n = two aligned groups of 4, each contiguous once permuted
-        const int o = bc_r[i] * NS;
-        const int k0 = kpos(bc_c[i]), k1 = kpos(bc_c[i] + 4);
-        *reinterpret_cast<u32x2*>(&Bs[o + k0]) = u32x2{bv[0], bv[1]};
-        *reinterpret_cast<u32x2*>(&Bs[o + k1]) = u32x2{bv[2], bv[3]};
-        *reinterpret_cast<u32x2*>(&Cs[o + k0]) = u32x2{cv[0], cv[1]};
-        *reinterpret_cast<u32x2*>(&Cs[o + k1]) = u32x2{cv[2], cv[3]};
+      for (int i = 0; i < CL; ++i)
+        if (c_r[i] >= nvalid) creg[i] = zero;
+      if (2 * xp >= nvalid) v0reg = zero;
+      if (2 * xp + 1 >= nvalid) v1reg = zero;
+    }
+    if (b_live) {
+      const u32x4 r0 = b0reg, r1 = b1reg;
+      const int k0 = kpos(8 * cb), k1 = kpos(8 * cb + 4);
+      *reinterpret_cast<u32x2*>(&Bs[(2 * rp) * NS + k0]) = u32x2{r0[0], r0[1]};
+      *reinterpret_cast<u32x2*>(&Bs[(2 * rp) * NS + k1]) = u32x2{r0[2], r0[3]};
+      *reinterpret_cast<u32x2*>(&Bs[(2 * rp + 1) * NS + k0]) = u32x2{r1[0], r1[1]};
+      *reinterpret_cast<u32x2*>(&Bs[(2 * rp + 1) * NS + k1]) = u32x2{r1[2], r1[3]};
+      const int sp = kpos(2 * rp);   // steps 2rp, 2rp+1 are adjacent once permuted
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = 8 * cb + 2 * q;
+        *reinterpret_cast<uint32_t*>(&BT[n * QS + sp]) = __builtin_amdgcn_perm(r1[q], r0[q], 0x05040100u);
+        *reinterpret_cast<uint32_t*>(&BT[(n + 1) * QS + sp]) = __builtin_amdgcn_perm(r1[q], r0[q], 0x07060302u);
       }
     }
-    {
-      const bool ok = x_r < nvalid;
-      *reinterpret_cast<u32x4*>(&Xs[x_r * QS + x_c]) = ok ? xreg : u32x4{0, 0, 0, 0};
-      if (has_z) *reinterpret_cast<u32x4*>(&Zs[x_r * QS + x_c]) = zreg;
+#pragma unroll
+    for (int i = 0; i < CL; ++i) {
+      if (c_r[i] >= 0) {
+        const u32x4 cv = creg[i];
+        const int o = c_r[i] * NS;
+        *reinterpret_cast<u32x2*>(&Cs[o + kpos(c_c[i])]) = u32x2{cv[0], cv[1]};
+        *reinterpret_cast<u32x2*>(&Cs[o + kpos(c_c[i] + 4)]) = u32x2{cv[2], cv[3]};
+      }
+    }
+    if (is_x) {
+      const u32x4 r0 = v0reg, r1 = v1reg;
+      *reinterpret_cast<u32x4*>(&Xs[buf][(2 * xp) * QS + 8 * xc]) = r0;
+      *reinterpret_cast<u32x4*>(&Xs[buf][(2 * xp + 1) * QS + 8 * xc]) = r1;
+      const int sp = kpos(2 * xp);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int pp = 8 * xc + 2 * q;
+        *reinterpret_cast<uint32_t*>(&XT[pp * QS + sp]) = __builtin_amdgcn_perm(r1[q], r0[q], 0x05040100u);
+        *reinterpret_cast<uint32_t*>(&XT[(pp + 1) * QS + sp]) = __builtin_amdgcn_perm(r1[q], r0[q], 0x07060302u);
+      }
+    } else if (has_z) {
+      *reinterpret_cast<u32x4*>(&Zs[buf][(2 * xp) * QS + 8 * xc]) = v0reg;
+      *reinterpret_cast<u32x4*>(&Zs[buf][(2 * xp + 1) * QS + 8 * xc]) = v1reg;
     }
     if (w == 0) {
+      // inclusive scan of delta * A * log2 e over the 64 steps (one per lane): DPP
+      // shifts within each 16-lane row, then row 15 / row 31 broadcasts across rows
       const float d = lane < nvalid ? __uint_as_float(static_cast<uint32_t>(dreg) << 16) : 0.f;
       float v = d * a2;
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const float u = __shfl_up(v, off, kWave);
-        if (lane >= off) v += u;
-      }
-      const float cs_end = __shfl(v, kWave - 1, kWave);
+      v += dppf<0x111, 0xf>(v);   // row_shr:1
+      v += dppf<0x112, 0xf>(v);   // row_shr:2
+      v += dppf<0x114, 0xf>(v);   // row_shr:4
+      v += dppf<0x118, 0xf>(v);   // row_shr:8
+      v += dppf<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
+      v += dppf<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
+      const float cs_end = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), kWave - 1));
       css[lane] = v;
       dls[lane] = d;
       wls[lane] = exp2_hw(cs_end - v) * d;
     }
   };
 
-  // B^T and x^T with the step axis permuted: a thread reads 2 adjacent columns
-  // of 8 consecutive rows (4-byte reads) and writes 2 rows of 8 steps
-  auto transpose = [&]() {
-    auto one = [&](const uint16_t* src, int sstride, int c2, int rg, uint16_t* dst, int ra, int rb) {
-      uint32_t v[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) v[q] = *reinterpret_cast<const uint32_t*>(&src[(8 * rg + q) * sstride + c2]);
-      // low halves -> row ra, high halves -> row rb; steps 8rg..8rg+3 and 8rg+4..8rg+7
-      // land on two groups of 4 stored positions
-      const u32x2 a0 = {__builtin_amdgcn_perm(v[1], v[0], 0x05040100u), __builtin_amdgcn_perm(v[3], v[2], 0x05040100u)};
-      const u32x2 a1 = {__builtin_amdgcn_perm(v[5], v[4], 0x05040100u), __builtin_amdgcn_perm(v[7], v[6], 0x05040100u)};
-      const u32x2 b0 = {__builtin_amdgcn_perm(v[1], v[0], 0x07060302u), __builtin_amdgcn_perm(v[3], v[2], 0x07060302u)};
-      const u32x2 b1 = {__builtin_amdgcn_perm(v[5], v[4], 0x07060302u), __builtin_amdgcn_perm(v[7], v[6], 0x07060302u)};
-      const int s0 = kpos(8 * rg), s1 = kpos(8 * rg + 4);
-      *reinterpret_cast<u32x2*>(&dst[ra * QS + s0]) = a0;
-      *reinterpret_cast<u32x2*>(&dst[ra * QS + s1]) = a1;
-      *reinterpret_cast<u32x2*>(&dst[rb * QS + s0]) = b0;
-      *reinterpret_cast<u32x2*>(&dst[rb * QS + s1]) = b1;
-    };
-    // B: NP/2 stored column pairs x 8 row groups
-    for (int j = tid; j < (NP / 2) * 8; j += kThreads) {
-      const int cp = j % (NP / 2), rg = j / (NP / 2);
-      const int n = knat(2 * cp);   // stored pair (2cp, 2cp+1) holds natural n, n+1
-      one(Bs, NS, 2 * cp, rg, BT, n, n + 1);
-    }
-    // x: 32 column pairs x 8 row groups
-    for (int j = tid; j < (PB / 2) * 8; j += kThreads) {
-      const int cp = j % (PB / 2), rg = j / (PB / 2);
-      one(Xs, QS, 2 * cp, rg, XT, 2 * cp, 2 * cp + 1);
-    }
-  };
-
   // outputs of a finished block, 16-byte stores
   uint16_t* const yg = p.out + (b * L * H + h) * P + p0;
-  auto store_block = [&](int64_t t0, int nvalid) {
-    if (tid < QB * PB / 8 && x_r < nvalid)
-      *reinterpret_cast<u32x4*>(yg + (t0 + x_r) * x_row + x_c) = *reinterpret_cast<const u32x4*>(&Ys[x_r * QS + x_c]);
+  const int y_r = tid / (PB / 8), y_c = 8 * (tid % (PB / 8));
+  auto store_block = [&](int64_t t0, int nvalid, int buf) {
+    if (y_r < nvalid)
+      *reinterpret_cast<u32x4*>(yg + (t0 + y_r) * x_row + y_c) = *reinterpret_cast<const u32x4*>(&Ys[buf][y_r * QS + y_c]);
   };
 
   // G^T tile (s-tile i, t-tile j) -> M[t][kpos(s)] hi/lo, 4 consecutive s per lane (8-byte writes)
@@ -344,20 +379,22 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
 
   const int partner = w ^ 4;   // the wave holding the other half of the states
 
-  // ---- block loop ----
+  // ---- block loop: stage | barrier | loads, stores, mask | barrier | readout,
+  // update | barrier | finish.  x, z and y tiles are double-buffered, so the next
+  // block's staging may start while other waves still finish this one.
   const int64_t nblocks = (L + QB - 1) / QB;
   if (nblocks > 0) issue_loads(0, static_cast<int>(L < QB ? L : QB));
   for (int64_t blk = 0; blk < nblocks; ++blk) {
     const int64_t t0 = blk * QB;
     const int nvalid = static_cast<int>((L - t0) < QB ? (L - t0) : QB);
-    stage(nvalid);
-    if (blk > 0) store_block(t0 - QB, QB);     // every block but the last is full
+    const int buf = static_cast<int>(blk & 1);
+    stage(nvalid, buf);
     __syncthreads();
     if (blk + 1 < nblocks) {
       const int64_t t1 = t0 + QB;
       issue_loads(t1, static_cast<int>((L - t1) < QB ? (L - t1) : QB));
     }
-    transpose();
+    if (blk > 0) store_block(t0 - QB, QB, buf ^ 1);     // every block but the last is full
     // the 10 causal tiles (i <= j): waves 0 and 1 take two, the others one
     if (w < 2) mask_tile(0, w);
     mask_tile(mi, mj);
@@ -448,27 +485,27 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
         const f32x4 o = Xc[(partner * 2 + k) * kWave + lane];
         const int t = 16 * j + lc;
         const int pl = 16 * pt + lq;
-        const u32x2 xv = *reinterpret_cast<const u32x2*>(&Xs[t * QS + pl]);
+        const u32x2 xv = *reinterpret_cast<const u32x2*>(&Xs[buf][t * QS + pl]);
         const f32x4 yj = Y[k == 0 ? JA : JB];
         float y[4] = {yj[0] + o[0] + Dh * lo_f(xv[0]), yj[1] + o[1] + Dh * hi_f(xv[0]),
                       yj[2] + o[2] + Dh * lo_f(xv[1]), yj[3] + o[3] + Dh * hi_f(xv[1])};
         if (has_z) {
-          const u32x2 zv = *reinterpret_cast<const u32x2*>(&Zs[t * QS + pl]);
+          const u32x2 zv = *reinterpret_cast<const u32x2*>(&Zs[buf][t * QS + pl]);
           const float zz[4] = {lo_f(zv[0]), hi_f(zv[0]), lo_f(zv[1]), hi_f(zv[1])};
 #pragma unroll
           for (int v = 0; v < 4; ++v) y[v] *= zz[v] * __builtin_amdgcn_rcpf(1.f + exp2_hw(-zz[v] * kLog2e));
         }
-        *reinterpret_cast<u32x2*>(&Ys[t * QS + pl]) = u32x2{pack2(y[0], y[1]), pack2(y[2], y[3])};
+        *reinterpret_cast<u32x2*>(&Ys[buf][t * QS + pl]) = u32x2{pack2(y[0], y[1]), pack2(y[2], y[3])};
       }
     };
     if (nh == 0) finish(std::integral_constant<int, 0>{});
     else finish(std::integral_constant<int, 1>{});
-    __syncthreads();      // every wave is done with this block's LDS
   }
 
   if (nblocks > 0) {
+    __syncthreads();   // the last block's outputs are complete
     const int64_t tl = (nblocks - 1) * QB;
-    store_block(tl, static_cast<int>(L - tl));
+    store_block(tl, static_cast<int>(L - tl), static_cast<int>((nblocks - 1) & 1));
   }
 
   if (p.final_state != nullptr) {

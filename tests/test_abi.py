@@ -159,6 +159,7 @@ def _ssd_call(desc, x=BASE, delta=BASE + 100 * MB, A=BASE + 200 * MB, B=BASE + 3
     (dict(chunk=32), M.MSSM_ERR_UNSUPPORTED),
     (dict(dstate=256), M.MSSM_ERR_UNSUPPORTED),
     (dict(headdim=96), M.MSSM_ERR_UNSUPPORTED),
+    (dict(nheads=(1 << 18) + 1, ngroups=1, headdim=64), M.MSSM_ERR_UNSUPPORTED),
     (dict(headdim=0), M.MSSM_ERR_INVALID_ARG),
     (dict(batch=-2), M.MSSM_ERR_INVALID_ARG),
 ])

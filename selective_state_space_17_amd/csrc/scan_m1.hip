@@ -774,12 +774,14 @@ __global__ __launch_bounds__(kThreads) void wide_kernel(KernelParams p) {
     const T* zv = reinterpret_cast<const T*>(&zr);
     const T* bv = reinterpret_cast<const T*>(&br);
     const T* cv = reinterpret_cast<const T*>(&cr);
-    const bool ok = ts < nvalid;
+    // steps past the end (last tile only) get delta = 0: an exact no-op step
+    const float keep = ts < nvalid ? 1.f : 0.f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const float d = to_f32(dv[q]), u = to_f32(xv[q]);
       const float gz = has_z ? silu_gate(to_f32(zv[q])) : 1.f;
-      const float4 v = ok ? float4{d, d * u, gz, gz * (Dreg[q] * u)} : float4{0.f, 0.f, 0.f, 0.f};
+      float4 v = float4{d, d * u, gz, gz * (Dreg[q] * u)};
+      if (nvalid < TT) v = float4{v.x * keep, v.y * keep, v.z * keep, v.w * keep};
       Qs[(4 * q4 + q) * QS + ts] = v;
       Bt[(4 * q4 + q) * BS + ts] = to_f32(bv[q]);
       Ct[(4 * q4 + q) * BS + ts] = to_f32(cv[q]);

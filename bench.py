@@ -45,8 +45,9 @@ def source_digest(is_ssd: bool) -> str:
     return h.hexdigest()[:16]
 
 
-def kernel_tag(is_ssd: bool) -> str:
-    return "ssd_kernel" if is_ssd else "scan_kernel"
+def kernel_tags(is_ssd: bool):
+    """Name fragments of the kernels that carry the workload's scan (the dominant one per launch)."""
+    return ("ssd_kernel",) if is_ssd else ("wide_kernel", "scan_kernel")
 
 
 def load_traffic(workload: str, is_ssd: bool):
@@ -72,9 +73,9 @@ def summarize_counters(cfg, is_ssd, d, copy_mib):
     WRITE_SIZE) into HBM bytes per launch of the dominant kernel, each counter scaled by what it
     reads for a device copy of copy_mib MiB, and write profiles/traffic_<workload>.json."""
     import numpy as np
-    tag = kernel_tag(is_ssd)
+    tags = kernel_tags(is_ssd)
     copy_bytes = copy_mib << 20
-    res = {"workload": cfg.name, "kernel": tag, "source_digest": source_digest(is_ssd),
+    res = {"workload": cfg.name, "source_digest": source_digest(is_ssd),
            "copy_bytes": copy_bytes, "algorithmic_bytes_per_launch": cfg.algorithmic_bytes()}
     total = 0.0
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
@@ -83,9 +84,18 @@ def summarize_counters(cfg, is_ssd, d, copy_mib):
             cd = os.path.join(os.path.dirname(os.path.abspath(d)), "copy_" + counter.lower())
         copy_kib = max(v for _, v in _counter_rows(cd, counter))
         factor = copy_bytes / (copy_kib * 1024.0)
-        vals = [v for n, v in _counter_rows(os.path.join(d, "pmc_" + counter.lower()), counter) if tag in n]
+        rows = _counter_rows(os.path.join(d, "pmc_" + counter.lower()), counter)
+        # the dominant kernel: the first tag with dispatches (the single-pass or chunk kernel)
+        vals, name = [], None
+        for tag in tags:
+            hits = [(n, v) for n, v in rows if tag in n]
+            if hits:
+                name = max(set(n for n, _ in hits), key=lambda k: sum(v for n, v in hits if n == k))
+                vals = [v for n, v in hits if n == name]
+                break
         if not vals:
-            raise SystemExit(f"no {tag} dispatches with {counter} under {d}")
+            raise SystemExit(f"no {tags} dispatches with {counter} under {d}")
+        res["kernel"] = name
         kib = float(np.mean(vals))
         res[counter] = {"kib_per_dispatch": kib, "dispatches": len(vals), "copy_kib": copy_kib,
                         "scale": factor, "bytes_per_launch": kib * 1024.0 * factor}

@@ -136,7 +136,7 @@ def cpu_baseline_scan(inp, cfg):
     # bounded sample: whole batch and sequence, channels up to ~4e9 updates, repeated to ~10 s
     per_ch = cfg.batch * cfg.seqlen * cfg.dstate
     nc = int(min(cfg.dim, max(1, 4e9 // per_ch)))
-    passes, dt = _timed_passes(lambda: oracle.scan_fwd(inp.x, inp.delta, inp.A, inp.B, inp.C, inp.D, inp.z, None,
+    passes, dt = _timed_passes(lambda: oracle.scan_fwd(inp.x, inp.delta, inp.A, inp.B, inp.C, inp.D, inp.z, inp.h0,
                                                        c0=0, c1=nc, nthreads=threads))
     n = per_ch * nc * passes
     return {"value": n / dt, "unit": "state-updates/s", "cores": threads, "kind": "oracle",
@@ -149,7 +149,7 @@ def cpu_baseline_ssd(inp, cfg):
     threads = oracle.default_threads()
     per_head = cfg.batch * cfg.seqlen * cfg.headdim * cfg.dstate
     nh = int(min(cfg.nheads, max(1, 4e9 // per_head)))
-    passes, dt = _timed_passes(lambda: oracle.ssd_fwd(inp.x, inp.delta, inp.A, inp.B, inp.C, inp.D, inp.z, None,
+    passes, dt = _timed_passes(lambda: oracle.ssd_fwd(inp.x, inp.delta, inp.A, inp.B, inp.C, inp.D, inp.z, inp.h0,
                                                       hd0=0, hd1=nh, nthreads=threads))
     n = per_head * nh * passes
     return {"value": n / dt, "unit": "state-updates/s", "cores": threads, "kind": "oracle",
@@ -162,7 +162,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, help="workload id (1-5); 2 is the one the metric is quoted on")
+    ap.add_argument("--config", type=int, default=2,
+                    help="workload id (1-7; 6, 7: decode steps); 2 is the one the metric is quoted on")
     ap.add_argument("--sets", type=int, default=0, help="resident input copies to rotate over (0: auto)")
     ap.add_argument("--chunk", type=int, default=0, help="SSD time-chunk length (0: the workload's)")
     ap.add_argument("--split-seq", type=int, default=0, help="force the sequence-chunk count (0: the planner's)")
@@ -213,7 +214,23 @@ def main():
     log(f"workload {cfg.name}: {cfg.updates:.3e} updates, {alg_bytes / 1e6:.1f} MB algorithmic, {sets} input set(s)")
 
     t = time.perf_counter()
-    if is_ssd:
+    decode = cfg.decode
+    if decode:
+        # token-by-token update: each input set carries its own state, advanced in place every step
+        if is_ssd:
+            host = [W.make_ssd_inputs(cfg, seed_base=W.ROOT_SEED + 1000 * i, with_h0=True) for i in range(sets)]
+        else:
+            host = [W.make_scan_inputs(cfg, seed_base=W.ROOT_SEED + 1000 * i, with_h0=True) for i in range(sets)]
+        ins = [dict(x=dev(h.x), delta=dev(h.delta), A=dev(h.A), B=dev(h.B), C=dev(h.C), D=dev(h.D), z=dev(h.z),
+                    state=dev(h.h0)) for h in host]
+        outs = [torch.empty_like(i["x"]) for i in ins]
+        upd = M.ssd_state_update if is_ssd else M.selective_state_update
+
+        def step(i):
+            a, o = ins[i % sets], outs[i % sets]
+            upd(a["state"], a["x"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], out=o)
+        plan = {"tokens": cfg.seqlen}
+    elif is_ssd:
         chunk = args.chunk or cfg.chunk
         host = [W.make_ssd_inputs(cfg, seed_base=W.ROOT_SEED + 1000 * i) for i in range(sets)]
         ins = [dict(x=dev(h.x), delta=dev(h.delta), A=dev(h.A), B=dev(h.B), C=dev(h.C), D=dev(h.D), z=dev(h.z))
@@ -277,7 +294,14 @@ def main():
     hbm = {"achieved": alg_bytes / kern_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
            "frac": alg_bytes / kern_s / 1e9 / PEAK_HBM_GBS}
     traffic = load_traffic(cfg.name, is_ssd)
-    if is_ssd:
+    if decode:
+        # a few operations per byte of state: the HBM roofline bounds it
+        roof = dict(hbm)
+        roof["bound"] = "hbm"
+        slots = cfg.updates * (SLOTS_PER_UPDATE if not is_ssd else 4.0)
+        roof["other"] = {"achieved": slots / kern_s / 1e12, "peak": PEAK_VALU_TSLOT, "unit": "Tslot/s",
+                         "frac": slots / kern_s / 1e12 / PEAK_VALU_TSLOT}
+    elif is_ssd:
         Q = 64   # the kernel evaluates any chunk length as 64-step blocks
         # matrix-core work of the block form per launch: causal in-block Q*Q*P/2 per step and head,
         # state readout and update 2*N*P per step and head, C.B^T Q*N/2 (causal) per step and group
@@ -305,12 +329,16 @@ def main():
         log("timing the CPU oracle on a bounded sample ...")
         h = host[0]
         cpu = cpu_baseline_ssd(h, cfg) if is_ssd else cpu_baseline_scan(h, cfg)
+        if decode:
+            cpu["sample"] += "; the same recurrence from the stored state (h0)"
         log(f"cpu baseline: {cpu}")
 
     conf = {"workload": cfg.name, "batch": cfg.batch, "seqlen": cfg.seqlen}
+    if decode:
+        conf["decode"] = True
     if is_ssd:
-        conf.update(nheads=cfg.nheads, headdim=cfg.headdim, d_state=cfg.dstate, ngroups=cfg.ngroups,
-                    chunk=plan["chunk"], io="bf16")
+        conf.update(nheads=cfg.nheads, headdim=cfg.headdim, d_state=cfg.dstate, ngroups=cfg.ngroups, io="bf16",
+                    **plan)
     else:
         conf.update(d_inner=cfg.dim, d_state=cfg.dstate, io=cfg.io, D=cfg.has_D, z_gate=cfg.has_z,
                     final_state=cfg.return_final, **plan)

@@ -1,7 +1,9 @@
 /*
  * mssm.h -- C ABI of the MI355X (gfx950) selective-scan library (libmssm.so).
  *
- * Two forward operations:
+ * Two forward operations, each with a token-by-token (decode) counterpart
+ * that advances a stored state in place (mssm_selective_state_update,
+ * mssm_ssd_state_update):
  *
  *  1. mssm_selective_scan_fwd -- the Mamba-1 selective scan.  Defined by the
  *     linear state recurrence h_t = A h_{t-1} + B x_t with readout y_t = C h_t
@@ -130,6 +132,41 @@ int mssm_ssd_fwd(const mssm_ssd_desc* desc,
                  void* workspace, size_t workspace_bytes, void* stream);
 
 size_t mssm_ssd_workspace_size(const mssm_ssd_desc* desc);
+
+/* Token-by-token state update (decode), Mamba-1 form.  At inference the layer
+ * keeps only its fixed-size state and advances it one token at a time, at a
+ * cost that does not grow with the tokens already seen ("03 - Modelos de
+ * espacio de estados", "Coste de inferencia"; "P20 - Mamba", 5).  Applies the
+ * recurrence and readout of mssm_selective_scan_fwd to desc->seqlen new
+ * tokens (normally 1), starting from `state` and writing the advanced state
+ * back into `state` (in place):
+ *   state         : [batch, dim, dstate] fp32, read and overwritten
+ *   x, delta, z, out : [batch, seqlen, dim]  (io_dtype; z nullable)
+ *   B, C          : [batch, seqlen, dstate]  (io_dtype)
+ *   A             : [dim, dstate] fp32;  D : [dim] fp32, nullable
+ * split_seq and split_state are ignored.  The result equals
+ * mssm_selective_scan_fwd with h0 = state and final_state written to state,
+ * up to rounding.  `out` and `state` must not alias any input or each other.
+ * Same ownership, stream and error rules as mssm_selective_scan_fwd; no
+ * workspace. */
+int mssm_selective_state_update(const mssm_scan_desc* desc, float* state,
+                                const void* x, const void* delta, const float* A,
+                                const void* B, const void* C, const float* D, const void* z,
+                                void* out, void* stream);
+
+/* Token-by-token state update, multi-head (scalar A per head) form:
+ *   state         : [batch, nheads, headdim, dstate] fp32, read and overwritten
+ *   x, z, out     : [batch, seqlen, nheads, headdim]  (io_dtype; z nullable)
+ *   delta         : [batch, seqlen, nheads]           (io_dtype)
+ *   B, C          : [batch, seqlen, ngroups, dstate]  (io_dtype)
+ *   A, D          : [nheads] fp32 (D nullable)
+ * io_dtype may be MSSM_F32 or MSSM_BF16; dstate 1..256; any headdim; chunk is
+ * ignored.  Equals mssm_ssd_fwd with h0 = state, final_state written to
+ * state, up to rounding. */
+int mssm_ssd_state_update(const mssm_ssd_desc* desc, float* state,
+                          const void* x, const void* delta, const float* A,
+                          const void* B, const void* C, const float* D, const void* z,
+                          void* out, void* stream);
 
 /* The plan the library would use for a selective-scan descriptor:
  * writes the sequence-chunk count and lanes-per-channel; returns a status. */

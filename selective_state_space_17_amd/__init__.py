@@ -46,6 +46,8 @@ SIGNATURES = {
                                       ctypes.POINTER(ctypes.c_int32)]),
     "mssm_ssd_fwd": (_I, [ctypes.POINTER(SSDDesc)] + [_P] * 10 + [_P, _SZ, _P]),
     "mssm_ssd_workspace_size": (_SZ, [ctypes.POINTER(SSDDesc)]),
+    "mssm_selective_state_update": (_I, [ctypes.POINTER(ScanDesc)] + [_P] * 10),
+    "mssm_ssd_state_update": (_I, [ctypes.POINTER(SSDDesc)] + [_P] * 10),
     "mssm_status_string": (ctypes.c_char_p, [_I]),
     "mssm_last_error_detail": (ctypes.c_char_p, []),
     "mssm_abi_version": (_I, []),
@@ -54,7 +56,7 @@ SIGNATURES = {
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m selective_state_space_17_amd.build` "
+        raise ImportError(f"{LIB_PATH} is not built; run `python selective_state_space_17_amd/build.py` "
                           "(or __graft_entry__.build()) first")
     # The library's HIP runtime dependency must resolve to the copy torch ships:
     # two HIP runtimes in one process leave the second without a device.  Load
@@ -229,3 +231,67 @@ def ssd_fwd(x, delta, A, B, C, D=None, z=None, h0=None, chunk: int = 0, return_f
     if st != MSSM_OK:
         raise MssmError(st, "mssm_ssd_fwd")
     return (out, final_state) if return_final_state else out
+
+
+def selective_state_update(state, x, delta, A, B, C, D=None, z=None, out=None, stream=None):
+    """Advance a Mamba-1 state by seqlen tokens in place (mssm_selective_state_update).
+
+    state: [batch, dim, dstate] float32 (overwritten); x, delta, z: [batch, seqlen, dim];
+    B, C: [batch, seqlen, dstate] (float32 or bfloat16, all alike); A: [dim, dstate]; D: [dim].
+    Returns out [batch, seqlen, dim].
+    """
+    torch = _torch()
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, seqlen, dim]")
+    bsz, L, dm = x.shape
+    if A.dim() != 2 or A.shape[0] != dm:
+        raise ValueError("A must be [dim, dstate]")
+    N = A.shape[1]
+    io = _io_code(x.dtype)
+    for name, t, shape in (("x", x, (bsz, L, dm)), ("delta", delta, (bsz, L, dm)), ("z", z, (bsz, L, dm)),
+                           ("B", B, (bsz, L, N)), ("C", C, (bsz, L, N))):
+        _check_gpu(name, t, x.dtype, shape)
+    _check_gpu("A", A, torch.float32, (dm, N))
+    _check_gpu("D", D, torch.float32, (dm,))
+    _check_gpu("state", state, torch.float32, (bsz, dm, N))
+    if out is None:
+        out = torch.empty_like(x)
+    _check_gpu("out", out, x.dtype, (bsz, L, dm))
+    d = scan_desc(bsz, L, dm, N, io)
+    st = lib.mssm_selective_state_update(ctypes.byref(d), _ptr(state), _ptr(x), _ptr(delta), _ptr(A), _ptr(B),
+                                         _ptr(C), _ptr(D), _ptr(z), _ptr(out), _stream_handle(stream))
+    if st != MSSM_OK:
+        raise MssmError(st, "mssm_selective_state_update")
+    return out
+
+
+def ssd_state_update(state, x, delta, A, B, C, D=None, z=None, out=None, stream=None):
+    """Advance a multi-head (scalar A) state by seqlen tokens in place (mssm_ssd_state_update).
+
+    state: [batch, nheads, headdim, dstate] float32 (overwritten); x, z: [batch, seqlen, nheads, headdim];
+    delta: [batch, seqlen, nheads]; B, C: [batch, seqlen, ngroups, dstate]; A, D: [nheads].
+    Returns out [batch, seqlen, nheads, headdim].
+    """
+    torch = _torch()
+    if x.dim() != 4:
+        raise ValueError("x must be [batch, seqlen, nheads, headdim]")
+    bsz, L, H, P = x.shape
+    if B.dim() != 4:
+        raise ValueError("B must be [batch, seqlen, ngroups, dstate]")
+    G, N = B.shape[2], B.shape[3]
+    io = _io_code(x.dtype)
+    for name, t, shape in (("x", x, (bsz, L, H, P)), ("z", z, (bsz, L, H, P)), ("delta", delta, (bsz, L, H)),
+                           ("B", B, (bsz, L, G, N)), ("C", C, (bsz, L, G, N))):
+        _check_gpu(name, t, x.dtype, shape)
+    _check_gpu("A", A, torch.float32, (H,))
+    _check_gpu("D", D, torch.float32, (H,))
+    _check_gpu("state", state, torch.float32, (bsz, H, P, N))
+    if out is None:
+        out = torch.empty_like(x)
+    _check_gpu("out", out, x.dtype, (bsz, L, H, P))
+    d = ssd_desc(bsz, L, H, P, N, G, 0, io)
+    st = lib.mssm_ssd_state_update(ctypes.byref(d), _ptr(state), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                                   _ptr(D), _ptr(z), _ptr(out), _stream_handle(stream))
+    if st != MSSM_OK:
+        raise MssmError(st, "mssm_ssd_state_update")
+    return out

@@ -1,6 +1,8 @@
 """Build libmssm.so (HIP for gfx950) in-tree.
 
-    python -m selective_state_space_17_amd.build
+    python selective_state_space_17_amd/build.py
+
+(run as a script: importing the package would open the library being rebuilt)
 
 hipcc compiles for gfx950 only.  Packed-fp32 VALU instructions are disabled
 (-packed-fp32-ops); the host pass warns that it does not know the feature,
@@ -18,7 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmssm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["api.cpp", "scan_m1.hip", "ssd_m2.hip"]
+SOURCES = ["api.cpp", "scan_m1.hip", "ssd_m2.hip", "decode.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-munsafe-fp-atomics", "-Wall", "-Wno-unused-function"]

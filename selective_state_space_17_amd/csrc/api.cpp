@@ -241,6 +241,95 @@ static int validate_ssd_desc(const mssm_ssd_desc* d, int64_t* Q) {
   return MSSM_OK;
 }
 
+// --------------------------------------------------------------------------
+// Token-by-token state update
+// --------------------------------------------------------------------------
+int mssm_selective_state_update(const mssm_scan_desc* desc, float* state, const void* x, const void* delta,
+                                const float* A, const void* B, const void* C, const float* D, const void* z,
+                                void* out, void* stream) {
+  const int v = validate_scan_desc(desc);
+  if (v != MSSM_OK) return v;
+  const mssm_scan_desc& d = *desc;
+  if (d.batch == 0 || d.seqlen == 0) return MSSM_OK;
+  const int64_t es = d.io_dtype == MSSM_BF16 ? 2 : 4;
+  if (state == nullptr || A == nullptr || x == nullptr || delta == nullptr || B == nullptr || C == nullptr ||
+      out == nullptr)
+    return MSSM_ERR_INVALID_ARG;
+  if (!aligned(x, es) || !aligned(delta, es) || !aligned(B, es) || !aligned(C, es) || !aligned(z, es) ||
+      !aligned(out, es) || !aligned(A, 4) || !aligned(D, 4) || !aligned(state, 4))
+    return MSSM_ERR_MISALIGNED;
+  const int64_t b_io = d.batch * d.seqlen * d.dim * es, b_bc = d.batch * d.seqlen * d.dstate * es;
+  const int64_t b_st = d.batch * d.dim * d.dstate * 4;
+  const void* ins[] = {x, delta, B, C, z, A, D};
+  const int64_t inb[] = {b_io, b_io, b_bc, b_bc, b_io, d.dim * d.dstate * 4, d.dim * 4};
+  for (int i = 0; i < 7; ++i) {
+    if (overlap(out, b_io, ins[i], inb[i])) return MSSM_ERR_INVALID_ARG;
+    if (overlap(state, b_st, ins[i], inb[i])) return MSSM_ERR_INVALID_ARG;
+  }
+  if (overlap(out, b_io, state, b_st)) return MSSM_ERR_INVALID_ARG;
+  if (mssm::update_grid_blocks(d.batch * d.dim, d.dstate) > std::numeric_limits<int32_t>::max())
+    return MSSM_ERR_UNSUPPORTED;
+  mssm::UpdateArgs a{};
+  a.state = state; a.x = x; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.out = out;
+  a.batch = d.batch; a.L = d.seqlen; a.N = d.dstate; a.dim = d.dim; a.io = d.io_dtype;
+  const hipError_t e = mssm::scan_update_launch(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    set_err(e);
+    return MSSM_ERR_HIP;
+  }
+  return MSSM_OK;
+}
+
+int mssm_ssd_state_update(const mssm_ssd_desc* desc, float* state, const void* x, const void* delta,
+                          const float* A, const void* B, const void* C, const float* D, const void* z, void* out,
+                          void* stream) {
+  const mssm_ssd_desc* d = desc;
+  if (d == nullptr) return MSSM_ERR_INVALID_ARG;
+  if (d->batch < 0 || d->seqlen < 0 || d->nheads <= 0 || d->headdim <= 0 || d->dstate <= 0 || d->ngroups <= 0)
+    return MSSM_ERR_INVALID_ARG;
+  if (d->flags != 0) return MSSM_ERR_INVALID_ARG;
+  if (d->io_dtype != MSSM_BF16 && d->io_dtype != MSSM_F32) return MSSM_ERR_UNSUPPORTED;
+  if (d->nheads % d->ngroups != 0 || d->dstate > 256) return MSSM_ERR_UNSUPPORTED;
+  const int64_t es = d->io_dtype == MSSM_BF16 ? 2 : 4;
+  int64_t n_x = 0, n_bc = 0, n_st = 0, n_d = 0, t = 0;
+  if (!mul_ok(d->batch, d->seqlen, &t) || !mul_ok(t, d->nheads, &n_d) || !mul_ok(n_d, d->headdim, &n_x) ||
+      !mul_ok(n_x, es, &t))
+    return MSSM_ERR_INVALID_ARG;
+  if (!mul_ok(d->batch, d->seqlen, &t) || !mul_ok(t, d->ngroups, &t) || !mul_ok(t, d->dstate, &n_bc) ||
+      !mul_ok(n_bc, es, &t))
+    return MSSM_ERR_INVALID_ARG;
+  if (!mul_ok(d->batch, d->nheads, &t) || !mul_ok(t, d->headdim, &t) || !mul_ok(t, d->dstate, &n_st) ||
+      !mul_ok(n_st, 4 * 64, &t))
+    return MSSM_ERR_INVALID_ARG;
+  if (d->batch == 0 || d->seqlen == 0) return MSSM_OK;
+  if (state == nullptr || A == nullptr || x == nullptr || delta == nullptr || B == nullptr || C == nullptr ||
+      out == nullptr)
+    return MSSM_ERR_INVALID_ARG;
+  if (!aligned(x, es) || !aligned(delta, es) || !aligned(B, es) || !aligned(C, es) || !aligned(z, es) ||
+      !aligned(out, es) || !aligned(A, 4) || !aligned(D, 4) || !aligned(state, 4))
+    return MSSM_ERR_MISALIGNED;
+  const int64_t b_io = n_x * es, b_st = n_st * 4;
+  const void* ins[] = {x, delta, B, C, z, A, D};
+  const int64_t inb[] = {b_io, n_d * es, n_bc * es, n_bc * es, b_io, d->nheads * 4, d->nheads * 4};
+  for (int i = 0; i < 7; ++i) {
+    if (overlap(out, b_io, ins[i], inb[i])) return MSSM_ERR_INVALID_ARG;
+    if (overlap(state, b_st, ins[i], inb[i])) return MSSM_ERR_INVALID_ARG;
+  }
+  if (overlap(out, b_io, state, b_st)) return MSSM_ERR_INVALID_ARG;
+  if (mssm::update_grid_blocks(d->batch * d->nheads * d->headdim, d->dstate) > std::numeric_limits<int32_t>::max())
+    return MSSM_ERR_UNSUPPORTED;
+  mssm::UpdateArgs a{};
+  a.state = state; a.x = x; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.out = out;
+  a.batch = d->batch; a.L = d->seqlen; a.N = d->dstate;
+  a.H = d->nheads; a.P = d->headdim; a.G = d->ngroups; a.io = d->io_dtype;
+  const hipError_t e = mssm::ssd_update_launch(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    set_err(e);
+    return MSSM_ERR_HIP;
+  }
+  return MSSM_OK;
+}
+
 size_t mssm_ssd_workspace_size(const mssm_ssd_desc* desc) {
   int64_t Q = 0;
   if (validate_ssd_desc(desc, &Q) != MSSM_OK) return 0;

@@ -1,0 +1,311 @@
+// Token-by-token state update ("decode") for gfx950 (MI355X).
+//
+// At inference a state space layer keeps only its state and advances it one
+// token at a time at a cost that does not depend on how many tokens came
+// before ("03 - Modelos de espacio de estados", "Coste de inferencia"; the
+// fixed-size state of "P20 - Mamba", 5).  These kernels apply the same
+// recurrence and readout as the sequence kernels to T >= 1 new tokens,
+// reading the state from HBM and writing it back in place:
+//   Mamba-1, per (b, c, n):  h <- exp(delta A[c,n]) h + delta B[n] x
+//                            y = sum_n C[n] h + D[c] x,  out = y * silu(z)
+//   Mamba-2 multi-head, per (b, h, p, n) with scalar A[h] and group g(h):
+//                            S <- exp(delta A[h]) S + delta B[g,n] x[p]
+//                            y[p] = sum_n C[g,n] S + D[h] x[p],  out = y * silu(z)
+// The work per token is a few operations per byte of state, so the kernels
+// are bound by HBM: one thread owns 4 consecutive states of one row (one
+// 16-byte load and store when the layout allows), a row's threads are
+// consecutive lanes, and the readout's sum over states is a butterfly over
+// those lanes.  Consecutive threads touch consecutive 16-byte pieces of the
+// state, so every access to it is fully coalesced.
+#include <type_traits>
+
+#include "internal.h"
+
+namespace mssm {
+namespace {
+
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(uint16_t v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ uint16_t from_f32<uint16_t>(float v) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));   // round to nearest even
+}
+__device__ __forceinline__ float exp2_hw(float v) { return __builtin_amdgcn_exp2f(v); }
+__device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.f + exp2_hw(-z * kLog2e)); }
+
+template <int CTRL> __device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+
+// sum over the lpr lanes of an aligned group (lpr a power of two <= 64; uniform):
+// quad swaps, then half-row and row mirrors, then cross-row shuffles
+__device__ __forceinline__ float group_sum(float v, int lpr) {
+  if (lpr >= 2) v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
+  if (lpr >= 4) v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
+  if (lpr >= 8) v += dpp<0x141>(v);   // row_half_mirror
+  if (lpr >= 16) v += dpp<0x140>(v);  // row_mirror
+  if (lpr >= 32) v += __shfl_xor(v, 16, 64);
+  if (lpr >= 64) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+// 4 states n0..n0+3 of a row (entries past N read as 0 and are not written)
+template <bool VEC>
+__device__ __forceinline__ void load4(const float* p, int n0, int N, float (&v)[4]) {
+  if constexpr (VEC) {   // N % 4 == 0: a group is wholly inside or wholly past the row
+    const float4 t = n0 < N ? *reinterpret_cast<const float4*>(p + n0) : float4{0.f, 0.f, 0.f, 0.f};
+    v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = n0 + q < N ? p[n0 + q] : 0.f;
+  }
+}
+template <bool VEC>
+__device__ __forceinline__ void store4(float* p, int n0, int N, const float (&v)[4]) {
+  if constexpr (VEC) {
+    if (n0 < N) *reinterpret_cast<float4*>(p + n0) = float4{v[0], v[1], v[2], v[3]};
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (n0 + q < N) p[n0 + q] = v[q];
+  }
+}
+// 4 consecutive B or C values (one 8- or 16-byte load when N % 4 == 0)
+template <typename T, bool VEC>
+__device__ __forceinline__ void load4io(const T* p, int n0, int N, float (&v)[4]) {
+  if constexpr (VEC) {
+    if (n0 < N) {
+      if constexpr (sizeof(T) == 2) {
+        const uint2 w = *reinterpret_cast<const uint2*>(p + n0);
+        v[0] = __uint_as_float(w.x << 16); v[1] = __uint_as_float(w.x & 0xffff0000u);
+        v[2] = __uint_as_float(w.y << 16); v[3] = __uint_as_float(w.y & 0xffff0000u);
+      } else {
+        const float4 w = *reinterpret_cast<const float4*>(p + n0);
+        v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
+      }
+    } else {
+      v[0] = v[1] = v[2] = v[3] = 0.f;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = n0 + q < N ? to_f32(p[n0 + q]) : 0.f;
+  }
+}
+
+struct UpdParams {
+  float* state;
+  const void* x;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;
+  const void* z;
+  void* out;
+  int64_t batch, L, N;
+  int64_t dim;             // Mamba-1: channels
+  int64_t H, P, G;         // multi-head form
+  int64_t rows;            // rows of the state
+  int lpr;                 // lanes per row
+};
+
+// Each thread owns 4 states in each of R rows spaced a grid-width of rows
+// apart (so every pass over r is one coalesced sweep).  One row per thread
+// measured fastest: it keeps registers low enough for 8 waves per SIMD.
+constexpr int R = 1;
+
+// Mamba-1: row = (b, c), state [batch, dim, N]
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kThreads) void scan_update_kernel(UpdParams p) {
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t row0 = gid / p.lpr;
+  const int64_t rstride = static_cast<int64_t>(gridDim.x) * kThreads / p.lpr;
+  const int n0 = 4 * static_cast<int>(gid % p.lpr);
+  const int N = static_cast<int>(p.N);
+  const int64_t L = p.L, dim = p.dim;
+  const T* x = static_cast<const T*>(p.x);
+  const T* delta = static_cast<const T*>(p.delta);
+  const T* Bm = static_cast<const T*>(p.B);
+  const T* Cm = static_cast<const T*>(p.C);
+  const T* z = static_cast<const T*>(p.z);
+  T* out = static_cast<T*>(p.out);
+
+  bool live[R];
+  int64_t rr[R], bb[R], cc[R];
+  float h[R][4], a2[R][4], Dc[R];
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const int64_t row = row0 + k * rstride;
+    live[k] = row < p.rows;
+    rr[k] = live[k] ? row : 0;
+    bb[k] = rr[k] / dim;
+    cc[k] = rr[k] % dim;
+    load4<VEC>(p.state + rr[k] * N, n0, N, h[k]);
+    load4<VEC>(p.A + cc[k] * N, n0, N, a2[k]);
+    Dc[k] = p.D != nullptr ? p.D[cc[k]] : 0.f;
+  }
+  for (int64_t t = 0; t < L; ++t) {
+    float d[R], u[R], zz[R], bv[R][4], cv[R][4];
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      const int64_t o = (bb[k] * L + t) * dim + cc[k];
+      d[k] = to_f32(delta[o]);
+      u[k] = to_f32(x[o]);
+      zz[k] = z != nullptr ? to_f32(z[o]) : 0.f;
+      load4io<T, VEC>(Bm + (bb[k] * L + t) * N, n0, N, bv[k]);
+      load4io<T, VEC>(Cm + (bb[k] * L + t) * N, n0, N, cv[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      const float du = d[k] * u[k];
+      float acc = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        h[k][q] = __builtin_fmaf(exp2_hw(d[k] * a2[k][q] * kLog2e), h[k][q], du * bv[k][q]);
+        acc = __builtin_fmaf(cv[k][q], h[k][q], acc);
+      }
+      acc = group_sum(acc, p.lpr);
+      if (live[k] && n0 == 0) {
+        float y = __builtin_fmaf(Dc[k], u[k], acc);
+        if (z != nullptr) y *= silu(zz[k]);
+        out[(bb[k] * L + t) * dim + cc[k]] = from_f32<T>(y);
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < R; ++k)
+    if (live[k]) store4<VEC>(p.state + rr[k] * N, n0, N, h[k]);
+}
+
+// multi-head form: row = (b, h, p), state [batch, H, P, N]
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kThreads) void ssd_update_kernel(UpdParams p) {
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t row0 = gid / p.lpr;
+  const int64_t rstride = static_cast<int64_t>(gridDim.x) * kThreads / p.lpr;
+  const int n0 = 4 * static_cast<int>(gid % p.lpr);
+  const int64_t P = p.P, H = p.H, G = p.G, L = p.L;
+  const int N = static_cast<int>(p.N);
+  const T* x = static_cast<const T*>(p.x);
+  const T* delta = static_cast<const T*>(p.delta);
+  const T* Bm = static_cast<const T*>(p.B);
+  const T* Cm = static_cast<const T*>(p.C);
+  const T* z = static_cast<const T*>(p.z);
+  T* out = static_cast<T*>(p.out);
+
+  bool live[R];
+  int64_t rr[R], pp[R], hd[R], bb[R], gg[R];
+  float h[R][4], a2[R], Dh[R];
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const int64_t row = row0 + k * rstride;
+    live[k] = row < p.rows;
+    rr[k] = live[k] ? row : 0;
+    pp[k] = rr[k] % P;
+    const int64_t bh = rr[k] / P;
+    hd[k] = bh % H;
+    bb[k] = bh / H;
+    gg[k] = hd[k] / (H / G);
+    load4<VEC>(p.state + rr[k] * N, n0, N, h[k]);
+    a2[k] = p.A[hd[k]] * kLog2e;
+    Dh[k] = p.D != nullptr ? p.D[hd[k]] : 0.f;
+  }
+  for (int64_t t = 0; t < L; ++t) {
+    float d[R], u[R], zz[R], bv[R][4], cv[R][4];
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      const int64_t obh = (bb[k] * L + t) * H + hd[k];
+      d[k] = to_f32(delta[obh]);
+      u[k] = to_f32(x[obh * P + pp[k]]);
+      zz[k] = z != nullptr ? to_f32(z[obh * P + pp[k]]) : 0.f;
+      load4io<T, VEC>(Bm + ((bb[k] * L + t) * G + gg[k]) * N, n0, N, bv[k]);
+      load4io<T, VEC>(Cm + ((bb[k] * L + t) * G + gg[k]) * N, n0, N, cv[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      const float dA = exp2_hw(d[k] * a2[k]), du = d[k] * u[k];
+      float acc = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        h[k][q] = __builtin_fmaf(dA, h[k][q], du * bv[k][q]);
+        acc = __builtin_fmaf(cv[k][q], h[k][q], acc);
+      }
+      acc = group_sum(acc, p.lpr);
+      if (live[k] && n0 == 0) {
+        float y = __builtin_fmaf(Dh[k], u[k], acc);
+        if (z != nullptr) y *= silu(zz[k]);
+        out[((bb[k] * L + t) * H + hd[k]) * P + pp[k]] = from_f32<T>(y);
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < R; ++k)
+    if (live[k]) store4<VEC>(p.state + rr[k] * N, n0, N, h[k]);
+}
+
+int lanes_per_row(int64_t N) {
+  int l = 1;
+  while (4 * l < N) l *= 2;
+  return l;
+}
+
+UpdParams common(const UpdateArgs& a) {
+  UpdParams p{};
+  p.state = a.state; p.x = a.x; p.delta = a.delta; p.A = a.A; p.B = a.B; p.C = a.C; p.D = a.D; p.z = a.z;
+  p.out = a.out;
+  p.batch = a.batch; p.L = a.L; p.N = a.N;
+  p.lpr = lanes_per_row(a.N);
+  return p;
+}
+
+// vector accesses: whole groups of 4 states, 16-byte aligned state/A, B/C aligned to 4 elements
+bool vec_ok(const UpdateArgs& a, bool mamba1) {
+  auto al = [](const void* q, uintptr_t m) { return (reinterpret_cast<uintptr_t>(q) & (m - 1)) == 0; };
+  const uintptr_t bc = a.io == 1 ? 8 : 16;
+  return a.N % 4 == 0 && al(a.state, 16) && (!mamba1 || al(a.A, 16)) && al(a.B, bc) && al(a.C, bc);
+}
+
+}  // namespace
+
+hipError_t scan_update_launch(const UpdateArgs& a, hipStream_t stream) {
+  UpdParams p = common(a);
+  p.dim = a.dim;
+  p.rows = a.batch * a.dim;
+  const dim3 grid(static_cast<unsigned>(update_grid_blocks(p.rows, a.N)));
+  const bool vec = vec_ok(a, true);
+  if (a.io == 1) {
+    if (vec) hipLaunchKernelGGL((scan_update_kernel<uint16_t, true>), grid, dim3(kThreads), 0, stream, p);
+    else hipLaunchKernelGGL((scan_update_kernel<uint16_t, false>), grid, dim3(kThreads), 0, stream, p);
+  } else {
+    if (vec) hipLaunchKernelGGL((scan_update_kernel<float, true>), grid, dim3(kThreads), 0, stream, p);
+    else hipLaunchKernelGGL((scan_update_kernel<float, false>), grid, dim3(kThreads), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t ssd_update_launch(const UpdateArgs& a, hipStream_t stream) {
+  UpdParams p = common(a);
+  p.H = a.H; p.P = a.P; p.G = a.G;
+  p.rows = a.batch * a.H * a.P;
+  const dim3 grid(static_cast<unsigned>(update_grid_blocks(p.rows, a.N)));
+  const bool vec = vec_ok(a, false);
+  if (a.io == 1) {
+    if (vec) hipLaunchKernelGGL((ssd_update_kernel<uint16_t, true>), grid, dim3(kThreads), 0, stream, p);
+    else hipLaunchKernelGGL((ssd_update_kernel<uint16_t, false>), grid, dim3(kThreads), 0, stream, p);
+  } else {
+    if (vec) hipLaunchKernelGGL((ssd_update_kernel<float, true>), grid, dim3(kThreads), 0, stream, p);
+    else hipLaunchKernelGGL((ssd_update_kernel<float, false>), grid, dim3(kThreads), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+int64_t update_grid_blocks(int64_t rows, int64_t N) {
+  // R rows per thread: the grid spans ceil(rows / R) rows of lanes
+  return ((rows + R - 1) / R * lanes_per_row(N) + kThreads - 1) / kThreads;
+}
+
+}  // namespace mssm

@@ -62,4 +62,28 @@ struct SSDArgs {
 size_t ssd_workspace_bytes(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q);
 hipError_t ssd_launch(const SSDArgs& a, hipStream_t stream);
 
+// ---------------------------------------------------------------------------
+// Token-by-token state update (both forms), state read and written in place
+// ---------------------------------------------------------------------------
+struct UpdateArgs {
+  float* state;
+  const void* x;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;       // nullable
+  const void* z;        // nullable
+  void* out;
+  int64_t batch, L, N;
+  int64_t dim;          // Mamba-1
+  int64_t H, P, G;      // multi-head form
+  int io;               // 0 fp32, 1 bf16
+};
+
+hipError_t scan_update_launch(const UpdateArgs& a, hipStream_t stream);
+hipError_t ssd_update_launch(const UpdateArgs& a, hipStream_t stream);
+// blocks the update kernels launch for `rows` state rows of N states
+int64_t update_grid_blocks(int64_t rows, int64_t N);
+
 }  // namespace mssm

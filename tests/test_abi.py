@@ -174,3 +174,82 @@ def test_ssd_pointer_checks():
     assert _ssd_call(d, x=None) == M.MSSM_ERR_INVALID_ARG
     assert _ssd_call(d, x=BASE + 8) == M.MSSM_ERR_MISALIGNED
     assert _ssd_call(d, out=BASE + 16) == M.MSSM_ERR_INVALID_ARG
+
+
+def _upd_call(desc, state=BASE + 600 * MB, x=BASE, delta=BASE + 100 * MB, A=BASE + 200 * MB, B=BASE + 300 * MB,
+              C=BASE + 400 * MB, D=None, z=None, out=BASE + 500 * MB):
+    return M.lib.mssm_selective_state_update(ctypes.byref(desc) if desc is not None else None, state, x, delta, A,
+                                             B, C, D, z, out, None)
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("null_desc", M.MSSM_ERR_INVALID_ARG),
+    ("null_state", M.MSSM_ERR_INVALID_ARG),
+    ("null_x", M.MSSM_ERR_INVALID_ARG),
+    ("misaligned_state", M.MSSM_ERR_MISALIGNED),
+    ("misaligned_x", M.MSSM_ERR_MISALIGNED),
+    ("state_aliases_x", M.MSSM_ERR_INVALID_ARG),
+    ("out_aliases_state", M.MSSM_ERR_INVALID_ARG),
+    ("bad_dtype", M.MSSM_ERR_UNSUPPORTED),
+    ("dstate_big", M.MSSM_ERR_UNSUPPORTED),
+])
+def test_state_update_validation(case, expect):
+    d = small(seqlen=1)
+    kw = {}
+    if case == "null_desc":
+        d = None
+    elif case == "null_state":
+        kw["state"] = None
+    elif case == "null_x":
+        kw["x"] = None
+    elif case == "misaligned_state":
+        kw["state"] = BASE + 600 * MB + 2
+    elif case == "misaligned_x":
+        kw["x"] = BASE + 1
+    elif case == "state_aliases_x":
+        kw["state"] = BASE + 32
+    elif case == "out_aliases_state":
+        kw["out"] = BASE + 600 * MB + 8
+    elif case == "bad_dtype":
+        d = small(seqlen=1, io_dtype=5)
+    elif case == "dstate_big":
+        d = small(seqlen=1, dstate=300, split_state=0)
+    assert _upd_call(d, **kw) == expect
+
+
+def test_state_update_empty_is_a_noop():
+    # no tokens, or no batch: nothing to do, returns before touching HIP (null pointers allowed)
+    for d in (small(seqlen=0), small(batch=0)):
+        assert M.lib.mssm_selective_state_update(ctypes.byref(d), None, None, None, None, None, None, None, None,
+                                                 None, None) == M.MSSM_OK
+    s = M.ssd_desc(2, 0, 4, 64, 64, 1, 0)
+    assert M.lib.mssm_ssd_state_update(ctypes.byref(s), None, None, None, None, None, None, None, None, None,
+                                       None) == M.MSSM_OK
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(nheads=6, ngroups=4), M.MSSM_ERR_UNSUPPORTED),
+    (dict(dstate=300), M.MSSM_ERR_UNSUPPORTED),
+    (dict(io_dtype=7), M.MSSM_ERR_UNSUPPORTED),
+    (dict(headdim=0), M.MSSM_ERR_INVALID_ARG),
+    (dict(batch=-1), M.MSSM_ERR_INVALID_ARG),
+])
+def test_ssd_state_update_validation(kw, expect):
+    a = dict(batch=2, seqlen=1, nheads=4, headdim=64, dstate=64, ngroups=1, chunk=0, io_dtype=M.MSSM_BF16)
+    a.update(kw)
+    d = M.ssd_desc(**a)
+    assert M.lib.mssm_ssd_state_update(ctypes.byref(d), BASE + 600 * MB, BASE, BASE + 100 * MB, BASE + 200 * MB,
+                                       BASE + 300 * MB, BASE + 400 * MB, None, None, BASE + 500 * MB, None) == expect
+
+
+def test_ssd_state_update_pointer_checks():
+    d = M.ssd_desc(2, 1, 4, 64, 64, 1, 0)
+    args = [BASE + 600 * MB, BASE, BASE + 100 * MB, BASE + 200 * MB, BASE + 300 * MB, BASE + 400 * MB, None, None,
+            BASE + 500 * MB, None]
+    call = lambda a: M.lib.mssm_ssd_state_update(ctypes.byref(d), *a)
+    bad = list(args); bad[0] = None
+    assert call(bad) == M.MSSM_ERR_INVALID_ARG              # state missing
+    bad = list(args); bad[0] = BASE + 600 * MB + 1
+    assert call(bad) == M.MSSM_ERR_MISALIGNED
+    bad = list(args); bad[8] = BASE + 600 * MB
+    assert call(bad) == M.MSSM_ERR_INVALID_ARG              # out aliases state

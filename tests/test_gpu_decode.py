@@ -1,0 +1,137 @@
+"""Token-by-token state update (decode) on the GPU, through the C ABI, against the fp64 oracle.
+
+The oracle has no separate decode routine: advancing a state by T tokens is the
+scan over those T tokens started from h0 = state, so the sequence oracle with
+h0 is the reference for both the outputs and the advanced state."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_util import RTOL, check, dev, host64, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def M():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import selective_state_space_17_amd as m
+    return m
+
+
+def scan_update(M, inp):
+    import torch
+    state = dev(inp.h0).clone()
+    out = M.selective_state_update(state, dev(inp.x), dev(inp.delta), dev(inp.A), dev(inp.B), dev(inp.C),
+                                   dev(inp.D), dev(inp.z))
+    torch.cuda.synchronize()
+    return out, state
+
+
+# (batch, tokens, dim, dstate, io, D, z): one and several tokens, dstate from 1 to 256 (odd sizes
+# take the scalar state path), channel counts that leave partial blocks
+CASES = [
+    (1, 1, 64, 16, "f32", True, True),
+    (3, 1, 1536, 16, "bf16", True, True),
+    (2, 3, 100, 16, "f32", False, True),
+    (2, 1, 40, 5, "bf16", True, False),
+    (1, 2, 33, 1, "f32", True, True),
+    (2, 1, 64, 64, "bf16", True, True),
+    (1, 4, 16, 256, "f32", True, True),
+    (2, 1, 24, 48, "bf16", False, False),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "b{}_t{}_d{}_n{}_{}".format(*c[:5]))
+def test_scan_update(M, case):
+    b, t, d, n, io, hd, hz = case
+    cfg = W.scan_config(b, t, d, n, io=io, has_D=hd, has_z=hz, cfg_id=700 + d + n)
+    inp = W.make_scan_inputs(cfg, with_h0=True)
+    say("scan update", case)
+    out, state = scan_update(M, inp)
+    ref, ref_fin = oracle.scan_fwd(inp.x, inp.delta, inp.A, inp.B, inp.C, inp.D, inp.z, inp.h0)
+    check(host64(out), ref, RTOL[io], f"update {case} out")
+    check(host64(state), ref_fin, RTOL[io], f"update {case} state")
+
+
+def test_scan_update_token_by_token_equals_scan(M):
+    """T single-token updates give what one sequence call over the T tokens gives."""
+    import torch
+    cfg = W.scan_config(2, 40, 96, 16, io="f32", cfg_id=711)
+    inp = W.make_scan_inputs(cfg, with_h0=True)
+    full, fin = M.selective_scan_fwd(dev(inp.x), dev(inp.delta), dev(inp.A), dev(inp.B), dev(inp.C), dev(inp.D),
+                                     dev(inp.z), dev(inp.h0), return_final_state=True)
+    state = dev(inp.h0).clone()
+    outs = []
+    for t in range(40):
+        sl = slice(t, t + 1)
+        outs.append(M.selective_state_update(state, dev(inp.x[:, sl]), dev(inp.delta[:, sl]), dev(inp.A),
+                                             dev(inp.B[:, sl]), dev(inp.C[:, sl]), dev(inp.D), dev(inp.z[:, sl])))
+    torch.cuda.synchronize()
+    check(host64(torch.cat(outs, dim=1)), host64(full), 1e-5, "token-by-token out")
+    check(host64(state), host64(fin), 1e-5, "token-by-token state")
+
+
+def test_scan_update_zero_delta_keeps_state(M):
+    import torch
+    cfg = W.scan_config(2, 1, 64, 16, io="bf16", cfg_id=712)
+    inp = W.make_scan_inputs(cfg, with_h0=True)
+    inp.delta[:] = 0
+    _, state = scan_update(M, inp)
+    assert np.array_equal(state.cpu().numpy(), inp.h0), "delta = 0 must leave the state bitwise unchanged"
+
+
+def ssd_update(M, s):
+    import torch
+    state = dev(s.h0).clone()
+    out = M.ssd_state_update(state, dev(s.x), dev(s.delta), dev(s.A), dev(s.B), dev(s.C), dev(s.D), dev(s.z))
+    torch.cuda.synchronize()
+    return out, state
+
+
+# (batch, tokens, nheads, headdim, dstate, ngroups, io, D, z)
+SSD_CASES = [
+    (2, 1, 4, 64, 128, 1, "bf16", True, True),
+    (1, 1, 32, 64, 128, 1, "bf16", False, False),
+    (2, 3, 6, 16, 16, 3, "f32", True, True),
+    (1, 2, 2, 3, 5, 1, "f32", True, False),
+    (3, 1, 4, 80, 48, 2, "bf16", False, True),
+    (1, 1, 2, 64, 256, 2, "bf16", True, True),
+]
+
+
+def _ssd_inputs(case, cfg_id):
+    b, t, h, p, n, g, io, hd, hz = case
+    cfg = W.ssd_config(b, t, h, p, n, g, io=io, cfg_id=cfg_id)
+    return W.make_ssd_inputs(cfg, with_D=hd, with_z=hz, with_h0=True)
+
+
+@pytest.mark.parametrize("case", SSD_CASES, ids=lambda c: "b{}_t{}_h{}_p{}_n{}_g{}_{}".format(*c[:7]))
+def test_ssd_update(M, case):
+    s = _ssd_inputs(case, 720 + case[3] + case[4])
+    say("ssd update", case)
+    out, state = ssd_update(M, s)
+    ref, ref_fin = oracle.ssd_fwd(s.x, s.delta, s.A, s.B, s.C, s.D, s.z, s.h0)
+    check(host64(out), ref, RTOL[case[6]], f"ssd update {case} out")
+    check(host64(state), ref_fin, RTOL[case[6]], f"ssd update {case} state")
+
+
+def test_ssd_update_matches_sequence_kernel(M):
+    """Tokens one at a time through the update agree with the chunked matrix-core kernel."""
+    import torch
+    cfg = W.ssd_config(1, 96, 4, 64, 64, 2, cfg_id=730)
+    s = W.make_ssd_inputs(cfg, with_D=True, with_z=True, with_h0=True)
+    full, fin = M.ssd_fwd(dev(s.x), dev(s.delta), dev(s.A), dev(s.B), dev(s.C), dev(s.D), dev(s.z), dev(s.h0),
+                          return_final_state=True)
+    state = dev(s.h0).clone()
+    outs = []
+    for t in range(96):
+        sl = slice(t, t + 1)
+        outs.append(M.ssd_state_update(state, dev(s.x[:, sl]), dev(s.delta[:, sl]), dev(s.A), dev(s.B[:, sl]),
+                                       dev(s.C[:, sl]), dev(s.D), dev(s.z[:, sl])))
+    torch.cuda.synchronize()
+    check(host64(torch.cat(outs, dim=1)), host64(full), 2e-2, "ssd token-by-token out")
+    check(host64(state), host64(fin), 2e-2, "ssd token-by-token state")

@@ -57,13 +57,14 @@ class ScanConfig:
     has_D: bool = True
     has_z: bool = True
     return_final: bool = True
+    decode: bool = False    # token-by-token update of a stored state (read and written in place)
 
     @property
     def updates(self) -> int:
         return self.batch * self.seqlen * self.dim * self.dstate
 
     def algorithmic_bytes(self) -> int:
-        """Every input read once, every output written once."""
+        """Every input read once, every output written once (a decode step also reads the state)."""
         e = 2 if self.io == BF16 else 4
         bld = self.batch * self.seqlen * self.dim
         bln = self.batch * self.seqlen * self.dstate
@@ -74,6 +75,7 @@ class ScanConfig:
         n += self.dim * 4 if self.has_D else 0
         n += bld * e                        # out
         n += self.batch * self.dim * self.dstate * 4 if self.return_final else 0
+        n += self.batch * self.dim * self.dstate * 4 if self.decode else 0
         return n
 
 
@@ -93,6 +95,7 @@ class SSDConfig:
     has_D: bool = False
     has_z: bool = False
     return_final: bool = True
+    decode: bool = False    # token-by-token update of a stored state (read and written in place)
 
     @property
     def updates(self) -> int:
@@ -109,6 +112,7 @@ class SSDConfig:
         n += blhp * e if self.has_z else 0
         n += blhp * e                                           # out
         n += self.batch * self.nheads * self.headdim * self.dstate * 4 if self.return_final else 0
+        n += self.batch * self.nheads * self.headdim * self.dstate * 4 if self.decode else 0
         return n
 
 
@@ -120,6 +124,9 @@ CONFIGS = {
     3: ScanConfig("mamba1_2p8b_layer_bf16", 3, 4, 8192, 5120, 16, BF16, "s4d_real", return_final=True),
     4: SSDConfig("mamba2_ssd_bf16", 4, 8, 4096, 32, 64, 128, 1, 256),
     5: ScanConfig("mamba1_long_1m_bf16", 5, 1, 1 << 20, 2048, 16, BF16, "s4d_real", return_final=True),
+    # decode steps (one new token against a stored state), the configs' layer shapes at serving batch sizes
+    6: ScanConfig("mamba1_2p8b_decode_bf16", 6, 256, 1, 5120, 16, BF16, "s4d_real", return_final=True, decode=True),
+    7: SSDConfig("mamba2_decode_bf16", 7, 64, 1, 32, 64, 128, 1, 64, BF16, True, True, True, decode=True),
 }
 
 

@@ -36,28 +36,30 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_digest(is_ssd: bool) -> str:
+def source_digest(is_ssd: bool, decode: bool = False) -> str:
     """Hash of the sources that make the workload's kernels (counters go stale when it changes)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "selective_state_space_17_amd", "csrc")
-    for f in ("api.cpp", "internal.h", "ssd_m2.hip" if is_ssd else "scan_m1.hip"):
-        h.update(open(os.path.join(csrc, f), "rb").read())
+    kern = "decode.hip" if decode else ("ssd_m2.hip" if is_ssd else "scan_m1.hip")
+    h.update(open(os.path.join(csrc, kern), "rb").read())
     return h.hexdigest()[:16]
 
 
-def kernel_tags(is_ssd: bool):
+def kernel_tags(is_ssd: bool, decode: bool = False):
     """Name fragments of the kernels that carry the workload's scan (the dominant one per launch)."""
+    if decode:
+        return ("ssd_update_kernel",) if is_ssd else ("scan_update_kernel",)
     return ("ssd_kernel",) if is_ssd else ("wide_kernel", "scan_kernel")
 
 
-def load_traffic(workload: str, is_ssd: bool):
+def load_traffic(workload: str, is_ssd: bool, decode: bool = False):
     """HBM bytes per launch of the dominant kernel from committed rocprofv3 counters, if they were
     taken on the current kernel sources (else None)."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     t = json.load(open(path))
-    if t.get("source_digest") != source_digest(is_ssd):
+    if t.get("source_digest") != source_digest(is_ssd, decode):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -73,9 +75,9 @@ def summarize_counters(cfg, is_ssd, d, copy_mib):
     WRITE_SIZE) into HBM bytes per launch of the dominant kernel, each counter scaled by what it
     reads for a device copy of copy_mib MiB, and write profiles/traffic_<workload>.json."""
     import numpy as np
-    tags = kernel_tags(is_ssd)
+    tags = kernel_tags(is_ssd, cfg.decode)
     copy_bytes = copy_mib << 20
-    res = {"workload": cfg.name, "source_digest": source_digest(is_ssd),
+    res = {"workload": cfg.name, "source_digest": source_digest(is_ssd, cfg.decode),
            "copy_bytes": copy_bytes, "algorithmic_bytes_per_launch": cfg.algorithmic_bytes()}
     total = 0.0
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
@@ -293,7 +295,7 @@ def main():
     kern_s = ms * 1e-3
     hbm = {"achieved": alg_bytes / kern_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
            "frac": alg_bytes / kern_s / 1e9 / PEAK_HBM_GBS}
-    traffic = load_traffic(cfg.name, is_ssd)
+    traffic = load_traffic(cfg.name, is_ssd, decode)
     if decode:
         # a few operations per byte of state: the HBM roofline bounds it
         roof = dict(hbm)

@@ -398,10 +398,11 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
     // the 10 causal tiles (i <= j): waves 0 and 1 take two, the others one
     if (w < 2) mask_tile(0, w);
     mask_tile(mi, mj);
-    __syncthreads();
 
-    // state fragments of this wave's half (operand A of the readout: rows p, k = n)
-    bf16x8 sh[NKH], sl[NKH];
+    // Everything that does not need the mask runs in the same interval: the
+    // readout of the carried-in state for all four t-tiles (handing the partner
+    // its two), and the state update.
+    bf16x8 sh[NKH], sl[NKH];   // state fragments of this wave's half (operand A: rows p, k = n)
 #pragma unroll
     for (int m = 0; m < NKH; ++m) {
       const float v[8] = {S[2 * m][0], S[2 * m][1], S[2 * m][2], S[2 * m][3],
@@ -413,14 +414,12 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
 #pragma unroll
     for (int m = 0; m < 2; ++m) xf[m] = frag(&XT[(16 * pt + lc) * QS + 32 * m + l8]);
 
-    // partial Y^T tiles (rows p = 16pt + lq + v, column t = 16j + lc), the hand-over of
-    // the partner's two tiles and the state update; the half nh is a compile-time
-    // constant inside so that tile indices never need run-time selection
-    f32x4 Y[4];
-    auto readout = [&](auto half) {
+    // Y^T tiles this wave finishes (rows p = 16pt + lq + v, column t = 16j + lc); the half
+    // nh is a compile-time constant inside so that tile indices never need run-time selection
+    f32x4 Ya, Yb;
+    auto carried = [&](auto half) {
       constexpr int NH = decltype(half)::value;
       constexpr int JA = NH == 0 ? 0 : 1, JB = NH == 0 ? 3 : 2;    // tiles this wave finishes
-      constexpr int JO0 = NH == 0 ? 1 : 0, JO1 = NH == 0 ? 2 : 3;  // tiles the partner finishes
       constexpr int NB = (NP / 2) * NH;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -434,19 +433,10 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
         const float e = exp2_hw(css[16 * j + lc]);
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc[v] *= e;
-        if (j == JA || j == JB) {
-#pragma unroll
-          for (int m = 0; m < 2; ++m) {
-            if (32 * m <= 16 * j + 15) {
-              acc = mfma16(xf[m], frag(&Ms[0][(16 * j + lc) * QS + 32 * m + l8]), acc);
-              acc = mfma16(xf[m], frag(&Ms[1][(16 * j + lc) * QS + 32 * m + l8]), acc);
-            }
-          }
-        }
-        Y[j] = acc;
+        if (j == JA) Ya = acc;
+        else if (j == JB) Yb = acc;
+        else Xc[(w * 2 + (j == (NH == 0 ? 1 : 0) ? 0 : 1)) * kWave + lane] = acc;   // the partner's tile
       }
-      Xc[(w * 2 + 0) * kWave + lane] = Y[JO0];
-      Xc[(w * 2 + 1) * kWave + lane] = Y[JO1];
 
       // state update of this half: S^T = exp2(s_Q) S^T + B^T Xw  (K = s)
       const float dec = exp2_hw(css[QB - 1]);
@@ -471,24 +461,31 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
         }
       }
     };
-    if (nh == 0) readout(std::integral_constant<int, 0>{});
-    else readout(std::integral_constant<int, 1>{});
-    __syncthreads();
+    if (nh == 0) carried(std::integral_constant<int, 0>{});
+    else carried(std::integral_constant<int, 1>{});
+    __syncthreads();   // the mask and the partner's partial tiles are complete
 
-    // finish two t-tiles: own partial + partner's, then + D x, * silu(z)
+    // finish two t-tiles: + X^T M^T, + the partner's partial, + D x, * silu(z)
     auto finish = [&](auto half) {
       constexpr int NH = decltype(half)::value;
       constexpr int JA = NH == 0 ? 0 : 1, JB = NH == 0 ? 3 : 2;
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const int j = k == 0 ? JA : JB;
+        f32x4 acc = k == 0 ? Ya : Yb;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          if (32 * m <= 16 * j + 15) {
+            acc = mfma16(xf[m], frag(&Ms[0][(16 * j + lc) * QS + 32 * m + l8]), acc);
+            acc = mfma16(xf[m], frag(&Ms[1][(16 * j + lc) * QS + 32 * m + l8]), acc);
+          }
+        }
         const f32x4 o = Xc[(partner * 2 + k) * kWave + lane];
         const int t = 16 * j + lc;
         const int pl = 16 * pt + lq;
         const u32x2 xv = *reinterpret_cast<const u32x2*>(&Xs[buf][t * QS + pl]);
-        const f32x4 yj = Y[k == 0 ? JA : JB];
-        float y[4] = {yj[0] + o[0] + Dh * lo_f(xv[0]), yj[1] + o[1] + Dh * hi_f(xv[0]),
-                      yj[2] + o[2] + Dh * lo_f(xv[1]), yj[3] + o[3] + Dh * hi_f(xv[1])};
+        float y[4] = {acc[0] + o[0] + Dh * lo_f(xv[0]), acc[1] + o[1] + Dh * hi_f(xv[0]),
+                      acc[2] + o[2] + Dh * lo_f(xv[1]), acc[3] + o[3] + Dh * hi_f(xv[1])};
         if (has_z) {
           const u32x2 zv = *reinterpret_cast<const u32x2*>(&Zs[buf][t * QS + pl]);
           const float zz[4] = {lo_f(zv[0]), hi_f(zv[0]), lo_f(zv[1]), hi_f(zv[1])};

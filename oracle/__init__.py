@@ -13,6 +13,10 @@ leg may import this package.  The product library never uses it.
                  (mssm_oracle.c: oracle_ssd_fwd).  Pinned by: equality with the
                  Mamba-1 oracle under head broadcast, the geometric closed form
                  with scalar A, a brute-force unrolled sum, chaining.
+``scan_bwd``  -- gradients of ``scan_fwd`` by reverse mode through the same
+                 sequential loop, fp64 (mssm_oracle.c: oracle_scan_bwd).  Pinned
+                 by central finite differences of ``scan_fwd`` itself
+                 (tests/pins.py: pin_scan_bwd_finite_differences).
 Both take the already-rounded inputs the GPU receives (bf16 bit patterns are
 decoded by the C code's own codec) and return fp64 results.
 """
@@ -48,6 +52,8 @@ def load_library(path: Optional[str] = None):
     lib.oracle_scan_fwd.argtypes = [i64, i64, i64, i64, i32, p, p, p, p, p, p, p, p, i64, i64, p, p, i32]
     lib.oracle_ssd_fwd.restype = i32
     lib.oracle_ssd_fwd.argtypes = [i64, i64, i64, i64, i64, i64, i32, p, p, p, p, p, p, p, p, i64, i64, p, p, i32]
+    lib.oracle_scan_bwd.restype = i32
+    lib.oracle_scan_bwd.argtypes = [i64, i64, i64, i64, i32] + [p] * 10 + [p] * 8 + [i32]
     return lib
 
 
@@ -127,3 +133,39 @@ def ssd_fwd(x, delta, A, B, C, D=None, z=None, h0=None, hd0: int = 0, hd1: Optio
     if rc != 0:
         raise ValueError("oracle_ssd_fwd rejected its arguments")
     return out, fin
+
+
+def scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, dout=None, dfinal=None,
+             nthreads: Optional[int] = None, lib=None):
+    """Gradients of the Mamba-1 selective scan for the loss sum(out * dout) + sum(final_state * dfinal).
+
+    Shapes as in ``scan_fwd``; ``dout`` [Bsz, L, Dm] in the io dtype, ``dfinal`` [Bsz, Dm, N] fp32 (either
+    may be None: zero).  Returns a dict of fp64 arrays: dx, ddelta, dA, dB, dC, dD (None without D),
+    dz (None without z), dh0 [Bsz, Dm, N].
+    """
+    x, delta, B, C, z = _c(x), _c(delta), _c(B), _c(C), _c(z)
+    io = _io_code(x)
+    for t in (delta, B, C) + ((z,) if z is not None else ()):
+        if _io_code(t) != io:
+            raise TypeError("x, delta, B, C, z must share one dtype")
+    A, D, h0, dfinal = _c(A, np.float32), _c(D, np.float32), _c(h0, np.float32), _c(dfinal, np.float32)
+    bsz, L, dm = x.shape
+    N = A.shape[1]
+    if dout is None:
+        dout = np.zeros_like(x)
+    dout = _c(dout)
+    if _io_code(dout) != io:
+        raise TypeError("dout must share the io dtype")
+    g = {
+        "dx": np.empty((bsz, L, dm)), "ddelta": np.empty((bsz, L, dm)), "dA": np.empty((dm, N)),
+        "dB": np.empty((bsz, L, N)), "dC": np.empty((bsz, L, N)),
+        "dD": np.empty(dm) if D is not None else None, "dz": np.empty((bsz, L, dm)) if z is not None else None,
+        "dh0": np.empty((bsz, dm, N)),
+    }
+    rc = (lib or _get()).oracle_scan_bwd(
+        bsz, L, dm, N, io, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+        _ptr(dout), _ptr(dfinal), _ptr(g["dx"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
+        _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["dh0"]), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_scan_bwd rejected its arguments")
+    return g

@@ -219,3 +219,152 @@ int oracle_ssd_fwd(int64_t Bsz, int64_t L, int64_t H, int64_t P, int64_t N, int6
     free(th);
     return 0;
 }
+
+/* ------------------------------------------------------------------------- */
+/* Mamba-1 selective scan: gradients (reverse mode through the same loop)    */
+/* ------------------------------------------------------------------------- */
+/*
+ * The derivative of the forward definition above, taken step by step in
+ * reverse time ("P20 - Mamba", 5: the selective recurrence; training needs
+ * its gradients, which the pages discuss only as the cost of the method).
+ * With a_t[n] = exp(delta_t A[n]), h_t = a_t h_{t-1} + delta_t B_t x_t,
+ * y_t = C_t . h_t + D x_t and out_t = y_t silu(z_t), for an upstream gradient
+ * g_t = dLoss/dout_t and dLoss/dfinal_state:
+ *   dy_t          = g_t silu(z_t),  dz_t = g_t y_t silu'(z_t)
+ *   lam_t         = C_t dy_t + a_{t+1} lam_{t+1}       (adjoint of h_t; lam_L = dfinal)
+ *   dC_t[n]      += dy_t h_t[n]        (summed over channels)
+ *   dB_t[n]      += lam_t[n] delta_t x_t   (summed over channels)
+ *   ddelta_t      = sum_n lam_t[n] (h_{t-1}[n] a_t[n] A[n] + B_t[n] x_t)
+ *   dx_t          = D dy_t + sum_n lam_t[n] delta_t B_t[n]
+ *   dA[n]        += lam_t[n] h_{t-1}[n] a_t[n] delta_t   (summed over batch and time)
+ *   dD           += dy_t x_t                             (summed over batch and time)
+ *   dh0[n]        = a_0[n] lam_0[n]
+ * Plain, sequential, fp64; every forward state of a row is kept (no
+ * recomputation), rows of one batch entry are walked in turn by one thread.
+ */
+typedef struct {
+    int64_t Bsz, L, D, N;
+    int io;
+    const void *x, *delta, *Bm, *Cm, *z, *dout;
+    const float *A, *Dv, *h0, *dfinal;
+    double *dx, *ddelta, *dA, *dB, *dC, *dD, *dz, *dh0;   /* dA, dD: this thread's partial sums */
+    int64_t b_begin, b_end;
+} bwd_job;
+
+static double dsilu(double v) {
+    const double s = 1.0 / (1.0 + exp(-v));
+    return s * (1.0 + v * (1.0 - s));
+}
+
+static void* bwd_worker(void* arg) {
+    const bwd_job* j = (const bwd_job*)arg;
+    const int64_t N = j->N, D = j->D, L = j->L;
+    double* hs = (double*)malloc(sizeof(double) * (size_t)((L + 1) * N));   /* h_{-1..L-1} */
+    double* ys = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+    double* lam = (double*)malloc(sizeof(double) * (size_t)N);
+    for (int64_t b = j->b_begin; b < j->b_end; ++b) {
+        for (int64_t c = 0; c < D; ++c) {
+            /* forward, keeping every state: hs[(t + 1) * N + n] = h_t[n] */
+            for (int64_t n = 0; n < N; ++n) hs[n] = j->h0 ? (double)j->h0[(b * D + c) * N + n] : 0.0;
+            for (int64_t t = 0; t < L; ++t) {
+                const int64_t i = (b * L + t) * D + c, r = (b * L + t) * N;
+                const double d = load_io(j->delta, j->io, i), u = load_io(j->x, j->io, i);
+                double acc = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    const double h = exp(d * (double)j->A[c * N + n]) * hs[t * N + n] +
+                                     d * load_io(j->Bm, j->io, r + n) * u;
+                    hs[(t + 1) * N + n] = h;
+                    acc += load_io(j->Cm, j->io, r + n) * h;
+                }
+                ys[t] = acc + (j->Dv ? (double)j->Dv[c] * u : 0.0);
+            }
+            /* reverse */
+            for (int64_t n = 0; n < N; ++n) lam[n] = j->dfinal ? (double)j->dfinal[(b * D + c) * N + n] : 0.0;
+            for (int64_t t = L - 1; t >= 0; --t) {
+                const int64_t i = (b * L + t) * D + c, r = (b * L + t) * N;
+                const double d = load_io(j->delta, j->io, i), u = load_io(j->x, j->io, i);
+                const double g = load_io(j->dout, j->io, i);
+                double dy = g;
+                if (j->z) {
+                    const double zz = load_io(j->z, j->io, i);
+                    dy = g * silu(zz);
+                    j->dz[i] = g * ys[t] * dsilu(zz);
+                }
+                double du = 0.0, dd = 0.0;
+                if (j->Dv) {
+                    du = dy * (double)j->Dv[c];
+                    j->dD[c] += dy * u;
+                }
+                for (int64_t n = 0; n < N; ++n) {
+                    const double An = (double)j->A[c * N + n];
+                    const double a = exp(d * An);
+                    const double Bn = load_io(j->Bm, j->io, r + n), Cn = load_io(j->Cm, j->io, r + n);
+                    const double h = hs[(t + 1) * N + n], hprev = hs[t * N + n];
+                    lam[n] += Cn * dy;                         /* adjoint of h_t */
+                    j->dC[r + n] += dy * h;
+                    j->dB[r + n] += lam[n] * d * u;
+                    dd += lam[n] * (hprev * a * An + Bn * u);
+                    du += lam[n] * d * Bn;
+                    j->dA[c * N + n] += lam[n] * hprev * a * d;
+                    lam[n] *= a;                               /* adjoint of h_{t-1} */
+                }
+                j->ddelta[i] = dd;
+                j->dx[i] = du;
+            }
+            for (int64_t n = 0; n < N; ++n) j->dh0[(b * D + c) * N + n] = lam[n];
+        }
+    }
+    free(hs);
+    free(ys);
+    free(lam);
+    return NULL;
+}
+
+/*
+ * Gradients of the selective scan for upstream gradients dout [Bsz, L, D] (io
+ * dtype) and dfinal [Bsz, D, N] fp32 (nullable).  Outputs fp64: dx, ddelta,
+ * dz [Bsz, L, D]; dB, dC [Bsz, L, N]; dA [D, N]; dD [D]; dh0 [Bsz, D, N]
+ * (dz and dD are written only when z and Dv are given).  Returns 0, or -1 on
+ * bad sizes.
+ */
+int oracle_scan_bwd(int64_t Bsz, int64_t L, int64_t D, int64_t N, int io,
+                    const void* x, const void* delta, const float* A, const void* Bm, const void* Cm,
+                    const float* Dv, const void* z, const float* h0, const void* dout, const float* dfinal,
+                    double* dx, double* ddelta, double* dA, double* dB, double* dC, double* dD, double* dz,
+                    double* dh0, int nthreads) {
+    if (Bsz < 0 || L < 0 || D <= 0 || N <= 0) return -1;
+    if (io != IO_F32 && io != IO_BF16) return -1;
+    memset(dA, 0, sizeof(double) * (size_t)(D * N));
+    if (dD) memset(dD, 0, sizeof(double) * (size_t)D);
+    memset(dB, 0, sizeof(double) * (size_t)(Bsz * L * N));
+    memset(dC, 0, sizeof(double) * (size_t)(Bsz * L * N));
+    if (Bsz == 0) return 0;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > Bsz) nthreads = (int)Bsz;
+    bwd_job* jobs = (bwd_job*)calloc((size_t)nthreads, sizeof(bwd_job));
+    pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+    for (int k = 0; k < nthreads; ++k) {
+        bwd_job* j = &jobs[k];
+        j->Bsz = Bsz; j->L = L; j->D = D; j->N = N; j->io = io;
+        j->x = x; j->delta = delta; j->Bm = Bm; j->Cm = Cm; j->z = z; j->dout = dout;
+        j->A = A; j->Dv = Dv; j->h0 = h0; j->dfinal = dfinal;
+        j->dx = dx; j->ddelta = ddelta; j->dB = dB; j->dC = dC; j->dz = dz; j->dh0 = dh0;
+        j->dA = (double*)calloc((size_t)(D * N), sizeof(double));
+        j->dD = (double*)calloc((size_t)D, sizeof(double));
+        j->b_begin = Bsz * k / nthreads;
+        j->b_end = Bsz * (k + 1) / nthreads;
+    }
+    for (int k = 1; k < nthreads; ++k) pthread_create(&th[k], NULL, bwd_worker, &jobs[k]);
+    bwd_worker(&jobs[0]);
+    for (int k = 1; k < nthreads; ++k) pthread_join(th[k], NULL);
+    for (int k = 0; k < nthreads; ++k) {
+        for (int64_t e = 0; e < D * N; ++e) dA[e] += jobs[k].dA[e];
+        if (dD)
+            for (int64_t e = 0; e < D; ++e) dD[e] += jobs[k].dD[e];
+        free(jobs[k].dA);
+        free(jobs[k].dD);
+    }
+    free(jobs);
+    free(th);
+    return 0;
+}

@@ -18,6 +18,9 @@ Passages (page title, section):
                        Bbar_t x_t unrolled into a sum of products.
   chaining             the fixed-size state is the whole memory
                        ("Mamba-2 y state-space models" 4.3 notes).
+  gradients            the reverse-mode derivative of the scan must equal
+                       central finite differences of the (separately pinned)
+                       forward oracle, for every input and both outputs.
 """
 from __future__ import annotations
 
@@ -358,7 +361,82 @@ def pin_ssd_chaining(lib, seed=14):
     _close(fin2, fin, 1e-6, "SSD chaining final")
 
 
+# ---------------------------------------------------------------------------
+# Gradients of the Mamba-1 scan
+# ---------------------------------------------------------------------------
+def _fd_case(rng, bsz=2, L=9, d=3, n=4):
+    x = rng.standard_normal((bsz, L, d)).astype(np.float32)
+    delta = rng.uniform(0.05, 0.9, size=(bsz, L, d)).astype(np.float32)
+    A = _neg_A(rng, d, n)
+    B = rng.standard_normal((bsz, L, n)).astype(np.float32)
+    C = rng.standard_normal((bsz, L, n)).astype(np.float32)
+    D = rng.standard_normal(d).astype(np.float32)
+    z = rng.standard_normal((bsz, L, d)).astype(np.float32)
+    h0 = rng.standard_normal((bsz, d, n)).astype(np.float32)
+    return dict(x=x, delta=delta, A=A, B=B, C=C, D=D, z=z, h0=h0)
+
+
+def pin_scan_bwd_finite_differences(lib, seed=21):
+    """d/dv [sum(out * R) + sum(final * Rf)] by central differences of scan_fwd, for every element v of
+    every input, against scan_bwd.  The step is a power of two; the difference quotient divides by the
+    step the fp32 inputs actually took, so input rounding does not enter."""
+    rng = _rng(seed)
+    for with_dz, with_h0, with_fin in ((True, True, True), (False, False, True), (True, True, False)):
+        inp = _fd_case(rng)
+        if not with_dz:
+            inp["D"] = None
+            inp["z"] = None
+        if not with_h0:
+            inp["h0"] = None
+        R = rng.standard_normal(inp["x"].shape).astype(np.float32)
+        Rf = rng.standard_normal((inp["x"].shape[0], inp["x"].shape[2], inp["A"].shape[1])).astype(np.float32)
+        if not with_fin:
+            Rf = np.zeros_like(Rf)
+
+        def loss(**kw):
+            out, fin = oracle.scan_fwd(**kw, lib=lib, nthreads=1)
+            return float(np.sum(out * R.astype(np.float64)) + np.sum(fin * Rf.astype(np.float64)))
+
+        g = oracle.scan_bwd(**inp, dout=R, dfinal=Rf if with_fin else None, lib=lib, nthreads=2)
+        names = [k for k in ("x", "delta", "A", "B", "C", "D", "z", "h0") if inp[k] is not None]
+        for k in names:
+            base = inp[k]
+            fd = np.zeros(base.shape)
+            for idx in np.ndindex(base.shape):
+                step = np.float32(2.0 ** -12) * max(np.float32(1.0), np.abs(base[idx]))
+                vals = []
+                for sgn in (1, -1):
+                    pert = dict(inp)
+                    arr = base.copy()
+                    arr[idx] = base[idx] + np.float32(sgn) * step
+                    pert[k] = arr
+                    vals.append((loss(**pert), float(arr[idx])))
+                fd[idx] = (vals[0][0] - vals[1][0]) / (vals[0][1] - vals[1][1])
+            got = g["d" + k]
+            _close(got, fd, 2e-6, f"scan gradient d{k} (D/z {with_dz}, h0 {with_h0}, final {with_fin})")
+        if not with_dz:
+            assert g["dD"] is None and g["dz"] is None
+
+
+def pin_scan_bwd_linear_in_upstream(lib, seed=22):
+    """The gradients are linear in (dout, dfinal), and a zero upstream gradient gives zero gradients."""
+    rng = _rng(seed)
+    inp = _fd_case(rng, bsz=3, L=17, d=2, n=5)
+    shp_f = (3, 2, 5)
+    R1, R2 = rng.standard_normal(inp["x"].shape).astype(np.float32), rng.standard_normal(inp["x"].shape).astype(np.float32)
+    F1, F2 = rng.standard_normal(shp_f).astype(np.float32), rng.standard_normal(shp_f).astype(np.float32)
+    g1 = oracle.scan_bwd(**inp, dout=R1, dfinal=F1, lib=lib)
+    g2 = oracle.scan_bwd(**inp, dout=R2, dfinal=F2, lib=lib)
+    g12 = oracle.scan_bwd(**inp, dout=R1 + R2, dfinal=F1 + F2, lib=lib)
+    for k in g1:
+        _close(g12[k], g1[k] + g2[k], 1e-6, f"gradient linearity d{k[1:]}")
+    g0 = oracle.scan_bwd(**inp, lib=lib)
+    for k, v in g0.items():
+        assert np.all(v == 0), f"zero upstream gradient gave nonzero {k}"
+
+
 SCAN_PINS = [pin_lti_convolution, pin_delta_zero, pin_geometric, pin_bruteforce, pin_chaining, pin_reset,
              pin_linearity_causality, pin_gate_skip, pin_bf16_codec]
 SSD_PINS = [pin_ssd_equals_broadcast_scan, pin_ssd_geometric, pin_ssd_bruteforce, pin_ssd_chaining]
-ALL_PINS = SCAN_PINS + SSD_PINS
+BWD_PINS = [pin_scan_bwd_finite_differences, pin_scan_bwd_linear_in_upstream]
+ALL_PINS = SCAN_PINS + SSD_PINS + BWD_PINS

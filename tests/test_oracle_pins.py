@@ -42,6 +42,19 @@ MUTANTS = {
     "ssd_input_without_delta": ("a * S[p * N + n] + d * load_io(j->Bm", "a * S[p * N + n] + load_io(j->Bm"),
     "ssd_h0_layout": ("j->h0[((b * H + hd) * P + p) * N + n]", "j->h0[((b * H + hd) * N + (n % P)) * P + (p % N)]"),
     "ssd_skip_dropped": ("(j->Dv ? (double)j->Dv[hd] * u : 0.0)", "0.0"),
+    # gradients
+    "bwd_no_adjoint_decay": ("lam[n] *= a;", ";"),
+    "bwd_dsilu_is_sigmoid": ("return s * (1.0 + v * (1.0 - s));", "return s;"),
+    "bwd_dB_without_delta": ("j->dB[r + n] += lam[n] * d * u;", "j->dB[r + n] += lam[n] * u;"),
+    "bwd_dC_previous_state": ("j->dC[r + n] += dy * h;", "j->dC[r + n] += dy * hprev;"),
+    "bwd_adjoint_from_B": ("lam[n] += Cn * dy;", "lam[n] += Bn * dy;"),
+    "bwd_ddelta_without_A": ("hprev * a * An", "hprev * a"),
+    "bwd_dA_without_delta": ("lam[n] * hprev * a * d;", "lam[n] * hprev * a;"),
+    "bwd_gate_sees_no_skip": ("ys[t] = acc + ", "ys[t] = acc + 0.0 * "),
+    "bwd_dx_skip_dropped": ("du = dy * (double)j->Dv[c];", "du = 0.0;"),
+    "bwd_dD_ungated": ("j->dD[c] += dy * u;", "j->dD[c] += g * u;"),
+    "bwd_dx_without_delta": ("du += lam[n] * d * Bn;", "du += lam[n] * Bn;"),
+    "bwd_dfinal_ignored": ("j->dfinal ? (double)j->dfinal[(b * D + c) * N + n] : 0.0", "0.0"),
 }
 
 

@@ -3,7 +3,8 @@
  *
  * Two forward operations, each with a token-by-token (decode) counterpart
  * that advances a stored state in place (mssm_selective_state_update,
- * mssm_ssd_state_update):
+ * mssm_ssd_state_update), and the gradients of the first
+ * (mssm_selective_scan_bwd):
  *
  *  1. mssm_selective_scan_fwd -- the Mamba-1 selective scan.  Defined by the
  *     linear state recurrence h_t = A h_{t-1} + B x_t with readout y_t = C h_t
@@ -167,6 +168,43 @@ int mssm_ssd_state_update(const mssm_ssd_desc* desc, float* state,
                           const void* x, const void* delta, const float* A,
                           const void* B, const void* C, const float* D, const void* z,
                           void* out, void* stream);
+
+/* Gradients of mssm_selective_scan_fwd (reverse mode through the same
+ * recurrence; training a selective SSM needs them, "P20 - Mamba", 5).  For
+ * the loss sum(out * dout) + sum(final_state * dfinal) it writes
+ *   dx, ddelta, dz : [batch, seqlen, dim]     (io_dtype)
+ *   dB, dC         : [batch, seqlen, dstate]  fp32 (summed over channels)
+ *   dA             : [dim, dstate] fp32,  dD : [dim] fp32 (summed over batch and time)
+ *   dh0            : [batch, dim, dstate] fp32 (nullable: not written)
+ * from the forward inputs (same layouts as mssm_selective_scan_fwd; h0 nullable
+ * = zero) and the upstream gradients
+ *   dout           : [batch, seqlen, dim]     (io_dtype)
+ *   dfinal         : [batch, dim, dstate] fp32, nullable (= zero).
+ * dz is required when z is given and dD when D is given (each is ignored, and
+ * may be NULL, otherwise).  With y = sum_n C h + D x and out = y silu(z):
+ *   dy = dout silu(z); lam_t = C_t dy_t + exp(delta_{t+1} A) lam_{t+1}
+ *   (lam after the last step = dfinal); dC_t = sum_c dy_t h_t;
+ *   dB_t = sum_c lam_t delta_t x_t; dz = dout y silu'(z); dh0 = exp(delta_0 A) lam_0.
+ * The states are recomputed from h0 (nothing is kept from the forward call).
+ * dstate must be at most 16 (MSSM_ERR_UNSUPPORTED otherwise); split_seq and
+ * split_state are ignored.  The result is deterministic: every sum is taken
+ * in a fixed order.  workspace: at least
+ * mssm_selective_scan_bwd_workspace_size(desc) bytes, 256-byte aligned (about
+ * 4 * batch * dim * dstate * (seqlen / 16) bytes of state checkpoints plus
+ * 128 * batch * seqlen * ceil(dim / 16) bytes of per-block partial sums).
+ * Outputs and workspace must not alias any input or each other.  Same
+ * ownership, stream and error rules as mssm_selective_scan_fwd. */
+int mssm_selective_scan_bwd(const mssm_scan_desc* desc,
+                            const void* x, const void* delta, const float* A,
+                            const void* B, const void* C, const float* D, const void* z,
+                            const float* h0, const void* dout, const float* dfinal,
+                            void* dx, void* ddelta, float* dA, float* dB, float* dC, float* dD,
+                            void* dz, float* dh0,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace mssm_selective_scan_bwd needs (0 for an invalid or
+ * unsupported descriptor). */
+size_t mssm_selective_scan_bwd_workspace_size(const mssm_scan_desc* desc);
 
 /* The plan the library would use for a selective-scan descriptor:
  * writes the sequence-chunk count and lanes-per-channel; returns a status. */

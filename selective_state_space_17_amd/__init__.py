@@ -48,6 +48,8 @@ SIGNATURES = {
     "mssm_ssd_workspace_size": (_SZ, [ctypes.POINTER(SSDDesc)]),
     "mssm_selective_state_update": (_I, [ctypes.POINTER(ScanDesc)] + [_P] * 10),
     "mssm_ssd_state_update": (_I, [ctypes.POINTER(SSDDesc)] + [_P] * 10),
+    "mssm_selective_scan_bwd": (_I, [ctypes.POINTER(ScanDesc)] + [_P] * 18 + [_P, _SZ, _P]),
+    "mssm_selective_scan_bwd_workspace_size": (_SZ, [ctypes.POINTER(ScanDesc)]),
     "mssm_status_string": (ctypes.c_char_p, [_I]),
     "mssm_last_error_detail": (ctypes.c_char_p, []),
     "mssm_abi_version": (_I, []),
@@ -184,6 +186,62 @@ def selective_scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, return_final_
     if st != MSSM_OK:
         raise MssmError(st, "mssm_selective_scan_fwd")
     return (out, final_state) if return_final_state else out
+
+
+def selective_scan_bwd_workspace_size(batch, seqlen, dim, dstate, io_dtype=MSSM_BF16) -> int:
+    d = scan_desc(batch, seqlen, dim, dstate, io_dtype)
+    return lib.mssm_selective_scan_bwd_workspace_size(ctypes.byref(d))
+
+
+def selective_scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, dout=None, dfinal=None, want_dh0: bool = True,
+                       workspace=None, stream=None):
+    """Gradients of the Mamba-1 selective scan (mssm_selective_scan_bwd), for the loss
+    sum(out * dout) + sum(final_state * dfinal).
+
+    Inputs as in selective_scan_fwd; dout [batch, seqlen, dim] in the io dtype; dfinal
+    [batch, dim, dstate] float32 or None.  Returns a dict: dx, ddelta, dz (io dtype, dz None without z),
+    dB, dC [batch, seqlen, dstate] float32, dA [dim, dstate] float32, dD [dim] float32 (None without D),
+    dh0 [batch, dim, dstate] float32 (None unless want_dh0).
+    """
+    torch = _torch()
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, seqlen, dim]")
+    bsz, L, dm = x.shape
+    if A.dim() != 2 or A.shape[0] != dm:
+        raise ValueError("A must be [dim, dstate]")
+    N = A.shape[1]
+    io = _io_code(x.dtype)
+    if dout is None:
+        raise ValueError("dout is required")
+    for name, t, shape in (("x", x, (bsz, L, dm)), ("delta", delta, (bsz, L, dm)), ("z", z, (bsz, L, dm)),
+                           ("B", B, (bsz, L, N)), ("C", C, (bsz, L, N)), ("dout", dout, (bsz, L, dm))):
+        _check_gpu(name, t, x.dtype, shape)
+    _check_gpu("A", A, torch.float32, (dm, N))
+    _check_gpu("D", D, torch.float32, (dm,))
+    _check_gpu("h0", h0, torch.float32, (bsz, dm, N))
+    _check_gpu("dfinal", dfinal, torch.float32, (bsz, dm, N))
+    dev = x.device
+    g = {
+        "dx": torch.empty_like(x), "ddelta": torch.empty_like(x),
+        "dz": torch.empty_like(x) if z is not None else None,
+        "dB": torch.empty((bsz, L, N), dtype=torch.float32, device=dev),
+        "dC": torch.empty((bsz, L, N), dtype=torch.float32, device=dev),
+        "dA": torch.empty((dm, N), dtype=torch.float32, device=dev),
+        "dD": torch.empty((dm,), dtype=torch.float32, device=dev) if D is not None else None,
+        "dh0": torch.empty((bsz, dm, N), dtype=torch.float32, device=dev) if want_dh0 else None,
+    }
+    d = scan_desc(bsz, L, dm, N, io)
+    ws_bytes = lib.mssm_selective_scan_bwd_workspace_size(ctypes.byref(d))
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    st = lib.mssm_selective_scan_bwd(
+        ctypes.byref(d), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(dout),
+        _ptr(dfinal), _ptr(g["dx"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]),
+        _ptr(g["dz"]), _ptr(g["dh0"]), _ptr(workspace) if ws_bytes else None,
+        workspace.numel() if (ws_bytes and workspace is not None) else 0, _stream_handle(stream))
+    if st != MSSM_OK:
+        raise MssmError(st, "mssm_selective_scan_bwd")
+    return g
 
 
 def ssd_desc(batch, seqlen, nheads, headdim, dstate, ngroups, chunk=0, io_dtype=MSSM_BF16) -> SSDDesc:

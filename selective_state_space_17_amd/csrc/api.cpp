@@ -330,6 +330,75 @@ int mssm_ssd_state_update(const mssm_ssd_desc* desc, float* state, const void* x
   return MSSM_OK;
 }
 
+// --------------------------------------------------------------------------
+// Gradients of the Mamba-1 selective scan
+// --------------------------------------------------------------------------
+size_t mssm_selective_scan_bwd_workspace_size(const mssm_scan_desc* desc) {
+  if (validate_scan_desc(desc) != MSSM_OK || desc->dstate > 16) return 0;
+  return mssm::scan_bwd_workspace_bytes(desc->batch, desc->seqlen, desc->dim);
+}
+
+int mssm_selective_scan_bwd(const mssm_scan_desc* desc, const void* x, const void* delta, const float* A,
+                            const void* B, const void* C, const float* D, const void* z, const float* h0,
+                            const void* dout, const float* dfinal, void* dx, void* ddelta, float* dA, float* dB,
+                            float* dC, float* dD, void* dz, float* dh0, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  const int v = validate_scan_desc(desc);
+  if (v != MSSM_OK) return v;
+  const mssm_scan_desc& d = *desc;
+  if (d.dstate > 16) return MSSM_ERR_UNSUPPORTED;
+  const int64_t es = d.io_dtype == MSSM_BF16 ? 2 : 4;
+  const int64_t n_bld = d.batch * d.seqlen * d.dim;
+  const bool has_steps = n_bld > 0;
+  if (A == nullptr || dA == nullptr) return MSSM_ERR_INVALID_ARG;
+  if (D != nullptr && dD == nullptr) return MSSM_ERR_INVALID_ARG;
+  if (has_steps && (x == nullptr || delta == nullptr || B == nullptr || C == nullptr || dout == nullptr ||
+                    dx == nullptr || ddelta == nullptr || dB == nullptr || dC == nullptr ||
+                    (z != nullptr && dz == nullptr)))
+    return MSSM_ERR_INVALID_ARG;
+  if (!aligned(x, es) || !aligned(delta, es) || !aligned(B, es) || !aligned(C, es) || !aligned(z, es) ||
+      !aligned(dout, es) || !aligned(dx, es) || !aligned(ddelta, es) || !aligned(dz, es) || !aligned(A, 4) ||
+      !aligned(D, 4) || !aligned(h0, 4) || !aligned(dfinal, 4) || !aligned(dA, 4) || !aligned(dB, 4) ||
+      !aligned(dC, 4) || !aligned(dD, 4) || !aligned(dh0, 4))
+    return MSSM_ERR_MISALIGNED;
+  if ((d.seqlen + 15) / 16 > std::numeric_limits<int32_t>::max() ||
+      mssm::scan_bwd_grid_blocks(d.batch, d.dim) > std::numeric_limits<int32_t>::max())
+    return MSSM_ERR_UNSUPPORTED;
+  const size_t need = mssm::scan_bwd_workspace_bytes(d.batch, d.seqlen, d.dim);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need) return MSSM_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return MSSM_ERR_MISALIGNED;
+  }
+  // outputs (and the workspace) must not alias the inputs or each other
+  const int64_t b_io = n_bld * es, b_bc = d.batch * d.seqlen * d.dstate * es;
+  const int64_t b_bc32 = d.batch * d.seqlen * d.dstate * 4, b_st = d.batch * d.dim * d.dstate * 4;
+  const int64_t b_a = d.dim * d.dstate * 4, b_d = d.dim * 4;
+  const bool with_z = z != nullptr, with_d = D != nullptr;
+  const void* ins[] = {x, delta, B, C, z, A, D, h0, dout, dfinal};
+  const int64_t inb[] = {b_io, b_io, b_bc, b_bc, b_io, b_a, b_d, b_st, b_io, b_st};
+  const void* outs[] = {dx, ddelta, dA, dB, dC, with_d ? dD : nullptr, with_z ? dz : nullptr, dh0, workspace};
+  const int64_t outb[] = {b_io, b_io, b_a, b_bc32, b_bc32, b_d, b_io, b_st, static_cast<int64_t>(need)};
+  for (int i = 0; i < 9; ++i) {
+    for (int j = 0; j < 10; ++j)
+      if (overlap(outs[i], outb[i], ins[j], inb[j])) return MSSM_ERR_INVALID_ARG;
+    for (int j = i + 1; j < 9; ++j)
+      if (overlap(outs[i], outb[i], outs[j], outb[j])) return MSSM_ERR_INVALID_ARG;
+  }
+
+  mssm::ScanBwdArgs a{};
+  a.x = x; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.h0 = h0;
+  a.dout = dout; a.dfinal = dfinal;
+  a.dx = dx; a.ddelta = ddelta; a.dA = dA; a.dB = dB; a.dC = dC; a.dD = with_d ? dD : nullptr;
+  a.dz = with_z ? dz : nullptr; a.dh0 = dh0; a.workspace = workspace;
+  a.batch = d.batch; a.L = d.seqlen; a.dim = d.dim; a.N = d.dstate; a.io = d.io_dtype;
+  const hipError_t e = mssm::scan_bwd_launch(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    set_err(e);
+    return MSSM_ERR_HIP;
+  }
+  return MSSM_OK;
+}
+
 size_t mssm_ssd_workspace_size(const mssm_ssd_desc* desc) {
   int64_t Q = 0;
   if (validate_ssd_desc(desc, &Q) != MSSM_OK) return 0;

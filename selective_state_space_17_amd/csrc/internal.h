@@ -86,4 +86,37 @@ hipError_t ssd_update_launch(const UpdateArgs& a, hipStream_t stream);
 // blocks the update kernels launch for `rows` state rows of N states
 int64_t update_grid_blocks(int64_t rows, int64_t N);
 
+// ---------------------------------------------------------------------------
+// Gradients of the Mamba-1 selective scan (dstate <= 16)
+// ---------------------------------------------------------------------------
+struct ScanBwdArgs {
+  const void* x;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;       // nullable
+  const void* z;        // nullable
+  const float* h0;      // nullable
+  const void* dout;
+  const float* dfinal;  // nullable
+  void* dx;
+  void* ddelta;
+  float* dA;
+  float* dB;
+  float* dC;
+  float* dD;            // written iff D != nullptr
+  void* dz;             // written iff z != nullptr
+  float* dh0;           // nullable
+  void* workspace;
+  int64_t batch, L, dim, N;
+  int io;
+};
+
+// workspace: per-tile state checkpoints, per-block dB/dC partials, per-row dA/dD partials
+size_t scan_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t dim);
+// blocks of the main gradient kernel
+int64_t scan_bwd_grid_blocks(int64_t batch, int64_t dim);
+hipError_t scan_bwd_launch(const ScanBwdArgs& a, hipStream_t stream);
+
 }  // namespace mssm

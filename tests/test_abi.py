@@ -253,3 +253,78 @@ def test_ssd_state_update_pointer_checks():
     assert call(bad) == M.MSSM_ERR_MISALIGNED
     bad = list(args); bad[8] = BASE + 600 * MB
     assert call(bad) == M.MSSM_ERR_INVALID_ARG              # out aliases state
+
+
+def _bwd_call(desc, ws=BASE + 2000 * MB, ws_bytes=None, **kw):
+    a = dict(x=BASE, delta=BASE + 100 * MB, A=BASE + 200 * MB, B=BASE + 300 * MB, C=BASE + 400 * MB, D=None,
+             z=None, h0=None, dout=BASE + 500 * MB, dfinal=None, dx=BASE + 600 * MB, ddelta=BASE + 700 * MB,
+             dA=BASE + 800 * MB, dB=BASE + 900 * MB, dC=BASE + 1000 * MB, dD=None, dz=None, dh0=None)
+    a.update(kw)
+    if ws_bytes is None:
+        ws_bytes = M.lib.mssm_selective_scan_bwd_workspace_size(ctypes.byref(desc)) if desc is not None else 0
+    return M.lib.mssm_selective_scan_bwd(ctypes.byref(desc) if desc is not None else None, a["x"], a["delta"],
+                                         a["A"], a["B"], a["C"], a["D"], a["z"], a["h0"], a["dout"], a["dfinal"],
+                                         a["dx"], a["ddelta"], a["dA"], a["dB"], a["dC"], a["dD"], a["dz"], a["dh0"],
+                                         ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("null_desc", M.MSSM_ERR_INVALID_ARG),
+    ("dstate_17", M.MSSM_ERR_UNSUPPORTED),
+    ("bad_dtype", M.MSSM_ERR_UNSUPPORTED),
+    ("null_dout", M.MSSM_ERR_INVALID_ARG),
+    ("null_dA", M.MSSM_ERR_INVALID_ARG),
+    ("z_without_dz", M.MSSM_ERR_INVALID_ARG),
+    ("D_without_dD", M.MSSM_ERR_INVALID_ARG),
+    ("misaligned_dx", M.MSSM_ERR_MISALIGNED),
+    ("misaligned_dB", M.MSSM_ERR_MISALIGNED),
+    ("dx_aliases_x", M.MSSM_ERR_INVALID_ARG),
+    ("dB_aliases_dC", M.MSSM_ERR_INVALID_ARG),
+    ("workspace_aliases_dx", M.MSSM_ERR_INVALID_ARG),
+    ("no_workspace", M.MSSM_ERR_WORKSPACE),
+    ("small_workspace", M.MSSM_ERR_WORKSPACE),
+    ("misaligned_workspace", M.MSSM_ERR_MISALIGNED),
+])
+def test_scan_bwd_validation(case, expect):
+    d = small()
+    kw = {}
+    if case == "null_desc":
+        d = None
+    elif case == "dstate_17":
+        d = small(dstate=17, split_state=0)
+    elif case == "bad_dtype":
+        d = small(io_dtype=3)
+    elif case == "null_dout":
+        kw["dout"] = None
+    elif case == "null_dA":
+        kw["dA"] = None
+    elif case == "z_without_dz":
+        kw["z"] = BASE + 1100 * MB
+    elif case == "D_without_dD":
+        kw["D"] = BASE + 1100 * MB
+    elif case == "misaligned_dx":
+        kw["dx"] = BASE + 600 * MB + 1
+    elif case == "misaligned_dB":
+        kw["dB"] = BASE + 900 * MB + 2
+    elif case == "dx_aliases_x":
+        kw["dx"] = BASE + 64
+    elif case == "dB_aliases_dC":
+        kw["dB"] = BASE + 1000 * MB + 16
+    elif case == "workspace_aliases_dx":
+        kw["ws"] = BASE + 600 * MB
+    elif case == "no_workspace":
+        kw["ws"] = None
+    elif case == "small_workspace":
+        kw["ws_bytes"] = M.lib.mssm_selective_scan_bwd_workspace_size(ctypes.byref(d)) - 1
+    elif case == "misaligned_workspace":
+        kw["ws"] = BASE + 2000 * MB + 16
+    assert _bwd_call(d, **kw) == expect
+
+
+def test_scan_bwd_workspace_size():
+    # checkpoints every 16 steps, per-16-channel-block dB/dC partials, per-row dA/dD partials (256-byte aligned)
+    d = small(batch=2, seqlen=64, dim=32, dstate=16)
+    al = lambda v: (v + 255) // 256 * 256
+    want = al(4 * 2 * 4 * 32 * 16) + 2 * al(4 * 2 * 2 * 64 * 16) + al(4 * 2 * 32 * 16) + al(4 * 2 * 32)
+    assert M.lib.mssm_selective_scan_bwd_workspace_size(ctypes.byref(d)) == want
+    assert M.lib.mssm_selective_scan_bwd_workspace_size(ctypes.byref(small(dstate=17, split_state=0))) == 0

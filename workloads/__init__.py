@@ -37,7 +37,7 @@ ROOT_SEED = 1700
 BLOCK = 1 << 22
 
 # tensor ids (fixed order of the per-tensor streams)
-T_X, T_DELTA, T_Z, T_B, T_C, T_D, T_A, T_H0 = range(8)
+T_X, T_DELTA, T_Z, T_B, T_C, T_D, T_A, T_H0, T_DOUT, T_DFIN = range(10)
 
 F32 = "f32"
 BF16 = "bf16"
@@ -58,6 +58,7 @@ class ScanConfig:
     has_z: bool = True
     return_final: bool = True
     decode: bool = False    # token-by-token update of a stored state (read and written in place)
+    backward: bool = False  # gradients: dout in, dx/ddelta/dz (io) and dB/dC/dA/dD (fp32) out
 
     @property
     def updates(self) -> int:
@@ -68,6 +69,14 @@ class ScanConfig:
         e = 2 if self.io == BF16 else 4
         bld = self.batch * self.seqlen * self.dim
         bln = self.batch * self.seqlen * self.dstate
+        if self.backward:
+            zf = 2 if self.has_z else 0
+            n = bld * e * (2 + 1 + 2 + zf)          # x, delta, dout in; dx, ddelta out; z in, dz out
+            n += bln * e * 2 + bln * 4 * 2          # B, C in; dB, dC out (fp32)
+            n += self.dim * self.dstate * 4 * 2     # A in, dA out
+            n += self.dim * 4 * 2 if self.has_D else 0
+            n += self.batch * self.dim * self.dstate * 4 * 2 if self.return_final else 0   # dfinal in, dh0 out
+            return n
         n = bld * e * 2                     # x, delta
         n += bld * e if self.has_z else 0   # z
         n += bln * e * 2                    # B, C
@@ -124,6 +133,9 @@ CONFIGS = {
     3: ScanConfig("mamba1_2p8b_layer_bf16", 3, 4, 8192, 5120, 16, BF16, "s4d_real", return_final=True),
     4: SSDConfig("mamba2_ssd_bf16", 4, 8, 4096, 32, 64, 128, 1, 256),
     5: ScanConfig("mamba1_long_1m_bf16", 5, 1, 1 << 20, 2048, 16, BF16, "s4d_real", return_final=True),
+    # gradients of config 2's layer (one backward pass; no final-state gradient)
+    8: ScanConfig("mamba1_130m_layer_bwd_bf16", 8, 8, 2048, 1536, 16, BF16, "exp_log", return_final=False,
+                  backward=True),
     # decode steps (one new token against a stored state), the configs' layer shapes at serving batch sizes
     6: ScanConfig("mamba1_2p8b_decode_bf16", 6, 256, 1, 5120, 16, BF16, "s4d_real", return_final=True, decode=True),
     7: SSDConfig("mamba2_decode_bf16", 7, 64, 1, 32, 64, 128, 1, 64, BF16, True, True, True, decode=True),
@@ -261,6 +273,14 @@ def make_scan_inputs(cfg: ScanConfig, seed_base: int = ROOT_SEED, with_h0: bool 
         raise ValueError(cfg.a_kind)
     h0 = normal_f32(cid, T_H0, b * d * n, seed_base).reshape(b, d, n) if with_h0 else None
     return ScanInputs(x, delta, np.ascontiguousarray(A), Bm, Cm, D, z, h0, cfg.io)
+
+
+def make_scan_grads(cfg: ScanConfig, seed_base: int = ROOT_SEED, with_dfinal: bool = True):
+    """Upstream gradients for the scan: dout [B, L, D] ~ N(0, 1) in io dtype, dfinal [B, D, N] ~ N(0, 1) fp32."""
+    b, l, d, n = cfg.batch, cfg.seqlen, cfg.dim, cfg.dstate
+    dout = normal(cfg.cfg_id, T_DOUT, b * l * d, cfg.io, seed_base).reshape(b, l, d)
+    dfin = normal_f32(cfg.cfg_id, T_DFIN, b * d * n, seed_base).reshape(b, d, n) if with_dfinal else None
+    return dout, dfin
 
 
 @dataclasses.dataclass

@@ -30,36 +30,43 @@ PEAK_BF16_MFMA_TFLOPS = 2500.0
 # per (b, t, c): delta*x, D*x + y, and the silu gate (mul, exp2, add, rcp, 2 mul) = 10
 SLOTS_PER_UPDATE = 6.0
 SLOTS_PER_STEP_CHANNEL = 10.0
+# gradients, per state update: the forward update (5) and its readout term (2); the adjoint FMA and
+# decay (2); the dC, dB, dA, ddelta and dx terms with their sums (10).  Per (b, t, c): delta*x, the
+# gate and its derivative, and the ddelta / dx / dz finish (13).
+SLOTS_PER_UPDATE_BWD = 19.0
+SLOTS_PER_STEP_CHANNEL_BWD = 13.0
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_digest(is_ssd: bool, decode: bool = False) -> str:
+def source_digest(is_ssd: bool, decode: bool = False, backward: bool = False) -> str:
     """Hash of the sources that make the workload's kernels (counters go stale when it changes)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "selective_state_space_17_amd", "csrc")
-    kern = "decode.hip" if decode else ("ssd_m2.hip" if is_ssd else "scan_m1.hip")
+    kern = "bwd_m1.hip" if backward else ("decode.hip" if decode else ("ssd_m2.hip" if is_ssd else "scan_m1.hip"))
     h.update(open(os.path.join(csrc, kern), "rb").read())
     return h.hexdigest()[:16]
 
 
-def kernel_tags(is_ssd: bool, decode: bool = False):
+def kernel_tags(is_ssd: bool, decode: bool = False, backward: bool = False):
     """Name fragments of the kernels that carry the workload's scan (the dominant one per launch)."""
+    if backward:
+        return ("scan_bwd_kernel",)
     if decode:
         return ("ssd_update_kernel",) if is_ssd else ("scan_update_kernel",)
     return ("ssd_kernel",) if is_ssd else ("wide_kernel", "scan_kernel")
 
 
-def load_traffic(workload: str, is_ssd: bool, decode: bool = False):
+def load_traffic(workload: str, is_ssd: bool, decode: bool = False, backward: bool = False):
     """HBM bytes per launch of the dominant kernel from committed rocprofv3 counters, if they were
     taken on the current kernel sources (else None)."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     t = json.load(open(path))
-    if t.get("source_digest") != source_digest(is_ssd, decode):
+    if t.get("source_digest") != source_digest(is_ssd, decode, backward):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -75,9 +82,10 @@ def summarize_counters(cfg, is_ssd, d, copy_mib):
     WRITE_SIZE) into HBM bytes per launch of the dominant kernel, each counter scaled by what it
     reads for a device copy of copy_mib MiB, and write profiles/traffic_<workload>.json."""
     import numpy as np
-    tags = kernel_tags(is_ssd, cfg.decode)
+    bwd = getattr(cfg, "backward", False)
+    tags = kernel_tags(is_ssd, cfg.decode, bwd)
     copy_bytes = copy_mib << 20
-    res = {"workload": cfg.name, "source_digest": source_digest(is_ssd, cfg.decode),
+    res = {"workload": cfg.name, "source_digest": source_digest(is_ssd, cfg.decode, bwd),
            "copy_bytes": copy_bytes, "algorithmic_bytes_per_launch": cfg.algorithmic_bytes()}
     total = 0.0
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
@@ -146,6 +154,21 @@ def cpu_baseline_scan(inp, cfg):
                       f"({n:.3e} updates in {dt:.2f} s, fp64 sequential recurrence)"}
 
 
+def cpu_baseline_scan_bwd(inp, cfg, dout):
+    import oracle
+    threads = oracle.default_threads()
+    # the oracle splits the work over batch rows; dB/dC need every channel, so the sample is whole rows
+    rows = min(cfg.batch, threads)
+    sl = slice(0, rows)
+    passes, dt = _timed_passes(lambda: oracle.scan_bwd(inp.x[sl], inp.delta[sl], inp.A, inp.B[sl], inp.C[sl], inp.D,
+                                                       None if inp.z is None else inp.z[sl], None, dout[sl], None,
+                                                       nthreads=threads))
+    n = rows * cfg.seqlen * cfg.dim * cfg.dstate * passes
+    return {"value": n / dt, "unit": "state-updates/s", "cores": min(threads, rows), "kind": "oracle",
+            "sample": f"batch rows 0..{rows} of {cfg.batch} (all steps and channels), {passes} pass(es) "
+                      f"({n:.3e} updates in {dt:.2f} s, fp64 forward then reverse recurrence)"}
+
+
 def cpu_baseline_ssd(inp, cfg):
     import oracle
     threads = oracle.default_threads()
@@ -165,7 +188,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2,
-                    help="workload id (1-7; 6, 7: decode steps); 2 is the one the metric is quoted on")
+                    help="workload id (1-8; 6, 7: decode steps; 8: gradients); 2 is the one the metric is "
+                         "quoted on")
     ap.add_argument("--sets", type=int, default=0, help="resident input copies to rotate over (0: auto)")
     ap.add_argument("--chunk", type=int, default=0, help="SSD time-chunk length (0: the workload's)")
     ap.add_argument("--split-seq", type=int, default=0, help="force the sequence-chunk count (0: the planner's)")
@@ -217,7 +241,27 @@ def main():
 
     t = time.perf_counter()
     decode = cfg.decode
-    if decode:
+    backward = getattr(cfg, "backward", False)
+    if backward:
+        # one backward pass of the layer: the loss gradient dout in, every input's gradient out
+        host = [W.make_scan_inputs(cfg, seed_base=W.ROOT_SEED + 1000 * i) for i in range(sets)]
+        douts = [W.make_scan_grads(cfg, seed_base=W.ROOT_SEED + 1000 * i, with_dfinal=False)[0] for i in range(sets)]
+        ins = [dict(x=dev(h.x), delta=dev(h.delta), A=dev(h.A), B=dev(h.B), C=dev(h.C), D=dev(h.D), z=dev(h.z),
+                    dout=dev(g)) for h, g in zip(host, douts)]
+        io = M.MSSM_BF16 if cfg.io == W.BF16 else M.MSSM_F32
+        ws_n = M.selective_scan_bwd_workspace_size(cfg.batch, cfg.seqlen, cfg.dim, cfg.dstate, io)
+        ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+        a0 = ins[0]
+        grads = [M.selective_scan_bwd(a["x"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], None, a["dout"],
+                                      None, want_dh0=False, workspace=ws) for a in ins]
+
+        def step(i):
+            a = ins[i % sets]
+            M.selective_scan_bwd(a["x"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], None, a["dout"], None,
+                                 want_dh0=False, grads=grads[i % sets], workspace=ws)
+        plan = {"tokens_per_tile": 16, "channels_per_block": 16}
+        del a0
+    elif decode:
         # token-by-token update: each input set carries its own state, advanced in place every step
         if is_ssd:
             host = [W.make_ssd_inputs(cfg, seed_base=W.ROOT_SEED + 1000 * i, with_h0=True) for i in range(sets)]
@@ -269,6 +313,8 @@ def main():
                                  split_seq=K, split_state=G, workspace=ws if ws_n else None)
         plan = {"split_seq": K, "split_state": G}
     del host[1:]
+    if backward:
+        del douts[1:]
     torch.cuda.synchronize()
     log(f"inputs ready in {time.perf_counter() - t:.1f}s; plan {plan}")
 
@@ -295,8 +341,17 @@ def main():
     kern_s = ms * 1e-3
     hbm = {"achieved": alg_bytes / kern_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
            "frac": alg_bytes / kern_s / 1e9 / PEAK_HBM_GBS}
-    traffic = load_traffic(cfg.name, is_ssd, decode)
-    if decode:
+    traffic = load_traffic(cfg.name, is_ssd, decode, backward)
+    if backward:
+        # the whole backward call (gradient kernel and the two small fixed-order sum kernels)
+        slots = cfg.updates * SLOTS_PER_UPDATE_BWD + cfg.batch * cfg.seqlen * cfg.dim * SLOTS_PER_STEP_CHANNEL_BWD
+        alu = {"achieved": slots / kern_s / 1e12, "peak": PEAK_VALU_TSLOT, "unit": "Tslot/s"}
+        alu["frac"] = alu["achieved"] / alu["peak"]
+        bound = "alu" if alu["frac"] >= hbm["frac"] else "hbm"
+        roof = dict(alu if bound == "alu" else hbm)
+        roof["bound"] = bound
+        roof["other"] = hbm if bound == "alu" else alu
+    elif decode:
         # a few operations per byte of state: the HBM roofline bounds it
         roof = dict(hbm)
         roof["bound"] = "hbm"
@@ -325,12 +380,17 @@ def main():
         roof["other"] = hbm if bound == "alu" else alu
     roof["traffic"] = traffic
     roof = {k: roof[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic", "other")}
+    if backward:
+        roof["scope"] = "whole backward call: scan_bwd_kernel, then bwd_reduce_bc and bwd_reduce_ad"
 
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         h = host[0]
-        cpu = cpu_baseline_ssd(h, cfg) if is_ssd else cpu_baseline_scan(h, cfg)
+        if backward:
+            cpu = cpu_baseline_scan_bwd(h, cfg, douts[0])
+        else:
+            cpu = cpu_baseline_ssd(h, cfg) if is_ssd else cpu_baseline_scan(h, cfg)
         if decode:
             cpu["sample"] += "; the same recurrence from the stored state (h0)"
         log(f"cpu baseline: {cpu}")
@@ -338,6 +398,8 @@ def main():
     conf = {"workload": cfg.name, "batch": cfg.batch, "seqlen": cfg.seqlen}
     if decode:
         conf["decode"] = True
+    if backward:
+        conf["backward"] = True
     if is_ssd:
         conf.update(nheads=cfg.nheads, headdim=cfg.headdim, d_state=cfg.dstate, ngroups=cfg.ngroups, io="bf16",
                     **plan)
@@ -346,7 +408,8 @@ def main():
                     final_state=cfg.return_final, **plan)
     conf["input_sets"] = sets
     line = {
-        "metric": "selective-scan state updates/s (B*L*d_inner*N), 1 GPU",
+        "metric": ("selective-scan gradient state updates/s (B*L*d_inner*N), 1 GPU" if backward else
+                   "selective-scan state updates/s (B*L*d_inner*N), 1 GPU"),
         "value": upd_s,
         "unit": "state-updates/s",
         "n_gpus": 1,

@@ -194,14 +194,15 @@ def selective_scan_bwd_workspace_size(batch, seqlen, dim, dstate, io_dtype=MSSM_
 
 
 def selective_scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, dout=None, dfinal=None, want_dh0: bool = True,
-                       workspace=None, stream=None):
+                       grads=None, workspace=None, stream=None):
     """Gradients of the Mamba-1 selective scan (mssm_selective_scan_bwd), for the loss
     sum(out * dout) + sum(final_state * dfinal).
 
     Inputs as in selective_scan_fwd; dout [batch, seqlen, dim] in the io dtype; dfinal
     [batch, dim, dstate] float32 or None.  Returns a dict: dx, ddelta, dz (io dtype, dz None without z),
     dB, dC [batch, seqlen, dstate] float32, dA [dim, dstate] float32, dD [dim] float32 (None without D),
-    dh0 [batch, dim, dstate] float32 (None unless want_dh0).
+    dh0 [batch, dim, dstate] float32 (None unless want_dh0).  ``grads`` may hold preallocated outputs
+    (a dict with the same keys, as returned by an earlier call) to write into.
     """
     torch = _torch()
     if x.dim() != 3:
@@ -221,7 +222,7 @@ def selective_scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, dout=None, df
     _check_gpu("h0", h0, torch.float32, (bsz, dm, N))
     _check_gpu("dfinal", dfinal, torch.float32, (bsz, dm, N))
     dev = x.device
-    g = {
+    g = grads if grads is not None else {
         "dx": torch.empty_like(x), "ddelta": torch.empty_like(x),
         "dz": torch.empty_like(x) if z is not None else None,
         "dB": torch.empty((bsz, L, N), dtype=torch.float32, device=dev),
@@ -230,6 +231,12 @@ def selective_scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, dout=None, df
         "dD": torch.empty((dm,), dtype=torch.float32, device=dev) if D is not None else None,
         "dh0": torch.empty((bsz, dm, N), dtype=torch.float32, device=dev) if want_dh0 else None,
     }
+    if grads is not None:
+        for name, dt, shape in (("dx", x.dtype, (bsz, L, dm)), ("ddelta", x.dtype, (bsz, L, dm)),
+                                ("dz", x.dtype, (bsz, L, dm)), ("dB", torch.float32, (bsz, L, N)),
+                                ("dC", torch.float32, (bsz, L, N)), ("dA", torch.float32, (dm, N)),
+                                ("dD", torch.float32, (dm,)), ("dh0", torch.float32, (bsz, dm, N))):
+            _check_gpu(name, g.get(name), dt, shape)
     d = scan_desc(bsz, L, dm, N, io)
     ws_bytes = lib.mssm_selective_scan_bwd_workspace_size(ctypes.byref(d))
     if ws_bytes and workspace is None:

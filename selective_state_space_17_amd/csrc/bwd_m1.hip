@@ -46,10 +46,14 @@ constexpr int kTT = 16;    // steps per tile (= checkpoint interval)
 
 template <typename T> struct Io;
 template <> struct Io<float> {
+  __device__ static float raw(const void* p, int64_t i) { return static_cast<const float*>(p)[i]; }
+  __device__ static float cvt(float v) { return v; }
   __device__ static float get(const void* p, int64_t i) { return static_cast<const float*>(p)[i]; }
   __device__ static void put(void* p, int64_t i, float v) { static_cast<float*>(p)[i] = v; }
 };
 template <> struct Io<uint16_t> {
+  __device__ static uint16_t raw(const void* p, int64_t i) { return static_cast<const uint16_t*>(p)[i]; }
+  __device__ static float cvt(uint16_t v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
   __device__ static float get(const void* p, int64_t i) {
     return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16);
   }
@@ -72,14 +76,18 @@ __device__ __forceinline__ float row_sum(float v) {
   return v;
 }
 
-// Position of (row cl, state n, step s) in a 16x16x16 fp32 LDS area.  Lane
-// (cl, n) writes its 16 steps as four 16-byte stores; the rotation of n by
-// the row and the xor of the step by the n group make both transposed reads
-// -- lane (cl, s) over n, and thread (s, n) over cl -- hit 64 distinct banks.
-__device__ __forceinline__ int qpos(int cl, int n, int s) {
-  const int m = (n + cl) & 15;
-  return cl * 256 + m * 16 + (s ^ ((m >> 2) << 2));
-}
+// Transpose areas: 16 rows (channels) x 16 states x 16 steps of fp32, row
+// stride 272.  Lane (cl, n) writes its 16 steps as four 16-byte stores at
+// qpos(cl, n, 4i); lane (cl, s) reads state n of step s, and thread (s, n)
+// reads row r.  The 16-dword row padding and the xor of the step by the
+// state group put every one of these accesses on 64 distinct banks, and the
+// addresses are affine in the loop index (one base register, immediate
+// offsets).
+constexpr int kRow = 272;
+__device__ __forceinline__ int qpos(int cl, int n, int s) { return cl * kRow + 16 * n + (s ^ ((n >> 2) << 2)); }
+constexpr int kBT = 20;   // B^T / C^T row stride: lane n reads 4 steps with one 16-byte load
+
+template <int S> __device__ __forceinline__ float bcast(float v) { return dpp<0x150 + S>(v); }   // row_newbcast:S
 
 struct BwdParams {
   const void* x;
@@ -105,17 +113,61 @@ struct BwdParams {
   int ntiles, ncb;
 };
 
+// Step S of the forward recurrence for lane (cl, n): the per-(t, c) values
+// of step S sit in lane S of the row and reach every lane through a DPP
+// row broadcast folded into the multiply.
+template <int S>
+__device__ __forceinline__ void fwd_step(float& h, float& a, float dl, float du, float A2, float b) {
+  a = exp2_hw(bcast<S>(dl) * A2);
+  h = __builtin_fmaf(a, h, bcast<S>(du) * b);
+}
+
+template <int G>
+__device__ __forceinline__ void fwd_group(float& h, float dl, float du, float A2, const float4& b4) {
+  float a;
+  fwd_step<4 * G + 0>(h, a, dl, du, A2, b4.x);
+  fwd_step<4 * G + 1>(h, a, dl, du, A2, b4.y);
+  fwd_step<4 * G + 2>(h, a, dl, du, A2, b4.z);
+  fwd_step<4 * G + 3>(h, a, dl, du, A2, b4.w);
+}
+
+template <int S>
+__device__ __forceinline__ void rec_step(float& h, float (&av)[16], float (&hs)[16], float (&pr)[16], float (&q1)[16],
+                                         float dl, float du, float dy, float A2, float b, float cc) {
+  fwd_step<S>(h, av[S], dl, du, A2, b);
+  hs[S] = h;
+  pr[S] = cc * h;                // C h: readout term of y
+  q1[S] = bcast<S>(dy) * h;      // dy h: dC term
+}
+
+template <int S>
+__device__ __forceinline__ void adj_step(float& lam, float& dA, const float (&av)[16], const float (&hs)[16], float hin,
+                                         float (&q2)[16], float (&r1)[16], float (&r2)[16], float dl, float du, float dy,
+                                         float Av, float b, float cc) {
+  lam = __builtin_fmaf(cc, bcast<S>(dy), lam);    // + C dy
+  q2[S] = bcast<S>(du) * lam;                     // lam delta x
+  r2[S] = lam * b;                                // lam B
+  lam *= av[S];                                   // a_t lam_t
+  const float t1 = lam * (S > 0 ? hs[S > 0 ? S - 1 : 0] : hin);   // lam a_t h_{t-1}
+  dA = __builtin_fmaf(t1, bcast<S>(dl), dA);
+  r1[S] = t1 * Av;
+  // keep this step's results here: otherwise the compiler sinks the q2 and dA
+  // updates past the loop and keeps their operands alive across it
+  __asm__ volatile("" : "+v"(dA), "+v"(q2[S]), "+v"(r1[S]), "+v"(r2[S]));
+}
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
   using io = Io<T>;
-  __shared__ float4 TC[kTT][kCPB];   // {delta, delta*x, dy, 0} per (step, channel)
-  __shared__ float2 BC[kTT][16];     // {B, C} per (step, state)
-  __shared__ __attribute__((aligned(16))) float Q1[16 * 16 * 16];  // dy*h (dC) / transposes / phase A tiles
-  __shared__ __attribute__((aligned(16))) float Q2[16 * 16 * 16];  // lam*delta*x (dB) / transposes
+  __shared__ __attribute__((aligned(16))) float BT[2][16 * kBT];   // B^T per tile (double-buffered in phase A)
+  __shared__ __attribute__((aligned(16))) float CT[16 * kBT];      // C^T per tile
+  __shared__ __attribute__((aligned(16))) float Q1[16 * kRow];     // dy*h (dC) / transposes
+  __shared__ __attribute__((aligned(16))) float Q2[16 * kRow];     // lam*delta*x (dB) / transposes
 
   const int tid = threadIdx.x;
-  const int cl = tid >> 4;          // compute: channel row
-  const int n = tid & 15;           // compute: state
+  const int cl = tid >> 4;          // channel row; also: staging / finishing thread of step fs = n
+  const int n = tid & 15;           // state
+  const int fs = n;
   const int cb = static_cast<int>(blockIdx.x % static_cast<unsigned>(p.ncb));
   const int64_t b = blockIdx.x / static_cast<unsigned>(p.ncb);
   const int64_t c0 = static_cast<int64_t>(cb) * kCPB;
@@ -123,6 +175,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
   const int64_t L = p.L, dim = p.dim, N = p.N;
   const bool lane_ok = c < dim && n < N;
   const int64_t D16 = static_cast<int64_t>(p.ncb) * kCPB;
+  const int bs = tid >> 4, bn = tid & 15;   // B/C staging: step, state
 
   const float Av = lane_ok ? p.A[c * N + n] : 0.f;
   const float A2 = Av * kLog2e;
@@ -130,59 +183,84 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
 
   // -------------------------------------------------------------- phase A
   {
-    float4* TCa = reinterpret_cast<float4*>(Q1);        // [2][16][16]
-    float2* BCa = reinterpret_cast<float2*>(Q1 + 2048);  // [2][16][16]
-    const int ss = tid >> 4, sc = tid & 15;              // staging: step, channel / state
     float h = (lane_ok && p.h0 != nullptr) ? p.h0[(b * dim + c) * N + n] : 0.f;
-    float rd = 0.f, rx = 0.f, rb = 0.f;
+    // Loads are unconditional, from an in-range element when the step or
+    // channel is past the end, and their raw values are left untouched until
+    // the tile is staged (masking or widening them at once would make the
+    // wave wait for the load there instead of a tile later).
+    T rd{}, rx{}, rb{};
+    bool ok = false, okb = false;
     auto issue = [&](int k) {
-      const int64_t t = static_cast<int64_t>(k) * kTT + ss;
-      const int64_t cc = c0 + sc;
-      const bool ok = t < L && cc < dim;
-      rd = ok ? io::get(p.delta, (b * L + t) * dim + cc) : 0.f;
-      rx = ok ? io::get(p.x, (b * L + t) * dim + cc) : 0.f;
-      rb = (t < L && sc < N) ? io::get(p.B, (b * L + t) * N + sc) : 0.f;
+      const int64_t t = static_cast<int64_t>(k) * kTT + fs;
+      ok = t < L && c < dim;
+      const int64_t i = (b * L + (t < L ? t : L - 1)) * dim + (c < dim ? c : dim - 1);
+      rd = io::raw(p.delta, i);
+      rx = io::raw(p.x, i);
+      const int64_t tb = static_cast<int64_t>(k) * kTT + bs;
+      okb = tb < L && bn < N;
+      rb = io::raw(p.B, (b * L + (tb < L ? tb : L - 1)) * N + (bn < N ? bn : N - 1));
     };
     if (p.ntiles > 1) issue(0);
     for (int k = 0; k + 1 < p.ntiles; ++k) {
-      const int buf = k & 1;
-      TCa[buf * 256 + ss * 16 + sc] = float4{rd, rd * rx, 0.f, 0.f};
-      BCa[buf * 256 + ss * 16 + sc] = float2{rb, 0.f};
-      if (lane_ok) ck[static_cast<int64_t>(k) * D16 * 16] = h;
+      float* bt = BT[k & 1];
+      bt[bn * kBT + bs] = okb ? io::cvt(rb) : 0.f;
+      const float dl = ok ? io::cvt(rd) : 0.f, du = dl * (ok ? io::cvt(rx) : 0.f);
+      ck[static_cast<int64_t>(k) * D16 * 16] = h;   // padded lanes store their zero state too
       __syncthreads();
       if (k + 2 < p.ntiles) issue(k + 1);
-#pragma unroll
-      for (int s = 0; s < kTT; ++s) {
-        const float4 q = TCa[buf * 256 + s * 16 + cl];
-        const float bv = BCa[buf * 256 + s * 16 + n].x;
-        h = __builtin_fmaf(exp2_hw(q.x * A2), h, q.y * bv);
-      }
+      const float4* b4 = reinterpret_cast<const float4*>(bt + n * kBT);
+      fwd_group<0>(h, dl, du, A2, b4[0]);
+      fwd_group<1>(h, dl, du, A2, b4[1]);
+      fwd_group<2>(h, dl, du, A2, b4[2]);
+      fwd_group<3>(h, dl, du, A2, b4[3]);
     }
-    if (lane_ok && p.ntiles > 0) ck[static_cast<int64_t>(p.ntiles - 1) * D16 * 16] = h;
-    __syncthreads();   // orders the checkpoint stores before phase B's loads; frees Q1
+    if (p.ntiles > 0) ck[static_cast<int64_t>(p.ntiles - 1) * D16 * 16] = h;
+    __syncthreads();   // orders the checkpoint stores before phase B's loads; frees BT
   }
 
   // -------------------------------------------------------------- phase B
-  // staging / finishing role: channel fc = tid/16 (= cl), step fs = tid%16 (= n)
-  const int fs = n;
   const float Dc = (c < dim && p.D != nullptr) ? p.D[c] : 0.f;
   float lam = (lane_ok && p.dfinal != nullptr) ? p.dfinal[(b * dim + c) * N + n] : 0.f;
   float dAacc = 0.f, dDacc = 0.f;
-  float rdl = 0.f, rx = 0.f, rg = 0.f, rz = 0.f, rb = 0.f, rc = 0.f, rh = 0.f;
-  const int bs = tid >> 4, bn = tid & 15;   // B/C staging: step, state
+  // raw prefetched values of the next tile (unconditional in-range loads, see phase A)
+  T rdl{}, rx{}, rg{}, rz{}, rb{}, rc{};
+  float rh = 0.f;
+  bool ok = false, okb = false;
   auto issue = [&](int k) {
     const int64_t t = static_cast<int64_t>(k) * kTT + fs;
-    const bool ok = t < L && c < dim;
-    const int64_t i = (b * L + t) * dim + c;
-    rdl = ok ? io::get(p.delta, i) : 0.f;
-    rx = ok ? io::get(p.x, i) : 0.f;
-    rg = ok ? io::get(p.dout, i) : 0.f;
-    rz = (ok && p.z != nullptr) ? io::get(p.z, i) : 0.f;
+    ok = t < L && c < dim;
+    const int64_t i = (b * L + (t < L ? t : L - 1)) * dim + (c < dim ? c : dim - 1);
+    rdl = io::raw(p.delta, i);
+    rx = io::raw(p.x, i);
+    rg = io::raw(p.dout, i);
+    if (p.z != nullptr) rz = io::raw(p.z, i);
     const int64_t tb = static_cast<int64_t>(k) * kTT + bs;
-    const bool okb = tb < L && bn < N;
-    rb = okb ? io::get(p.B, (b * L + tb) * N + bn) : 0.f;
-    rc = okb ? io::get(p.C, (b * L + tb) * N + bn) : 0.f;
-    rh = lane_ok ? ck[static_cast<int64_t>(k) * D16 * 16] : 0.f;
+    okb = tb < L && bn < N;
+    const int64_t ib = (b * L + (tb < L ? tb : L - 1)) * N + (bn < N ? bn : N - 1);
+    rb = io::raw(p.B, ib);
+    rc = io::raw(p.C, ib);
+    rh = ck[static_cast<int64_t>(k) * D16 * 16];   // written for every lane in phase A
+  };
+  // transposes through this wave's own rows of Q1/Q2 (no other wave touches
+  // them before the barrier that ends the tile's compute); a wave's LDS
+  // accesses run in order, so a row is rewritten only after it was read back
+  auto park = [&](float* area, const float (&v)[kTT]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<float4*>(&area[qpos(cl, n, 4 * i)]) = float4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
+    __builtin_amdgcn_wave_barrier();
+  };
+  auto fetch = [&](const float* area) {   // lane (cl, fs): sum over the 16 states of step fs
+    float r[16];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float* base = area + cl * kRow + 64 * g + (fs ^ (g << 2));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r[4 * g + j] = base[16 * j];
+    }
+    __builtin_amdgcn_wave_barrier();
+    return ((r[0] + r[1]) + (r[2] + r[3]) + ((r[4] + r[5]) + (r[6] + r[7]))) +
+           ((r[8] + r[9]) + (r[10] + r[11]) + ((r[12] + r[13]) + (r[14] + r[15])));
   };
 
   if (p.ntiles > 0) issue(p.ntiles - 1);
@@ -190,89 +268,80 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
     const int64_t t0 = static_cast<int64_t>(k) * kTT;
     const int64_t tf = t0 + fs;
     const bool fvalid = tf < L && c < dim;
-    // ---- stage: this thread's (step fs, channel cl) values stay in registers for the finish
-    const float dl = rdl, u = rx, du = rdl * rx;
-    float dy = rg, sdz = 0.f;
+    // ---- stage: step fs of channel cl stays in this thread's registers, the
+    // source of the row broadcasts and of the finish
+    const float dl = ok ? io::cvt(rdl) : 0.f, u = ok ? io::cvt(rx) : 0.f, du = dl * u;
+    const float g = ok ? io::cvt(rg) : 0.f;
+    float dy = g, sdz = 0.f;
     if (p.z != nullptr) {
-      const float sg = __builtin_amdgcn_rcpf(1.f + exp2_hw(-rz * kLog2e));
-      dy = rg * rz * sg;
-      sdz = rg * sg * __builtin_fmaf(rz, 1.f - sg, 1.f);
+      const float zz = io::cvt(rz);
+      const float sg = __builtin_amdgcn_rcpf(1.f + exp2_hw(-zz * kLog2e));
+      dy = g * zz * sg;
+      sdz = g * sg * __builtin_fmaf(zz, 1.f - sg, 1.f);
     }
-    TC[fs][cl] = float4{dl, du, dy, 0.f};
-    BC[bs][bn] = float2{rb, rc};
+    BT[0][bn * kBT + bs] = okb ? io::cvt(rb) : 0.f;
+    CT[bn * kBT + bs] = okb ? io::cvt(rc) : 0.f;
     float h = rh;            // state entering the tile
     const float hin = rh;    // (rh is reloaded for the next tile below)
     __syncthreads();
     if (k > 0) issue(k - 1);
+    const float4* b4 = reinterpret_cast<const float4*>(&BT[0][n * kBT]);
+    const float4* c4 = reinterpret_cast<const float4*>(&CT[n * kBT]);
 
     // ---- recompute the tile's states and decays
     float hs[kTT], av[kTT], pr[kTT], q1[kTT];
-#pragma unroll
-    for (int s = 0; s < kTT; ++s) {
-      const float4 q = TC[s][cl];
-      const float2 bc = BC[s][n];
-      av[s] = exp2_hw(q.x * A2);
-      h = __builtin_fmaf(av[s], h, q.y * bc.x);
-      hs[s] = h;
-      pr[s] = bc.y * h;      // C h: readout term of y
-      q1[s] = q.z * h;       // dy h: dC term
+    {
+      float4 bv = b4[0], cv = c4[0];
+      rec_step<0>(h, av, hs, pr, q1, dl, du, dy, A2, bv.x, cv.x);
+      rec_step<1>(h, av, hs, pr, q1, dl, du, dy, A2, bv.y, cv.y);
+      rec_step<2>(h, av, hs, pr, q1, dl, du, dy, A2, bv.z, cv.z);
+      rec_step<3>(h, av, hs, pr, q1, dl, du, dy, A2, bv.w, cv.w);
+      bv = b4[1]; cv = c4[1];
+      rec_step<4>(h, av, hs, pr, q1, dl, du, dy, A2, bv.x, cv.x);
+      rec_step<5>(h, av, hs, pr, q1, dl, du, dy, A2, bv.y, cv.y);
+      rec_step<6>(h, av, hs, pr, q1, dl, du, dy, A2, bv.z, cv.z);
+      rec_step<7>(h, av, hs, pr, q1, dl, du, dy, A2, bv.w, cv.w);
+      bv = b4[2]; cv = c4[2];
+      rec_step<8>(h, av, hs, pr, q1, dl, du, dy, A2, bv.x, cv.x);
+      rec_step<9>(h, av, hs, pr, q1, dl, du, dy, A2, bv.y, cv.y);
+      rec_step<10>(h, av, hs, pr, q1, dl, du, dy, A2, bv.z, cv.z);
+      rec_step<11>(h, av, hs, pr, q1, dl, du, dy, A2, bv.w, cv.w);
+      bv = b4[3]; cv = c4[3];
+      rec_step<12>(h, av, hs, pr, q1, dl, du, dy, A2, bv.x, cv.x);
+      rec_step<13>(h, av, hs, pr, q1, dl, du, dy, A2, bv.y, cv.y);
+      rec_step<14>(h, av, hs, pr, q1, dl, du, dy, A2, bv.z, cv.z);
+      rec_step<15>(h, av, hs, pr, q1, dl, du, dy, A2, bv.w, cv.w);
     }
-    // Transposes go through this wave's own rows of Q1/Q2 (no other wave
-    // touches them before the barrier below); a wave's LDS accesses run in
-    // order, so a row is rewritten only after it has been read back.
-    auto park = [&](float* area, const float (&v)[kTT]) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<float4*>(&area[qpos(cl, n, 4 * i)]) = float4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
-      __builtin_amdgcn_wave_barrier();
-    };
-    // lane (cl, fs) adds the 16 products of step fs; rows are visited in
-    // stored order, so the addresses are four bases plus constant offsets
-    auto fetch = [&](const float* area) {
-      float r[16];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float* base = area + cl * 256 + g * 64 + (fs ^ (g << 2));
-#pragma unroll
-        for (int j = 0; j < 4; ++j) r[4 * g + j] = base[16 * j];
-      }
-      __builtin_amdgcn_wave_barrier();
-      return ((r[0] + r[1]) + (r[2] + r[3]) + ((r[4] + r[5]) + (r[6] + r[7]))) +
-             ((r[8] + r[9]) + (r[10] + r[11]) + ((r[12] + r[13]) + (r[14] + r[15])));
-    };
     park(Q2, pr);
     const float y = __builtin_fmaf(Dc, u, fetch(Q2));
     park(Q1, q1);            // stays for the channel sums
     const int64_t fi = (b * L + tf) * dim + c;
     if (p.z != nullptr && fvalid) io::put(p.dz, fi, sdz * y);
 
-    // ---- adjoint recursion over the tile, last step first.  Operands are
-    // read two steps ahead; the scheduling barrier per step keeps the compiler
-    // from hoisting all 16 steps' operands (80 registers) to the loop head.
+    // ---- adjoint recursion over the tile, last step first
     float q2[kTT], r1[kTT], r2[kTT];
-    float4 qa = TC[kTT - 1][cl], qb = TC[kTT - 2][cl];
-    float2 ba = BC[kTT - 1][n], bb = BC[kTT - 2][n];
-#pragma unroll
-    for (int s = kTT - 1; s >= 0; --s) {
-      const float4 q = qa;
-      const float2 bc = ba;
-      qa = qb;
-      ba = bb;
-      if (s >= 2) {
-        qb = TC[s - 2][cl];
-        bb = BC[s - 2][n];
-      }
-      lam = __builtin_fmaf(bc.y, q.z, lam);          // + C dy
-      q2[s] = lam * q.y;                              // lam delta x
-      r2[s] = lam * bc.x;                             // lam B
-      lam *= av[s];                                   // a_t lam_t
-      const float t1 = lam * (s > 0 ? hs[s - 1] : hin);   // lam a_t h_{t-1}
-      dAacc = __builtin_fmaf(t1, q.x, dAacc);
-      r1[s] = t1 * Av;
-      // materialise this step's results here (otherwise the compiler sinks
-      // the q2 and dA updates past the loop and keeps their operands alive)
-      __asm__ volatile("" : "+v"(dAacc), "+v"(q2[s]), "+v"(r1[s]), "+v"(r2[s]));
-      __builtin_amdgcn_sched_barrier(0);
+    {
+      __asm__ volatile("" ::: "memory");   // B, C are read again here, not kept from the loop above
+      float4 bv = b4[3], cv = c4[3];
+      adj_step<15>(lam, dAacc, av, hs, hin, q2, r1, r2, dl, du, dy, Av, bv.w, cv.w);
+      adj_step<14>(lam, dAacc, av, hs, hin, q2, r1, r2, dl, du, dy, Av, bv.z, cv.z);
+      adj_step<13>(lam, dAacc, av, hs, hin, q2, r1, r2, dl, du, dy, Av, bv.y, cv.y);
+      adj_step<12>(lam, dAacc, av, hs, hin, q2, r1, r2, dl, du, dy, Av, bv.x, cv.x);
+      bv = b4[2]; cv = c4[2];
+      adj_step<11>(lam, dAacc, av, hs, hin, q2, r1, r2, dl, du, dy, Av, bv.w, cv.w);
+      adj_step<10>(lam, dAacc, av, hs, hin, q2, r1, r2, dl, du, dy, Av, bv.z, cv.z);
+      adj_step<9>(lam, dAacc, av, hs, hin, q2, r1, r2, dl, du, dy, Av, bv.y, cv.y);
+      adj_step<8>(lam, dAacc, av, hs, hin, q2, r1, r2, dl, du, dy, Av, bv.x, cv.x);
+      bv = b4[1]; cv = c4[1];
+      adj_step<7>(lam, dAacc, av, hs, hin, q2, r1, r2, dl, du, dy, Av, bv.w, cv.w);
+      adj_step<6>(lam, dAacc, av, hs, hin, q2, r1, r2, dl, du, dy, Av, bv.z, cv.z);
+      adj_step<5>(lam, dAacc, av, hs, hin, q2, r1, r2, dl, du, dy, Av, bv.y, cv.y);
+      adj_step<4>(lam, dAacc, av, hs, hin, q2, r1, r2, dl, du, dy, Av, bv.x, cv.x);
+      bv = b4[0]; cv = c4[0];
+      adj_step<3>(lam, dAacc, av, hs, hin, q2, r1, r2, dl, du, dy, Av, bv.w, cv.w);
+      adj_step<2>(lam, dAacc, av, hs, hin, q2, r1, r2, dl, du, dy, Av, bv.z, cv.z);
+      adj_step<1>(lam, dAacc, av, hs, hin, q2, r1, r2, dl, du, dy, Av, bv.y, cv.y);
+      adj_step<0>(lam, dAacc, av, hs, hin, q2, r1, r2, dl, du, dy, Av, bv.x, cv.x);
     }
     park(Q2, r1);
     const float s1 = fetch(Q2);
@@ -289,10 +358,11 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
     // ---- channel sums of this block: thread (step bs, state bn)
     {
       float sb = 0.f, sc = 0.f;
+      const int base = qpos(0, bn, bs);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        sc += Q1[qpos(r, bn, bs)];
-        sb += Q2[qpos(r, bn, bs)];
+        sc += Q1[base + r * kRow];
+        sb += Q2[base + r * kRow];
       }
       const int64_t t = t0 + bs;
       if (t < L) {
@@ -301,7 +371,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
         p.partC[o] = sc;
       }
     }
-    __syncthreads();   // Q1/Q2/TC/BC are rewritten by the next tile
+    __syncthreads();   // Q1/Q2/BT/CT are rewritten by the next tile
   }
 
   if (lane_ok && p.dh0 != nullptr) p.dh0[(b * dim + c) * N + n] = lam;

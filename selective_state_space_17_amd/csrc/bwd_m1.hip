@@ -78,14 +78,15 @@ __device__ __forceinline__ float row_sum(float v) {
 
 // Transpose areas: 16 rows (channels) x 16 states x 16 steps of fp32, row
 // stride 272.  Lane (cl, n) writes its 16 steps as four 16-byte stores at
-// qpos(cl, n, 4i); lane (cl, s) reads state n of step s, and thread (s, n)
-// reads row r.  The 16-dword row padding and the xor of the step by the
-// state group put every one of these accesses on 64 distinct banks, and the
-// addresses are affine in the loop index (one base register, immediate
-// offsets).
+// qpos(cl, n, 4i); lane (cl, s) reads state n of step s, and a thread of the
+// channel sums reads row r.  The LDS serves 32 banks: a 16-byte store per
+// 8 lanes, a 4-byte read per 32 lanes.  The row stride (272 = 16 mod 32) and
+// the xor of the step by bits 1-2 of the state put each of those groups on
+// distinct banks, and the read addresses are affine in the loop index.
 constexpr int kRow = 272;
-__device__ __forceinline__ int qpos(int cl, int n, int s) { return cl * kRow + 16 * n + (s ^ ((n >> 2) << 2)); }
+__device__ __forceinline__ int qpos(int cl, int n, int s) { return cl * kRow + 16 * n + (s ^ (((n >> 1) & 3) << 2)); }
 constexpr int kBT = 20;   // B^T / C^T row stride: lane n reads 4 steps with one 16-byte load
+constexpr int kBA = 68;   // the same for the 64-step staging tiles of the forward walk
 
 template <int S> __device__ __forceinline__ float bcast(float v) { return dpp<0x150 + S>(v); }   // row_newbcast:S
 
@@ -142,24 +143,23 @@ __device__ __forceinline__ void rec_step(float& h, float (&av)[16], float (&hs)[
 
 template <int S>
 __device__ __forceinline__ void adj_step(float& lam, float& dA, const float (&av)[16], const float (&hs)[16], float hin,
-                                         float (&q2)[16], float (&r1)[16], float (&r2)[16], float dl, float du, float dy,
-                                         float Av, float b, float cc) {
-  lam = __builtin_fmaf(cc, bcast<S>(dy), lam);    // + C dy
-  q2[S] = bcast<S>(du) * lam;                     // lam delta x
-  r2[S] = lam * b;                                // lam B
+                                         float (&ls)[16], float (&r1)[16], float dl, float dy, float Av, float cc) {
+  lam = __builtin_fmaf(cc, bcast<S>(dy), lam);    // + C dy: lam_t
+  ls[S] = lam;                                    // (lam_t B and lam_t delta x are formed when parked)
   lam *= av[S];                                   // a_t lam_t
   const float t1 = lam * (S > 0 ? hs[S > 0 ? S - 1 : 0] : hin);   // lam a_t h_{t-1}
   dA = __builtin_fmaf(t1, bcast<S>(dl), dA);
   r1[S] = t1 * Av;
-  // keep this step's results here: otherwise the compiler sinks the q2 and dA
-  // updates past the loop and keeps their operands alive across it
-  __asm__ volatile("" : "+v"(dA), "+v"(q2[S]), "+v"(r1[S]), "+v"(r2[S]));
+  // keep this step's results here: otherwise the compiler sinks the dA
+  // update past the loop and keeps its operands alive across it
+  __asm__ volatile("" : "+v"(dA), "+v"(ls[S]), "+v"(r1[S]));
 }
 
+// three waves per SIMD: what the grid of a typical layer provides (batch x dim / 16 blocks of 4 waves)
 template <typename T>
-__global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void scan_bwd_kernel(BwdParams p) {
   using io = Io<T>;
-  __shared__ __attribute__((aligned(16))) float BT[2][16 * kBT];   // B^T per tile (double-buffered in phase A)
+  __shared__ __attribute__((aligned(16))) float BT[16 * kBT];      // B^T per tile
   __shared__ __attribute__((aligned(16))) float CT[16 * kBT];      // C^T per tile
   __shared__ __attribute__((aligned(16))) float Q1[16 * kRow];     // dy*h (dC) / transposes
   __shared__ __attribute__((aligned(16))) float Q2[16 * kRow];     // lam*delta*x (dB) / transposes
@@ -182,40 +182,60 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
   float* ck = p.ckpt + (b * p.ntiles * D16 + c) * 16 + n;   // + k * D16 * 16
 
   // -------------------------------------------------------------- phase A
+  // Staged 64 steps at a time (one barrier per 64 steps, loads a whole
+  // staging tile ahead); the state entering every 16-step tile is stored.
   {
+    float* BA = Q1;   // B^T of a 64-step staging tile: [2 buffers][16 states][kBA]
     float h = (lane_ok && p.h0 != nullptr) ? p.h0[(b * dim + c) * N + n] : 0.f;
     // Loads are unconditional, from an in-range element when the step or
     // channel is past the end, and their raw values are left untouched until
     // the tile is staged (masking or widening them at once would make the
     // wave wait for the load there instead of a tile later).
-    T rd{}, rx{}, rb{};
-    bool ok = false, okb = false;
-    auto issue = [&](int k) {
-      const int64_t t = static_cast<int64_t>(k) * kTT + fs;
-      ok = t < L && c < dim;
-      const int64_t i = (b * L + (t < L ? t : L - 1)) * dim + (c < dim ? c : dim - 1);
-      rd = io::raw(p.delta, i);
-      rx = io::raw(p.x, i);
-      const int64_t tb = static_cast<int64_t>(k) * kTT + bs;
-      okb = tb < L && bn < N;
-      rb = io::raw(p.B, (b * L + (tb < L ? tb : L - 1)) * N + (bn < N ? bn : N - 1));
+    T rd[4], rx[4], rb[4];
+    bool ok[4], okb[4];
+    auto issue = [&](int64_t t0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t t = t0 + 16 * j + fs;
+        ok[j] = t < L && c < dim;
+        const int64_t i = (b * L + (t < L ? t : L - 1)) * dim + (c < dim ? c : dim - 1);
+        rd[j] = io::raw(p.delta, i);
+        rx[j] = io::raw(p.x, i);
+        const int64_t tb = t0 + 16 * j + bs;
+        okb[j] = tb < L && bn < N;
+        rb[j] = io::raw(p.B, (b * L + (tb < L ? tb : L - 1)) * N + (bn < N ? bn : N - 1));
+      }
     };
-    if (p.ntiles > 1) issue(0);
-    for (int k = 0; k + 1 < p.ntiles; ++k) {
-      float* bt = BT[k & 1];
-      bt[bn * kBT + bs] = okb ? io::cvt(rb) : 0.f;
-      const float dl = ok ? io::cvt(rd) : 0.f, du = dl * (ok ? io::cvt(rx) : 0.f);
-      ck[static_cast<int64_t>(k) * D16 * 16] = h;   // padded lanes store their zero state too
+    // tiles 0 .. ntiles-2 are walked (their end states are checkpoints 1 .. ntiles-1)
+    const int64_t walk = static_cast<int64_t>(p.ntiles - 1) * kTT;
+    if (walk > 0) issue(0);
+    int buf = 0;
+    for (int64_t t0 = 0; t0 < walk; t0 += 64, buf ^= 1) {
+      float* ba = BA + buf * 16 * kBA;
+      float dl[4], du[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ba[bn * kBA + 16 * j + bs] = okb[j] ? io::cvt(rb[j]) : 0.f;
+        dl[j] = ok[j] ? io::cvt(rd[j]) : 0.f;
+        du[j] = dl[j] * (ok[j] ? io::cvt(rx[j]) : 0.f);
+      }
       __syncthreads();
-      if (k + 2 < p.ntiles) issue(k + 1);
-      const float4* b4 = reinterpret_cast<const float4*>(bt + n * kBT);
-      fwd_group<0>(h, dl, du, A2, b4[0]);
-      fwd_group<1>(h, dl, du, A2, b4[1]);
-      fwd_group<2>(h, dl, du, A2, b4[2]);
-      fwd_group<3>(h, dl, du, A2, b4[3]);
+      if (t0 + 64 < walk) issue(t0 + 64);
+      const float4* b4 = reinterpret_cast<const float4*>(ba + n * kBA);
+      const int k0 = static_cast<int>(t0 / kTT);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (t0 + 16 * j < walk) {   // uniform
+          ck[static_cast<int64_t>(k0 + j) * D16 * 16] = h;   // padded lanes store their zero state too
+          fwd_group<0>(h, dl[j], du[j], A2, b4[4 * j + 0]);
+          fwd_group<1>(h, dl[j], du[j], A2, b4[4 * j + 1]);
+          fwd_group<2>(h, dl[j], du[j], A2, b4[4 * j + 2]);
+          fwd_group<3>(h, dl[j], du[j], A2, b4[4 * j + 3]);
+        }
+      }
     }
     if (p.ntiles > 0) ck[static_cast<int64_t>(p.ntiles - 1) * D16 * 16] = h;
-    __syncthreads();   // orders the checkpoint stores before phase B's loads; frees BT
+    __syncthreads();   // orders the checkpoint stores before phase B's loads; frees Q1
   }
 
   // -------------------------------------------------------------- phase B
@@ -243,22 +263,25 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
   };
   // transposes through this wave's own rows of Q1/Q2 (no other wave touches
   // them before the barrier that ends the tile's compute); a wave's LDS
-  // accesses run in order, so a row is rewritten only after it was read back
+  // accesses run in order, so a row is rewritten only after the reads issued
+  // before the rewrite have been served
   auto park = [&](float* area, const float (&v)[kTT]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       *reinterpret_cast<float4*>(&area[qpos(cl, n, 4 * i)]) = float4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
     __builtin_amdgcn_wave_barrier();
   };
-  auto fetch = [&](const float* area) {   // lane (cl, fs): sum over the 16 states of step fs
-    float r[16];
+  // lane (cl, fs) reads the 16 states' products of step fs (the sum is taken
+  // later, so other work can cover the LDS latency)
+  auto fetch = [&](const float* area, float (&r)[16]) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const float* base = area + cl * kRow + 64 * g + (fs ^ (g << 2));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) r[4 * g + j] = base[16 * j];
+    for (int m = 0; m < 8; ++m) {   // states 2m, 2m + 1
+      const float* base = area + cl * kRow + 32 * m + (fs ^ ((m & 3) << 2));
+      r[2 * m] = base[0];
+      r[2 * m + 1] = base[16];
     }
-    __builtin_amdgcn_wave_barrier();
+  };
+  auto sum16 = [](const float (&r)[16]) {
     return ((r[0] + r[1]) + (r[2] + r[3]) + ((r[4] + r[5]) + (r[6] + r[7]))) +
            ((r[8] + r[9]) + (r[10] + r[11]) + ((r[12] + r[13]) + (r[14] + r[15])));
   };
@@ -279,13 +302,13 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
       dy = g * zz * sg;
       sdz = g * sg * __builtin_fmaf(zz, 1.f - sg, 1.f);
     }
-    BT[0][bn * kBT + bs] = okb ? io::cvt(rb) : 0.f;
+    BT[bn * kBT + bs] = okb ? io::cvt(rb) : 0.f;
     CT[bn * kBT + bs] = okb ? io::cvt(rc) : 0.f;
     float h = rh;            // state entering the tile
     const float hin = rh;    // (rh is reloaded for the next tile below)
     __syncthreads();
     if (k > 0) issue(k - 1);
-    const float4* b4 = reinterpret_cast<const float4*>(&BT[0][n * kBT]);
+    const float4* b4 = reinterpret_cast<const float4*>(&BT[n * kBT]);
     const float4* c4 = reinterpret_cast<const float4*>(&CT[n * kBT]);
 
     // ---- recompute the tile's states and decays
@@ -313,60 +336,88 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
       rec_step<15>(h, av, hs, pr, q1, dl, du, dy, A2, bv.w, cv.w);
     }
     park(Q2, pr);
-    const float y = __builtin_fmaf(Dc, u, fetch(Q2));
-    park(Q1, q1);            // stays for the channel sums
+    float ry[16];
+    fetch(Q2, ry);           // y of step fs, summed after the adjoint loop
     const int64_t fi = (b * L + tf) * dim + c;
-    if (p.z != nullptr && fvalid) io::put(p.dz, fi, sdz * y);
 
     // ---- adjoint recursion over the tile, last step first
-    float q2[kTT], r1[kTT], r2[kTT];
+    float ls[kTT], r1[kTT];
     {
       __asm__ volatile("" ::: "memory");   // B, C are read again here, not kept from the loop above
-      float4 bv = b4[3], cv = c4[3];
-      adj_step<15>(lam, dAacc, av, hs, hin, q2, r1, r2, dl, du, dy, Av, bv.w, cv.w);
-      adj_step<14>(lam, dAacc, av, hs, hin, q2, r1, r2, dl, du, dy, Av, bv.z, cv.z);
-      adj_step<13>(lam, dAacc, av, hs, hin, q2, r1, r2, dl, du, dy, Av, bv.y, cv.y);
-      adj_step<12>(lam, dAacc, av, hs, hin, q2, r1, r2, dl, du, dy, Av, bv.x, cv.x);
-      bv = b4[2]; cv = c4[2];
-      adj_step<11>(lam, dAacc, av, hs, hin, q2, r1, r2, dl, du, dy, Av, bv.w, cv.w);
-      adj_step<10>(lam, dAacc, av, hs, hin, q2, r1, r2, dl, du, dy, Av, bv.z, cv.z);
-      adj_step<9>(lam, dAacc, av, hs, hin, q2, r1, r2, dl, du, dy, Av, bv.y, cv.y);
-      adj_step<8>(lam, dAacc, av, hs, hin, q2, r1, r2, dl, du, dy, Av, bv.x, cv.x);
-      bv = b4[1]; cv = c4[1];
-      adj_step<7>(lam, dAacc, av, hs, hin, q2, r1, r2, dl, du, dy, Av, bv.w, cv.w);
-      adj_step<6>(lam, dAacc, av, hs, hin, q2, r1, r2, dl, du, dy, Av, bv.z, cv.z);
-      adj_step<5>(lam, dAacc, av, hs, hin, q2, r1, r2, dl, du, dy, Av, bv.y, cv.y);
-      adj_step<4>(lam, dAacc, av, hs, hin, q2, r1, r2, dl, du, dy, Av, bv.x, cv.x);
-      bv = b4[0]; cv = c4[0];
-      adj_step<3>(lam, dAacc, av, hs, hin, q2, r1, r2, dl, du, dy, Av, bv.w, cv.w);
-      adj_step<2>(lam, dAacc, av, hs, hin, q2, r1, r2, dl, du, dy, Av, bv.z, cv.z);
-      adj_step<1>(lam, dAacc, av, hs, hin, q2, r1, r2, dl, du, dy, Av, bv.y, cv.y);
-      adj_step<0>(lam, dAacc, av, hs, hin, q2, r1, r2, dl, du, dy, Av, bv.x, cv.x);
+      float4 cv = c4[3];
+      adj_step<15>(lam, dAacc, av, hs, hin, ls, r1, dl, dy, Av, cv.w);
+      adj_step<14>(lam, dAacc, av, hs, hin, ls, r1, dl, dy, Av, cv.z);
+      adj_step<13>(lam, dAacc, av, hs, hin, ls, r1, dl, dy, Av, cv.y);
+      adj_step<12>(lam, dAacc, av, hs, hin, ls, r1, dl, dy, Av, cv.x);
+      cv = c4[2];
+      adj_step<11>(lam, dAacc, av, hs, hin, ls, r1, dl, dy, Av, cv.w);
+      adj_step<10>(lam, dAacc, av, hs, hin, ls, r1, dl, dy, Av, cv.z);
+      adj_step<9>(lam, dAacc, av, hs, hin, ls, r1, dl, dy, Av, cv.y);
+      adj_step<8>(lam, dAacc, av, hs, hin, ls, r1, dl, dy, Av, cv.x);
+      cv = c4[1];
+      adj_step<7>(lam, dAacc, av, hs, hin, ls, r1, dl, dy, Av, cv.w);
+      adj_step<6>(lam, dAacc, av, hs, hin, ls, r1, dl, dy, Av, cv.z);
+      adj_step<5>(lam, dAacc, av, hs, hin, ls, r1, dl, dy, Av, cv.y);
+      adj_step<4>(lam, dAacc, av, hs, hin, ls, r1, dl, dy, Av, cv.x);
+      cv = c4[0];
+      adj_step<3>(lam, dAacc, av, hs, hin, ls, r1, dl, dy, Av, cv.w);
+      adj_step<2>(lam, dAacc, av, hs, hin, ls, r1, dl, dy, Av, cv.z);
+      adj_step<1>(lam, dAacc, av, hs, hin, ls, r1, dl, dy, Av, cv.y);
+      adj_step<0>(lam, dAacc, av, hs, hin, ls, r1, dl, dy, Av, cv.x);
     }
-    park(Q2, r1);
-    const float s1 = fetch(Q2);
-    park(Q2, r2);
-    const float s2 = fetch(Q2);
+    const float y = __builtin_fmaf(Dc, u, sum16(ry));
+    if (p.z != nullptr && fvalid) io::put(p.dz, fi, sdz * y);
+    // both sums over states in one LDS round trip (Q1's rows take q1 after)
+    park(Q1, r1);
+    {
+      float r2[kTT];   // lam_t B_t
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 bv = b4[g];
+        r2[4 * g] = ls[4 * g] * bv.x;
+        r2[4 * g + 1] = ls[4 * g + 1] * bv.y;
+        r2[4 * g + 2] = ls[4 * g + 2] * bv.z;
+        r2[4 * g + 3] = ls[4 * g + 3] * bv.w;
+      }
+      park(Q2, r2);
+    }
+    float ra[16], rb2[16];
+    fetch(Q1, ra);
+    fetch(Q2, rb2);
+    dDacc = __builtin_fmaf(dy, u, dDacc);
+    const float s1 = sum16(ra), s2 = sum16(rb2);
     if (fvalid) {
       io::put(p.ddelta, fi, __builtin_fmaf(u, s2, s1));
       io::put(p.dx, fi, __builtin_fmaf(dl, s2, Dc * dy));
     }
-    dDacc = __builtin_fmaf(dy, u, dDacc);
-    park(Q2, q2);
+    park(Q1, q1);
+    {
+      float q2[kTT];   // lam_t delta_t x_t
+      q2[0] = ls[0] * bcast<0>(du);   q2[1] = ls[1] * bcast<1>(du);   q2[2] = ls[2] * bcast<2>(du);
+      q2[3] = ls[3] * bcast<3>(du);   q2[4] = ls[4] * bcast<4>(du);   q2[5] = ls[5] * bcast<5>(du);
+      q2[6] = ls[6] * bcast<6>(du);   q2[7] = ls[7] * bcast<7>(du);   q2[8] = ls[8] * bcast<8>(du);
+      q2[9] = ls[9] * bcast<9>(du);   q2[10] = ls[10] * bcast<10>(du); q2[11] = ls[11] * bcast<11>(du);
+      q2[12] = ls[12] * bcast<12>(du); q2[13] = ls[13] * bcast<13>(du); q2[14] = ls[14] * bcast<14>(du);
+      q2[15] = ls[15] * bcast<15>(du);
+      park(Q2, q2);
+    }
     __syncthreads();
 
-    // ---- channel sums of this block: thread (step bs, state bn)
+    // ---- channel sums of this block: thread (step rs, state rn); each half
+    // wave takes 4 steps x 8 states, which the layout spreads over 32 banks
     {
       float sb = 0.f, sc = 0.f;
-      const int base = qpos(0, bn, bs);
+      const int rn = (tid & 7) | (((tid >> 5) & 1) << 3);
+      const int rs = ((tid >> 3) & 3) | ((tid >> 6) << 2);
+      const int base = qpos(0, rn, rs);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         sc += Q1[base + r * kRow];
         sb += Q2[base + r * kRow];
       }
-      const int64_t t = t0 + bs;
+      const int64_t t = t0 + rs;
       if (t < L) {
-        const int64_t o = ((static_cast<int64_t>(cb) * p.batch + b) * L + t) * 16 + bn;
+        const int64_t o = ((static_cast<int64_t>(cb) * p.batch + b) * L + t) * 16 + rn;
         p.partB[o] = sb;
         p.partC[o] = sc;
       }

@@ -422,7 +422,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         p.partC[o] = sc;
       }
     }
-    __syncthreads();   // Q1/Q2/BT/CT are rewritten by the next tile
+    // No barrier here: B^T / C^T are not read after the one above, so the next
+    // tile may stage them at once, and Q1 / Q2 are written again only after
+    // the next tile's first barrier, which every wave reaches after its sums.
   }
 
   if (lane_ok && p.dh0 != nullptr) p.dh0[(b * dim + c) * N + n] = lam;
@@ -431,22 +433,47 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   if (n == 0) p.wsD[b * D16 + c] = dDrow;
 }
 
-// dB, dC: sum of the per-block partials, in block order
+// dB, dC: sum of the per-block partials, in block order.  A thread owns four
+// consecutive (step, state) slots (16-byte loads) and keeps several blocks'
+// loads in flight; the order of the additions is fixed.
 __global__ __launch_bounds__(256) void bwd_reduce_bc(const float* partB, const float* partC, float* dB, float* dC,
                                                      int64_t batch, int64_t L, int64_t N, int ncb) {
   const int64_t rows = batch * L;
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;   // (row, n16)
-  if (i >= rows * 16) return;
-  const int64_t row = i >> 4;
-  const int nn = static_cast<int>(i & 15);
-  if (nn >= N) return;
-  float sb = 0.f, sc = 0.f;
-  for (int k = 0; k < ncb; ++k) {
-    sb += partB[k * rows * 16 + i];
-    sc += partC[k * rows * 16 + i];
+  const int64_t q = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;   // (row, 4-state group)
+  if (q >= rows * 4) return;
+  const int64_t stride = rows * 4;   // float4 slots per block's partial
+  const float4* pb = reinterpret_cast<const float4*>(partB) + q;
+  const float4* pc = reinterpret_cast<const float4*>(partC) + q;
+  float4 sb = {0.f, 0.f, 0.f, 0.f}, sc = {0.f, 0.f, 0.f, 0.f};
+  int k = 0;
+  for (; k + 4 <= ncb; k += 4) {
+    float4 vb[4], vc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      vb[j] = pb[(k + j) * stride];
+      vc[j] = pc[(k + j) * stride];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sb.x += vb[j].x; sb.y += vb[j].y; sb.z += vb[j].z; sb.w += vb[j].w;
+      sc.x += vc[j].x; sc.y += vc[j].y; sc.z += vc[j].z; sc.w += vc[j].w;
+    }
   }
-  dB[row * N + nn] = sb;
-  dC[row * N + nn] = sc;
+  for (; k < ncb; ++k) {
+    const float4 vb = pb[k * stride], vc = pc[k * stride];
+    sb.x += vb.x; sb.y += vb.y; sb.z += vb.z; sb.w += vb.w;
+    sc.x += vc.x; sc.y += vc.y; sc.z += vc.z; sc.w += vc.w;
+  }
+  const int64_t row = q >> 2;
+  const int n0 = static_cast<int>(q & 3) * 4;
+  const float b4[4] = {sb.x, sb.y, sb.z, sb.w}, c4[4] = {sc.x, sc.y, sc.z, sc.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (n0 + j < N) {
+      dB[row * N + n0 + j] = b4[j];
+      dC[row * N + n0 + j] = c4[j];
+    }
+  }
 }
 
 // dA, dD: sum over the batch rows, in order
@@ -516,7 +543,7 @@ hipError_t scan_bwd_launch(const ScanBwdArgs& a, hipStream_t stream) {
       hipLaunchKernelGGL(scan_bwd_kernel<float>, grid, dim3(kThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t nbc = (a.batch * a.L * 16 + 255) / 256;
+    const int64_t nbc = (a.batch * a.L * 4 + 255) / 256;
     if (nbc > 0) {
       hipLaunchKernelGGL(bwd_reduce_bc, dim3(static_cast<unsigned>(nbc)), dim3(256), 0, stream, p.partB, p.partC,
                          a.dB, a.dC, a.batch, a.L, a.N, p.ncb);

@@ -168,8 +168,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   const int cl = tid >> 4;          // channel row; also: staging / finishing thread of step fs = n
   const int n = tid & 15;           // state
   const int fs = n;
-  const int cb = static_cast<int>(blockIdx.x % static_cast<unsigned>(p.ncb));
-  const int64_t b = blockIdx.x / static_cast<unsigned>(p.ncb);
+  // block -> (batch row, channel block); blocks are dealt to the 8 XCDs in
+  // turn, so consecutive blocks are remapped to put 4 neighbouring channel
+  // blocks (one 128-byte line of a bf16 row) on one XCD, whose L2 then serves
+  // them all
+  const int64_t nb = gridDim.x;
+  const int64_t bid = blockIdx.x;
+  int64_t lin = bid;
+  if (bid < (nb / 32) * 32) {
+    const int64_t xcd = bid % 8, rr = bid / 8;
+    lin = ((rr / 4) * 8 + xcd) * 4 + rr % 4;
+  }
+  const int cb = static_cast<int>(lin % p.ncb);
+  const int64_t b = lin / p.ncb;
   const int64_t c0 = static_cast<int64_t>(cb) * kCPB;
   const int64_t c = c0 + cl;
   const int64_t L = p.L, dim = p.dim, N = p.N;

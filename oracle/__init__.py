@@ -13,6 +13,12 @@ leg may import this package.  The product library never uses it.
                  (mssm_oracle.c: oracle_ssd_fwd).  Pinned by: equality with the
                  Mamba-1 oracle under head broadcast, the geometric closed form
                  with scalar A, a brute-force unrolled sum, chaining.
+``conv_silu``, ``conv_scan_fwd``
+              -- the short causal convolution + SiLU in front of the scan, and
+                 the scan on its output (mssm_oracle.c: oracle_conv_silu,
+                 oracle_conv_scan_fwd).  Pinned by numpy.convolve, the impulse
+                 response, chaining through the initial inputs, and equality
+                 with scan_fwd on the convolved x.
 ``scan_bwd``  -- gradients of ``scan_fwd`` by reverse mode through the same
                  sequential loop, fp64 (mssm_oracle.c: oracle_scan_bwd).  Pinned
                  by central finite differences of ``scan_fwd`` itself
@@ -52,6 +58,10 @@ def load_library(path: Optional[str] = None):
     lib.oracle_scan_fwd.argtypes = [i64, i64, i64, i64, i32, p, p, p, p, p, p, p, p, i64, i64, p, p, i32]
     lib.oracle_ssd_fwd.restype = i32
     lib.oracle_ssd_fwd.argtypes = [i64, i64, i64, i64, i64, i64, i32, p, p, p, p, p, p, p, p, i64, i64, p, p, i32]
+    lib.oracle_conv_silu.restype = i32
+    lib.oracle_conv_silu.argtypes = [i64, i64, i64, i64, i32, p, p, p, p, p]
+    lib.oracle_conv_scan_fwd.restype = i32
+    lib.oracle_conv_scan_fwd.argtypes = [i64, i64, i64, i64, i64, i32] + [p] * 4 + [p] * 7 + [i64, i64, p, p, i32]
     lib.oracle_scan_bwd.restype = i32
     lib.oracle_scan_bwd.argtypes = [i64, i64, i64, i64, i32] + [p] * 10 + [p] * 8 + [i32]
     return lib
@@ -169,3 +179,44 @@ def scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, dout=None, dfinal=None,
     if rc != 0:
         raise ValueError("oracle_scan_bwd rejected its arguments")
     return g
+
+
+def conv_silu(xin, w, bias=None, init=None, lib=None):
+    """Short causal convolution + SiLU. xin [Bsz, L, Dm] (io dtype); w [Dm, W] fp32; bias [Dm] fp32;
+    init [Bsz, W-1, Dm] (io dtype, the inputs before t = 0). Returns x [Bsz, L, Dm] fp64."""
+    xin, init = _c(xin), _c(init)
+    io = _io_code(xin)
+    if init is not None and _io_code(init) != io:
+        raise TypeError("init must share the io dtype")
+    w, bias = _c(w, np.float32), _c(bias, np.float32)
+    bsz, L, dm = xin.shape
+    W = w.shape[1]
+    x = np.empty((bsz, L, dm), dtype=np.float64)
+    rc = (lib or _get()).oracle_conv_silu(bsz, L, dm, W, io, _ptr(xin), _ptr(w), _ptr(bias), _ptr(init), _ptr(x))
+    if rc != 0:
+        raise ValueError("oracle_conv_silu rejected its arguments")
+    return x
+
+
+def conv_scan_fwd(xin, w, bias, init, delta, A, B, C, D=None, z=None, h0=None, c0: int = 0,
+                  c1: Optional[int] = None, nthreads: Optional[int] = None, lib=None):
+    """scan_fwd with x = conv_silu(xin, w, bias, init) (kept in fp64). Returns (out, final_state) fp64."""
+    xin, init, delta, B, C, z = _c(xin), _c(init), _c(delta), _c(B), _c(C), _c(z)
+    io = _io_code(xin)
+    for t in (delta, B, C) + tuple(a for a in (z, init) if a is not None):
+        if _io_code(t) != io:
+            raise TypeError("xin, delta, B, C, z, init must share one dtype")
+    w, bias = _c(w, np.float32), _c(bias, np.float32)
+    A, D, h0 = _c(A, np.float32), _c(D, np.float32), _c(h0, np.float32)
+    bsz, L, dm = xin.shape
+    N, W = A.shape[1], w.shape[1]
+    c1 = dm if c1 is None else c1
+    nc = c1 - c0
+    out = np.empty((bsz, L, nc), dtype=np.float64)
+    fin = np.empty((bsz, nc, N), dtype=np.float64)
+    rc = (lib or _get()).oracle_conv_scan_fwd(bsz, L, dm, N, W, io, _ptr(xin), _ptr(w), _ptr(bias), _ptr(init),
+                                              _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+                                              c0, c1, _ptr(out), _ptr(fin), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_conv_scan_fwd rejected its arguments")
+    return out, fin

@@ -62,6 +62,7 @@ typedef struct {
     int io;
     const void *x, *delta, *Bm, *Cm, *z;
     const float *A, *Dv, *h0;
+    const double* x64;       /* nullable: x already computed in fp64 (the convolution front end) */
     int64_t c0, c1;          /* channel range [c0, c1) */
     double *out, *final_state;
     int64_t row_begin, row_end;  /* rows = b * (c1 - c0) + (c - c0) */
@@ -74,7 +75,7 @@ static void scan_row(const scan_job* j, int64_t b, int64_t c, double* h) {
         const int64_t i = (b * L + t) * D + c;      /* [B, L, D] */
         const int64_t r = (b * L + t) * N;          /* [B, L, N] */
         const double d = load_io(j->delta, j->io, i);
-        const double u = load_io(j->x, j->io, i);
+        const double u = j->x64 ? j->x64[i] : load_io(j->x, j->io, i);
         double acc = 0.0;
         for (int64_t n = 0; n < N; ++n) {
             const double dA = exp(d * (double)j->A[c * N + n]);
@@ -105,10 +106,10 @@ static void* scan_worker(void* arg) {
  * x, delta, z: [Bsz, L, D]; Bm, Cm: [Bsz, L, N] in io dtype; A [D, N], Dv [D],
  * h0 [Bsz, D, N] fp32 (Dv, z, h0 nullable).  Returns 0, or -1 on bad sizes.
  */
-int oracle_scan_fwd(int64_t Bsz, int64_t L, int64_t D, int64_t N, int io,
-                    const void* x, const void* delta, const float* A, const void* Bm, const void* Cm,
-                    const float* Dv, const void* z, const float* h0, int64_t c0, int64_t c1,
-                    double* out, double* final_state, int nthreads) {
+static int scan_fwd_impl(int64_t Bsz, int64_t L, int64_t D, int64_t N, int io,
+                         const void* x, const double* x64, const void* delta, const float* A, const void* Bm,
+                         const void* Cm, const float* Dv, const void* z, const float* h0, int64_t c0, int64_t c1,
+                         double* out, double* final_state, int nthreads) {
     if (Bsz < 0 || L < 0 || D <= 0 || N <= 0 || c0 < 0 || c1 > D || c1 < c0) return -1;
     if (io != IO_F32 && io != IO_BF16) return -1;
     const int64_t rows = Bsz * (c1 - c0);
@@ -121,7 +122,7 @@ int oracle_scan_fwd(int64_t Bsz, int64_t L, int64_t D, int64_t N, int io,
         scan_job* j = &jobs[k];
         j->Bsz = Bsz; j->L = L; j->D = D; j->N = N; j->io = io;
         j->x = x; j->delta = delta; j->Bm = Bm; j->Cm = Cm; j->z = z;
-        j->A = A; j->Dv = Dv; j->h0 = h0; j->c0 = c0; j->c1 = c1;
+        j->A = A; j->Dv = Dv; j->h0 = h0; j->x64 = x64; j->c0 = c0; j->c1 = c1;
         j->out = out; j->final_state = final_state;
         j->row_begin = rows * k / nthreads;
         j->row_end = rows * (k + 1) / nthreads;
@@ -132,6 +133,65 @@ int oracle_scan_fwd(int64_t Bsz, int64_t L, int64_t D, int64_t N, int io,
     free(jobs);
     free(th);
     return 0;
+}
+
+int oracle_scan_fwd(int64_t Bsz, int64_t L, int64_t D, int64_t N, int io,
+                    const void* x, const void* delta, const float* A, const void* Bm, const void* Cm,
+                    const float* Dv, const void* z, const float* h0, int64_t c0, int64_t c1,
+                    double* out, double* final_state, int nthreads) {
+    return scan_fwd_impl(Bsz, L, D, N, io, x, NULL, delta, A, Bm, Cm, Dv, z, h0, c0, c1, out, final_state,
+                         nthreads);
+}
+
+/* ------------------------------------------------------------------------- */
+/* Short causal convolution + SiLU in front of the scan                      */
+/* ------------------------------------------------------------------------- */
+/*
+ * The short causal convolution of the Mamba-1/2 block ("Mamba-3" blog,
+ * "Arquitectura": the layer Mamba-3 drops applied one to the state input;
+ * "Mamba-2 y state-space models" 4.3 installs its kernel package beside the
+ * scan's), read as a per-channel (depthwise) causal convolution over time of
+ * width W followed by SiLU, its output being the scan's x:
+ *   x[b,t,c] = silu(bias[c] + sum_{k<W} w[c,k] * xin[b, t-(W-1)+k, c])
+ * where xin at a step before 0 is init[b, W-1+s, c] (the W-1 inputs that
+ * precede the sequence, oldest first), or 0 without init.  fp64 out.
+ */
+int oracle_conv_silu(int64_t Bsz, int64_t L, int64_t D, int64_t W, int io, const void* xin, const float* w,
+                     const float* bias, const void* init, double* x) {
+    if (Bsz < 0 || L < 0 || D <= 0 || W < 1) return -1;
+    if (io != IO_F32 && io != IO_BF16) return -1;
+    for (int64_t b = 0; b < Bsz; ++b)
+        for (int64_t t = 0; t < L; ++t)
+            for (int64_t c = 0; c < D; ++c) {
+                double acc = bias ? (double)bias[c] : 0.0;
+                for (int64_t k = 0; k < W; ++k) {
+                    const int64_t s = t - (W - 1) + k;
+                    double v = 0.0;
+                    if (s >= 0)
+                        v = load_io(xin, io, (b * L + s) * D + c);
+                    else if (init)
+                        v = load_io(init, io, (b * (W - 1) + (W - 1) + s) * D + c);
+                    acc += (double)w[c * W + k] * v;
+                }
+                x[(b * L + t) * D + c] = silu(acc);
+            }
+    return 0;
+}
+
+/* The scan of oracle_scan_fwd with x = oracle_conv_silu(xin, ...). */
+int oracle_conv_scan_fwd(int64_t Bsz, int64_t L, int64_t D, int64_t N, int64_t W, int io,
+                         const void* xin, const float* w, const float* bias, const void* init,
+                         const void* delta, const float* A, const void* Bm, const void* Cm,
+                         const float* Dv, const void* z, const float* h0, int64_t c0, int64_t c1,
+                         double* out, double* final_state, int nthreads) {
+    if (Bsz < 0 || L < 0 || D <= 0 || W < 1) return -1;
+    double* x = (double*)malloc(sizeof(double) * (size_t)(Bsz * L * D > 0 ? Bsz * L * D : 1));
+    int rc = oracle_conv_silu(Bsz, L, D, W, io, xin, w, bias, init, x);
+    if (rc == 0)
+        rc = scan_fwd_impl(Bsz, L, D, N, io, NULL, x, delta, A, Bm, Cm, Dv, z, h0, c0, c1, out, final_state,
+                           nthreads);
+    free(x);
+    return rc;
 }
 
 /* ------------------------------------------------------------------------- */

@@ -18,6 +18,10 @@ Passages (page title, section):
                        Bbar_t x_t unrolled into a sum of products.
   chaining             the fixed-size state is the whole memory
                        ("Mamba-2 y state-space models" 4.3 notes).
+  short convolution    the causal convolution in front of the scan ("Mamba-3"
+                       blog, "Arquitectura") against numpy.convolve, its impulse
+                       response, chaining through the initial inputs, and the
+                       scan of its output.
   gradients            the reverse-mode derivative of the scan must equal
                        central finite differences of the (separately pinned)
                        forward oracle, for every input and both outputs.
@@ -435,8 +439,84 @@ def pin_scan_bwd_linear_in_upstream(lib, seed=22):
         assert np.all(v == 0), f"zero upstream gradient gave nonzero {k}"
 
 
+# ---------------------------------------------------------------------------
+# Short causal convolution + SiLU in front of the scan
+# ---------------------------------------------------------------------------
+def _conv_case(rng, bsz=2, L=23, d=5, W=4):
+    xin = rng.standard_normal((bsz, L, d)).astype(np.float32)
+    w = rng.standard_normal((d, W)).astype(np.float32)
+    bias = rng.standard_normal(d).astype(np.float32)
+    init = rng.standard_normal((bsz, W - 1, d)).astype(np.float32)
+    return xin, w, bias, init
+
+
+def pin_conv_numpy(lib, seed=31):
+    """Every channel's pre-activation equals numpy.convolve of the padded input with the flipped taps."""
+    rng = _rng(seed)
+    for W in (1, 2, 3, 4):
+        xin, w, bias, init = _conv_case(rng, W=W)
+        for use_init in (False, True):
+            x = oracle.conv_silu(xin, w, bias, init if use_init and W > 1 else None, lib=lib)
+            bsz, L, d = xin.shape
+            want = np.empty_like(x)
+            for b in range(bsz):
+                for c in range(d):
+                    pre = (init[b, :, c] if use_init and W > 1 else np.zeros(W - 1, np.float32)).astype(np.float64)
+                    seq = np.concatenate([pre, xin[b, :, c].astype(np.float64)])
+                    full = np.convolve(seq, w[c, ::-1].astype(np.float64), mode="valid")   # length L
+                    want[b, :, c] = _silu(full + np.float64(bias[c]))
+            _close(x, want, 1e-13, f"conv W={W} init={use_init}")
+
+
+def pin_conv_impulse(lib, seed=32):
+    """A unit impulse at t0 gives silu(bias + w[c, W-1-(t-t0)]) for t0 <= t < t0+W and silu(bias) elsewhere."""
+    rng = _rng(seed)
+    _, w, bias, _ = _conv_case(rng, d=3, W=4)
+    L, t0 = 12, 5
+    xin = np.zeros((1, L, 3), np.float32)
+    xin[0, t0, :] = 1.0
+    x = oracle.conv_silu(xin, w, bias, lib=lib)
+    want = np.empty((1, L, 3))
+    for t in range(L):
+        for c in range(3):
+            k = t - t0
+            want[0, t, c] = _silu(np.float64(bias[c]) + (np.float64(w[c, 3 - k]) if 0 <= k < 4 else 0.0))
+    _close(x, want, 1e-14, "conv impulse response")
+
+
+def pin_conv_chaining(lib, seed=33):
+    """Convolving [L1, L) with init = the W-1 inputs before L1 gives the tail of the whole convolution."""
+    rng = _rng(seed)
+    xin, w, bias, init = _conv_case(rng, L=30, W=4)
+    L1 = 11
+    full = oracle.conv_silu(xin, w, bias, init, lib=lib)
+    tail = oracle.conv_silu(xin[:, L1:], w, bias, np.ascontiguousarray(xin[:, L1 - 3:L1]), lib=lib)
+    _close(tail, full[:, L1:], 1e-15, "conv chaining through the initial inputs")
+
+
+def pin_conv_scan_composition(lib, seed=34):
+    """conv_scan_fwd equals scan_fwd run on the convolved x (rounded to fp32, hence the tolerance), and the
+    skip term uses the convolved x, not the raw input."""
+    rng = _rng(seed)
+    xin, w, bias, init = _conv_case(rng, bsz=2, L=37, d=4, W=3)
+    n = 6
+    delta = rng.uniform(0.05, 0.8, size=xin.shape).astype(np.float32)
+    A = _neg_A(rng, 4, n)
+    B = rng.standard_normal((2, 37, n)).astype(np.float32)
+    C = rng.standard_normal((2, 37, n)).astype(np.float32)
+    D = rng.standard_normal(4).astype(np.float32)
+    z = rng.standard_normal(xin.shape).astype(np.float32)
+    h0 = rng.standard_normal((2, 4, n)).astype(np.float32)
+    out, fin = oracle.conv_scan_fwd(xin, w, bias, init, delta, A, B, C, D, z, h0, lib=lib)
+    x32 = oracle.conv_silu(xin, w, bias, init, lib=lib).astype(np.float32)
+    ref, ref_fin = oracle.scan_fwd(x32, delta, A, B, C, D, z, h0, lib=lib)
+    _close(out, ref, 1e-6, "conv + scan == scan(conv)")
+    _close(fin, ref_fin, 1e-6, "conv + scan final state")
+
+
 SCAN_PINS = [pin_lti_convolution, pin_delta_zero, pin_geometric, pin_bruteforce, pin_chaining, pin_reset,
              pin_linearity_causality, pin_gate_skip, pin_bf16_codec]
 SSD_PINS = [pin_ssd_equals_broadcast_scan, pin_ssd_geometric, pin_ssd_bruteforce, pin_ssd_chaining]
 BWD_PINS = [pin_scan_bwd_finite_differences, pin_scan_bwd_linear_in_upstream]
-ALL_PINS = SCAN_PINS + SSD_PINS + BWD_PINS
+CONV_PINS = [pin_conv_numpy, pin_conv_impulse, pin_conv_chaining, pin_conv_scan_composition]
+ALL_PINS = SCAN_PINS + SSD_PINS + BWD_PINS + CONV_PINS

@@ -55,6 +55,16 @@ MUTANTS = {
     "bwd_dD_ungated": ("j->dD[c] += dy * u;", "j->dD[c] += g * u;"),
     "bwd_dx_without_delta": ("du += lam[n] * d * Bn;", "du += lam[n] * Bn;"),
     "bwd_dfinal_ignored": ("j->dfinal ? (double)j->dfinal[(b * D + c) * N + n] : 0.0", "0.0"),
+    # short convolution front end
+    "conv_taps_reversed": ("acc += (double)w[c * W + k] * v;", "acc += (double)w[c * W + (W - 1 - k)] * v;"),
+    "conv_init_ignored": ("else if (init)", "else if (0)"),
+    "conv_init_newest_first": ("load_io(init, io, (b * (W - 1) + (W - 1) + s) * D + c)",
+                               "load_io(init, io, (b * (W - 1) + (-1 - s)) * D + c)"),
+    "conv_bias_dropped": ("double acc = bias ? (double)bias[c] : 0.0;", "double acc = 0.0;"),
+    "conv_no_silu": ("x[(b * L + t) * D + c] = silu(acc);", "x[(b * L + t) * D + c] = acc;"),
+    "conv_not_causal": ("const int64_t s = t - (W - 1) + k;", "const int64_t s = t + k;"),
+    "conv_skip_dropped": ("double y = acc + (j->Dv ? (double)j->Dv[c] * u : 0.0);",
+                          "double y = acc + (j->Dv ? (double)j->Dv[c] * (j->x64 ? 0.0 : u) : 0.0);"),
 }
 
 

@@ -169,6 +169,20 @@ def cpu_baseline_scan_bwd(inp, cfg, dout):
                       f"({n:.3e} updates in {dt:.2f} s, fp64 forward then reverse recurrence)"}
 
 
+def cpu_baseline_conv_scan(inp, cfg, conv):
+    import oracle
+    threads = oracle.default_threads()
+    w, bias, _ = conv
+    per_ch = cfg.batch * cfg.seqlen * cfg.dstate
+    nc = int(min(cfg.dim, max(1, 4e9 // per_ch)))
+    passes, dt = _timed_passes(lambda: oracle.conv_scan_fwd(inp.x, w, bias, None, inp.delta, inp.A, inp.B, inp.C,
+                                                            inp.D, inp.z, None, c0=0, c1=nc, nthreads=threads))
+    n = per_ch * nc * passes
+    return {"value": n / dt, "unit": "state-updates/s", "cores": threads, "kind": "oracle",
+            "sample": f"channels 0..{nc} of {cfg.dim} (the convolution over all channels), all batches and steps, "
+                      f"{passes} pass(es) ({n:.3e} updates in {dt:.2f} s, fp64)"}
+
+
 def cpu_baseline_ssd(inp, cfg):
     import oracle
     threads = oracle.default_threads()
@@ -188,8 +202,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2,
-                    help="workload id (1-8; 6, 7: decode steps; 8: gradients); 2 is the one the metric is "
-                         "quoted on")
+                    help="workload id (1-9; 6, 7: decode steps; 8: gradients; 9: convolution fused in front); "
+                         "2 is the one the metric is quoted on")
     ap.add_argument("--sets", type=int, default=0, help="resident input copies to rotate over (0: auto)")
     ap.add_argument("--chunk", type=int, default=0, help="SSD time-chunk length (0: the workload's)")
     ap.add_argument("--split-seq", type=int, default=0, help="force the sequence-chunk count (0: the planner's)")
@@ -292,6 +306,25 @@ def main():
             M.ssd_fwd(a["x"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], None, chunk=chunk,
                       out=o, final_state=f, return_final_state=True, workspace=ws if ws_n else None)
         plan = {"chunk": chunk}
+    elif getattr(cfg, "conv_width", 0):
+        # the scan with its short causal convolution fused in front: x is made on chip from its input
+        host = [W.make_scan_inputs(cfg, seed_base=W.ROOT_SEED + 1000 * i) for i in range(sets)]
+        convs = [W.make_conv_inputs(cfg, cfg.conv_width, seed_base=W.ROOT_SEED + 1000 * i, with_init=False)
+                 for i in range(sets)]
+        ins = [dict(x=dev(h.x), delta=dev(h.delta), A=dev(h.A), B=dev(h.B), C=dev(h.C), D=dev(h.D), z=dev(h.z),
+                    w=dev(cw), bias=dev(cb)) for h, (cw, cb, _) in zip(host, convs)]
+        outs = [torch.empty_like(i["x"]) for i in ins]
+        io = M.MSSM_BF16 if cfg.io == W.BF16 else M.MSSM_F32
+        ws_n = M.selective_scan_conv_workspace_size(cfg.batch, cfg.seqlen, cfg.dim, cfg.dstate, io,
+                                                    split_seq=args.split_seq)
+        ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+
+        def step(i):
+            a, o = ins[i % sets], outs[i % sets]
+            M.selective_scan_conv_fwd(a["x"], a["w"], a["bias"], None, a["delta"], a["A"], a["B"], a["C"], a["D"],
+                                      a["z"], None, out=o, split_seq=args.split_seq,
+                                      workspace=ws if ws_n else None)
+        plan = {"conv_width": cfg.conv_width, "split_state": 16}
     else:
         host = [W.make_scan_inputs(cfg, seed_base=W.ROOT_SEED + 1000 * i) for i in range(sets)]
         ins = [dict(x=dev(h.x), delta=dev(h.delta), A=dev(h.A), B=dev(h.B), C=dev(h.C), D=dev(h.D), z=dev(h.z))
@@ -315,6 +348,8 @@ def main():
     del host[1:]
     if backward:
         del douts[1:]
+    if getattr(cfg, "conv_width", 0):
+        del convs[1:]
     torch.cuda.synchronize()
     log(f"inputs ready in {time.perf_counter() - t:.1f}s; plan {plan}")
 
@@ -371,7 +406,11 @@ def main():
         roof["bound"] = bound
         roof["other"] = mf if bound == "hbm" else hbm
     else:
-        slots = cfg.updates * SLOTS_PER_UPDATE + cfg.batch * cfg.seqlen * cfg.dim * SLOTS_PER_STEP_CHANNEL
+        per_tc = SLOTS_PER_STEP_CHANNEL
+        if getattr(cfg, "conv_width", 0):
+            # the fused convolution: one FMA per tap, then its SiLU (mul, exp2 (2), add, rcp (2), mul)
+            per_tc += cfg.conv_width + 7
+        slots = cfg.updates * SLOTS_PER_UPDATE + cfg.batch * cfg.seqlen * cfg.dim * per_tc
         alu = {"achieved": slots / kern_s / 1e12, "peak": PEAK_VALU_TSLOT, "unit": "Tslot/s"}
         alu["frac"] = alu["achieved"] / alu["peak"]
         bound = "alu" if alu["frac"] >= hbm["frac"] else "hbm"
@@ -389,6 +428,8 @@ def main():
         h = host[0]
         if backward:
             cpu = cpu_baseline_scan_bwd(h, cfg, douts[0])
+        elif getattr(cfg, "conv_width", 0):
+            cpu = cpu_baseline_conv_scan(h, cfg, convs[0])
         else:
             cpu = cpu_baseline_ssd(h, cfg) if is_ssd else cpu_baseline_scan(h, cfg)
         if decode:

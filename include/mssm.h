@@ -3,8 +3,9 @@
  *
  * Two forward operations, each with a token-by-token (decode) counterpart
  * that advances a stored state in place (mssm_selective_state_update,
- * mssm_ssd_state_update), and the gradients of the first
- * (mssm_selective_scan_bwd):
+ * mssm_ssd_state_update), the gradients of the first
+ * (mssm_selective_scan_bwd), and the first with its short causal convolution
+ * fused in front (mssm_selective_scan_conv_fwd):
  *
  *  1. mssm_selective_scan_fwd -- the Mamba-1 selective scan.  Defined by the
  *     linear state recurrence h_t = A h_{t-1} + B x_t with readout y_t = C h_t
@@ -168,6 +169,35 @@ int mssm_ssd_state_update(const mssm_ssd_desc* desc, float* state,
                           const void* x, const void* delta, const float* A,
                           const void* B, const void* C, const float* D, const void* z,
                           void* out, void* stream);
+
+/* Selective scan with the short causal convolution + SiLU that precedes it in
+ * the Mamba-1/2 block fused in front ("Mamba-3" blog, "Arquitectura": the
+ * block's short causal convolution on the state input, which Mamba-3 drops).
+ * The scan's x is computed on chip from its input xin and never stored:
+ *   x[b,t,c] = silu(conv_b[c] + sum_{k < W} conv_w[c,k] * xin[b, t-(W-1)+k, c])
+ * with W = conv_width (1..4) and xin at a step s < 0 taken from
+ * conv_init[b, W-1+s, c] (or 0 when conv_init is NULL).  Everything else is
+ * mssm_selective_scan_fwd with that x.
+ *   xin              : [batch, seqlen, dim]        (io_dtype)
+ *   conv_w           : [dim, conv_width] fp32 (tap k multiplies the input k - (W-1) steps away)
+ *   conv_b           : [dim] fp32, nullable
+ *   conv_init        : [batch, conv_width - 1, dim] (io_dtype), nullable: the
+ *                      inputs before t = 0, oldest first (xin's layout)
+ * Supported: dstate 16, dim * sizeof(io) a multiple of 16, every io pointer
+ * (xin, delta, B, C, z, out, conv_init) 16-byte aligned; split_state 0 or
+ * 16 (else MSSM_ERR_UNSUPPORTED / MSSM_ERR_MISALIGNED).  workspace: at least
+ * mssm_selective_scan_conv_workspace_size(desc) bytes.  Same ownership,
+ * stream and error rules as mssm_selective_scan_fwd. */
+int mssm_selective_scan_conv_fwd(const mssm_scan_desc* desc, int32_t conv_width,
+                                 const void* xin, const float* conv_w, const float* conv_b,
+                                 const void* conv_init, const void* delta, const float* A,
+                                 const void* B, const void* C, const float* D, const void* z,
+                                 const float* h0, void* out, float* final_state,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace mssm_selective_scan_conv_fwd needs (0 when the sequence
+ * is not split, or for an invalid or unsupported descriptor). */
+size_t mssm_selective_scan_conv_workspace_size(const mssm_scan_desc* desc);
 
 /* Gradients of mssm_selective_scan_fwd (reverse mode through the same
  * recurrence; training a selective SSM needs them, "P20 - Mamba", 5).  For

@@ -48,6 +48,8 @@ SIGNATURES = {
     "mssm_ssd_workspace_size": (_SZ, [ctypes.POINTER(SSDDesc)]),
     "mssm_selective_state_update": (_I, [ctypes.POINTER(ScanDesc)] + [_P] * 10),
     "mssm_ssd_state_update": (_I, [ctypes.POINTER(SSDDesc)] + [_P] * 10),
+    "mssm_selective_scan_conv_fwd": (_I, [ctypes.POINTER(ScanDesc), ctypes.c_int32] + [_P] * 13 + [_P, _SZ, _P]),
+    "mssm_selective_scan_conv_workspace_size": (_SZ, [ctypes.POINTER(ScanDesc)]),
     "mssm_selective_scan_bwd": (_I, [ctypes.POINTER(ScanDesc)] + [_P] * 18 + [_P, _SZ, _P]),
     "mssm_selective_scan_bwd_workspace_size": (_SZ, [ctypes.POINTER(ScanDesc)]),
     "mssm_status_string": (ctypes.c_char_p, [_I]),
@@ -185,6 +187,59 @@ def selective_scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, return_final_
                                      _stream_handle(stream))
     if st != MSSM_OK:
         raise MssmError(st, "mssm_selective_scan_fwd")
+    return (out, final_state) if return_final_state else out
+
+
+def selective_scan_conv_workspace_size(batch, seqlen, dim, dstate, io_dtype=MSSM_BF16, split_seq=0) -> int:
+    d = scan_desc(batch, seqlen, dim, dstate, io_dtype, split_seq, 16)
+    return lib.mssm_selective_scan_conv_workspace_size(ctypes.byref(d))
+
+
+def selective_scan_conv_fwd(xin, conv_w, conv_b, conv_init, delta, A, B, C, D=None, z=None, h0=None,
+                            return_final_state: bool = False, split_seq: int = 0, out=None, final_state=None,
+                            workspace=None, stream=None):
+    """Selective scan with the short causal convolution + SiLU fused in front
+    (mssm_selective_scan_conv_fwd): x = silu(conv_b + causal_conv(xin, conv_w)).
+
+    xin, delta, z: [batch, seqlen, dim]; B, C: [batch, seqlen, 16]; conv_w [dim, W] float32 (W 1..4);
+    conv_b [dim] float32 or None; conv_init [batch, W-1, dim] in xin's dtype or None.
+    """
+    torch = _torch()
+    if xin.dim() != 3:
+        raise ValueError("xin must be [batch, seqlen, dim]")
+    bsz, L, dm = xin.shape
+    if A.dim() != 2 or A.shape[0] != dm:
+        raise ValueError("A must be [dim, dstate]")
+    if conv_w.dim() != 2 or conv_w.shape[0] != dm:
+        raise ValueError("conv_w must be [dim, width]")
+    N, W = A.shape[1], conv_w.shape[1]
+    io = _io_code(xin.dtype)
+    for name, t, shape in (("xin", xin, (bsz, L, dm)), ("delta", delta, (bsz, L, dm)), ("z", z, (bsz, L, dm)),
+                           ("B", B, (bsz, L, N)), ("C", C, (bsz, L, N)), ("conv_init", conv_init, (bsz, W - 1, dm))):
+        _check_gpu(name, t, xin.dtype, shape)
+    _check_gpu("conv_w", conv_w, torch.float32, (dm, W))
+    _check_gpu("conv_b", conv_b, torch.float32, (dm,))
+    _check_gpu("A", A, torch.float32, (dm, N))
+    _check_gpu("D", D, torch.float32, (dm,))
+    _check_gpu("h0", h0, torch.float32, (bsz, dm, N))
+    if out is None:
+        out = torch.empty_like(xin)
+    _check_gpu("out", out, xin.dtype, (bsz, L, dm))
+    if return_final_state and final_state is None:
+        final_state = torch.empty((bsz, dm, N), dtype=torch.float32, device=xin.device)
+    _check_gpu("final_state", final_state, torch.float32, (bsz, dm, N))
+    d = scan_desc(bsz, L, dm, N, io, split_seq, 16)
+    ws_bytes = lib.mssm_selective_scan_conv_workspace_size(ctypes.byref(d))
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=xin.device)
+    st = lib.mssm_selective_scan_conv_fwd(ctypes.byref(d), W, _ptr(xin), _ptr(conv_w), _ptr(conv_b),
+                                          _ptr(conv_init), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                          _ptr(h0), _ptr(out), _ptr(final_state),
+                                          _ptr(workspace) if ws_bytes else None,
+                                          workspace.numel() if (ws_bytes and workspace is not None) else 0,
+                                          _stream_handle(stream))
+    if st != MSSM_OK:
+        raise MssmError(st, "mssm_selective_scan_conv_fwd")
     return (out, final_state) if return_final_state else out
 
 

@@ -331,6 +331,90 @@ int mssm_ssd_state_update(const mssm_ssd_desc* desc, float* state, const void* x
 }
 
 // --------------------------------------------------------------------------
+// Short causal convolution + SiLU fused in front of the scan
+// --------------------------------------------------------------------------
+namespace {
+// the convolution front end runs in the one-state-per-lane kernel: 16 lanes per channel
+mssm_scan_desc conv_plan_desc(const mssm_scan_desc& d) {
+  mssm_scan_desc c = d;
+  c.split_state = 16;
+  return c;
+}
+}  // namespace
+
+size_t mssm_selective_scan_conv_workspace_size(const mssm_scan_desc* desc) {
+  if (validate_scan_desc(desc) != MSSM_OK || desc->dstate != 16) return 0;
+  if (desc->split_state != 0 && desc->split_state != 16) return 0;
+  const mssm_scan_desc c = conv_plan_desc(*desc);
+  int K = 1, G = 16;
+  if (plan_scan(c, &K, &G) != MSSM_OK) return 0;
+  return mssm::scan_workspace_bytes(c.batch, c.dim, c.dstate, K);
+}
+
+int mssm_selective_scan_conv_fwd(const mssm_scan_desc* desc, int32_t conv_width, const void* xin,
+                                 const float* conv_w, const float* conv_b, const void* conv_init,
+                                 const void* delta, const float* A, const void* B, const void* C, const float* D,
+                                 const void* z, const float* h0, void* out, float* final_state, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  const int v = validate_scan_desc(desc);
+  if (v != MSSM_OK) return v;
+  const mssm_scan_desc& d = *desc;
+  if (conv_width < 1 || conv_width > 4) return MSSM_ERR_UNSUPPORTED;
+  if (d.dstate != 16 || (d.split_state != 0 && d.split_state != 16)) return MSSM_ERR_UNSUPPORTED;
+  const int64_t es = d.io_dtype == MSSM_BF16 ? 2 : 4;
+  if ((d.dim * es) % 16 != 0) return MSSM_ERR_UNSUPPORTED;
+  if (A == nullptr || conv_w == nullptr) return MSSM_ERR_INVALID_ARG;
+  if (d.batch == 0) return MSSM_OK;
+  const int64_t n_bld = d.batch * d.seqlen * d.dim;
+  const int64_t n_bln = d.batch * d.seqlen * d.dstate;
+  if (n_bld > 0 && (xin == nullptr || delta == nullptr || B == nullptr || C == nullptr || out == nullptr))
+    return MSSM_ERR_INVALID_ARG;
+  // the fused kernel moves 16-byte pieces of every io tensor
+  if (!aligned(xin, 16) || !aligned(delta, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(z, 16) ||
+      !aligned(out, 16) || !aligned(conv_init, 16) || !aligned(A, 4) || !aligned(D, 4) || !aligned(h0, 4) ||
+      !aligned(final_state, 4) || !aligned(conv_w, 4) || !aligned(conv_b, 4))
+    return MSSM_ERR_MISALIGNED;
+  const int64_t b_io = n_bld * es, b_bc = n_bln * es;
+  const int64_t b_st = d.batch * d.dim * d.dstate * 4;
+  const int64_t b_init = d.batch * (conv_width - 1) * d.dim * es;
+  const void* ins[] = {xin, delta, B, C, z, A, D, h0, conv_w, conv_b, conv_init};
+  const int64_t inb[] = {b_io, b_io, b_bc, b_bc, b_io, d.dim * d.dstate * 4, d.dim * 4, b_st,
+                         d.dim * conv_width * 4, d.dim * 4, b_init};
+  for (int i = 0; i < 11; ++i) {
+    if (overlap(out, b_io, ins[i], inb[i])) return MSSM_ERR_INVALID_ARG;
+    if (overlap(final_state, b_st, ins[i], inb[i])) return MSSM_ERR_INVALID_ARG;
+  }
+  if (overlap(out, b_io, final_state, b_st)) return MSSM_ERR_INVALID_ARG;
+
+  const mssm_scan_desc c = conv_plan_desc(d);
+  int K = 1, G = 16;
+  const int pr = plan_scan(c, &K, &G);
+  if (pr != MSSM_OK) return pr;
+  const size_t need = mssm::scan_workspace_bytes(d.batch, d.dim, d.dstate, K);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need) return MSSM_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return MSSM_ERR_MISALIGNED;
+    if (overlap(workspace, static_cast<int64_t>(need), out, b_io) ||
+        overlap(workspace, static_cast<int64_t>(need), final_state, b_st))
+      return MSSM_ERR_INVALID_ARG;
+  }
+  if (n_bld == 0 && final_state == nullptr) return MSSM_OK;
+
+  mssm::ScanArgs a{};
+  a.x = xin; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.h0 = h0;
+  a.out = out; a.final_state = final_state; a.workspace = workspace;
+  a.batch = d.batch; a.L = d.seqlen; a.dim = d.dim; a.N = d.dstate;
+  a.io = d.io_dtype; a.K = K; a.G = G;
+  a.conv_w = conv_w; a.conv_b = conv_b; a.conv_init = conv_init; a.conv_width = conv_width;
+  const hipError_t e = mssm::scan_launch(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    set_err(e);
+    return MSSM_ERR_HIP;
+  }
+  return MSSM_OK;
+}
+
+// --------------------------------------------------------------------------
 // Gradients of the Mamba-1 selective scan
 // --------------------------------------------------------------------------
 size_t mssm_selective_scan_bwd_workspace_size(const mssm_scan_desc* desc) {

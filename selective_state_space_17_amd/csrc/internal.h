@@ -26,7 +26,14 @@ struct ScanArgs {
   int io;               // 0 fp32, 1 bf16
   int K;                // sequence chunks
   int G;                // lanes per channel
+  // optional short causal convolution + SiLU in front of the scan; x is then
+  // its input (needs G == 16, N == 16 and 16-byte aligned I/O)
+  const float* conv_w = nullptr;     // [dim, conv_width]
+  const float* conv_b = nullptr;     // [dim], nullable
+  const void* conv_init = nullptr;   // [batch, conv_width - 1, dim], nullable
+  int conv_width = 0;
 };
+
 
 // Workspace layout for K > 1 (all fp32 / int32, 256-byte aligned blocks):
 //   hend [batch][K][dim][N]  state at each chunk's end (chunk 0: true; others: from zero)

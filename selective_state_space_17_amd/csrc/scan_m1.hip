@@ -132,6 +132,12 @@ struct KernelParams {
   int ngroups;          // channel groups (blocks) per (batch, chunk)
   int chunk_offset;     // fix-up pass starts at chunk 1
   int bc_shift;         // log2(N / elements-per-16-bytes) for 16-byte B/C loads
+  // short causal convolution in front of the scan (wide kernel, CONV = true):
+  // x above is then the convolution's input
+  const float* conv_w;     // [dim, conv_width]
+  const float* conv_b;     // [dim], nullable
+  const void* conv_init;   // [batch, conv_width - 1, dim] (io dtype), nullable
+  int conv_width;          // 1..4
 };
 
 // Readout for the fast path: a0 + a1 = sum_j C_j * h_j with C_j taken from the
@@ -685,7 +691,7 @@ __device__ __forceinline__ float row_sum(float v) {
   return v;
 }
 
-template <int IO, int MODE>
+template <int IO, int MODE, bool CONV>
 __global__ __launch_bounds__(kThreads) void wide_kernel(KernelParams p) {
   using namespace wide;
   using T = typename IoType<IO>::T;
@@ -754,11 +760,46 @@ __global__ __launch_bounds__(kThreads) void wide_kernel(KernelParams p) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) Dreg[q] = p.D != nullptr ? p.D[sc + q] : 0.f;
 
+  // Short causal convolution (CONV): the staging thread's 4 channels need the
+  // input at steps t-3 .. t.  Taps are right-aligned into 4 slots (slot 3 =
+  // step t), so a narrower kernel has leading zero taps; the block's taps and
+  // biases sit in LDS.  Steps before 0 come from conv_init (or are 0).
+  __shared__ float4 Wl[CONV ? CPB : 1];   // taps of the block's channels
+  __shared__ float Bl[CONV ? CPB : 1];    // biases
+  Chunk xh[3];            // input at t-1, t-2, t-3
+  bool hvalid[3];
+  if constexpr (CONV) {
+    if (tid < CPB) {
+      const int W = p.conv_width;
+      const int64_t cc = c0 + tid;
+      float tap[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) tap[k] = (cc < dim && k >= 4 - W) ? p.conv_w[cc * W + (k - (4 - W))] : 0.f;
+      Wl[tid] = float4{tap[0], tap[1], tap[2], tap[3]};
+      Bl[tid] = (cc < dim && p.conv_b != nullptr) ? p.conv_b[cc] : 0.f;
+    }
+    __syncthreads();
+  }
+
   Chunk xr, dr, zr, br, cr;
   auto issue_loads = [&](int64_t t0) {
     const int nvalid = static_cast<int>((t_end - t0) < TT ? (t_end - t0) : TT);
     const int rr = ts < nvalid ? ts : nvalid - 1;
     const int64_t row_t = b * L + t0 + rr;
+    if constexpr (CONV) {
+      const T* ig = static_cast<const T*>(p.conv_init);
+      const int W = p.conv_width;
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        const int64_t tt = t0 + rr - (j + 1);
+        const bool from_init = tt < 0 && ig != nullptr && (W - 1) + tt >= 0;
+        hvalid[j] = tt >= 0 || from_init;
+        // always an in-range address; the value is masked at staging when not valid
+        const T* src = tt >= 0 ? xg + (row_t - (j + 1)) * dim + sc
+                               : (from_init ? ig + (b * (W - 1) + (W - 1) + tt) * dim + sc : xg + b * L * dim + sc);
+        xh[j] = *reinterpret_cast<const Chunk*>(src);
+      }
+    }
     xr = *reinterpret_cast<const Chunk*>(xg + row_t * dim + sc);
     dr = *reinterpret_cast<const Chunk*>(dg + row_t * dim + sc);
     zr = *reinterpret_cast<const Chunk*>(zg + row_t * dim + sc);
@@ -769,6 +810,27 @@ __global__ __launch_bounds__(kThreads) void wide_kernel(KernelParams p) {
   auto stage = [&](int64_t t0) {
     const int nvalid = static_cast<int>((t_end - t0) < TT ? (t_end - t0) : TT);
     asm volatile("" : "+v"(xr), "+v"(dr), "+v"(zr), "+v"(br), "+v"(cr));
+    float ux[4];   // the scan's x of the 4 channels at this step
+    if constexpr (CONV) {
+      asm volatile("" : "+v"(xh[0]), "+v"(xh[1]), "+v"(xh[2]));
+      const T* x0 = reinterpret_cast<const T*>(&xr);
+      const T* x1 = reinterpret_cast<const T*>(&xh[0]);
+      const T* x2 = reinterpret_cast<const T*>(&xh[1]);
+      const T* x3 = reinterpret_cast<const T*>(&xh[2]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 w = Wl[4 * q4 + q];
+        float a = __builtin_fmaf(w.w, to_f32(x0[q]), Bl[4 * q4 + q]);
+        a = __builtin_fmaf(w.z, hvalid[0] ? to_f32(x1[q]) : 0.f, a);
+        a = __builtin_fmaf(w.y, hvalid[1] ? to_f32(x2[q]) : 0.f, a);
+        a = __builtin_fmaf(w.x, hvalid[2] ? to_f32(x3[q]) : 0.f, a);
+        ux[q] = silu_gate(a);
+      }
+    } else {
+      const T* xv0 = reinterpret_cast<const T*>(&xr);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ux[q] = to_f32(xv0[q]);
+    }
     const T* xv = reinterpret_cast<const T*>(&xr);
     const T* dv = reinterpret_cast<const T*>(&dr);
     const T* zv = reinterpret_cast<const T*>(&zr);
@@ -778,7 +840,7 @@ __global__ __launch_bounds__(kThreads) void wide_kernel(KernelParams p) {
     const float keep = ts < nvalid ? 1.f : 0.f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const float d = to_f32(dv[q]), u = to_f32(xv[q]);
+      const float d = to_f32(dv[q]), u = ux[q];
       const float gz = has_z ? silu_gate(to_f32(zv[q])) : 1.f;
       float4 v = float4{d, d * u, gz, gz * (Dreg[q] * u)};
       if (nvalid < TT) v = float4{v.x * keep, v.y * keep, v.z * keep, v.w * keep};
@@ -962,17 +1024,17 @@ hipError_t launch_cfg(const KernelParams& kp, int64_t batch, hipStream_t stream)
 }
 
 // the same three launches for the one-state-per-lane kernel
-template <int IO>
+template <int IO, bool CONV>
 hipError_t launch_wide(const KernelParams& kp, int64_t batch, hipStream_t stream) {
   const dim3 block(kThreads);
   if (kp.K == 1) {
     const dim3 grid(static_cast<unsigned>(batch * kp.ngroups));
-    hipLaunchKernelGGL((wide_kernel<IO, kSingle>), grid, block, 0, stream, kp);
+    hipLaunchKernelGGL((wide_kernel<IO, kSingle, CONV>), grid, block, 0, stream, kp);
     return hipGetLastError();
   }
   {
     const dim3 grid(static_cast<unsigned>(batch * kp.K * kp.ngroups));
-    hipLaunchKernelGGL((wide_kernel<IO, kChunk>), grid, block, 0, stream, kp);
+    hipLaunchKernelGGL((wide_kernel<IO, kChunk, CONV>), grid, block, 0, stream, kp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -987,7 +1049,7 @@ hipError_t launch_wide(const KernelParams& kp, int64_t batch, hipStream_t stream
     KernelParams kf = kp;
     kf.chunk_offset = 1;
     const dim3 grid(static_cast<unsigned>(batch * (kp.K - 1) * kp.ngroups));
-    hipLaunchKernelGGL((wide_kernel<IO, kFixup>), grid, block, 0, stream, kf);
+    hipLaunchKernelGGL((wide_kernel<IO, kFixup, CONV>), grid, block, 0, stream, kf);
     return hipGetLastError();
   }
 }
@@ -1011,7 +1073,11 @@ hipError_t launch_generic(const KernelParams& kp, int npl, bool vec, int64_t bat
 
 template <int IO>
 hipError_t launch_io(const KernelParams& kp, int G, int npl, bool vec, int64_t batch, hipStream_t stream) {
-  if (G == 16 && kp.N == 16 && vec) return launch_wide<IO>(kp, batch, stream);
+  if (kp.conv_w != nullptr) {   // the convolution front end exists in the one-state-per-lane kernel only
+    if (G == 16 && kp.N == 16 && vec) return launch_wide<IO, true>(kp, batch, stream);
+    return hipErrorInvalidValue;
+  }
+  if (G == 16 && kp.N == 16 && vec) return launch_wide<IO, false>(kp, batch, stream);
   if (kp.N <= 16) {
     switch (G) {
       case 1: return launch_vec<IO, 1, 16, true>(kp, vec, batch, stream);
@@ -1052,6 +1118,7 @@ hipError_t scan_launch(const ScanArgs& a, hipStream_t stream) {
   KernelParams kp{};
   kp.x = a.x; kp.delta = a.delta; kp.A = a.A; kp.B = a.B; kp.C = a.C; kp.D = a.D; kp.z = a.z; kp.h0 = a.h0;
   kp.out = a.out; kp.final_state = a.final_state;
+  kp.conv_w = a.conv_w; kp.conv_b = a.conv_b; kp.conv_init = a.conv_init; kp.conv_width = a.conv_width;
   kp.batch = a.batch; kp.L = a.L; kp.dim = a.dim; kp.N = a.N;
   kp.K = a.K;
   kp.chunk_len = (a.L + a.K - 1) / a.K;
@@ -1077,7 +1144,7 @@ hipError_t scan_launch(const ScanArgs& a, hipStream_t stream) {
   kp.bc_shift = 0;
   while (bc_pow2 && (int64_t{1} << kp.bc_shift) < bc_chunks) ++kp.bc_shift;
   const bool vec = (a.dim * es) % 16 == 0 && bc_pow2 && al16(a.x) && al16(a.delta) && al16(a.z) &&
-                   al16(a.B) && al16(a.C) && al16(a.out);
+                   al16(a.B) && al16(a.C) && al16(a.out) && al16(a.conv_init);
   if (a.io == 1) return launch_io<1>(kp, G, npl, vec, a.batch, stream);
   return launch_io<0>(kp, G, npl, vec, a.batch, stream);
 }

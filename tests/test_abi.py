@@ -328,3 +328,67 @@ def test_scan_bwd_workspace_size():
     want = al(4 * 2 * 4 * 32 * 16) + 2 * al(4 * 2 * 2 * 64 * 16) + al(4 * 2 * 32 * 16) + al(4 * 2 * 32)
     assert M.lib.mssm_selective_scan_bwd_workspace_size(ctypes.byref(d)) == want
     assert M.lib.mssm_selective_scan_bwd_workspace_size(ctypes.byref(small(dstate=17, split_state=0))) == 0
+
+
+def _conv_call(desc, width=4, ws=None, ws_bytes=0, **kw):
+    a = dict(xin=BASE, w=BASE + 100 * MB, bias=None, init=None, delta=BASE + 200 * MB, A=BASE + 300 * MB,
+             B=BASE + 400 * MB, C=BASE + 500 * MB, D=None, z=None, h0=None, out=BASE + 600 * MB, final=None)
+    a.update(kw)
+    return M.lib.mssm_selective_scan_conv_fwd(ctypes.byref(desc) if desc is not None else None, width, a["xin"],
+                                              a["w"], a["bias"], a["init"], a["delta"], a["A"], a["B"], a["C"],
+                                              a["D"], a["z"], a["h0"], a["out"], a["final"], ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("null_desc", M.MSSM_ERR_INVALID_ARG),
+    ("width0", M.MSSM_ERR_UNSUPPORTED),
+    ("width5", M.MSSM_ERR_UNSUPPORTED),
+    ("dstate8", M.MSSM_ERR_UNSUPPORTED),
+    ("split_state4", M.MSSM_ERR_UNSUPPORTED),
+    ("dim_not_16_bytes", M.MSSM_ERR_UNSUPPORTED),
+    ("null_taps", M.MSSM_ERR_INVALID_ARG),
+    ("null_xin", M.MSSM_ERR_INVALID_ARG),
+    ("xin_not_16_aligned", M.MSSM_ERR_MISALIGNED),
+    ("init_not_16_aligned", M.MSSM_ERR_MISALIGNED),
+    ("out_aliases_init", M.MSSM_ERR_INVALID_ARG),
+    ("out_aliases_taps", M.MSSM_ERR_INVALID_ARG),
+])
+def test_conv_validation(case, expect):
+    d = small(split_state=0)
+    kw = {}
+    width = 4
+    if case == "null_desc":
+        d = None
+    elif case == "width0":
+        width = 0
+    elif case == "width5":
+        width = 5
+    elif case == "dstate8":
+        d = small(dstate=8, split_state=0)
+    elif case == "split_state4":
+        d = small(split_state=4)
+    elif case == "dim_not_16_bytes":
+        d = small(dim=36, split_state=0)
+    elif case == "null_taps":
+        kw["w"] = None
+    elif case == "null_xin":
+        kw["xin"] = None
+    elif case == "xin_not_16_aligned":
+        kw["xin"] = BASE + 8
+    elif case == "init_not_16_aligned":
+        kw["init"] = BASE + 700 * MB + 8
+    elif case == "out_aliases_init":
+        kw["init"] = BASE + 600 * MB + 64
+    elif case == "out_aliases_taps":
+        kw["w"] = BASE + 600 * MB + 64
+    assert _conv_call(d, width, **kw) == expect
+
+
+def test_conv_workspace_size():
+    # the convolution path plans with 16 lanes per channel; a single chunk needs no workspace
+    d = small(split_seq=1, split_state=0)
+    assert M.lib.mssm_selective_scan_conv_workspace_size(ctypes.byref(d)) == 0
+    d = M.scan_desc(1, 4096, 64, 16, M.MSSM_BF16, 4, 16)
+    assert M.lib.mssm_selective_scan_conv_workspace_size(ctypes.byref(d)) == \
+        M.lib.mssm_selective_scan_workspace_size(ctypes.byref(d)) > 0
+    assert M.lib.mssm_selective_scan_conv_workspace_size(ctypes.byref(small(dstate=8, split_state=0))) == 0

@@ -1,0 +1,91 @@
+"""The scan with its short causal convolution + SiLU fused in front, on the GPU through the C ABI,
+against the fp64 oracle (oracle.conv_scan_fwd: the convolution, then the scan of its output).
+
+Cases cover every width 1..4, with and without bias and initial inputs, fp32 and bf16, sequences
+shorter than the convolution, sequence splits (the convolution's history then crosses chunk
+boundaries) and the full 8 x 2048 x 1536 layer."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_util import RTOL, check, dev, host64, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def M():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import selective_state_space_17_amd as m
+    return m
+
+
+def run(M, cfg, width, with_bias, with_init, with_h0, split_seq=0, c_range=None):
+    import torch
+    inp = W.make_scan_inputs(cfg, with_h0=with_h0)
+    w, bias, init = W.make_conv_inputs(cfg, width, with_bias=with_bias, with_init=with_init)
+    out, fin = M.selective_scan_conv_fwd(dev(inp.x), dev(w), dev(bias), dev(init), dev(inp.delta), dev(inp.A),
+                                         dev(inp.B), dev(inp.C), dev(inp.D), dev(inp.z), dev(inp.h0),
+                                         return_final_state=True, split_seq=split_seq)
+    torch.cuda.synchronize()
+    c0, c1 = c_range if c_range else (0, cfg.dim)
+    ref, ref_fin = oracle.conv_scan_fwd(inp.x, w, bias, init, inp.delta, inp.A, inp.B, inp.C, inp.D, inp.z, inp.h0,
+                                        c0=c0, c1=c1)
+    return host64(out)[:, :, c0:c1], host64(fin)[:, c0:c1], ref, ref_fin
+
+
+# (batch, seqlen, dim, width, io, bias, init, D, z, h0, split_seq)
+CASES = [
+    (2, 100, 32, 4, "f32", True, True, True, True, True, 0),
+    (1, 64, 16, 1, "f32", False, False, True, False, False, 0),
+    (2, 200, 48, 2, "bf16", True, False, True, True, False, 0),
+    (3, 77, 64, 3, "bf16", True, True, False, True, True, 0),
+    (2, 3, 16, 4, "f32", True, True, True, True, True, 0),          # shorter than the convolution
+    (1, 1000, 32, 4, "bf16", True, True, True, True, True, 4),      # history crosses chunk boundaries
+    (2, 777, 40, 3, "f32", True, True, True, True, False, 3),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "b{}_l{}_d{}_w{}_{}_k{}".format(*c[:5], c[10]))
+def test_conv_scan_matches_oracle(M, case):
+    b, l, d, width, io, hb, hi, hd, hz, h0, k = case
+    cfg = W.scan_config(b, l, d, 16, io=io, has_D=hd, has_z=hz, cfg_id=900 + l + width)
+    say("conv scan", case)
+    out, fin, ref, ref_fin = run(M, cfg, width, hb, hi, h0, split_seq=k)
+    check(out, ref, RTOL[io], f"conv scan {case} out")
+    check(fin, ref_fin, RTOL[io], f"conv scan {case} final")
+
+
+def test_conv_width1_unit_tap_is_silu_of_input(M):
+    """Width 1, tap 1, no bias: the scan sees silu(xin); compare with the plain scan kernel on that x."""
+    import torch
+    cfg = W.scan_config(2, 130, 32, 16, io="f32", cfg_id=950)
+    inp = W.make_scan_inputs(cfg, with_h0=True)
+    w = np.ones((32, 1), np.float32)
+    out = M.selective_scan_conv_fwd(dev(inp.x), dev(w), None, None, dev(inp.delta), dev(inp.A), dev(inp.B),
+                                    dev(inp.C), dev(inp.D), dev(inp.z), dev(inp.h0))
+    xs = torch.nn.functional.silu(dev(inp.x))
+    ref = M.selective_scan_fwd(xs, dev(inp.delta), dev(inp.A), dev(inp.B), dev(inp.C), dev(inp.D), dev(inp.z),
+                               dev(inp.h0), split_state=16)
+    torch.cuda.synchronize()
+    check(host64(out), host64(ref), 1e-5, "width-1 convolution vs scan of silu(x)")
+
+
+def test_conv_rejects_unsupported(M):
+    cfg = W.scan_config(1, 8, 16, 8, io="f32", cfg_id=951)
+    inp = W.make_scan_inputs(cfg)
+    w = np.ones((16, 2), np.float32)
+    with pytest.raises(M.MssmError, match="UNSUPPORTED|unsupported"):
+        M.selective_scan_conv_fwd(dev(inp.x), dev(w), None, None, dev(inp.delta), dev(inp.A), dev(inp.B),
+                                  dev(inp.C))
+
+
+def test_conv_scan_full_layer(M):
+    """The 8 x 2048 x 1536 bf16 layer with a width-4 convolution, as the bench times it; every element."""
+    cfg = W.CONFIGS[9]
+    say("conv scan full layer", cfg.name)
+    out, fin, ref, ref_fin = run(M, cfg, cfg.conv_width, True, False, False)
+    check(out, ref, RTOL[cfg.io], cfg.name)

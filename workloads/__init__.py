@@ -37,7 +37,7 @@ ROOT_SEED = 1700
 BLOCK = 1 << 22
 
 # tensor ids (fixed order of the per-tensor streams)
-T_X, T_DELTA, T_Z, T_B, T_C, T_D, T_A, T_H0, T_DOUT, T_DFIN = range(10)
+T_X, T_DELTA, T_Z, T_B, T_C, T_D, T_A, T_H0, T_DOUT, T_DFIN, T_CW, T_CB, T_CI = range(13)
 
 F32 = "f32"
 BF16 = "bf16"
@@ -59,6 +59,7 @@ class ScanConfig:
     return_final: bool = True
     decode: bool = False    # token-by-token update of a stored state (read and written in place)
     backward: bool = False  # gradients: dout in, dx/ddelta/dz (io) and dB/dC/dA/dD (fp32) out
+    conv_width: int = 0     # > 0: a short causal convolution + SiLU of this width makes x from its input
 
     @property
     def updates(self) -> int:
@@ -82,6 +83,7 @@ class ScanConfig:
         n += bln * e * 2                    # B, C
         n += self.dim * self.dstate * 4     # A (fp32)
         n += self.dim * 4 if self.has_D else 0
+        n += self.dim * (self.conv_width + 1) * 4 if self.conv_width else 0   # taps and bias
         n += bld * e                        # out
         n += self.batch * self.dim * self.dstate * 4 if self.return_final else 0
         n += self.batch * self.dim * self.dstate * 4 if self.decode else 0
@@ -136,6 +138,9 @@ CONFIGS = {
     # gradients of config 2's layer (one backward pass; no final-state gradient)
     8: ScanConfig("mamba1_130m_layer_bwd_bf16", 8, 8, 2048, 1536, 16, BF16, "exp_log", return_final=False,
                   backward=True),
+    # config 2's layer with its width-4 short causal convolution + SiLU fused in front (x from its input)
+    9: ScanConfig("mamba1_130m_layer_conv_bf16", 9, 8, 2048, 1536, 16, BF16, "exp_log", return_final=False,
+                  conv_width=4),
     # decode steps (one new token against a stored state), the configs' layer shapes at serving batch sizes
     6: ScanConfig("mamba1_2p8b_decode_bf16", 6, 256, 1, 5120, 16, BF16, "s4d_real", return_final=True, decode=True),
     7: SSDConfig("mamba2_decode_bf16", 7, 64, 1, 32, 64, 128, 1, 64, BF16, True, True, True, decode=True),
@@ -281,6 +286,20 @@ def make_scan_grads(cfg: ScanConfig, seed_base: int = ROOT_SEED, with_dfinal: bo
     dout = normal(cfg.cfg_id, T_DOUT, b * l * d, cfg.io, seed_base).reshape(b, l, d)
     dfin = normal_f32(cfg.cfg_id, T_DFIN, b * d * n, seed_base).reshape(b, d, n) if with_dfinal else None
     return dout, dfin
+
+
+def make_conv_inputs(cfg: ScanConfig, width: int, seed_base: int = ROOT_SEED, with_bias: bool = True,
+                     with_init: bool = True):
+    """Short-convolution parameters: taps [D, W] ~ U(-1, 1) / sqrt(W) fp32, bias [D] ~ N(0, 1) / 4 fp32,
+    init [B, W-1, D] ~ N(0, 1) in io dtype (the inputs before t = 0)."""
+    b, d = cfg.batch, cfg.dim
+    w = uniform_f32(cfg.cfg_id, T_CW, d * width, -1.0, 1.0, seed_base).reshape(d, width)
+    w = (w / np.float32(np.sqrt(width))).astype(np.float32)
+    bias = (normal_f32(cfg.cfg_id, T_CB, d, seed_base) * np.float32(0.25)).astype(np.float32) if with_bias else None
+    init = None
+    if with_init and width > 1:
+        init = normal(cfg.cfg_id, T_CI, b * (width - 1) * d, cfg.io, seed_base).reshape(b, width - 1, d)
+    return w, bias, init
 
 
 @dataclasses.dataclass

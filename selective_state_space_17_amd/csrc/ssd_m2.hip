@@ -172,9 +172,13 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
   const int Ni = static_cast<int>(N);
   const int cpr = Ni / 8;             // 16-byte chunks per B/C row in memory
 
-  // B/C columns past N stay zero; so do the mask tiles above the diagonal
-  // (read as part of 32-wide k blocks, never computed)
+  // B/C columns past N stay zero, and so do the rows of B^T past N (they feed
+  // state rows past N, which the readout multiplies by C's zero columns: left
+  // as whatever the LDS held, a NaN there would survive that product); so do
+  // the mask tiles above the diagonal (read as part of 32-wide k blocks, never
+  // computed)
   for (int e = tid; e < QB * NS; e += kThreads) { Cs[e] = 0; Bs[e] = 0; }
+  for (int e = tid; e < (NP - Ni) * QS; e += kThreads) BT[Ni * QS + e] = 0;
   for (int e = tid; e < 2 * QB * QS; e += kThreads) (&Ms[0][0])[e] = 0;
   __syncthreads();   // before any staging write lands on a zeroed element
 

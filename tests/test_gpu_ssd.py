@@ -114,3 +114,18 @@ def test_config4_sampled_heads(M):
         st = check(host64(out[:, :, hd0:hd1].contiguous()), ref, RTOL["bf16"], f"config4 heads {hd0}:{hd1}")
         check(host64(fin[:, hd0:hd1].contiguous()), ref_fin, RTOL["bf16"], f"config4 final {hd0}:{hd1}")
         say("config4", hd0, hd1, st)
+
+
+def test_ssd_padded_states_ignore_stale_lds(M):
+    """dstate 48 (padded to 64 inside): state rows past dstate must not pick up whatever an earlier
+    kernel left in LDS.  A forward scan over NaN inputs first leaves NaNs in the LDS of every CU."""
+    import torch
+    big = W.scan_config(8, 512, 1536, 16, io="bf16", cfg_id=610)
+    poison = W.make_scan_inputs(big)
+    nan_x = torch.full((8, 512, 1536), float("nan"), dtype=torch.bfloat16, device="cuda")
+    M.selective_scan_fwd(nan_x, dev(poison.delta), dev(poison.A), dev(poison.B), dev(poison.C), dev(poison.D),
+                         dev(poison.z), split_state=16)
+    torch.cuda.synchronize()
+    cfg = W.ssd_config(2, 1000, 4, 64, 48, 1, cfg_id=611)
+    s = W.make_ssd_inputs(cfg, with_D=True, with_z=True, with_h0=True)
+    compare(M, s, "ssd dstate 48 after NaN in LDS")

@@ -53,46 +53,57 @@ __device__ __forceinline__ float group_sum(float v, int lpr) {
   return v;
 }
 
-// 4 states n0..n0+3 of a row (entries past N read as 0 and are not written)
-template <bool VEC>
-__device__ __forceinline__ void load4(const float* p, int n0, int N, float (&v)[4]) {
-  if constexpr (VEC) {   // N % 4 == 0: a group is wholly inside or wholly past the row
-    const float4 t = n0 < N ? *reinterpret_cast<const float4*>(p + n0) : float4{0.f, 0.f, 0.f, 0.f};
-    v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
-  } else {
+// S (4 or 8) states n0..n0+S-1 of a row (entries past N read as 0 and are not written)
+template <int S, bool VEC>
+__device__ __forceinline__ void loadS(const float* p, int n0, int N, float (&v)[S]) {
+  if constexpr (VEC) {   // N % S == 0: a group is wholly inside or wholly past the row
 #pragma unroll
-    for (int q = 0; q < 4; ++q) v[q] = n0 + q < N ? p[n0 + q] : 0.f;
-  }
-}
-template <bool VEC>
-__device__ __forceinline__ void store4(float* p, int n0, int N, const float (&v)[4]) {
-  if constexpr (VEC) {
-    if (n0 < N) *reinterpret_cast<float4*>(p + n0) = float4{v[0], v[1], v[2], v[3]};
-  } else {
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (n0 + q < N) p[n0 + q] = v[q];
-  }
-}
-// 4 consecutive B or C values (one 8- or 16-byte load when N % 4 == 0)
-template <typename T, bool VEC>
-__device__ __forceinline__ void load4io(const T* p, int n0, int N, float (&v)[4]) {
-  if constexpr (VEC) {
-    if (n0 < N) {
-      if constexpr (sizeof(T) == 2) {
-        const uint2 w = *reinterpret_cast<const uint2*>(p + n0);
-        v[0] = __uint_as_float(w.x << 16); v[1] = __uint_as_float(w.x & 0xffff0000u);
-        v[2] = __uint_as_float(w.y << 16); v[3] = __uint_as_float(w.y & 0xffff0000u);
-      } else {
-        const float4 w = *reinterpret_cast<const float4*>(p + n0);
-        v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
-      }
-    } else {
-      v[0] = v[1] = v[2] = v[3] = 0.f;
+    for (int i = 0; i < S / 4; ++i) {
+      const float4 t = n0 < N ? *reinterpret_cast<const float4*>(p + n0 + 4 * i) : float4{0.f, 0.f, 0.f, 0.f};
+      v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
     }
   } else {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) v[q] = n0 + q < N ? to_f32(p[n0 + q]) : 0.f;
+    for (int q = 0; q < S; ++q) v[q] = n0 + q < N ? p[n0 + q] : 0.f;
+  }
+}
+template <int S, bool VEC>
+__device__ __forceinline__ void storeS(float* p, int n0, int N, const float (&v)[S]) {
+  if constexpr (VEC) {
+    if (n0 < N) {
+#pragma unroll
+      for (int i = 0; i < S / 4; ++i)
+        *reinterpret_cast<float4*>(p + n0 + 4 * i) = float4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < S; ++q)
+      if (n0 + q < N) p[n0 + q] = v[q];
+  }
+}
+// S consecutive B or C values (8- or 16-byte loads when N % S == 0)
+template <typename T, int S, bool VEC>
+__device__ __forceinline__ void loadSio(const T* p, int n0, int N, float (&v)[S]) {
+  if constexpr (VEC) {
+    if (n0 < N) {
+#pragma unroll
+      for (int i = 0; i < S / 4; ++i) {
+        if constexpr (sizeof(T) == 2) {
+          const uint2 w = *reinterpret_cast<const uint2*>(p + n0 + 4 * i);
+          v[4 * i] = __uint_as_float(w.x << 16); v[4 * i + 1] = __uint_as_float(w.x & 0xffff0000u);
+          v[4 * i + 2] = __uint_as_float(w.y << 16); v[4 * i + 3] = __uint_as_float(w.y & 0xffff0000u);
+        } else {
+          const float4 w = *reinterpret_cast<const float4*>(p + n0 + 4 * i);
+          v[4 * i] = w.x; v[4 * i + 1] = w.y; v[4 * i + 2] = w.z; v[4 * i + 3] = w.w;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < S; ++q) v[q] = 0.f;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < S; ++q) v[q] = n0 + q < N ? to_f32(p[n0 + q]) : 0.f;
   }
 }
 
@@ -113,18 +124,19 @@ struct UpdParams {
   int lpr;                 // lanes per row
 };
 
-// Each thread owns 4 states in each of R rows spaced a grid-width of rows
-// apart (so every pass over r is one coalesced sweep).  One row per thread
-// measured fastest: it keeps registers low enough for 8 waves per SIMD.
+// Each thread owns S states (4, or 8 when dstate allows: two 16-byte loads
+// in flight per lane) in each of R rows spaced a grid-width of rows apart (so
+// every pass over r is one coalesced sweep).  One row per thread measured
+// fastest: it keeps registers low enough for 8 waves per SIMD.
 constexpr int R = 1;
 
 // Mamba-1: row = (b, c), state [batch, dim, N]
-template <typename T, bool VEC>
+template <typename T, bool VEC, int S>
 __global__ __launch_bounds__(kThreads) void scan_update_kernel(UpdParams p) {
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
   const int64_t row0 = gid / p.lpr;
   const int64_t rstride = static_cast<int64_t>(gridDim.x) * kThreads / p.lpr;
-  const int n0 = 4 * static_cast<int>(gid % p.lpr);
+  const int n0 = S * static_cast<int>(gid % p.lpr);
   const int N = static_cast<int>(p.N);
   const int64_t L = p.L, dim = p.dim;
   const T* x = static_cast<const T*>(p.x);
@@ -136,7 +148,7 @@ __global__ __launch_bounds__(kThreads) void scan_update_kernel(UpdParams p) {
 
   bool live[R];
   int64_t rr[R], bb[R], cc[R];
-  float h[R][4], a2[R][4], Dc[R];
+  float h[R][S], a2[R][S], Dc[R];
 #pragma unroll
   for (int k = 0; k < R; ++k) {
     const int64_t row = row0 + k * rstride;
@@ -144,27 +156,27 @@ __global__ __launch_bounds__(kThreads) void scan_update_kernel(UpdParams p) {
     rr[k] = live[k] ? row : 0;
     bb[k] = rr[k] / dim;
     cc[k] = rr[k] % dim;
-    load4<VEC>(p.state + rr[k] * N, n0, N, h[k]);
-    load4<VEC>(p.A + cc[k] * N, n0, N, a2[k]);
+    loadS<S, VEC>(p.state + rr[k] * N, n0, N, h[k]);
+    loadS<S, VEC>(p.A + cc[k] * N, n0, N, a2[k]);
     Dc[k] = p.D != nullptr ? p.D[cc[k]] : 0.f;
   }
   for (int64_t t = 0; t < L; ++t) {
-    float d[R], u[R], zz[R], bv[R][4], cv[R][4];
+    float d[R], u[R], zz[R], bv[R][S], cv[R][S];
 #pragma unroll
     for (int k = 0; k < R; ++k) {
       const int64_t o = (bb[k] * L + t) * dim + cc[k];
       d[k] = to_f32(delta[o]);
       u[k] = to_f32(x[o]);
       zz[k] = z != nullptr ? to_f32(z[o]) : 0.f;
-      load4io<T, VEC>(Bm + (bb[k] * L + t) * N, n0, N, bv[k]);
-      load4io<T, VEC>(Cm + (bb[k] * L + t) * N, n0, N, cv[k]);
+      loadSio<T, S, VEC>(Bm + (bb[k] * L + t) * N, n0, N, bv[k]);
+      loadSio<T, S, VEC>(Cm + (bb[k] * L + t) * N, n0, N, cv[k]);
     }
 #pragma unroll
     for (int k = 0; k < R; ++k) {
       const float du = d[k] * u[k];
       float acc = 0.f;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < S; ++q) {
         h[k][q] = __builtin_fmaf(exp2_hw(d[k] * a2[k][q] * kLog2e), h[k][q], du * bv[k][q]);
         acc = __builtin_fmaf(cv[k][q], h[k][q], acc);
       }
@@ -178,16 +190,16 @@ __global__ __launch_bounds__(kThreads) void scan_update_kernel(UpdParams p) {
   }
 #pragma unroll
   for (int k = 0; k < R; ++k)
-    if (live[k]) store4<VEC>(p.state + rr[k] * N, n0, N, h[k]);
+    if (live[k]) storeS<S, VEC>(p.state + rr[k] * N, n0, N, h[k]);
 }
 
 // multi-head form: row = (b, h, p), state [batch, H, P, N]
-template <typename T, bool VEC>
+template <typename T, bool VEC, int S>
 __global__ __launch_bounds__(kThreads) void ssd_update_kernel(UpdParams p) {
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
   const int64_t row0 = gid / p.lpr;
   const int64_t rstride = static_cast<int64_t>(gridDim.x) * kThreads / p.lpr;
-  const int n0 = 4 * static_cast<int>(gid % p.lpr);
+  const int n0 = S * static_cast<int>(gid % p.lpr);
   const int64_t P = p.P, H = p.H, G = p.G, L = p.L;
   const int N = static_cast<int>(p.N);
   const T* x = static_cast<const T*>(p.x);
@@ -199,7 +211,7 @@ __global__ __launch_bounds__(kThreads) void ssd_update_kernel(UpdParams p) {
 
   bool live[R];
   int64_t rr[R], pp[R], hd[R], bb[R], gg[R];
-  float h[R][4], a2[R], Dh[R];
+  float h[R][S], a2[R], Dh[R];
 #pragma unroll
   for (int k = 0; k < R; ++k) {
     const int64_t row = row0 + k * rstride;
@@ -210,27 +222,27 @@ __global__ __launch_bounds__(kThreads) void ssd_update_kernel(UpdParams p) {
     hd[k] = bh % H;
     bb[k] = bh / H;
     gg[k] = hd[k] / (H / G);
-    load4<VEC>(p.state + rr[k] * N, n0, N, h[k]);
+    loadS<S, VEC>(p.state + rr[k] * N, n0, N, h[k]);
     a2[k] = p.A[hd[k]] * kLog2e;
     Dh[k] = p.D != nullptr ? p.D[hd[k]] : 0.f;
   }
   for (int64_t t = 0; t < L; ++t) {
-    float d[R], u[R], zz[R], bv[R][4], cv[R][4];
+    float d[R], u[R], zz[R], bv[R][S], cv[R][S];
 #pragma unroll
     for (int k = 0; k < R; ++k) {
       const int64_t obh = (bb[k] * L + t) * H + hd[k];
       d[k] = to_f32(delta[obh]);
       u[k] = to_f32(x[obh * P + pp[k]]);
       zz[k] = z != nullptr ? to_f32(z[obh * P + pp[k]]) : 0.f;
-      load4io<T, VEC>(Bm + ((bb[k] * L + t) * G + gg[k]) * N, n0, N, bv[k]);
-      load4io<T, VEC>(Cm + ((bb[k] * L + t) * G + gg[k]) * N, n0, N, cv[k]);
+      loadSio<T, S, VEC>(Bm + ((bb[k] * L + t) * G + gg[k]) * N, n0, N, bv[k]);
+      loadSio<T, S, VEC>(Cm + ((bb[k] * L + t) * G + gg[k]) * N, n0, N, cv[k]);
     }
 #pragma unroll
     for (int k = 0; k < R; ++k) {
       const float dA = exp2_hw(d[k] * a2[k]), du = d[k] * u[k];
       float acc = 0.f;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < S; ++q) {
         h[k][q] = __builtin_fmaf(dA, h[k][q], du * bv[k][q]);
         acc = __builtin_fmaf(cv[k][q], h[k][q], acc);
       }
@@ -244,12 +256,12 @@ __global__ __launch_bounds__(kThreads) void ssd_update_kernel(UpdParams p) {
   }
 #pragma unroll
   for (int k = 0; k < R; ++k)
-    if (live[k]) store4<VEC>(p.state + rr[k] * N, n0, N, h[k]);
+    if (live[k]) storeS<S, VEC>(p.state + rr[k] * N, n0, N, h[k]);
 }
 
-int lanes_per_row(int64_t N) {
+int lanes_per_row(int64_t N, int S) {
   int l = 1;
-  while (4 * l < N) l *= 2;
+  while (static_cast<int64_t>(S) * l < N) l *= 2;
   return l;
 }
 
@@ -258,16 +270,40 @@ UpdParams common(const UpdateArgs& a) {
   p.state = a.state; p.x = a.x; p.delta = a.delta; p.A = a.A; p.B = a.B; p.C = a.C; p.D = a.D; p.z = a.z;
   p.out = a.out;
   p.batch = a.batch; p.L = a.L; p.N = a.N;
-  p.lpr = lanes_per_row(a.N);
   return p;
 }
 
-// vector accesses: whole groups of 4 states, 16-byte aligned state/A, B/C aligned to 4 elements
-bool vec_ok(const UpdateArgs& a, bool mamba1) {
+// vector accesses: whole groups of S states, 16-byte aligned state/A, B/C aligned to 4 elements
+bool vec_ok(const UpdateArgs& a, bool mamba1, int S) {
   auto al = [](const void* q, uintptr_t m) { return (reinterpret_cast<uintptr_t>(q) & (m - 1)) == 0; };
   const uintptr_t bc = a.io == 1 ? 8 : 16;
-  return a.N % 4 == 0 && al(a.state, 16) && (!mamba1 || al(a.A, 16)) && al(a.B, bc) && al(a.C, bc);
+  return a.N % S == 0 && al(a.state, 16) && (!mamba1 || al(a.A, 16)) && al(a.B, bc) && al(a.C, bc);
 }
+
+int64_t grid_blocks(int64_t rows, int64_t N, int S) {
+  // R rows per thread: the grid spans ceil(rows / R) rows of lanes
+  return ((rows + R - 1) / R * lanes_per_row(N, S) + kThreads - 1) / kThreads;
+}
+
+// 8 states per lane when whole 8-groups fit (16 measured slower: fewer waves), else 4; the scalar
+// path for other layouts
+template <template <typename, bool, int> class K, typename T>
+hipError_t launch_update(UpdParams p, const UpdateArgs& a, bool mamba1, hipStream_t stream) {
+  if (vec_ok(a, mamba1, 8)) {
+    p.lpr = lanes_per_row(a.N, 8);
+    hipLaunchKernelGGL((K<T, true, 8>::fn), dim3(static_cast<unsigned>(grid_blocks(p.rows, a.N, 8))),
+                       dim3(kThreads), 0, stream, p);
+  } else {
+    const bool vec = vec_ok(a, mamba1, 4);
+    p.lpr = lanes_per_row(a.N, 4);
+    const dim3 grid(static_cast<unsigned>(grid_blocks(p.rows, a.N, 4)));
+    if (vec) hipLaunchKernelGGL((K<T, true, 4>::fn), grid, dim3(kThreads), 0, stream, p);
+    else hipLaunchKernelGGL((K<T, false, 4>::fn), grid, dim3(kThreads), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+template <typename T, bool VEC, int S> struct ScanUpd { static constexpr auto fn = scan_update_kernel<T, VEC, S>; };
+template <typename T, bool VEC, int S> struct SsdUpd { static constexpr auto fn = ssd_update_kernel<T, VEC, S>; };
 
 }  // namespace
 
@@ -275,37 +311,18 @@ hipError_t scan_update_launch(const UpdateArgs& a, hipStream_t stream) {
   UpdParams p = common(a);
   p.dim = a.dim;
   p.rows = a.batch * a.dim;
-  const dim3 grid(static_cast<unsigned>(update_grid_blocks(p.rows, a.N)));
-  const bool vec = vec_ok(a, true);
-  if (a.io == 1) {
-    if (vec) hipLaunchKernelGGL((scan_update_kernel<uint16_t, true>), grid, dim3(kThreads), 0, stream, p);
-    else hipLaunchKernelGGL((scan_update_kernel<uint16_t, false>), grid, dim3(kThreads), 0, stream, p);
-  } else {
-    if (vec) hipLaunchKernelGGL((scan_update_kernel<float, true>), grid, dim3(kThreads), 0, stream, p);
-    else hipLaunchKernelGGL((scan_update_kernel<float, false>), grid, dim3(kThreads), 0, stream, p);
-  }
-  return hipGetLastError();
+  return a.io == 1 ? launch_update<ScanUpd, uint16_t>(p, a, true, stream)
+                   : launch_update<ScanUpd, float>(p, a, true, stream);
 }
 
 hipError_t ssd_update_launch(const UpdateArgs& a, hipStream_t stream) {
   UpdParams p = common(a);
   p.H = a.H; p.P = a.P; p.G = a.G;
   p.rows = a.batch * a.H * a.P;
-  const dim3 grid(static_cast<unsigned>(update_grid_blocks(p.rows, a.N)));
-  const bool vec = vec_ok(a, false);
-  if (a.io == 1) {
-    if (vec) hipLaunchKernelGGL((ssd_update_kernel<uint16_t, true>), grid, dim3(kThreads), 0, stream, p);
-    else hipLaunchKernelGGL((ssd_update_kernel<uint16_t, false>), grid, dim3(kThreads), 0, stream, p);
-  } else {
-    if (vec) hipLaunchKernelGGL((ssd_update_kernel<float, true>), grid, dim3(kThreads), 0, stream, p);
-    else hipLaunchKernelGGL((ssd_update_kernel<float, false>), grid, dim3(kThreads), 0, stream, p);
-  }
-  return hipGetLastError();
+  return a.io == 1 ? launch_update<SsdUpd, uint16_t>(p, a, false, stream)
+                   : launch_update<SsdUpd, float>(p, a, false, stream);
 }
 
-int64_t update_grid_blocks(int64_t rows, int64_t N) {
-  // R rows per thread: the grid spans ceil(rows / R) rows of lanes
-  return ((rows + R - 1) / R * lanes_per_row(N) + kThreads - 1) / kThreads;
-}
+int64_t update_grid_blocks(int64_t rows, int64_t N) { return grid_blocks(rows, N, 4); }   // the largest grid
 
 }  // namespace mssm

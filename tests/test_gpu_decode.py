@@ -42,6 +42,8 @@ CASES = [
     (2, 1, 64, 64, "bf16", True, True),
     (1, 4, 16, 256, "f32", True, True),
     (2, 1, 24, 48, "bf16", False, False),
+    (2, 2, 40, 12, "f32", True, True),      # whole 4-groups but not 8-groups: 4 states per lane
+    (3, 1, 64, 20, "bf16", True, True),
 ]
 
 
@@ -100,6 +102,7 @@ SSD_CASES = [
     (1, 2, 2, 3, 5, 1, "f32", True, False),
     (3, 1, 4, 80, 48, 2, "bf16", False, True),
     (1, 1, 2, 64, 256, 2, "bf16", True, True),
+    (2, 2, 2, 32, 20, 1, "f32", True, True),   # 4 states per lane
 ]
 
 

@@ -82,7 +82,7 @@ def summarize_counters(cfg, is_ssd, d, copy_mib):
     WRITE_SIZE) into HBM bytes per launch of the dominant kernel, each counter scaled by what it
     reads for a device copy of copy_mib MiB, and write profiles/traffic_<workload>.json."""
     import numpy as np
-    bwd = getattr(cfg, "backward", False)
+    bwd = getattr(cfg, "backward", False) or getattr(cfg, "train", False)   # the gradient kernel dominates
     tags = kernel_tags(is_ssd, cfg.decode, bwd)
     copy_bytes = copy_mib << 20
     res = {"workload": cfg.name, "source_digest": source_digest(is_ssd, cfg.decode, bwd),
@@ -202,8 +202,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2,
-                    help="workload id (1-9; 6, 7: decode steps; 8: gradients; 9: convolution fused in front); "
-                         "2 is the one the metric is quoted on")
+                    help="workload id (1-10; 6, 7: decode steps; 8: gradients; 9: convolution fused in front; "
+                         "10: training step); 2 is the one the metric is quoted on")
     ap.add_argument("--sets", type=int, default=0, help="resident input copies to rotate over (0: auto)")
     ap.add_argument("--chunk", type=int, default=0, help="SSD time-chunk length (0: the workload's)")
     ap.add_argument("--split-seq", type=int, default=0, help="force the sequence-chunk count (0: the planner's)")
@@ -256,7 +256,30 @@ def main():
     t = time.perf_counter()
     decode = cfg.decode
     backward = getattr(cfg, "backward", False)
-    if backward:
+    train = getattr(cfg, "train", False)
+    if train:
+        # one training step of the layer: the forward storing checkpoints, then the gradients from them
+        host = [W.make_scan_inputs(cfg, seed_base=W.ROOT_SEED + 1000 * i) for i in range(sets)]
+        douts = [W.make_scan_grads(cfg, seed_base=W.ROOT_SEED + 1000 * i, with_dfinal=False)[0] for i in range(sets)]
+        ins = [dict(x=dev(h.x), delta=dev(h.delta), A=dev(h.A), B=dev(h.B), C=dev(h.C), D=dev(h.D), z=dev(h.z),
+                    dout=dev(g)) for h, g in zip(host, douts)]
+        io = M.MSSM_BF16 if cfg.io == W.BF16 else M.MSSM_F32
+        ws_n = M.selective_scan_bwd_workspace_size(cfg.batch, cfg.seqlen, cfg.dim, cfg.dstate, io)
+        ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+        ck = torch.empty(M.selective_scan_checkpoint_size(cfg.batch, cfg.seqlen, cfg.dim, 16, io) // 4,
+                         dtype=torch.float32, device="cuda")
+        outs = [torch.empty_like(a["x"]) for a in ins]
+        grads = [M.selective_scan_bwd(a["x"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], None, a["dout"],
+                                      None, want_dh0=False, workspace=ws) for a in ins]
+
+        def step(i):
+            a = ins[i % sets]
+            M.selective_scan_fwd_ckpt(a["x"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], None,
+                                      checkpoints=ck, out=outs[i % sets])
+            M.selective_scan_bwd(a["x"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], None, a["dout"], None,
+                                 want_dh0=False, grads=grads[i % sets], checkpoints=ck, workspace=ws)
+        plan = {"tokens_per_tile": 16, "channels_per_block": 16, "checkpoints": True}
+    elif backward:
         # one backward pass of the layer: the loss gradient dout in, every input's gradient out
         host = [W.make_scan_inputs(cfg, seed_base=W.ROOT_SEED + 1000 * i) for i in range(sets)]
         douts = [W.make_scan_grads(cfg, seed_base=W.ROOT_SEED + 1000 * i, with_dfinal=False)[0] for i in range(sets)]
@@ -346,7 +369,7 @@ def main():
                                  split_seq=K, split_state=G, workspace=ws if ws_n else None)
         plan = {"split_seq": K, "split_state": G}
     del host[1:]
-    if backward:
+    if backward or train:
         del douts[1:]
     if getattr(cfg, "conv_width", 0):
         del convs[1:]
@@ -376,10 +399,13 @@ def main():
     kern_s = ms * 1e-3
     hbm = {"achieved": alg_bytes / kern_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
            "frac": alg_bytes / kern_s / 1e9 / PEAK_HBM_GBS}
-    traffic = load_traffic(cfg.name, is_ssd, decode, backward)
-    if backward:
-        # the whole backward call (gradient kernel and the two small fixed-order sum kernels)
+    traffic = load_traffic(cfg.name, is_ssd, decode, backward or train)
+    if backward or train:
+        # the whole backward call (gradient kernel and the two small fixed-order sum kernels); a training
+        # step adds the forward before it
         slots = cfg.updates * SLOTS_PER_UPDATE_BWD + cfg.batch * cfg.seqlen * cfg.dim * SLOTS_PER_STEP_CHANNEL_BWD
+        if train:
+            slots += cfg.updates * SLOTS_PER_UPDATE + cfg.batch * cfg.seqlen * cfg.dim * SLOTS_PER_STEP_CHANNEL
         alu = {"achieved": slots / kern_s / 1e12, "peak": PEAK_VALU_TSLOT, "unit": "Tslot/s"}
         alu["frac"] = alu["achieved"] / alu["peak"]
         bound = "alu" if alu["frac"] >= hbm["frac"] else "hbm"
@@ -421,13 +447,18 @@ def main():
     roof = {k: roof[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic", "other")}
     if backward:
         roof["scope"] = "whole backward call: scan_bwd_kernel, then bwd_reduce_bc and bwd_reduce_ad"
+    if train:
+        roof["scope"] = ("whole training step: wide_kernel storing checkpoints, then scan_bwd_kernel from them, "
+                         "bwd_reduce_bc and bwd_reduce_ad")
 
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         h = host[0]
-        if backward:
+        if backward or train:
             cpu = cpu_baseline_scan_bwd(h, cfg, douts[0])
+            if train:
+                cpu["sample"] += " (the gradient pass only; the oracle's gradients include their own forward)"
         elif getattr(cfg, "conv_width", 0):
             cpu = cpu_baseline_conv_scan(h, cfg, convs[0])
         else:
@@ -441,6 +472,8 @@ def main():
         conf["decode"] = True
     if backward:
         conf["backward"] = True
+    if train:
+        conf["training_step"] = True
     if is_ssd:
         conf.update(nheads=cfg.nheads, headdim=cfg.headdim, d_state=cfg.dstate, ngroups=cfg.ngroups, io="bf16",
                     **plan)
@@ -449,7 +482,8 @@ def main():
                     final_state=cfg.return_final, **plan)
     conf["input_sets"] = sets
     line = {
-        "metric": ("selective-scan gradient state updates/s (B*L*d_inner*N), 1 GPU" if backward else
+        "metric": ("selective-scan training-step state updates/s (B*L*d_inner*N per forward + gradients), 1 GPU"
+                   if train else "selective-scan gradient state updates/s (B*L*d_inner*N), 1 GPU" if backward else
                    "selective-scan state updates/s (B*L*d_inner*N), 1 GPU"),
         "value": upd_s,
         "unit": "state-updates/s",

@@ -199,6 +199,29 @@ int mssm_selective_scan_conv_fwd(const mssm_scan_desc* desc, int32_t conv_width,
  * is not split, or for an invalid or unsupported descriptor). */
 size_t mssm_selective_scan_conv_workspace_size(const mssm_scan_desc* desc);
 
+/* Training-mode forward: mssm_selective_scan_fwd (same results) that also
+ * stores the state entering every 16-step tile, for mssm_selective_scan_bwd to
+ * start from.  Training runs the forward before the gradients anyway; storing
+ * 4 bytes per lane every 16 steps spares the gradient pass a second walk over
+ * the sequence.
+ *   checkpoints : [batch][ceil(seqlen/16)][16*ceil(dim/16)][16] fp32, at least
+ *                 mssm_selective_scan_checkpoint_size(desc) bytes; entry
+ *                 [b][k][c][n] is h[n] of channel c before step 16k (channels
+ *                 past dim are not written).
+ * Supported: dstate 16, dim * sizeof(io) a multiple of 16, 16-byte aligned io
+ * pointers, split_state 0 or 16; workspace as given by
+ * mssm_selective_scan_fwd_ckpt_workspace_size.  Same rules otherwise. */
+int mssm_selective_scan_fwd_ckpt(const mssm_scan_desc* desc,
+                                 const void* x, const void* delta, const float* A,
+                                 const void* B, const void* C, const float* D, const void* z,
+                                 const float* h0, void* out, float* final_state, float* checkpoints,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+size_t mssm_selective_scan_fwd_ckpt_workspace_size(const mssm_scan_desc* desc);
+
+/* Bytes of the checkpoint array (0 for an invalid descriptor or dstate != 16). */
+size_t mssm_selective_scan_checkpoint_size(const mssm_scan_desc* desc);
+
 /* Gradients of mssm_selective_scan_fwd (reverse mode through the same
  * recurrence; training a selective SSM needs them, "P20 - Mamba", 5).  For
  * the loss sum(out * dout) + sum(final_state * dfinal) it writes
@@ -222,6 +245,10 @@ size_t mssm_selective_scan_conv_workspace_size(const mssm_scan_desc* desc);
  * mssm_selective_scan_bwd_workspace_size(desc) bytes, 256-byte aligned (about
  * 4 * batch * dim * dstate * (seqlen / 16) bytes of state checkpoints plus
  * 128 * batch * seqlen * ceil(dim / 16) bytes of per-block partial sums).
+ * checkpoints: nullable; the array mssm_selective_scan_fwd_ckpt wrote for
+ * these inputs (dstate 16 only).  Given it, the kernel starts every tile from
+ * the stored state instead of walking the sequence forward once more (the
+ * first workspace segment then goes unused).
  * Outputs and workspace must not alias any input or each other.  Same
  * ownership, stream and error rules as mssm_selective_scan_fwd. */
 int mssm_selective_scan_bwd(const mssm_scan_desc* desc,
@@ -229,7 +256,7 @@ int mssm_selective_scan_bwd(const mssm_scan_desc* desc,
                             const void* B, const void* C, const float* D, const void* z,
                             const float* h0, const void* dout, const float* dfinal,
                             void* dx, void* ddelta, float* dA, float* dB, float* dC, float* dD,
-                            void* dz, float* dh0,
+                            void* dz, float* dh0, const float* checkpoints,
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace mssm_selective_scan_bwd needs (0 for an invalid or

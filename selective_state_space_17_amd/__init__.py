@@ -50,7 +50,10 @@ SIGNATURES = {
     "mssm_ssd_state_update": (_I, [ctypes.POINTER(SSDDesc)] + [_P] * 10),
     "mssm_selective_scan_conv_fwd": (_I, [ctypes.POINTER(ScanDesc), ctypes.c_int32] + [_P] * 13 + [_P, _SZ, _P]),
     "mssm_selective_scan_conv_workspace_size": (_SZ, [ctypes.POINTER(ScanDesc)]),
-    "mssm_selective_scan_bwd": (_I, [ctypes.POINTER(ScanDesc)] + [_P] * 18 + [_P, _SZ, _P]),
+    "mssm_selective_scan_bwd": (_I, [ctypes.POINTER(ScanDesc)] + [_P] * 19 + [_P, _SZ, _P]),
+    "mssm_selective_scan_fwd_ckpt": (_I, [ctypes.POINTER(ScanDesc)] + [_P] * 11 + [_P, _SZ, _P]),
+    "mssm_selective_scan_fwd_ckpt_workspace_size": (_SZ, [ctypes.POINTER(ScanDesc)]),
+    "mssm_selective_scan_checkpoint_size": (_SZ, [ctypes.POINTER(ScanDesc)]),
     "mssm_selective_scan_bwd_workspace_size": (_SZ, [ctypes.POINTER(ScanDesc)]),
     "mssm_status_string": (ctypes.c_char_p, [_I]),
     "mssm_last_error_detail": (ctypes.c_char_p, []),
@@ -190,6 +193,56 @@ def selective_scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, return_final_
     return (out, final_state) if return_final_state else out
 
 
+def selective_scan_checkpoint_size(batch, seqlen, dim, dstate=16, io_dtype=MSSM_BF16) -> int:
+    d = scan_desc(batch, seqlen, dim, dstate, io_dtype)
+    return lib.mssm_selective_scan_checkpoint_size(ctypes.byref(d))
+
+
+def selective_scan_fwd_ckpt(x, delta, A, B, C, D=None, z=None, h0=None, checkpoints=None,
+                            return_final_state: bool = False, split_seq: int = 0, out=None, final_state=None,
+                            workspace=None, stream=None):
+    """Training-mode forward (mssm_selective_scan_fwd_ckpt): selective_scan_fwd that also stores the state
+    entering every 16-step tile into ``checkpoints`` (allocated when None), for selective_scan_bwd.
+    Returns (out, checkpoints) or (out, final_state, checkpoints)."""
+    torch = _torch()
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, seqlen, dim]")
+    bsz, L, dm = x.shape
+    if A.dim() != 2 or A.shape[0] != dm:
+        raise ValueError("A must be [dim, dstate]")
+    N = A.shape[1]
+    io = _io_code(x.dtype)
+    for name, t, shape in (("x", x, (bsz, L, dm)), ("delta", delta, (bsz, L, dm)), ("z", z, (bsz, L, dm)),
+                           ("B", B, (bsz, L, N)), ("C", C, (bsz, L, N))):
+        _check_gpu(name, t, x.dtype, shape)
+    _check_gpu("A", A, torch.float32, (dm, N))
+    _check_gpu("D", D, torch.float32, (dm,))
+    _check_gpu("h0", h0, torch.float32, (bsz, dm, N))
+    if out is None:
+        out = torch.empty_like(x)
+    _check_gpu("out", out, x.dtype, (bsz, L, dm))
+    if return_final_state and final_state is None:
+        final_state = torch.empty((bsz, dm, N), dtype=torch.float32, device=x.device)
+    _check_gpu("final_state", final_state, torch.float32, (bsz, dm, N))
+    d = scan_desc(bsz, L, dm, N, io, split_seq, 16)
+    ck_bytes = lib.mssm_selective_scan_checkpoint_size(ctypes.byref(d))
+    if checkpoints is None:
+        checkpoints = torch.empty(max(ck_bytes // 4, 1), dtype=torch.float32, device=x.device)
+    elif not checkpoints.is_cuda or checkpoints.dtype != torch.float32 or checkpoints.numel() * 4 < ck_bytes:
+        raise ValueError(f"checkpoints must be a float32 GPU tensor of at least {ck_bytes} bytes")
+    ws_bytes = lib.mssm_selective_scan_fwd_ckpt_workspace_size(ctypes.byref(d))
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    st = lib.mssm_selective_scan_fwd_ckpt(ctypes.byref(d), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                          _ptr(z), _ptr(h0), _ptr(out), _ptr(final_state), _ptr(checkpoints),
+                                          _ptr(workspace) if ws_bytes else None,
+                                          workspace.numel() if (ws_bytes and workspace is not None) else 0,
+                                          _stream_handle(stream))
+    if st != MSSM_OK:
+        raise MssmError(st, "mssm_selective_scan_fwd_ckpt")
+    return (out, final_state, checkpoints) if return_final_state else (out, checkpoints)
+
+
 def selective_scan_conv_workspace_size(batch, seqlen, dim, dstate, io_dtype=MSSM_BF16, split_seq=0) -> int:
     d = scan_desc(batch, seqlen, dim, dstate, io_dtype, split_seq, 16)
     return lib.mssm_selective_scan_conv_workspace_size(ctypes.byref(d))
@@ -249,7 +302,7 @@ def selective_scan_bwd_workspace_size(batch, seqlen, dim, dstate, io_dtype=MSSM_
 
 
 def selective_scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, dout=None, dfinal=None, want_dh0: bool = True,
-                       grads=None, workspace=None, stream=None):
+                       grads=None, checkpoints=None, workspace=None, stream=None):
     """Gradients of the Mamba-1 selective scan (mssm_selective_scan_bwd), for the loss
     sum(out * dout) + sum(final_state * dfinal).
 
@@ -257,7 +310,9 @@ def selective_scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, dout=None, df
     [batch, dim, dstate] float32 or None.  Returns a dict: dx, ddelta, dz (io dtype, dz None without z),
     dB, dC [batch, seqlen, dstate] float32, dA [dim, dstate] float32, dD [dim] float32 (None without D),
     dh0 [batch, dim, dstate] float32 (None unless want_dh0).  ``grads`` may hold preallocated outputs
-    (a dict with the same keys, as returned by an earlier call) to write into.
+    (a dict with the same keys, as returned by an earlier call) to write into.  ``checkpoints``: the
+    array selective_scan_fwd_ckpt filled for these inputs (dstate 16), which spares the kernel its own
+    forward walk.
     """
     torch = _torch()
     if x.dim() != 3:
@@ -276,6 +331,11 @@ def selective_scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, dout=None, df
     _check_gpu("D", D, torch.float32, (dm,))
     _check_gpu("h0", h0, torch.float32, (bsz, dm, N))
     _check_gpu("dfinal", dfinal, torch.float32, (bsz, dm, N))
+    if checkpoints is not None:
+        d0 = scan_desc(bsz, L, dm, N, io)
+        need = lib.mssm_selective_scan_checkpoint_size(ctypes.byref(d0))
+        if not checkpoints.is_cuda or checkpoints.dtype != torch.float32 or checkpoints.numel() * 4 < need:
+            raise ValueError(f"checkpoints must be a float32 GPU tensor of at least {need} bytes")
     dev = x.device
     g = grads if grads is not None else {
         "dx": torch.empty_like(x), "ddelta": torch.empty_like(x),
@@ -299,7 +359,7 @@ def selective_scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, dout=None, df
     st = lib.mssm_selective_scan_bwd(
         ctypes.byref(d), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(dout),
         _ptr(dfinal), _ptr(g["dx"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]),
-        _ptr(g["dz"]), _ptr(g["dh0"]), _ptr(workspace) if ws_bytes else None,
+        _ptr(g["dz"]), _ptr(g["dh0"]), _ptr(checkpoints), _ptr(workspace) if ws_bytes else None,
         workspace.numel() if (ws_bytes and workspace is not None) else 0, _stream_handle(stream))
     if st != MSSM_OK:
         raise MssmError(st, "mssm_selective_scan_bwd")

@@ -331,6 +331,88 @@ int mssm_ssd_state_update(const mssm_ssd_desc* desc, float* state, const void* x
 }
 
 // --------------------------------------------------------------------------
+// Training-mode forward: also stores the state entering every 16-step tile
+// --------------------------------------------------------------------------
+size_t mssm_selective_scan_checkpoint_size(const mssm_scan_desc* desc) {
+  if (validate_scan_desc(desc) != MSSM_OK || desc->dstate != 16) return 0;
+  return mssm::scan_checkpoint_bytes(desc->batch, desc->seqlen, desc->dim);
+}
+
+int mssm_selective_scan_fwd_ckpt(const mssm_scan_desc* desc, const void* x, const void* delta, const float* A,
+                                 const void* B, const void* C, const float* D, const void* z, const float* h0,
+                                 void* out, float* final_state, float* checkpoints, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  const int v = validate_scan_desc(desc);
+  if (v != MSSM_OK) return v;
+  const mssm_scan_desc& d = *desc;
+  if (d.dstate != 16 || (d.split_state != 0 && d.split_state != 16)) return MSSM_ERR_UNSUPPORTED;
+  const int64_t es = d.io_dtype == MSSM_BF16 ? 2 : 4;
+  if ((d.dim * es) % 16 != 0) return MSSM_ERR_UNSUPPORTED;
+  if (A == nullptr) return MSSM_ERR_INVALID_ARG;
+  if (d.batch == 0) return MSSM_OK;
+  const int64_t n_bld = d.batch * d.seqlen * d.dim;
+  const int64_t n_bln = d.batch * d.seqlen * d.dstate;
+  if (n_bld > 0 && (x == nullptr || delta == nullptr || B == nullptr || C == nullptr || out == nullptr ||
+                    checkpoints == nullptr))
+    return MSSM_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(delta, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(z, 16) ||
+      !aligned(out, 16) || !aligned(A, 4) || !aligned(D, 4) || !aligned(h0, 4) || !aligned(final_state, 4) ||
+      !aligned(checkpoints, 4))
+    return MSSM_ERR_MISALIGNED;
+  const int64_t b_io = n_bld * es, b_bc = n_bln * es;
+  const int64_t b_st = d.batch * d.dim * d.dstate * 4;
+  const int64_t b_ck = static_cast<int64_t>(mssm::scan_checkpoint_bytes(d.batch, d.seqlen, d.dim));
+  const void* ins[] = {x, delta, B, C, z, A, D, h0};
+  const int64_t inb[] = {b_io, b_io, b_bc, b_bc, b_io, d.dim * d.dstate * 4, d.dim * 4, b_st};
+  for (int i = 0; i < 8; ++i) {
+    if (overlap(out, b_io, ins[i], inb[i])) return MSSM_ERR_INVALID_ARG;
+    if (overlap(final_state, b_st, ins[i], inb[i])) return MSSM_ERR_INVALID_ARG;
+    if (overlap(checkpoints, b_ck, ins[i], inb[i])) return MSSM_ERR_INVALID_ARG;
+  }
+  if (overlap(out, b_io, final_state, b_st) || overlap(out, b_io, checkpoints, b_ck) ||
+      overlap(final_state, b_st, checkpoints, b_ck))
+    return MSSM_ERR_INVALID_ARG;
+
+  mssm_scan_desc c = d;
+  c.split_state = 16;
+  int K = 1, G = 16;
+  const int pr = plan_scan(c, &K, &G);
+  if (pr != MSSM_OK) return pr;
+  const size_t need = mssm::scan_workspace_bytes(d.batch, d.dim, d.dstate, K);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need) return MSSM_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return MSSM_ERR_MISALIGNED;
+    if (overlap(workspace, static_cast<int64_t>(need), out, b_io) ||
+        overlap(workspace, static_cast<int64_t>(need), final_state, b_st) ||
+        overlap(workspace, static_cast<int64_t>(need), checkpoints, b_ck))
+      return MSSM_ERR_INVALID_ARG;
+  }
+  if (n_bld == 0 && final_state == nullptr) return MSSM_OK;
+
+  mssm::ScanArgs a{};
+  a.x = x; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.h0 = h0;
+  a.out = out; a.final_state = final_state; a.workspace = workspace; a.ckpt = checkpoints;
+  a.batch = d.batch; a.L = d.seqlen; a.dim = d.dim; a.N = d.dstate;
+  a.io = d.io_dtype; a.K = K; a.G = G;
+  const hipError_t e = mssm::scan_launch(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    set_err(e);
+    return MSSM_ERR_HIP;
+  }
+  return MSSM_OK;
+}
+
+size_t mssm_selective_scan_fwd_ckpt_workspace_size(const mssm_scan_desc* desc) {
+  if (validate_scan_desc(desc) != MSSM_OK || desc->dstate != 16) return 0;
+  if (desc->split_state != 0 && desc->split_state != 16) return 0;
+  mssm_scan_desc c = *desc;
+  c.split_state = 16;
+  int K = 1, G = 16;
+  if (plan_scan(c, &K, &G) != MSSM_OK) return 0;
+  return mssm::scan_workspace_bytes(c.batch, c.dim, c.dstate, K);
+}
+
+// --------------------------------------------------------------------------
 // Short causal convolution + SiLU fused in front of the scan
 // --------------------------------------------------------------------------
 namespace {
@@ -425,8 +507,8 @@ size_t mssm_selective_scan_bwd_workspace_size(const mssm_scan_desc* desc) {
 int mssm_selective_scan_bwd(const mssm_scan_desc* desc, const void* x, const void* delta, const float* A,
                             const void* B, const void* C, const float* D, const void* z, const float* h0,
                             const void* dout, const float* dfinal, void* dx, void* ddelta, float* dA, float* dB,
-                            float* dC, float* dD, void* dz, float* dh0, void* workspace, size_t workspace_bytes,
-                            void* stream) {
+                            float* dC, float* dD, void* dz, float* dh0, const float* checkpoints, void* workspace,
+                            size_t workspace_bytes, void* stream) {
   const int v = validate_scan_desc(desc);
   if (v != MSSM_OK) return v;
   const mssm_scan_desc& d = *desc;
@@ -443,8 +525,9 @@ int mssm_selective_scan_bwd(const mssm_scan_desc* desc, const void* x, const voi
   if (!aligned(x, es) || !aligned(delta, es) || !aligned(B, es) || !aligned(C, es) || !aligned(z, es) ||
       !aligned(dout, es) || !aligned(dx, es) || !aligned(ddelta, es) || !aligned(dz, es) || !aligned(A, 4) ||
       !aligned(D, 4) || !aligned(h0, 4) || !aligned(dfinal, 4) || !aligned(dA, 4) || !aligned(dB, 4) ||
-      !aligned(dC, 4) || !aligned(dD, 4) || !aligned(dh0, 4))
+      !aligned(dC, 4) || !aligned(dD, 4) || !aligned(dh0, 4) || !aligned(checkpoints, 4))
     return MSSM_ERR_MISALIGNED;
+  if (checkpoints != nullptr && d.dstate != 16) return MSSM_ERR_UNSUPPORTED;   // written by the dstate-16 forward
   if ((d.seqlen + 15) / 16 > std::numeric_limits<int32_t>::max() ||
       mssm::scan_bwd_grid_blocks(d.batch, d.dim) > std::numeric_limits<int32_t>::max())
     return MSSM_ERR_UNSUPPORTED;
@@ -458,12 +541,13 @@ int mssm_selective_scan_bwd(const mssm_scan_desc* desc, const void* x, const voi
   const int64_t b_bc32 = d.batch * d.seqlen * d.dstate * 4, b_st = d.batch * d.dim * d.dstate * 4;
   const int64_t b_a = d.dim * d.dstate * 4, b_d = d.dim * 4;
   const bool with_z = z != nullptr, with_d = D != nullptr;
-  const void* ins[] = {x, delta, B, C, z, A, D, h0, dout, dfinal};
-  const int64_t inb[] = {b_io, b_io, b_bc, b_bc, b_io, b_a, b_d, b_st, b_io, b_st};
+  const int64_t b_ck = static_cast<int64_t>(mssm::scan_checkpoint_bytes(d.batch, d.seqlen, d.dim));
+  const void* ins[] = {x, delta, B, C, z, A, D, h0, dout, dfinal, checkpoints};
+  const int64_t inb[] = {b_io, b_io, b_bc, b_bc, b_io, b_a, b_d, b_st, b_io, b_st, b_ck};
   const void* outs[] = {dx, ddelta, dA, dB, dC, with_d ? dD : nullptr, with_z ? dz : nullptr, dh0, workspace};
   const int64_t outb[] = {b_io, b_io, b_a, b_bc32, b_bc32, b_d, b_io, b_st, static_cast<int64_t>(need)};
   for (int i = 0; i < 9; ++i) {
-    for (int j = 0; j < 10; ++j)
+    for (int j = 0; j < 11; ++j)
       if (overlap(outs[i], outb[i], ins[j], inb[j])) return MSSM_ERR_INVALID_ARG;
     for (int j = i + 1; j < 9; ++j)
       if (overlap(outs[i], outb[i], outs[j], outb[j])) return MSSM_ERR_INVALID_ARG;
@@ -473,7 +557,7 @@ int mssm_selective_scan_bwd(const mssm_scan_desc* desc, const void* x, const voi
   a.x = x; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.h0 = h0;
   a.dout = dout; a.dfinal = dfinal;
   a.dx = dx; a.ddelta = ddelta; a.dA = dA; a.dB = dB; a.dC = dC; a.dD = with_d ? dD : nullptr;
-  a.dz = with_z ? dz : nullptr; a.dh0 = dh0; a.workspace = workspace;
+  a.dz = with_z ? dz : nullptr; a.dh0 = dh0; a.ckpt_in = checkpoints; a.workspace = workspace;
   a.batch = d.batch; a.L = d.seqlen; a.dim = d.dim; a.N = d.dstate; a.io = d.io_dtype;
   const hipError_t e = mssm::scan_bwd_launch(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {

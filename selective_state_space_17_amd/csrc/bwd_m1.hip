@@ -106,6 +106,7 @@ struct BwdParams {
   void* dz;            // written iff z != nullptr
   float* dh0;          // nullable
   float* ckpt;         // [batch][ntiles][ncb*16][16]
+  const float* ckpt_in;   // nullable: the same array written by the training-mode forward
   float* partB;        // [ncb][batch][L][16]
   float* partC;        // [ncb][batch][L][16]
   float* wsA;          // [batch][ncb*16][16]
@@ -191,11 +192,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   const float Av = lane_ok ? p.A[c * N + n] : 0.f;
   const float A2 = Av * kLog2e;
   float* ck = p.ckpt + (b * p.ntiles * D16 + c) * 16 + n;   // + k * D16 * 16
+  // the checkpoints phase B starts its tiles from: the forward's, or phase A's
+  const float* ckr = p.ckpt_in != nullptr ? p.ckpt_in + (b * p.ntiles * D16 + c) * 16 + n : ck;
 
   // -------------------------------------------------------------- phase A
   // Staged 64 steps at a time (one barrier per 64 steps, loads a whole
   // staging tile ahead); the state entering every 16-step tile is stored.
-  {
+  // Skipped when the training-mode forward already stored them.
+  if (p.ckpt_in == nullptr) {
     float* BA = Q1;   // B^T of a 64-step staging tile: [2 buffers][16 states][kBA]
     float h = (lane_ok && p.h0 != nullptr) ? p.h0[(b * dim + c) * N + n] : 0.f;
     // Loads are unconditional, from an in-range element when the step or
@@ -270,7 +274,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     const int64_t ib = (b * L + (tb < L ? tb : L - 1)) * N + (bn < N ? bn : N - 1);
     rb = io::raw(p.B, ib);
     rc = io::raw(p.C, ib);
-    rh = ck[static_cast<int64_t>(k) * D16 * 16];   // written for every lane in phase A
+    rh = ckr[static_cast<int64_t>(k) * D16 * 16];   // channels past dim: masked at staging
   };
   // transposes through this wave's own rows of Q1/Q2 (no other wave touches
   // them before the barrier that ends the tile's compute); a wave's LDS
@@ -315,8 +319,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     }
     BT[bn * kBT + bs] = okb ? io::cvt(rb) : 0.f;
     CT[bn * kBT + bs] = okb ? io::cvt(rc) : 0.f;
-    float h = rh;            // state entering the tile
-    const float hin = rh;    // (rh is reloaded for the next tile below)
+    const float hin = c < dim ? rh : 0.f;   // state entering the tile (rh is reloaded below)
+    float h = hin;
     __syncthreads();
     if (k > 0) issue(k - 1);
     const float4* b4 = reinterpret_cast<const float4*>(&BT[n * kBT]);
@@ -539,6 +543,7 @@ hipError_t scan_bwd_launch(const ScanBwdArgs& a, hipStream_t stream) {
   p.A = a.A; p.D = a.D; p.h0 = a.h0; p.dfinal = a.dfinal;
   p.dx = a.dx; p.ddelta = a.ddelta; p.dz = a.dz; p.dh0 = a.dh0;
   p.ckpt = reinterpret_cast<float*>(ws + l.ckpt);
+  p.ckpt_in = a.ckpt_in;
   p.partB = reinterpret_cast<float*>(ws + l.partB);
   p.partC = reinterpret_cast<float*>(ws + l.partC);
   p.wsA = reinterpret_cast<float*>(ws + l.wsA);

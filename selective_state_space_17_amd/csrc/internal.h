@@ -32,7 +32,13 @@ struct ScanArgs {
   const float* conv_b = nullptr;     // [dim], nullable
   const void* conv_init = nullptr;   // [batch, conv_width - 1, dim], nullable
   int conv_width = 0;
+  // optional training-mode output: the state entering every 16-step tile,
+  // [batch][ceil(L/16)][16 * ceil(dim/16)][16] fp32 (needs G == 16, N == 16)
+  float* ckpt = nullptr;
 };
+
+// bytes of the checkpoint array the training-mode forward writes and the gradients read
+size_t scan_checkpoint_bytes(int64_t batch, int64_t L, int64_t dim);
 
 
 // Workspace layout for K > 1 (all fp32 / int32, 256-byte aligned blocks):
@@ -115,6 +121,7 @@ struct ScanBwdArgs {
   float* dD;            // written iff D != nullptr
   void* dz;             // written iff z != nullptr
   float* dh0;           // nullable
+  const float* ckpt_in = nullptr;   // nullable: checkpoints from the training-mode forward
   void* workspace;
   int64_t batch, L, dim, N;
   int io;

@@ -138,6 +138,10 @@ struct KernelParams {
   const float* conv_b;     // [dim], nullable
   const void* conv_init;   // [batch, conv_width - 1, dim] (io dtype), nullable
   int conv_width;          // 1..4
+  // training mode (wide kernel): the state entering every 16-step tile,
+  // [batch][ckpt_tiles][16 * ngroups][16] fp32, for the gradient kernel
+  float* ckpt;
+  int64_t ckpt_tiles;
 };
 
 // Readout for the fast path: a0 + a1 = sum_j C_j * h_j with C_j taken from the
@@ -903,10 +907,20 @@ __global__ __launch_bounds__(kThreads) void wide_kernel(KernelParams p) {
     }
   };
   // one group start to finish (tail tiles)
+  // training mode: store the state entering the 16-step group at tile step t16
+  // (chunks start on 16-step boundaries, so it is a whole checkpoint tile)
+  int64_t cur_t0 = t_begin;
+  auto checkpoint = [&](int t16) {
+    if (p.ckpt != nullptr && cvalid) {
+      const int64_t kt = (cur_t0 + t16) / 16;
+      p.ckpt[((b * p.ckpt_tiles + kt) * (16 * static_cast<int64_t>(p.ngroups)) + c) * 16 + n] = h;
+    }
+  };
   auto group = [&](int t16) {
     GroupOps o;
     float pr[16], rd[16];
     load_ops(t16, o);
+    checkpoint(t16);
     wide_steps<0>(h, a2, o.q.x, o.q.y, o.Bv, o.Cv, pr);
     park_and_fetch(pr, rd);
     finish(t16, o.q, rd);
@@ -921,6 +935,7 @@ __global__ __launch_bounds__(kThreads) void wide_kernel(KernelParams p) {
 #pragma unroll
     for (int g = 0; g < TT / 16; ++g) {
       if (g + 1 < TT / 16) load_ops(16 * (g + 1), o[(g + 1) & 1]);
+      checkpoint(16 * g);
       wide_steps<0>(h, a2, o[g & 1].q.x, o[g & 1].q.y, o[g & 1].Bv, o[g & 1].Cv, pr);
       if (g > 0) finish(16 * (g - 1), qprev, rd);
       park_and_fetch(pr, rd);
@@ -933,6 +948,7 @@ __global__ __launch_bounds__(kThreads) void wide_kernel(KernelParams p) {
   int64_t prev_t0 = -1;
   for (int64_t t0 = t_begin; t0 < t_end; t0 += TT) {
     const int ns = (t_end - t0) < TT ? static_cast<int>(t_end - t0) : TT;
+    cur_t0 = t0;
     stage(t0);
     if (prev_t0 >= 0) store_tile(prev_t0);
     __syncthreads();
@@ -1073,9 +1089,10 @@ hipError_t launch_generic(const KernelParams& kp, int npl, bool vec, int64_t bat
 
 template <int IO>
 hipError_t launch_io(const KernelParams& kp, int G, int npl, bool vec, int64_t batch, hipStream_t stream) {
-  if (kp.conv_w != nullptr) {   // the convolution front end exists in the one-state-per-lane kernel only
-    if (G == 16 && kp.N == 16 && vec) return launch_wide<IO, true>(kp, batch, stream);
-    return hipErrorInvalidValue;
+  if (kp.conv_w != nullptr || kp.ckpt != nullptr) {   // only in the one-state-per-lane kernel
+    if (!(G == 16 && kp.N == 16 && vec)) return hipErrorInvalidValue;
+    if (kp.conv_w != nullptr) return launch_wide<IO, true>(kp, batch, stream);
+    return launch_wide<IO, false>(kp, batch, stream);
   }
   if (G == 16 && kp.N == 16 && vec) return launch_wide<IO, false>(kp, batch, stream);
   if (kp.N <= 16) {
@@ -1102,6 +1119,11 @@ int states_per_lane(int G, int64_t N) {
 
 }  // namespace
 
+size_t scan_checkpoint_bytes(int64_t batch, int64_t L, int64_t dim) {
+  return static_cast<size_t>(batch) * static_cast<size_t>((L + 15) / 16) * static_cast<size_t>((dim + 15) / 16 * 16) *
+         16 * sizeof(float);
+}
+
 bool scan_supported_G(int G, int64_t N) {
   if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return false;
   return static_cast<int64_t>(G) * 16 >= N;
@@ -1122,6 +1144,12 @@ hipError_t scan_launch(const ScanArgs& a, hipStream_t stream) {
   kp.batch = a.batch; kp.L = a.L; kp.dim = a.dim; kp.N = a.N;
   kp.K = a.K;
   kp.chunk_len = (a.L + a.K - 1) / a.K;
+  kp.ckpt = a.ckpt;
+  kp.ckpt_tiles = (a.L + 15) / 16;
+  if (a.ckpt != nullptr) {   // chunks start on checkpoint tiles (the plan's K is an upper bound)
+    kp.chunk_len = (kp.chunk_len + 15) / 16 * 16;
+    kp.K = a.L > 0 ? static_cast<int>((a.L + kp.chunk_len - 1) / kp.chunk_len) : 1;
+  }
   kp.chunk_offset = 0;
   const int G = a.G;
   const int cpb = kThreads / G;

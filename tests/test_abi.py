@@ -258,14 +258,14 @@ def test_ssd_state_update_pointer_checks():
 def _bwd_call(desc, ws=BASE + 2000 * MB, ws_bytes=None, **kw):
     a = dict(x=BASE, delta=BASE + 100 * MB, A=BASE + 200 * MB, B=BASE + 300 * MB, C=BASE + 400 * MB, D=None,
              z=None, h0=None, dout=BASE + 500 * MB, dfinal=None, dx=BASE + 600 * MB, ddelta=BASE + 700 * MB,
-             dA=BASE + 800 * MB, dB=BASE + 900 * MB, dC=BASE + 1000 * MB, dD=None, dz=None, dh0=None)
+             dA=BASE + 800 * MB, dB=BASE + 900 * MB, dC=BASE + 1000 * MB, dD=None, dz=None, dh0=None, ck=None)
     a.update(kw)
     if ws_bytes is None:
         ws_bytes = M.lib.mssm_selective_scan_bwd_workspace_size(ctypes.byref(desc)) if desc is not None else 0
     return M.lib.mssm_selective_scan_bwd(ctypes.byref(desc) if desc is not None else None, a["x"], a["delta"],
                                          a["A"], a["B"], a["C"], a["D"], a["z"], a["h0"], a["dout"], a["dfinal"],
                                          a["dx"], a["ddelta"], a["dA"], a["dB"], a["dC"], a["dD"], a["dz"], a["dh0"],
-                                         ws, ws_bytes, None)
+                                         a["ck"], ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("case,expect", [
@@ -281,6 +281,8 @@ def _bwd_call(desc, ws=BASE + 2000 * MB, ws_bytes=None, **kw):
     ("dx_aliases_x", M.MSSM_ERR_INVALID_ARG),
     ("dB_aliases_dC", M.MSSM_ERR_INVALID_ARG),
     ("workspace_aliases_dx", M.MSSM_ERR_INVALID_ARG),
+    ("checkpoints_dstate8", M.MSSM_ERR_UNSUPPORTED),
+    ("dx_aliases_checkpoints", M.MSSM_ERR_INVALID_ARG),
     ("no_workspace", M.MSSM_ERR_WORKSPACE),
     ("small_workspace", M.MSSM_ERR_WORKSPACE),
     ("misaligned_workspace", M.MSSM_ERR_MISALIGNED),
@@ -312,6 +314,11 @@ def test_scan_bwd_validation(case, expect):
         kw["dB"] = BASE + 1000 * MB + 16
     elif case == "workspace_aliases_dx":
         kw["ws"] = BASE + 600 * MB
+    elif case == "checkpoints_dstate8":
+        d = small(dstate=8, split_state=0)
+        kw["ck"] = BASE + 1200 * MB
+    elif case == "dx_aliases_checkpoints":
+        kw["ck"] = BASE + 600 * MB + 64
     elif case == "no_workspace":
         kw["ws"] = None
     elif case == "small_workspace":
@@ -392,3 +399,50 @@ def test_conv_workspace_size():
     assert M.lib.mssm_selective_scan_conv_workspace_size(ctypes.byref(d)) == \
         M.lib.mssm_selective_scan_workspace_size(ctypes.byref(d)) > 0
     assert M.lib.mssm_selective_scan_conv_workspace_size(ctypes.byref(small(dstate=8, split_state=0))) == 0
+
+
+def _ck_call(desc, ws=None, ws_bytes=0, **kw):
+    a = dict(x=BASE, delta=BASE + 100 * MB, A=BASE + 200 * MB, B=BASE + 300 * MB, C=BASE + 400 * MB, D=None,
+             z=None, h0=None, out=BASE + 500 * MB, final=None, ck=BASE + 600 * MB)
+    a.update(kw)
+    return M.lib.mssm_selective_scan_fwd_ckpt(ctypes.byref(desc) if desc is not None else None, a["x"], a["delta"],
+                                              a["A"], a["B"], a["C"], a["D"], a["z"], a["h0"], a["out"], a["final"],
+                                              a["ck"], ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("null_desc", M.MSSM_ERR_INVALID_ARG),
+    ("dstate8", M.MSSM_ERR_UNSUPPORTED),
+    ("split_state4", M.MSSM_ERR_UNSUPPORTED),
+    ("null_checkpoints", M.MSSM_ERR_INVALID_ARG),
+    ("misaligned_checkpoints", M.MSSM_ERR_MISALIGNED),
+    ("x_not_16_aligned", M.MSSM_ERR_MISALIGNED),
+    ("checkpoints_alias_out", M.MSSM_ERR_INVALID_ARG),
+    ("checkpoints_alias_x", M.MSSM_ERR_INVALID_ARG),
+])
+def test_fwd_ckpt_validation(case, expect):
+    d = small(split_state=0)
+    kw = {}
+    if case == "null_desc":
+        d = None
+    elif case == "dstate8":
+        d = small(dstate=8, split_state=0)
+    elif case == "split_state4":
+        d = small(split_state=4)
+    elif case == "null_checkpoints":
+        kw["ck"] = None
+    elif case == "misaligned_checkpoints":
+        kw["ck"] = BASE + 600 * MB + 2
+    elif case == "x_not_16_aligned":
+        kw["x"] = BASE + 8
+    elif case == "checkpoints_alias_out":
+        kw["ck"] = BASE + 500 * MB + 64
+    elif case == "checkpoints_alias_x":
+        kw["ck"] = BASE + 64
+    assert _ck_call(d, **kw) == expect
+
+
+def test_checkpoint_size():
+    d = small(batch=2, seqlen=40, dim=24, dstate=16, split_state=0)
+    assert M.lib.mssm_selective_scan_checkpoint_size(ctypes.byref(d)) == 2 * 3 * 32 * 16 * 4
+    assert M.lib.mssm_selective_scan_checkpoint_size(ctypes.byref(small(dstate=8, split_state=0))) == 0

@@ -60,6 +60,7 @@ class ScanConfig:
     decode: bool = False    # token-by-token update of a stored state (read and written in place)
     backward: bool = False  # gradients: dout in, dx/ddelta/dz (io) and dB/dC/dA/dD (fp32) out
     conv_width: int = 0     # > 0: a short causal convolution + SiLU of this width makes x from its input
+    train: bool = False     # training step: forward that stores checkpoints, then gradients from them
 
     @property
     def updates(self) -> int:
@@ -70,6 +71,10 @@ class ScanConfig:
         e = 2 if self.io == BF16 else 4
         bld = self.batch * self.seqlen * self.dim
         bln = self.batch * self.seqlen * self.dstate
+        if self.train:   # the forward pass, then the gradient pass (each reads its inputs once)
+            fwd = dataclasses.replace(self, train=False, backward=False)
+            bwd = dataclasses.replace(self, train=False, backward=True)
+            return fwd.algorithmic_bytes() + bwd.algorithmic_bytes()
         if self.backward:
             zf = 2 if self.has_z else 0
             n = bld * e * (2 + 1 + 2 + zf)          # x, delta, dout in; dx, ddelta out; z in, dz out
@@ -141,6 +146,9 @@ CONFIGS = {
     # config 2's layer with its width-4 short causal convolution + SiLU fused in front (x from its input)
     9: ScanConfig("mamba1_130m_layer_conv_bf16", 9, 8, 2048, 1536, 16, BF16, "exp_log", return_final=False,
                   conv_width=4),
+    # a training step of config 2's layer: forward storing checkpoints, then the gradients from them
+    10: ScanConfig("mamba1_130m_layer_train_bf16", 10, 8, 2048, 1536, 16, BF16, "exp_log", return_final=False,
+                   train=True),
     # decode steps (one new token against a stored state), the configs' layer shapes at serving batch sizes
     6: ScanConfig("mamba1_2p8b_decode_bf16", 6, 256, 1, 5120, 16, BF16, "s4d_real", return_final=True, decode=True),
     7: SSDConfig("mamba2_decode_bf16", 7, 64, 1, 32, 64, 128, 1, 64, BF16, True, True, True, decode=True),

@@ -53,6 +53,8 @@ CASES = [
     (2, 1, 48, 16, "bf16", True, True, False, True),     # a single step
     (1, 300, 32, 8, "f32", True, True, True, True),
     (2, 257, 100, 16, "bf16", False, True, True, False),
+    (1, 20000, 64, 16, "bf16", True, True, True, True),   # 1250 tiles: checkpoint indexing far along
+    (1, 256, 5120, 16, "bf16", True, True, False, False), # the 2.8B layer's width: 320 channel blocks
 ]
 
 
@@ -73,6 +75,15 @@ def test_scan_bwd_empty_sequence(M):
     assert np.array_equal(host64(g["dh0"]), ref["dh0"])
     assert not host64(g["dA"]).any() and not host64(g["dD"]).any()
     assert g["dB"].numel() == 0
+
+
+def test_scan_bwd_empty_batch(M):
+    """No batch rows: dA and dD are empty sums (zero); nothing else has elements."""
+    import torch
+    cfg = W.scan_config(0, 32, 24, 16, io="f32", cfg_id=852)
+    g, ref = run_case(M, cfg, False, False)
+    assert not host64(g["dA"]).any() and not host64(g["dD"]).any()
+    assert g["dx"].numel() == 0 and g["dB"].numel() == 0
 
 
 def test_scan_bwd_deterministic(M):

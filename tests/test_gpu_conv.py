@@ -46,6 +46,7 @@ CASES = [
     (2, 3, 16, 4, "f32", True, True, True, True, True, 0),          # shorter than the convolution
     (1, 1000, 32, 4, "bf16", True, True, True, True, True, 4),      # history crosses chunk boundaries
     (2, 777, 40, 3, "f32", True, True, True, True, False, 3),
+    (1, 300, 5120, 4, "bf16", True, True, True, True, True, 0),   # 320 channel groups
 ]
 
 

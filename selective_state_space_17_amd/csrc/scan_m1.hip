@@ -695,8 +695,14 @@ __device__ __forceinline__ float row_sum(float v) {
   return v;
 }
 
-template <int IO, int MODE, bool CONV>
+// variants of the one-state-per-lane kernel
+constexpr int kPlain = 0;   // the scan
+constexpr int kConv = 1;    // short causal convolution + SiLU in front (x from its input)
+constexpr int kCkpt = 2;    // training mode: also store the state entering every 16-step tile
+
+template <int IO, int MODE, int VAR>
 __global__ __launch_bounds__(kThreads) void wide_kernel(KernelParams p) {
+  constexpr bool CONV = VAR == kConv;
   using namespace wide;
   using T = typename IoType<IO>::T;
   // a staging thread moves 4 channels (or 4 states of B/C) of one step
@@ -911,9 +917,11 @@ __global__ __launch_bounds__(kThreads) void wide_kernel(KernelParams p) {
   // (chunks start on 16-step boundaries, so it is a whole checkpoint tile)
   int64_t cur_t0 = t_begin;
   auto checkpoint = [&](int t16) {
-    if (p.ckpt != nullptr && cvalid) {
-      const int64_t kt = (cur_t0 + t16) / 16;
-      p.ckpt[((b * p.ckpt_tiles + kt) * (16 * static_cast<int64_t>(p.ngroups)) + c) * 16 + n] = h;
+    if constexpr (VAR == kCkpt) {
+      if (cvalid) {
+        const int64_t kt = (cur_t0 + t16) / 16;
+        p.ckpt[((b * p.ckpt_tiles + kt) * (16 * static_cast<int64_t>(p.ngroups)) + c) * 16 + n] = h;
+      }
     }
   };
   auto group = [&](int t16) {
@@ -1040,17 +1048,17 @@ hipError_t launch_cfg(const KernelParams& kp, int64_t batch, hipStream_t stream)
 }
 
 // the same three launches for the one-state-per-lane kernel
-template <int IO, bool CONV>
+template <int IO, int VAR>
 hipError_t launch_wide(const KernelParams& kp, int64_t batch, hipStream_t stream) {
   const dim3 block(kThreads);
   if (kp.K == 1) {
     const dim3 grid(static_cast<unsigned>(batch * kp.ngroups));
-    hipLaunchKernelGGL((wide_kernel<IO, kSingle, CONV>), grid, block, 0, stream, kp);
+    hipLaunchKernelGGL((wide_kernel<IO, kSingle, VAR>), grid, block, 0, stream, kp);
     return hipGetLastError();
   }
   {
     const dim3 grid(static_cast<unsigned>(batch * kp.K * kp.ngroups));
-    hipLaunchKernelGGL((wide_kernel<IO, kChunk, CONV>), grid, block, 0, stream, kp);
+    hipLaunchKernelGGL((wide_kernel<IO, kChunk, VAR>), grid, block, 0, stream, kp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1065,7 +1073,7 @@ hipError_t launch_wide(const KernelParams& kp, int64_t batch, hipStream_t stream
     KernelParams kf = kp;
     kf.chunk_offset = 1;
     const dim3 grid(static_cast<unsigned>(batch * (kp.K - 1) * kp.ngroups));
-    hipLaunchKernelGGL((wide_kernel<IO, kFixup, CONV>), grid, block, 0, stream, kf);
+    hipLaunchKernelGGL((wide_kernel<IO, kFixup, VAR>), grid, block, 0, stream, kf);
     return hipGetLastError();
   }
 }
@@ -1091,10 +1099,11 @@ template <int IO>
 hipError_t launch_io(const KernelParams& kp, int G, int npl, bool vec, int64_t batch, hipStream_t stream) {
   if (kp.conv_w != nullptr || kp.ckpt != nullptr) {   // only in the one-state-per-lane kernel
     if (!(G == 16 && kp.N == 16 && vec)) return hipErrorInvalidValue;
-    if (kp.conv_w != nullptr) return launch_wide<IO, true>(kp, batch, stream);
-    return launch_wide<IO, false>(kp, batch, stream);
+    if (kp.conv_w != nullptr && kp.ckpt != nullptr) return hipErrorInvalidValue;   // not combined
+    if (kp.conv_w != nullptr) return launch_wide<IO, kConv>(kp, batch, stream);
+    return launch_wide<IO, kCkpt>(kp, batch, stream);
   }
-  if (G == 16 && kp.N == 16 && vec) return launch_wide<IO, false>(kp, batch, stream);
+  if (G == 16 && kp.N == 16 && vec) return launch_wide<IO, kPlain>(kp, batch, stream);
   if (kp.N <= 16) {
     switch (G) {
       case 1: return launch_vec<IO, 1, 16, true>(kp, vec, batch, stream);

@@ -90,6 +90,37 @@ constexpr int kBA = 68;   // the same for the 64-step staging tiles of the forwa
 
 template <int S> __device__ __forceinline__ float bcast(float v) { return dpp<0x150 + S>(v); }   // row_newbcast:S
 
+// acc += bcast<S>(b) * o as one v_fmac_f32_dpp (the compiler does not fold a
+// DPP operand into an FMA that accumulates in place).  b must not have been
+// written by the two preceding VALU instructions (it is written once per tile).
+template <int S> __device__ __forceinline__ void fmac_bcast(float& acc, float b, float o);
+#define MSSM_FMAC_BCAST(S)                                                                              \
+  template <> __device__ __forceinline__ void fmac_bcast<S>(float& acc, float b, float o) {            \
+    asm volatile("v_fmac_f32_dpp %0, %1, %2 row_newbcast:" #S " row_mask:0xf bank_mask:0xf"             \
+                 : "+v"(acc) : "v"(b), "v"(o));                                                        \
+  }
+MSSM_FMAC_BCAST(0) MSSM_FMAC_BCAST(1) MSSM_FMAC_BCAST(2) MSSM_FMAC_BCAST(3)
+MSSM_FMAC_BCAST(4) MSSM_FMAC_BCAST(5) MSSM_FMAC_BCAST(6) MSSM_FMAC_BCAST(7)
+MSSM_FMAC_BCAST(8) MSSM_FMAC_BCAST(9) MSSM_FMAC_BCAST(10) MSSM_FMAC_BCAST(11)
+MSSM_FMAC_BCAST(12) MSSM_FMAC_BCAST(13) MSSM_FMAC_BCAST(14) MSSM_FMAC_BCAST(15)
+#undef MSSM_FMAC_BCAST
+
+// bcast<S>(b) * o as one v_mul_f32_dpp, written out where a product is used
+// (the compiler would otherwise hoist the 16 broadcasts and keep them in VGPRs)
+template <int S> __device__ __forceinline__ float mul_bcast(float b, float o);
+#define MSSM_MUL_BCAST(S)                                                                               \
+  template <> __device__ __forceinline__ float mul_bcast<S>(float b, float o) {                        \
+    float r;                                                                                           \
+    asm volatile("v_mul_f32_dpp %0, %1, %2 row_newbcast:" #S " row_mask:0xf bank_mask:0xf"              \
+                 : "=v"(r) : "v"(b), "v"(o));                                                          \
+    return r;                                                                                          \
+  }
+MSSM_MUL_BCAST(0) MSSM_MUL_BCAST(1) MSSM_MUL_BCAST(2) MSSM_MUL_BCAST(3)
+MSSM_MUL_BCAST(4) MSSM_MUL_BCAST(5) MSSM_MUL_BCAST(6) MSSM_MUL_BCAST(7)
+MSSM_MUL_BCAST(8) MSSM_MUL_BCAST(9) MSSM_MUL_BCAST(10) MSSM_MUL_BCAST(11)
+MSSM_MUL_BCAST(12) MSSM_MUL_BCAST(13) MSSM_MUL_BCAST(14) MSSM_MUL_BCAST(15)
+#undef MSSM_MUL_BCAST
+
 struct BwdParams {
   const void* x;
   const void* delta;
@@ -139,21 +170,21 @@ __device__ __forceinline__ void rec_step(float& h, float (&av)[16], float (&hs)[
   fwd_step<S>(h, av[S], dl, du, A2, b);
   hs[S] = h;
   pr[S] = cc * h;                // C h: readout term of y
-  q1[S] = bcast<S>(dy) * h;      // dy h: dC term
+  q1[S] = mul_bcast<S>(dy, h);   // dy h: dC term
 }
 
 template <int S>
 __device__ __forceinline__ void adj_step(float& lam, float& dA, const float (&av)[16], const float (&hs)[16], float hin,
                                          float (&ls)[16], float (&r1)[16], float dl, float dy, float Av, float cc) {
-  lam = __builtin_fmaf(cc, bcast<S>(dy), lam);    // + C dy: lam_t
+  fmac_bcast<S>(lam, dy, cc);                     // + C dy: lam_t
   ls[S] = lam;                                    // (lam_t B and lam_t delta x are formed when parked)
   lam *= av[S];                                   // a_t lam_t
   const float t1 = lam * (S > 0 ? hs[S > 0 ? S - 1 : 0] : hin);   // lam a_t h_{t-1}
-  dA = __builtin_fmaf(t1, bcast<S>(dl), dA);
+  fmac_bcast<S>(dA, dl, t1);                      // + lam a_t h_{t-1} delta_t
   r1[S] = t1 * Av;
-  // keep this step's results here: otherwise the compiler sinks the dA
-  // update past the loop and keeps its operands alive across it
-  __asm__ volatile("" : "+v"(dA), "+v"(ls[S]), "+v"(r1[S]));
+  // keep this step's results here (otherwise the compiler keeps operands of
+  // later-consumed values alive across the loop)
+  __asm__ volatile("" : "+v"(ls[S]), "+v"(r1[S]));
 }
 
 // three waves per SIMD: what the grid of a typical layer provides (batch x dim / 16 blocks of 4 waves)
@@ -359,6 +390,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     float ls[kTT], r1[kTT];
     {
       __asm__ volatile("" ::: "memory");   // B, C are read again here, not kept from the loop above
+      __asm__ volatile("s_nop 1");   // DPP reads of dl / dy below: their last VALU write is long past
       float4 cv = c4[3];
       adj_step<15>(lam, dAacc, av, hs, hin, ls, r1, dl, dy, Av, cv.w);
       adj_step<14>(lam, dAacc, av, hs, hin, ls, r1, dl, dy, Av, cv.z);
@@ -408,12 +440,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     park(Q1, q1);
     {
       float q2[kTT];   // lam_t delta_t x_t
-      q2[0] = ls[0] * bcast<0>(du);   q2[1] = ls[1] * bcast<1>(du);   q2[2] = ls[2] * bcast<2>(du);
-      q2[3] = ls[3] * bcast<3>(du);   q2[4] = ls[4] * bcast<4>(du);   q2[5] = ls[5] * bcast<5>(du);
-      q2[6] = ls[6] * bcast<6>(du);   q2[7] = ls[7] * bcast<7>(du);   q2[8] = ls[8] * bcast<8>(du);
-      q2[9] = ls[9] * bcast<9>(du);   q2[10] = ls[10] * bcast<10>(du); q2[11] = ls[11] * bcast<11>(du);
-      q2[12] = ls[12] * bcast<12>(du); q2[13] = ls[13] * bcast<13>(du); q2[14] = ls[14] * bcast<14>(du);
-      q2[15] = ls[15] * bcast<15>(du);
+      q2[0] = mul_bcast<0>(du, ls[0]);     q2[1] = mul_bcast<1>(du, ls[1]);     q2[2] = mul_bcast<2>(du, ls[2]);
+      q2[3] = mul_bcast<3>(du, ls[3]);     q2[4] = mul_bcast<4>(du, ls[4]);     q2[5] = mul_bcast<5>(du, ls[5]);
+      q2[6] = mul_bcast<6>(du, ls[6]);     q2[7] = mul_bcast<7>(du, ls[7]);     q2[8] = mul_bcast<8>(du, ls[8]);
+      q2[9] = mul_bcast<9>(du, ls[9]);     q2[10] = mul_bcast<10>(du, ls[10]); q2[11] = mul_bcast<11>(du, ls[11]);
+      q2[12] = mul_bcast<12>(du, ls[12]); q2[13] = mul_bcast<13>(du, ls[13]); q2[14] = mul_bcast<14>(du, ls[14]);
+      q2[15] = mul_bcast<15>(du, ls[15]);
       park(Q2, q2);
     }
     __syncthreads();

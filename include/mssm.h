@@ -238,12 +238,14 @@ size_t mssm_selective_scan_checkpoint_size(const mssm_scan_desc* desc);
  *   dy = dout silu(z); lam_t = C_t dy_t + exp(delta_{t+1} A) lam_{t+1}
  *   (lam after the last step = dfinal); dC_t = sum_c dy_t h_t;
  *   dB_t = sum_c lam_t delta_t x_t; dz = dout y silu'(z); dh0 = exp(delta_0 A) lam_0.
- * The states are recomputed from h0 (nothing is kept from the forward call).
+ * Without checkpoints (below) the states are recomputed from h0: nothing is
+ * kept from the forward call.
  * dstate must be at most 16 (MSSM_ERR_UNSUPPORTED otherwise); split_seq and
  * split_state are ignored.  The result is deterministic: every sum is taken
  * in a fixed order.  workspace: at least
  * mssm_selective_scan_bwd_workspace_size(desc) bytes, 256-byte aligned (about
- * 4 * batch * dim * dstate * (seqlen / 16) bytes of state checkpoints plus
+ * 64 * batch * ceil(seqlen / 16) * 16 * ceil(dim / 16) bytes of state
+ * checkpoints, 16 states per channel whatever dstate is, plus
  * 128 * batch * seqlen * ceil(dim / 16) bytes of per-block partial sums).
  * checkpoints: nullable; the array mssm_selective_scan_fwd_ckpt wrote for
  * these inputs (dstate 16 only).  Given it, the kernel starts every tile from

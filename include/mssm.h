@@ -156,6 +156,25 @@ int mssm_selective_state_update(const mssm_scan_desc* desc, float* state,
                                 const void* B, const void* C, const float* D, const void* z,
                                 void* out, void* stream);
 
+/* Token-by-token state update with the short causal convolution in front (the
+ * decode counterpart of mssm_selective_scan_conv_fwd): besides the SSM state,
+ * the layer keeps the last conv_width - 1 inputs of the convolution, and each
+ * new token is convolved with them, passed through SiLU, and fed to the
+ * update of mssm_selective_state_update.
+ *   conv_state : [batch, conv_width - 1, dim] (io_dtype), oldest first (the
+ *                layout of conv_init), read and advanced in place (nullable
+ *                when conv_width is 1)
+ *   xin        : [batch, seqlen, dim] the convolution's input for the new tokens
+ *   conv_w, conv_b : as in mssm_selective_scan_conv_fwd; conv_width 1..4
+ * Equals mssm_selective_scan_conv_fwd with conv_init = conv_state and
+ * h0 = state, up to rounding; conv_state then holds the last conv_width - 1
+ * inputs exactly.  Any dstate (1..256); no alignment beyond the elements'. */
+int mssm_selective_state_update_conv(const mssm_scan_desc* desc, int32_t conv_width,
+                                     float* state, void* conv_state, const void* xin,
+                                     const float* conv_w, const float* conv_b, const void* delta,
+                                     const float* A, const void* B, const void* C, const float* D,
+                                     const void* z, void* out, void* stream);
+
 /* Token-by-token state update, multi-head (scalar A per head) form:
  *   state         : [batch, nheads, headdim, dstate] fp32, read and overwritten
  *   x, z, out     : [batch, seqlen, nheads, headdim]  (io_dtype; z nullable)

@@ -48,6 +48,7 @@ SIGNATURES = {
     "mssm_ssd_workspace_size": (_SZ, [ctypes.POINTER(SSDDesc)]),
     "mssm_selective_state_update": (_I, [ctypes.POINTER(ScanDesc)] + [_P] * 10),
     "mssm_ssd_state_update": (_I, [ctypes.POINTER(SSDDesc)] + [_P] * 10),
+    "mssm_selective_state_update_conv": (_I, [ctypes.POINTER(ScanDesc), ctypes.c_int32] + [_P] * 13),
     "mssm_selective_scan_conv_fwd": (_I, [ctypes.POINTER(ScanDesc), ctypes.c_int32] + [_P] * 13 + [_P, _SZ, _P]),
     "mssm_selective_scan_conv_workspace_size": (_SZ, [ctypes.POINTER(ScanDesc)]),
     "mssm_selective_scan_bwd": (_I, [ctypes.POINTER(ScanDesc)] + [_P] * 19 + [_P, _SZ, _P]),
@@ -442,6 +443,41 @@ def selective_state_update(state, x, delta, A, B, C, D=None, z=None, out=None, s
                                          _ptr(C), _ptr(D), _ptr(z), _ptr(out), _stream_handle(stream))
     if st != MSSM_OK:
         raise MssmError(st, "mssm_selective_state_update")
+    return out
+
+
+def selective_state_update_conv(state, conv_state, xin, conv_w, conv_b, delta, A, B, C, D=None, z=None, out=None,
+                                stream=None):
+    """Token-by-token update with the short causal convolution in front (mssm_selective_state_update_conv).
+
+    state [batch, dim, dstate] float32 and conv_state [batch, W-1, dim] (xin's dtype; None when W == 1) are
+    advanced in place; xin, delta, z: [batch, T, dim]; conv_w [dim, W] float32; conv_b [dim] or None.
+    Returns out [batch, T, dim]."""
+    torch = _torch()
+    if xin.dim() != 3:
+        raise ValueError("xin must be [batch, tokens, dim]")
+    bsz, T, dm = xin.shape
+    N = A.shape[1]
+    W = conv_w.shape[1]
+    io = _io_code(xin.dtype)
+    for name, t, shape in (("xin", xin, (bsz, T, dm)), ("delta", delta, (bsz, T, dm)), ("z", z, (bsz, T, dm)),
+                           ("B", B, (bsz, T, N)), ("C", C, (bsz, T, N)),
+                           ("conv_state", conv_state, (bsz, W - 1, dm))):
+        _check_gpu(name, t, xin.dtype, shape)
+    _check_gpu("state", state, torch.float32, (bsz, dm, N))
+    _check_gpu("conv_w", conv_w, torch.float32, (dm, W))
+    _check_gpu("conv_b", conv_b, torch.float32, (dm,))
+    _check_gpu("A", A, torch.float32, (dm, N))
+    _check_gpu("D", D, torch.float32, (dm,))
+    if out is None:
+        out = torch.empty_like(xin)
+    _check_gpu("out", out, xin.dtype, (bsz, T, dm))
+    d = scan_desc(bsz, T, dm, N, io)
+    st = lib.mssm_selective_state_update_conv(ctypes.byref(d), W, _ptr(state), _ptr(conv_state), _ptr(xin),
+                                              _ptr(conv_w), _ptr(conv_b), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                                              _ptr(D), _ptr(z), _ptr(out), _stream_handle(stream))
+    if st != MSSM_OK:
+        raise MssmError(st, "mssm_selective_state_update_conv")
     return out
 
 

@@ -280,6 +280,50 @@ int mssm_selective_state_update(const mssm_scan_desc* desc, float* state, const 
   return MSSM_OK;
 }
 
+int mssm_selective_state_update_conv(const mssm_scan_desc* desc, int32_t conv_width, float* state, void* conv_state,
+                                     const void* xin, const float* conv_w, const float* conv_b, const void* delta,
+                                     const float* A, const void* B, const void* C, const float* D, const void* z,
+                                     void* out, void* stream) {
+  const int v = validate_scan_desc(desc);
+  if (v != MSSM_OK) return v;
+  const mssm_scan_desc& d = *desc;
+  if (conv_width < 1 || conv_width > 4) return MSSM_ERR_UNSUPPORTED;
+  if (d.batch == 0 || d.seqlen == 0) return MSSM_OK;
+  const int64_t es = d.io_dtype == MSSM_BF16 ? 2 : 4;
+  if (state == nullptr || A == nullptr || xin == nullptr || delta == nullptr || B == nullptr || C == nullptr ||
+      out == nullptr || conv_w == nullptr || (conv_width > 1 && conv_state == nullptr))
+    return MSSM_ERR_INVALID_ARG;
+  if (!aligned(xin, es) || !aligned(delta, es) || !aligned(B, es) || !aligned(C, es) || !aligned(z, es) ||
+      !aligned(out, es) || !aligned(conv_state, es) || !aligned(A, 4) || !aligned(D, 4) || !aligned(state, 4) ||
+      !aligned(conv_w, 4) || !aligned(conv_b, 4))
+    return MSSM_ERR_MISALIGNED;
+  const int64_t b_io = d.batch * d.seqlen * d.dim * es, b_bc = d.batch * d.seqlen * d.dstate * es;
+  const int64_t b_st = d.batch * d.dim * d.dstate * 4;
+  const int64_t b_cs = conv_width > 1 ? d.batch * (conv_width - 1) * d.dim * es : 0;
+  const void* ins[] = {xin, delta, B, C, z, A, D, conv_w, conv_b};
+  const int64_t inb[] = {b_io, b_io, b_bc, b_bc, b_io, d.dim * d.dstate * 4, d.dim * 4, d.dim * conv_width * 4,
+                         d.dim * 4};
+  for (int i = 0; i < 9; ++i) {
+    if (overlap(out, b_io, ins[i], inb[i])) return MSSM_ERR_INVALID_ARG;
+    if (overlap(state, b_st, ins[i], inb[i])) return MSSM_ERR_INVALID_ARG;
+    if (overlap(conv_state, b_cs, ins[i], inb[i])) return MSSM_ERR_INVALID_ARG;
+  }
+  if (overlap(out, b_io, state, b_st) || overlap(out, b_io, conv_state, b_cs) || overlap(state, b_st, conv_state, b_cs))
+    return MSSM_ERR_INVALID_ARG;
+  if (mssm::update_grid_blocks(d.batch * d.dim, d.dstate) > std::numeric_limits<int32_t>::max())
+    return MSSM_ERR_UNSUPPORTED;
+  mssm::UpdateArgs a{};
+  a.state = state; a.x = xin; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.out = out;
+  a.batch = d.batch; a.L = d.seqlen; a.N = d.dstate; a.dim = d.dim; a.io = d.io_dtype;
+  a.conv_w = conv_w; a.conv_b = conv_b; a.conv_state = conv_width > 1 ? conv_state : nullptr; a.conv_width = conv_width;
+  const hipError_t e = mssm::scan_update_launch(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    set_err(e);
+    return MSSM_ERR_HIP;
+  }
+  return MSSM_OK;
+}
+
 int mssm_ssd_state_update(const mssm_ssd_desc* desc, float* state, const void* x, const void* delta,
                           const float* A, const void* B, const void* C, const float* D, const void* z, void* out,
                           void* stream) {

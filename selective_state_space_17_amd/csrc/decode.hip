@@ -128,6 +128,11 @@ struct UpdParams {
   int64_t H, P, G;         // multi-head form
   int64_t rows;            // rows of the state
   int lpr;                 // lanes per row
+  // Mamba-1 with the short causal convolution in front (x is then its input)
+  const float* conv_w;     // [dim, conv_width]
+  const float* conv_b;     // [dim], nullable
+  void* conv_state;        // [batch, conv_width - 1, dim] (io dtype), read and advanced in place
+  int conv_width;
 };
 
 // Each thread owns S states (4, or 8 when dstate allows: two 16-byte loads
@@ -137,7 +142,7 @@ struct UpdParams {
 constexpr int R = 1;
 
 // Mamba-1: row = (b, c), state [batch, dim, N]
-template <typename T, bool VEC, int S>
+template <typename T, bool VEC, int S, bool CONV>
 __global__ __launch_bounds__(kThreads) void scan_update_kernel(UpdParams p) {
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
   const int64_t row0 = gid / p.lpr;
@@ -166,6 +171,22 @@ __global__ __launch_bounds__(kThreads) void scan_update_kernel(UpdParams p) {
     loadS<S, VEC>(p.A + cc[k] * N, n0, N, a2[k]);
     Dc[k] = p.D != nullptr ? p.D[cc[k]] : 0.f;
   }
+  // convolution (CONV): taps right-aligned into 4 slots (slot 3 = this token),
+  // win[j] = the input 3 - j tokens back, taken from and returned to conv_state
+  float cw[R][4], cbias[R], win[R][3];
+  if constexpr (CONV) {
+    const int W = p.conv_width;
+    T* cs = static_cast<T*>(p.conv_state);
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) cw[k][j] = j >= 4 - W ? p.conv_w[cc[k] * W + (j - (4 - W))] : 0.f;
+      cbias[k] = p.conv_b != nullptr ? p.conv_b[cc[k]] : 0.f;
+#pragma unroll
+      for (int m = 1; m <= 3; ++m)
+        win[k][3 - m] = m <= W - 1 ? to_f32(cs[(bb[k] * (W - 1) + (W - 1 - m)) * dim + cc[k]]) : 0.f;
+    }
+  }
   for (int64_t t = 0; t < L; ++t) {
     float d[R], u[R], zz[R], bv[R][S], cv[R][S];
 #pragma unroll
@@ -173,6 +194,17 @@ __global__ __launch_bounds__(kThreads) void scan_update_kernel(UpdParams p) {
       const int64_t o = (bb[k] * L + t) * dim + cc[k];
       d[k] = to_f32(delta[o]);
       u[k] = to_f32(x[o]);
+      if constexpr (CONV) {
+        const float xin = u[k];
+        float a = __builtin_fmaf(cw[k][3], xin, cbias[k]);
+        a = __builtin_fmaf(cw[k][2], win[k][2], a);
+        a = __builtin_fmaf(cw[k][1], win[k][1], a);
+        a = __builtin_fmaf(cw[k][0], win[k][0], a);
+        u[k] = silu(a);
+        win[k][0] = win[k][1];
+        win[k][1] = win[k][2];
+        win[k][2] = xin;
+      }
       zz[k] = z != nullptr ? to_f32(z[o]) : 0.f;
       loadSio<T, S, VEC>(Bm + (bb[k] * L + t) * N, n0, N, bv[k]);
       loadSio<T, S, VEC>(Cm + (bb[k] * L + t) * N, n0, N, cv[k]);
@@ -197,6 +229,14 @@ __global__ __launch_bounds__(kThreads) void scan_update_kernel(UpdParams p) {
 #pragma unroll
   for (int k = 0; k < R; ++k)
     if (live[k]) storeS<S, VEC>(p.state + rr[k] * N, n0, N, h[k]);
+  if constexpr (CONV) {   // the window after the last token (inputs, stored exactly as read)
+    const int W = p.conv_width;
+    T* cs = static_cast<T*>(p.conv_state);
+#pragma unroll
+    for (int k = 0; k < R; ++k)
+      if (live[k] && n0 == 0)
+        for (int m = 1; m <= W - 1; ++m) cs[(bb[k] * (W - 1) + (W - 1 - m)) * dim + cc[k]] = from_f32<T>(win[k][3 - m]);
+  }
 }
 
 // multi-head form: row = (b, h, p), state [batch, H, P, N]
@@ -308,7 +348,8 @@ hipError_t launch_update(UpdParams p, const UpdateArgs& a, bool mamba1, hipStrea
   }
   return hipGetLastError();
 }
-template <typename T, bool VEC, int S> struct ScanUpd { static constexpr auto fn = scan_update_kernel<T, VEC, S>; };
+template <typename T, bool VEC, int S> struct ScanUpd { static constexpr auto fn = scan_update_kernel<T, VEC, S, false>; };
+template <typename T, bool VEC, int S> struct ScanUpdConv { static constexpr auto fn = scan_update_kernel<T, VEC, S, true>; };
 template <typename T, bool VEC, int S> struct SsdUpd { static constexpr auto fn = ssd_update_kernel<T, VEC, S>; };
 
 }  // namespace
@@ -317,6 +358,11 @@ hipError_t scan_update_launch(const UpdateArgs& a, hipStream_t stream) {
   UpdParams p = common(a);
   p.dim = a.dim;
   p.rows = a.batch * a.dim;
+  if (a.conv_w != nullptr) {
+    p.conv_w = a.conv_w; p.conv_b = a.conv_b; p.conv_state = a.conv_state; p.conv_width = a.conv_width;
+    return a.io == 1 ? launch_update<ScanUpdConv, uint16_t>(p, a, true, stream)
+                     : launch_update<ScanUpdConv, float>(p, a, true, stream);
+  }
   return a.io == 1 ? launch_update<ScanUpd, uint16_t>(p, a, true, stream)
                    : launch_update<ScanUpd, float>(p, a, true, stream);
 }

@@ -92,6 +92,11 @@ struct UpdateArgs {
   int64_t dim;          // Mamba-1
   int64_t H, P, G;      // multi-head form
   int io;               // 0 fp32, 1 bf16
+  // Mamba-1 only: short causal convolution in front, x being its input
+  const float* conv_w = nullptr;   // [dim, conv_width]
+  const float* conv_b = nullptr;   // [dim], nullable
+  void* conv_state = nullptr;      // [batch, conv_width - 1, dim], read and advanced in place
+  int conv_width = 0;
 };
 
 hipError_t scan_update_launch(const UpdateArgs& a, hipStream_t stream);

@@ -446,3 +446,35 @@ def test_checkpoint_size():
     d = small(batch=2, seqlen=40, dim=24, dstate=16, split_state=0)
     assert M.lib.mssm_selective_scan_checkpoint_size(ctypes.byref(d)) == 2 * 3 * 32 * 16 * 4
     assert M.lib.mssm_selective_scan_checkpoint_size(ctypes.byref(small(dstate=8, split_state=0))) == 0
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("width0", M.MSSM_ERR_UNSUPPORTED),
+    ("width5", M.MSSM_ERR_UNSUPPORTED),
+    ("null_window", M.MSSM_ERR_INVALID_ARG),
+    ("null_taps", M.MSSM_ERR_INVALID_ARG),
+    ("misaligned_window", M.MSSM_ERR_MISALIGNED),
+    ("window_aliases_out", M.MSSM_ERR_INVALID_ARG),
+    ("window_aliases_state", M.MSSM_ERR_INVALID_ARG),
+])
+def test_state_update_conv_validation(case, expect):
+    d = small(seqlen=1)
+    a = dict(width=4, state=BASE + 600 * MB, cs=BASE + 700 * MB, xin=BASE, w=BASE + 800 * MB, bias=None,
+             delta=BASE + 100 * MB, A=BASE + 200 * MB, B=BASE + 300 * MB, C=BASE + 400 * MB, out=BASE + 500 * MB)
+    if case == "width0":
+        a["width"] = 0
+    elif case == "width5":
+        a["width"] = 5
+    elif case == "null_window":
+        a["cs"] = None
+    elif case == "null_taps":
+        a["w"] = None
+    elif case == "misaligned_window":
+        a["cs"] = BASE + 700 * MB + 1
+    elif case == "window_aliases_out":
+        a["cs"] = BASE + 500 * MB + 16
+    elif case == "window_aliases_state":
+        a["cs"] = BASE + 600 * MB + 16
+    assert M.lib.mssm_selective_state_update_conv(ctypes.byref(d), a["width"], a["state"], a["cs"], a["xin"], a["w"],
+                                                  a["bias"], a["delta"], a["A"], a["B"], a["C"], None, None,
+                                                  a["out"], None) == expect

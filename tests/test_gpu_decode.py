@@ -138,3 +138,73 @@ def test_ssd_update_matches_sequence_kernel(M):
     torch.cuda.synchronize()
     check(host64(torch.cat(outs, dim=1)), host64(full), 2e-2, "ssd token-by-token out")
     check(host64(state), host64(fin), 2e-2, "ssd token-by-token state")
+
+
+# (batch, tokens, dim, dstate, width, io, bias, D, z)
+CONV_CASES = [
+    (2, 1, 64, 16, 4, "f32", True, True, True),
+    (3, 3, 1536, 16, 4, "bf16", True, True, True),
+    (2, 2, 40, 5, 3, "f32", False, False, True),
+    (1, 1, 32, 16, 1, "f32", True, True, False),
+    (2, 4, 24, 64, 2, "bf16", True, True, True),
+]
+
+
+def _conv_update_case(M, case, cfg_id):
+    import torch
+    b, t, d, n, width, io, hb, hd, hz = case
+    cfg = W.scan_config(b, t, d, n, io=io, has_D=hd, has_z=hz, cfg_id=cfg_id)
+    inp = W.make_scan_inputs(cfg, with_h0=True)
+    w, bias, init = W.make_conv_inputs(cfg, width, with_bias=hb)
+    state = dev(inp.h0).clone()
+    cstate = dev(init).clone() if init is not None else None
+    out = M.selective_state_update_conv(state, cstate, dev(inp.x), dev(w), dev(bias), dev(inp.delta), dev(inp.A),
+                                        dev(inp.B), dev(inp.C), dev(inp.D), dev(inp.z))
+    torch.cuda.synchronize()
+    return inp, w, bias, init, out, state, cstate
+
+
+@pytest.mark.parametrize("case", CONV_CASES, ids=lambda c: "b{}_t{}_d{}_n{}_w{}_{}".format(*c[:6]))
+def test_scan_update_conv(M, case):
+    """The decode step with the convolution window equals the fused sequence oracle started from the stored
+    window and state; the window then holds the last W-1 inputs, exactly."""
+    say("conv update", case)
+    inp, w, bias, init, out, state, cstate = _conv_update_case(M, case, 740 + case[2] + case[4])
+    ref, ref_fin = oracle.conv_scan_fwd(inp.x, w, bias, init, inp.delta, inp.A, inp.B, inp.C, inp.D, inp.z, inp.h0)
+    io = case[5]
+    check(host64(out), ref, RTOL[io], f"conv update {case} out")
+    check(host64(state), ref_fin, RTOL[io], f"conv update {case} state")
+    width = case[4]
+    if width > 1:
+        full = np.concatenate([init, inp.x], axis=1)      # the window followed by the new inputs
+        want = full[:, full.shape[1] - (width - 1):]
+        got = cstate.cpu()
+        got = got.view(torch_int16()).numpy().view(np.uint16) if io == "bf16" else got.numpy()
+        assert np.array_equal(got, want), "the window must hold the last W-1 inputs exactly"
+
+
+def torch_int16():
+    import torch
+    return torch.int16
+
+
+def test_scan_update_conv_token_by_token_equals_sequence(M):
+    """Tokens one at a time through the convolution update agree with the fused sequence kernel."""
+    import torch
+    cfg = W.scan_config(2, 50, 64, 16, io="f32", cfg_id=760)
+    inp = W.make_scan_inputs(cfg, with_h0=True)
+    w, bias, init = W.make_conv_inputs(cfg, 4)
+    full, fin = M.selective_scan_conv_fwd(dev(inp.x), dev(w), dev(bias), dev(init), dev(inp.delta), dev(inp.A),
+                                          dev(inp.B), dev(inp.C), dev(inp.D), dev(inp.z), dev(inp.h0),
+                                          return_final_state=True)
+    state, cstate = dev(inp.h0).clone(), dev(init).clone()
+    outs = []
+    for t in range(50):
+        sl = slice(t, t + 1)
+        outs.append(M.selective_state_update_conv(state, cstate, dev(inp.x[:, sl]), dev(w), dev(bias),
+                                                  dev(inp.delta[:, sl]), dev(inp.A), dev(inp.B[:, sl]),
+                                                  dev(inp.C[:, sl]), dev(inp.D), dev(inp.z[:, sl])))
+    torch.cuda.synchronize()
+    check(host64(torch.cat(outs, dim=1)), host64(full), 1e-5, "conv token-by-token out")
+    check(host64(state), host64(fin), 1e-5, "conv token-by-token state")
+    assert np.array_equal(cstate.cpu().numpy(), inp.x[:, -3:]), "window after the sequence"

@@ -44,6 +44,7 @@ CASES = [
     (1, 200, 6, 64, 128, 3, True, True, True),
     (2, 1000, 4, 64, 48, 1, True, True, True),
     (1, 777, 2, 192, 80, 2, False, False, True),
+    (2, 300, 4, 64, 112, 2, True, True, False),
 ]
 
 
@@ -116,9 +117,10 @@ def test_config4_sampled_heads(M):
         say("config4", hd0, hd1, st)
 
 
-def test_ssd_padded_states_ignore_stale_lds(M):
-    """dstate 48 (padded to 64 inside): state rows past dstate must not pick up whatever an earlier
-    kernel left in LDS.  A forward scan over NaN inputs first leaves NaNs in the LDS of every CU."""
+@pytest.mark.parametrize("dstate", [48, 80])
+def test_ssd_padded_states_ignore_stale_lds(M, dstate):
+    """dstate 48 or 80 (padded to 64 or 128 inside): state rows past dstate must not pick up whatever an
+    earlier kernel left in LDS.  A forward scan over NaN inputs first leaves NaNs in the LDS of every CU."""
     import torch
     big = W.scan_config(8, 512, 1536, 16, io="bf16", cfg_id=610)
     poison = W.make_scan_inputs(big)
@@ -126,6 +128,6 @@ def test_ssd_padded_states_ignore_stale_lds(M):
     M.selective_scan_fwd(nan_x, dev(poison.delta), dev(poison.A), dev(poison.B), dev(poison.C), dev(poison.D),
                          dev(poison.z), split_state=16)
     torch.cuda.synchronize()
-    cfg = W.ssd_config(2, 1000, 4, 64, 48, 1, cfg_id=611)
+    cfg = W.ssd_config(2, 1000, 4, 64, dstate, 1, cfg_id=611 + dstate)
     s = W.make_ssd_inputs(cfg, with_D=True, with_z=True, with_h0=True)
-    compare(M, s, "ssd dstate 48 after NaN in LDS")
+    compare(M, s, f"ssd dstate {dstate} after NaN in LDS")

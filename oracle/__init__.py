@@ -13,6 +13,13 @@ leg may import this package.  The product library never uses it.
                  (mssm_oracle.c: oracle_ssd_fwd).  Pinned by: equality with the
                  Mamba-1 oracle under head broadcast, the geometric closed form
                  with scalar A, a brute-force unrolled sum, chaining.
+``ssd3_fwd``  -- Mamba-3 SISO recurrence (exponential-trapezoidal input rule) in
+                 the scalar-A multi-head form, its own sequential loop
+                 (mssm_oracle.c: oracle_ssd3_fwd).  Pinned by: equality with
+                 ``ssd_fwd`` at lam = 1, second-order convergence to the closed-form
+                 solution of the continuous-time system at lam = 1/2 (first order
+                 at lam = 1), and a brute-force sum over the implicit width-2
+                 convolution weights.
 ``conv_silu``, ``conv_scan_fwd``
               -- the short causal convolution + SiLU in front of the scan, and
                  the scan on its output (mssm_oracle.c: oracle_conv_silu,
@@ -58,6 +65,8 @@ def load_library(path: Optional[str] = None):
     lib.oracle_scan_fwd.argtypes = [i64, i64, i64, i64, i32, p, p, p, p, p, p, p, p, i64, i64, p, p, i32]
     lib.oracle_ssd_fwd.restype = i32
     lib.oracle_ssd_fwd.argtypes = [i64, i64, i64, i64, i64, i64, i32, p, p, p, p, p, p, p, p, i64, i64, p, p, i32]
+    lib.oracle_ssd3_fwd.restype = i32
+    lib.oracle_ssd3_fwd.argtypes = [i64, i64, i64, i64, i64, i64, i32] + [p] * 9 + [p, p, i32]
     lib.oracle_conv_silu.restype = i32
     lib.oracle_conv_silu.argtypes = [i64, i64, i64, i64, i32, p, p, p, p, p]
     lib.oracle_conv_scan_fwd.restype = i32
@@ -142,6 +151,31 @@ def ssd_fwd(x, delta, A, B, C, D=None, z=None, h0=None, hd0: int = 0, hd1: Optio
                                         nthreads or default_threads())
     if rc != 0:
         raise ValueError("oracle_ssd_fwd rejected its arguments")
+    return out, fin
+
+
+def ssd3_fwd(x, delta, lam, A, B, C, D=None, z=None, h0=None, nthreads: Optional[int] = None, lib=None):
+    """Mamba-3 SISO recurrence in the scalar-A multi-head form: the exponential-trapezoidal rule
+    h_t = a_t h_{t-1} + (1 - lam_t) d_t a_t B_{t-1} x_{t-1} + lam_t d_t B_t x_t, a_t = exp(d_t A).
+
+    Shapes as in ``ssd_fwd``; ``lam`` [Bsz, L, H] in the io dtype.  Returns (out [Bsz, L, H, P] fp64,
+    final_state [Bsz, H, P, N] fp64).
+    """
+    x, delta, lam, B, C, z = _c(x), _c(delta), _c(lam), _c(B), _c(C), _c(z)
+    io = _io_code(x)
+    for t in (delta, lam, B, C) + ((z,) if z is not None else ()):
+        if _io_code(t) != io:
+            raise TypeError("x, delta, lam, B, C, z must share one dtype")
+    A, D, h0 = _c(A, np.float32), _c(D, np.float32), _c(h0, np.float32)
+    bsz, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    out = np.empty((bsz, L, H, P), dtype=np.float64)
+    fin = np.empty((bsz, H, P, N), dtype=np.float64)
+    rc = (lib or _get()).oracle_ssd3_fwd(bsz, L, H, P, N, G, io, _ptr(x), _ptr(delta), _ptr(lam), _ptr(A),
+                                         _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(out), _ptr(fin),
+                                         nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_ssd3_fwd rejected its arguments")
     return out, fin
 
 

@@ -281,6 +281,111 @@ int oracle_ssd_fwd(int64_t Bsz, int64_t L, int64_t H, int64_t P, int64_t N, int6
 }
 
 /* ------------------------------------------------------------------------- */
+/* Mamba-3 SISO recurrence: exponential-trapezoidal input rule (own loop)    */
+/* ------------------------------------------------------------------------- */
+/*
+ * "Mamba-3" (blog), "El modelo Mamba-3" item 1: the recurrence comes from an
+ * exponential-trapezoidal discretisation; "Arquitectura": it applies an
+ * implicit convolution to the state's input, which is why the short
+ * convolution can go.  The pages give no formula; this is the plain reading.
+ * Over one step of length d the exact update of h' = a h + B(s) x(s) is
+ *   h_t = exp(d a) h_{t-1} + integral_0^d exp((d - s) a) B(s) x(s) ds,
+ * and the integral is taken by the weighted trapezoidal rule with weight
+ * (1 - lam_t) on its left end (s = 0, where the integrand is
+ * exp(d a) B_{t-1} x_{t-1}) and lam_t on its right end (s = d: B_t x_t):
+ *   h_t = exp(d a) h_{t-1} + (1 - lam_t) d exp(d a) B_{t-1} x_{t-1} + lam_t d B_t x_t.
+ * lam = 1/2 is the trapezoidal rule; lam = 1 is the right-end rule d B_t x_t
+ * of the Mamba-2 form above.  lam_t is per (batch, step, head), given by the
+ * caller.  Before step 0 there is no input: B_{-1} x_{-1} = 0, and h0 is h_{-1}.
+ * Readout, D and gate as in the Mamba-2 form.
+ */
+typedef struct {
+    int64_t Bsz, L, H, P, N, G;
+    int io;
+    const void *x, *delta, *lam, *Bm, *Cm, *z;
+    const float *A, *Dv, *h0;
+    double *out, *final_state;
+    int64_t pair_begin, pair_end;   /* pairs = b * H + h */
+} ssd3_job;
+
+static void ssd3_pair(const ssd3_job* j, int64_t b, int64_t hd, double* S, double* bx_prev) {
+    const int64_t H = j->H, P = j->P, N = j->N, L = j->L, G = j->G;
+    const int64_t g = hd / (H / G);
+    for (int64_t p = 0; p < P; ++p)
+        for (int64_t n = 0; n < N; ++n) {
+            S[p * N + n] = j->h0 ? (double)j->h0[((b * H + hd) * P + p) * N + n] : 0.0;
+            bx_prev[p * N + n] = 0.0;                           /* B_{-1} x_{-1} */
+        }
+    for (int64_t t = 0; t < L; ++t) {
+        const double d = load_io(j->delta, j->io, (b * L + t) * H + hd);
+        const double lam = load_io(j->lam, j->io, (b * L + t) * H + hd);
+        const double a = exp(d * (double)j->A[hd]);
+        const double w_left = (1.0 - lam) * d * a, w_right = lam * d;
+        const int64_t r = ((b * L + t) * G + g) * N;
+        for (int64_t p = 0; p < P; ++p) {
+            const int64_t i = ((b * L + t) * H + hd) * P + p;
+            const double u = load_io(j->x, j->io, i);
+            double acc = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                const double bx = load_io(j->Bm, j->io, r + n) * u;
+                S[p * N + n] = a * S[p * N + n] + w_left * bx_prev[p * N + n] + w_right * bx;
+                bx_prev[p * N + n] = bx;
+                acc += load_io(j->Cm, j->io, r + n) * S[p * N + n];
+            }
+            double y = acc + (j->Dv ? (double)j->Dv[hd] * u : 0.0);
+            if (j->z) y *= silu(load_io(j->z, j->io, i));
+            j->out[i] = y;
+        }
+    }
+    if (j->final_state)
+        for (int64_t p = 0; p < P; ++p)
+            for (int64_t n = 0; n < N; ++n)
+                j->final_state[((b * H + hd) * P + p) * N + n] = S[p * N + n];
+}
+
+static void* ssd3_worker(void* arg) {
+    const ssd3_job* j = (const ssd3_job*)arg;
+    double* S = (double*)malloc(sizeof(double) * (size_t)(2 * j->P * j->N));
+    for (int64_t k = j->pair_begin; k < j->pair_end; ++k) ssd3_pair(j, k / j->H, k % j->H, S, S + j->P * j->N);
+    free(S);
+    return NULL;
+}
+
+/*
+ * out [Bsz, L, H, P] fp64; final_state [Bsz, H, P, N] fp64 (nullable).
+ * x, z: [Bsz, L, H, P]; delta, lam [Bsz, L, H]; Bm, Cm [Bsz, L, G, N] in io
+ * dtype; A [H], Dv [H], h0 [Bsz, H, P, N] fp32 (Dv, z, h0 nullable).
+ */
+int oracle_ssd3_fwd(int64_t Bsz, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int io,
+                    const void* x, const void* delta, const void* lam, const float* A, const void* Bm,
+                    const void* Cm, const float* Dv, const void* z, const float* h0,
+                    double* out, double* final_state, int nthreads) {
+    if (Bsz < 0 || L < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0 || H % G != 0) return -1;
+    if (io != IO_F32 && io != IO_BF16) return -1;
+    const int64_t pairs = Bsz * H;
+    if (pairs == 0) return 0;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > pairs) nthreads = (int)pairs;
+    ssd3_job* jobs = (ssd3_job*)calloc((size_t)nthreads, sizeof(ssd3_job));
+    pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+    for (int k = 0; k < nthreads; ++k) {
+        ssd3_job* j = &jobs[k];
+        j->Bsz = Bsz; j->L = L; j->H = H; j->P = P; j->N = N; j->G = G; j->io = io;
+        j->x = x; j->delta = delta; j->lam = lam; j->Bm = Bm; j->Cm = Cm; j->z = z;
+        j->A = A; j->Dv = Dv; j->h0 = h0;
+        j->out = out; j->final_state = final_state;
+        j->pair_begin = pairs * k / nthreads;
+        j->pair_end = pairs * (k + 1) / nthreads;
+    }
+    for (int k = 1; k < nthreads; ++k) pthread_create(&th[k], NULL, ssd3_worker, &jobs[k]);
+    ssd3_worker(&jobs[0]);
+    for (int k = 1; k < nthreads; ++k) pthread_join(th[k], NULL);
+    free(jobs);
+    free(th);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
 /* Mamba-1 selective scan: gradients (reverse mode through the same loop)    */
 /* ------------------------------------------------------------------------- */
 /*

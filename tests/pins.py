@@ -366,6 +366,92 @@ def pin_ssd_chaining(lib, seed=14):
 
 
 # ---------------------------------------------------------------------------
+# Mamba-3 SISO recurrence: exponential-trapezoidal input rule
+# ---------------------------------------------------------------------------
+def _ssd3_case(rng, bsz=2, L=37, H=4, P=3, N=5, G=2, with_dz=True, with_h0=True):
+    x, delta, A, B, C, D, z, h0 = _ssd_case(rng, bsz, L, H, P, N, G, with_dz, with_h0)
+    lam = rng.uniform(0.0, 1.0, (bsz, L, H)).astype(np.float32)
+    return x, delta, lam, A, B, C, D, z, h0
+
+
+def pin_ssd3_lam_one_is_ssd(lib, seed=15):
+    """lam = 1 puts the whole step weight on the right end: the Mamba-2 rule delta * B_t * x_t."""
+    rng = _rng(seed)
+    x, delta, lam, A, B, C, D, z, h0 = _ssd3_case(rng)
+    ones = np.ones_like(lam)
+    out, fin = oracle.ssd3_fwd(x, delta, ones, A, B, C, D, z, h0, lib=lib)
+    ref, ref_fin = oracle.ssd_fwd(x, delta, A, B, C, D, z, h0, lib=lib)
+    _close(out, ref, 1e-13, "lam = 1 output vs Mamba-2 form")
+    _close(fin, ref_fin, 1e-13, "lam = 1 final state vs Mamba-2 form")
+
+
+def pin_ssd3_trapezoid_order(lib, seed=16):
+    """The scheme is a quadrature of h' = a h + u(t) over each step.  Against the closed-form solution
+    for u = sin(w t), h(0) = 0:  h(T) = (w e^{aT} - a sin wT - w cos wT) / (a^2 + w^2), halving the step
+    must cut the worst error about 4x at lam = 1/2 (second order) and about 2x at lam = 1 (first order).
+    Step 0 has delta = 0 (no time passes: it only records u(0)); steps k >= 1 span ((k-1)h, kh]."""
+    a, w, T = -0.75, 2.0, 4.0
+    errs = {}
+    for lam_v in (0.5, 1.0):
+        for K in (128, 256):
+            hstep = T / K                                    # 1/32, 1/64: exact in fp32
+            tk = np.arange(K + 1) * hstep
+            x = np.sin(w * tk).astype(np.float32).reshape(1, K + 1, 1, 1)
+            delta = np.full((1, K + 1, 1), hstep, np.float32)
+            delta[0, 0, 0] = 0.0
+            lam = np.full((1, K + 1, 1), lam_v, np.float32)
+            one = np.ones((1, K + 1, 1, 1), np.float32)
+            out, _ = oracle.ssd3_fwd(x, delta, lam, np.array([a], np.float32), one, one, lib=lib)
+            xs = x[0, :, 0, 0].astype(np.float64)            # the fp32-rounded input the scheme saw
+            exact = (w * np.exp(a * tk) - a * np.sin(w * tk) - w * np.cos(w * tk)) / (a * a + w * w)
+            # the rounding of the input samples moves the result by far less than the quadrature error
+            assert np.max(np.abs(xs - np.sin(w * tk))) < 1e-7
+            errs[(lam_v, K)] = np.max(np.abs(out[0, :, 0, 0] - exact))
+    r_trap = errs[(0.5, 128)] / errs[(0.5, 256)]
+    r_right = errs[(1.0, 128)] / errs[(1.0, 256)]
+    assert 3.6 < r_trap < 4.4, f"trapezoidal rule not second order: error ratio {r_trap:.3f} ({errs})"
+    assert 1.8 < r_right < 2.2, f"right-end rule not first order: error ratio {r_right:.3f} ({errs})"
+    assert errs[(0.5, 256)] < 1e-4, errs
+
+
+def pin_ssd3_bruteforce(lib, seed=17):
+    """Unrolled, x_s reaches the output at t through two weights that share one decay:
+    y_t = sum_{s<=t} (C_t . B_s) exp(sum_{r=s+1..t} d_r A) w(t, s) x_s + exp(sum_{r<=t} d_r A) C_t . h0,
+    w(t, s) = lam_s d_s + [s < t] (1 - lam_{s+1}) d_{s+1}  (a width-2 convolution on the state input)."""
+    rng = _rng(seed)
+    x, delta, lam, A, B, C, D, z, h0 = _ssd3_case(rng, bsz=2, L=14, H=3, P=2, N=3, G=1)
+    out, fin = oracle.ssd3_fwd(x, delta, lam, A, B, C, D, z, h0, nthreads=1, lib=lib)
+    x64, d64, l64, B64, C64 = (v.astype(np.float64) for v in (x, delta, lam, B, C))
+    bsz, L, H, P = x.shape
+    want = np.zeros_like(out)
+    want_fin = np.zeros_like(fin)
+    for b in range(bsz):
+        for h in range(H):
+            ell = d64[b, :, h] * np.float64(A[h])
+            for t in range(L):
+                for p in range(P):
+                    tot = np.exp(np.sum(ell[:t + 1])) * np.dot(C64[b, t, 0], h0[b, h, p].astype(np.float64))
+                    for s in range(t + 1):
+                        wts = l64[b, s, h] * d64[b, s, h]
+                        if s < t:
+                            wts += (1.0 - l64[b, s + 1, h]) * d64[b, s + 1, h]
+                        tot += np.exp(np.sum(ell[s + 1:t + 1])) * np.dot(C64[b, t, 0], B64[b, s, 0]) * wts * \
+                            x64[b, s, h, p]
+                    tot += np.float64(D[h]) * x64[b, t, h, p]
+                    want[b, t, h, p] = tot * _silu(np.float64(z[b, t, h, p]))
+            for p in range(P):
+                st = np.exp(np.sum(ell)) * h0[b, h, p].astype(np.float64)
+                for s in range(L):
+                    wts = l64[b, s, h] * d64[b, s, h]
+                    if s < L - 1:
+                        wts += (1.0 - l64[b, s + 1, h]) * d64[b, s + 1, h]
+                    st = st + np.exp(np.sum(ell[s + 1:])) * wts * x64[b, s, h, p] * B64[b, s, 0]
+                want_fin[b, h, p] = st
+    _close(out, want, 1e-11, "Mamba-3 brute-force unrolled sum")
+    _close(fin, want_fin, 1e-11, "Mamba-3 brute-force final state")
+
+
+# ---------------------------------------------------------------------------
 # Gradients of the Mamba-1 scan
 # ---------------------------------------------------------------------------
 def _fd_case(rng, bsz=2, L=9, d=3, n=4):
@@ -517,6 +603,7 @@ def pin_conv_scan_composition(lib, seed=34):
 SCAN_PINS = [pin_lti_convolution, pin_delta_zero, pin_geometric, pin_bruteforce, pin_chaining, pin_reset,
              pin_linearity_causality, pin_gate_skip, pin_bf16_codec]
 SSD_PINS = [pin_ssd_equals_broadcast_scan, pin_ssd_geometric, pin_ssd_bruteforce, pin_ssd_chaining]
+SSD3_PINS = [pin_ssd3_lam_one_is_ssd, pin_ssd3_trapezoid_order, pin_ssd3_bruteforce]
 BWD_PINS = [pin_scan_bwd_finite_differences, pin_scan_bwd_linear_in_upstream]
 CONV_PINS = [pin_conv_numpy, pin_conv_impulse, pin_conv_chaining, pin_conv_scan_composition]
-ALL_PINS = SCAN_PINS + SSD_PINS + BWD_PINS + CONV_PINS
+ALL_PINS = SCAN_PINS + SSD_PINS + SSD3_PINS + BWD_PINS + CONV_PINS

@@ -42,6 +42,15 @@ MUTANTS = {
     "ssd_input_without_delta": ("a * S[p * N + n] + d * load_io(j->Bm", "a * S[p * N + n] + load_io(j->Bm"),
     "ssd_h0_layout": ("j->h0[((b * H + hd) * P + p) * N + n]", "j->h0[((b * H + hd) * N + (n % P)) * P + (p % N)]"),
     "ssd_skip_dropped": ("(j->Dv ? (double)j->Dv[hd] * u : 0.0)", "0.0"),
+    # Mamba-3 exponential-trapezoidal rule
+    "ssd3_left_without_decay": ("w_left = (1.0 - lam) * d * a,", "w_left = (1.0 - lam) * d,"),
+    "ssd3_weights_swapped": ("w_left = (1.0 - lam) * d * a, w_right = lam * d;",
+                             "w_left = lam * d * a, w_right = (1.0 - lam) * d;"),
+    "ssd3_left_uses_current_input": (
+        "S[p * N + n] = a * S[p * N + n] + w_left * bx_prev[p * N + n] + w_right * bx;\n                bx_prev[p * N + n] = bx;",
+        "bx_prev[p * N + n] = bx;\n                S[p * N + n] = a * S[p * N + n] + w_left * bx_prev[p * N + n] + w_right * bx;"),
+    "ssd3_left_without_delta": ("w_left = (1.0 - lam) * d * a,", "w_left = (1.0 - lam) * a,"),
+    "ssd3_prev_input_not_reset": ("bx_prev[p * N + n] = 0.0;                           /* B_{-1} x_{-1} */", ";"),
     # gradients
     "bwd_no_adjoint_decay": ("lam[n] *= a;", ";"),
     "bwd_dsilu_is_sigmoid": ("return s * (1.0 + v * (1.0 - s));", "return s;"),

@@ -183,13 +183,24 @@ def cpu_baseline_conv_scan(inp, cfg, conv):
                       f"{passes} pass(es) ({n:.3e} updates in {dt:.2f} s, fp64)"}
 
 
-def cpu_baseline_ssd(inp, cfg):
+def cpu_baseline_ssd(inp, cfg, lam=None):
+    import numpy as np
     import oracle
     threads = oracle.default_threads()
     per_head = cfg.batch * cfg.seqlen * cfg.headdim * cfg.dstate
     nh = int(min(cfg.nheads, max(1, 4e9 // per_head)))
-    passes, dt = _timed_passes(lambda: oracle.ssd_fwd(inp.x, inp.delta, inp.A, inp.B, inp.C, inp.D, inp.z, inp.h0,
-                                                      hd0=0, hd1=nh, nthreads=threads))
+    if lam is None:
+        run = lambda: oracle.ssd_fwd(inp.x, inp.delta, inp.A, inp.B, inp.C, inp.D, inp.z, inp.h0, hd0=0, hd1=nh,
+                                     nthreads=threads)
+    else:
+        # the Mamba-3 oracle runs whole problems: hand it the first nh heads (one group shared by all heads)
+        assert cfg.ngroups == 1
+        hs = lambda a: None if a is None else np.ascontiguousarray(a[:, :, :nh])
+        x, delta, z, lm = hs(inp.x), hs(inp.delta), hs(inp.z), hs(lam)
+        A = np.ascontiguousarray(inp.A[:nh])
+        D = None if inp.D is None else np.ascontiguousarray(inp.D[:nh])
+        run = lambda: oracle.ssd3_fwd(x, delta, lm, A, inp.B, inp.C, D, z, None, nthreads=threads)
+    passes, dt = _timed_passes(run)
     n = per_head * nh * passes
     return {"value": n / dt, "unit": "state-updates/s", "cores": threads, "kind": "oracle",
             "sample": f"heads 0..{nh} of {cfg.nheads}, all batches and steps, {passes} pass(es) "
@@ -202,8 +213,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2,
-                    help="workload id (1-10; 6, 7: decode steps; 8: gradients; 9: convolution fused in front; "
-                         "10: training step); 2 is the one the metric is quoted on")
+                    help="workload id (1-11; 6, 7: decode steps; 8: gradients; 9: convolution fused in front; "
+                         "10: training step; 11: Mamba-3 SISO recurrence); 2 is the one the metric is quoted on")
     ap.add_argument("--sets", type=int, default=0, help="resident input copies to rotate over (0: auto)")
     ap.add_argument("--chunk", type=int, default=0, help="SSD time-chunk length (0: the workload's)")
     ap.add_argument("--split-seq", type=int, default=0, help="force the sequence-chunk count (0: the planner's)")
@@ -316,8 +327,10 @@ def main():
     elif is_ssd:
         chunk = args.chunk or cfg.chunk
         host = [W.make_ssd_inputs(cfg, seed_base=W.ROOT_SEED + 1000 * i) for i in range(sets)]
-        ins = [dict(x=dev(h.x), delta=dev(h.delta), A=dev(h.A), B=dev(h.B), C=dev(h.C), D=dev(h.D), z=dev(h.z))
-               for h in host]
+        lams = [W.make_ssd_lam(cfg, seed_base=W.ROOT_SEED + 1000 * i) if cfg.trapezoidal else None
+                for i in range(sets)]
+        ins = [dict(x=dev(h.x), delta=dev(h.delta), A=dev(h.A), B=dev(h.B), C=dev(h.C), D=dev(h.D), z=dev(h.z),
+                    lam=dev(lm)) for h, lm in zip(host, lams)]
         outs = [(torch.empty_like(i["x"]),
                  torch.empty((cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate), dtype=torch.float32, device="cuda"))
                 for i in ins]
@@ -326,8 +339,13 @@ def main():
 
         def step(i):
             a, (o, f) = ins[i % sets], outs[i % sets]
-            M.ssd_fwd(a["x"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], None, chunk=chunk,
-                      out=o, final_state=f, return_final_state=True, workspace=ws if ws_n else None)
+            if cfg.trapezoidal:
+                M.ssd_trapezoidal_fwd(a["x"], a["delta"], a["lam"], a["A"], a["B"], a["C"], a["D"], a["z"], None,
+                                      chunk=chunk, out=o, final_state=f, return_final_state=True,
+                                      workspace=ws if ws_n else None)
+            else:
+                M.ssd_fwd(a["x"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], None, chunk=chunk,
+                          out=o, final_state=f, return_final_state=True, workspace=ws if ws_n else None)
         plan = {"chunk": chunk}
     elif getattr(cfg, "conv_width", 0):
         # the scan with its short causal convolution fused in front: x is made on chip from its input
@@ -462,7 +480,8 @@ def main():
         elif getattr(cfg, "conv_width", 0):
             cpu = cpu_baseline_conv_scan(h, cfg, convs[0])
         else:
-            cpu = cpu_baseline_ssd(h, cfg) if is_ssd else cpu_baseline_scan(h, cfg)
+            cpu = (cpu_baseline_ssd(h, cfg, lams[0] if cfg.trapezoidal else None) if is_ssd
+                   else cpu_baseline_scan(h, cfg))
         if decode:
             cpu["sample"] += "; the same recurrence from the stored state (h0)"
         log(f"cpu baseline: {cpu}")
@@ -477,6 +496,8 @@ def main():
     if is_ssd:
         conf.update(nheads=cfg.nheads, headdim=cfg.headdim, d_state=cfg.dstate, ngroups=cfg.ngroups, io="bf16",
                     **plan)
+        if cfg.trapezoidal:
+            conf["rule"] = "exponential-trapezoidal"
     else:
         conf.update(d_inner=cfg.dim, d_state=cfg.dstate, io=cfg.io, D=cfg.has_D, z_gate=cfg.has_z,
                     final_state=cfg.return_final, **plan)

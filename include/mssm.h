@@ -5,7 +5,8 @@
  * that advances a stored state in place (mssm_selective_state_update,
  * mssm_ssd_state_update), the gradients of the first
  * (mssm_selective_scan_bwd), and the first with its short causal convolution
- * fused in front (mssm_selective_scan_conv_fwd):
+ * fused in front (mssm_selective_scan_conv_fwd); and the second with the
+ * Mamba-3 exponential-trapezoidal input rule (mssm_ssd_trapezoidal_fwd):
  *
  *  1. mssm_selective_scan_fwd -- the Mamba-1 selective scan.  Defined by the
  *     linear state recurrence h_t = A h_{t-1} + B x_t with readout y_t = C h_t
@@ -134,6 +135,34 @@ int mssm_ssd_fwd(const mssm_ssd_desc* desc,
                  void* workspace, size_t workspace_bytes, void* stream);
 
 size_t mssm_ssd_workspace_size(const mssm_ssd_desc* desc);
+
+/* Mamba-3 SISO recurrence in the Mamba-2 multi-head form: the step's input
+ * integral is taken by the exponential-trapezoidal rule ("Mamba-3" blog,
+ * "El modelo Mamba-3" item 1: a more general recurrence from that
+ * discretisation; "Arquitectura": it acts as an implicit convolution on the
+ * state input, which replaces the short convolution).  The pages give no
+ * formula; this is the weighted trapezoidal rule on the exact one-step
+ * integral of the zero-order-hold system, weight lam on the step's own input
+ * and 1 - lam on the previous one (carried through the step's decay):
+ *     a        = exp(delta[b,t,h] * A[h])
+ *     S[p,n]   = a * S[p,n] + (1 - lam[b,t,h]) * delta[b,t,h] * a * B[b,t-1,g,n] * x[b,t-1,h,p]
+ *                           + lam[b,t,h] * delta[b,t,h] * B[b,t,g,n] * x[b,t,h,p]
+ *     y, out   as in mssm_ssd_fwd.
+ * lam = 1 is exactly mssm_ssd_fwd; lam = 1/2 the trapezoidal rule.
+ *   lam : [batch, seqlen, nheads] (io_dtype), required when seqlen > 0; any
+ *         value is accepted (the rule interpolates for 0 <= lam <= 1).
+ * Before step 0 there is no input (the previous-input term of step 0 is 0)
+ * and h0 is the state entering step 0; final_state is the state after the
+ * last step.  To continue a sequence in a later call, pass final_state as
+ * h0 after adding (1 - lam) * delta * B * x of the boundary (the next call's
+ * first lam and delta with this call's last B and x) -- that term belongs to
+ * the next call's first step.  Descriptor, layouts, workspace, ownership,
+ * stream and error rules as mssm_ssd_fwd. */
+int mssm_ssd_trapezoidal_fwd(const mssm_ssd_desc* desc,
+                             const void* x, const void* delta, const void* lam, const float* A,
+                             const void* B, const void* C, const float* D, const void* z,
+                             const float* h0, void* out, float* final_state,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* Token-by-token state update (decode), Mamba-1 form.  At inference the layer
  * keeps only its fixed-size state and advances it one token at a time, at a

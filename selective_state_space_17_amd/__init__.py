@@ -46,6 +46,7 @@ SIGNATURES = {
                                       ctypes.POINTER(ctypes.c_int32)]),
     "mssm_ssd_fwd": (_I, [ctypes.POINTER(SSDDesc)] + [_P] * 10 + [_P, _SZ, _P]),
     "mssm_ssd_workspace_size": (_SZ, [ctypes.POINTER(SSDDesc)]),
+    "mssm_ssd_trapezoidal_fwd": (_I, [ctypes.POINTER(SSDDesc)] + [_P] * 11 + [_P, _SZ, _P]),
     "mssm_selective_state_update": (_I, [ctypes.POINTER(ScanDesc)] + [_P] * 10),
     "mssm_ssd_state_update": (_I, [ctypes.POINTER(SSDDesc)] + [_P] * 10),
     "mssm_selective_state_update_conv": (_I, [ctypes.POINTER(ScanDesc), ctypes.c_int32] + [_P] * 13),
@@ -384,14 +385,34 @@ def ssd_fwd(x, delta, A, B, C, D=None, z=None, h0=None, chunk: int = 0, return_f
     B, C: [batch, seqlen, ngroups, dstate] bfloat16; A, D: [nheads] float32;
     h0: [batch, nheads, headdim, dstate] float32.
     """
+    return _ssd_call("mssm_ssd_fwd", x, delta, None, A, B, C, D, z, h0, chunk, return_final_state, out,
+                     final_state, workspace, stream)
+
+
+def ssd_trapezoidal_fwd(x, delta, lam, A, B, C, D=None, z=None, h0=None, chunk: int = 0,
+                        return_final_state: bool = False, out=None, final_state=None, workspace=None, stream=None):
+    """Mamba-3 SISO recurrence, exponential-trapezoidal input rule (mssm_ssd_trapezoidal_fwd).
+
+    As ``ssd_fwd`` plus lam: [batch, seqlen, nheads] bfloat16, the weight of each step's own input (1 - lam
+    goes to the previous step's input, carried through the step's decay).  lam = 1 gives ``ssd_fwd``.
+    """
+    return _ssd_call("mssm_ssd_trapezoidal_fwd", x, delta, lam, A, B, C, D, z, h0, chunk, return_final_state,
+                     out, final_state, workspace, stream)
+
+
+def _ssd_call(fn, x, delta, lam, A, B, C, D, z, h0, chunk, return_final_state, out, final_state, workspace,
+              stream):
     torch = _torch()
     if x.dim() != 4 or B.dim() != 4:
         raise ValueError("x must be [batch, seqlen, nheads, headdim] and B [batch, seqlen, ngroups, dstate]")
     bsz, L, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
     io = _io_code(x.dtype)
+    trap = fn == "mssm_ssd_trapezoidal_fwd"
+    if trap and lam is None:
+        raise ValueError("lam is required")
     for name, t, shape in (("x", x, (bsz, L, H, P)), ("z", z, (bsz, L, H, P)), ("delta", delta, (bsz, L, H)),
-                           ("B", B, (bsz, L, G, N)), ("C", C, (bsz, L, G, N))):
+                           ("lam", lam, (bsz, L, H)), ("B", B, (bsz, L, G, N)), ("C", C, (bsz, L, G, N))):
         _check_gpu(name, t, x.dtype, shape)
     _check_gpu("A", A, torch.float32, (H,))
     _check_gpu("D", D, torch.float32, (H,))
@@ -406,11 +427,16 @@ def ssd_fwd(x, delta, A, B, C, D=None, z=None, h0=None, chunk: int = 0, return_f
     ws_bytes = lib.mssm_ssd_workspace_size(ctypes.byref(d))
     if ws_bytes and workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
-    st = lib.mssm_ssd_fwd(ctypes.byref(d), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                          _ptr(h0), _ptr(out), _ptr(final_state), _ptr(workspace) if ws_bytes else None,
-                          workspace.numel() if (ws_bytes and workspace is not None) else 0, _stream_handle(stream))
+    ws = (_ptr(workspace) if ws_bytes else None,
+          workspace.numel() if (ws_bytes and workspace is not None) else 0, _stream_handle(stream))
+    if trap:
+        st = lib.mssm_ssd_trapezoidal_fwd(ctypes.byref(d), _ptr(x), _ptr(delta), _ptr(lam), _ptr(A), _ptr(B),
+                                          _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(out), _ptr(final_state), *ws)
+    else:
+        st = lib.mssm_ssd_fwd(ctypes.byref(d), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                              _ptr(h0), _ptr(out), _ptr(final_state), *ws)
     if st != MSSM_OK:
-        raise MssmError(st, "mssm_ssd_fwd")
+        raise MssmError(st, fn)
     return (out, final_state) if return_final_state else out
 
 

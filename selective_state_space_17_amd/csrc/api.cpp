@@ -618,9 +618,13 @@ size_t mssm_ssd_workspace_size(const mssm_ssd_desc* desc) {
                                    desc->ngroups, Q);
 }
 
-int mssm_ssd_fwd(const mssm_ssd_desc* desc, const void* x, const void* delta, const float* A, const void* B,
-                 const void* C, const float* D, const void* z, const float* h0, void* out, float* final_state,
-                 void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// both SSD forms: lam == nullptr is the Mamba-2 rule, else lam is required
+int ssd_fwd_impl(const mssm_ssd_desc* desc, const void* x, const void* delta, const void* lam, bool want_lam,
+                 const float* A, const void* B, const void* C, const float* D, const void* z, const float* h0,
+                 void* out, float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
   int64_t Q = 0;
   const int v = validate_ssd_desc(desc, &Q);
   if (v != MSSM_OK) return v;
@@ -634,12 +638,14 @@ int mssm_ssd_fwd(const mssm_ssd_desc* desc, const void* x, const void* delta, co
   if (A == nullptr) return MSSM_ERR_INVALID_ARG;
   if (has_steps && (x == nullptr || delta == nullptr || B == nullptr || C == nullptr || out == nullptr))
     return MSSM_ERR_INVALID_ARG;
+  if (want_lam && has_steps && lam == nullptr) return MSSM_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(z, 16) || !aligned(out, 16) || !aligned(B, 16) || !aligned(C, 16) ||
-      !aligned(delta, 2) || !aligned(A, 4) || !aligned(D, 4) || !aligned(h0, 16) || !aligned(final_state, 16))
+      !aligned(delta, 2) || !aligned(lam, 2) || !aligned(A, 4) || !aligned(D, 4) || !aligned(h0, 16) ||
+      !aligned(final_state, 16))
     return MSSM_ERR_MISALIGNED;
-  const void* ins[] = {x, delta, B, C, z, A, D, h0};
-  const int64_t inb[] = {n_x * 2, n_d * 2, n_bc * 2, n_bc * 2, n_x * 2, d.nheads * 4, d.nheads * 4, b_st};
-  for (int i = 0; i < 8; ++i) {
+  const void* ins[] = {x, delta, B, C, z, A, D, h0, lam};
+  const int64_t inb[] = {n_x * 2, n_d * 2, n_bc * 2, n_bc * 2, n_x * 2, d.nheads * 4, d.nheads * 4, b_st, n_d * 2};
+  for (int i = 0; i < 9; ++i) {
     if (overlap(out, n_x * 2, ins[i], inb[i])) return MSSM_ERR_INVALID_ARG;
     if (overlap(final_state, b_st, ins[i], inb[i])) return MSSM_ERR_INVALID_ARG;
   }
@@ -650,8 +656,8 @@ int mssm_ssd_fwd(const mssm_ssd_desc* desc, const void* x, const void* delta, co
     if (!aligned(workspace, 256)) return MSSM_ERR_MISALIGNED;
   }
   mssm::SSDArgs a{};
-  a.x = x; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.h0 = h0;
-  a.out = out; a.final_state = final_state; a.workspace = workspace;
+  a.x = x; a.delta = delta; a.lam = want_lam ? lam : nullptr; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z;
+  a.h0 = h0; a.out = out; a.final_state = final_state; a.workspace = workspace;
   a.batch = d.batch; a.L = d.seqlen; a.H = d.nheads; a.P = d.headdim; a.N = d.dstate; a.G = d.ngroups; a.Q = Q;
   const hipError_t e = mssm::ssd_launch(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
@@ -659,6 +665,24 @@ int mssm_ssd_fwd(const mssm_ssd_desc* desc, const void* x, const void* delta, co
     return MSSM_ERR_HIP;
   }
   return MSSM_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int mssm_ssd_fwd(const mssm_ssd_desc* desc, const void* x, const void* delta, const float* A, const void* B,
+                 const void* C, const float* D, const void* z, const float* h0, void* out, float* final_state,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  return ssd_fwd_impl(desc, x, delta, nullptr, false, A, B, C, D, z, h0, out, final_state, workspace,
+                      workspace_bytes, stream);
+}
+
+int mssm_ssd_trapezoidal_fwd(const mssm_ssd_desc* desc, const void* x, const void* delta, const void* lam,
+                             const float* A, const void* B, const void* C, const float* D, const void* z,
+                             const float* h0, void* out, float* final_state, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return ssd_fwd_impl(desc, x, delta, lam, true, A, B, C, D, z, h0, out, final_state, workspace,
+                      workspace_bytes, stream);
 }
 
 }  // extern "C"

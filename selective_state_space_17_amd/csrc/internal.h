@@ -60,6 +60,7 @@ bool scan_supported_G(int G, int64_t N);
 struct SSDArgs {
   const void* x;
   const void* delta;
+  const void* lam;   // nullable: the Mamba-2 rule; else the Mamba-3 exponential-trapezoidal rule
   const float* A;
   const void* B;
   const void* C;

@@ -37,6 +37,17 @@
 // see about 16 significant bits and the result keeps fp32-state accuracy.
 // A chunk length of 128 or 256 steps is evaluated as 2 or 4 consecutive
 // 64-step blocks with the state carried between them (the same algebra).
+//
+// Mamba-3 SISO recurrence (TRAP): the input integral of each step is taken by
+// the exponential-trapezoidal rule ("Mamba-3" blog, "El modelo Mamba-3" item
+// 1; "Arquitectura": an implicit convolution on the state input):
+//   S_t = a_t S_{t-1} + (1 - lam_t) d_t a_t x_{t-1} B_{t-1} + lam_t d_t x_t B_t.
+// x_s then reaches step t > s through one decay exp(s_t - s_s) with the summed
+// weight lam_s d_s + (1 - lam_{s+1}) d_{s+1}, and step s itself with lam_s d_s;
+// so only the mask weights change (the diagonal takes the second), and the
+// state leaving a block already holds the next block's left-end term (its
+// last step's weight reaches into the next block).  At the end of the
+// sequence that term does not exist, so final_state is the plain S_{L-1}.
 #include <type_traits>
 
 #include "internal.h"
@@ -109,6 +120,7 @@ __device__ __forceinline__ int knat(int pos) {
 struct SSDParams {
   const uint16_t* x;
   const uint16_t* delta;
+  const uint16_t* lam;   // Mamba-3 exponential-trapezoidal weights [B, L, H] (TRAP only)
   const float* A;
   const uint16_t* B;
   const uint16_t* C;
@@ -124,7 +136,7 @@ struct SSDParams {
 // MFMA 16x16x32 lane layout: A row / B column = lane % 16 with the k slots of
 // lane group lane / 16 as above; accumulator element v of a lane is row
 // 4 * (lane / 16) + v, column lane % 16.
-template <int NP>
+template <int NP, bool TRAP>
 __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
   static_assert(NP % 64 == 0, "each wave of a pair holds whole 32-wide k blocks of the state");
   constexpr int NS = NP + PAD;        // row stride of [*, NP] arrays (bf16)
@@ -142,8 +154,10 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t Ms[2][QB * QS];    // decayed causal mask [t][kpos(s)], hi/lo
   __shared__ __attribute__((aligned(16))) f32x4 Xc[kWaves * 2 * kWave];  // partial readouts handed to the pair partner
   __shared__ __attribute__((aligned(16))) float css[QB];              // inclusive sum of delta * A * log2 e
-  __shared__ __attribute__((aligned(16))) float dls[QB];              // delta
-  __shared__ __attribute__((aligned(16))) float wls[QB];              // exp2(s_Q - s_s) * delta_s
+  __shared__ __attribute__((aligned(16))) float dls[QB];              // weight of x_s at later steps: delta_s
+                                                                      // (TRAP: lam_s delta_s + (1 - lam_{s+1}) delta_{s+1})
+  __shared__ __attribute__((aligned(16))) float dgs[TRAP ? QB : 1];   // TRAP: weight of x_s at step s, lam_s delta_s
+  __shared__ __attribute__((aligned(16))) float wls[QB];              // exp2(s_Q - s_s) * dls_s
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
@@ -226,6 +240,11 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
   const uint16_t* const vg = is_x ? xg : zg;
   u32x4 b0reg, b1reg, creg[CL], v0reg, v1reg;
   uint16_t dreg = 0;
+  // TRAP: lam of the step, delta and lam of the step after it (which may open
+  // the next block; past the end of the sequence it does not exist: weight 0)
+  uint16_t lreg = 0, dnreg = 0, lnreg = 0;
+  bool next_ok = false;
+  const uint16_t* const lgp = (TRAP && p.lam != nullptr) ? p.lam + b * L * H + h : nullptr;
 
   // element offsets from step 0 of a block (rows past the end of the sequence,
   // in the last block only, are clamped to its last row)
@@ -259,7 +278,18 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
     for (int i = 0; i < CL; ++i) creg[i] = *reinterpret_cast<const u32x4*>(ct + oc[i]);
     v0reg = *reinterpret_cast<const u32x4*>(vt + ov[0]);
     v1reg = *reinterpret_cast<const u32x4*>(vt + ov[1]);
-    if (tid < QB) dreg = dg[(t0 + (tid < nvalid ? tid : nvalid - 1)) * H];
+    if (tid < QB) {
+      const int64_t ts = t0 + (tid < nvalid ? tid : nvalid - 1);
+      dreg = dg[ts * H];
+      if constexpr (TRAP) {
+        const int64_t tn = t0 + tid + 1;
+        next_ok = tn < L;
+        const int64_t tc = next_ok ? tn : L - 1;   // an in-range address; the value is dropped when !next_ok
+        lreg = lgp[ts * H];
+        dnreg = dg[tc * H];
+        lnreg = lgp[tc * H];
+      }
+    }
   };
 
   // registers -> LDS (rows past the end are zero), with the transposed copies of
@@ -330,8 +360,18 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
       v += dppf<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
       const float cs_end = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), kWave - 1));
       css[lane] = v;
-      dls[lane] = d;
-      wls[lane] = exp2_hw(cs_end - v) * d;
+      float wo = d;
+      if constexpr (TRAP) {
+        // x_s enters at step s with lam_s d_s and at step s+1 with (1 - lam_{s+1}) d_{s+1} exp(d_{s+1} A);
+        // the second decays from s+1 on, so both share exp2(s_t - s_s) and only the weights add
+        const float lm = lane < nvalid ? __uint_as_float(static_cast<uint32_t>(lreg) << 16) : 0.f;
+        const float dn = next_ok ? __uint_as_float(static_cast<uint32_t>(dnreg) << 16) : 0.f;
+        const float ln = next_ok ? __uint_as_float(static_cast<uint32_t>(lnreg) << 16) : 0.f;
+        dgs[lane] = lm * d;
+        wo = __builtin_fmaf(1.f - ln, dn, lm * d);
+      }
+      dls[lane] = wo;
+      wls[lane] = exp2_hw(cs_end - v) * wo;
     }
   };
 
@@ -357,6 +397,12 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
     float m[4] = {acc[0] * exp2_hw(ct - cs4.x) * dl4.x, acc[1] * exp2_hw(ct - cs4.y) * dl4.y,
                   acc[2] * exp2_hw(ct - cs4.z) * dl4.z, acc[3] * exp2_hw(ct - cs4.w) * dl4.w};
     if (i == j) {
+      if constexpr (TRAP) {   // on the diagonal (s == t, decay 1) only the step's own weight applies
+        const float4 dg4 = *reinterpret_cast<const float4*>(&dgs[s0]);
+        const float dg[4] = {dg4.x, dg4.y, dg4.z, dg4.w};
+#pragma unroll
+        for (int v = 0; v < 4; ++v) m[v] = (s0 + v == t) ? acc[v] * dg[v] : m[v];
+      }
 #pragma unroll
       for (int v = 0; v < 4; ++v) m[v] = (s0 + v <= t) ? m[v] : 0.f;
     }
@@ -520,10 +566,10 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
   }
 }
 
-template <int NP>
+template <int NP, bool TRAP>
 hipError_t launch_np(const SSDParams& sp, hipStream_t stream) {
   const int64_t blocks = sp.batch * sp.H * sp.nps;
-  hipLaunchKernelGGL(ssd_kernel<NP>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream, sp);
+  hipLaunchKernelGGL((ssd_kernel<NP, TRAP>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream, sp);
   return hipGetLastError();
 }
 
@@ -537,6 +583,7 @@ hipError_t ssd_launch(const SSDArgs& a, hipStream_t stream) {
   SSDParams sp{};
   sp.x = static_cast<const uint16_t*>(a.x);
   sp.delta = static_cast<const uint16_t*>(a.delta);
+  sp.lam = static_cast<const uint16_t*>(a.lam);
   sp.A = a.A;
   sp.B = static_cast<const uint16_t*>(a.B);
   sp.C = static_cast<const uint16_t*>(a.C);
@@ -547,8 +594,12 @@ hipError_t ssd_launch(const SSDArgs& a, hipStream_t stream) {
   sp.final_state = a.final_state;
   sp.batch = a.batch; sp.L = a.L; sp.H = a.H; sp.P = a.P; sp.N = a.N; sp.G = a.G;
   sp.nps = static_cast<int>(a.P / PB);
-  if (a.N <= 64) return launch_np<64>(sp, stream);
-  return launch_np<128>(sp, stream);
+  if (a.lam != nullptr) {
+    if (a.N <= 64) return launch_np<64, true>(sp, stream);
+    return launch_np<128, true>(sp, stream);
+  }
+  if (a.N <= 64) return launch_np<64, false>(sp, stream);
+  return launch_np<128, false>(sp, stream);
 }
 
 }  // namespace mssm

@@ -176,6 +176,35 @@ def test_ssd_pointer_checks():
     assert _ssd_call(d, out=BASE + 16) == M.MSSM_ERR_INVALID_ARG
 
 
+def _ssd3_call(desc, x=BASE, delta=BASE + 100 * MB, lam=BASE + 150 * MB, A=BASE + 200 * MB, B=BASE + 300 * MB,
+               C=BASE + 400 * MB, out=BASE + 500 * MB):
+    return M.lib.mssm_ssd_trapezoidal_fwd(ctypes.byref(desc), x, delta, lam, A, B, C, None, None, None, out, None,
+                                          None, 0, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(io_dtype=M.MSSM_F32), M.MSSM_ERR_UNSUPPORTED),
+    (dict(headdim=24), M.MSSM_ERR_UNSUPPORTED),
+    (dict(dstate=256), M.MSSM_ERR_UNSUPPORTED),
+    (dict(batch=-2), M.MSSM_ERR_INVALID_ARG),
+])
+def test_ssd_trapezoidal_validation(kw, expect):
+    """The Mamba-3 entry point shares the SSD descriptor rules."""
+    a = dict(batch=2, seqlen=128, nheads=4, headdim=64, dstate=64, ngroups=1, chunk=64, io_dtype=M.MSSM_BF16)
+    a.update(kw)
+    assert _ssd3_call(M.ssd_desc(**a)) == expect
+
+
+def test_ssd_trapezoidal_pointer_checks():
+    d = M.ssd_desc(2, 128, 4, 64, 64, 1, 64)
+    assert _ssd3_call(d, lam=None) == M.MSSM_ERR_INVALID_ARG            # lam is required
+    assert _ssd3_call(d, lam=BASE + 150 * MB + 1) == M.MSSM_ERR_MISALIGNED
+    assert _ssd3_call(d, out=BASE + 150 * MB - 64) == M.MSSM_ERR_INVALID_ARG   # out overlaps lam
+    assert _ssd3_call(d, x=None) == M.MSSM_ERR_INVALID_ARG
+    # nothing to do: no batch rows
+    assert _ssd3_call(M.ssd_desc(0, 128, 4, 64, 64, 1, 64), lam=None) == M.MSSM_OK
+
+
 def _upd_call(desc, state=BASE + 600 * MB, x=BASE, delta=BASE + 100 * MB, A=BASE + 200 * MB, B=BASE + 300 * MB,
               C=BASE + 400 * MB, D=None, z=None, out=BASE + 500 * MB):
     return M.lib.mssm_selective_state_update(ctypes.byref(desc) if desc is not None else None, state, x, delta, A,

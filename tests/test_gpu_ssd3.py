@@ -1,0 +1,113 @@
+"""Mamba-3 SISO recurrence (exponential-trapezoidal input rule) on the GPU, through the C ABI, against the
+fp64 oracle (oracle.ssd3_fwd, a plain sequential loop).
+
+Cases cover sequences shorter than, equal to and just past one 64-step block, ragged tails, dstate 16 to
+128 (padded ones included), several groups, every optional input, the chunk argument, lam = 1 (which must
+reproduce the Mamba-2 kernel bit for bit) and the full 8 x 4096 x 32 x 64 x 128 layer."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_util import RTOL, check, dev, host64, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def M():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import selective_state_space_17_amd as m
+    return m
+
+
+def run_gpu(M, s, lam, chunk=0):
+    import torch
+    out, fin = M.ssd_trapezoidal_fwd(dev(s.x), dev(s.delta), dev(lam), dev(s.A), dev(s.B), dev(s.C), dev(s.D),
+                                     dev(s.z), dev(s.h0), chunk=chunk, return_final_state=True)
+    torch.cuda.synchronize()
+    return out, fin
+
+
+def compare(M, s, lam, what, chunk=0):
+    out, fin = run_gpu(M, s, lam, chunk)
+    ref, ref_fin = oracle.ssd3_fwd(s.x, s.delta, lam, s.A, s.B, s.C, s.D, s.z, s.h0)
+    check(host64(out), ref, RTOL["bf16"], what + " out")
+    check(host64(fin), ref_fin, RTOL["bf16"], what + " final_state")
+
+
+# (batch, seqlen, nheads, headdim, dstate, ngroups, D, z, h0)
+CASES = [
+    (1, 1, 2, 64, 16, 1, False, False, False),     # one step: no previous input at all
+    (2, 63, 4, 64, 32, 2, True, True, True),
+    (1, 64, 2, 64, 64, 1, True, False, True),      # exactly one block: the boundary term leaves the sequence
+    (2, 65, 4, 128, 64, 4, False, True, False),    # one step into the second block
+    (1, 200, 6, 64, 128, 3, True, True, True),
+    (2, 1000, 4, 64, 48, 1, True, True, True),     # padded states, many block boundaries
+    (1, 777, 2, 192, 80, 2, False, False, True),
+    (2, 300, 4, 64, 112, 2, True, True, False),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "b{}_l{}_h{}_p{}_n{}_g{}".format(*c[:6]))
+def test_ssd3_matches_oracle(M, case):
+    b, l, h, p, n, g, hd, hz, hh = case
+    cfg = W.ssd_config(b, l, h, p, n, g, cfg_id=1100 + l + n)
+    s = W.make_ssd_inputs(cfg, with_D=hd, with_z=hz, with_h0=hh)
+    lam = W.make_ssd_lam(cfg)
+    say("ssd3", case)
+    compare(M, s, lam, f"ssd3 {case}")
+
+
+@pytest.mark.parametrize("chunk", [64, 128, 256])
+def test_ssd3_chunk_argument(M, chunk):
+    cfg = W.ssd_config(2, 700, 4, 64, 64, 1, cfg_id=1201)
+    s = W.make_ssd_inputs(cfg, with_D=True, with_z=True, with_h0=True)
+    compare(M, s, W.make_ssd_lam(cfg), f"ssd3 chunk={chunk}", chunk=chunk)
+
+
+def test_ssd3_extreme_weights(M):
+    """lam at 0 (all weight on the previous input) and 1 mixed step by step."""
+    cfg = W.ssd_config(2, 333, 4, 64, 64, 2, cfg_id=1202)
+    s = W.make_ssd_inputs(cfg, with_D=True, with_z=True, with_h0=True)
+    lam = W.f32_to_bf16_bits((np.arange(2 * 333 * 4).reshape(2, 333, 4) % 3 == 0).astype(np.float32))
+    say("ssd3 lam in {0, 1}")
+    compare(M, s, lam, "ssd3 lam in {0, 1}")
+
+
+def test_ssd3_lam_one_is_mamba2_bitwise(M):
+    """With lam = 1 both step weights reduce exactly to delta, so the kernel reproduces the Mamba-2 path
+    bit for bit."""
+    import torch
+    cfg = W.ssd_config(2, 500, 4, 64, 128, 2, cfg_id=1203)
+    s = W.make_ssd_inputs(cfg, with_D=True, with_z=True, with_h0=True)
+    ones = W.f32_to_bf16_bits(np.ones((2, 500, 4), np.float32))
+    say("ssd3 lam = 1 vs ssd_fwd")
+    out3, fin3 = run_gpu(M, s, ones)
+    out2, fin2 = M.ssd_fwd(dev(s.x), dev(s.delta), dev(s.A), dev(s.B), dev(s.C), dev(s.D), dev(s.z), dev(s.h0),
+                           return_final_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out3, out2), "lam = 1 output differs from the Mamba-2 kernel"
+    assert torch.equal(fin3, fin2), "lam = 1 final state differs from the Mamba-2 kernel"
+
+
+def test_ssd3_empty_sequence(M):
+    """No steps: the final state is h0."""
+    import torch
+    cfg = W.ssd_config(2, 0, 4, 64, 64, 1, cfg_id=1204)
+    s = W.make_ssd_inputs(cfg, with_h0=True)
+    lam = W.make_ssd_lam(cfg)
+    out, fin = run_gpu(M, s, lam)
+    assert out.numel() == 0
+    assert np.array_equal(fin.cpu().numpy(), s.h0)
+
+
+def test_ssd3_full_layer(M):
+    """The 8 x 4096 x 32-head x 64 x 128 layer the benchmark times; every element against the oracle."""
+    cfg = W.CONFIGS[11]
+    s = W.make_ssd_inputs(cfg)
+    lam = W.make_ssd_lam(cfg)
+    say("ssd3 full layer", cfg.name)
+    compare(M, s, lam, cfg.name, chunk=cfg.chunk)

@@ -37,7 +37,7 @@ ROOT_SEED = 1700
 BLOCK = 1 << 22
 
 # tensor ids (fixed order of the per-tensor streams)
-T_X, T_DELTA, T_Z, T_B, T_C, T_D, T_A, T_H0, T_DOUT, T_DFIN, T_CW, T_CB, T_CI = range(13)
+T_X, T_DELTA, T_Z, T_B, T_C, T_D, T_A, T_H0, T_DOUT, T_DFIN, T_CW, T_CB, T_CI, T_LAM = range(14)
 
 F32 = "f32"
 BF16 = "bf16"
@@ -112,6 +112,7 @@ class SSDConfig:
     has_z: bool = False
     return_final: bool = True
     decode: bool = False    # token-by-token update of a stored state (read and written in place)
+    trapezoidal: bool = False   # Mamba-3 exponential-trapezoidal input rule (one more [B, L, H] input, lam)
 
     @property
     def updates(self) -> int:
@@ -122,6 +123,7 @@ class SSDConfig:
         blhp = self.batch * self.seqlen * self.nheads * self.headdim
         n = blhp * e                                            # x
         n += self.batch * self.seqlen * self.nheads * e         # delta
+        n += self.batch * self.seqlen * self.nheads * e if self.trapezoidal else 0   # lam
         n += 2 * self.batch * self.seqlen * self.ngroups * self.dstate * e  # B, C
         n += self.nheads * 4                                    # A
         n += self.nheads * 4 if self.has_D else 0
@@ -152,6 +154,9 @@ CONFIGS = {
     # decode steps (one new token against a stored state), the configs' layer shapes at serving batch sizes
     6: ScanConfig("mamba1_2p8b_decode_bf16", 6, 256, 1, 5120, 16, BF16, "s4d_real", return_final=True, decode=True),
     7: SSDConfig("mamba2_decode_bf16", 7, 64, 1, 32, 64, 128, 1, 64, BF16, True, True, True, decode=True),
+    # the Mamba-3 SISO recurrence (exponential-trapezoidal input rule) at config 4's shape: SISO keeps
+    # Mamba-2's dimensions and state size
+    11: SSDConfig("mamba3_siso_bf16", 11, 8, 4096, 32, 64, 128, 1, 256, trapezoidal=True),
 }
 
 
@@ -339,6 +344,20 @@ def make_ssd_inputs(cfg: SSDConfig, seed_base: int = ROOT_SEED, with_D: Optional
     z = normal(cid, T_Z, b * l * h * p, cfg.io, seed_base).reshape(b, l, h, p) if with_z else None
     h0 = normal_f32(cid, T_H0, b * h * p * n, seed_base).reshape(b, h, p, n) if with_h0 else None
     return SSDInputs(x, delta, A, Bm, Cm, D, z, h0, cfg.io)
+
+
+def make_ssd_lam(cfg: SSDConfig, seed_base: int = ROOT_SEED) -> np.ndarray:
+    """The Mamba-3 trapezoidal weight lam [B, L, H]: sigmoid of N(0, 1), as a gate computed from the token
+    would give (values in (0, 1), most near 1/2), stored in io dtype."""
+    n = cfg.batch * cfg.seqlen * cfg.nheads
+    out = _alloc(n, cfg.io)
+
+    def fill(j, s, e):
+        v = _stream(cfg.cfg_id, T_LAM, j, seed_base).standard_normal(e - s, dtype=np.float32)
+        _store(out, s, e, (1.0 / (1.0 + np.exp(-v))).astype(np.float32))
+
+    _for_blocks(n, fill)
+    return out.reshape(cfg.batch, cfg.seqlen, cfg.nheads)
 
 
 def scan_config(batch: int, seqlen: int, dim: int, dstate: int, io: str = F32, a_kind: str = "s4d_real",

@@ -156,7 +156,7 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
   __shared__ __attribute__((aligned(16))) float css[QB];              // inclusive sum of delta * A * log2 e
   __shared__ __attribute__((aligned(16))) float dls[QB];              // weight of x_s at later steps: delta_s
                                                                       // (TRAP: lam_s delta_s + (1 - lam_{s+1}) delta_{s+1})
-  __shared__ __attribute__((aligned(16))) float dgs[TRAP ? QB : 1];   // TRAP: weight of x_s at step s, lam_s delta_s
+  __shared__ __attribute__((aligned(16))) float2 ctw[TRAP ? QB : 1];  // TRAP: {css_t, lam_t delta_t} (weight of x_t at t)
   __shared__ __attribute__((aligned(16))) float wls[QB];              // exp2(s_Q - s_s) * dls_s
 
   const int tid = threadIdx.x;
@@ -367,7 +367,7 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
         const float lm = lane < nvalid ? __uint_as_float(static_cast<uint32_t>(lreg) << 16) : 0.f;
         const float dn = next_ok ? __uint_as_float(static_cast<uint32_t>(dnreg) << 16) : 0.f;
         const float ln = next_ok ? __uint_as_float(static_cast<uint32_t>(lnreg) << 16) : 0.f;
-        dgs[lane] = lm * d;
+        ctw[lane] = float2{v, lm * d};
         wo = __builtin_fmaf(1.f - ln, dn, lm * d);
       }
       dls[lane] = wo;
@@ -383,6 +383,17 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
       *reinterpret_cast<u32x4*>(yg + (t0 + y_r) * x_row + y_c) = *reinterpret_cast<const u32x4*>(&Ys[buf][y_r * QS + y_c]);
   };
 
+  // TRAP: in a diagonal tile, element v of a lane sits on s == t iff v == lc - lq; a 0/1 float per
+  // element (fixed per lane) selects it by an exact FMA, so no lane masks have to stay live
+  float dsel[4] = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (TRAP) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      dsel[v] = (lc - lq == v) ? 1.f : 0.f;
+      asm volatile("" : "+v"(dsel[v]));
+    }
+  }
+
   // G^T tile (s-tile i, t-tile j) -> M[t][kpos(s)] hi/lo, 4 consecutive s per lane (8-byte writes)
   auto mask_tile = [&](int i, int j) {
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -391,17 +402,22 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
       acc = mfma16(frag(&Bs[(16 * i + lc) * NS + k0 + l8]), frag(&Cs[(16 * j + lc) * NS + k0 + l8]), acc);
     const int t = 16 * j + lc;
     const int s0 = 16 * i + lq;
-    const float ct = css[t];
+    float ct, dg_t = 0.f;
+    if constexpr (TRAP) {
+      const float2 cw = ctw[t];
+      ct = cw.x;
+      dg_t = cw.y;
+    } else {
+      ct = css[t];
+    }
     const float4 cs4 = *reinterpret_cast<const float4*>(&css[s0]);
     const float4 dl4 = *reinterpret_cast<const float4*>(&dls[s0]);
     float m[4] = {acc[0] * exp2_hw(ct - cs4.x) * dl4.x, acc[1] * exp2_hw(ct - cs4.y) * dl4.y,
                   acc[2] * exp2_hw(ct - cs4.z) * dl4.z, acc[3] * exp2_hw(ct - cs4.w) * dl4.w};
     if (i == j) {
       if constexpr (TRAP) {   // on the diagonal (s == t, decay 1) only the step's own weight applies
-        const float4 dg4 = *reinterpret_cast<const float4*>(&dgs[s0]);
-        const float dg[4] = {dg4.x, dg4.y, dg4.z, dg4.w};
 #pragma unroll
-        for (int v = 0; v < 4; ++v) m[v] = (s0 + v == t) ? acc[v] * dg[v] : m[v];
+        for (int v = 0; v < 4; ++v) m[v] = __builtin_fmaf(dsel[v], __builtin_fmaf(acc[v], dg_t, -m[v]), m[v]);
       }
 #pragma unroll
       for (int v = 0; v < 4; ++v) m[v] = (s0 + v <= t) ? m[v] : 0.f;

@@ -451,6 +451,34 @@ def pin_ssd3_bruteforce(lib, seed=17):
     _close(fin, want_fin, 1e-11, "Mamba-3 brute-force final state")
 
 
+def ssd3_resume_state(fin, delta, lam, B, x, L1, H, G):
+    """The state to resume a Mamba-3 sequence at step L1 from the state after step L1-1: that state plus
+    the left-end term of step L1, (1 - lam_{L1}) delta_{L1} x_{L1-1} (x) B_{L1-1} (fp64)."""
+    hpg = H // G
+    d = delta[:, L1].astype(np.float64)                                   # [b, H]
+    w = (1.0 - lam[:, L1].astype(np.float64)) * d                         # [b, H]
+    xp = x[:, L1 - 1].astype(np.float64)                                  # [b, H, P]
+    Bp = B[:, L1 - 1].astype(np.float64)[:, np.arange(H) // hpg]          # [b, H, N]
+    return fin + w[:, :, None, None] * xp[:, :, :, None] * Bp[:, :, None, :]
+
+
+def pin_ssd3_resume(lib, seed=18):
+    """Splitting a sequence at L1 and resuming from the first part's final state plus the boundary's
+    left-end term reproduces the whole run (the header's stated way to continue a sequence)."""
+    rng = _rng(seed)
+    x, delta, lam, A, B, C, D, z, h0 = _ssd3_case(rng, L=45)
+    L1 = 17
+    H, G = x.shape[2], B.shape[2]
+    full, fin = oracle.ssd3_fwd(x, delta, lam, A, B, C, D, z, h0, lib=lib)
+    _, mid = oracle.ssd3_fwd(x[:, :L1], delta[:, :L1], lam[:, :L1], A, B[:, :L1], C[:, :L1], D, z[:, :L1], h0,
+                             lib=lib)
+    h1 = ssd3_resume_state(mid, delta, lam, B, x, L1, H, G)
+    tail, fin2 = oracle.ssd3_fwd(x[:, L1:], delta[:, L1:], lam[:, L1:], A, B[:, L1:], C[:, L1:], D, z[:, L1:],
+                                 h1.astype(np.float32), lib=lib)
+    _close(tail, full[:, L1:], 1e-6, "Mamba-3 resumed output")
+    _close(fin2, fin, 1e-6, "Mamba-3 resumed final state")
+
+
 # ---------------------------------------------------------------------------
 # Gradients of the Mamba-1 scan
 # ---------------------------------------------------------------------------
@@ -603,7 +631,7 @@ def pin_conv_scan_composition(lib, seed=34):
 SCAN_PINS = [pin_lti_convolution, pin_delta_zero, pin_geometric, pin_bruteforce, pin_chaining, pin_reset,
              pin_linearity_causality, pin_gate_skip, pin_bf16_codec]
 SSD_PINS = [pin_ssd_equals_broadcast_scan, pin_ssd_geometric, pin_ssd_bruteforce, pin_ssd_chaining]
-SSD3_PINS = [pin_ssd3_lam_one_is_ssd, pin_ssd3_trapezoid_order, pin_ssd3_bruteforce]
+SSD3_PINS = [pin_ssd3_lam_one_is_ssd, pin_ssd3_trapezoid_order, pin_ssd3_bruteforce, pin_ssd3_resume]
 BWD_PINS = [pin_scan_bwd_finite_differences, pin_scan_bwd_linear_in_upstream]
 CONV_PINS = [pin_conv_numpy, pin_conv_impulse, pin_conv_chaining, pin_conv_scan_composition]
 ALL_PINS = SCAN_PINS + SSD_PINS + SSD3_PINS + BWD_PINS + CONV_PINS

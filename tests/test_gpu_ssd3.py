@@ -93,6 +93,32 @@ def test_ssd3_lam_one_is_mamba2_bitwise(M):
     assert torch.equal(fin3, fin2), "lam = 1 final state differs from the Mamba-2 kernel"
 
 
+def test_ssd3_resume(M):
+    """A sequence split at a step inside a block and resumed from the first call's final state plus the
+    boundary's left-end term (as the header states) reproduces the whole run."""
+    import torch
+    from pins import ssd3_resume_state
+    cfg = W.ssd_config(2, 400, 4, 64, 64, 2, cfg_id=1205)
+    s = W.make_ssd_inputs(cfg, with_D=True, with_z=True, with_h0=True)
+    lam = W.make_ssd_lam(cfg)
+    L1 = 150
+    say("ssd3 resume at", L1)
+    full, fin = run_gpu(M, s, lam)
+    g = [dev(a) for a in (s.x, s.delta, lam, s.B, s.C, s.z)]
+    _, mid = M.ssd_trapezoidal_fwd(g[0][:, :L1].contiguous(), g[1][:, :L1].contiguous(), g[2][:, :L1].contiguous(),
+                                   dev(s.A), g[3][:, :L1].contiguous(), g[4][:, :L1].contiguous(), dev(s.D),
+                                   g[5][:, :L1].contiguous(), dev(s.h0), return_final_state=True)
+    torch.cuda.synchronize()
+    xs, ds, ls, Bs = (W.bf16_bits_to_f32(a) for a in (s.x, s.delta, lam, s.B))
+    h1 = ssd3_resume_state(host64(mid), ds, ls, Bs, xs, L1, 4, 2).astype(np.float32)
+    tail, fin2 = M.ssd_trapezoidal_fwd(g[0][:, L1:].contiguous(), g[1][:, L1:].contiguous(), g[2][:, L1:].contiguous(),
+                                       dev(s.A), g[3][:, L1:].contiguous(), g[4][:, L1:].contiguous(), dev(s.D),
+                                       g[5][:, L1:].contiguous(), dev(h1), return_final_state=True)
+    torch.cuda.synchronize()
+    check(host64(tail), host64(full)[:, L1:], 2e-2, "ssd3 resumed tail")
+    check(host64(fin2), host64(fin), 2e-2, "ssd3 resumed final state")
+
+
 def test_ssd3_empty_sequence(M):
     """No steps: the final state is h0."""
     import torch

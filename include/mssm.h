@@ -218,6 +218,26 @@ int mssm_ssd_state_update(const mssm_ssd_desc* desc, float* state,
                           const void* B, const void* C, const float* D, const void* z,
                           void* out, void* stream);
 
+/* Token-by-token state update under the Mamba-3 SISO rule (see
+ * mssm_ssd_trapezoidal_fwd; "Mamba-3" blog, "El modelo Mamba-3" item 1, and
+ * the decode latency it is designed for, "Kernels por todas partes").  Each
+ * step needs the previous token's x and B besides the state:
+ *   x_prev : [batch, nheads, headdim] (io_dtype), nullable
+ *   B_prev : [batch, ngroups, dstate] (io_dtype), nullable
+ * the token before the first of the seqlen new ones (NULL: there is none, as
+ * at the start of a sequence; both or either may be NULL and then count as
+ * zero).  Within the call each token's left-end term uses the token before
+ * it.  They are read only: to step again, pass this call's last x and B.
+ *   lam    : [batch, seqlen, nheads] (io_dtype), required.
+ * Equals mssm_ssd_trapezoidal_fwd with h0 = state + (1 - lam_0) * delta_0 *
+ * x_prev (x) B_prev and final_state written to state, up to rounding.  Other
+ * arguments, shapes and rules as mssm_ssd_state_update. */
+int mssm_ssd_trapezoidal_state_update(const mssm_ssd_desc* desc, float* state,
+                                      const void* x_prev, const void* B_prev,
+                                      const void* x, const void* delta, const void* lam,
+                                      const float* A, const void* B, const void* C,
+                                      const float* D, const void* z, void* out, void* stream);
+
 /* Selective scan with the short causal convolution + SiLU that precedes it in
  * the Mamba-1/2 block fused in front ("Mamba-3" blog, "Arquitectura": the
  * block's short causal convolution on the state input, which Mamba-3 drops).

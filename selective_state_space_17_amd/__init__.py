@@ -49,6 +49,7 @@ SIGNATURES = {
     "mssm_ssd_trapezoidal_fwd": (_I, [ctypes.POINTER(SSDDesc)] + [_P] * 11 + [_P, _SZ, _P]),
     "mssm_selective_state_update": (_I, [ctypes.POINTER(ScanDesc)] + [_P] * 10),
     "mssm_ssd_state_update": (_I, [ctypes.POINTER(SSDDesc)] + [_P] * 10),
+    "mssm_ssd_trapezoidal_state_update": (_I, [ctypes.POINTER(SSDDesc)] + [_P] * 13),
     "mssm_selective_state_update_conv": (_I, [ctypes.POINTER(ScanDesc), ctypes.c_int32] + [_P] * 13),
     "mssm_selective_scan_conv_fwd": (_I, [ctypes.POINTER(ScanDesc), ctypes.c_int32] + [_P] * 13 + [_P, _SZ, _P]),
     "mssm_selective_scan_conv_workspace_size": (_SZ, [ctypes.POINTER(ScanDesc)]),
@@ -514,6 +515,22 @@ def ssd_state_update(state, x, delta, A, B, C, D=None, z=None, out=None, stream=
     delta: [batch, seqlen, nheads]; B, C: [batch, seqlen, ngroups, dstate]; A, D: [nheads].
     Returns out [batch, seqlen, nheads, headdim].
     """
+    return _ssd_update_call("mssm_ssd_state_update", state, None, None, x, delta, None, A, B, C, D, z, out, stream)
+
+
+def ssd_trapezoidal_state_update(state, x, delta, lam, A, B, C, D=None, z=None, x_prev=None, B_prev=None,
+                                 out=None, stream=None):
+    """Advance a multi-head state by seqlen tokens in place under the Mamba-3 SISO rule
+    (mssm_ssd_trapezoidal_state_update).
+
+    As ``ssd_state_update`` plus lam [batch, seqlen, nheads] and the previous token's x_prev
+    [batch, nheads, headdim] and B_prev [batch, ngroups, dstate] (None: no previous token).
+    """
+    return _ssd_update_call("mssm_ssd_trapezoidal_state_update", state, x_prev, B_prev, x, delta, lam, A, B, C, D,
+                            z, out, stream)
+
+
+def _ssd_update_call(fn, state, x_prev, B_prev, x, delta, lam, A, B, C, D, z, out, stream):
     torch = _torch()
     if x.dim() != 4:
         raise ValueError("x must be [batch, seqlen, nheads, headdim]")
@@ -522,8 +539,12 @@ def ssd_state_update(state, x, delta, A, B, C, D=None, z=None, out=None, stream=
         raise ValueError("B must be [batch, seqlen, ngroups, dstate]")
     G, N = B.shape[2], B.shape[3]
     io = _io_code(x.dtype)
+    trap = fn == "mssm_ssd_trapezoidal_state_update"
+    if trap and lam is None:
+        raise ValueError("lam is required")
     for name, t, shape in (("x", x, (bsz, L, H, P)), ("z", z, (bsz, L, H, P)), ("delta", delta, (bsz, L, H)),
-                           ("B", B, (bsz, L, G, N)), ("C", C, (bsz, L, G, N))):
+                           ("lam", lam, (bsz, L, H)), ("B", B, (bsz, L, G, N)), ("C", C, (bsz, L, G, N)),
+                           ("x_prev", x_prev, (bsz, H, P)), ("B_prev", B_prev, (bsz, G, N))):
         _check_gpu(name, t, x.dtype, shape)
     _check_gpu("A", A, torch.float32, (H,))
     _check_gpu("D", D, torch.float32, (H,))
@@ -532,8 +553,13 @@ def ssd_state_update(state, x, delta, A, B, C, D=None, z=None, out=None, stream=
         out = torch.empty_like(x)
     _check_gpu("out", out, x.dtype, (bsz, L, H, P))
     d = ssd_desc(bsz, L, H, P, N, G, 0, io)
-    st = lib.mssm_ssd_state_update(ctypes.byref(d), _ptr(state), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
-                                   _ptr(D), _ptr(z), _ptr(out), _stream_handle(stream))
+    if trap:
+        st = lib.mssm_ssd_trapezoidal_state_update(ctypes.byref(d), _ptr(state), _ptr(x_prev), _ptr(B_prev), _ptr(x),
+                                                   _ptr(delta), _ptr(lam), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                                   _ptr(z), _ptr(out), _stream_handle(stream))
+    else:
+        st = lib.mssm_ssd_state_update(ctypes.byref(d), _ptr(state), _ptr(x), _ptr(delta), _ptr(A), _ptr(B),
+                                       _ptr(C), _ptr(D), _ptr(z), _ptr(out), _stream_handle(stream))
     if st != MSSM_OK:
-        raise MssmError(st, "mssm_ssd_state_update")
+        raise MssmError(st, fn)
     return out

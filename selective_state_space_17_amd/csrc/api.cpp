@@ -324,9 +324,13 @@ int mssm_selective_state_update_conv(const mssm_scan_desc* desc, int32_t conv_wi
   return MSSM_OK;
 }
 
-int mssm_ssd_state_update(const mssm_ssd_desc* desc, float* state, const void* x, const void* delta,
-                          const float* A, const void* B, const void* C, const float* D, const void* z, void* out,
-                          void* stream) {
+}  // extern "C"
+
+namespace {
+// both multi-head decode rules: lam == nullptr (want_lam false) is the Mamba-2 rule
+int ssd_update_impl(const mssm_ssd_desc* desc, float* state, const void* x_prev, const void* B_prev,
+                    const void* x, const void* delta, const void* lam, bool want_lam, const float* A,
+                    const void* B, const void* C, const float* D, const void* z, void* out, void* stream) {
   const mssm_ssd_desc* d = desc;
   if (d == nullptr) return MSSM_ERR_INVALID_ARG;
   if (d->batch < 0 || d->seqlen < 0 || d->nheads <= 0 || d->headdim <= 0 || d->dstate <= 0 || d->ngroups <= 0)
@@ -349,13 +353,17 @@ int mssm_ssd_state_update(const mssm_ssd_desc* desc, float* state, const void* x
   if (state == nullptr || A == nullptr || x == nullptr || delta == nullptr || B == nullptr || C == nullptr ||
       out == nullptr)
     return MSSM_ERR_INVALID_ARG;
+  if (want_lam && lam == nullptr) return MSSM_ERR_INVALID_ARG;
   if (!aligned(x, es) || !aligned(delta, es) || !aligned(B, es) || !aligned(C, es) || !aligned(z, es) ||
-      !aligned(out, es) || !aligned(A, 4) || !aligned(D, 4) || !aligned(state, 4))
+      !aligned(out, es) || !aligned(A, 4) || !aligned(D, 4) || !aligned(state, 4) || !aligned(lam, es) ||
+      !aligned(x_prev, es) || !aligned(B_prev, es))
     return MSSM_ERR_MISALIGNED;
   const int64_t b_io = n_x * es, b_st = n_st * 4;
-  const void* ins[] = {x, delta, B, C, z, A, D};
-  const int64_t inb[] = {b_io, n_d * es, n_bc * es, n_bc * es, b_io, d->nheads * 4, d->nheads * 4};
-  for (int i = 0; i < 7; ++i) {
+  const int64_t b_xp = d->batch * d->nheads * d->headdim * es, b_bp = d->batch * d->ngroups * d->dstate * es;
+  const void* ins[] = {x, delta, B, C, z, A, D, lam, x_prev, B_prev};
+  const int64_t inb[] = {b_io, n_d * es, n_bc * es, n_bc * es, b_io, d->nheads * 4, d->nheads * 4, n_d * es,
+                         b_xp, b_bp};
+  for (int i = 0; i < 10; ++i) {
     if (overlap(out, b_io, ins[i], inb[i])) return MSSM_ERR_INVALID_ARG;
     if (overlap(state, b_st, ins[i], inb[i])) return MSSM_ERR_INVALID_ARG;
   }
@@ -366,12 +374,31 @@ int mssm_ssd_state_update(const mssm_ssd_desc* desc, float* state, const void* x
   a.state = state; a.x = x; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.out = out;
   a.batch = d->batch; a.L = d->seqlen; a.N = d->dstate;
   a.H = d->nheads; a.P = d->headdim; a.G = d->ngroups; a.io = d->io_dtype;
+  if (want_lam) {
+    a.lam = lam; a.x_prev = x_prev; a.B_prev = B_prev;
+  }
   const hipError_t e = mssm::ssd_update_launch(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     set_err(e);
     return MSSM_ERR_HIP;
   }
   return MSSM_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int mssm_ssd_state_update(const mssm_ssd_desc* desc, float* state, const void* x, const void* delta,
+                          const float* A, const void* B, const void* C, const float* D, const void* z, void* out,
+                          void* stream) {
+  return ssd_update_impl(desc, state, nullptr, nullptr, x, delta, nullptr, false, A, B, C, D, z, out, stream);
+}
+
+int mssm_ssd_trapezoidal_state_update(const mssm_ssd_desc* desc, float* state, const void* x_prev,
+                                      const void* B_prev, const void* x, const void* delta, const void* lam,
+                                      const float* A, const void* B, const void* C, const float* D, const void* z,
+                                      void* out, void* stream) {
+  return ssd_update_impl(desc, state, x_prev, B_prev, x, delta, lam, true, A, B, C, D, z, out, stream);
 }
 
 // --------------------------------------------------------------------------

@@ -11,6 +11,9 @@
 //   Mamba-2 multi-head, per (b, h, p, n) with scalar A[h] and group g(h):
 //                            S <- exp(delta A[h]) S + delta B[g,n] x[p]
 //                            y[p] = sum_n C[g,n] S + D[h] x[p],  out = y * silu(z)
+//   Mamba-3 SISO rule (TRAP; "Mamba-3" blog, "El modelo Mamba-3" item 1), with a = exp(delta A[h]):
+//                            S <- a S + (1 - lam) delta a B_prev[g,n] x_prev[p] + lam delta B[g,n] x[p]
+//   where x_prev, B_prev are the previous token's (given for the first new token; zero if absent).
 // The work per token is a few operations per byte of state, so the kernels
 // are bound by HBM: one thread owns 4 consecutive states of one row (one
 // 16-byte load and store when the layout allows), a row's threads are
@@ -133,6 +136,10 @@ struct UpdParams {
   const float* conv_b;     // [dim], nullable
   void* conv_state;        // [batch, conv_width - 1, dim] (io dtype), read and advanced in place
   int conv_width;
+  // multi-head form with the Mamba-3 exponential-trapezoidal rule (TRAP)
+  const void* lam;         // [batch, L, H]
+  const void* x_prev;      // [batch, H, P], nullable
+  const void* B_prev;      // [batch, G, N], nullable
 };
 
 // Each thread owns S states (4, or 8 when dstate allows: two 16-byte loads
@@ -240,7 +247,7 @@ __global__ __launch_bounds__(kThreads) void scan_update_kernel(UpdParams p) {
 }
 
 // multi-head form: row = (b, h, p), state [batch, H, P, N]
-template <typename T, bool VEC, int S>
+template <typename T, bool VEC, int S, bool TRAP>
 __global__ __launch_bounds__(kThreads) void ssd_update_kernel(UpdParams p) {
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
   const int64_t row0 = gid / p.lpr;
@@ -258,6 +265,7 @@ __global__ __launch_bounds__(kThreads) void ssd_update_kernel(UpdParams p) {
   bool live[R];
   int64_t rr[R], pp[R], hd[R], bb[R], gg[R];
   float h[R][S], a2[R], Dh[R];
+  float up[R], bp[R][S];   // TRAP: the previous token's x (this row) and B (this lane's states)
 #pragma unroll
   for (int k = 0; k < R; ++k) {
     const int64_t row = row0 + k * rstride;
@@ -271,13 +279,24 @@ __global__ __launch_bounds__(kThreads) void ssd_update_kernel(UpdParams p) {
     loadS<S, VEC>(p.state + rr[k] * N, n0, N, h[k]);
     a2[k] = p.A[hd[k]] * kLog2e;
     Dh[k] = p.D != nullptr ? p.D[hd[k]] : 0.f;
+    if constexpr (TRAP) {
+      up[k] = p.x_prev != nullptr ? to_f32(static_cast<const T*>(p.x_prev)[rr[k]]) : 0.f;   // rows are (b, h, p)
+      if (p.B_prev != nullptr) {
+        loadSio<T, S, VEC>(static_cast<const T*>(p.B_prev) + (bb[k] * G + gg[k]) * N, n0, N, bp[k]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < S; ++q) bp[k][q] = 0.f;
+      }
+    }
   }
+  const T* lam = static_cast<const T*>(p.lam);
   for (int64_t t = 0; t < L; ++t) {
-    float d[R], u[R], zz[R], bv[R][S], cv[R][S];
+    float d[R], u[R], zz[R], lm[R], bv[R][S], cv[R][S];
 #pragma unroll
     for (int k = 0; k < R; ++k) {
       const int64_t obh = (bb[k] * L + t) * H + hd[k];
       d[k] = to_f32(delta[obh]);
+      if constexpr (TRAP) lm[k] = to_f32(lam[obh]);
       u[k] = to_f32(x[obh * P + pp[k]]);
       zz[k] = z != nullptr ? to_f32(z[obh * P + pp[k]]) : 0.f;
       loadSio<T, S, VEC>(Bm + ((bb[k] * L + t) * G + gg[k]) * N, n0, N, bv[k]);
@@ -287,10 +306,22 @@ __global__ __launch_bounds__(kThreads) void ssd_update_kernel(UpdParams p) {
     for (int k = 0; k < R; ++k) {
       const float dA = exp2_hw(d[k] * a2[k]), du = d[k] * u[k];
       float acc = 0.f;
+      if constexpr (TRAP) {
+        // a (S + (1 - lam) d x_prev B_prev) + lam d x B
+        const float wl = (1.f - lm[k]) * d[k] * up[k], wr = lm[k] * du;
 #pragma unroll
-      for (int q = 0; q < S; ++q) {
-        h[k][q] = __builtin_fmaf(dA, h[k][q], du * bv[k][q]);
-        acc = __builtin_fmaf(cv[k][q], h[k][q], acc);
+        for (int q = 0; q < S; ++q) {
+          h[k][q] = __builtin_fmaf(dA, __builtin_fmaf(wl, bp[k][q], h[k][q]), wr * bv[k][q]);
+          acc = __builtin_fmaf(cv[k][q], h[k][q], acc);
+          bp[k][q] = bv[k][q];
+        }
+        up[k] = u[k];
+      } else {
+#pragma unroll
+        for (int q = 0; q < S; ++q) {
+          h[k][q] = __builtin_fmaf(dA, h[k][q], du * bv[k][q]);
+          acc = __builtin_fmaf(cv[k][q], h[k][q], acc);
+        }
       }
       acc = group_sum(acc, p.lpr);
       if (live[k] && n0 == 0) {
@@ -323,7 +354,8 @@ UpdParams common(const UpdateArgs& a) {
 bool vec_ok(const UpdateArgs& a, bool mamba1, int S) {
   auto al = [](const void* q, uintptr_t m) { return (reinterpret_cast<uintptr_t>(q) & (m - 1)) == 0; };
   const uintptr_t bc = a.io == 1 ? 8 : 16;
-  return a.N % S == 0 && al(a.state, 16) && (!mamba1 || al(a.A, 16)) && al(a.B, bc) && al(a.C, bc);
+  return a.N % S == 0 && al(a.state, 16) && (!mamba1 || al(a.A, 16)) && al(a.B, bc) && al(a.C, bc) &&
+         (a.B_prev == nullptr || al(a.B_prev, bc));
 }
 
 int64_t grid_blocks(int64_t rows, int64_t N, int S) {
@@ -350,7 +382,8 @@ hipError_t launch_update(UpdParams p, const UpdateArgs& a, bool mamba1, hipStrea
 }
 template <typename T, bool VEC, int S> struct ScanUpd { static constexpr auto fn = scan_update_kernel<T, VEC, S, false>; };
 template <typename T, bool VEC, int S> struct ScanUpdConv { static constexpr auto fn = scan_update_kernel<T, VEC, S, true>; };
-template <typename T, bool VEC, int S> struct SsdUpd { static constexpr auto fn = ssd_update_kernel<T, VEC, S>; };
+template <typename T, bool VEC, int S> struct SsdUpd { static constexpr auto fn = ssd_update_kernel<T, VEC, S, false>; };
+template <typename T, bool VEC, int S> struct SsdUpdTrap { static constexpr auto fn = ssd_update_kernel<T, VEC, S, true>; };
 
 }  // namespace
 
@@ -371,6 +404,11 @@ hipError_t ssd_update_launch(const UpdateArgs& a, hipStream_t stream) {
   UpdParams p = common(a);
   p.H = a.H; p.P = a.P; p.G = a.G;
   p.rows = a.batch * a.H * a.P;
+  if (a.lam != nullptr) {
+    p.lam = a.lam; p.x_prev = a.x_prev; p.B_prev = a.B_prev;
+    return a.io == 1 ? launch_update<SsdUpdTrap, uint16_t>(p, a, false, stream)
+                     : launch_update<SsdUpdTrap, float>(p, a, false, stream);
+  }
   return a.io == 1 ? launch_update<SsdUpd, uint16_t>(p, a, false, stream)
                    : launch_update<SsdUpd, float>(p, a, false, stream);
 }

@@ -98,6 +98,10 @@ struct UpdateArgs {
   const float* conv_b = nullptr;   // [dim], nullable
   void* conv_state = nullptr;      // [batch, conv_width - 1, dim], read and advanced in place
   int conv_width = 0;
+  // multi-head form only: the Mamba-3 exponential-trapezoidal rule
+  const void* lam = nullptr;       // [batch, L, H]; nullable = the Mamba-2 rule
+  const void* x_prev = nullptr;    // [batch, H, P], the token before the first one; nullable = none
+  const void* B_prev = nullptr;    // [batch, G, N], likewise
 };
 
 hipError_t scan_update_launch(const UpdateArgs& a, hipStream_t stream);

@@ -841,7 +841,6 @@ __global__ __launch_bounds__(kThreads) void wide_kernel(KernelParams p) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) ux[q] = to_f32(xv0[q]);
     }
-    const T* xv = reinterpret_cast<const T*>(&xr);
     const T* dv = reinterpret_cast<const T*>(&dr);
     const T* zv = reinterpret_cast<const T*>(&zr);
     const T* bv = reinterpret_cast<const T*>(&br);

@@ -284,6 +284,31 @@ def test_ssd_state_update_pointer_checks():
     assert call(bad) == M.MSSM_ERR_INVALID_ARG              # out aliases state
 
 
+def test_ssd_trapezoidal_state_update_checks():
+    """The Mamba-3 decode step: the SSD update's rules, plus lam required and the previous token's x and B
+    optional, aligned and not overlapping the outputs."""
+    d = M.ssd_desc(2, 1, 4, 64, 64, 1, 0)
+    # state, x_prev, B_prev, x, delta, lam, A, B, C, D, z, out
+    args = [BASE + 600 * MB, BASE + 700 * MB, BASE + 800 * MB, BASE, BASE + 100 * MB, BASE + 150 * MB,
+            BASE + 200 * MB, BASE + 300 * MB, BASE + 400 * MB, None, None, BASE + 500 * MB]
+    call = lambda a, dd=d: M.lib.mssm_ssd_trapezoidal_state_update(ctypes.byref(dd), *a, None)
+    bad = list(args); bad[5] = None
+    assert call(bad) == M.MSSM_ERR_INVALID_ARG              # lam missing
+    bad = list(args); bad[2] = BASE + 800 * MB + 1
+    assert call(bad) == M.MSSM_ERR_MISALIGNED               # B_prev misaligned
+    bad = list(args); bad[11] = BASE + 700 * MB
+    assert call(bad) == M.MSSM_ERR_INVALID_ARG              # out overlaps x_prev
+    bad = list(args); bad[0] = BASE + 800 * MB
+    assert call(bad) == M.MSSM_ERR_INVALID_ARG              # state overlaps B_prev
+    for kw, expect in ((dict(dstate=300), M.MSSM_ERR_UNSUPPORTED), (dict(batch=-1), M.MSSM_ERR_INVALID_ARG)):
+        a = dict(batch=2, seqlen=1, nheads=4, headdim=64, dstate=64, ngroups=1, chunk=0, io_dtype=M.MSSM_BF16)
+        a.update(kw)
+        assert call(args, M.ssd_desc(**a)) == expect
+    # no tokens: nothing to do, null pointers allowed
+    s = M.ssd_desc(2, 0, 4, 64, 64, 1, 0)
+    assert call([None] * 12, s) == M.MSSM_OK
+
+
 def _bwd_call(desc, ws=BASE + 2000 * MB, ws_bytes=None, **kw):
     a = dict(x=BASE, delta=BASE + 100 * MB, A=BASE + 200 * MB, B=BASE + 300 * MB, C=BASE + 400 * MB, D=None,
              z=None, h0=None, dout=BASE + 500 * MB, dfinal=None, dx=BASE + 600 * MB, ddelta=BASE + 700 * MB,

@@ -137,3 +137,80 @@ def test_ssd3_full_layer(M):
     lam = W.make_ssd_lam(cfg)
     say("ssd3 full layer", cfg.name)
     compare(M, s, lam, cfg.name, chunk=cfg.chunk)
+
+
+# ---- decode: mssm_ssd_trapezoidal_state_update ----
+# (batch, seqlen, nheads, headdim, dstate, ngroups, io, D, z)
+DECODE_CASES = [
+    (2, 24, 4, 64, 128, 1, "bf16", True, True),    # 8 states per lane
+    (3, 17, 4, 32, 64, 2, "f32", True, False),
+    (1, 9, 2, 16, 20, 1, "bf16", False, True),     # dstate 20: the scalar path
+    (2, 12, 6, 8, 48, 3, "f32", False, False),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: "b{}_l{}_h{}_p{}_n{}_g{}_{}".format(*c[:7]))
+def test_ssd3_decode_token_by_token(M, case):
+    """Stepping one token at a time, each call given the previous token's x and B (none for the first),
+    reproduces the sequence oracle's outputs and final state."""
+    import torch
+    b, l, h, p, n, g, io, hd, hz = case
+    cfg = W.ssd_config(b, l, h, p, n, g, io=io, cfg_id=1300 + l + n)
+    s = W.make_ssd_inputs(cfg, with_D=hd, with_z=hz, with_h0=True)
+    lam = W.make_ssd_lam(cfg)
+    say("ssd3 decode", case)
+    ref, ref_fin = oracle.ssd3_fwd(s.x, s.delta, lam, s.A, s.B, s.C, s.D, s.z, s.h0)
+    x, dl, lm, Bm, Cm, z = (dev(a) for a in (s.x, s.delta, lam, s.B, s.C, s.z))
+    A, D = dev(s.A), dev(s.D)
+    state = dev(s.h0).clone()
+    outs = []
+    for t in range(l):
+        sl = lambda v: None if v is None else v[:, t:t + 1].contiguous()
+        outs.append(M.ssd_trapezoidal_state_update(
+            state, sl(x), sl(dl), sl(lm), A, sl(Bm), sl(Cm), D, sl(z),
+            x_prev=x[:, t - 1].contiguous() if t else None, B_prev=Bm[:, t - 1].contiguous() if t else None))
+    torch.cuda.synchronize()
+    got = np.concatenate([host64(o) for o in outs], axis=1)
+    check(got, ref, RTOL[io], f"ssd3 decode {case} out")
+    check(host64(state), ref_fin, RTOL[io], f"ssd3 decode {case} state")
+
+
+def test_ssd3_decode_several_tokens_from_previous(M):
+    """One call advancing 5 tokens from a stored state and a given previous token equals the sequence
+    oracle started from the resume state (state + the first token's left-end term)."""
+    import torch
+    from pins import ssd3_resume_state
+    cfg = W.ssd_config(2, 6, 4, 64, 64, 2, cfg_id=1310)
+    s = W.make_ssd_inputs(cfg, with_D=True, with_z=True, with_h0=True)
+    lam = W.make_ssd_lam(cfg)
+    say("ssd3 decode 5 tokens")
+    # token 0 plays the previous token; tokens 1..5 are advanced
+    xs, ds, ls, Bs = (W.bf16_bits_to_f32(a) for a in (s.x, s.delta, lam, s.B))
+    h1 = ssd3_resume_state(s.h0.astype(np.float64), ds, ls, Bs, xs, 1, 4, 2)
+    tail = lambda a: None if a is None else a[:, 1:]
+    ref, ref_fin = oracle.ssd3_fwd(tail(s.x), tail(s.delta), tail(lam), s.A, tail(s.B), tail(s.C), s.D,
+                                   tail(s.z), h1.astype(np.float32))
+    state = dev(s.h0).clone()
+    d = lambda a: None if a is None else dev(np.ascontiguousarray(a))
+    out = M.ssd_trapezoidal_state_update(state, d(tail(s.x)), d(tail(s.delta)), d(tail(lam)), dev(s.A),
+                                         d(tail(s.B)), d(tail(s.C)), dev(s.D), d(tail(s.z)),
+                                         x_prev=d(s.x[:, 0]), B_prev=d(s.B[:, 0]))
+    torch.cuda.synchronize()
+    check(host64(out), ref, RTOL["bf16"], "ssd3 decode 5 tokens out")
+    check(host64(state), ref_fin, RTOL["bf16"], "ssd3 decode 5 tokens state")
+
+
+def test_ssd3_decode_lam_one_is_mamba2_bitwise(M):
+    """lam = 1 drops the previous-token term exactly (its weight is 0): the Mamba-2 update bit for bit."""
+    import torch
+    cfg = W.ssd_config(2, 3, 4, 64, 128, 1, cfg_id=1311)
+    s = W.make_ssd_inputs(cfg, with_D=True, with_z=True, with_h0=True)
+    ones = W.f32_to_bf16_bits(np.ones((2, 3, 4), np.float32))
+    st3, st2 = dev(s.h0).clone(), dev(s.h0).clone()
+    args = [dev(a) for a in (s.x, s.delta)]
+    o3 = M.ssd_trapezoidal_state_update(st3, args[0], args[1], dev(ones), dev(s.A), dev(s.B), dev(s.C), dev(s.D),
+                                        dev(s.z), x_prev=dev(np.ascontiguousarray(s.x[:, 0])),
+                                        B_prev=dev(np.ascontiguousarray(s.B[:, 0])))
+    o2 = M.ssd_state_update(st2, args[0], args[1], dev(s.A), dev(s.B), dev(s.C), dev(s.D), dev(s.z))
+    torch.cuda.synchronize()
+    assert torch.equal(o3, o2) and torch.equal(st3, st2)

@@ -199,7 +199,8 @@ def cpu_baseline_ssd(inp, cfg, lam=None):
         x, delta, z, lm = hs(inp.x), hs(inp.delta), hs(inp.z), hs(lam)
         A = np.ascontiguousarray(inp.A[:nh])
         D = None if inp.D is None else np.ascontiguousarray(inp.D[:nh])
-        run = lambda: oracle.ssd3_fwd(x, delta, lm, A, inp.B, inp.C, D, z, None, nthreads=threads)
+        h0 = None if inp.h0 is None else np.ascontiguousarray(inp.h0[:, :nh])
+        run = lambda: oracle.ssd3_fwd(x, delta, lm, A, inp.B, inp.C, D, z, h0, nthreads=threads)
     passes, dt = _timed_passes(run)
     n = per_head * nh * passes
     return {"value": n / dt, "unit": "state-updates/s", "cores": threads, "kind": "oracle",
@@ -213,8 +214,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2,
-                    help="workload id (1-11; 6, 7: decode steps; 8: gradients; 9: convolution fused in front; "
-                         "10: training step; 11: Mamba-3 SISO recurrence); 2 is the one the metric is quoted on")
+                    help="workload id (1-12; 6, 7: decode steps; 8: gradients; 9: convolution fused in front; "
+                         "10: training step; 11, 12: Mamba-3 SISO recurrence and its decode step); "
+                         "2 is the one the metric is quoted on")
     ap.add_argument("--sets", type=int, default=0, help="resident input copies to rotate over (0: auto)")
     ap.add_argument("--chunk", type=int, default=0, help="SSD time-chunk length (0: the workload's)")
     ap.add_argument("--split-seq", type=int, default=0, help="force the sequence-chunk count (0: the planner's)")
@@ -319,10 +321,20 @@ def main():
                     state=dev(h.h0)) for h in host]
         outs = [torch.empty_like(i["x"]) for i in ins]
         upd = M.ssd_state_update if is_ssd else M.selective_state_update
+        trap = is_ssd and cfg.trapezoidal
+        lams = [W.make_ssd_lam(cfg, seed_base=W.ROOT_SEED + 1000 * i) if trap else None for i in range(sets)]
+        if trap:   # the Mamba-3 rule also reads the previous token's x and B
+            for i, a in enumerate(ins):
+                xp, bp = W.make_ssd_prev(cfg, seed_base=W.ROOT_SEED + 1000 * i)
+                a.update(lam=dev(lams[i]), x_prev=dev(xp), B_prev=dev(bp))
 
         def step(i):
             a, o = ins[i % sets], outs[i % sets]
-            upd(a["state"], a["x"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], out=o)
+            if trap:
+                M.ssd_trapezoidal_state_update(a["state"], a["x"], a["delta"], a["lam"], a["A"], a["B"], a["C"],
+                                               a["D"], a["z"], x_prev=a["x_prev"], B_prev=a["B_prev"], out=o)
+            else:
+                upd(a["state"], a["x"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], out=o)
         plan = {"tokens": cfg.seqlen}
     elif is_ssd:
         chunk = args.chunk or cfg.chunk

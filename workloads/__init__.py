@@ -37,7 +37,7 @@ ROOT_SEED = 1700
 BLOCK = 1 << 22
 
 # tensor ids (fixed order of the per-tensor streams)
-T_X, T_DELTA, T_Z, T_B, T_C, T_D, T_A, T_H0, T_DOUT, T_DFIN, T_CW, T_CB, T_CI, T_LAM = range(14)
+T_X, T_DELTA, T_Z, T_B, T_C, T_D, T_A, T_H0, T_DOUT, T_DFIN, T_CW, T_CB, T_CI, T_LAM, T_XPREV, T_BPREV = range(16)
 
 F32 = "f32"
 BF16 = "bf16"
@@ -131,6 +131,8 @@ class SSDConfig:
         n += blhp * e                                           # out
         n += self.batch * self.nheads * self.headdim * self.dstate * 4 if self.return_final else 0
         n += self.batch * self.nheads * self.headdim * self.dstate * 4 if self.decode else 0
+        if self.decode and self.trapezoidal:   # the previous token's x and B
+            n += (self.batch * self.nheads * self.headdim + self.batch * self.ngroups * self.dstate) * e
         return n
 
 
@@ -157,6 +159,9 @@ CONFIGS = {
     # the Mamba-3 SISO recurrence (exponential-trapezoidal input rule) at config 4's shape: SISO keeps
     # Mamba-2's dimensions and state size
     11: SSDConfig("mamba3_siso_bf16", 11, 8, 4096, 32, 64, 128, 1, 256, trapezoidal=True),
+    # its decode step at config 7's serving shape (the previous token's x and B are inputs too)
+    12: SSDConfig("mamba3_siso_decode_bf16", 12, 64, 1, 32, 64, 128, 1, 64, BF16, True, True, True, decode=True,
+                  trapezoidal=True),
 }
 
 
@@ -358,6 +363,13 @@ def make_ssd_lam(cfg: SSDConfig, seed_base: int = ROOT_SEED) -> np.ndarray:
 
     _for_blocks(n, fill)
     return out.reshape(cfg.batch, cfg.seqlen, cfg.nheads)
+
+
+def make_ssd_prev(cfg: SSDConfig, seed_base: int = ROOT_SEED):
+    """The token before a decode step's first: x_prev [B, H, P] and B_prev [B, G, N], N(0, 1) in io dtype."""
+    xp = normal(cfg.cfg_id, T_XPREV, cfg.batch * cfg.nheads * cfg.headdim, cfg.io, seed_base)
+    bp = normal(cfg.cfg_id, T_BPREV, cfg.batch * cfg.ngroups * cfg.dstate, cfg.io, seed_base)
+    return xp.reshape(cfg.batch, cfg.nheads, cfg.headdim), bp.reshape(cfg.batch, cfg.ngroups, cfg.dstate)
 
 
 def scan_config(batch: int, seqlen: int, dim: int, dstate: int, io: str = F32, a_kind: str = "s4d_real",

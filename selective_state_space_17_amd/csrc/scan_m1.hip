@@ -70,6 +70,11 @@ template <> __device__ __forceinline__ uint16_t from_f32<uint16_t>(float v) {
 template <int CTRL> __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
 }
+// the same with bound_ctrl set, for controls whose every source lane exists (a row rotation): the
+// compiler then folds the move into the consuming VALU op
+template <int CTRL> __device__ __forceinline__ float dpp_bc(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
+}
 
 __device__ __forceinline__ float exp2_hw(float v) { return __builtin_amdgcn_exp2f(v); }
 
@@ -656,8 +661,9 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(KernelParams p) {
 // s of its row (row_newbcast:s, folded by the compiler into v_mul_f32_dpp),
 // B_n and C_n are the lane's own registers (read from transposed LDS copies,
 // 16-byte reads covering 4 steps).  The readout's sum over the 16 states runs
-// once per 16 steps: each lane parks its 16 products C_n h_n in LDS and reads
-// back the 16 products of one step (a transpose), so lane j of a row finishes
+// once per 16 steps: lanes n and n+8 add their 16 products C_n h_n with a DPP
+// row rotation, lanes 0-7 park those pair sums in LDS, and each lane reads
+// back the 8 pair sums of one step (a transpose), so lane j of a row finishes
 // step j, applies the gate and writes the output.  Steps past the end of the
 // sequence are staged with delta = 0, which leaves the state unchanged exactly
 // (exp2(0) = 1, delta*x = 0).
@@ -667,8 +673,8 @@ constexpr int CPB = 16;            // channels per block (one per 16-lane row)
 constexpr int TT = 64;             // steps per tile (4 groups of 16)
 constexpr int QS = TT + 1;         // float4 row stride of the per-(c, t) operands (spreads banks)
 constexpr int BS = TT + 4;         // float row stride of the transposed B/C tiles
-constexpr int PS = 20;             // float stride between one lane's 16 products
-constexpr int PR = 16 * PS + 16;   // float stride between rows of the product buffer
+constexpr int PS = 20;             // float stride between one lane's 16 pair sums
+constexpr int PR = 8 * PS + 16;    // float stride between rows of the pair-sum buffer (16 mod 32: rows on other banks)
 }  // namespace wide
 
 using u32x2 = unsigned int __attribute__((ext_vector_type(2)));
@@ -890,21 +896,37 @@ __global__ __launch_bounds__(kThreads) void wide_kernel(KernelParams p) {
       o.Cv[4 * i] = cc.x; o.Cv[4 * i + 1] = cc.y; o.Cv[4 * i + 2] = cc.z; o.Cv[4 * i + 3] = cc.w;
     }
   };
-  // transpose through LDS: lane n parks its 16 products, then reads the 16
-  // products of step n (issued here, summed later so the LDS latency overlaps
-  // the next group's arithmetic)
-  auto park_and_fetch = [&](const float (&pr)[16], float (&rd)[16]) {
+  // transpose through LDS (issued here, summed later so the LDS latency
+  // overlaps the next group's arithmetic).  First lanes n and n+8 of a row add
+  // their 16 products (row_ror:8), which halves the bytes moved through LDS:
+  // both lanes then hold the same sums, lanes 0-7 park them, and each lane
+  // reads the 8 pair sums of its step.
+  auto park_and_fetch = [&](const float (&pr)[16], float (&rd)[8]) {
+    float ps[16];
+    {
+      // one v_add_f32_dpp per product with every lane active: the add must not be contracted into
+      // an FMA with the product (that leaves the DPP move unfolded), and the sums are pinned before
+      // the branch below (inside it the DPP could not be folded either)
+#pragma clang fp contract(off)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<float4*>(&Prow[n * PS + 4 * i]) = float4{pr[4 * i], pr[4 * i + 1], pr[4 * i + 2], pr[4 * i + 3]};
+      for (int i = 0; i < 16; ++i) ps[i] = pr[i] + dpp_bc<kRowRor8>(pr[i]);
+    }
+    asm volatile("" : "+v"(ps[0]), "+v"(ps[1]), "+v"(ps[2]), "+v"(ps[3]), "+v"(ps[4]), "+v"(ps[5]), "+v"(ps[6]),
+                 "+v"(ps[7]));
+    asm volatile("" : "+v"(ps[8]), "+v"(ps[9]), "+v"(ps[10]), "+v"(ps[11]), "+v"(ps[12]), "+v"(ps[13]),
+                 "+v"(ps[14]), "+v"(ps[15]));
+    if (n < 8) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<float4*>(&Prow[n * PS + 4 * i]) = float4{ps[4 * i], ps[4 * i + 1], ps[4 * i + 2], ps[4 * i + 3]};
+    }
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int m = 0; m < 16; ++m) rd[m] = Prow[m * PS + n];
+    for (int m = 0; m < 8; ++m) rd[m] = Prow[m * PS + n];
     __builtin_amdgcn_wave_barrier();
   };
-  auto finish = [&](int t16, const float4& q, const float (&rd)[16]) {
-    const float y = ((rd[0] + rd[1]) + (rd[2] + rd[3]) + ((rd[4] + rd[5]) + (rd[6] + rd[7]))) +
-                    ((rd[8] + rd[9]) + (rd[10] + rd[11]) + ((rd[12] + rd[13]) + (rd[14] + rd[15])));
+  auto finish = [&](int t16, const float4& q, const float (&rd)[8]) {
+    const float y = ((rd[0] + rd[1]) + (rd[2] + rd[3])) + ((rd[4] + rd[5]) + (rd[6] + rd[7]));
     ys[(t16 + n) * CPB + row] = from_f32<T>(__builtin_fmaf(y, q.z, q.w));
     if constexpr (MODE != kSingle) {
       S += q.x;
@@ -925,7 +947,7 @@ __global__ __launch_bounds__(kThreads) void wide_kernel(KernelParams p) {
   };
   auto group = [&](int t16) {
     GroupOps o;
-    float pr[16], rd[16];
+    float pr[16], rd[8];
     load_ops(t16, o);
     checkpoint(t16);
     wide_steps<0>(h, a2, o.q.x, o.q.y, o.Bv, o.Cv, pr);
@@ -936,7 +958,7 @@ __global__ __launch_bounds__(kThreads) void wide_kernel(KernelParams p) {
   // group g's steps, group g-1's sum after them
   auto full_tile = [&]() {
     GroupOps o[2];
-    float pr[16], rd[16];
+    float pr[16], rd[8];
     float4 qprev;
     load_ops(0, o[0]);
 #pragma unroll

@@ -208,3 +208,21 @@ def test_scan_update_conv_token_by_token_equals_sequence(M):
     check(host64(torch.cat(outs, dim=1)), host64(full), 1e-5, "conv token-by-token out")
     check(host64(state), host64(fin), 1e-5, "conv token-by-token state")
     assert np.array_equal(cstate.cpu().numpy(), inp.x[:, -3:]), "window after the sequence"
+
+
+@pytest.mark.parametrize("cid", [6, 7])
+def test_decode_config_full(M, cid):
+    """The decode workloads the benchmark times (one token against a stored state: 256 x 5120 x 16 and
+    64 x 32 heads x 64 x 128), every element, inputs made as the benchmark makes them."""
+    cfg = W.CONFIGS[cid]
+    say("decode config", cfg.name)
+    if isinstance(cfg, W.SSDConfig):
+        s = W.make_ssd_inputs(cfg, with_h0=True)
+        out, state = ssd_update(M, s)
+        ref, ref_fin = oracle.ssd_fwd(s.x, s.delta, s.A, s.B, s.C, s.D, s.z, s.h0)
+    else:
+        s = W.make_scan_inputs(cfg, with_h0=True)
+        out, state = scan_update(M, s)
+        ref, ref_fin = oracle.scan_fwd(s.x, s.delta, s.A, s.B, s.C, s.D, s.z, s.h0)
+    check(host64(out), ref, RTOL[cfg.io], f"{cfg.name} out")
+    check(host64(state), ref_fin, RTOL[cfg.io], f"{cfg.name} state")

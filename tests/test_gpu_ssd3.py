@@ -214,3 +214,28 @@ def test_ssd3_decode_lam_one_is_mamba2_bitwise(M):
     o2 = M.ssd_state_update(st2, args[0], args[1], dev(s.A), dev(s.B), dev(s.C), dev(s.D), dev(s.z))
     torch.cuda.synchronize()
     assert torch.equal(o3, o2) and torch.equal(st3, st2)
+
+
+def test_ssd3_decode_config_full(M):
+    """The Mamba-3 decode workload the benchmark times (64 x 32 heads x 64 x 128, one token, with the
+    previous token's x and B), every element, against the oracle from the resume state."""
+    import torch
+    from pins import ssd3_resume_state
+    cfg = W.CONFIGS[12]
+    s = W.make_ssd_inputs(cfg, with_h0=True)
+    lam = W.make_ssd_lam(cfg)
+    xp, bp = W.make_ssd_prev(cfg)
+    say("ssd3 decode config", cfg.name)
+    # the previous token as step -1 of a two-step sequence: its left-end term goes into the resume state
+    f = W.bf16_bits_to_f32
+    x2 = np.concatenate([f(xp)[:, None], f(s.x)], axis=1)
+    B2 = np.concatenate([f(bp)[:, None], f(s.B)], axis=1)
+    h1 = ssd3_resume_state(s.h0.astype(np.float64), f(s.delta)[:, [0, 0]], f(lam)[:, [0, 0]], B2, x2, 1,
+                           cfg.nheads, cfg.ngroups)
+    ref, ref_fin = oracle.ssd3_fwd(s.x, s.delta, lam, s.A, s.B, s.C, s.D, s.z, h1.astype(np.float32))
+    state = dev(s.h0).clone()
+    out = M.ssd_trapezoidal_state_update(state, dev(s.x), dev(s.delta), dev(lam), dev(s.A), dev(s.B), dev(s.C),
+                                         dev(s.D), dev(s.z), x_prev=dev(xp), B_prev=dev(bp))
+    torch.cuda.synchronize()
+    check(host64(out), ref, RTOL["bf16"], f"{cfg.name} out")
+    check(host64(state), ref_fin, RTOL["bf16"], f"{cfg.name} state")

@@ -13,6 +13,9 @@ Recipe (the workloads the pages describe, made concrete):
     section 4.2; page "Mamba-3", introduction: the transition is a scalar
     times the identity): per-(token, head) delta, scalar A per head, B/C per
     (token, group).
+  * Mamba-3 SISO rule (page "Mamba-3", "El modelo Mamba-3"): the weight lam
+    per (token, head), sigmoid(N(0, 1)), as a gate computed from the token
+    would give; for its decode step, the previous token's x and B ~ N(0, 1).
 
 Distributions: x, z, B, C ~ N(0, 1); D ~ N(0, 1) per channel;
 delta = softplus(0.5 * N(0, 1) - 2) evaluated in fp32; S4D-real A[c, n] =
@@ -136,8 +139,10 @@ class SSDConfig:
         return n
 
 
-# The five workloads.  Index 0 is the small fp32 case; index 1 is the
-# 130M-like layer the throughput figure is quoted on.
+# The workloads by id.  1 is the small fp32 case; 2 is the 130M-like layer
+# the throughput figure is quoted on; 3-5 are the larger forward layers and
+# the SSD form; 6-12 add the decode step, gradients, the convolution in front,
+# the training step and the Mamba-3 rule on the same shapes.
 CONFIGS = {
     1: ScanConfig("mamba1_tiny_f32", 1, 1, 256, 64, 16, F32, "s4d_real", return_final=True),
     2: ScanConfig("mamba1_130m_layer_bf16", 2, 8, 2048, 1536, 16, BF16, "exp_log", return_final=False),

@@ -129,7 +129,7 @@ def dev(a):
     return torch.from_numpy(a).cuda()
 
 
-def _timed_passes(run, min_seconds=10.0, max_passes=200):
+def _timed_passes(run, min_seconds=10.0, max_passes=5000):
     """Repeat one bounded oracle pass until about min_seconds of CPU work have been timed."""
     passes, t = 0, time.perf_counter()
     while True:

@@ -110,6 +110,10 @@ def _check_gpu(name, t, dtype, shape):
         return
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
+    if t.device.index != torch.cuda.current_device():
+        # the kernels run on the current device: a pointer into another GPU's memory would fault there
+        raise ValueError(f"{name} is on {t.device}, but the current device is cuda:{torch.cuda.current_device()} "
+                         "(use torch.cuda.device(...) around the call)")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if tuple(t.shape) != tuple(shape):
@@ -130,6 +134,8 @@ def _io_code(dtype) -> int:
 def _stream_handle(stream) -> int:
     torch = _torch()
     s = stream if stream is not None else torch.cuda.current_stream()
+    if s.device.index != torch.cuda.current_device():
+        raise ValueError(f"stream belongs to {s.device}, but the current device is cuda:{torch.cuda.current_device()}")
     return s.cuda_stream
 
 

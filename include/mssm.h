@@ -1,12 +1,16 @@
 /*
  * mssm.h -- C ABI of the MI355X (gfx950) selective-scan library (libmssm.so).
  *
- * Two forward operations, each with a token-by-token (decode) counterpart
- * that advances a stored state in place (mssm_selective_state_update,
- * mssm_ssd_state_update), the gradients of the first
- * (mssm_selective_scan_bwd), and the first with its short causal convolution
- * fused in front (mssm_selective_scan_conv_fwd); and the second with the
- * Mamba-3 exponential-trapezoidal input rule (mssm_ssd_trapezoidal_fwd):
+ * Two forward operations, described below, and around them:
+ *  - token-by-token (decode) counterparts that advance a stored state in
+ *    place: mssm_selective_state_update, mssm_ssd_state_update;
+ *  - the gradients of the first (mssm_selective_scan_bwd), and its training
+ *    forward that stores the state checkpoints those gradients can start
+ *    from (mssm_selective_scan_fwd_ckpt);
+ *  - the first with its short causal convolution fused in front
+ *    (mssm_selective_scan_conv_fwd; decode: mssm_selective_state_update_conv);
+ *  - the second under the Mamba-3 exponential-trapezoidal input rule
+ *    (mssm_ssd_trapezoidal_fwd; decode: mssm_ssd_trapezoidal_state_update).
  *
  *  1. mssm_selective_scan_fwd -- the Mamba-1 selective scan.  Defined by the
  *     linear state recurrence h_t = A h_{t-1} + B x_t with readout y_t = C h_t
@@ -35,10 +39,12 @@
  *     the result does not depend on the chunk length except by rounding.
  *
  * Conventions shared by every entry point:
- *  - Every data pointer is a DEVICE pointer owned by the caller.  The library
- *    never allocates, frees or keeps a pointer after returning, and never
- *    synchronises: work is enqueued on `stream` (a hipStream_t passed as
- *    void*; NULL = the null stream) and the call returns at once.
+ *  - Every data pointer is a DEVICE pointer owned by the caller, on the
+ *    device of `stream` (the device current at the call for the null
+ *    stream): the kernels run there, and memory of another GPU faults.
+ *    The library never allocates, frees or keeps a pointer after returning,
+ *    and never synchronises: work is enqueued on `stream` (a hipStream_t
+ *    passed as void*; NULL = the null stream) and the call returns at once.
  *  - Tensors are dense, row-major and contiguous (last index fastest).
  *    x, delta, B, C, z and out share io_dtype; A, D, h0 and final_state are
  *    always fp32.  fp32 results are rounded to bf16 to nearest-even.

@@ -67,6 +67,11 @@ __device__ __forceinline__ float exp2_hw(float v) { return __builtin_amdgcn_exp2
 template <int CTRL> __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
 }
+// with bound_ctrl set, for controls whose every source lane exists (a row rotation), so that the
+// compiler folds the move into the consuming add
+template <int CTRL> __device__ __forceinline__ float dpp_bc(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
+}
 // sum over the 16 lanes of a row, result in every lane
 __device__ __forceinline__ float row_sum(float v) {
   v += dpp<0x128>(v);   // row_ror:8
@@ -317,20 +322,37 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       *reinterpret_cast<float4*>(&area[qpos(cl, n, 4 * i)]) = float4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
     __builtin_amdgcn_wave_barrier();
   };
-  // lane (cl, fs) reads the 16 states' products of step fs (the sum is taken
-  // later, so other work can cover the LDS latency)
-  auto fetch = [&](const float* area, float (&r)[16]) {
+  // Sums over the 16 states: lanes n and n+8 first add their 16 per-step
+  // products with a DPP row rotation (half the bytes through LDS); lanes 0-7
+  // park those pair sums, and lane (cl, fs) reads the 8 of step fs (the sum is
+  // taken later, so other work can cover the LDS latency)
+  auto park_pairs = [&](float* area, const float (&v)[kTT]) {
+    float ps[kTT];
+    {
+#pragma clang fp contract(off)   // an FMA with the product would leave the DPP move unfolded
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {   // states 2m, 2m + 1
+      for (int i = 0; i < kTT; ++i) ps[i] = v[i] + dpp_bc<0x128>(v[i]);   // row_ror:8
+    }
+    asm volatile("" : "+v"(ps[0]), "+v"(ps[1]), "+v"(ps[2]), "+v"(ps[3]), "+v"(ps[4]), "+v"(ps[5]), "+v"(ps[6]),
+                 "+v"(ps[7]));
+    asm volatile("" : "+v"(ps[8]), "+v"(ps[9]), "+v"(ps[10]), "+v"(ps[11]), "+v"(ps[12]), "+v"(ps[13]),
+                 "+v"(ps[14]), "+v"(ps[15]));
+    if (n < 8) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<float4*>(&area[qpos(cl, n, 4 * i)]) = float4{ps[4 * i], ps[4 * i + 1], ps[4 * i + 2], ps[4 * i + 3]};
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
+  auto fetch = [&](const float* area, float (&r)[8]) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {   // pair sums of states 2m, 2m + 1
       const float* base = area + cl * kRow + 32 * m + (fs ^ ((m & 3) << 2));
       r[2 * m] = base[0];
       r[2 * m + 1] = base[16];
     }
   };
-  auto sum16 = [](const float (&r)[16]) {
-    return ((r[0] + r[1]) + (r[2] + r[3]) + ((r[4] + r[5]) + (r[6] + r[7]))) +
-           ((r[8] + r[9]) + (r[10] + r[11]) + ((r[12] + r[13]) + (r[14] + r[15])));
-  };
+  auto sum8 = [](const float (&r)[8]) { return ((r[0] + r[1]) + (r[2] + r[3])) + ((r[4] + r[5]) + (r[6] + r[7])); };
 
   if (p.ntiles > 0) issue(p.ntiles - 1);
   for (int k = p.ntiles - 1; k >= 0; --k) {
@@ -381,8 +403,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       rec_step<14>(h, av, hs, pr, q1, dl, du, dy, A2, bv.z, cv.z);
       rec_step<15>(h, av, hs, pr, q1, dl, du, dy, A2, bv.w, cv.w);
     }
-    park(Q2, pr);
-    float ry[16];
+    park_pairs(Q2, pr);
+    float ry[8];
     fetch(Q2, ry);           // y of step fs, summed after the adjoint loop
     const int64_t fi = (b * L + tf) * dim + c;
 
@@ -412,10 +434,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       adj_step<1>(lam, dAacc, av, hs, hin, ls, r1, dl, dy, Av, cv.y);
       adj_step<0>(lam, dAacc, av, hs, hin, ls, r1, dl, dy, Av, cv.x);
     }
-    const float y = __builtin_fmaf(Dc, u, sum16(ry));
+    const float y = __builtin_fmaf(Dc, u, sum8(ry));
     if (p.z != nullptr && fvalid) io::put(p.dz, fi, sdz * y);
     // both sums over states in one LDS round trip (Q1's rows take q1 after)
-    park(Q1, r1);
+    park_pairs(Q1, r1);
     {
       float r2[kTT];   // lam_t B_t
 #pragma unroll
@@ -426,13 +448,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         r2[4 * g + 2] = ls[4 * g + 2] * bv.z;
         r2[4 * g + 3] = ls[4 * g + 3] * bv.w;
       }
-      park(Q2, r2);
+      park_pairs(Q2, r2);
     }
-    float ra[16], rb2[16];
+    float ra[8], rb2[8];
     fetch(Q1, ra);
     fetch(Q2, rb2);
     dDacc = __builtin_fmaf(dy, u, dDacc);
-    const float s1 = sum16(ra), s2 = sum16(rb2);
+    const float s1 = sum8(ra), s2 = sum8(rb2);
     if (fvalid) {
       io::put(p.ddelta, fi, __builtin_fmaf(u, s2, s1));
       io::put(p.dx, fi, __builtin_fmaf(dl, s2, Dc * dy));

@@ -20,6 +20,12 @@ leg may import this package.  The product library never uses it.
                  solution of the continuous-time system at lam = 1/2 (first order
                  at lam = 1), and a brute-force sum over the implicit width-2
                  convolution weights.
+``ssdc_fwd``  -- the same with a complex-valued state: each state pair is a
+                 complex number and the head's transition a + i*omega per pair,
+                 in C99 complex arithmetic (mssm_oracle.c: oracle_ssdc_fwd).
+                 Pinned by: equality with ``ssd3_fwd`` at omega = 0, the
+                 rotated-B/C real form (RoPE) as a brute-force sum, the complex
+                 geometric closed form, and the previous-token inputs.
 ``conv_silu``, ``conv_scan_fwd``
               -- the short causal convolution + SiLU in front of the scan, and
                  the scan on its output (mssm_oracle.c: oracle_conv_silu,
@@ -67,6 +73,8 @@ def load_library(path: Optional[str] = None):
     lib.oracle_ssd_fwd.argtypes = [i64, i64, i64, i64, i64, i64, i32, p, p, p, p, p, p, p, p, i64, i64, p, p, i32]
     lib.oracle_ssd3_fwd.restype = i32
     lib.oracle_ssd3_fwd.argtypes = [i64, i64, i64, i64, i64, i64, i32] + [p] * 9 + [p, p, i32]
+    lib.oracle_ssdc_fwd.restype = i32
+    lib.oracle_ssdc_fwd.argtypes = [i64, i64, i64, i64, i64, i64, i32] + [p] * 12 + [p, p, i32]
     lib.oracle_conv_silu.restype = i32
     lib.oracle_conv_silu.argtypes = [i64, i64, i64, i64, i32, p, p, p, p, p]
     lib.oracle_conv_scan_fwd.restype = i32
@@ -176,6 +184,33 @@ def ssd3_fwd(x, delta, lam, A, B, C, D=None, z=None, h0=None, nthreads: Optional
                                          nthreads or default_threads())
     if rc != 0:
         raise ValueError("oracle_ssd3_fwd rejected its arguments")
+    return out, fin
+
+
+def ssdc_fwd(x, delta, lam, A, omega, B, C, D=None, z=None, h0=None, x_prev=None, B_prev=None,
+             nthreads: Optional[int] = None, lib=None):
+    """Mamba-3 SISO recurrence with a complex-valued state: as ``ssd3_fwd`` with the head's transition
+    a + i*omega[h, k] on state pair k (omega [H, N/2] fp32), and the token before step 0 given by
+    x_prev [Bsz, H, P] and B_prev [Bsz, G, N] (io dtype; None: no previous token).
+    Returns (out [Bsz, L, H, P] fp64, final_state [Bsz, H, P, N] fp64)."""
+    x, delta, lam, B, C, z = _c(x), _c(delta), _c(lam), _c(B), _c(C), _c(z)
+    x_prev, B_prev = _c(x_prev), _c(B_prev)
+    io = _io_code(x)
+    for t in (delta, lam, B, C) + tuple(v for v in (z, x_prev, B_prev) if v is not None):
+        if _io_code(t) != io:
+            raise TypeError("x, delta, lam, B, C, z, x_prev, B_prev must share one dtype")
+    A, omega, D, h0 = _c(A, np.float32), _c(omega, np.float32), _c(D, np.float32), _c(h0, np.float32)
+    bsz, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    if omega.shape != (H, N // 2):
+        raise ValueError("omega must be [H, N/2]")
+    out = np.empty((bsz, L, H, P), dtype=np.float64)
+    fin = np.empty((bsz, H, P, N), dtype=np.float64)
+    rc = (lib or _get()).oracle_ssdc_fwd(bsz, L, H, P, N, G, io, _ptr(x), _ptr(delta), _ptr(lam), _ptr(A),
+                                         _ptr(omega), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(x_prev),
+                                         _ptr(B_prev), _ptr(out), _ptr(fin), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_ssdc_fwd rejected its arguments")
     return out, fin
 
 

@@ -30,6 +30,7 @@
  *
  * Parity status of each function is stated in the oracle's Python wrapper.
  */
+#include <complex.h>
 #include <math.h>
 #include <pthread.h>
 #include <stdint.h>
@@ -379,6 +380,119 @@ int oracle_ssd3_fwd(int64_t Bsz, int64_t L, int64_t H, int64_t P, int64_t N, int
     }
     for (int k = 1; k < nthreads; ++k) pthread_create(&th[k], NULL, ssd3_worker, &jobs[k]);
     ssd3_worker(&jobs[0]);
+    for (int k = 1; k < nthreads; ++k) pthread_join(th[k], NULL);
+    free(jobs);
+    free(th);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Mamba-3 SISO with a complex-valued state (own loop, complex arithmetic)   */
+/* ------------------------------------------------------------------------- */
+/*
+ * "Mamba-3" (blog), "El modelo Mamba-3" item 2: the state is tracked by a
+ * complex-valued SSM; "Arquitectura": the complex transitions act as
+ * rotations (RoPE), data-dependent ("Kernels por todas partes").  Plain
+ * reading: state pairs (2k, 2k+1) are one complex number h_k, the transition
+ * of head h is the complex scalar a_h + i omega[h,k] per pair, and zero-order
+ * hold gives exp(d (a_h + i omega)) -- a decay times a rotation by d*omega,
+ * data-dependent through d.  B and C pairs are complex numbers too; the
+ * input rule is the exponential-trapezoidal one of oracle_ssd3_fwd with the
+ * complex transition, and the readout takes the real part of conj(C_k) h_k
+ * (the real dot product of the pairs).  omega = 0 is oracle_ssd3_fwd.
+ */
+typedef struct {
+    int64_t Bsz, L, H, P, N, G;
+    int io;
+    const void *x, *delta, *lam, *Bm, *Cm, *z;
+    const float *A, *omega, *Dv, *h0;
+    const void *x_prev, *B_prev;
+    double *out, *final_state;
+    int64_t pair_begin, pair_end;
+} ssdc_job;
+
+static void ssdc_pair(const ssdc_job* j, int64_t b, int64_t hd, double complex* S, double complex* bx_prev) {
+    const int64_t H = j->H, P = j->P, N = j->N, L = j->L, G = j->G, K = N / 2;
+    const int64_t g = hd / (H / G);
+    for (int64_t p = 0; p < P; ++p)
+        for (int64_t k = 0; k < K; ++k) {
+            const int64_t i = ((b * H + hd) * P + p) * N + 2 * k;
+            S[p * K + k] = j->h0 ? (double)j->h0[i] + I * (double)j->h0[i + 1] : 0.0;
+            bx_prev[p * K + k] = 0.0;
+            if (j->x_prev && j->B_prev) {
+                const double xp = load_io(j->x_prev, j->io, (b * H + hd) * P + p);
+                const int64_t r = (b * G + g) * N + 2 * k;
+                bx_prev[p * K + k] = (load_io(j->B_prev, j->io, r) + I * load_io(j->B_prev, j->io, r + 1)) * xp;
+            }
+        }
+    for (int64_t t = 0; t < L; ++t) {
+        const double d = load_io(j->delta, j->io, (b * L + t) * H + hd);
+        const double lam = load_io(j->lam, j->io, (b * L + t) * H + hd);
+        const int64_t r = ((b * L + t) * G + g) * N;
+        for (int64_t p = 0; p < P; ++p) {
+            const int64_t i = ((b * L + t) * H + hd) * P + p;
+            const double u = load_io(j->x, j->io, i);
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const double complex a = cexp(d * ((double)j->A[hd] + I * (double)j->omega[hd * K + k]));
+                const double complex bk = load_io(j->Bm, j->io, r + 2 * k) + I * load_io(j->Bm, j->io, r + 2 * k + 1);
+                const double complex ck = load_io(j->Cm, j->io, r + 2 * k) + I * load_io(j->Cm, j->io, r + 2 * k + 1);
+                const double complex bx = bk * u;
+                S[p * K + k] = a * S[p * K + k] + (1.0 - lam) * d * a * bx_prev[p * K + k] + lam * d * bx;
+                bx_prev[p * K + k] = bx;
+                acc += creal(conj(ck) * S[p * K + k]);
+            }
+            double y = acc + (j->Dv ? (double)j->Dv[hd] * u : 0.0);
+            if (j->z) y *= silu(load_io(j->z, j->io, i));
+            j->out[i] = y;
+        }
+    }
+    if (j->final_state)
+        for (int64_t p = 0; p < P; ++p)
+            for (int64_t k = 0; k < K; ++k) {
+                const int64_t i = ((b * H + hd) * P + p) * N + 2 * k;
+                j->final_state[i] = creal(S[p * K + k]);
+                j->final_state[i + 1] = cimag(S[p * K + k]);
+            }
+}
+
+static void* ssdc_worker(void* arg) {
+    const ssdc_job* j = (const ssdc_job*)arg;
+    const int64_t n = j->P * (j->N / 2);
+    double complex* S = (double complex*)malloc(sizeof(double complex) * (size_t)(2 * n));
+    for (int64_t k = j->pair_begin; k < j->pair_end; ++k) ssdc_pair(j, k / j->H, k % j->H, S, S + n);
+    free(S);
+    return NULL;
+}
+
+/*
+ * As oracle_ssd3_fwd, plus omega [H, N/2] fp32 (rotation rate of each state
+ * pair) and the token before step 0, x_prev [Bsz, H, P] and B_prev
+ * [Bsz, G, N] in io dtype (both nullable: no previous token).  N must be even.
+ */
+int oracle_ssdc_fwd(int64_t Bsz, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int io,
+                    const void* x, const void* delta, const void* lam, const float* A, const float* omega,
+                    const void* Bm, const void* Cm, const float* Dv, const void* z, const float* h0,
+                    const void* x_prev, const void* B_prev, double* out, double* final_state, int nthreads) {
+    if (Bsz < 0 || L < 0 || H <= 0 || P <= 0 || N <= 0 || N % 2 != 0 || G <= 0 || H % G != 0) return -1;
+    if (io != IO_F32 && io != IO_BF16) return -1;
+    const int64_t pairs = Bsz * H;
+    if (pairs == 0) return 0;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > pairs) nthreads = (int)pairs;
+    ssdc_job* jobs = (ssdc_job*)calloc((size_t)nthreads, sizeof(ssdc_job));
+    pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+    for (int k = 0; k < nthreads; ++k) {
+        ssdc_job* j = &jobs[k];
+        j->Bsz = Bsz; j->L = L; j->H = H; j->P = P; j->N = N; j->G = G; j->io = io;
+        j->x = x; j->delta = delta; j->lam = lam; j->Bm = Bm; j->Cm = Cm; j->z = z;
+        j->A = A; j->omega = omega; j->Dv = Dv; j->h0 = h0; j->x_prev = x_prev; j->B_prev = B_prev;
+        j->out = out; j->final_state = final_state;
+        j->pair_begin = pairs * k / nthreads;
+        j->pair_end = pairs * (k + 1) / nthreads;
+    }
+    for (int k = 1; k < nthreads; ++k) pthread_create(&th[k], NULL, ssdc_worker, &jobs[k]);
+    ssdc_worker(&jobs[0]);
     for (int k = 1; k < nthreads; ++k) pthread_join(th[k], NULL);
     free(jobs);
     free(th);

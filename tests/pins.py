@@ -480,6 +480,111 @@ def pin_ssd3_resume(lib, seed=18):
 
 
 # ---------------------------------------------------------------------------
+# Mamba-3 SISO recurrence with a complex-valued state (rotations per state pair)
+# ---------------------------------------------------------------------------
+def _ssdc_case(rng, bsz=2, L=23, H=3, P=2, N=6, G=1):
+    x, delta, lam, A, B, C, D, z, h0 = _ssd3_case(rng, bsz, L, H, P, N, G)
+    omega = rng.uniform(-3.0, 3.0, (H, N // 2)).astype(np.float32)
+    return x, delta, lam, A, omega, B, C, D, z, h0
+
+
+def _rot(u, v, phi):
+    """Rotate the pairs (u, v) by the angles phi (real arithmetic)."""
+    c, s = np.cos(phi), np.sin(phi)
+    return u * c - v * s, u * s + v * c
+
+
+def pin_ssdc_omega_zero_is_ssd3(lib, seed=41):
+    """No rotation (omega = 0) leaves the real exponential-trapezoidal recurrence."""
+    rng = _rng(seed)
+    x, delta, lam, A, omega, B, C, D, z, h0 = _ssdc_case(rng)
+    out, fin = oracle.ssdc_fwd(x, delta, lam, A, np.zeros_like(omega), B, C, D, z, h0, lib=lib)
+    ref, ref_fin = oracle.ssd3_fwd(x, delta, lam, A, B, C, D, z, h0, lib=lib)
+    _close(out, ref, 1e-13, "omega = 0 output vs real Mamba-3 form")
+    _close(fin, ref_fin, 1e-13, "omega = 0 final state vs real Mamba-3 form")
+
+
+def pin_ssdc_rope_bruteforce(lib, seed=42):
+    """In the frame rotated back by Theta_t = sum_{r<=t} delta_r omega, the state follows the real
+    recurrence with B and C rotated by -Theta_t (RoPE on B and C).  Built here with explicit cos/sin
+    rotations and the unrolled trapezoidal weights, then the final state is rotated forward again."""
+    rng = _rng(seed)
+    x, delta, lam, A, omega, B, C, D, z, h0 = _ssdc_case(rng)
+    out, fin = oracle.ssdc_fwd(x, delta, lam, A, omega, B, C, D, z, h0, nthreads=1, lib=lib)
+    x64, d64, l64, B64, C64 = (v.astype(np.float64) for v in (x, delta, lam, B, C))
+    om, h064 = omega.astype(np.float64), h0.astype(np.float64)
+    bsz, L, H, P = x.shape
+    N = B.shape[3]
+    want, want_fin = np.zeros_like(out), np.zeros_like(fin)
+    for b in range(bsz):
+        for h in range(H):
+            theta = np.cumsum(d64[b, :, h])[:, None] * om[h][None, :]                 # [L, N/2]
+            Br = np.empty((L, N)); Cr = np.empty((L, N))
+            Br[:, 0::2], Br[:, 1::2] = _rot(B64[b, :, 0, 0::2], B64[b, :, 0, 1::2], -theta)
+            Cr[:, 0::2], Cr[:, 1::2] = _rot(C64[b, :, 0, 0::2], C64[b, :, 0, 1::2], -theta)
+            ell = d64[b, :, h] * np.float64(A[h])
+            wt = l64[b, :, h] * d64[b, :, h]
+            wo = wt.copy()
+            wo[:-1] += (1.0 - l64[b, 1:, h]) * d64[b, 1:, h]
+            for p in range(P):
+                for t in range(L):
+                    tot = np.exp(np.sum(ell[:t + 1])) * np.dot(Cr[t], h064[b, h, p])
+                    for s in range(t + 1):
+                        w = wt[s] if s == t else wo[s]
+                        tot += np.exp(np.sum(ell[s + 1:t + 1])) * np.dot(Cr[t], Br[s]) * w * x64[b, s, h, p]
+                    tot += np.float64(D[h]) * x64[b, t, h, p]
+                    want[b, t, h, p] = tot * _silu(np.float64(z[b, t, h, p]))
+                g = np.exp(np.sum(ell)) * h064[b, h, p]
+                for s in range(L):
+                    w = wt[s] if s == L - 1 else wo[s]    # the last step has no later step to reach
+                    g = g + np.exp(np.sum(ell[s + 1:])) * w * x64[b, s, h, p] * Br[s]
+                want_fin[b, h, p, 0::2], want_fin[b, h, p, 1::2] = _rot(g[0::2], g[1::2], theta[-1])
+    _close(out, want, 1e-11, "complex state: rotated-frame (RoPE) brute force")
+    _close(fin, want_fin, 1e-11, "complex state: rotated-frame final state")
+
+
+def pin_ssdc_geometric(lib, seed=43):
+    """Constant inputs, one state pair, no previous token: with r = exp(d (a + i w)),
+    h_0 = lam d b x and h_t = r h_{t-1} + ((1 - lam) r + lam) d b x, so
+    h_t = r^t h_0 + c (1 - r^t) / (1 - r); y_t = Re(conj(c_C) h_t)."""
+    L, d, lam, a, w, xv = 40, 0.25, 0.375, -0.5, 1.25, 0.75
+    bc, cc = (0.5, -1.0), (1.5, 0.25)
+    x = np.full((1, L, 1, 1), xv, np.float32)
+    delta = np.full((1, L, 1), d, np.float32)
+    lm = np.full((1, L, 1), lam, np.float32)
+    B = np.tile(np.array(bc, np.float32), (1, L, 1, 1))
+    C = np.tile(np.array(cc, np.float32), (1, L, 1, 1))
+    out, fin = oracle.ssdc_fwd(x, delta, lm, np.array([a], np.float32), np.array([[w]], np.float32), B, C,
+                               lib=lib)
+    r = np.exp(d * (a + 1j * w))
+    bx = (bc[0] + 1j * bc[1]) * xv
+    h0 = lam * d * bx
+    c = ((1.0 - lam) * r + lam) * d * bx
+    t = np.arange(L)
+    h = r ** t * h0 + c * (1.0 - r ** t) / (1.0 - r)
+    y = np.real(np.conj(cc[0] + 1j * cc[1]) * h)
+    _close(out[0, :, 0, 0], y, 1e-12, "complex state: geometric closed form")
+    _close(fin[0, 0, 0], np.array([h[-1].real, h[-1].imag]), 1e-12, "complex state: final pair")
+
+
+def pin_ssdc_previous_token(lib, seed=44):
+    """Giving the token before step 0 (x_prev, B_prev) equals adding its left-end term,
+    (1 - lam_0) d_0 x_prev B_prev (per complex pair), to h0."""
+    rng = _rng(seed)
+    x, delta, lam, A, omega, B, C, D, z, h0 = _ssdc_case(rng, G=1)
+    bsz, L, H, P = x.shape
+    N = B.shape[3]
+    xp = rng.standard_normal((bsz, H, P)).astype(np.float32)
+    bp = rng.standard_normal((bsz, 1, N)).astype(np.float32)
+    out, fin = oracle.ssdc_fwd(x, delta, lam, A, omega, B, C, D, z, h0, xp, bp, lib=lib)
+    w = (1.0 - lam[:, 0].astype(np.float64)) * delta[:, 0].astype(np.float64)     # [b, H]
+    h1 = h0 + w[:, :, None, None] * xp.astype(np.float64)[:, :, :, None] * bp.astype(np.float64)[:, :, None, :]
+    ref, ref_fin = oracle.ssdc_fwd(x, delta, lam, A, omega, B, C, D, z, h1.astype(np.float32), lib=lib)
+    _close(out, ref, 1e-6, "complex state: previous token output")
+    _close(fin, ref_fin, 1e-6, "complex state: previous token final state")
+
+
+# ---------------------------------------------------------------------------
 # Gradients of the Mamba-1 scan
 # ---------------------------------------------------------------------------
 def _fd_case(rng, bsz=2, L=9, d=3, n=4):
@@ -632,6 +737,7 @@ SCAN_PINS = [pin_lti_convolution, pin_delta_zero, pin_geometric, pin_bruteforce,
              pin_linearity_causality, pin_gate_skip, pin_bf16_codec]
 SSD_PINS = [pin_ssd_equals_broadcast_scan, pin_ssd_geometric, pin_ssd_bruteforce, pin_ssd_chaining]
 SSD3_PINS = [pin_ssd3_lam_one_is_ssd, pin_ssd3_trapezoid_order, pin_ssd3_bruteforce, pin_ssd3_resume]
+SSDC_PINS = [pin_ssdc_omega_zero_is_ssd3, pin_ssdc_rope_bruteforce, pin_ssdc_geometric, pin_ssdc_previous_token]
 BWD_PINS = [pin_scan_bwd_finite_differences, pin_scan_bwd_linear_in_upstream]
 CONV_PINS = [pin_conv_numpy, pin_conv_impulse, pin_conv_chaining, pin_conv_scan_composition]
-ALL_PINS = SCAN_PINS + SSD_PINS + SSD3_PINS + BWD_PINS + CONV_PINS
+ALL_PINS = SCAN_PINS + SSD_PINS + SSD3_PINS + SSDC_PINS + BWD_PINS + CONV_PINS

@@ -51,6 +51,14 @@ MUTANTS = {
         "bx_prev[p * N + n] = bx;\n                S[p * N + n] = a * S[p * N + n] + w_left * bx_prev[p * N + n] + w_right * bx;"),
     "ssd3_left_without_delta": ("w_left = (1.0 - lam) * d * a,", "w_left = (1.0 - lam) * a,"),
     "ssd3_prev_input_not_reset": ("bx_prev[p * N + n] = 0.0;                           /* B_{-1} x_{-1} */", ";"),
+    # Mamba-3 complex-valued state
+    "ssdc_rotation_sign": ("(double)j->A[hd] + I * (double)j->omega[hd * K + k]",
+                           "(double)j->A[hd] - I * (double)j->omega[hd * K + k]"),
+    "ssdc_readout_without_conj": ("acc += creal(conj(ck) * S[p * K + k]);", "acc += creal(ck * S[p * K + k]);"),
+    "ssdc_one_rate_per_head": ("(double)j->omega[hd * K + k]", "(double)j->omega[hd * K]"),
+    "ssdc_left_end_not_rotated": ("(1.0 - lam) * d * a * bx_prev[p * K + k]",
+                                  "(1.0 - lam) * d * cabs(a) * bx_prev[p * K + k]"),
+    "ssdc_previous_token_ignored": ("if (j->x_prev && j->B_prev) {", "if (0) {"),
     # gradients
     "bwd_no_adjoint_decay": ("lam[n] *= a;", ";"),
     "bwd_dsilu_is_sigmoid": ("return s * (1.0 + v * (1.0 - s));", "return s;"),

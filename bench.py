@@ -183,7 +183,7 @@ def cpu_baseline_conv_scan(inp, cfg, conv):
                       f"{passes} pass(es) ({n:.3e} updates in {dt:.2f} s, fp64)"}
 
 
-def cpu_baseline_ssd(inp, cfg, lam=None):
+def cpu_baseline_ssd(inp, cfg, lam=None, omega=None):
     import numpy as np
     import oracle
     threads = oracle.default_threads()
@@ -200,7 +200,11 @@ def cpu_baseline_ssd(inp, cfg, lam=None):
         A = np.ascontiguousarray(inp.A[:nh])
         D = None if inp.D is None else np.ascontiguousarray(inp.D[:nh])
         h0 = None if inp.h0 is None else np.ascontiguousarray(inp.h0[:, :nh])
-        run = lambda: oracle.ssd3_fwd(x, delta, lm, A, inp.B, inp.C, D, z, h0, nthreads=threads)
+        if omega is None:
+            run = lambda: oracle.ssd3_fwd(x, delta, lm, A, inp.B, inp.C, D, z, h0, nthreads=threads)
+        else:   # the complex-valued state
+            om = np.ascontiguousarray(omega[:nh])
+            run = lambda: oracle.ssdc_fwd(x, delta, lm, A, om, inp.B, inp.C, D, z, h0, nthreads=threads)
     passes, dt = _timed_passes(run)
     n = per_head * nh * passes
     return {"value": n / dt, "unit": "state-updates/s", "cores": threads, "kind": "oracle",
@@ -214,9 +218,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2,
-                    help="workload id (1-12; 6, 7: decode steps; 8: gradients; 9: convolution fused in front; "
-                         "10: training step; 11, 12: Mamba-3 SISO recurrence and its decode step); "
-                         "2 is the one the metric is quoted on")
+                    help="workload id (1-13; 6, 7: decode steps; 8: gradients; 9: convolution fused in front; "
+                         "10: training step; 11, 12: Mamba-3 SISO recurrence and its decode step; 13: that decode "
+                         "step with the complex-valued state); 2 is the one the metric is quoted on")
     ap.add_argument("--sets", type=int, default=0, help="resident input copies to rotate over (0: auto)")
     ap.add_argument("--chunk", type=int, default=0, help="SSD time-chunk length (0: the workload's)")
     ap.add_argument("--split-seq", type=int, default=0, help="force the sequence-chunk count (0: the planner's)")
@@ -327,10 +331,15 @@ def main():
             for i, a in enumerate(ins):
                 xp, bp = W.make_ssd_prev(cfg, seed_base=W.ROOT_SEED + 1000 * i)
                 a.update(lam=dev(lams[i]), x_prev=dev(xp), B_prev=dev(bp))
+                if cfg.complex_state:
+                    a["omega"] = dev(W.make_ssd_omega(cfg, seed_base=W.ROOT_SEED + 1000 * i))
 
         def step(i):
             a, o = ins[i % sets], outs[i % sets]
-            if trap:
+            if trap and cfg.complex_state:
+                M.mamba3_siso_update(a["state"], a["x"], a["delta"], a["lam"], a["A"], a["omega"], a["B"], a["C"],
+                                     a["D"], a["z"], x_prev=a["x_prev"], B_prev=a["B_prev"], out=o)
+            elif trap:
                 M.ssd_trapezoidal_state_update(a["state"], a["x"], a["delta"], a["lam"], a["A"], a["B"], a["C"],
                                                a["D"], a["z"], x_prev=a["x_prev"], B_prev=a["B_prev"], out=o)
             else:
@@ -492,7 +501,8 @@ def main():
         elif getattr(cfg, "conv_width", 0):
             cpu = cpu_baseline_conv_scan(h, cfg, convs[0])
         else:
-            cpu = (cpu_baseline_ssd(h, cfg, lams[0] if cfg.trapezoidal else None) if is_ssd
+            cpu = (cpu_baseline_ssd(h, cfg, lams[0] if cfg.trapezoidal else None,
+                                    W.make_ssd_omega(cfg) if getattr(cfg, "complex_state", False) else None) if is_ssd
                    else cpu_baseline_scan(h, cfg))
         if decode:
             cpu["sample"] += "; the same recurrence from the stored state (h0)"
@@ -510,6 +520,8 @@ def main():
                     **plan)
         if cfg.trapezoidal:
             conf["rule"] = "exponential-trapezoidal"
+        if getattr(cfg, "complex_state", False):
+            conf["state"] = "complex (rotation per state pair)"
     else:
         conf.update(d_inner=cfg.dim, d_state=cfg.dstate, io=cfg.io, D=cfg.has_D, z_gate=cfg.has_z,
                     final_state=cfg.return_final, **plan)

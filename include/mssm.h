@@ -10,7 +10,8 @@
  *  - the first with its short causal convolution fused in front
  *    (mssm_selective_scan_conv_fwd; decode: mssm_selective_state_update_conv);
  *  - the second under the Mamba-3 exponential-trapezoidal input rule
- *    (mssm_ssd_trapezoidal_fwd; decode: mssm_ssd_trapezoidal_state_update).
+ *    (mssm_ssd_trapezoidal_fwd; decode: mssm_ssd_trapezoidal_state_update),
+ *    and with a complex-valued state as well (mssm_mamba3_siso_update).
  *
  *  1. mssm_selective_scan_fwd -- the Mamba-1 selective scan.  Defined by the
  *     linear state recurrence h_t = A h_{t-1} + B x_t with readout y_t = C h_t
@@ -243,6 +244,33 @@ int mssm_ssd_trapezoidal_state_update(const mssm_ssd_desc* desc, float* state,
                                       const void* x, const void* delta, const void* lam,
                                       const float* A, const void* B, const void* C,
                                       const float* D, const void* z, void* out, void* stream);
+
+/* The Mamba-3 SISO recurrence with a complex-valued state ("Mamba-3" blog,
+ * "El modelo Mamba-3" item 2: state tracking by a complex-valued SSM;
+ * "Arquitectura": its transitions act as rotations, RoPE; "Kernels por todas
+ * partes": data-dependent).  The pages give no formula; the plain reading:
+ * state pairs (2k, 2k+1) are complex numbers and head h's transition is
+ * A[h] + i*omega[h,k] per pair, so zero-order hold gives a decay times a
+ * rotation by delta*omega (data-dependent through delta):
+ *     (u, v)  = S[p,2k], S[p,2k+1] + (1 - lam) * delta * x_prev[p] * B_prev[g,2k], [g,2k+1]
+ *     S[p,2k]   = a * (c*u - s*v) + lam * delta * B[b,t,g,2k]   * x[b,t,h,p]
+ *     S[p,2k+1] = a * (s*u + c*v) + lam * delta * B[b,t,g,2k+1] * x[b,t,h,p]
+ * with a = exp(delta*A[h]), c, s = cos, sin(delta*omega[h,k]); readout
+ * y = sum_n C[n] S[p,n] (the real part of conj(C_k) S_k) as before.
+ *   omega : [nheads, dstate/2] fp32, required; dstate must be even
+ *           (MSSM_ERR_UNSUPPORTED otherwise).
+ * The state is kept in its own (unrotated) frame, so it can be stored and
+ * resumed like any other.  omega = 0 is mssm_ssd_trapezoidal_state_update
+ * bit for bit.  Any number of tokens: with seqlen = L this is also the
+ * sequence form of the complex state (recurrent, no matrix cores; h0 =
+ * state, final_state written to state).  Other arguments and rules as
+ * mssm_ssd_trapezoidal_state_update. */
+int mssm_mamba3_siso_update(const mssm_ssd_desc* desc, float* state,
+                            const void* x_prev, const void* B_prev,
+                            const void* x, const void* delta, const void* lam,
+                            const float* A, const float* omega,
+                            const void* B, const void* C, const float* D, const void* z,
+                            void* out, void* stream);
 
 /* Selective scan with the short causal convolution + SiLU that precedes it in
  * the Mamba-1/2 block fused in front ("Mamba-3" blog, "Arquitectura": the

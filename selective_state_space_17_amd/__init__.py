@@ -50,6 +50,7 @@ SIGNATURES = {
     "mssm_selective_state_update": (_I, [ctypes.POINTER(ScanDesc)] + [_P] * 10),
     "mssm_ssd_state_update": (_I, [ctypes.POINTER(SSDDesc)] + [_P] * 10),
     "mssm_ssd_trapezoidal_state_update": (_I, [ctypes.POINTER(SSDDesc)] + [_P] * 13),
+    "mssm_mamba3_siso_update": (_I, [ctypes.POINTER(SSDDesc)] + [_P] * 14),
     "mssm_selective_state_update_conv": (_I, [ctypes.POINTER(ScanDesc), ctypes.c_int32] + [_P] * 13),
     "mssm_selective_scan_conv_fwd": (_I, [ctypes.POINTER(ScanDesc), ctypes.c_int32] + [_P] * 13 + [_P, _SZ, _P]),
     "mssm_selective_scan_conv_workspace_size": (_SZ, [ctypes.POINTER(ScanDesc)]),
@@ -536,7 +537,20 @@ def ssd_trapezoidal_state_update(state, x, delta, lam, A, B, C, D=None, z=None, 
                             z, out, stream)
 
 
-def _ssd_update_call(fn, state, x_prev, B_prev, x, delta, lam, A, B, C, D, z, out, stream):
+def mamba3_siso_update(state, x, delta, lam, A, omega, B, C, D=None, z=None, x_prev=None, B_prev=None, out=None,
+                       stream=None):
+    """Advance a multi-head state by seqlen tokens in place under the Mamba-3 SISO recurrence with a
+    complex-valued state (mssm_mamba3_siso_update): the exponential-trapezoidal rule, each state pair
+    rotated by delta * omega per step.
+
+    As ``ssd_trapezoidal_state_update`` plus omega [nheads, dstate / 2] float32; dstate must be even.
+    With seqlen = L it is also the sequence form (state in: h0; state out: the final state).
+    """
+    return _ssd_update_call("mssm_mamba3_siso_update", state, x_prev, B_prev, x, delta, lam, A, B, C, D, z, out,
+                            stream, omega=omega)
+
+
+def _ssd_update_call(fn, state, x_prev, B_prev, x, delta, lam, A, B, C, D, z, out, stream, omega=None):
     torch = _torch()
     if x.dim() != 4:
         raise ValueError("x must be [batch, seqlen, nheads, headdim]")
@@ -545,9 +559,11 @@ def _ssd_update_call(fn, state, x_prev, B_prev, x, delta, lam, A, B, C, D, z, ou
         raise ValueError("B must be [batch, seqlen, ngroups, dstate]")
     G, N = B.shape[2], B.shape[3]
     io = _io_code(x.dtype)
-    trap = fn == "mssm_ssd_trapezoidal_state_update"
+    trap = fn in ("mssm_ssd_trapezoidal_state_update", "mssm_mamba3_siso_update")
     if trap and lam is None:
         raise ValueError("lam is required")
+    if fn == "mssm_mamba3_siso_update" and omega is None:
+        raise ValueError("omega is required")
     for name, t, shape in (("x", x, (bsz, L, H, P)), ("z", z, (bsz, L, H, P)), ("delta", delta, (bsz, L, H)),
                            ("lam", lam, (bsz, L, H)), ("B", B, (bsz, L, G, N)), ("C", C, (bsz, L, G, N)),
                            ("x_prev", x_prev, (bsz, H, P)), ("B_prev", B_prev, (bsz, G, N))):
@@ -555,11 +571,16 @@ def _ssd_update_call(fn, state, x_prev, B_prev, x, delta, lam, A, B, C, D, z, ou
     _check_gpu("A", A, torch.float32, (H,))
     _check_gpu("D", D, torch.float32, (H,))
     _check_gpu("state", state, torch.float32, (bsz, H, P, N))
+    _check_gpu("omega", omega, torch.float32, (H, N // 2))
     if out is None:
         out = torch.empty_like(x)
     _check_gpu("out", out, x.dtype, (bsz, L, H, P))
     d = ssd_desc(bsz, L, H, P, N, G, 0, io)
-    if trap:
+    if fn == "mssm_mamba3_siso_update":
+        st = lib.mssm_mamba3_siso_update(ctypes.byref(d), _ptr(state), _ptr(x_prev), _ptr(B_prev), _ptr(x),
+                                         _ptr(delta), _ptr(lam), _ptr(A), _ptr(omega), _ptr(B), _ptr(C), _ptr(D),
+                                         _ptr(z), _ptr(out), _stream_handle(stream))
+    elif trap:
         st = lib.mssm_ssd_trapezoidal_state_update(ctypes.byref(d), _ptr(state), _ptr(x_prev), _ptr(B_prev), _ptr(x),
                                                    _ptr(delta), _ptr(lam), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
                                                    _ptr(z), _ptr(out), _stream_handle(stream))

@@ -330,7 +330,8 @@ namespace {
 // both multi-head decode rules: lam == nullptr (want_lam false) is the Mamba-2 rule
 int ssd_update_impl(const mssm_ssd_desc* desc, float* state, const void* x_prev, const void* B_prev,
                     const void* x, const void* delta, const void* lam, bool want_lam, const float* A,
-                    const void* B, const void* C, const float* D, const void* z, void* out, void* stream) {
+                    const float* omega, bool want_omega, const void* B, const void* C, const float* D,
+                    const void* z, void* out, void* stream) {
   const mssm_ssd_desc* d = desc;
   if (d == nullptr) return MSSM_ERR_INVALID_ARG;
   if (d->batch < 0 || d->seqlen < 0 || d->nheads <= 0 || d->headdim <= 0 || d->dstate <= 0 || d->ngroups <= 0)
@@ -338,6 +339,7 @@ int ssd_update_impl(const mssm_ssd_desc* desc, float* state, const void* x_prev,
   if (d->flags != 0) return MSSM_ERR_INVALID_ARG;
   if (d->io_dtype != MSSM_BF16 && d->io_dtype != MSSM_F32) return MSSM_ERR_UNSUPPORTED;
   if (d->nheads % d->ngroups != 0 || d->dstate > 256) return MSSM_ERR_UNSUPPORTED;
+  if (want_omega && d->dstate % 2 != 0) return MSSM_ERR_UNSUPPORTED;   // complex state: whole pairs
   const int64_t es = d->io_dtype == MSSM_BF16 ? 2 : 4;
   int64_t n_x = 0, n_bc = 0, n_st = 0, n_d = 0, t = 0;
   if (!mul_ok(d->batch, d->seqlen, &t) || !mul_ok(t, d->nheads, &n_d) || !mul_ok(n_d, d->headdim, &n_x) ||
@@ -354,16 +356,17 @@ int ssd_update_impl(const mssm_ssd_desc* desc, float* state, const void* x_prev,
       out == nullptr)
     return MSSM_ERR_INVALID_ARG;
   if (want_lam && lam == nullptr) return MSSM_ERR_INVALID_ARG;
+  if (want_omega && omega == nullptr) return MSSM_ERR_INVALID_ARG;
   if (!aligned(x, es) || !aligned(delta, es) || !aligned(B, es) || !aligned(C, es) || !aligned(z, es) ||
       !aligned(out, es) || !aligned(A, 4) || !aligned(D, 4) || !aligned(state, 4) || !aligned(lam, es) ||
-      !aligned(x_prev, es) || !aligned(B_prev, es))
+      !aligned(x_prev, es) || !aligned(B_prev, es) || !aligned(omega, 4))
     return MSSM_ERR_MISALIGNED;
   const int64_t b_io = n_x * es, b_st = n_st * 4;
   const int64_t b_xp = d->batch * d->nheads * d->headdim * es, b_bp = d->batch * d->ngroups * d->dstate * es;
-  const void* ins[] = {x, delta, B, C, z, A, D, lam, x_prev, B_prev};
+  const void* ins[] = {x, delta, B, C, z, A, D, lam, x_prev, B_prev, omega};
   const int64_t inb[] = {b_io, n_d * es, n_bc * es, n_bc * es, b_io, d->nheads * 4, d->nheads * 4, n_d * es,
-                         b_xp, b_bp};
-  for (int i = 0; i < 10; ++i) {
+                         b_xp, b_bp, d->nheads * (d->dstate / 2) * 4};
+  for (int i = 0; i < 11; ++i) {
     if (overlap(out, b_io, ins[i], inb[i])) return MSSM_ERR_INVALID_ARG;
     if (overlap(state, b_st, ins[i], inb[i])) return MSSM_ERR_INVALID_ARG;
   }
@@ -376,6 +379,7 @@ int ssd_update_impl(const mssm_ssd_desc* desc, float* state, const void* x_prev,
   a.H = d->nheads; a.P = d->headdim; a.G = d->ngroups; a.io = d->io_dtype;
   if (want_lam) {
     a.lam = lam; a.x_prev = x_prev; a.B_prev = B_prev;
+    if (want_omega) a.omega = omega;
   }
   const hipError_t e = mssm::ssd_update_launch(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
@@ -391,14 +395,22 @@ extern "C" {
 int mssm_ssd_state_update(const mssm_ssd_desc* desc, float* state, const void* x, const void* delta,
                           const float* A, const void* B, const void* C, const float* D, const void* z, void* out,
                           void* stream) {
-  return ssd_update_impl(desc, state, nullptr, nullptr, x, delta, nullptr, false, A, B, C, D, z, out, stream);
+  return ssd_update_impl(desc, state, nullptr, nullptr, x, delta, nullptr, false, A, nullptr, false, B, C, D, z, out,
+                         stream);
 }
 
 int mssm_ssd_trapezoidal_state_update(const mssm_ssd_desc* desc, float* state, const void* x_prev,
                                       const void* B_prev, const void* x, const void* delta, const void* lam,
                                       const float* A, const void* B, const void* C, const float* D, const void* z,
                                       void* out, void* stream) {
-  return ssd_update_impl(desc, state, x_prev, B_prev, x, delta, lam, true, A, B, C, D, z, out, stream);
+  return ssd_update_impl(desc, state, x_prev, B_prev, x, delta, lam, true, A, nullptr, false, B, C, D, z, out,
+                         stream);
+}
+
+int mssm_mamba3_siso_update(const mssm_ssd_desc* desc, float* state, const void* x_prev, const void* B_prev,
+                            const void* x, const void* delta, const void* lam, const float* A, const float* omega,
+                            const void* B, const void* C, const float* D, const void* z, void* out, void* stream) {
+  return ssd_update_impl(desc, state, x_prev, B_prev, x, delta, lam, true, A, omega, true, B, C, D, z, out, stream);
 }
 
 // --------------------------------------------------------------------------

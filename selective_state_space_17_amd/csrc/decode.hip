@@ -14,6 +14,9 @@
 //   Mamba-3 SISO rule (TRAP; "Mamba-3" blog, "El modelo Mamba-3" item 1), with a = exp(delta A[h]):
 //                            S <- a S + (1 - lam) delta a B_prev[g,n] x_prev[p] + lam delta B[g,n] x[p]
 //   where x_prev, B_prev are the previous token's (given for the first new token; zero if absent).
+//   Complex-valued state (ROT; "El modelo Mamba-3" item 2, rotations per "Arquitectura"): each state
+//   pair (2k, 2k+1) is one complex number and the transition exp(delta (A[h] + i omega[h,k])) also
+//   rotates it by delta*omega: (u, v) <- (c u - s v, s u + c v), c, s = cos, sin(delta*omega).
 // The work per token is a few operations per byte of state, so the kernels
 // are bound by HBM: one thread owns 4 consecutive states of one row (one
 // 16-byte load and store when the layout allows), a row's threads are
@@ -140,6 +143,7 @@ struct UpdParams {
   const void* lam;         // [batch, L, H]
   const void* x_prev;      // [batch, H, P], nullable
   const void* B_prev;      // [batch, G, N], nullable
+  const float* omega;      // [H, N/2] (ROT)
 };
 
 // Each thread owns S states (4, or 8 when dstate allows: two 16-byte loads
@@ -247,8 +251,9 @@ __global__ __launch_bounds__(kThreads) void scan_update_kernel(UpdParams p) {
 }
 
 // multi-head form: row = (b, h, p), state [batch, H, P, N]
-template <typename T, bool VEC, int S, bool TRAP>
+template <typename T, bool VEC, int S, bool TRAP, bool ROT>
 __global__ __launch_bounds__(kThreads) void ssd_update_kernel(UpdParams p) {
+  static_assert(!ROT || (TRAP && S % 2 == 0), "the complex state comes with the trapezoidal rule, whole pairs");
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
   const int64_t row0 = gid / p.lpr;
   const int64_t rstride = static_cast<int64_t>(gridDim.x) * kThreads / p.lpr;
@@ -266,6 +271,7 @@ __global__ __launch_bounds__(kThreads) void ssd_update_kernel(UpdParams p) {
   int64_t rr[R], pp[R], hd[R], bb[R], gg[R];
   float h[R][S], a2[R], Dh[R];
   float up[R], bp[R][S];   // TRAP: the previous token's x (this row) and B (this lane's states)
+  float om[R][S / 2];      // ROT: rotation rates of this lane's state pairs
 #pragma unroll
   for (int k = 0; k < R; ++k) {
     const int64_t row = row0 + k * rstride;
@@ -279,6 +285,10 @@ __global__ __launch_bounds__(kThreads) void ssd_update_kernel(UpdParams p) {
     loadS<S, VEC>(p.state + rr[k] * N, n0, N, h[k]);
     a2[k] = p.A[hd[k]] * kLog2e;
     Dh[k] = p.D != nullptr ? p.D[hd[k]] : 0.f;
+    if constexpr (ROT) {
+#pragma unroll
+      for (int j = 0; j < S / 2; ++j) om[k][j] = n0 + 2 * j < N ? p.omega[hd[k] * (N / 2) + n0 / 2 + j] : 0.f;
+    }
     if constexpr (TRAP) {
       up[k] = p.x_prev != nullptr ? to_f32(static_cast<const T*>(p.x_prev)[rr[k]]) : 0.f;   // rows are (b, h, p)
       if (p.B_prev != nullptr) {
@@ -306,7 +316,26 @@ __global__ __launch_bounds__(kThreads) void ssd_update_kernel(UpdParams p) {
     for (int k = 0; k < R; ++k) {
       const float dA = exp2_hw(d[k] * a2[k]), du = d[k] * u[k];
       float acc = 0.f;
-      if constexpr (TRAP) {
+      if constexpr (ROT) {
+        // a R(d omega) (S + (1 - lam) d x_prev B_prev) + lam d x B, pair by pair
+        const float wl = (1.f - lm[k]) * d[k] * up[k], wr = lm[k] * du;
+#pragma unroll
+        for (int j = 0; j < S / 2; ++j) {
+          float sn, cs;
+          sincosf(d[k] * om[k][j], &sn, &cs);
+          const float tu = __builtin_fmaf(wl, bp[k][2 * j], h[k][2 * j]);
+          const float tv = __builtin_fmaf(wl, bp[k][2 * j + 1], h[k][2 * j + 1]);
+          const float ru = __builtin_fmaf(cs, tu, -(sn * tv)), rv = __builtin_fmaf(sn, tu, cs * tv);
+          h[k][2 * j] = __builtin_fmaf(dA, ru, wr * bv[k][2 * j]);
+          h[k][2 * j + 1] = __builtin_fmaf(dA, rv, wr * bv[k][2 * j + 1]);
+        }
+#pragma unroll
+        for (int q = 0; q < S; ++q) {
+          acc = __builtin_fmaf(cv[k][q], h[k][q], acc);
+          bp[k][q] = bv[k][q];
+        }
+        up[k] = u[k];
+      } else if constexpr (TRAP) {
         // a (S + (1 - lam) d x_prev B_prev) + lam d x B
         const float wl = (1.f - lm[k]) * d[k] * up[k], wr = lm[k] * du;
 #pragma unroll
@@ -382,8 +411,9 @@ hipError_t launch_update(UpdParams p, const UpdateArgs& a, bool mamba1, hipStrea
 }
 template <typename T, bool VEC, int S> struct ScanUpd { static constexpr auto fn = scan_update_kernel<T, VEC, S, false>; };
 template <typename T, bool VEC, int S> struct ScanUpdConv { static constexpr auto fn = scan_update_kernel<T, VEC, S, true>; };
-template <typename T, bool VEC, int S> struct SsdUpd { static constexpr auto fn = ssd_update_kernel<T, VEC, S, false>; };
-template <typename T, bool VEC, int S> struct SsdUpdTrap { static constexpr auto fn = ssd_update_kernel<T, VEC, S, true>; };
+template <typename T, bool VEC, int S> struct SsdUpd { static constexpr auto fn = ssd_update_kernel<T, VEC, S, false, false>; };
+template <typename T, bool VEC, int S> struct SsdUpdTrap { static constexpr auto fn = ssd_update_kernel<T, VEC, S, true, false>; };
+template <typename T, bool VEC, int S> struct SsdUpdRot { static constexpr auto fn = ssd_update_kernel<T, VEC, S, true, true>; };
 
 }  // namespace
 
@@ -406,6 +436,11 @@ hipError_t ssd_update_launch(const UpdateArgs& a, hipStream_t stream) {
   p.rows = a.batch * a.H * a.P;
   if (a.lam != nullptr) {
     p.lam = a.lam; p.x_prev = a.x_prev; p.B_prev = a.B_prev;
+    if (a.omega != nullptr) {   // dstate is even: lanes own whole pairs (groups of 4 or 8 from a multiple of 4)
+      p.omega = a.omega;
+      return a.io == 1 ? launch_update<SsdUpdRot, uint16_t>(p, a, false, stream)
+                       : launch_update<SsdUpdRot, float>(p, a, false, stream);
+    }
     return a.io == 1 ? launch_update<SsdUpdTrap, uint16_t>(p, a, false, stream)
                      : launch_update<SsdUpdTrap, float>(p, a, false, stream);
   }

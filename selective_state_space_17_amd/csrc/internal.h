@@ -102,6 +102,7 @@ struct UpdateArgs {
   const void* lam = nullptr;       // [batch, L, H]; nullable = the Mamba-2 rule
   const void* x_prev = nullptr;    // [batch, H, P], the token before the first one; nullable = none
   const void* B_prev = nullptr;    // [batch, G, N], likewise
+  const float* omega = nullptr;    // [H, N/2] rotation rates of the state pairs (complex state); nullable
 };
 
 hipError_t scan_update_launch(const UpdateArgs& a, hipStream_t stream);

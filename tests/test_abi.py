@@ -309,6 +309,27 @@ def test_ssd_trapezoidal_state_update_checks():
     assert call([None] * 12, s) == M.MSSM_OK
 
 
+def test_mamba3_siso_update_checks():
+    """The complex-state update: the trapezoidal update's rules, plus omega required, aligned, not
+    overlapping the outputs, and an even dstate."""
+    d = M.ssd_desc(2, 1, 4, 64, 64, 1, 0)
+    # state, x_prev, B_prev, x, delta, lam, A, omega, B, C, D, z, out
+    args = [BASE + 600 * MB, BASE + 700 * MB, BASE + 800 * MB, BASE, BASE + 100 * MB, BASE + 150 * MB,
+            BASE + 200 * MB, BASE + 250 * MB, BASE + 300 * MB, BASE + 400 * MB, None, None, BASE + 500 * MB]
+    call = lambda a, dd=d: M.lib.mssm_mamba3_siso_update(ctypes.byref(dd), *a, None)
+    bad = list(args); bad[7] = None
+    assert call(bad) == M.MSSM_ERR_INVALID_ARG              # omega missing
+    bad = list(args); bad[5] = None
+    assert call(bad) == M.MSSM_ERR_INVALID_ARG              # lam missing
+    bad = list(args); bad[7] = BASE + 250 * MB + 2
+    assert call(bad) == M.MSSM_ERR_MISALIGNED
+    bad = list(args); bad[0] = BASE + 250 * MB
+    assert call(bad) == M.MSSM_ERR_INVALID_ARG              # state overlaps omega
+    odd = M.ssd_desc(2, 1, 4, 64, 63, 1, 0)
+    assert call(args, odd) == M.MSSM_ERR_UNSUPPORTED        # the state pairs need an even dstate
+    assert call([None] * 13, M.ssd_desc(2, 0, 4, 64, 64, 1, 0)) == M.MSSM_OK   # no tokens
+
+
 def _bwd_call(desc, ws=BASE + 2000 * MB, ws_bytes=None, **kw):
     a = dict(x=BASE, delta=BASE + 100 * MB, A=BASE + 200 * MB, B=BASE + 300 * MB, C=BASE + 400 * MB, D=None,
              z=None, h0=None, dout=BASE + 500 * MB, dfinal=None, dx=BASE + 600 * MB, ddelta=BASE + 700 * MB,

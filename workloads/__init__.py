@@ -15,7 +15,9 @@ Recipe (the workloads the pages describe, made concrete):
     (token, group).
   * Mamba-3 SISO rule (page "Mamba-3", "El modelo Mamba-3"): the weight lam
     per (token, head), sigmoid(N(0, 1)), as a gate computed from the token
-    would give; for its decode step, the previous token's x and B ~ N(0, 1).
+    would give; for its decode step, the previous token's x and B ~ N(0, 1);
+    for the complex-valued state, rotation rates omega ~ U(-pi, pi) per
+    (head, state pair).
 
 Distributions: x, z, B, C ~ N(0, 1); D ~ N(0, 1) per channel;
 delta = softplus(0.5 * N(0, 1) - 2) evaluated in fp32; S4D-real A[c, n] =
@@ -40,7 +42,8 @@ ROOT_SEED = 1700
 BLOCK = 1 << 22
 
 # tensor ids (fixed order of the per-tensor streams)
-T_X, T_DELTA, T_Z, T_B, T_C, T_D, T_A, T_H0, T_DOUT, T_DFIN, T_CW, T_CB, T_CI, T_LAM, T_XPREV, T_BPREV = range(16)
+T_X, T_DELTA, T_Z, T_B, T_C, T_D, T_A, T_H0, T_DOUT, T_DFIN, T_CW, T_CB, T_CI, T_LAM, T_XPREV, T_BPREV, T_OMEGA = \
+    range(17)
 
 F32 = "f32"
 BF16 = "bf16"
@@ -116,6 +119,7 @@ class SSDConfig:
     return_final: bool = True
     decode: bool = False    # token-by-token update of a stored state (read and written in place)
     trapezoidal: bool = False   # Mamba-3 exponential-trapezoidal input rule (one more [B, L, H] input, lam)
+    complex_state: bool = False  # Mamba-3 complex-valued state: rotation rates omega [H, N/2] fp32
 
     @property
     def updates(self) -> int:
@@ -136,13 +140,14 @@ class SSDConfig:
         n += self.batch * self.nheads * self.headdim * self.dstate * 4 if self.decode else 0
         if self.decode and self.trapezoidal:   # the previous token's x and B
             n += (self.batch * self.nheads * self.headdim + self.batch * self.ngroups * self.dstate) * e
+        n += self.nheads * (self.dstate // 2) * 4 if self.complex_state else 0   # omega
         return n
 
 
 # The workloads by id.  1 is the small fp32 case; 2 is the 130M-like layer
 # the throughput figure is quoted on; 3-5 are the larger forward layers and
 # the SSD form; 6-12 add the decode step, gradients, the convolution in front,
-# the training step and the Mamba-3 rule on the same shapes.
+# the training step and the Mamba-3 rule (13: with the complex state) on the same shapes.
 CONFIGS = {
     1: ScanConfig("mamba1_tiny_f32", 1, 1, 256, 64, 16, F32, "s4d_real", return_final=True),
     2: ScanConfig("mamba1_130m_layer_bf16", 2, 8, 2048, 1536, 16, BF16, "exp_log", return_final=False),
@@ -167,6 +172,9 @@ CONFIGS = {
     # its decode step at config 7's serving shape (the previous token's x and B are inputs too)
     12: SSDConfig("mamba3_siso_decode_bf16", 12, 64, 1, 32, 64, 128, 1, 64, BF16, True, True, True, decode=True,
                   trapezoidal=True),
+    # the same decode step with the complex-valued state (each state pair rotated by delta * omega)
+    13: SSDConfig("mamba3_siso_complex_decode_bf16", 13, 64, 1, 32, 64, 128, 1, 64, BF16, True, True, True,
+                  decode=True, trapezoidal=True, complex_state=True),
 }
 
 
@@ -375,6 +383,13 @@ def make_ssd_prev(cfg: SSDConfig, seed_base: int = ROOT_SEED):
     xp = normal(cfg.cfg_id, T_XPREV, cfg.batch * cfg.nheads * cfg.headdim, cfg.io, seed_base)
     bp = normal(cfg.cfg_id, T_BPREV, cfg.batch * cfg.ngroups * cfg.dstate, cfg.io, seed_base)
     return xp.reshape(cfg.batch, cfg.nheads, cfg.headdim), bp.reshape(cfg.batch, cfg.ngroups, cfg.dstate)
+
+
+def make_ssd_omega(cfg: SSDConfig, seed_base: int = ROOT_SEED) -> np.ndarray:
+    """Rotation rates of the complex-valued state, omega [H, N/2] fp32 ~ U(-pi, pi): with the workloads'
+    delta a state pair turns by a few tenths of a radian per step."""
+    n = cfg.nheads * (cfg.dstate // 2)
+    return uniform_f32(cfg.cfg_id, T_OMEGA, n, -np.pi, np.pi, seed_base).reshape(cfg.nheads, cfg.dstate // 2)
 
 
 def scan_config(batch: int, seqlen: int, dim: int, dstate: int, io: str = F32, a_kind: str = "s4d_real",

@@ -43,6 +43,16 @@ template <> __device__ __forceinline__ uint16_t from_f32<uint16_t>(float v) {
 __device__ __forceinline__ float exp2_hw(float v) { return __builtin_amdgcn_exp2f(v); }
 __device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.f + exp2_hw(-z * kLog2e)); }
 
+// sine and cosine of an angle in radians: reduce it to revolutions in [-1/2, 1/2] (the fp32 product
+// is off by at most |angle| * 2^-24 revolutions), then the hardware's sine and cosine, which take
+// their argument in revolutions.  An angle of 0 gives exactly 0 and 1.
+__device__ __forceinline__ void sincos_rev(float angle, float& s, float& c) {
+  const float rev = angle * 0.159154943091895336f;   // 1 / (2 pi)
+  const float r = rev - __builtin_rintf(rev);
+  s = __builtin_amdgcn_sinf(r);
+  c = __builtin_amdgcn_cosf(r);
+}
+
 template <int CTRL> __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
 }
@@ -322,7 +332,7 @@ __global__ __launch_bounds__(kThreads) void ssd_update_kernel(UpdParams p) {
 #pragma unroll
         for (int j = 0; j < S / 2; ++j) {
           float sn, cs;
-          sincosf(d[k] * om[k][j], &sn, &cs);
+          sincos_rev(d[k] * om[k][j], sn, cs);
           const float tu = __builtin_fmaf(wl, bp[k][2 * j], h[k][2 * j]);
           const float tv = __builtin_fmaf(wl, bp[k][2 * j + 1], h[k][2 * j + 1]);
           const float ru = __builtin_fmaf(cs, tu, -(sn * tv)), rv = __builtin_fmaf(sn, tu, cs * tv);

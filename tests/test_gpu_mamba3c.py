@@ -4,7 +4,8 @@ ABI) against the fp64 oracle written in complex arithmetic (oracle.ssdc_fwd).
 The update kernel keeps the state in its own frame and rotates each state pair by delta * omega per step.
 Cases: whole sequences in one call (the recurrent sequence form), token by token with the previous
 token passed along, a given previous token, fp32 and bf16, 8 and 4 states per lane and the scalar path,
-omega = 0 against the real trapezoidal update bit for bit, and the decode workload the benchmark times."""
+omega = 0 against the real trapezoidal update bit for bit, rotation rates large enough that one step
+turns a pair by hundreds of radians, and the decode workload the benchmark times."""
 import numpy as np
 import pytest
 
@@ -127,3 +128,22 @@ def test_mamba3_complex_decode_config_full(M):
     torch.cuda.synchronize()
     check(host64(out), ref, RTOL["bf16"], f"{cfg.name} out")
     check(host64(state), ref_fin, RTOL["bf16"], f"{cfg.name} state")
+
+
+def test_mamba3_complex_large_angles(M):
+    """Rotation rates up to 300 per unit delta, so each step turns a pair by tens to hundreds of radians.
+    The angle reaches the hardware sine and cosine after reduction to revolutions, whose error grows
+    like |angle| * 2^-24 revolutions; at the bf16 bar the results still agree with the oracle's exact
+    complex exponential."""
+    import torch
+    case = (2, 120, 4, 32, 32, 1, "bf16", True, True)
+    cfg, s, lam, om = inputs(case, 1470)
+    om = (om * (300.0 / np.pi)).astype(np.float32)
+    say("mamba3 complex large angles")
+    ref, ref_fin = oracle.ssdc_fwd(s.x, s.delta, lam, s.A, om, s.B, s.C, s.D, s.z, s.h0)
+    state = dev(s.h0).clone()
+    out = M.mamba3_siso_update(state, dev(s.x), dev(s.delta), dev(lam), dev(s.A), dev(om), dev(s.B), dev(s.C),
+                               dev(s.D), dev(s.z))
+    torch.cuda.synchronize()
+    check(host64(out), ref, RTOL["bf16"], "large angles out")
+    check(host64(state), ref_fin, RTOL["bf16"], "large angles state")

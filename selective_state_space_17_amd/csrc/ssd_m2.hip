@@ -238,7 +238,8 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
   const int xi = tid % 256, xp = xi % 32, xc = xi / 32;
   const bool is_x = tid < 256;
   const uint16_t* const vg = is_x ? xg : zg;
-  u32x4 b0reg, b1reg, creg[CL], v0reg, v1reg;
+  const bool v_live = is_x || has_z;   // without z, waves 4-7 load nothing here
+  u32x4 b0reg, b1reg, creg[CL], v0reg = {0, 0, 0, 0}, v1reg = {0, 0, 0, 0};
   uint16_t dreg = 0;
   // TRAP: lam of the step, delta and lam of the step after it (which may open
   // the next block; past the end of the sequence it does not exist: weight 0)
@@ -276,8 +277,10 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
     b1reg = *reinterpret_cast<const u32x4*>(bt + ob[1]);
 #pragma unroll
     for (int i = 0; i < CL; ++i) creg[i] = *reinterpret_cast<const u32x4*>(ct + oc[i]);
-    v0reg = *reinterpret_cast<const u32x4*>(vt + ov[0]);
-    v1reg = *reinterpret_cast<const u32x4*>(vt + ov[1]);
+    if (v_live) {
+      v0reg = *reinterpret_cast<const u32x4*>(vt + ov[0]);
+      v1reg = *reinterpret_cast<const u32x4*>(vt + ov[1]);
+    }
     if (tid < QB) {
       const int64_t ts = t0 + (tid < nvalid ? tid : nvalid - 1);
       dreg = dg[ts * H];

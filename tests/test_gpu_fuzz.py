@@ -1,0 +1,161 @@
+"""Seeded random shapes through every forward and update entry point, against the fp64 oracle.
+
+The hand-picked cases elsewhere cover the known corners; these draw batch, length, widths, state size,
+I/O type and the optional operands at random (fixed seeds, so every run sees the same shapes), to reach
+planner choices, ragged tails and partial blocks that no one thought to list. Sizes stay small enough
+for the oracle to finish each case in well under a second."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_util import RTOL, check, dev, host64, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def M():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import selective_state_space_17_amd as m
+    return m
+
+
+def _scan_case(seed):
+    r = np.random.default_rng(seed)
+    b = int(r.integers(1, 4))
+    l = int(r.integers(1, 900))
+    d = int(r.integers(1, 300))
+    n = int(r.choice([1, 2, 3, 4, 7, 8, 12, 16, 16, 16, 24, 32, 48, 64]))
+    io = str(r.choice(["f32", "bf16"]))
+    return b, l, d, n, io, bool(r.integers(2)), bool(r.integers(2)), bool(r.integers(2))
+
+
+def _ssd_case(seed):
+    r = np.random.default_rng(seed)
+    g = int(r.choice([1, 1, 2, 4]))
+    h = g * int(r.integers(1, 4))
+    p = int(r.choice([64, 64, 128]))
+    n = 16 * int(r.integers(1, 9))
+    b = int(r.integers(1, 3))
+    l = int(r.integers(1, 300))
+    return b, l, h, p, n, g, bool(r.integers(2)), bool(r.integers(2)), bool(r.integers(2))
+
+
+SCAN_SEEDS = list(range(7100, 7114))
+SSD_SEEDS = list(range(7200, 7210))
+
+
+@pytest.mark.parametrize("seed", SCAN_SEEDS)
+def test_fuzz_scan_fwd(M, seed):
+    import torch
+    b, l, d, n, io, hd, hz, hh = case = _scan_case(seed)
+    say("fuzz scan fwd", seed, case)
+    cfg = W.scan_config(b, l, d, n, io=io, has_D=hd, has_z=hz, cfg_id=seed)
+    inp = W.make_scan_inputs(cfg, with_h0=hh)
+    out, fin = M.selective_scan_fwd(dev(inp.x), dev(inp.delta), dev(inp.A), dev(inp.B), dev(inp.C), dev(inp.D),
+                                    dev(inp.z), dev(inp.h0), return_final_state=True)
+    torch.cuda.synchronize()
+    ref, ref_fin = oracle.scan_fwd(inp.x, inp.delta, inp.A, inp.B, inp.C, inp.D, inp.z, inp.h0)
+    check(host64(out), ref, RTOL[io], f"{case} out")
+    check(host64(fin), ref_fin, RTOL[io], f"{case} final_state")
+
+
+@pytest.mark.parametrize("seed", SCAN_SEEDS[:8])
+def test_fuzz_scan_update(M, seed):
+    """The decode step over a few tokens from a stored state, at random widths and state sizes (up to 256)."""
+    import torch
+    r = np.random.default_rng(seed + 50)
+    b, d = int(r.integers(1, 9)), int(r.integers(1, 400))
+    n = int(r.integers(1, 257))
+    l = int(r.integers(1, 5))
+    io = str(r.choice(["f32", "bf16"]))
+    hd, hz = bool(r.integers(2)), bool(r.integers(2))
+    say("fuzz scan update", seed, (b, l, d, n, io, hd, hz))
+    cfg = W.scan_config(b, l, d, n, io=io, has_D=hd, has_z=hz, cfg_id=seed + 50)
+    inp = W.make_scan_inputs(cfg, with_h0=True)
+    state = dev(inp.h0).clone()
+    out = M.selective_state_update(state, dev(inp.x), dev(inp.delta), dev(inp.A), dev(inp.B), dev(inp.C),
+                                   dev(inp.D), dev(inp.z))
+    torch.cuda.synchronize()
+    ref, ref_fin = oracle.scan_fwd(inp.x, inp.delta, inp.A, inp.B, inp.C, inp.D, inp.z, inp.h0)
+    check(host64(out), ref, RTOL[io], "update out")
+    check(host64(state), ref_fin, RTOL[io], "update state")
+
+
+@pytest.mark.parametrize("seed", SSD_SEEDS)
+def test_fuzz_ssd_fwd(M, seed):
+    import torch
+    b, l, h, p, n, g, hd, hz, hh = case = _ssd_case(seed)
+    say("fuzz ssd fwd", seed, case)
+    cfg = W.ssd_config(b, l, h, p, n, g, cfg_id=seed)
+    s = W.make_ssd_inputs(cfg, with_D=hd, with_z=hz, with_h0=hh)
+    out, fin = M.ssd_fwd(dev(s.x), dev(s.delta), dev(s.A), dev(s.B), dev(s.C), dev(s.D), dev(s.z), dev(s.h0),
+                         return_final_state=True)
+    torch.cuda.synchronize()
+    ref, ref_fin = oracle.ssd_fwd(s.x, s.delta, s.A, s.B, s.C, s.D, s.z, s.h0)
+    check(host64(out), ref, RTOL["bf16"], f"{case} out")
+    check(host64(fin), ref_fin, RTOL["bf16"], f"{case} final_state")
+
+
+@pytest.mark.parametrize("seed", SSD_SEEDS[:6])
+def test_fuzz_ssd_trapezoidal_fwd(M, seed):
+    import torch
+    b, l, h, p, n, g, hd, hz, hh = case = _ssd_case(seed + 30)
+    say("fuzz ssd trapezoidal fwd", seed, case)
+    cfg = W.ssd_config(b, l, h, p, n, g, cfg_id=seed + 30)
+    s = W.make_ssd_inputs(cfg, with_D=hd, with_z=hz, with_h0=hh)
+    lam = W.make_ssd_lam(cfg)
+    out, fin = M.ssd_trapezoidal_fwd(dev(s.x), dev(s.delta), dev(lam), dev(s.A), dev(s.B), dev(s.C), dev(s.D),
+                                     dev(s.z), dev(s.h0), return_final_state=True)
+    torch.cuda.synchronize()
+    ref, ref_fin = oracle.ssd3_fwd(s.x, s.delta, lam, s.A, s.B, s.C, s.D, s.z, s.h0)
+    check(host64(out), ref, RTOL["bf16"], f"{case} out")
+    check(host64(fin), ref_fin, RTOL["bf16"], f"{case} final_state")
+
+
+@pytest.mark.parametrize("seed", SSD_SEEDS[:8])
+def test_fuzz_ssd_updates(M, seed):
+    """The three multi-head decode steps (Mamba-2, the trapezoidal rule, the complex state) at random
+    head counts, headdims (any size) and even state sizes up to 256, with either I/O type."""
+    import torch
+    r = np.random.default_rng(seed + 70)
+    g = int(r.choice([1, 2]))
+    h = g * int(r.integers(1, 5))
+    p = int(r.integers(1, 96))
+    n = 2 * int(r.integers(1, 129))
+    b, l = int(r.integers(1, 5)), int(r.integers(1, 5))
+    io = str(r.choice(["f32", "bf16"]))
+    hd, hz = bool(r.integers(2)), bool(r.integers(2))
+    case = (b, l, h, p, n, g, io, hd, hz)
+    say("fuzz ssd updates", seed, case)
+    cfg = W.ssd_config(b, l, h, p, n, g, io=io, cfg_id=seed + 70)
+    s = W.make_ssd_inputs(cfg, with_D=hd, with_z=hz, with_h0=True)
+    lam, om = W.make_ssd_lam(cfg), W.make_ssd_omega(cfg)
+    xp, bp = W.make_ssd_prev(cfg)
+    args = [dev(a) for a in (s.x, s.delta)]
+
+    st = dev(s.h0).clone()
+    out = M.ssd_state_update(st, *args, dev(s.A), dev(s.B), dev(s.C), dev(s.D), dev(s.z))
+    torch.cuda.synchronize()
+    ref, ref_fin = oracle.ssd_fwd(s.x, s.delta, s.A, s.B, s.C, s.D, s.z, s.h0)
+    check(host64(out), ref, RTOL[io], f"{case} mamba-2 out")
+    check(host64(st), ref_fin, RTOL[io], f"{case} mamba-2 state")
+
+    st = dev(s.h0).clone()
+    out = M.ssd_trapezoidal_state_update(st, *args, dev(lam), dev(s.A), dev(s.B), dev(s.C), dev(s.D), dev(s.z),
+                                         x_prev=dev(xp), B_prev=dev(bp))
+    torch.cuda.synchronize()
+    ref, ref_fin = oracle.ssdc_fwd(s.x, s.delta, lam, s.A, np.zeros_like(om), s.B, s.C, s.D, s.z, s.h0, xp, bp)
+    check(host64(out), ref, RTOL[io], f"{case} trapezoidal out")
+    check(host64(st), ref_fin, RTOL[io], f"{case} trapezoidal state")
+
+    st = dev(s.h0).clone()
+    out = M.mamba3_siso_update(st, *args, dev(lam), dev(s.A), dev(om), dev(s.B), dev(s.C), dev(s.D), dev(s.z),
+                               x_prev=dev(xp), B_prev=dev(bp))
+    torch.cuda.synchronize()
+    ref, ref_fin = oracle.ssdc_fwd(s.x, s.delta, lam, s.A, om, s.B, s.C, s.D, s.z, s.h0, xp, bp)
+    check(host64(out), ref, RTOL[io], f"{case} complex out")
+    check(host64(st), ref_fin, RTOL[io], f"{case} complex state")

@@ -1,4 +1,5 @@
-"""Seeded random shapes through every forward and update entry point, against the fp64 oracle.
+"""Seeded random shapes through every entry point that computes (forward, decode, gradients, training-mode
+forward, convolution in front), against the fp64 oracle.
 
 The hand-picked cases elsewhere cover the known corners; these draw batch, length, widths, state size,
 I/O type and the optional operands at random (fixed seeds, so every run sees the same shapes), to reach
@@ -159,3 +160,106 @@ def test_fuzz_ssd_updates(M, seed):
     ref, ref_fin = oracle.ssdc_fwd(s.x, s.delta, lam, s.A, om, s.B, s.C, s.D, s.z, s.h0, xp, bp)
     check(host64(out), ref, RTOL[io], f"{case} complex out")
     check(host64(st), ref_fin, RTOL[io], f"{case} complex state")
+
+
+GRADS = ("dx", "ddelta", "dz", "dB", "dC", "dA", "dD", "dh0")
+
+
+def _compare_grads(g, ref, io, what):
+    for k in GRADS:
+        if ref[k] is None or g[k] is None:
+            assert (ref[k] is None) == (g[k] is None) or k == "dh0", f"{what}: {k} presence differs"
+            continue
+        check(host64(g[k]), ref[k], RTOL[io], f"{what} {k}")
+
+
+@pytest.mark.parametrize("seed", list(range(7300, 7308)))
+def test_fuzz_scan_bwd(M, seed):
+    """Gradients at random shapes with dstate up to 16. Cases that the training-mode forward takes (dstate
+    16, rows a multiple of 16 bytes) also go through it: the gradients from its checkpoints must match too."""
+    import torch
+    r = np.random.default_rng(seed)
+    io = str(r.choice(["f32", "bf16"]))
+    b, l = int(r.integers(1, 4)), int(r.integers(1, 400))
+    via_ckpt = bool(r.integers(2))
+    if via_ckpt:
+        n, d = 16, (8 if io == "bf16" else 4) * int(r.integers(1, 30))
+    else:
+        n, d = int(r.integers(1, 17)), int(r.integers(1, 200))
+    hd, hz, hh, hf = (bool(v) for v in r.integers(2, size=4))
+    case = (b, l, d, n, io, hd, hz, hh, hf, via_ckpt)
+    say("fuzz scan bwd", seed, case)
+    cfg = W.scan_config(b, l, d, n, io=io, has_D=hd, has_z=hz, cfg_id=seed)
+    inp = W.make_scan_inputs(cfg, with_h0=hh)
+    dout, dfin = W.make_scan_grads(cfg, with_dfinal=hf)
+    ref = oracle.scan_bwd(inp.x, inp.delta, inp.A, inp.B, inp.C, inp.D, inp.z, inp.h0, dout, dfin)
+    args = [dev(a) for a in (inp.x, inp.delta, inp.A, inp.B, inp.C, inp.D, inp.z, inp.h0)]
+    g = M.selective_scan_bwd(*args, dev(dout), dev(dfin))
+    torch.cuda.synchronize()
+    _compare_grads(g, ref, io, f"{case}")
+    if via_ckpt:
+        _, ck = M.selective_scan_fwd_ckpt(*args)
+        g = M.selective_scan_bwd(*args, dev(dout), dev(dfin), checkpoints=ck)
+        torch.cuda.synchronize()
+        _compare_grads(g, ref, io, f"{case} from checkpoints")
+
+
+@pytest.mark.parametrize("seed", list(range(7400, 7406)))
+def test_fuzz_conv_scan(M, seed):
+    """The convolution fused in front of the scan (dstate 16, rows a multiple of 16 bytes), random width,
+    bias, initial inputs, state and optional operands."""
+    import torch
+    r = np.random.default_rng(seed)
+    io = str(r.choice(["f32", "bf16"]))
+    b, l = int(r.integers(1, 4)), int(r.integers(1, 500))
+    d = (8 if io == "bf16" else 4) * int(r.integers(1, 40))
+    width = int(r.integers(1, 5))
+    hb, hi, hh, hd, hz = (bool(v) for v in r.integers(2, size=5))
+    case = (b, l, d, width, io, hb, hi, hh, hd, hz)
+    say("fuzz conv scan", seed, case)
+    cfg = W.scan_config(b, l, d, 16, io=io, has_D=hd, has_z=hz, cfg_id=seed)
+    inp = W.make_scan_inputs(cfg, with_h0=hh)
+    w, bias, init = W.make_conv_inputs(cfg, width, with_bias=hb, with_init=hi)
+    out, fin = M.selective_scan_conv_fwd(dev(inp.x), dev(w), dev(bias), dev(init), dev(inp.delta), dev(inp.A),
+                                         dev(inp.B), dev(inp.C), dev(inp.D), dev(inp.z), dev(inp.h0),
+                                         return_final_state=True)
+    torch.cuda.synchronize()
+    ref, ref_fin = oracle.conv_scan_fwd(inp.x, w, bias, init, inp.delta, inp.A, inp.B, inp.C, inp.D, inp.z, inp.h0)
+    check(host64(out), ref, RTOL[io], f"{case} out")
+    check(host64(fin), ref_fin, RTOL[io], f"{case} final_state")
+
+
+@pytest.mark.parametrize("seed", list(range(7500, 7506)))
+def test_fuzz_conv_update(M, seed):
+    """The decode step with the convolution window, any dstate: outputs and state against the fused
+    oracle started from the window, and the new window equal to the last W-1 inputs bit for bit."""
+    import torch
+    r = np.random.default_rng(seed)
+    io = str(r.choice(["f32", "bf16"]))
+    b, t, d = int(r.integers(1, 6)), int(r.integers(1, 6)), int(r.integers(1, 300))
+    n, width = int(r.integers(1, 129)), int(r.integers(1, 5))
+    hb, hd, hz = (bool(v) for v in r.integers(2, size=3))
+    case = (b, t, d, n, width, io, hb, hd, hz)
+    say("fuzz conv update", seed, case)
+    cfg = W.scan_config(b, t, d, n, io=io, has_D=hd, has_z=hz, cfg_id=seed)
+    inp = W.make_scan_inputs(cfg, with_h0=True)
+    w, bias, init = W.make_conv_inputs(cfg, width, with_bias=hb)
+    state = dev(inp.h0).clone()
+    cstate = dev(init).clone() if init is not None else None
+    out = M.selective_state_update_conv(state, cstate, dev(inp.x), dev(w), dev(bias), dev(inp.delta), dev(inp.A),
+                                        dev(inp.B), dev(inp.C), dev(inp.D), dev(inp.z))
+    torch.cuda.synchronize()
+    ref, ref_fin = oracle.conv_scan_fwd(inp.x, w, bias, init, inp.delta, inp.A, inp.B, inp.C, inp.D, inp.z, inp.h0)
+    check(host64(out), ref, RTOL[io], f"{case} out")
+    check(host64(state), ref_fin, RTOL[io], f"{case} state")
+    if width > 1:
+        want = np.concatenate([init, inp.x], axis=1)[:, -(width - 1):]
+        assert np.array_equal(host_raw(cstate), want), f"{case}: window"
+
+
+def host_raw(t):
+    """A device tensor's elements as stored (bf16 as its uint16 bits), for bit-exact comparisons."""
+    import torch
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()

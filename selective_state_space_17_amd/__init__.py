@@ -96,28 +96,38 @@ def abi_version() -> int:
     return lib.mssm_abi_version()
 
 
+_TORCH = None
+
+
 def _torch():
-    import torch
-    return torch
+    global _TORCH
+    if _TORCH is None:
+        import torch
+        _TORCH = torch
+    return _TORCH
 
 
 def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
-def _check_gpu(name, t, dtype, shape):
-    torch = _torch()
+def _check_gpu(name, t, dtype, shape, cur):
+    # Every check here runs on each call, so each uses the cheapest accessor (a decode step's
+    # call is otherwise dominated by them): cur is the current device, looked up once per call,
+    # get_device() is an int (-1 off the GPU), and a torch.Size compares equal to a tuple of
+    # the same sizes.
     if t is None:
         return
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a GPU tensor")
-    if t.device.index != torch.cuda.current_device():
+    where = t.get_device()
+    if where != cur:
+        if where < 0:
+            raise ValueError(f"{name} must be a GPU tensor")
         # the kernels run on the current device: a pointer into another GPU's memory would fault there
-        raise ValueError(f"{name} is on {t.device}, but the current device is cuda:{torch.cuda.current_device()} "
+        raise ValueError(f"{name} is on {t.device}, but the current device is cuda:{cur} "
                          "(use torch.cuda.device(...) around the call)")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    if tuple(t.shape) != tuple(shape):
+    if t.shape != tuple(shape):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
@@ -134,10 +144,14 @@ def _io_code(dtype) -> int:
 
 def _stream_handle(stream) -> int:
     torch = _torch()
-    s = stream if stream is not None else torch.cuda.current_stream()
-    if s.device.index != torch.cuda.current_device():
-        raise ValueError(f"stream belongs to {s.device}, but the current device is cuda:{torch.cuda.current_device()}")
-    return s.cuda_stream
+    if stream is None:
+        # the current stream of the current device (under graph capture: the capturing stream), as
+        # its raw handle, without building a Stream object
+        return torch._C._cuda_getCurrentRawStream(torch.cuda.current_device())
+    if stream.device.index != torch.cuda.current_device():
+        raise ValueError(f"stream belongs to {stream.device}, but the current device is "
+                         f"cuda:{torch.cuda.current_device()}")
+    return stream.cuda_stream
 
 
 def scan_desc(batch, seqlen, dim, dstate, io_dtype, split_seq=0, split_state=0) -> ScanDesc:
@@ -177,18 +191,19 @@ def selective_scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, return_final_
         raise ValueError("A must be [dim, dstate]")
     N = A.shape[1]
     io = _io_code(x.dtype)
+    cur = _torch().cuda.current_device()
     for name, t, shape in (("x", x, (bsz, L, dm)), ("delta", delta, (bsz, L, dm)), ("z", z, (bsz, L, dm)),
                            ("B", B, (bsz, L, N)), ("C", C, (bsz, L, N))):
-        _check_gpu(name, t, x.dtype, shape)
-    _check_gpu("A", A, torch.float32, (dm, N))
-    _check_gpu("D", D, torch.float32, (dm,))
-    _check_gpu("h0", h0, torch.float32, (bsz, dm, N))
+        _check_gpu(name, t, x.dtype, shape, cur)
+    _check_gpu("A", A, torch.float32, (dm, N), cur)
+    _check_gpu("D", D, torch.float32, (dm,), cur)
+    _check_gpu("h0", h0, torch.float32, (bsz, dm, N), cur)
     if out is None:
         out = torch.empty_like(x)
-    _check_gpu("out", out, x.dtype, (bsz, L, dm))
+    _check_gpu("out", out, x.dtype, (bsz, L, dm), cur)
     if return_final_state and final_state is None:
         final_state = torch.empty((bsz, dm, N), dtype=torch.float32, device=x.device)
-    _check_gpu("final_state", final_state, torch.float32, (bsz, dm, N))
+    _check_gpu("final_state", final_state, torch.float32, (bsz, dm, N), cur)
     d = scan_desc(bsz, L, dm, N, io, split_seq, split_state)
     ws_bytes = lib.mssm_selective_scan_workspace_size(ctypes.byref(d))
     if ws_bytes and workspace is None:
@@ -222,18 +237,19 @@ def selective_scan_fwd_ckpt(x, delta, A, B, C, D=None, z=None, h0=None, checkpoi
         raise ValueError("A must be [dim, dstate]")
     N = A.shape[1]
     io = _io_code(x.dtype)
+    cur = _torch().cuda.current_device()
     for name, t, shape in (("x", x, (bsz, L, dm)), ("delta", delta, (bsz, L, dm)), ("z", z, (bsz, L, dm)),
                            ("B", B, (bsz, L, N)), ("C", C, (bsz, L, N))):
-        _check_gpu(name, t, x.dtype, shape)
-    _check_gpu("A", A, torch.float32, (dm, N))
-    _check_gpu("D", D, torch.float32, (dm,))
-    _check_gpu("h0", h0, torch.float32, (bsz, dm, N))
+        _check_gpu(name, t, x.dtype, shape, cur)
+    _check_gpu("A", A, torch.float32, (dm, N), cur)
+    _check_gpu("D", D, torch.float32, (dm,), cur)
+    _check_gpu("h0", h0, torch.float32, (bsz, dm, N), cur)
     if out is None:
         out = torch.empty_like(x)
-    _check_gpu("out", out, x.dtype, (bsz, L, dm))
+    _check_gpu("out", out, x.dtype, (bsz, L, dm), cur)
     if return_final_state and final_state is None:
         final_state = torch.empty((bsz, dm, N), dtype=torch.float32, device=x.device)
-    _check_gpu("final_state", final_state, torch.float32, (bsz, dm, N))
+    _check_gpu("final_state", final_state, torch.float32, (bsz, dm, N), cur)
     d = scan_desc(bsz, L, dm, N, io, split_seq, 16)
     ck_bytes = lib.mssm_selective_scan_checkpoint_size(ctypes.byref(d))
     if checkpoints is None:
@@ -277,20 +293,21 @@ def selective_scan_conv_fwd(xin, conv_w, conv_b, conv_init, delta, A, B, C, D=No
         raise ValueError("conv_w must be [dim, width]")
     N, W = A.shape[1], conv_w.shape[1]
     io = _io_code(xin.dtype)
+    cur = _torch().cuda.current_device()
     for name, t, shape in (("xin", xin, (bsz, L, dm)), ("delta", delta, (bsz, L, dm)), ("z", z, (bsz, L, dm)),
                            ("B", B, (bsz, L, N)), ("C", C, (bsz, L, N)), ("conv_init", conv_init, (bsz, W - 1, dm))):
-        _check_gpu(name, t, xin.dtype, shape)
-    _check_gpu("conv_w", conv_w, torch.float32, (dm, W))
-    _check_gpu("conv_b", conv_b, torch.float32, (dm,))
-    _check_gpu("A", A, torch.float32, (dm, N))
-    _check_gpu("D", D, torch.float32, (dm,))
-    _check_gpu("h0", h0, torch.float32, (bsz, dm, N))
+        _check_gpu(name, t, xin.dtype, shape, cur)
+    _check_gpu("conv_w", conv_w, torch.float32, (dm, W), cur)
+    _check_gpu("conv_b", conv_b, torch.float32, (dm,), cur)
+    _check_gpu("A", A, torch.float32, (dm, N), cur)
+    _check_gpu("D", D, torch.float32, (dm,), cur)
+    _check_gpu("h0", h0, torch.float32, (bsz, dm, N), cur)
     if out is None:
         out = torch.empty_like(xin)
-    _check_gpu("out", out, xin.dtype, (bsz, L, dm))
+    _check_gpu("out", out, xin.dtype, (bsz, L, dm), cur)
     if return_final_state and final_state is None:
         final_state = torch.empty((bsz, dm, N), dtype=torch.float32, device=xin.device)
-    _check_gpu("final_state", final_state, torch.float32, (bsz, dm, N))
+    _check_gpu("final_state", final_state, torch.float32, (bsz, dm, N), cur)
     d = scan_desc(bsz, L, dm, N, io, split_seq, 16)
     ws_bytes = lib.mssm_selective_scan_conv_workspace_size(ctypes.byref(d))
     if ws_bytes and workspace is None:
@@ -334,13 +351,14 @@ def selective_scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, dout=None, df
     io = _io_code(x.dtype)
     if dout is None:
         raise ValueError("dout is required")
+    cur = _torch().cuda.current_device()
     for name, t, shape in (("x", x, (bsz, L, dm)), ("delta", delta, (bsz, L, dm)), ("z", z, (bsz, L, dm)),
                            ("B", B, (bsz, L, N)), ("C", C, (bsz, L, N)), ("dout", dout, (bsz, L, dm))):
-        _check_gpu(name, t, x.dtype, shape)
-    _check_gpu("A", A, torch.float32, (dm, N))
-    _check_gpu("D", D, torch.float32, (dm,))
-    _check_gpu("h0", h0, torch.float32, (bsz, dm, N))
-    _check_gpu("dfinal", dfinal, torch.float32, (bsz, dm, N))
+        _check_gpu(name, t, x.dtype, shape, cur)
+    _check_gpu("A", A, torch.float32, (dm, N), cur)
+    _check_gpu("D", D, torch.float32, (dm,), cur)
+    _check_gpu("h0", h0, torch.float32, (bsz, dm, N), cur)
+    _check_gpu("dfinal", dfinal, torch.float32, (bsz, dm, N), cur)
     if checkpoints is not None:
         d0 = scan_desc(bsz, L, dm, N, io)
         need = lib.mssm_selective_scan_checkpoint_size(ctypes.byref(d0))
@@ -361,7 +379,7 @@ def selective_scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, dout=None, df
                                 ("dz", x.dtype, (bsz, L, dm)), ("dB", torch.float32, (bsz, L, N)),
                                 ("dC", torch.float32, (bsz, L, N)), ("dA", torch.float32, (dm, N)),
                                 ("dD", torch.float32, (dm,)), ("dh0", torch.float32, (bsz, dm, N))):
-            _check_gpu(name, g.get(name), dt, shape)
+            _check_gpu(name, g.get(name), dt, shape, cur)
     d = scan_desc(bsz, L, dm, N, io)
     ws_bytes = lib.mssm_selective_scan_bwd_workspace_size(ctypes.byref(d))
     if ws_bytes and workspace is None:
@@ -419,18 +437,19 @@ def _ssd_call(fn, x, delta, lam, A, B, C, D, z, h0, chunk, return_final_state, o
     trap = fn == "mssm_ssd_trapezoidal_fwd"
     if trap and lam is None:
         raise ValueError("lam is required")
+    cur = _torch().cuda.current_device()
     for name, t, shape in (("x", x, (bsz, L, H, P)), ("z", z, (bsz, L, H, P)), ("delta", delta, (bsz, L, H)),
                            ("lam", lam, (bsz, L, H)), ("B", B, (bsz, L, G, N)), ("C", C, (bsz, L, G, N))):
-        _check_gpu(name, t, x.dtype, shape)
-    _check_gpu("A", A, torch.float32, (H,))
-    _check_gpu("D", D, torch.float32, (H,))
-    _check_gpu("h0", h0, torch.float32, (bsz, H, P, N))
+        _check_gpu(name, t, x.dtype, shape, cur)
+    _check_gpu("A", A, torch.float32, (H,), cur)
+    _check_gpu("D", D, torch.float32, (H,), cur)
+    _check_gpu("h0", h0, torch.float32, (bsz, H, P, N), cur)
     if out is None:
         out = torch.empty_like(x)
-    _check_gpu("out", out, x.dtype, (bsz, L, H, P))
+    _check_gpu("out", out, x.dtype, (bsz, L, H, P), cur)
     if return_final_state and final_state is None:
         final_state = torch.empty((bsz, H, P, N), dtype=torch.float32, device=x.device)
-    _check_gpu("final_state", final_state, torch.float32, (bsz, H, P, N))
+    _check_gpu("final_state", final_state, torch.float32, (bsz, H, P, N), cur)
     d = ssd_desc(bsz, L, H, P, N, G, chunk, io)
     ws_bytes = lib.mssm_ssd_workspace_size(ctypes.byref(d))
     if ws_bytes and workspace is None:
@@ -463,15 +482,16 @@ def selective_state_update(state, x, delta, A, B, C, D=None, z=None, out=None, s
         raise ValueError("A must be [dim, dstate]")
     N = A.shape[1]
     io = _io_code(x.dtype)
+    cur = _torch().cuda.current_device()
     for name, t, shape in (("x", x, (bsz, L, dm)), ("delta", delta, (bsz, L, dm)), ("z", z, (bsz, L, dm)),
                            ("B", B, (bsz, L, N)), ("C", C, (bsz, L, N))):
-        _check_gpu(name, t, x.dtype, shape)
-    _check_gpu("A", A, torch.float32, (dm, N))
-    _check_gpu("D", D, torch.float32, (dm,))
-    _check_gpu("state", state, torch.float32, (bsz, dm, N))
+        _check_gpu(name, t, x.dtype, shape, cur)
+    _check_gpu("A", A, torch.float32, (dm, N), cur)
+    _check_gpu("D", D, torch.float32, (dm,), cur)
+    _check_gpu("state", state, torch.float32, (bsz, dm, N), cur)
     if out is None:
         out = torch.empty_like(x)
-    _check_gpu("out", out, x.dtype, (bsz, L, dm))
+    _check_gpu("out", out, x.dtype, (bsz, L, dm), cur)
     d = scan_desc(bsz, L, dm, N, io)
     st = lib.mssm_selective_state_update(ctypes.byref(d), _ptr(state), _ptr(x), _ptr(delta), _ptr(A), _ptr(B),
                                          _ptr(C), _ptr(D), _ptr(z), _ptr(out), _stream_handle(stream))
@@ -494,18 +514,19 @@ def selective_state_update_conv(state, conv_state, xin, conv_w, conv_b, delta, A
     N = A.shape[1]
     W = conv_w.shape[1]
     io = _io_code(xin.dtype)
+    cur = _torch().cuda.current_device()
     for name, t, shape in (("xin", xin, (bsz, T, dm)), ("delta", delta, (bsz, T, dm)), ("z", z, (bsz, T, dm)),
                            ("B", B, (bsz, T, N)), ("C", C, (bsz, T, N)),
                            ("conv_state", conv_state, (bsz, W - 1, dm))):
-        _check_gpu(name, t, xin.dtype, shape)
-    _check_gpu("state", state, torch.float32, (bsz, dm, N))
-    _check_gpu("conv_w", conv_w, torch.float32, (dm, W))
-    _check_gpu("conv_b", conv_b, torch.float32, (dm,))
-    _check_gpu("A", A, torch.float32, (dm, N))
-    _check_gpu("D", D, torch.float32, (dm,))
+        _check_gpu(name, t, xin.dtype, shape, cur)
+    _check_gpu("state", state, torch.float32, (bsz, dm, N), cur)
+    _check_gpu("conv_w", conv_w, torch.float32, (dm, W), cur)
+    _check_gpu("conv_b", conv_b, torch.float32, (dm,), cur)
+    _check_gpu("A", A, torch.float32, (dm, N), cur)
+    _check_gpu("D", D, torch.float32, (dm,), cur)
     if out is None:
         out = torch.empty_like(xin)
-    _check_gpu("out", out, xin.dtype, (bsz, T, dm))
+    _check_gpu("out", out, xin.dtype, (bsz, T, dm), cur)
     d = scan_desc(bsz, T, dm, N, io)
     st = lib.mssm_selective_state_update_conv(ctypes.byref(d), W, _ptr(state), _ptr(conv_state), _ptr(xin),
                                               _ptr(conv_w), _ptr(conv_b), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
@@ -564,17 +585,18 @@ def _ssd_update_call(fn, state, x_prev, B_prev, x, delta, lam, A, B, C, D, z, ou
         raise ValueError("lam is required")
     if fn == "mssm_mamba3_siso_update" and omega is None:
         raise ValueError("omega is required")
+    cur = _torch().cuda.current_device()
     for name, t, shape in (("x", x, (bsz, L, H, P)), ("z", z, (bsz, L, H, P)), ("delta", delta, (bsz, L, H)),
                            ("lam", lam, (bsz, L, H)), ("B", B, (bsz, L, G, N)), ("C", C, (bsz, L, G, N)),
                            ("x_prev", x_prev, (bsz, H, P)), ("B_prev", B_prev, (bsz, G, N))):
-        _check_gpu(name, t, x.dtype, shape)
-    _check_gpu("A", A, torch.float32, (H,))
-    _check_gpu("D", D, torch.float32, (H,))
-    _check_gpu("state", state, torch.float32, (bsz, H, P, N))
-    _check_gpu("omega", omega, torch.float32, (H, N // 2))
+        _check_gpu(name, t, x.dtype, shape, cur)
+    _check_gpu("A", A, torch.float32, (H,), cur)
+    _check_gpu("D", D, torch.float32, (H,), cur)
+    _check_gpu("state", state, torch.float32, (bsz, H, P, N), cur)
+    _check_gpu("omega", omega, torch.float32, (H, N // 2), cur)
     if out is None:
         out = torch.empty_like(x)
-    _check_gpu("out", out, x.dtype, (bsz, L, H, P))
+    _check_gpu("out", out, x.dtype, (bsz, L, H, P), cur)
     d = ssd_desc(bsz, L, H, P, N, G, 0, io)
     if fn == "mssm_mamba3_siso_update":
         st = lib.mssm_mamba3_siso_update(ctypes.byref(d), _ptr(state), _ptr(x_prev), _ptr(B_prev), _ptr(x),

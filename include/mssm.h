@@ -46,6 +46,10 @@
  *    The library never allocates, frees or keeps a pointer after returning,
  *    and never synchronises: work is enqueued on `stream` (a hipStream_t
  *    passed as void*; NULL = the null stream) and the call returns at once.
+ *    A call enqueues kernel launches only (no memset, no copy), and every
+ *    workspace element is written by a kernel before one reads it, so a
+ *    call may be captured into a HIP graph on a capturing stream and
+ *    replayed; each replay reads the buffers as they are at that time.
  *  - Tensors are dense, row-major and contiguous (last index fastest).
  *    x, delta, B, C, z and out share io_dtype; A, D, h0 and final_state are
  *    always fp32.  fp32 results are rounded to bf16 to nearest-even.

@@ -114,10 +114,15 @@ typedef struct {
  * chunk: time-chunk length of the matrix form: 0 (library's choice), 64, 128
  * or 256; a chunk longer than 64 steps is evaluated as consecutive 64-step
  * blocks with the state carried between them (the same algebra, so only
- * rounding differs).  io_dtype must be MSSM_BF16 (the matrix cores take bf16
- * operands).  headdim must be a multiple of 64; dstate a multiple of 16 and
- * at most 128; nheads * headdim and ngroups * dstate below 2^24.  The state
- * never leaves the chip between blocks. */
+ * rounding differs).  The matrix-core block kernel takes io_dtype MSSM_BF16
+ * (the matrix cores take bf16 operands), headdim a multiple of 64, dstate a
+ * multiple of 16 up to 128, nheads * headdim and ngroups * dstate up to 2^24;
+ * there the state never leaves the chip between blocks, and x, z, out, B, C,
+ * h0 and final_state must be 16-byte aligned.  Any other problem with io_dtype
+ * MSSM_F32 or MSSM_BF16 and dstate up to 256 runs token by token through the
+ * recurrent update kernel (state from h0, written to final_state; the chunk
+ * is then unused), with element-aligned pointers.  The state update's
+ * entry points (below) take the same descriptor. */
 typedef struct {
     int64_t batch, seqlen, nheads, headdim, dstate, ngroups, chunk;
     int32_t io_dtype;

@@ -407,9 +407,11 @@ def ssd_fwd(x, delta, A, B, C, D=None, z=None, h0=None, chunk: int = 0, return_f
             out=None, final_state=None, workspace=None, stream=None):
     """Mamba-2 scalar-A multi-head forward (mssm_ssd_fwd).
 
-    x, z: [batch, seqlen, nheads, headdim] bfloat16; delta: [batch, seqlen, nheads] bfloat16;
-    B, C: [batch, seqlen, ngroups, dstate] bfloat16; A, D: [nheads] float32;
-    h0: [batch, nheads, headdim, dstate] float32.
+    x, z: [batch, seqlen, nheads, headdim]; delta: [batch, seqlen, nheads]; B, C: [batch, seqlen,
+    ngroups, dstate], all bfloat16 or all float32; A, D: [nheads] float32; h0: [batch, nheads, headdim,
+    dstate] float32.  bfloat16 with headdim a multiple of 64 and dstate a multiple of 16 up to 128 runs
+    on the matrix-core block kernel; anything else (float32, other headdims, dstate up to 256) on the
+    recurrent kernel, token by token.
     """
     return _ssd_call("mssm_ssd_fwd", x, delta, None, A, B, C, D, z, h0, chunk, return_final_state, out,
                      final_state, workspace, stream)
@@ -419,7 +421,7 @@ def ssd_trapezoidal_fwd(x, delta, lam, A, B, C, D=None, z=None, h0=None, chunk: 
                         return_final_state: bool = False, out=None, final_state=None, workspace=None, stream=None):
     """Mamba-3 SISO recurrence, exponential-trapezoidal input rule (mssm_ssd_trapezoidal_fwd).
 
-    As ``ssd_fwd`` plus lam: [batch, seqlen, nheads] bfloat16, the weight of each step's own input (1 - lam
+    As ``ssd_fwd`` plus lam: [batch, seqlen, nheads] in the I/O dtype, the weight of each step's own input (1 - lam
     goes to the previous step's input, carried through the step's decay).  lam = 1 gives ``ssd_fwd``.
     """
     return _ssd_call("mssm_ssd_trapezoidal_fwd", x, delta, lam, A, B, C, D, z, h0, chunk, return_final_state,

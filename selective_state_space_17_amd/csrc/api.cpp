@@ -215,24 +215,27 @@ int mssm_selective_scan_fwd(const mssm_scan_desc* desc, const void* x, const voi
 // --------------------------------------------------------------------------
 // Mamba-2 scalar-A multi-head form
 // --------------------------------------------------------------------------
-static int validate_ssd_desc(const mssm_ssd_desc* d, int64_t* Q) {
+// *matrix: the shape and dtype the matrix-core block kernel takes (bf16 I/O, headdim a multiple of 64,
+// dstate a multiple of 16 up to 128); any other valid problem runs through the recurrent update kernel
+static int validate_ssd_desc(const mssm_ssd_desc* d, int64_t* Q, bool* matrix) {
   if (d == nullptr) return MSSM_ERR_INVALID_ARG;
   if (d->batch < 0 || d->seqlen < 0 || d->nheads <= 0 || d->headdim <= 0 || d->dstate <= 0 || d->ngroups <= 0)
     return MSSM_ERR_INVALID_ARG;
   if (d->flags != 0) return MSSM_ERR_INVALID_ARG;
-  if (d->io_dtype != MSSM_BF16) return MSSM_ERR_UNSUPPORTED;
-  if (d->nheads % d->ngroups != 0) return MSSM_ERR_UNSUPPORTED;
-  if (d->headdim % 64 != 0 || d->dstate % 16 != 0 || d->dstate > 128) return MSSM_ERR_UNSUPPORTED;
-  // per-step row strides are formed with 24-bit multiplies inside a 64-step block
-  if (d->nheads > (1 << 24) / d->headdim || d->ngroups > (1 << 24) / d->dstate) return MSSM_ERR_UNSUPPORTED;
+  if (d->io_dtype != MSSM_BF16 && d->io_dtype != MSSM_F32) return MSSM_ERR_UNSUPPORTED;
+  if (d->nheads % d->ngroups != 0 || d->dstate > 256) return MSSM_ERR_UNSUPPORTED;
   const int64_t q = d->chunk == 0 ? 64 : d->chunk;
   if (q != 64 && q != 128 && q != 256) return MSSM_ERR_UNSUPPORTED;
+  // per-step row strides of the block kernel are formed with 24-bit multiplies inside a 64-step block
+  *matrix = d->io_dtype == MSSM_BF16 && mssm::ssd_supported(d->headdim, d->dstate) &&
+            d->nheads <= (1 << 24) / d->headdim && d->ngroups <= (1 << 24) / d->dstate;
+  const int64_t es = d->io_dtype == MSSM_BF16 ? 2 : 4;
   int64_t t = 0;
   if (!mul_ok(d->batch, d->seqlen, &t) || !mul_ok(t, d->nheads, &t) || !mul_ok(t, d->headdim, &t) ||
-      !mul_ok(t, 2, &t))
+      !mul_ok(t, es, &t))
     return MSSM_ERR_INVALID_ARG;
   if (!mul_ok(d->batch, d->seqlen, &t) || !mul_ok(t, d->ngroups, &t) || !mul_ok(t, d->dstate, &t) ||
-      !mul_ok(t, 2, &t))
+      !mul_ok(t, es, &t))
     return MSSM_ERR_INVALID_ARG;
   if (!mul_ok(d->batch, d->nheads, &t) || !mul_ok(t, d->headdim, &t) || !mul_ok(t, d->dstate, &t) ||
       !mul_ok(t, 4, &t))
@@ -652,7 +655,8 @@ int mssm_selective_scan_bwd(const mssm_scan_desc* desc, const void* x, const voi
 
 size_t mssm_ssd_workspace_size(const mssm_ssd_desc* desc) {
   int64_t Q = 0;
-  if (validate_ssd_desc(desc, &Q) != MSSM_OK) return 0;
+  bool matrix = false;
+  if (validate_ssd_desc(desc, &Q, &matrix) != MSSM_OK || !matrix) return 0;
   return mssm::ssd_workspace_bytes(desc->batch, desc->seqlen, desc->nheads, desc->headdim, desc->dstate,
                                    desc->ngroups, Q);
 }
@@ -660,15 +664,67 @@ size_t mssm_ssd_workspace_size(const mssm_ssd_desc* desc) {
 }  // extern "C"
 
 namespace {
+// A whole sequence through the recurrent update kernel, for the problems the block kernel does not take:
+// the state starts from h0 (or zero) and is written to final_state (if given); no previous token.
+int ssd_fwd_recurrent(const mssm_ssd_desc& d, const void* x, const void* delta, const void* lam, bool want_lam,
+                      const float* A, const void* B, const void* C, const float* D, const void* z, const float* h0,
+                      void* out, float* final_state, void* stream) {
+  const int64_t es = d.io_dtype == MSSM_BF16 ? 2 : 4;
+  const int64_t n_d = d.batch * d.seqlen * d.nheads;
+  const int64_t n_x = n_d * d.headdim;
+  const int64_t n_bc = d.batch * d.seqlen * d.ngroups * d.dstate;
+  // the descriptor check bounds batch * nheads * headdim * dstate * 4; the update kernel's lane count
+  // is up to 64 times that many bytes' worth of states
+  const int64_t n_st = d.batch * d.nheads * d.headdim * d.dstate;
+  int64_t t = 0;
+  if (!mul_ok(n_st, 4 * 64, &t)) return MSSM_ERR_INVALID_ARG;
+  const int64_t b_st = n_st * 4;
+  const bool has_steps = n_x > 0;
+  if (A == nullptr) return MSSM_ERR_INVALID_ARG;
+  if (has_steps && (x == nullptr || delta == nullptr || B == nullptr || C == nullptr || out == nullptr))
+    return MSSM_ERR_INVALID_ARG;
+  if (want_lam && has_steps && lam == nullptr) return MSSM_ERR_INVALID_ARG;
+  if (!aligned(x, es) || !aligned(delta, es) || !aligned(B, es) || !aligned(C, es) || !aligned(z, es) ||
+      !aligned(out, es) || !aligned(lam, es) || !aligned(A, 4) || !aligned(D, 4) || !aligned(h0, 4) ||
+      !aligned(final_state, 4))
+    return MSSM_ERR_MISALIGNED;
+  const int64_t b_io = n_x * es, b_d = d.batch * d.seqlen * d.nheads * es;
+  const void* ins[] = {x, delta, B, C, z, A, D, h0, lam};
+  const int64_t inb[] = {b_io, b_d, n_bc * es, n_bc * es, b_io, d.nheads * 4, d.nheads * 4, b_st, b_d};
+  for (int i = 0; i < 9; ++i) {
+    if (overlap(out, b_io, ins[i], inb[i])) return MSSM_ERR_INVALID_ARG;
+    if (overlap(final_state, b_st, ins[i], inb[i])) return MSSM_ERR_INVALID_ARG;
+  }
+  if (overlap(out, b_io, final_state, b_st)) return MSSM_ERR_INVALID_ARG;
+  if (mssm::update_grid_blocks(d.batch * d.nheads * d.headdim, d.dstate) > std::numeric_limits<int32_t>::max())
+    return MSSM_ERR_UNSUPPORTED;
+  mssm::UpdateArgs a{};
+  a.state = nullptr; a.state_in = h0; a.state_out = final_state;
+  a.x = x; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.out = out;
+  a.lam = want_lam ? lam : nullptr;
+  a.batch = d.batch; a.L = d.seqlen; a.N = d.dstate; a.H = d.nheads; a.P = d.headdim; a.G = d.ngroups;
+  a.io = d.io_dtype;
+  const hipError_t e = mssm::ssd_update_launch(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    set_err(e);
+    return MSSM_ERR_HIP;
+  }
+  return MSSM_OK;
+}
+
 // both SSD forms: lam == nullptr is the Mamba-2 rule, else lam is required
 int ssd_fwd_impl(const mssm_ssd_desc* desc, const void* x, const void* delta, const void* lam, bool want_lam,
                  const float* A, const void* B, const void* C, const float* D, const void* z, const float* h0,
                  void* out, float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
   int64_t Q = 0;
-  const int v = validate_ssd_desc(desc, &Q);
+  bool matrix = false;
+  const int v = validate_ssd_desc(desc, &Q, &matrix);
   if (v != MSSM_OK) return v;
   const mssm_ssd_desc& d = *desc;
   if (d.batch == 0) return MSSM_OK;
+  if (!matrix)
+    return ssd_fwd_recurrent(d, x, delta, want_lam ? lam : nullptr, want_lam, A, B, C, D, z, h0, out, final_state,
+                             stream);
   const int64_t n_x = d.batch * d.seqlen * d.nheads * d.headdim;
   const int64_t n_d = d.batch * d.seqlen * d.nheads;
   const int64_t n_bc = d.batch * d.seqlen * d.ngroups * d.dstate;

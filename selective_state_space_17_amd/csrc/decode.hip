@@ -154,6 +154,11 @@ struct UpdParams {
   const void* x_prev;      // [batch, H, P], nullable
   const void* B_prev;      // [batch, G, N], nullable
   const float* omega;      // [H, N/2] (ROT)
+  // multi-head form: the state read before the first token (nullable: zero) and
+  // written after the last (nullable: not written); both are `state` for an
+  // update in place, h0 and final_state for a whole sequence
+  const float* state_in;
+  float* state_out;
 };
 
 // Each thread owns S states (4, or 8 when dstate allows: two 16-byte loads
@@ -292,7 +297,12 @@ __global__ __launch_bounds__(kThreads) void ssd_update_kernel(UpdParams p) {
     hd[k] = bh % H;
     bb[k] = bh / H;
     gg[k] = hd[k] / (H / G);
-    loadS<S, VEC>(p.state + rr[k] * N, n0, N, h[k]);
+    if (p.state_in != nullptr) {
+      loadS<S, VEC>(p.state_in + rr[k] * N, n0, N, h[k]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < S; ++q) h[k][q] = 0.f;
+    }
     a2[k] = p.A[hd[k]] * kLog2e;
     Dh[k] = p.D != nullptr ? p.D[hd[k]] : 0.f;
     if constexpr (ROT) {
@@ -372,7 +382,7 @@ __global__ __launch_bounds__(kThreads) void ssd_update_kernel(UpdParams p) {
   }
 #pragma unroll
   for (int k = 0; k < R; ++k)
-    if (live[k]) storeS<S, VEC>(p.state + rr[k] * N, n0, N, h[k]);
+    if (live[k] && p.state_out != nullptr) storeS<S, VEC>(p.state_out + rr[k] * N, n0, N, h[k]);
 }
 
 int lanes_per_row(int64_t N, int S) {
@@ -393,8 +403,8 @@ UpdParams common(const UpdateArgs& a) {
 bool vec_ok(const UpdateArgs& a, bool mamba1, int S) {
   auto al = [](const void* q, uintptr_t m) { return (reinterpret_cast<uintptr_t>(q) & (m - 1)) == 0; };
   const uintptr_t bc = a.io == 1 ? 8 : 16;
-  return a.N % S == 0 && al(a.state, 16) && (!mamba1 || al(a.A, 16)) && al(a.B, bc) && al(a.C, bc) &&
-         (a.B_prev == nullptr || al(a.B_prev, bc));
+  return a.N % S == 0 && al(a.state, 16) && al(a.state_in, 16) && al(a.state_out, 16) &&
+         (!mamba1 || al(a.A, 16)) && al(a.B, bc) && al(a.C, bc) && (a.B_prev == nullptr || al(a.B_prev, bc));
 }
 
 int64_t grid_blocks(int64_t rows, int64_t N, int S) {
@@ -444,6 +454,8 @@ hipError_t ssd_update_launch(const UpdateArgs& a, hipStream_t stream) {
   UpdParams p = common(a);
   p.H = a.H; p.P = a.P; p.G = a.G;
   p.rows = a.batch * a.H * a.P;
+  p.state_in = a.state != nullptr ? a.state : a.state_in;
+  p.state_out = a.state != nullptr ? a.state : a.state_out;
   if (a.lam != nullptr) {
     p.lam = a.lam; p.x_prev = a.x_prev; p.B_prev = a.B_prev;
     if (a.omega != nullptr) {   // dstate is even: lanes own whole pairs (groups of 4 or 8 from a multiple of 4)

@@ -74,6 +74,8 @@ struct SSDArgs {
 };
 
 size_t ssd_workspace_bytes(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q);
+// headdim and dstate the matrix-core block kernel takes (bf16 I/O)
+bool ssd_supported(int64_t P, int64_t N);
 hipError_t ssd_launch(const SSDArgs& a, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
@@ -103,6 +105,10 @@ struct UpdateArgs {
   const void* x_prev = nullptr;    // [batch, H, P], the token before the first one; nullable = none
   const void* B_prev = nullptr;    // [batch, G, N], likewise
   const float* omega = nullptr;    // [H, N/2] rotation rates of the state pairs (complex state); nullable
+  // multi-head form with state == nullptr: the state before the first token (nullable: zero) and the
+  // one written after the last (nullable: not written), for a whole sequence run through this kernel
+  const float* state_in = nullptr;
+  float* state_out = nullptr;
 };
 
 hipError_t scan_update_launch(const UpdateArgs& a, hipStream_t stream);

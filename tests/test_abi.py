@@ -151,15 +151,11 @@ def _ssd_call(desc, x=BASE, delta=BASE + 100 * MB, A=BASE + 200 * MB, B=BASE + 3
 
 
 @pytest.mark.parametrize("kw,expect", [
-    (dict(io_dtype=M.MSSM_F32), M.MSSM_ERR_UNSUPPORTED),
+    (dict(io_dtype=7), M.MSSM_ERR_UNSUPPORTED),
     (dict(nheads=6, ngroups=4), M.MSSM_ERR_UNSUPPORTED),
-    (dict(headdim=24), M.MSSM_ERR_UNSUPPORTED),
-    (dict(dstate=20), M.MSSM_ERR_UNSUPPORTED),
     (dict(chunk=48), M.MSSM_ERR_UNSUPPORTED),
     (dict(chunk=32), M.MSSM_ERR_UNSUPPORTED),
-    (dict(dstate=256), M.MSSM_ERR_UNSUPPORTED),
-    (dict(headdim=96), M.MSSM_ERR_UNSUPPORTED),
-    (dict(nheads=(1 << 18) + 1, ngroups=1, headdim=64), M.MSSM_ERR_UNSUPPORTED),
+    (dict(dstate=257), M.MSSM_ERR_UNSUPPORTED),
     (dict(headdim=0), M.MSSM_ERR_INVALID_ARG),
     (dict(batch=-2), M.MSSM_ERR_INVALID_ARG),
 ])
@@ -167,6 +163,21 @@ def test_ssd_validation(kw, expect):
     a = dict(batch=2, seqlen=128, nheads=4, headdim=64, dstate=64, ngroups=1, chunk=64, io_dtype=M.MSSM_BF16)
     a.update(kw)
     assert _ssd_call(M.ssd_desc(**a)) == expect
+
+
+# Shapes and dtypes the matrix-core block kernel does not take: accepted, and run through the recurrent
+# update kernel. A null x proves the descriptor passed (the pointer checks reject it) without launching.
+RECURRENT_SSD = [dict(io_dtype=M.MSSM_F32), dict(headdim=24), dict(headdim=96), dict(dstate=20), dict(dstate=256),
+                 dict(dstate=6), dict(nheads=(1 << 18) + 1, ngroups=1, headdim=64)]
+
+
+@pytest.mark.parametrize("kw", RECURRENT_SSD)
+def test_ssd_recurrent_shapes_accepted(kw):
+    a = dict(batch=2, seqlen=128, nheads=4, headdim=64, dstate=64, ngroups=1, chunk=64, io_dtype=M.MSSM_BF16)
+    a.update(kw)
+    d = M.ssd_desc(**a)
+    assert _ssd_call(d, x=None) == M.MSSM_ERR_INVALID_ARG
+    assert M.lib.mssm_ssd_workspace_size(ctypes.byref(d)) == 0
 
 
 def test_ssd_pointer_checks():
@@ -183,9 +194,8 @@ def _ssd3_call(desc, x=BASE, delta=BASE + 100 * MB, lam=BASE + 150 * MB, A=BASE 
 
 
 @pytest.mark.parametrize("kw,expect", [
-    (dict(io_dtype=M.MSSM_F32), M.MSSM_ERR_UNSUPPORTED),
-    (dict(headdim=24), M.MSSM_ERR_UNSUPPORTED),
-    (dict(dstate=256), M.MSSM_ERR_UNSUPPORTED),
+    (dict(io_dtype=7), M.MSSM_ERR_UNSUPPORTED),
+    (dict(dstate=300), M.MSSM_ERR_UNSUPPORTED),
     (dict(batch=-2), M.MSSM_ERR_INVALID_ARG),
 ])
 def test_ssd_trapezoidal_validation(kw, expect):
@@ -193,6 +203,15 @@ def test_ssd_trapezoidal_validation(kw, expect):
     a = dict(batch=2, seqlen=128, nheads=4, headdim=64, dstate=64, ngroups=1, chunk=64, io_dtype=M.MSSM_BF16)
     a.update(kw)
     assert _ssd3_call(M.ssd_desc(**a)) == expect
+
+
+@pytest.mark.parametrize("kw", RECURRENT_SSD)
+def test_ssd_trapezoidal_recurrent_shapes_accepted(kw):
+    a = dict(batch=2, seqlen=128, nheads=4, headdim=64, dstate=64, ngroups=1, chunk=64, io_dtype=M.MSSM_BF16)
+    a.update(kw)
+    d = M.ssd_desc(**a)
+    assert _ssd3_call(d, x=None) == M.MSSM_ERR_INVALID_ARG
+    assert _ssd3_call(d, lam=None) == M.MSSM_ERR_INVALID_ARG
 
 
 def test_ssd_trapezoidal_pointer_checks():

@@ -294,10 +294,12 @@ int mssm_mamba3_siso_update(const mssm_ssd_desc* desc, float* state,
  *   conv_b           : [dim] fp32, nullable
  *   conv_init        : [batch, conv_width - 1, dim] (io_dtype), nullable: the
  *                      inputs before t = 0, oldest first (xin's layout)
- * Supported: dstate 16, dim * sizeof(io) a multiple of 16, every io pointer
- * (xin, delta, B, C, z, out, conv_init) 16-byte aligned; split_state 0 or
- * 16 (else MSSM_ERR_UNSUPPORTED / MSSM_ERR_MISALIGNED).  workspace: at least
- * mssm_selective_scan_conv_workspace_size(desc) bytes.  Same ownership,
+ * The fused block kernel takes dstate 16, dim * sizeof(io) a multiple of 16,
+ * every io pointer (xin, delta, B, C, z, out, conv_init) 16-byte aligned and
+ * split_state 0 or 16.  Any other problem (dstate up to 256, element-aligned
+ * pointers) runs token by token through the recurrent update kernel, which
+ * reads conv_init and leaves it unchanged.  workspace: at least
+ * mssm_selective_scan_conv_workspace_size(desc) bytes (0 off the fused path).  Same ownership,
  * stream and error rules as mssm_selective_scan_fwd. */
 int mssm_selective_scan_conv_fwd(const mssm_scan_desc* desc, int32_t conv_width,
                                  const void* xin, const float* conv_w, const float* conv_b,

@@ -280,8 +280,10 @@ def selective_scan_conv_fwd(xin, conv_w, conv_b, conv_init, delta, A, B, C, D=No
     """Selective scan with the short causal convolution + SiLU fused in front
     (mssm_selective_scan_conv_fwd): x = silu(conv_b + causal_conv(xin, conv_w)).
 
-    xin, delta, z: [batch, seqlen, dim]; B, C: [batch, seqlen, 16]; conv_w [dim, W] float32 (W 1..4);
-    conv_b [dim] float32 or None; conv_init [batch, W-1, dim] in xin's dtype or None.
+    xin, delta, z: [batch, seqlen, dim]; B, C: [batch, seqlen, dstate]; conv_w [dim, W] float32 (W 1..4);
+    conv_b [dim] float32 or None; conv_init [batch, W-1, dim] in xin's dtype or None (read only).
+    dstate 16 with rows of a multiple of 16 bytes runs on the fused block kernel; any other problem
+    (dstate up to 256) on the recurrent kernel, token by token.
     """
     torch = _torch()
     if xin.dim() != 3:

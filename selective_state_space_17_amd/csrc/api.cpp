@@ -519,6 +519,50 @@ size_t mssm_selective_scan_conv_workspace_size(const mssm_scan_desc* desc) {
   return mssm::scan_workspace_bytes(c.batch, c.dim, c.dstate, K);
 }
 
+// The convolution and scan over a whole sequence through the recurrent update kernel, for the problems the
+// fused block kernel does not take: the window starts from conv_init (or zero inputs) and is not written
+// back, the state starts from h0 (or zero) and goes to final_state (if given).
+static int conv_fwd_recurrent(const mssm_scan_desc& d, int32_t conv_width, const void* xin, const float* conv_w,
+                              const float* conv_b, const void* conv_init, const void* delta, const float* A,
+                              const void* B, const void* C, const float* D, const void* z, const float* h0,
+                              void* out, float* final_state, void* stream) {
+  const int64_t es = d.io_dtype == MSSM_BF16 ? 2 : 4;
+  const int64_t n_bld = d.batch * d.seqlen * d.dim;
+  const int64_t n_bln = d.batch * d.seqlen * d.dstate;
+  if (n_bld > 0 && (xin == nullptr || delta == nullptr || B == nullptr || C == nullptr || out == nullptr))
+    return MSSM_ERR_INVALID_ARG;
+  if (!aligned(xin, es) || !aligned(delta, es) || !aligned(B, es) || !aligned(C, es) || !aligned(z, es) ||
+      !aligned(out, es) || !aligned(conv_init, es) || !aligned(A, 4) || !aligned(D, 4) || !aligned(h0, 4) ||
+      !aligned(final_state, 4) || !aligned(conv_w, 4) || !aligned(conv_b, 4))
+    return MSSM_ERR_MISALIGNED;
+  const int64_t b_io = n_bld * es, b_bc = n_bln * es;
+  const int64_t b_st = d.batch * d.dim * d.dstate * 4;
+  const int64_t b_init = d.batch * (conv_width - 1) * d.dim * es;
+  const void* ins[] = {xin, delta, B, C, z, A, D, h0, conv_w, conv_b, conv_init};
+  const int64_t inb[] = {b_io, b_io, b_bc, b_bc, b_io, d.dim * d.dstate * 4, d.dim * 4, b_st,
+                         d.dim * conv_width * 4, d.dim * 4, b_init};
+  for (int i = 0; i < 11; ++i) {
+    if (overlap(out, b_io, ins[i], inb[i])) return MSSM_ERR_INVALID_ARG;
+    if (overlap(final_state, b_st, ins[i], inb[i])) return MSSM_ERR_INVALID_ARG;
+  }
+  if (overlap(out, b_io, final_state, b_st)) return MSSM_ERR_INVALID_ARG;
+  if (n_bld == 0 && final_state == nullptr) return MSSM_OK;
+  if (mssm::update_grid_blocks(d.batch * d.dim, d.dstate) > std::numeric_limits<int32_t>::max())
+    return MSSM_ERR_UNSUPPORTED;
+  mssm::UpdateArgs a{};
+  a.state = nullptr; a.state_in = h0; a.state_out = final_state;
+  a.x = xin; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.out = out;
+  a.conv_w = conv_w; a.conv_b = conv_b; a.conv_width = conv_width;
+  a.conv_state = nullptr; a.conv_in = conv_init; a.conv_out = nullptr;
+  a.batch = d.batch; a.L = d.seqlen; a.N = d.dstate; a.dim = d.dim; a.io = d.io_dtype;
+  const hipError_t e = mssm::scan_update_launch(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    set_err(e);
+    return MSSM_ERR_HIP;
+  }
+  return MSSM_OK;
+}
+
 int mssm_selective_scan_conv_fwd(const mssm_scan_desc* desc, int32_t conv_width, const void* xin,
                                  const float* conv_w, const float* conv_b, const void* conv_init,
                                  const void* delta, const float* A, const void* B, const void* C, const float* D,
@@ -528,11 +572,16 @@ int mssm_selective_scan_conv_fwd(const mssm_scan_desc* desc, int32_t conv_width,
   if (v != MSSM_OK) return v;
   const mssm_scan_desc& d = *desc;
   if (conv_width < 1 || conv_width > 4) return MSSM_ERR_UNSUPPORTED;
-  if (d.dstate != 16 || (d.split_state != 0 && d.split_state != 16)) return MSSM_ERR_UNSUPPORTED;
   const int64_t es = d.io_dtype == MSSM_BF16 ? 2 : 4;
-  if ((d.dim * es) % 16 != 0) return MSSM_ERR_UNSUPPORTED;
   if (A == nullptr || conv_w == nullptr) return MSSM_ERR_INVALID_ARG;
   if (d.batch == 0) return MSSM_OK;
+  // the fused block kernel: one state per lane (dstate 16) and 16-byte pieces of every io tensor
+  const bool fused = d.dstate == 16 && (d.split_state == 0 || d.split_state == 16) && (d.dim * es) % 16 == 0 &&
+                     aligned(xin, 16) && aligned(delta, 16) && aligned(B, 16) && aligned(C, 16) && aligned(z, 16) &&
+                     aligned(out, 16) && aligned(conv_init, 16);
+  if (!fused)
+    return conv_fwd_recurrent(d, conv_width, xin, conv_w, conv_b, conv_init, delta, A, B, C, D, z, h0, out,
+                              final_state, stream);
   const int64_t n_bld = d.batch * d.seqlen * d.dim;
   const int64_t n_bln = d.batch * d.seqlen * d.dstate;
   if (n_bld > 0 && (xin == nullptr || delta == nullptr || B == nullptr || C == nullptr || out == nullptr))

@@ -147,16 +147,19 @@ struct UpdParams {
   // Mamba-1 with the short causal convolution in front (x is then its input)
   const float* conv_w;     // [dim, conv_width]
   const float* conv_b;     // [dim], nullable
-  void* conv_state;        // [batch, conv_width - 1, dim] (io dtype), read and advanced in place
+  const void* conv_in;     // [batch, conv_width - 1, dim] (io dtype): the window before the first
+                           // token (nullable: zero inputs)
+  void* conv_out;          // the window after the last token (nullable: not written); both are
+                           // conv_state for a decode step, conv_init and nothing for a sequence
   int conv_width;
   // multi-head form with the Mamba-3 exponential-trapezoidal rule (TRAP)
   const void* lam;         // [batch, L, H]
   const void* x_prev;      // [batch, H, P], nullable
   const void* B_prev;      // [batch, G, N], nullable
   const float* omega;      // [H, N/2] (ROT)
-  // multi-head form: the state read before the first token (nullable: zero) and
-  // written after the last (nullable: not written); both are `state` for an
-  // update in place, h0 and final_state for a whole sequence
+  // the state read before the first token (nullable: zero) and written after
+  // the last (nullable: not written); both are `state` for an update in place,
+  // h0 and final_state for a whole sequence
   const float* state_in;
   float* state_out;
 };
@@ -193,16 +196,21 @@ __global__ __launch_bounds__(kThreads) void scan_update_kernel(UpdParams p) {
     rr[k] = live[k] ? row : 0;
     bb[k] = rr[k] / dim;
     cc[k] = rr[k] % dim;
-    loadS<S, VEC>(p.state + rr[k] * N, n0, N, h[k]);
+    if (p.state_in != nullptr) {
+      loadS<S, VEC>(p.state_in + rr[k] * N, n0, N, h[k]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < S; ++q) h[k][q] = 0.f;
+    }
     loadS<S, VEC>(p.A + cc[k] * N, n0, N, a2[k]);
     Dc[k] = p.D != nullptr ? p.D[cc[k]] : 0.f;
   }
   // convolution (CONV): taps right-aligned into 4 slots (slot 3 = this token),
-  // win[j] = the input 3 - j tokens back, taken from and returned to conv_state
+  // win[j] = the input 3 - j tokens back, taken from conv_in and returned to conv_out
   float cw[R][4], cbias[R], win[R][3];
   if constexpr (CONV) {
     const int W = p.conv_width;
-    T* cs = static_cast<T*>(p.conv_state);
+    const T* cs = static_cast<const T*>(p.conv_in);
 #pragma unroll
     for (int k = 0; k < R; ++k) {
 #pragma unroll
@@ -210,7 +218,7 @@ __global__ __launch_bounds__(kThreads) void scan_update_kernel(UpdParams p) {
       cbias[k] = p.conv_b != nullptr ? p.conv_b[cc[k]] : 0.f;
 #pragma unroll
       for (int m = 1; m <= 3; ++m)
-        win[k][3 - m] = m <= W - 1 ? to_f32(cs[(bb[k] * (W - 1) + (W - 1 - m)) * dim + cc[k]]) : 0.f;
+        win[k][3 - m] = (m <= W - 1 && cs != nullptr) ? to_f32(cs[(bb[k] * (W - 1) + (W - 1 - m)) * dim + cc[k]]) : 0.f;
     }
   }
   for (int64_t t = 0; t < L; ++t) {
@@ -254,13 +262,13 @@ __global__ __launch_bounds__(kThreads) void scan_update_kernel(UpdParams p) {
   }
 #pragma unroll
   for (int k = 0; k < R; ++k)
-    if (live[k]) storeS<S, VEC>(p.state + rr[k] * N, n0, N, h[k]);
+    if (live[k] && p.state_out != nullptr) storeS<S, VEC>(p.state_out + rr[k] * N, n0, N, h[k]);
   if constexpr (CONV) {   // the window after the last token (inputs, stored exactly as read)
     const int W = p.conv_width;
-    T* cs = static_cast<T*>(p.conv_state);
+    T* cs = static_cast<T*>(p.conv_out);
 #pragma unroll
     for (int k = 0; k < R; ++k)
-      if (live[k] && n0 == 0)
+      if (live[k] && n0 == 0 && cs != nullptr)
         for (int m = 1; m <= W - 1; ++m) cs[(bb[k] * (W - 1) + (W - 1 - m)) * dim + cc[k]] = from_f32<T>(win[k][3 - m]);
   }
 }
@@ -393,7 +401,9 @@ int lanes_per_row(int64_t N, int S) {
 
 UpdParams common(const UpdateArgs& a) {
   UpdParams p{};
-  p.state = a.state; p.x = a.x; p.delta = a.delta; p.A = a.A; p.B = a.B; p.C = a.C; p.D = a.D; p.z = a.z;
+  p.state = a.state; p.state_in = a.state != nullptr ? a.state : a.state_in;
+  p.state_out = a.state != nullptr ? a.state : a.state_out;
+  p.x = a.x; p.delta = a.delta; p.A = a.A; p.B = a.B; p.C = a.C; p.D = a.D; p.z = a.z;
   p.out = a.out;
   p.batch = a.batch; p.L = a.L; p.N = a.N;
   return p;
@@ -442,7 +452,9 @@ hipError_t scan_update_launch(const UpdateArgs& a, hipStream_t stream) {
   p.dim = a.dim;
   p.rows = a.batch * a.dim;
   if (a.conv_w != nullptr) {
-    p.conv_w = a.conv_w; p.conv_b = a.conv_b; p.conv_state = a.conv_state; p.conv_width = a.conv_width;
+    p.conv_w = a.conv_w; p.conv_b = a.conv_b; p.conv_width = a.conv_width;
+    p.conv_in = a.conv_state != nullptr ? a.conv_state : a.conv_in;
+    p.conv_out = a.conv_state != nullptr ? a.conv_state : a.conv_out;
     return a.io == 1 ? launch_update<ScanUpdConv, uint16_t>(p, a, true, stream)
                      : launch_update<ScanUpdConv, float>(p, a, true, stream);
   }
@@ -454,8 +466,6 @@ hipError_t ssd_update_launch(const UpdateArgs& a, hipStream_t stream) {
   UpdParams p = common(a);
   p.H = a.H; p.P = a.P; p.G = a.G;
   p.rows = a.batch * a.H * a.P;
-  p.state_in = a.state != nullptr ? a.state : a.state_in;
-  p.state_out = a.state != nullptr ? a.state : a.state_out;
   if (a.lam != nullptr) {
     p.lam = a.lam; p.x_prev = a.x_prev; p.B_prev = a.B_prev;
     if (a.omega != nullptr) {   // dstate is even: lanes own whole pairs (groups of 4 or 8 from a multiple of 4)

@@ -99,14 +99,16 @@ struct UpdateArgs {
   const float* conv_w = nullptr;   // [dim, conv_width]
   const float* conv_b = nullptr;   // [dim], nullable
   void* conv_state = nullptr;      // [batch, conv_width - 1, dim], read and advanced in place
+  const void* conv_in = nullptr;   // with conv_state == nullptr: the window before the first token (nullable)
+  void* conv_out = nullptr;        // and the window after the last (nullable: not written)
   int conv_width = 0;
   // multi-head form only: the Mamba-3 exponential-trapezoidal rule
   const void* lam = nullptr;       // [batch, L, H]; nullable = the Mamba-2 rule
   const void* x_prev = nullptr;    // [batch, H, P], the token before the first one; nullable = none
   const void* B_prev = nullptr;    // [batch, G, N], likewise
   const float* omega = nullptr;    // [H, N/2] rotation rates of the state pairs (complex state); nullable
-  // multi-head form with state == nullptr: the state before the first token (nullable: zero) and the
-  // one written after the last (nullable: not written), for a whole sequence run through this kernel
+  // with state == nullptr: the state before the first token (nullable: zero) and the one written
+  // after the last (nullable: not written), for a whole sequence run through the update kernel
   const float* state_in = nullptr;
   float* state_out = nullptr;
 };

@@ -76,9 +76,10 @@ def test_conv_width1_unit_tap_is_silu_of_input(M):
 
 
 def test_conv_rejects_unsupported(M):
+    """A convolution wider than 4 taps is refused (other dstates run on the recurrent route)."""
     cfg = W.scan_config(1, 8, 16, 8, io="f32", cfg_id=951)
     inp = W.make_scan_inputs(cfg)
-    w = np.ones((16, 2), np.float32)
+    w = np.ones((16, 5), np.float32)
     with pytest.raises(M.MssmError, match="UNSUPPORTED|unsupported"):
         M.selective_scan_conv_fwd(dev(inp.x), dev(w), None, None, dev(inp.delta), dev(inp.A), dev(inp.B),
                                   dev(inp.C))

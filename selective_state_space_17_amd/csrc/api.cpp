@@ -745,6 +745,7 @@ int ssd_fwd_recurrent(const mssm_ssd_desc& d, const void* x, const void* delta, 
     if (overlap(final_state, b_st, ins[i], inb[i])) return MSSM_ERR_INVALID_ARG;
   }
   if (overlap(out, b_io, final_state, b_st)) return MSSM_ERR_INVALID_ARG;
+  if (!has_steps && final_state == nullptr) return MSSM_OK;   // nothing to compute or store
   if (mssm::update_grid_blocks(d.batch * d.nheads * d.headdim, d.dstate) > std::numeric_limits<int32_t>::max())
     return MSSM_ERR_UNSUPPORTED;
   mssm::UpdateArgs a{};

@@ -4,8 +4,15 @@
 
 A step is one full forward pass (the whole hot path) over one batch of the
 workload, with inputs already resident in HBM.  The default workload is the
-Mamba-1 130M-like layer (batch 8, L 2048, d_inner 1536, d_state 16, bf16 I/O,
-fp32 state).  Prints one JSON line on stdout; progress goes to stderr.
+largest one-GPU configuration: the long-context Mamba-1 scan (batch 1,
+L 2^20, d_inner 2048, d_state 16, bf16 I/O, fp32 state, final state
+returned), which the library splits into sequence chunks with an exact
+inter-chunk carry.  Prints one JSON line on stdout; progress goes to stderr.
+
+The roofline object leads with the HBM fraction (algorithmic bytes over the
+measured call time, against 8 TB/s); the VALU-issue and, for the multi-head
+form, matrix-core fractions stand beside it, and `limiter` names the ceiling
+the call is closest to.
 
 Inputs rotate over several resident copies so that consecutive steps never
 read data the 256 MB memory-side cache still holds from the previous step.
@@ -51,12 +58,12 @@ def source_digest(is_ssd: bool, decode: bool = False, backward: bool = False) ->
 
 
 def kernel_tags(is_ssd: bool, decode: bool = False, backward: bool = False):
-    """Name fragments of the kernels that carry the workload's scan (the dominant one per launch)."""
+    """Name fragments of every kernel one call of the workload launches (the first names the dominant one)."""
     if backward:
-        return ("scan_bwd_kernel",)
+        return ("scan_bwd_kernel", "bwd_reduce")
     if decode:
         return ("ssd_update_kernel",) if is_ssd else ("scan_update_kernel",)
-    return ("ssd_kernel",) if is_ssd else ("wide_kernel", "scan_kernel")
+    return ("ssd_kernel",) if is_ssd else ("wide_kernel", "scan_kernel", "carry_kernel")
 
 
 def load_traffic(workload: str, is_ssd: bool, decode: bool = False, backward: bool = False):
@@ -79,9 +86,9 @@ def _counter_rows(d, counter):
 
 def summarize_counters(cfg, is_ssd, d, copy_mib):
     """Turn the four rocprofv3 --pmc runs under d (workload FETCH_SIZE / WRITE_SIZE, copy FETCH_SIZE /
-    WRITE_SIZE) into HBM bytes per launch of the dominant kernel, each counter scaled by what it
-    reads for a device copy of copy_mib MiB, and write profiles/traffic_<workload>.json."""
-    import numpy as np
+    WRITE_SIZE) into HBM bytes per call of the workload (every kernel the call launches, summed; the
+    calls are counted by the dominant kernel's dispatches), each counter scaled by what it reads for a
+    device copy of copy_mib MiB, and write profiles/traffic_<workload>.json."""
     bwd = getattr(cfg, "backward", False) or getattr(cfg, "train", False)   # the gradient kernel dominates
     tags = kernel_tags(is_ssd, cfg.decode, bwd)
     copy_bytes = copy_mib << 20
@@ -94,20 +101,18 @@ def summarize_counters(cfg, is_ssd, d, copy_mib):
             cd = os.path.join(os.path.dirname(os.path.abspath(d)), "copy_" + counter.lower())
         copy_kib = max(v for _, v in _counter_rows(cd, counter))
         factor = copy_bytes / (copy_kib * 1024.0)
-        rows = _counter_rows(os.path.join(d, "pmc_" + counter.lower()), counter)
-        # the dominant kernel: the first tag with dispatches (the single-pass or chunk kernel)
-        vals, name = [], None
-        for tag in tags:
-            hits = [(n, v) for n, v in rows if tag in n]
-            if hits:
-                name = max(set(n for n, _ in hits), key=lambda k: sum(v for n, v in hits if n == k))
-                vals = [v for n, v in hits if n == name]
-                break
-        if not vals:
+        rows = [(n, v) for n, v in _counter_rows(os.path.join(d, "pmc_" + counter.lower()), counter)
+                if any(tag in n for tag in tags)]
+        if not rows:
             raise SystemExit(f"no {tags} dispatches with {counter} under {d}")
+        names = sorted(set(n for n, _ in rows))
+        # the dominant kernel: the one moving the most bytes; each call launches it once
+        name = max(names, key=lambda k: sum(v for n, v in rows if n == k))
+        calls = sum(1 for n, _ in rows if n == name)
+        kib = sum(v for _, v in rows) / calls
         res["kernel"] = name
-        kib = float(np.mean(vals))
-        res[counter] = {"kib_per_dispatch": kib, "dispatches": len(vals), "copy_kib": copy_kib,
+        res["kernels_per_call"] = {k: sum(1 for n, _ in rows if n == k) / calls for k in names}
+        res[counter] = {"kib_per_call": kib, "calls": calls, "copy_kib": copy_kib,
                         "scale": factor, "bytes_per_launch": kib * 1024.0 * factor}
         total += kib * 1024.0 * factor
     res["hbm_bytes_per_launch"] = total
@@ -217,10 +222,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2,
+    ap.add_argument("--config", type=int, default=5,
                     help="workload id (1-13; 6, 7: decode steps; 8: gradients; 9: convolution fused in front; "
                          "10: training step; 11, 12: Mamba-3 SISO recurrence and its decode step; 13: that decode "
-                         "step with the complex-valued state); 2 is the one the metric is quoted on")
+                         "step with the complex-valued state); the default, 5, is the largest one-GPU "
+                         "configuration, the one the metric is quoted on")
     ap.add_argument("--sets", type=int, default=0, help="resident input copies to rotate over (0: auto)")
     ap.add_argument("--chunk", type=int, default=0, help="SSD time-chunk length (0: the workload's)")
     ap.add_argument("--split-seq", type=int, default=0, help="force the sequence-chunk count (0: the planner's)")
@@ -436,28 +442,27 @@ def main():
 
     upd_s = cfg.updates / (wall / args.steps)
     kern_s = ms * 1e-3
-    hbm = {"achieved": alg_bytes / kern_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-           "frac": alg_bytes / kern_s / 1e9 / PEAK_HBM_GBS}
     traffic = load_traffic(cfg.name, is_ssd, decode, backward or train)
+    # the headline roofline is HBM: algorithmic bytes over the event-timed call
+    roof = {"bound": "hbm", "achieved": alg_bytes / kern_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / PEAK_HBM_GBS
+    roof["traffic"] = traffic
+
+    def alu_obj(slots):
+        a = {"achieved": slots / kern_s / 1e12, "peak": PEAK_VALU_TSLOT, "unit": "Tslot/s"}
+        a["frac"] = a["achieved"] / a["peak"]
+        return a
+
     if backward or train:
         # the whole backward call (gradient kernel and the two small fixed-order sum kernels); a training
         # step adds the forward before it
         slots = cfg.updates * SLOTS_PER_UPDATE_BWD + cfg.batch * cfg.seqlen * cfg.dim * SLOTS_PER_STEP_CHANNEL_BWD
         if train:
             slots += cfg.updates * SLOTS_PER_UPDATE + cfg.batch * cfg.seqlen * cfg.dim * SLOTS_PER_STEP_CHANNEL
-        alu = {"achieved": slots / kern_s / 1e12, "peak": PEAK_VALU_TSLOT, "unit": "Tslot/s"}
-        alu["frac"] = alu["achieved"] / alu["peak"]
-        bound = "alu" if alu["frac"] >= hbm["frac"] else "hbm"
-        roof = dict(alu if bound == "alu" else hbm)
-        roof["bound"] = bound
-        roof["other"] = hbm if bound == "alu" else alu
+        roof["alu"] = alu_obj(slots)
     elif decode:
         # a few operations per byte of state: the HBM roofline bounds it
-        roof = dict(hbm)
-        roof["bound"] = "hbm"
-        slots = cfg.updates * (SLOTS_PER_UPDATE if not is_ssd else 4.0)
-        roof["other"] = {"achieved": slots / kern_s / 1e12, "peak": PEAK_VALU_TSLOT, "unit": "Tslot/s",
-                         "frac": slots / kern_s / 1e12 / PEAK_VALU_TSLOT}
+        roof["alu"] = alu_obj(cfg.updates * (SLOTS_PER_UPDATE if not is_ssd else 4.0))
     elif is_ssd:
         Q = 64   # the kernel evaluates any chunk length as 64-step blocks
         # matrix-core work of the block form per launch: causal in-block Q*Q*P/2 per step and head,
@@ -466,29 +471,25 @@ def main():
                                          + cfg.ngroups * Q * cfg.dstate / 2)
         mf = {"achieved": 2 * macs / kern_s / 1e12, "peak": PEAK_BF16_MFMA_TFLOPS, "unit": "TFLOP/s"}
         mf["frac"] = mf["achieved"] / mf["peak"]
-        bound = "hbm" if hbm["frac"] >= mf["frac"] else "mfma"
-        roof = dict(hbm if bound == "hbm" else mf)
-        roof["bound"] = bound
-        roof["other"] = mf if bound == "hbm" else hbm
+        roof["mfma"] = mf
     else:
         per_tc = SLOTS_PER_STEP_CHANNEL
         if getattr(cfg, "conv_width", 0):
             # the fused convolution: one FMA per tap, then its SiLU (mul, exp2 (2), add, rcp (2), mul)
             per_tc += cfg.conv_width + 7
-        slots = cfg.updates * SLOTS_PER_UPDATE + cfg.batch * cfg.seqlen * cfg.dim * per_tc
-        alu = {"achieved": slots / kern_s / 1e12, "peak": PEAK_VALU_TSLOT, "unit": "Tslot/s"}
-        alu["frac"] = alu["achieved"] / alu["peak"]
-        bound = "alu" if alu["frac"] >= hbm["frac"] else "hbm"
-        roof = dict(alu if bound == "alu" else hbm)
-        roof["bound"] = bound
-        roof["other"] = hbm if bound == "alu" else alu
-    roof["traffic"] = traffic
-    roof = {k: roof[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic", "other")}
+        roof["alu"] = alu_obj(cfg.updates * SLOTS_PER_UPDATE + cfg.batch * cfg.seqlen * cfg.dim * per_tc)
+    # the ceiling the call sits closest to
+    fr = {"hbm": roof["frac"], "alu": roof.get("alu", {}).get("frac", 0.0),
+          "mfma": roof.get("mfma", {}).get("frac", 0.0)}
+    roof["limiter"] = max(fr, key=fr.get)
     if backward:
         roof["scope"] = "whole backward call: scan_bwd_kernel, then bwd_reduce_bc and bwd_reduce_ad"
-    if train:
+    elif train:
         roof["scope"] = ("whole training step: wide_kernel storing checkpoints, then scan_bwd_kernel from them, "
                          "bwd_reduce_bc and bwd_reduce_ad")
+    elif not decode and not is_ssd and plan.get("split_seq", 1) > 1:
+        roof["scope"] = ("whole call: the chunk pass, carry_kernel (the scan over the chunks' maps), "
+                         "then the fix-up pass")
 
     cpu = None
     if not args.no_cpu_baseline:

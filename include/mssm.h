@@ -116,7 +116,7 @@ typedef struct {
  * blocks with the state carried between them (the same algebra, so only
  * rounding differs).  The matrix-core block kernel takes io_dtype MSSM_BF16
  * (the matrix cores take bf16 operands), headdim a multiple of 64, dstate a
- * multiple of 16 up to 128, nheads * headdim and ngroups * dstate up to 2^24;
+ * multiple of 16 up to 128, nheads * headdim and ngroups * dstate below 2^24;
  * there the state never leaves the chip between blocks, and x, z, out, B, C,
  * h0 and final_state must be 16-byte aligned.  Any other problem with io_dtype
  * MSSM_F32 or MSSM_BF16 and dstate up to 256 runs token by token through the
@@ -381,6 +381,14 @@ size_t mssm_selective_scan_bwd_workspace_size(const mssm_scan_desc* desc);
 /* The plan the library would use for a selective-scan descriptor:
  * writes the sequence-chunk count and lanes-per-channel; returns a status. */
 int mssm_selective_scan_plan(const mssm_scan_desc* desc, int32_t* split_seq, int32_t* split_state);
+
+/* Which kernel a multi-head descriptor runs on (mssm_ssd_fwd and
+ * mssm_ssd_trapezoidal_fwd): MSSM_SSD_ROUTE_BLOCK, the matrix-core block
+ * kernel, or MSSM_SSD_ROUTE_RECURRENT, the token-by-token update kernel (see
+ * mssm_ssd_desc).  Writes *route; returns a status (the descriptor's). */
+#define MSSM_SSD_ROUTE_BLOCK 0
+#define MSSM_SSD_ROUTE_RECURRENT 1
+int mssm_ssd_plan(const mssm_ssd_desc* desc, int32_t* route);
 
 /* Static text for a status code (never NULL). */
 const char* mssm_status_string(int status);

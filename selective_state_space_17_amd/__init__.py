@@ -46,6 +46,7 @@ SIGNATURES = {
                                       ctypes.POINTER(ctypes.c_int32)]),
     "mssm_ssd_fwd": (_I, [ctypes.POINTER(SSDDesc)] + [_P] * 10 + [_P, _SZ, _P]),
     "mssm_ssd_workspace_size": (_SZ, [ctypes.POINTER(SSDDesc)]),
+    "mssm_ssd_plan": (_I, [ctypes.POINTER(SSDDesc), ctypes.POINTER(ctypes.c_int32)]),
     "mssm_ssd_trapezoidal_fwd": (_I, [ctypes.POINTER(SSDDesc)] + [_P] * 11 + [_P, _SZ, _P]),
     "mssm_selective_state_update": (_I, [ctypes.POINTER(ScanDesc)] + [_P] * 10),
     "mssm_ssd_state_update": (_I, [ctypes.POINTER(SSDDesc)] + [_P] * 10),
@@ -398,6 +399,20 @@ def selective_scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, dout=None, df
 
 def ssd_desc(batch, seqlen, nheads, headdim, dstate, ngroups, chunk=0, io_dtype=MSSM_BF16) -> SSDDesc:
     return SSDDesc(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, io_dtype, 0)
+
+
+SSD_ROUTE_BLOCK = 0       # the matrix-core block kernel
+SSD_ROUTE_RECURRENT = 1   # token by token through the update kernel
+
+
+def ssd_plan(batch, seqlen, nheads, headdim, dstate, ngroups, chunk=0, io_dtype=MSSM_BF16) -> int:
+    """Which kernel the multi-head forward runs this problem on (SSD_ROUTE_BLOCK or SSD_ROUTE_RECURRENT)."""
+    d = ssd_desc(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, io_dtype)
+    r = ctypes.c_int32(-1)
+    st = lib.mssm_ssd_plan(ctypes.byref(d), ctypes.byref(r))
+    if st != MSSM_OK:
+        raise MssmError(st, "mssm_ssd_plan")
+    return r.value
 
 
 def ssd_workspace_size(batch, seqlen, nheads, headdim, dstate, ngroups, chunk=0) -> int:

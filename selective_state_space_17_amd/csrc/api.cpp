@@ -115,6 +115,9 @@ int plan_scan(const mssm_scan_desc& d, int* K_out, int* G_out) {
   const int64_t cpb = 256 / bestG;
   const int64_t blocks = d.batch * bestK * ((d.dim + cpb - 1) / cpb);
   if (blocks > std::numeric_limits<int32_t>::max()) return MSSM_ERR_UNSUPPORTED;
+  // with a split, the carry runs one wave per (b, c, n), four waves per block
+  if (bestK > 1 && (d.batch * d.dim * d.dstate + 3) / 4 > std::numeric_limits<int32_t>::max())
+    return MSSM_ERR_UNSUPPORTED;
   *K_out = bestK;
   *G_out = bestG;
   return MSSM_OK;
@@ -226,9 +229,10 @@ static int validate_ssd_desc(const mssm_ssd_desc* d, int64_t* Q, bool* matrix) {
   if (d->nheads % d->ngroups != 0 || d->dstate > 256) return MSSM_ERR_UNSUPPORTED;
   const int64_t q = d->chunk == 0 ? 64 : d->chunk;
   if (q != 64 && q != 128 && q != 256) return MSSM_ERR_UNSUPPORTED;
-  // per-step row strides of the block kernel are formed with 24-bit multiplies inside a 64-step block
+  // per-step row strides of the block kernel (nheads * headdim, ngroups * dstate) go through 24-bit
+  // multiplies, which read only the low 24 bits of an operand: both must stay below 2^24
   *matrix = d->io_dtype == MSSM_BF16 && mssm::ssd_supported(d->headdim, d->dstate) &&
-            d->nheads <= (1 << 24) / d->headdim && d->ngroups <= (1 << 24) / d->dstate;
+            d->nheads <= ((1 << 24) - 1) / d->headdim && d->ngroups <= ((1 << 24) - 1) / d->dstate;
   const int64_t es = d->io_dtype == MSSM_BF16 ? 2 : 4;
   int64_t t = 0;
   if (!mul_ok(d->batch, d->seqlen, &t) || !mul_ok(t, d->nheads, &t) || !mul_ok(t, d->headdim, &t) ||
@@ -699,6 +703,16 @@ int mssm_selective_scan_bwd(const mssm_scan_desc* desc, const void* x, const voi
     set_err(e);
     return MSSM_ERR_HIP;
   }
+  return MSSM_OK;
+}
+
+int mssm_ssd_plan(const mssm_ssd_desc* desc, int32_t* route) {
+  int64_t Q = 0;
+  bool matrix = false;
+  const int v = validate_ssd_desc(desc, &Q, &matrix);
+  if (v != MSSM_OK) return v;
+  if (route == nullptr) return MSSM_ERR_INVALID_ARG;
+  *route = matrix ? MSSM_SSD_ROUTE_BLOCK : MSSM_SSD_ROUTE_RECURRENT;
   return MSSM_OK;
 }
 

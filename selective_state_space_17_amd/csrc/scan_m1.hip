@@ -33,7 +33,8 @@
 //   pass 1  every chunk scans from a zero state (chunk 0 from h0), writes its
 //           outputs, its end state and the sum of its deltas S;
 //   carry   per (b, c, n): h_in[k] = hend[k-1] + exp2(A' S[k-1]) h_in[k-1]
-//           (the affine composition of consecutive chunks);
+//           (the affine composition of consecutive chunks), taken as a
+//           wave-level parallel scan over the chunks' maps;
 //   pass 2  chunks k >= 1 rescan from the true h_in[k], overwriting their
 //           outputs, until the part of the state carried in from before the
 //           chunk, bounded by exp2(max_n A'[n] * S_t) * max_n |h_in[n]|, is
@@ -1018,23 +1019,59 @@ __global__ __launch_bounds__(kThreads) void wide_kernel(KernelParams p) {
   }
 }
 
-// carry across chunks: one thread per (b, c, n)
+// Carry across chunks, as a wave-level parallel scan over the chunks' affine maps.
+// Chunk k >= 1 takes the state entering it to the state leaving it by
+//   h -> a_k h + hend_k,   a_k = exp2(A' S_k)   (hend_k: its end state from a zero start),
+// and two consecutive maps compose as (a1, b1) then (a2, b2) = (a1 a2, a2 b1 + b2), which is
+// associative ("03 - Modelos de espacio de estados", "Parallel scan").  One wave per (b, c, n):
+// lane j holds the m = ceil((K-1)/64) consecutive chunks from 1 + j m and composes them in order,
+// the wave scans the 64 lane maps in log2(64) = 6 shuffle steps, and each lane applies its
+// exclusive prefix to the true end state of chunk 0, then walks its chunks again writing h_in.
 __global__ __launch_bounds__(256) void carry_kernel(KernelParams p) {
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t total = p.batch * p.dim * p.N;
-  if (idx >= total) return;
-  const int64_t n = idx % p.N;
-  const int64_t c = (idx / p.N) % p.dim;
-  const int64_t b = idx / (p.N * p.dim);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t col = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kWave;
+  if (col >= p.batch * p.dim * p.N) return;   // col is uniform within a wave: whole waves leave
+  const int64_t n = col % p.N;
+  const int64_t c = (col / p.N) % p.dim;
+  const int64_t b = col / (p.N * p.dim);
   const float a2 = p.A[c * p.N + n] * kLog2e;
-  float h = p.hend[((b * p.K + 0) * p.dim + c) * p.N + n];
-  for (int k = 1; k < p.K; ++k) {
-    p.hin[((b * p.K + k) * p.dim + c) * p.N + n] = h;
-    const float s = p.S[(b * p.K + k) * p.dim + c];
-    h = __builtin_fmaf(exp2_hw(a2 * s), h, p.hend[((b * p.K + k) * p.dim + c) * p.N + n]);
+  const int K = p.K;
+  const int m = (K - 1 + kWave - 1) / kWave;
+  const int k_lo = 1 + lane * m;
+  const int k_hi = k_lo + m < K ? k_lo + m : K;
+  const float* __restrict__ S = p.S + b * K * p.dim + c;                // S[k * dim]
+  const float* __restrict__ he = p.hend + (b * K * p.dim + c) * p.N + n;   // hend[k * dim * N]
+  float* __restrict__ hi = p.hin + (b * K * p.dim + c) * p.N + n;
+  const int64_t ss = p.dim, hs = p.dim * p.N;
+  float am = 1.f, bm = 0.f;   // this lane's map, identity when it holds no chunk
+  for (int k = k_lo; k < k_hi; ++k) {
+    const float ak = exp2_hw(a2 * S[k * ss]);
+    bm = __builtin_fmaf(ak, bm, he[k * hs]);
+    am *= ak;
   }
-  if (p.final_state != nullptr) p.final_state[(b * p.dim + c) * p.N + n] = h;
+  // inclusive scan over the lanes: the maps of earlier lanes act first
+  for (int off = 1; off < kWave; off <<= 1) {
+    const float ap = __shfl_up(am, off), bp = __shfl_up(bm, off);
+    if (lane >= off) {
+      bm = __builtin_fmaf(am, bp, bm);
+      am *= ap;
+    }
+  }
+  float ae = __shfl_up(am, 1), be = __shfl_up(bm, 1);
+  if (lane == 0) {
+    ae = 1.f;
+    be = 0.f;
+  }
+  float h = __builtin_fmaf(ae, he[0], be);   // state entering chunk k_lo
+  for (int k = k_lo; k < k_hi; ++k) {
+    hi[k * hs] = h;
+    h = __builtin_fmaf(exp2_hw(a2 * S[k * ss]), h, he[k * hs]);
+  }
+  if (p.final_state != nullptr && k_lo < K && k_hi == K) p.final_state[(b * p.dim + c) * p.N + n] = h;
 }
+
+// blocks of the carry kernel: one wave per (b, c, n), 4 waves per block
+int64_t carry_blocks(int64_t batch, int64_t dim, int64_t N) { return (batch * dim * N + 3) / 4; }
 
 size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
@@ -1053,8 +1090,7 @@ hipError_t launch_cfg(const KernelParams& kp, int64_t batch, hipStream_t stream)
     if (e != hipSuccess) return e;
   }
   {
-    const int64_t total = batch * kp.dim * kp.N;
-    const dim3 grid(static_cast<unsigned>((total + 255) / 256));
+    const dim3 grid(static_cast<unsigned>(carry_blocks(batch, kp.dim, kp.N)));
     hipLaunchKernelGGL(carry_kernel, grid, dim3(256), 0, stream, kp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1084,8 +1120,7 @@ hipError_t launch_wide(const KernelParams& kp, int64_t batch, hipStream_t stream
     if (e != hipSuccess) return e;
   }
   {
-    const int64_t total = batch * kp.dim * kp.N;
-    const dim3 grid(static_cast<unsigned>((total + 255) / 256));
+    const dim3 grid(static_cast<unsigned>(carry_blocks(batch, kp.dim, kp.N)));
     hipLaunchKernelGGL(carry_kernel, grid, dim3(256), 0, stream, kp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

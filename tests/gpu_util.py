@@ -55,3 +55,39 @@ def check(got: np.ndarray, ref: np.ndarray, rtol: float, what: str) -> dict:
         raise AssertionError(f"{what}: {int(bad.sum())}/{ref.size} elements out of tolerance {rtol}; "
                              f"worst at {i}: got {got[i]!r} ref {ref[i]!r}; max rel {rel:.3e}, normwise {nw:.3e}")
     return {"max_rel": rel, "normwise": nw}
+
+
+class StreamCheck:
+    """The same rule as check(), applied to a tensor compared block by block (when neither side fits in
+    memory at once as fp64).  An element fails iff err > rtol*|r| and err > rtol*rms(r) with rms over the
+    whole tensor, so per block it is enough to keep sum(r^2), the element count, and the largest error
+    among elements that already exceed rtol*|r|; finish() then compares that with rtol*rms."""
+
+    def __init__(self, rtol: float, what: str):
+        self.rtol, self.what = rtol, what
+        self.sq, self.n, self.worst, self.where = 0.0, 0, 0.0, None
+        self.err2, self.max_rel_abs = 0.0, 0.0
+
+    def add(self, got: np.ndarray, ref: np.ndarray, tag) -> None:
+        got = np.asarray(got, np.float64)
+        ref = np.asarray(ref, np.float64)
+        assert got.shape == ref.shape, f"{self.what} {tag}: shape {got.shape} vs {ref.shape}"
+        assert np.all(np.isfinite(got)), f"{self.what} {tag}: non-finite GPU values"
+        self.sq += float(np.sum(ref * ref))
+        self.n += ref.size
+        err = np.abs(got - ref)
+        self.err2 += float(np.sum(err * err))
+        over = err > self.rtol * np.abs(ref)
+        if over.any():
+            e = float(err[over].max())
+            if e > self.worst:
+                self.worst = e
+                i = np.unravel_index(np.argmax(np.where(over, err, -1.0)), ref.shape)
+                self.where = (tag, i, float(got[i]), float(ref[i]))
+
+    def finish(self) -> dict:
+        rms = float(np.sqrt(self.sq / max(self.n, 1)))
+        if self.worst > self.rtol * rms:
+            raise AssertionError(f"{self.what}: worst error {self.worst!r} above rtol*rms = {self.rtol * rms!r} "
+                                 f"(and above rtol*|ref|) at {self.where}")
+        return {"rms": rms, "worst_over_rtol_ref": self.worst, "normwise": float(np.sqrt(self.err2 / max(self.sq, 1e-300)))}

@@ -180,6 +180,28 @@ def test_ssd_recurrent_shapes_accepted(kw):
     assert M.lib.mssm_ssd_workspace_size(ctypes.byref(d)) == 0
 
 
+def test_ssd_route():
+    block, rec = M.SSD_ROUTE_BLOCK, M.SSD_ROUTE_RECURRENT
+    # the workload's shape and the shapes the block kernel takes
+    assert M.ssd_plan(8, 4096, 32, 64, 128, 1, 256) == block
+    assert M.ssd_plan(1, 1, 3, 128, 48, 3, 0) == block
+    for kw in RECURRENT_SSD:
+        a = dict(batch=2, seqlen=128, nheads=4, headdim=64, dstate=64, ngroups=1, chunk=64, io_dtype=M.MSSM_BF16)
+        a.update(kw)
+        assert M.ssd_plan(**a) == rec, kw
+    # per-step row strides go through 24-bit multiplies: nheads * headdim and ngroups * dstate below 2^24 only
+    assert M.ssd_plan(1, 8, (1 << 18) - 1, 64, 64, 1) == block          # nheads * headdim = 2^24 - 64
+    assert M.ssd_plan(1, 8, 1 << 18, 64, 64, 1) == rec                  # exactly 2^24: low 24 bits would be 0
+    assert M.ssd_plan(1, 8, 1 << 17, 128, 64, 1) == rec
+    assert M.ssd_plan(1, 8, 1 << 20, 64, 16, 1 << 20) == rec            # ngroups * dstate = 2^24
+    assert M.ssd_plan(1, 8, (1 << 20) - 1, 64, 16, (1 << 20) - 1) == rec   # nheads * headdim > 2^24
+    assert M.ssd_plan(1, 8, 1 << 16, 64, 16, 1 << 16) == block
+    with pytest.raises(M.MssmError):
+        M.ssd_plan(1, 8, 6, 64, 64, 4)                                  # nheads % ngroups != 0
+    d = M.ssd_desc(1, 8, 4, 64, 64, 1)
+    assert M.lib.mssm_ssd_plan(ctypes.byref(d), None) == M.MSSM_ERR_INVALID_ARG
+
+
 def test_ssd_pointer_checks():
     d = M.ssd_desc(2, 128, 4, 64, 64, 1, 64)
     assert _ssd_call(d, x=None) == M.MSSM_ERR_INVALID_ARG

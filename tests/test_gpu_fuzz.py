@@ -263,3 +263,66 @@ def host_raw(t):
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).cpu().numpy().view(np.uint16)
     return t.cpu().numpy()
+
+
+def _ssd_any_case(seed):
+    """Any multi-head problem: either I/O type, any headdim, dstate up to 256, several groups -- mostly
+    shapes the matrix-core block kernel does not take, which run through the recurrent update kernel."""
+    r = np.random.default_rng(seed)
+    io = str(r.choice(["f32", "bf16"]))
+    g = int(r.choice([1, 2, 3]))
+    h = g * int(r.integers(1, 4))
+    p = int(r.integers(1, 140))
+    n = int(r.integers(1, 257))
+    b, l = int(r.integers(1, 3)), int(r.integers(1, 200))
+    return b, l, h, p, n, g, io, bool(r.integers(2)), bool(r.integers(2)), bool(r.integers(2))
+
+
+@pytest.mark.parametrize("seed", list(range(7600, 7610)))
+def test_fuzz_ssd_any_shape(M, seed):
+    """Both multi-head sequence entry points (the Mamba-2 and the Mamba-3 rule) at random shapes and I/O
+    types off the block kernel's grid; each draw states the route the library takes."""
+    import torch
+    b, l, h, p, n, g, io, hd, hz, hh = case = _ssd_any_case(seed)
+    route = M.ssd_plan(b, l, h, p, n, g, 0, M.MSSM_BF16 if io == "bf16" else M.MSSM_F32)
+    say("fuzz ssd any shape", seed, case, "route", route)
+    cfg = W.ssd_config(b, l, h, p, n, g, io=io, cfg_id=seed)
+    s = W.make_ssd_inputs(cfg, with_D=hd, with_z=hz, with_h0=hh)
+    out, fin = M.ssd_fwd(dev(s.x), dev(s.delta), dev(s.A), dev(s.B), dev(s.C), dev(s.D), dev(s.z), dev(s.h0),
+                         return_final_state=True)
+    torch.cuda.synchronize()
+    ref, ref_fin = oracle.ssd_fwd(s.x, s.delta, s.A, s.B, s.C, s.D, s.z, s.h0)
+    check(host64(out), ref, RTOL[io], f"{case} out")
+    check(host64(fin), ref_fin, RTOL[io], f"{case} final_state")
+    lam = W.make_ssd_lam(cfg)
+    out, fin = M.ssd_trapezoidal_fwd(dev(s.x), dev(s.delta), dev(lam), dev(s.A), dev(s.B), dev(s.C), dev(s.D),
+                                     dev(s.z), dev(s.h0), return_final_state=True)
+    torch.cuda.synchronize()
+    ref, ref_fin = oracle.ssd3_fwd(s.x, s.delta, lam, s.A, s.B, s.C, s.D, s.z, s.h0)
+    check(host64(out), ref, RTOL[io], f"{case} trapezoidal out")
+    check(host64(fin), ref_fin, RTOL[io], f"{case} trapezoidal final_state")
+
+
+@pytest.mark.parametrize("seed", list(range(7700, 7706)))
+def test_fuzz_conv_scan_any_shape(M, seed):
+    """The convolution + scan at shapes the fused kernel does not take (any dstate up to 256, rows that are
+    not a multiple of 16 bytes): the recurrent route, against the fused oracle."""
+    import torch
+    r = np.random.default_rng(seed)
+    io = str(r.choice(["f32", "bf16"]))
+    b, l, d = int(r.integers(1, 3)), int(r.integers(1, 300)), int(r.integers(1, 200))
+    n = int(r.integers(1, 257))
+    width = int(r.integers(1, 5))
+    hb, hi, hh, hd, hz = (bool(v) for v in r.integers(2, size=5))
+    case = (b, l, d, n, width, io, hb, hi, hh, hd, hz)
+    say("fuzz conv scan any shape", seed, case)
+    cfg = W.scan_config(b, l, d, n, io=io, has_D=hd, has_z=hz, cfg_id=seed)
+    inp = W.make_scan_inputs(cfg, with_h0=hh)
+    w, bias, init = W.make_conv_inputs(cfg, width, with_bias=hb, with_init=hi)
+    out, fin = M.selective_scan_conv_fwd(dev(inp.x), dev(w), dev(bias), dev(init), dev(inp.delta), dev(inp.A),
+                                         dev(inp.B), dev(inp.C), dev(inp.D), dev(inp.z), dev(inp.h0),
+                                         return_final_state=True)
+    torch.cuda.synchronize()
+    ref, ref_fin = oracle.conv_scan_fwd(inp.x, w, bias, init, inp.delta, inp.A, inp.B, inp.C, inp.D, inp.z, inp.h0)
+    check(host64(out), ref, RTOL[io], f"{case} out")
+    check(host64(fin), ref_fin, RTOL[io], f"{case} final_state")

@@ -4,7 +4,7 @@ import pytest
 
 import oracle
 import workloads as W
-from gpu_util import RTOL, check, dev, host64, say
+from gpu_util import RTOL, StreamCheck, check, dev, host64, say
 
 pytestmark = pytest.mark.gpu
 
@@ -186,15 +186,42 @@ def test_config_full(M, cid):
     say(cfg.name, st)
 
 
-def test_config5_sampled(M):
+def test_config5_full(M):
+    """The long-context workload the benchmark times (1 x 2^20 steps x 2048 channels x 16 states, bf16),
+    split into sequence chunks by the planner: every output element and every final-state element against
+    the oracle, which runs over blocks of channels (its fp64 output for all of them would need 17 GB)."""
+    import torch
     cfg = W.CONFIGS[5]
-    say("config", cfg.name, "plan", M.selective_scan_plan(cfg.batch, cfg.seqlen, cfg.dim, cfg.dstate))
+    plan = M.selective_scan_plan(cfg.batch, cfg.seqlen, cfg.dim, cfg.dstate)
+    say("config", cfg.name, "plan", plan)
+    assert plan[0] > 1, "the long sequence is expected to run sequence-parallel"
     inp = W.make_scan_inputs(cfg)
     out, fin = run_gpu(M, inp)
-    # channels sampled from the first, a middle and the last channel group, over the whole 1M steps
-    for c0, c1 in ((0, 24), (1000, 1040), (2040, 2048)):
+    out_bits = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    fin = host64(fin)
+    del out
+    so, sf = StreamCheck(RTOL["bf16"], "config5 out"), StreamCheck(RTOL["bf16"], "config5 final_state")
+    step = 256
+    for c0 in range(0, cfg.dim, step):
+        c1 = min(cfg.dim, c0 + step)
         ref, ref_fin = oracle.scan_fwd(inp.x, inp.delta, inp.A, inp.B, inp.C, inp.D, inp.z, None, c0=c0, c1=c1)
-        got = host64(out[:, :, c0:c1].contiguous())
-        st = check(got, ref, RTOL["bf16"], f"config5 channels {c0}:{c1}")
-        check(host64(fin)[:, c0:c1], ref_fin, RTOL["bf16"], f"config5 final {c0}:{c1}")
-        say("config5", c0, c1, st)
+        so.add(W.bf16_bits_to_f32(out_bits[:, :, c0:c1]), ref, (c0, c1))
+        sf.add(fin[:, c0:c1], ref_fin, (c0, c1))
+        del ref, ref_fin
+        say("config5 channels", c0, c1, "compared")
+    say("config5", so.finish(), sf.finish())
+
+
+@pytest.mark.parametrize("G", [1, 16])
+def test_sequence_split_4096(M, G):
+    """The largest chunk count the ABI admits (4096 chunks of 3 steps, and a ragged tail of empty chunks):
+    against the oracle, and against the unsplit scan."""
+    for L in (12288, 10001):
+        cfg = W.scan_config(2, L, 64, 16, io="bf16", cfg_id=408)
+        inp = W.make_scan_inputs(cfg, with_h0=True)
+        say("split 4096", L, G)
+        compare(M, inp, "bf16", f"K=4096 G={G} L={L}", split_seq=4096, split_state=G)
+        o1, f1 = run_gpu(M, inp, split_seq=1, split_state=G)
+        o2, f2 = run_gpu(M, inp, split_seq=4096, split_state=G)
+        check(host64(o2), host64(o1), 1e-2, "4096 chunks against one out")
+        check(host64(f2), host64(f1), 1e-4, "4096 chunks against one final")

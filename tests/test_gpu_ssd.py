@@ -105,16 +105,17 @@ def test_ssd_matches_broadcast_scan_on_gpu(M):
     check(host64(fin).reshape(b, h * p, 16), host64(f2), 2e-2, "ssd vs scan final")
 
 
-def test_config4_sampled_heads(M):
+def test_config4_full(M):
+    """The 8 x 4096 x 32-head x 64 x 128 workload the benchmark times: every output and final-state element
+    against the oracle."""
     cfg = W.CONFIGS[4]
     say("config", cfg.name)
     s = W.make_ssd_inputs(cfg)
     out, fin = run_gpu(M, s, chunk=cfg.chunk)
-    for hd0, hd1 in ((0, 2), (17, 18), (31, 32)):
-        ref, ref_fin = oracle.ssd_fwd(s.x, s.delta, s.A, s.B, s.C, None, None, None, hd0=hd0, hd1=hd1)
-        st = check(host64(out[:, :, hd0:hd1].contiguous()), ref, RTOL["bf16"], f"config4 heads {hd0}:{hd1}")
-        check(host64(fin[:, hd0:hd1].contiguous()), ref_fin, RTOL["bf16"], f"config4 final {hd0}:{hd1}")
-        say("config4", hd0, hd1, st)
+    ref, ref_fin = oracle.ssd_fwd(s.x, s.delta, s.A, s.B, s.C, None, None, None)
+    st = check(host64(out), ref, RTOL["bf16"], "config4 out")
+    check(host64(fin), ref_fin, RTOL["bf16"], "config4 final")
+    say("config4", st)
 
 
 @pytest.mark.parametrize("dstate", [48, 80])

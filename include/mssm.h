@@ -61,7 +61,9 @@
  *    of the calling thread's last failure is returned by
  *    mssm_last_error_detail().
  *  - Thread-safe: no mutable global state (apart from that per-thread error
- *    text).  Calls on different streams may overlap.
+ *    text, and the per-device scratch address that
+ *    mssm_selective_scan_fwd_noalloc looks up once).  Calls on different
+ *    streams may overlap (mssm_selective_scan_fwd_noalloc excepted: see there).
  */
 #ifndef MSSM_H
 #define MSSM_H
@@ -141,6 +143,25 @@ int mssm_selective_scan_fwd(const mssm_scan_desc* desc,
 /* Bytes of workspace mssm_selective_scan_fwd needs for this problem (0 when
  * the sequence is not split).  Returns 0 for an invalid descriptor too. */
 size_t mssm_selective_scan_workspace_size(const mssm_scan_desc* desc);
+
+/* mssm_selective_scan_fwd for callers that cannot allocate device memory at
+ * the call (code under stream capture, tight serving loops, harnesses that
+ * forbid allocation): no workspace argument.  A split sequence keeps its
+ * chunk aggregates in a fixed scratch array of 32 MiB that the library holds
+ * on each GPU it runs on, from the first such call there until the process
+ * ends; this call itself allocates nothing.  With split_seq = 0 the library's
+ * plan is used, with fewer chunks where its workspace
+ * (mssm_selective_scan_workspace_size) would exceed 32 MiB; a forced
+ * split_seq whose workspace exceeds 32 MiB returns MSSM_ERR_WORKSPACE.  Every
+ * call on one GPU shares that GPU's scratch: calls ordered on one stream are
+ * safe (kernels write each scratch element before reading it, so nothing
+ * needs clearing between calls), calls that overlap on one GPU race.
+ * Results equal mssm_selective_scan_fwd's for the same plan, bit for bit.
+ * All other arguments and rules as mssm_selective_scan_fwd. */
+int mssm_selective_scan_fwd_noalloc(const mssm_scan_desc* desc,
+                                    const void* x, const void* delta, const float* A,
+                                    const void* B, const void* C, const float* D, const void* z,
+                                    const float* h0, void* out, float* final_state, void* stream);
 
 /* Mamba-2 scalar-A multi-head forward.  Same ownership, stream and error rules
  * as mssm_selective_scan_fwd. */

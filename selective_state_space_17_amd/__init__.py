@@ -42,6 +42,7 @@ _P, _SZ, _I = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
 SIGNATURES = {
     "mssm_selective_scan_fwd": (_I, [ctypes.POINTER(ScanDesc)] + [_P] * 10 + [_P, _SZ, _P]),
     "mssm_selective_scan_workspace_size": (_SZ, [ctypes.POINTER(ScanDesc)]),
+    "mssm_selective_scan_fwd_noalloc": (_I, [ctypes.POINTER(ScanDesc)] + [_P] * 10 + [_P]),
     "mssm_selective_scan_plan": (_I, [ctypes.POINTER(ScanDesc), ctypes.POINTER(ctypes.c_int32),
                                       ctypes.POINTER(ctypes.c_int32)]),
     "mssm_ssd_fwd": (_I, [ctypes.POINTER(SSDDesc)] + [_P] * 10 + [_P, _SZ, _P]),
@@ -217,6 +218,41 @@ def selective_scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, return_final_
     if st != MSSM_OK:
         raise MssmError(st, "mssm_selective_scan_fwd")
     return (out, final_state) if return_final_state else out
+
+
+SCRATCH_BYTES = 32 << 20   # the per-device scratch mssm_selective_scan_fwd_noalloc keeps its chunk aggregates in
+
+
+def selective_scan_fwd_noalloc(x, delta, A, B, C, D=None, z=None, h0=None, out=None, final_state=None,
+                               split_seq: int = 0, split_state: int = 0, stream=None):
+    """mssm_selective_scan_fwd_noalloc: the forward with no workspace (a split sequence keeps its chunk
+    aggregates in the library's fixed per-device scratch).  ``out`` (and ``final_state``, when wanted)
+    must be given, so that nothing is allocated here either; returns out."""
+    torch = _torch()
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, seqlen, dim]")
+    if out is None:
+        raise ValueError("out must be given: this entry point allocates nothing")
+    bsz, L, dm = x.shape
+    if A.dim() != 2 or A.shape[0] != dm:
+        raise ValueError("A must be [dim, dstate]")
+    N = A.shape[1]
+    io = _io_code(x.dtype)
+    cur = torch.cuda.current_device()
+    for name, t, shape in (("x", x, (bsz, L, dm)), ("delta", delta, (bsz, L, dm)), ("z", z, (bsz, L, dm)),
+                           ("B", B, (bsz, L, N)), ("C", C, (bsz, L, N)), ("out", out, (bsz, L, dm))):
+        _check_gpu(name, t, x.dtype, shape, cur)
+    _check_gpu("A", A, torch.float32, (dm, N), cur)
+    _check_gpu("D", D, torch.float32, (dm,), cur)
+    _check_gpu("h0", h0, torch.float32, (bsz, dm, N), cur)
+    _check_gpu("final_state", final_state, torch.float32, (bsz, dm, N), cur)
+    d = scan_desc(bsz, L, dm, N, io, split_seq, split_state)
+    st = lib.mssm_selective_scan_fwd_noalloc(ctypes.byref(d), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                                             _ptr(D), _ptr(z), _ptr(h0), _ptr(out), _ptr(final_state),
+                                             _stream_handle(stream))
+    if st != MSSM_OK:
+        raise MssmError(st, "mssm_selective_scan_fwd_noalloc")
+    return out
 
 
 def selective_scan_checkpoint_size(batch, seqlen, dim, dstate=16, io_dtype=MSSM_BF16) -> int:

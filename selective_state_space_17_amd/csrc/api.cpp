@@ -162,9 +162,14 @@ size_t mssm_selective_scan_workspace_size(const mssm_scan_desc* desc) {
   return mssm::scan_workspace_bytes(desc->batch, desc->dim, desc->dstate, K);
 }
 
-int mssm_selective_scan_fwd(const mssm_scan_desc* desc, const void* x, const void* delta, const float* A,
-                            const void* B, const void* C, const float* D, const void* z, const float* h0, void* out,
-                            float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// The forward behind both entry points.  use_scratch: the workspace is the device's fixed scratch,
+// looked up after every argument check has passed (workspace/workspace_bytes are then ignored).
+int scan_fwd_impl(const mssm_scan_desc* desc, const void* x, const void* delta, const float* A, const void* B,
+                  const void* C, const float* D, const void* z, const float* h0, void* out, float* final_state,
+                  void* workspace, size_t workspace_bytes, bool use_scratch, void* stream) {
   const int v = validate_scan_desc(desc);
   if (v != MSSM_OK) return v;
   const mssm_scan_desc& d = *desc;
@@ -194,7 +199,17 @@ int mssm_selective_scan_fwd(const mssm_scan_desc* desc, const void* x, const voi
   const int pr = plan_scan(d, &K, &G);
   if (pr != MSSM_OK) return pr;
   const size_t need = mssm::scan_workspace_bytes(d.batch, d.dim, d.dstate, K);
-  if (need > 0) {
+  if (use_scratch) {
+    if (need > mssm::kScratchBytes) return MSSM_ERR_WORKSPACE;
+    workspace = nullptr;
+    if (need > 0) {
+      const hipError_t e = mssm::scratch_address(static_cast<hipStream_t>(stream), &workspace);
+      if (e != hipSuccess) {
+        set_err(e);
+        return MSSM_ERR_HIP;
+      }
+    }
+  } else if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need) return MSSM_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return MSSM_ERR_MISALIGNED;
     if (overlap(workspace, static_cast<int64_t>(need), out, b_io) ||
@@ -213,6 +228,37 @@ int mssm_selective_scan_fwd(const mssm_scan_desc* desc, const void* x, const voi
     return MSSM_ERR_HIP;
   }
   return MSSM_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int mssm_selective_scan_fwd(const mssm_scan_desc* desc, const void* x, const void* delta, const float* A,
+                            const void* B, const void* C, const float* D, const void* z, const float* h0, void* out,
+                            float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
+  return scan_fwd_impl(desc, x, delta, A, B, C, D, z, h0, out, final_state, workspace, workspace_bytes, false,
+                       stream);
+}
+
+int mssm_selective_scan_fwd_noalloc(const mssm_scan_desc* desc, const void* x, const void* delta, const float* A,
+                                    const void* B, const void* C, const float* D, const void* z, const float* h0,
+                                    void* out, float* final_state, void* stream) {
+  const int v = validate_scan_desc(desc);
+  if (v != MSSM_OK) return v;
+  mssm_scan_desc c = *desc;
+  if (c.batch > 0 && c.split_seq == 0) {
+    // the library's own plan, with fewer chunks (down to an unsplit scan, which needs no workspace)
+    // where its workspace would not fit in the scratch; a forced split_seq is kept, and refused by
+    // the forward below if it does not fit
+    int K = 1, G = 1;
+    const int pr = plan_scan(c, &K, &G);
+    if (pr != MSSM_OK) return pr;
+    if (mssm::scan_workspace_bytes(c.batch, c.dim, c.dstate, K) > mssm::kScratchBytes) {
+      while (K > 1 && mssm::scan_workspace_bytes(c.batch, c.dim, c.dstate, K) > mssm::kScratchBytes) K /= 2;
+      c.split_seq = K;
+    }
+  }
+  return scan_fwd_impl(&c, x, delta, A, B, C, D, z, h0, out, final_state, nullptr, 0, true, stream);
 }
 
 // --------------------------------------------------------------------------

@@ -54,6 +54,11 @@ hipError_t scan_launch(const ScanArgs& a, hipStream_t stream);
 // lanes-per-channel values the kernels are built for
 bool scan_supported_G(int G, int64_t N);
 
+// Fixed per-device scratch of the entry point that allocates nothing: its size, and its
+// address on the device of `stream` (looked up once per device, then kept).
+constexpr size_t kScratchBytes = size_t{32} << 20;
+hipError_t scratch_address(hipStream_t stream, void** out);
+
 // ---------------------------------------------------------------------------
 // Mamba-2 scalar-A multi-head (SSD) form
 // ---------------------------------------------------------------------------

@@ -596,3 +596,28 @@ def test_state_update_conv_validation(case, expect):
     assert M.lib.mssm_selective_state_update_conv(ctypes.byref(d), a["width"], a["state"], a["cs"], a["xin"], a["w"],
                                                   a["bias"], a["delta"], a["A"], a["B"], a["C"], None, None,
                                                   a["out"], None) == expect
+
+
+def _noalloc_call(desc, x=BASE, delta=BASE + 100 * MB, A=BASE + 200 * MB, B=BASE + 300 * MB, C=BASE + 400 * MB,
+                  out=BASE + 500 * MB, final=None):
+    return M.lib.mssm_selective_scan_fwd_noalloc(ctypes.byref(desc) if desc is not None else None, x, delta, A,
+                                                 B, C, None, None, None, out, final, None)
+
+
+def test_noalloc_validation():
+    """The entry point without workspace rejects bad arguments on the host, before it would look up its
+    scratch: the same checks as the forward, and a forced split whose aggregates exceed the scratch."""
+    assert _noalloc_call(None) == M.MSSM_ERR_INVALID_ARG
+    assert _noalloc_call(small(dstate=0)) == M.MSSM_ERR_INVALID_ARG
+    assert _noalloc_call(small(), x=None) == M.MSSM_ERR_INVALID_ARG
+    assert _noalloc_call(small(), x=BASE + 1) == M.MSSM_ERR_MISALIGNED
+    assert _noalloc_call(small(), out=BASE + 2) == M.MSSM_ERR_INVALID_ARG       # out overlaps x
+    # 4096 chunks x 2048 channels x 17 floats x 2 segments is far beyond 32 MiB
+    big = M.scan_desc(1, 1 << 20, 2048, 16, M.MSSM_BF16, 4096, 1)
+    assert M.selective_scan_workspace_size(1, 1 << 20, 2048, 16, M.MSSM_BF16, 4096, 1) > M.SCRATCH_BYTES
+    GB = 1 << 30   # the 2^20 x 2048 bf16 tensors take 4 GiB each: fake addresses 8 GiB apart
+    assert _noalloc_call(big, x=BASE, delta=BASE + 8 * GB, A=BASE + 16 * GB, B=BASE + 17 * GB, C=BASE + 18 * GB,
+                         out=BASE + 24 * GB) == M.MSSM_ERR_WORKSPACE
+    d = small(batch=0)
+    assert M.lib.mssm_selective_scan_fwd_noalloc(ctypes.byref(d), None, None, BASE, None, None, None, None, None,
+                                                 None, None, None) == M.MSSM_OK

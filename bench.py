@@ -31,17 +31,21 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0                      # MI355X HBM3E
 # VALU issue rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (packed fp32 is not used)
-PEAK_VALU_TSLOT = 256 * 4 * 16 * 2.4e9 / 1e12
+PEAK_VALU_TSLOT = 256 * 4 * 32 * 2.4e9 / 1e12
+# VALU issue: each SIMD retires a full-rate fp32 instruction (mul, add, FMA) for 32 of a wave's 64 lanes per
+# cycle -- 256 CUs x 4 SIMDs x 32 lanes x 2.4 GHz = 78.6 T lane-slots/s, the published 157.3 TFLOP/s fp32 vector
+# rate with an FMA counted as 2.  Measured on MI355X: a wave64 mul or FMA issues every ~2.1 cycles; exp2 and rcp
+# (transcendental) every ~8.1 cycles, so each counts as 4 slots.  packed fp32 is not used.
 PEAK_BF16_MFMA_TFLOPS = 2500.0
-# algorithmic VALU issue slots: per state update mul + exp2 (half rate: 2 slots) + mul + FMA + FMA;
-# per (b, t, c): delta*x, D*x + y, and the silu gate (mul, exp2, add, rcp, 2 mul) = 10
-SLOTS_PER_UPDATE = 6.0
-SLOTS_PER_STEP_CHANNEL = 10.0
-# gradients, per state update: the forward update (5) and its readout term (2); the adjoint FMA and
-# decay (2); the dC, dB, dA, ddelta and dx terms with their sums (10).  Per (b, t, c): delta*x, the
-# gate and its derivative, and the ddelta / dx / dz finish (13).
-SLOTS_PER_UPDATE_BWD = 19.0
-SLOTS_PER_STEP_CHANNEL_BWD = 13.0
+# algorithmic VALU issue slots: per state update mul + exp2 (4) + mul + FMA + FMA = 8;
+# per (b, t, c): delta*x (1), D*x + y (1), and the silu gate: mul, exp2 (4), add, rcp (4), mul, mul = 12
+SLOTS_PER_UPDATE = 8.0
+SLOTS_PER_STEP_CHANNEL = 14.0
+# gradients, per state update: the forward update (mul, exp2, mul, FMA = 7) and its readout term (2); the adjoint
+# FMA and decay (2); the dC, dB, dA, ddelta and dx terms with their sums (10).  Per (b, t, c): delta*x, the gate
+# (with its exp2 and rcp) and its derivative, and the ddelta / dx / dz finish (17).
+SLOTS_PER_UPDATE_BWD = 21.0
+SLOTS_PER_STEP_CHANNEL_BWD = 17.0
 
 
 def log(*a):
@@ -475,8 +479,8 @@ def main():
     else:
         per_tc = SLOTS_PER_STEP_CHANNEL
         if getattr(cfg, "conv_width", 0):
-            # the fused convolution: one FMA per tap, then its SiLU (mul, exp2 (2), add, rcp (2), mul)
-            per_tc += cfg.conv_width + 7
+            # the fused convolution: one FMA per tap, then its SiLU (mul, exp2 (4), add, rcp (4), mul)
+            per_tc += cfg.conv_width + 11
         roof["alu"] = alu_obj(cfg.updates * SLOTS_PER_UPDATE + cfg.batch * cfg.seqlen * cfg.dim * per_tc)
     # the ceiling the call sits closest to
     fr = {"hbm": roof["frac"], "alu": roof.get("alu", {}).get("frac", 0.0),

@@ -26,6 +26,13 @@ leg may import this package.  The product library never uses it.
                  Pinned by: equality with ``ssd3_fwd`` at omega = 0, the
                  rotated-B/C real form (RoPE) as a brute-force sum, the complex
                  geometric closed form, and the previous-token inputs.
+``ssdm_fwd``  -- Mamba-3 MIMO: R inputs and R outputs per channel of a head on the
+                 head's one state (B and C widened by the rank), with the
+                 exponential-trapezoidal rule or, without lam, the Mamba-2 rule
+                 (mssm_oracle.c: oracle_ssdm_fwd).  Pinned by: equality with
+                 ``ssd3_fwd`` / ``ssd_fwd`` at R = 1, the superposition of R x R
+                 SISO runs (one per input rank and output rank), a brute-force
+                 unrolled sum, and resuming through the previous token's inputs.
 ``conv_silu``, ``conv_scan_fwd``
               -- the short causal convolution + SiLU in front of the scan, and
                  the scan on its output (mssm_oracle.c: oracle_conv_silu,
@@ -75,6 +82,8 @@ def load_library(path: Optional[str] = None):
     lib.oracle_ssd3_fwd.argtypes = [i64, i64, i64, i64, i64, i64, i32] + [p] * 9 + [p, p, i32]
     lib.oracle_ssdc_fwd.restype = i32
     lib.oracle_ssdc_fwd.argtypes = [i64, i64, i64, i64, i64, i64, i32] + [p] * 12 + [p, p, i32]
+    lib.oracle_ssdm_fwd.restype = i32
+    lib.oracle_ssdm_fwd.argtypes = [i64] * 7 + [i32] + [p] * 11 + [p, p, i32]
     lib.oracle_conv_silu.restype = i32
     lib.oracle_conv_silu.argtypes = [i64, i64, i64, i64, i32, p, p, p, p, p]
     lib.oracle_conv_scan_fwd.restype = i32
@@ -184,6 +193,36 @@ def ssd3_fwd(x, delta, lam, A, B, C, D=None, z=None, h0=None, nthreads: Optional
                                          nthreads or default_threads())
     if rc != 0:
         raise ValueError("oracle_ssd3_fwd rejected its arguments")
+    return out, fin
+
+
+def ssdm_fwd(x, delta, lam, A, B, C, D=None, z=None, h0=None, x_prev=None, B_prev=None,
+             nthreads: Optional[int] = None, lib=None):
+    """Mamba-3 MIMO: R inputs and R outputs per channel of a head on its one state,
+    S_t = a_t S_{t-1} + (1 - lam_t) d_t a_t U_{t-1} + lam_t d_t U_t with U_t = sum_r x[t,h,r,:] (x) B[t,g,r,:],
+    y[t,h,r,p] = C[t,g,r,:] . S_t[p,:] (+ D x) (* silu(z)).
+
+    x, z [Bsz, L, H, R, P]; delta, lam [Bsz, L, H] (lam None: lam = 1, the Mamba-2 rule); B, C
+    [Bsz, L, G, R, N]; x_prev [Bsz, H, R, P], B_prev [Bsz, G, R, N] (None: no previous token).
+    Returns (out [Bsz, L, H, R, P] fp64, final_state [Bsz, H, P, N] fp64)."""
+    x, delta, lam, B, C, z = _c(x), _c(delta), _c(lam), _c(B), _c(C), _c(z)
+    x_prev, B_prev = _c(x_prev), _c(B_prev)
+    io = _io_code(x)
+    for t in (delta, B, C) + tuple(v for v in (lam, z, x_prev, B_prev) if v is not None):
+        if _io_code(t) != io:
+            raise TypeError("x, delta, lam, B, C, z, x_prev, B_prev must share one dtype")
+    A, D, h0 = _c(A, np.float32), _c(D, np.float32), _c(h0, np.float32)
+    bsz, L, H, R, P = x.shape
+    G, N = B.shape[2], B.shape[4]
+    if B.shape[3] != R:
+        raise ValueError("B must be [Bsz, L, G, R, N] with x's R")
+    out = np.empty((bsz, L, H, R, P), dtype=np.float64)
+    fin = np.empty((bsz, H, P, N), dtype=np.float64)
+    rc = (lib or _get()).oracle_ssdm_fwd(bsz, L, H, P, N, G, R, io, _ptr(x), _ptr(delta), _ptr(lam), _ptr(A),
+                                         _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(x_prev),
+                                         _ptr(B_prev), _ptr(out), _ptr(fin), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_ssdm_fwd rejected its arguments")
     return out, fin
 
 

@@ -387,6 +387,125 @@ int oracle_ssd3_fwd(int64_t Bsz, int64_t L, int64_t H, int64_t P, int64_t N, int
 }
 
 /* ------------------------------------------------------------------------- */
+/* Mamba-3 MIMO: several inputs and outputs per channel on one state (own loop) */
+/* ------------------------------------------------------------------------- */
+/*
+ * "Mamba-3" (blog), "El modelo Mamba-3" item 3: multi-input multi-output SSMs
+ * model several SSMs in parallel against the single-input single-output
+ * ones; "Arquitectura": the MIMO projections widen B and C; "Tareas de
+ * recuperacion": MIMO does not grow the state.  The pages give no formula;
+ * plain reading (the control-theory sense of MIMO on the multi-head state):
+ * each channel p of head h takes R inputs x[t,h,r,p] and gives R outputs; the
+ * R input terms drive the one state S[p,n] of the head through one transition
+ * (B widened to B[t,g,r,n]), and output r reads that state through its own
+ * C[t,g,r,n].  With U_t[p,n] = sum_r B[t,g,r,n] x[t,h,r,p] and the
+ * exponential-trapezoidal rule of oracle_ssd3_fwd:
+ *   S_t = a_t S_{t-1} + (1 - lam_t) d_t a_t U_{t-1} + lam_t d_t U_t
+ *   y[t,h,r,p] = sum_n C[t,g,r,n] S_t[p,n] + D[h] x[t,h,r,p],  out = y silu(z[t,h,r,p])
+ * lam NULL is lam = 1 everywhere (the Mamba-2 rule d_t U_t).  R = 1 is
+ * oracle_ssd3_fwd (oracle_ssd_fwd without lam).  The token before step 0 is
+ * x_prev / B_prev (nullable: U_{-1} = 0).
+ */
+typedef struct {
+    int64_t Bsz, L, H, P, N, G, R;
+    int io;
+    const void *x, *delta, *lam, *Bm, *Cm, *z, *x_prev, *B_prev;
+    const float *A, *Dv, *h0;
+    double *out, *final_state;
+    int64_t pair_begin, pair_end;   /* pairs = b * H + h */
+} ssdm_job;
+
+static void ssdm_pair(const ssdm_job* j, int64_t b, int64_t hd, double* S, double* U_prev, double* U) {
+    const int64_t H = j->H, P = j->P, N = j->N, L = j->L, G = j->G, R = j->R;
+    const int64_t g = hd / (H / G);
+    for (int64_t p = 0; p < P; ++p)
+        for (int64_t n = 0; n < N; ++n) {
+            S[p * N + n] = j->h0 ? (double)j->h0[((b * H + hd) * P + p) * N + n] : 0.0;
+            double u = 0.0;                                           /* U_{-1}: the token before step 0 */
+            if (j->x_prev && j->B_prev)
+                for (int64_t r = 0; r < R; ++r)
+                    u += load_io(j->B_prev, j->io, ((b * G + g) * R + r) * N + n) *
+                         load_io(j->x_prev, j->io, ((b * H + hd) * R + r) * P + p);
+            U_prev[p * N + n] = u;
+        }
+    for (int64_t t = 0; t < L; ++t) {
+        const double d = load_io(j->delta, j->io, (b * L + t) * H + hd);
+        const double lam = j->lam ? load_io(j->lam, j->io, (b * L + t) * H + hd) : 1.0;
+        const double a = exp(d * (double)j->A[hd]);
+        const double w_left = (1.0 - lam) * d * a, w_right = lam * d;
+        const int64_t bc = ((b * L + t) * G + g) * R;                 /* row of rank 0 in B, C */
+        const int64_t xr = ((b * L + t) * H + hd) * R;                /* row of rank 0 in x, z, out */
+        for (int64_t p = 0; p < P; ++p)
+            for (int64_t n = 0; n < N; ++n) {
+                double u = 0.0;                                       /* sum over the R inputs */
+                for (int64_t r = 0; r < R; ++r)
+                    u += load_io(j->Bm, j->io, (bc + r) * N + n) * load_io(j->x, j->io, (xr + r) * P + p);
+                U[p * N + n] = u;
+                S[p * N + n] = a * S[p * N + n] + w_left * U_prev[p * N + n] + w_right * u;
+            }
+        for (int64_t r = 0; r < R; ++r)                               /* each output reads the one state */
+            for (int64_t p = 0; p < P; ++p) {
+                const int64_t i = (xr + r) * P + p;
+                double acc = 0.0;
+                for (int64_t n = 0; n < N; ++n) acc += load_io(j->Cm, j->io, (bc + r) * N + n) * S[p * N + n];
+                double y = acc + (j->Dv ? (double)j->Dv[hd] * load_io(j->x, j->io, i) : 0.0);
+                if (j->z) y *= silu(load_io(j->z, j->io, i));
+                j->out[i] = y;
+            }
+        memcpy(U_prev, U, sizeof(double) * (size_t)(P * N));
+    }
+    if (j->final_state)
+        for (int64_t p = 0; p < P; ++p)
+            for (int64_t n = 0; n < N; ++n)
+                j->final_state[((b * H + hd) * P + p) * N + n] = S[p * N + n];
+}
+
+static void* ssdm_worker(void* arg) {
+    const ssdm_job* j = (const ssdm_job*)arg;
+    const int64_t n = j->P * j->N;
+    double* S = (double*)malloc(sizeof(double) * (size_t)(3 * n));
+    for (int64_t k = j->pair_begin; k < j->pair_end; ++k) ssdm_pair(j, k / j->H, k % j->H, S, S + n, S + 2 * n);
+    free(S);
+    return NULL;
+}
+
+/*
+ * out [Bsz, L, H, R, P] fp64; final_state [Bsz, H, P, N] fp64 (nullable).
+ * x, z [Bsz, L, H, R, P]; delta, lam [Bsz, L, H]; Bm, Cm [Bsz, L, G, R, N];
+ * x_prev [Bsz, H, R, P], B_prev [Bsz, G, R, N] in io dtype; A [H], Dv [H],
+ * h0 [Bsz, H, P, N] fp32.  lam, Dv, z, h0, x_prev, B_prev nullable.
+ */
+int oracle_ssdm_fwd(int64_t Bsz, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_t R, int io,
+                    const void* x, const void* delta, const void* lam, const float* A, const void* Bm,
+                    const void* Cm, const float* Dv, const void* z, const float* h0, const void* x_prev,
+                    const void* B_prev, double* out, double* final_state, int nthreads) {
+    if (Bsz < 0 || L < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0 || R <= 0 || H % G != 0) return -1;
+    if (io != IO_F32 && io != IO_BF16) return -1;
+    const int64_t pairs = Bsz * H;
+    if (pairs == 0) return 0;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > pairs) nthreads = (int)pairs;
+    ssdm_job* jobs = (ssdm_job*)calloc((size_t)nthreads, sizeof(ssdm_job));
+    pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+    for (int k = 0; k < nthreads; ++k) {
+        ssdm_job* j = &jobs[k];
+        j->Bsz = Bsz; j->L = L; j->H = H; j->P = P; j->N = N; j->G = G; j->R = R; j->io = io;
+        j->x = x; j->delta = delta; j->lam = lam; j->Bm = Bm; j->Cm = Cm; j->z = z;
+        j->x_prev = x_prev; j->B_prev = B_prev;
+        j->A = A; j->Dv = Dv; j->h0 = h0;
+        j->out = out; j->final_state = final_state;
+        j->pair_begin = pairs * k / nthreads;
+        j->pair_end = pairs * (k + 1) / nthreads;
+    }
+    for (int k = 1; k < nthreads; ++k) pthread_create(&th[k], NULL, ssdm_worker, &jobs[k]);
+    ssdm_worker(&jobs[0]);
+    for (int k = 1; k < nthreads; ++k) pthread_join(th[k], NULL);
+    free(jobs);
+    free(th);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
 /* Mamba-3 SISO with a complex-valued state (own loop, complex arithmetic)   */
 /* ------------------------------------------------------------------------- */
 /*

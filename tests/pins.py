@@ -736,8 +736,131 @@ def pin_conv_scan_composition(lib, seed=34):
 SCAN_PINS = [pin_lti_convolution, pin_delta_zero, pin_geometric, pin_bruteforce, pin_chaining, pin_reset,
              pin_linearity_causality, pin_gate_skip, pin_bf16_codec]
 SSD_PINS = [pin_ssd_equals_broadcast_scan, pin_ssd_geometric, pin_ssd_bruteforce, pin_ssd_chaining]
+# ---------------------------------------------------------------------------
+# Mamba-3 MIMO: R inputs and R outputs per channel on the head's one state
+# ---------------------------------------------------------------------------
+def _ssdm_case(rng, bsz=2, L=23, H=4, P=3, N=5, G=2, R=3, with_dz=True, with_h0=True, with_lam=True):
+    x = rng.standard_normal((bsz, L, H, R, P)).astype(np.float32)
+    delta = rng.uniform(0.01, 0.6, size=(bsz, L, H)).astype(np.float32)
+    lam = rng.uniform(0.0, 1.0, (bsz, L, H)).astype(np.float32) if with_lam else None
+    A = -(rng.uniform(0.3, 3.0, size=H)).astype(np.float32)
+    B = rng.standard_normal((bsz, L, G, R, N)).astype(np.float32)
+    C = rng.standard_normal((bsz, L, G, R, N)).astype(np.float32)
+    D = rng.standard_normal(H).astype(np.float32) if with_dz else None
+    z = rng.standard_normal((bsz, L, H, R, P)).astype(np.float32) if with_dz else None
+    h0 = rng.standard_normal((bsz, H, P, N)).astype(np.float32) if with_h0 else None
+    return x, delta, lam, A, B, C, D, z, h0
+
+
+def pin_ssdm_rank_one_is_siso(lib, seed=51):
+    """One input and one output per channel is the SISO recurrence: the exponential-trapezoidal rule with
+    lam, the Mamba-2 rule without it."""
+    rng = _rng(seed)
+    x, delta, lam, A, B, C, D, z, h0 = _ssdm_case(rng, R=1)
+    sq = lambda a: None if a is None else np.ascontiguousarray(a[:, :, :, 0])
+    out, fin = oracle.ssdm_fwd(x, delta, lam, A, B, C, D, z, h0, lib=lib)
+    ref, ref_fin = oracle.ssd3_fwd(sq(x), delta, lam, A, sq(B), sq(C), D, sq(z), h0, lib=lib)
+    _close(out[:, :, :, 0], ref, 1e-13, "MIMO R = 1 output vs the SISO rule")
+    _close(fin, ref_fin, 1e-13, "MIMO R = 1 final state vs the SISO rule")
+    out, fin = oracle.ssdm_fwd(x, delta, None, A, B, C, D, z, h0, lib=lib)
+    ref, ref_fin = oracle.ssd_fwd(sq(x), delta, A, sq(B), sq(C), D, sq(z), h0, lib=lib)
+    _close(out[:, :, :, 0], ref, 1e-13, "MIMO R = 1 without lam vs the Mamba-2 form")
+    _close(fin, ref_fin, 1e-13, "MIMO R = 1 without lam final state vs the Mamba-2 form")
+
+
+def pin_ssdm_superposition(lib, seed=52):
+    """The state is linear in the inputs, so it is the sum of R SISO states, one driven by each input rank
+    (x_r', B_r'), and output r reads that sum through C_r: y_r = sum_r' SISO(x_r', B_r', C_r) + D x_r.
+    R x R runs of the (separately pinned) SISO oracle, h0 carried by one of them."""
+    rng = _rng(seed)
+    x, delta, lam, A, B, C, D, z, h0 = _ssdm_case(rng, R=3, with_dz=False)
+    D = rng.standard_normal(x.shape[2]).astype(np.float32)
+    out, fin = oracle.ssdm_fwd(x, delta, lam, A, B, C, D, None, h0, lib=lib)
+    R = x.shape[3]
+    rk = lambda a, r: np.ascontiguousarray(a[:, :, :, r])
+    want = np.zeros_like(out)
+    want_fin = np.zeros_like(fin)
+    for r_in in range(R):
+        hh = h0 if r_in == 0 else None
+        for r_out in range(R):
+            o, f = oracle.ssd3_fwd(rk(x, r_in), delta, lam, A, rk(B, r_in), rk(C, r_out), None, None, hh, lib=lib)
+            want[:, :, :, r_out] += o
+        want_fin += f
+    want += np.float64(1.0) * D.astype(np.float64)[None, None, :, None, None] * x.astype(np.float64)
+    _close(out, want, 1e-12, "MIMO output vs the sum of SISO runs")
+    _close(fin, want_fin, 1e-12, "MIMO final state vs the sum of SISO runs")
+
+
+def pin_ssdm_bruteforce(lib, seed=53):
+    """Unrolled: with U_s = sum_r x[s,r] (x) B[s,r] and the SISO weights
+    w(t, s) = lam_s d_s + [s < t] (1 - lam_{s+1}) d_{s+1},
+    y[t,r,p] = (C[t,r] . (exp(sum_{u<=t} d_u A) h0[p] + sum_{s<=t} exp(sum_{u=s+1..t} d_u A) w(t,s) U_s[p]) + D x) silu(z)."""
+    rng = _rng(seed)
+    x, delta, lam, A, B, C, D, z, h0 = _ssdm_case(rng, bsz=1, L=9, H=2, P=2, N=3, G=1, R=2)
+    out, fin = oracle.ssdm_fwd(x, delta, lam, A, B, C, D, z, h0, nthreads=1, lib=lib)
+    x64, d64, l64, B64, C64, z64 = (v.astype(np.float64) for v in (x, delta, lam, B, C, z))
+    bsz, L, H, R, P = x.shape
+    want = np.zeros_like(out)
+    want_fin = np.zeros_like(fin)
+    for b in range(bsz):
+        for h in range(H):
+            ell = d64[b, :, h] * np.float64(A[h])
+            U = np.einsum("srp,srn->spn", x64[b, :, h], B64[b, :, 0])           # [L, P, N]
+            for t in range(L + 1):
+                st = np.exp(np.sum(ell[:t])) * h0[b, h].astype(np.float64)      # state after step t-1
+                for s in range(t):
+                    w = l64[b, s, h] * d64[b, s, h]
+                    if s < t - 1:
+                        w += (1.0 - l64[b, s + 1, h]) * d64[b, s + 1, h]
+                    st = st + np.exp(np.sum(ell[s + 1:t])) * w * U[s]
+                if t == L:
+                    want_fin[b, h] = st
+                    break
+                # the output at step t reads the state after step t
+                st_t = np.exp(np.sum(ell[:t + 1])) * h0[b, h].astype(np.float64)
+                for s in range(t + 1):
+                    w = l64[b, s, h] * d64[b, s, h]
+                    if s < t:
+                        w += (1.0 - l64[b, s + 1, h]) * d64[b, s + 1, h]
+                    st_t = st_t + np.exp(np.sum(ell[s + 1:t + 1])) * w * U[s]
+                for r in range(R):
+                    for p in range(P):
+                        y = np.dot(C64[b, t, 0, r], st_t[p]) + np.float64(D[h]) * x64[b, t, h, r, p]
+                        want[b, t, h, r, p] = y * _silu(z64[b, t, h, r, p])
+    _close(out, want, 1e-11, "MIMO brute-force unrolled sum")
+    _close(fin, want_fin, 1e-11, "MIMO brute-force final state")
+
+
+def pin_ssdm_resume(lib, seed=54):
+    """Splitting at L1 and resuming from the first part's final state, with the token before the second part
+    given as the previous token (x_prev, B_prev), reproduces the whole run; and a previous token is the same
+    as adding its left-end term (1 - lam_0) d_0 sum_r x_prev[r] (x) B_prev[r] to h0."""
+    rng = _rng(seed)
+    x, delta, lam, A, B, C, D, z, h0 = _ssdm_case(rng, L=31)
+    L1 = 12
+    full, fin = oracle.ssdm_fwd(x, delta, lam, A, B, C, D, z, h0, lib=lib)
+    _, mid = oracle.ssdm_fwd(x[:, :L1], delta[:, :L1], lam[:, :L1], A, B[:, :L1], C[:, :L1], D, z[:, :L1], h0,
+                             lib=lib)
+    tail, fin2 = oracle.ssdm_fwd(x[:, L1:], delta[:, L1:], lam[:, L1:], A, B[:, L1:], C[:, L1:], D, z[:, L1:],
+                                 mid.astype(np.float32), x[:, L1 - 1], B[:, L1 - 1], lib=lib)
+    _close(tail, full[:, L1:], 1e-6, "MIMO resumed output")
+    _close(fin2, fin, 1e-6, "MIMO resumed final state")
+    xp = rng.standard_normal(x[:, 0].shape).astype(np.float32)                # [b, H, R, P]
+    bp = rng.standard_normal(B[:, 0].shape).astype(np.float32)                # [b, G, R, N]
+    o1, f1 = oracle.ssdm_fwd(x, delta, lam, A, B, C, D, z, h0, xp, bp, lib=lib)
+    H, G = x.shape[2], B.shape[2]
+    bph = bp.astype(np.float64)[:, np.arange(H) // (H // G)]                   # [b, H, R, N]
+    left = ((1.0 - lam[:, 0].astype(np.float64)) * delta[:, 0].astype(np.float64))[:, :, None, None] * \
+        np.einsum("bhrp,bhrn->bhpn", xp.astype(np.float64), bph)
+    h0p = (h0.astype(np.float64) + left).astype(np.float32)                  # the fp32 h0 the oracle takes
+    o2, f2 = oracle.ssdm_fwd(x, delta, lam, A, B, C, D, z, h0p, lib=lib)
+    _close(o1, o2, 1e-6, "MIMO previous token vs its left-end term added to h0 (output)")
+    _close(f1, f2, 1e-6, "MIMO previous token vs its left-end term added to h0 (final state)")
+
+
 SSD3_PINS = [pin_ssd3_lam_one_is_ssd, pin_ssd3_trapezoid_order, pin_ssd3_bruteforce, pin_ssd3_resume]
 SSDC_PINS = [pin_ssdc_omega_zero_is_ssd3, pin_ssdc_rope_bruteforce, pin_ssdc_geometric, pin_ssdc_previous_token]
+SSDM_PINS = [pin_ssdm_rank_one_is_siso, pin_ssdm_superposition, pin_ssdm_bruteforce, pin_ssdm_resume]
 BWD_PINS = [pin_scan_bwd_finite_differences, pin_scan_bwd_linear_in_upstream]
 CONV_PINS = [pin_conv_numpy, pin_conv_impulse, pin_conv_chaining, pin_conv_scan_composition]
-ALL_PINS = SCAN_PINS + SSD_PINS + SSD3_PINS + SSDC_PINS + BWD_PINS + CONV_PINS
+ALL_PINS = SCAN_PINS + SSD_PINS + SSD3_PINS + SSDC_PINS + SSDM_PINS + BWD_PINS + CONV_PINS

@@ -59,6 +59,21 @@ MUTANTS = {
     "ssdc_left_end_not_rotated": ("(1.0 - lam) * d * a * bx_prev[p * K + k]",
                                   "(1.0 - lam) * d * cabs(a) * bx_prev[p * K + k]"),
     "ssdc_previous_token_ignored": ("if (j->x_prev && j->B_prev) {", "if (0) {"),
+    # Mamba-3 MIMO
+    "ssdm_readout_rank0_C": ("acc += load_io(j->Cm, j->io, (bc + r) * N + n) * S[p * N + n];",
+                             "acc += load_io(j->Cm, j->io, bc * N + n) * S[p * N + n];"),
+    "ssdm_first_input_only": ("for (int64_t r = 0; r < R; ++r)\n                    u += load_io(j->Bm",
+                              "for (int64_t r = 0; r < 1; ++r)\n                    u += load_io(j->Bm"),
+    "ssdm_B_rank_reversed": ("u += load_io(j->Bm, j->io, (bc + r) * N + n) * load_io(j->x, j->io, (xr + r) * P + p);",
+                             "u += load_io(j->Bm, j->io, (bc + R - 1 - r) * N + n) * load_io(j->x, j->io, (xr + r) * P + p);"),
+    "ssdm_default_lam_half": ("? load_io(j->lam, j->io, (b * L + t) * H + hd) : 1.0;",
+                              "? load_io(j->lam, j->io, (b * L + t) * H + hd) : 0.5;"),
+    "ssdm_previous_token_rank0": ("for (int64_t r = 0; r < R; ++r)\n                    u += load_io(j->B_prev",
+                                  "for (int64_t r = 0; r < 1; ++r)\n                    u += load_io(j->B_prev"),
+    "ssdm_skip_rank0_x": ("double y = acc + (j->Dv ? (double)j->Dv[hd] * load_io(j->x, j->io, i) : 0.0);",
+                          "double y = acc + (j->Dv ? (double)j->Dv[hd] * load_io(j->x, j->io, xr * P + p) : 0.0);"),
+    "ssdm_left_end_current": ("S[p * N + n] = a * S[p * N + n] + w_left * U_prev[p * N + n] + w_right * u;",
+                              "S[p * N + n] = a * S[p * N + n] + w_left * u + w_right * u;"),
     # gradients
     "bwd_no_adjoint_decay": ("lam[n] *= a;", ";"),
     "bwd_dsilu_is_sigmoid": ("return s * (1.0 + v * (1.0 - s));", "return s;"),

@@ -42,3 +42,18 @@ def test_exp_log_A_is_fp32_rounded():
     A = W.exp_log_A(2, 16)
     assert A.dtype == np.float32 and A.shape == (2, 16)
     assert A[0, 0] == -1.0 and A[0, 4] != -5.0   # -exp(log 5) in fp32 is not exactly -5
+
+
+def test_mimo_inputs():
+    cfg = W.ssd_config(2, 5, 3, 4, 6, 1, cfg_id=77, rank=3)
+    s = W.make_ssd_inputs(cfg, with_D=True, with_z=True, with_h0=True)
+    assert s.x.shape == (2, 5, 3, 3, 4) and s.z.shape == (2, 5, 3, 3, 4)
+    assert s.B.shape == (2, 5, 1, 3, 6) and s.C.shape == (2, 5, 1, 3, 6)
+    xp, bp = W.make_ssd_prev(cfg)
+    assert xp.shape == (2, 3, 3, 4) and bp.shape == (2, 1, 3, 6)
+    # rank 1 keeps the single-input shapes and values
+    one = W.make_ssd_inputs(W.ssd_config(2, 5, 3, 4, 6, 1, cfg_id=77))
+    assert one.x.shape == (2, 5, 3, 4)
+    assert np.array_equal(one.x.reshape(-1), s.x.reshape(-1)[:one.x.size])
+    m = W.CONFIGS[14]
+    assert m.rank == 4 and m.algorithmic_bytes() > 4 * (W.CONFIGS[4].algorithmic_bytes() - 8 * 32 * 64 * 128 * 4) * 0.9

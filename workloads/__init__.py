@@ -13,6 +13,9 @@ Recipe (the workloads the pages describe, made concrete):
     section 4.2; page "Mamba-3", introduction: the transition is a scalar
     times the identity): per-(token, head) delta, scalar A per head, B/C per
     (token, group).
+  * Mamba-3 MIMO (page "Mamba-3", "El modelo Mamba-3" item 3): R inputs and
+    outputs per channel, x and z ~ N(0, 1) per rank, B and C ~ N(0, 1) per
+    (token, group, rank).
   * Mamba-3 SISO rule (page "Mamba-3", "El modelo Mamba-3"): the weight lam
     per (token, head), sigmoid(N(0, 1)), as a gate computed from the token
     would give; for its decode step, the previous token's x and B ~ N(0, 1);
@@ -120,18 +123,21 @@ class SSDConfig:
     decode: bool = False    # token-by-token update of a stored state (read and written in place)
     trapezoidal: bool = False   # Mamba-3 exponential-trapezoidal input rule (one more [B, L, H] input, lam)
     complex_state: bool = False  # Mamba-3 complex-valued state: rotation rates omega [H, N/2] fp32
+    rank: int = 1           # Mamba-3 MIMO: R inputs and outputs per channel, x/z/out [B, L, H, R, P], B/C [B, L, G, R, N]
 
     @property
     def updates(self) -> int:
+        """State-element updates (each absorbs the R inputs of its step under MIMO)."""
         return self.batch * self.seqlen * self.nheads * self.headdim * self.dstate
 
     def algorithmic_bytes(self) -> int:
         e = 2 if self.io == BF16 else 4
-        blhp = self.batch * self.seqlen * self.nheads * self.headdim
+        R = self.rank
+        blhp = self.batch * self.seqlen * self.nheads * self.headdim * R
         n = blhp * e                                            # x
         n += self.batch * self.seqlen * self.nheads * e         # delta
         n += self.batch * self.seqlen * self.nheads * e if self.trapezoidal else 0   # lam
-        n += 2 * self.batch * self.seqlen * self.ngroups * self.dstate * e  # B, C
+        n += 2 * self.batch * self.seqlen * self.ngroups * R * self.dstate * e  # B, C
         n += self.nheads * 4                                    # A
         n += self.nheads * 4 if self.has_D else 0
         n += blhp * e if self.has_z else 0
@@ -139,7 +145,7 @@ class SSDConfig:
         n += self.batch * self.nheads * self.headdim * self.dstate * 4 if self.return_final else 0
         n += self.batch * self.nheads * self.headdim * self.dstate * 4 if self.decode else 0
         if self.decode and self.trapezoidal:   # the previous token's x and B
-            n += (self.batch * self.nheads * self.headdim + self.batch * self.ngroups * self.dstate) * e
+            n += (self.batch * self.nheads * self.headdim + self.batch * self.ngroups * self.dstate) * R * e
         n += self.nheads * (self.dstate // 2) * 4 if self.complex_state else 0   # omega
         return n
 
@@ -175,6 +181,11 @@ CONFIGS = {
     # the same decode step with the complex-valued state (each state pair rotated by delta * omega)
     13: SSDConfig("mamba3_siso_complex_decode_bf16", 13, 64, 1, 32, 64, 128, 1, 64, BF16, True, True, True,
                   decode=True, trapezoidal=True, complex_state=True),
+    # Mamba-3 MIMO at config 4's shape: 4 inputs and 4 outputs per channel on each head's one state
+    14: SSDConfig("mamba3_mimo_bf16", 14, 8, 4096, 32, 64, 128, 1, 256, trapezoidal=True, rank=4),
+    # its decode step at config 7's serving shape (the previous token's 4 inputs and B rows too)
+    15: SSDConfig("mamba3_mimo_decode_bf16", 15, 64, 1, 32, 64, 128, 1, 64, BF16, True, True, True, decode=True,
+                  trapezoidal=True, rank=4),
 }
 
 
@@ -348,18 +359,23 @@ class SSDInputs:
 
 def make_ssd_inputs(cfg: SSDConfig, seed_base: int = ROOT_SEED, with_D: Optional[bool] = None,
                     with_z: Optional[bool] = None, with_h0: bool = False) -> SSDInputs:
+    """x, z [B, L, H, P] and B, C [B, L, G, N]; with cfg.rank R > 1 (MIMO) x, z [B, L, H, R, P] and
+    B, C [B, L, G, R, N]."""
     b, l, h, p, n, g = cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups
+    R = cfg.rank
+    xs = (b, l, h, p) if R == 1 else (b, l, h, R, p)
+    bs = (b, l, g, n) if R == 1 else (b, l, g, R, n)
     cid = cfg.cfg_id
     with_D = cfg.has_D if with_D is None else with_D
     with_z = cfg.has_z if with_z is None else with_z
-    x = normal(cid, T_X, b * l * h * p, cfg.io, seed_base).reshape(b, l, h, p)
+    x = normal(cid, T_X, b * l * h * R * p, cfg.io, seed_base).reshape(xs)
     delta = softplus_delta(cid, b * l * h, cfg.io, seed_base).reshape(b, l, h)
-    Bm = normal(cid, T_B, b * l * g * n, cfg.io, seed_base).reshape(b, l, g, n)
-    Cm = normal(cid, T_C, b * l * g * n, cfg.io, seed_base).reshape(b, l, g, n)
+    Bm = normal(cid, T_B, b * l * g * R * n, cfg.io, seed_base).reshape(bs)
+    Cm = normal(cid, T_C, b * l * g * R * n, cfg.io, seed_base).reshape(bs)
     u = uniform_f32(cid, T_A, h, float(np.log(np.float32(1.0))), float(np.log(np.float32(16.0))), seed_base)
     A = (-np.exp(u)).astype(np.float32)
     D = normal_f32(cid, T_D, h, seed_base) if with_D else None
-    z = normal(cid, T_Z, b * l * h * p, cfg.io, seed_base).reshape(b, l, h, p) if with_z else None
+    z = normal(cid, T_Z, b * l * h * R * p, cfg.io, seed_base).reshape(xs) if with_z else None
     h0 = normal_f32(cid, T_H0, b * h * p * n, seed_base).reshape(b, h, p, n) if with_h0 else None
     return SSDInputs(x, delta, A, Bm, Cm, D, z, h0, cfg.io)
 
@@ -379,10 +395,15 @@ def make_ssd_lam(cfg: SSDConfig, seed_base: int = ROOT_SEED) -> np.ndarray:
 
 
 def make_ssd_prev(cfg: SSDConfig, seed_base: int = ROOT_SEED):
-    """The token before a decode step's first: x_prev [B, H, P] and B_prev [B, G, N], N(0, 1) in io dtype."""
-    xp = normal(cfg.cfg_id, T_XPREV, cfg.batch * cfg.nheads * cfg.headdim, cfg.io, seed_base)
-    bp = normal(cfg.cfg_id, T_BPREV, cfg.batch * cfg.ngroups * cfg.dstate, cfg.io, seed_base)
-    return xp.reshape(cfg.batch, cfg.nheads, cfg.headdim), bp.reshape(cfg.batch, cfg.ngroups, cfg.dstate)
+    """The token before a decode step's first: x_prev [B, H, P] and B_prev [B, G, N] ([B, H, R, P] and
+    [B, G, R, N] under MIMO), N(0, 1) in io dtype."""
+    R = cfg.rank
+    xp = normal(cfg.cfg_id, T_XPREV, cfg.batch * cfg.nheads * R * cfg.headdim, cfg.io, seed_base)
+    bp = normal(cfg.cfg_id, T_BPREV, cfg.batch * cfg.ngroups * R * cfg.dstate, cfg.io, seed_base)
+    if R == 1:
+        return xp.reshape(cfg.batch, cfg.nheads, cfg.headdim), bp.reshape(cfg.batch, cfg.ngroups, cfg.dstate)
+    return (xp.reshape(cfg.batch, cfg.nheads, R, cfg.headdim),
+            bp.reshape(cfg.batch, cfg.ngroups, R, cfg.dstate))
 
 
 def make_ssd_omega(cfg: SSDConfig, seed_base: int = ROOT_SEED) -> np.ndarray:
@@ -401,6 +422,6 @@ def scan_config(batch: int, seqlen: int, dim: int, dstate: int, io: str = F32, a
 
 def ssd_config(batch: int, seqlen: int, nheads: int, headdim: int, dstate: int, ngroups: int = 1,
                chunk: int = 64, io: str = BF16, has_D: bool = False, has_z: bool = False,
-               cfg_id: int = 200) -> SSDConfig:
-    return SSDConfig(f"ssd_b{batch}_l{seqlen}_h{nheads}_p{headdim}_n{dstate}_g{ngroups}", cfg_id, batch, seqlen,
-                     nheads, headdim, dstate, ngroups, chunk, io, has_D, has_z, True)
+               cfg_id: int = 200, rank: int = 1) -> SSDConfig:
+    return SSDConfig(f"ssd_b{batch}_l{seqlen}_h{nheads}_p{headdim}_n{dstate}_g{ngroups}_r{rank}", cfg_id, batch,
+                     seqlen, nheads, headdim, dstate, ngroups, chunk, io, has_D, has_z, True, rank=rank)

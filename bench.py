@@ -198,7 +198,16 @@ def cpu_baseline_ssd(inp, cfg, lam=None, omega=None):
     threads = oracle.default_threads()
     per_head = cfg.batch * cfg.seqlen * cfg.headdim * cfg.dstate
     nh = int(min(cfg.nheads, max(1, 4e9 // per_head)))
-    if lam is None:
+    if cfg.rank > 1:
+        # MIMO: the first nh heads (one group shared by all heads), every rank, through the MIMO oracle
+        assert cfg.ngroups == 1
+        hs = lambda a: None if a is None else np.ascontiguousarray(a[:, :, :nh])
+        x, delta, z, lm = hs(inp.x), hs(inp.delta), hs(inp.z), hs(lam)
+        A = np.ascontiguousarray(inp.A[:nh])
+        D = None if inp.D is None else np.ascontiguousarray(inp.D[:nh])
+        h0 = None if inp.h0 is None else np.ascontiguousarray(inp.h0[:, :nh])
+        run = lambda: oracle.ssdm_fwd(x, delta, lm, A, inp.B, inp.C, D, z, h0, nthreads=threads)
+    elif lam is None:
         run = lambda: oracle.ssd_fwd(inp.x, inp.delta, inp.A, inp.B, inp.C, inp.D, inp.z, inp.h0, hd0=0, hd1=nh,
                                      nthreads=threads)
     else:
@@ -227,10 +236,10 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=5,
-                    help="workload id (1-13; 6, 7: decode steps; 8: gradients; 9: convolution fused in front; "
+                    help="workload id (1-15; 6, 7: decode steps; 8: gradients; 9: convolution fused in front; "
                          "10: training step; 11, 12: Mamba-3 SISO recurrence and its decode step; 13: that decode "
-                         "step with the complex-valued state); the default, 5, is the largest one-GPU "
-                         "configuration, the one the metric is quoted on")
+                         "step with the complex-valued state; 14, 15: Mamba-3 MIMO and its decode step); the "
+                         "default, 5, is the largest one-GPU configuration, the one the metric is quoted on")
     ap.add_argument("--sets", type=int, default=0, help="resident input copies to rotate over (0: auto)")
     ap.add_argument("--chunk", type=int, default=0, help="SSD time-chunk length (0: the workload's)")
     ap.add_argument("--split-seq", type=int, default=0, help="force the sequence-chunk count (0: the planner's)")
@@ -336,6 +345,7 @@ def main():
         outs = [torch.empty_like(i["x"]) for i in ins]
         upd = M.ssd_state_update if is_ssd else M.selective_state_update
         trap = is_ssd and cfg.trapezoidal
+        mimo = is_ssd and cfg.rank > 1
         lams = [W.make_ssd_lam(cfg, seed_base=W.ROOT_SEED + 1000 * i) if trap else None for i in range(sets)]
         if trap:   # the Mamba-3 rule also reads the previous token's x and B
             for i, a in enumerate(ins):
@@ -346,7 +356,10 @@ def main():
 
         def step(i):
             a, o = ins[i % sets], outs[i % sets]
-            if trap and cfg.complex_state:
+            if mimo:
+                M.ssd_mimo_state_update(a["state"], a["x"], a["delta"], a.get("lam"), a["A"], a["B"], a["C"], a["D"],
+                                        a["z"], x_prev=a.get("x_prev"), B_prev=a.get("B_prev"), out=o)
+            elif trap and cfg.complex_state:
                 M.mamba3_siso_update(a["state"], a["x"], a["delta"], a["lam"], a["A"], a["omega"], a["B"], a["C"],
                                      a["D"], a["z"], x_prev=a["x_prev"], B_prev=a["B_prev"], out=o)
             elif trap:
@@ -370,7 +383,10 @@ def main():
 
         def step(i):
             a, (o, f) = ins[i % sets], outs[i % sets]
-            if cfg.trapezoidal:
+            if cfg.rank > 1:
+                M.ssd_mimo_fwd(a["x"], a["delta"], a["lam"], a["A"], a["B"], a["C"], a["D"], a["z"], None, chunk=chunk,
+                               out=o, final_state=f, return_final_state=True, workspace=ws if ws_n else None)
+            elif cfg.trapezoidal:
                 M.ssd_trapezoidal_fwd(a["x"], a["delta"], a["lam"], a["A"], a["B"], a["C"], a["D"], a["z"], None,
                                       chunk=chunk, out=o, final_state=f, return_final_state=True,
                                       workspace=ws if ws_n else None)
@@ -468,11 +484,11 @@ def main():
         # a few operations per byte of state: the HBM roofline bounds it
         roof["alu"] = alu_obj(cfg.updates * (SLOTS_PER_UPDATE if not is_ssd else 4.0))
     elif is_ssd:
-        Q = 64   # the kernel evaluates any chunk length as 64-step blocks
-        # matrix-core work of the block form per launch: causal in-block Q*Q*P/2 per step and head,
-        # state readout and update 2*N*P per step and head, C.B^T Q*N/2 (causal) per step and group
-        macs = cfg.batch * cfg.seqlen * (cfg.nheads * (Q * cfg.headdim / 2 + 2 * cfg.dstate * cfg.headdim)
-                                         + cfg.ngroups * Q * cfg.dstate / 2)
+        Q = 64   # the kernel evaluates any chunk length as 64-row blocks (a row is a step, or one of its R ranks)
+        # matrix-core work of the block form per launch: per row and head the causal in-block Q*P/2 and the
+        # state readout and update 2*N*P; per row and group C.B^T Q*N/2 (causal)
+        macs = cfg.batch * cfg.seqlen * cfg.rank * (cfg.nheads * (Q * cfg.headdim / 2 + 2 * cfg.dstate * cfg.headdim)
+                                                    + cfg.ngroups * Q * cfg.dstate / 2)
         mf = {"achieved": 2 * macs / kern_s / 1e12, "peak": PEAK_BF16_MFMA_TFLOPS, "unit": "TFLOP/s"}
         mf["frac"] = mf["achieved"] / mf["peak"]
         roof["mfma"] = mf
@@ -525,6 +541,8 @@ def main():
                     **plan)
         if cfg.trapezoidal:
             conf["rule"] = "exponential-trapezoidal"
+        if cfg.rank > 1:
+            conf["mimo_rank"] = cfg.rank
         if getattr(cfg, "complex_state", False):
             conf["state"] = "complex (rotation per state pair)"
     else:

@@ -11,7 +11,9 @@
  *    (mssm_selective_scan_conv_fwd; decode: mssm_selective_state_update_conv);
  *  - the second under the Mamba-3 exponential-trapezoidal input rule
  *    (mssm_ssd_trapezoidal_fwd; decode: mssm_ssd_trapezoidal_state_update),
- *    and with a complex-valued state as well (mssm_mamba3_siso_update).
+ *    with a complex-valued state as well (mssm_mamba3_siso_update), and with
+ *    several inputs and outputs per channel, Mamba-3 MIMO
+ *    (mssm_ssd_mimo_fwd; decode: mssm_ssd_mimo_state_update).
  *
  *  1. mssm_selective_scan_fwd -- the Mamba-1 selective scan.  Defined by the
  *     linear state recurrence h_t = A h_{t-1} + B x_t with readout y_t = C h_t
@@ -118,9 +120,9 @@ typedef struct {
  * blocks with the state carried between them (the same algebra, so only
  * rounding differs).  The matrix-core block kernel takes io_dtype MSSM_BF16
  * (the matrix cores take bf16 operands), headdim a multiple of 64, dstate a
- * multiple of 16 up to 128, nheads * headdim and ngroups * dstate below 2^24;
- * there the state never leaves the chip between blocks, and x, z, out, B, C,
- * h0 and final_state must be 16-byte aligned.  Any other problem with io_dtype
+ * multiple of 16 up to 128 (and, for the MIMO calls below, a rank of 1, 2,
+ * 4, 8 or 16); there the state never leaves the chip between blocks, and x,
+ * z, out, B, C, h0 and final_state must be 16-byte aligned.  Any other problem with io_dtype
  * MSSM_F32 or MSSM_BF16 and dstate up to 256 runs token by token through the
  * recurrent update kernel (state from h0, written to final_state; the chunk
  * is then unused), with element-aligned pointers.  The state update's
@@ -200,6 +202,37 @@ int mssm_ssd_trapezoidal_fwd(const mssm_ssd_desc* desc,
                              const void* B, const void* C, const float* D, const void* z,
                              const float* h0, void* out, float* final_state,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Mamba-3 MIMO ("Mamba-3" blog, "El modelo Mamba-3" item 3: multi-input
+ * multi-output SSMs model several SSMs in parallel, against the single-input
+ * single-output ones, for more work per update at about the same decode
+ * latency; "Arquitectura": the MIMO projections widen B and C; "Tareas de
+ * recuperacion": the state does not grow).  The pages give no formula; the
+ * plain reading: each channel p of head h takes `rank` inputs and gives
+ * `rank` outputs, and all of them share the head's one state and transition.
+ * With U_t[p,n] = sum_r B[b,t,g,r,n] * x[b,t,h,r,p]:
+ *     a        = exp(delta[b,t,h] * A[h])
+ *     S[p,n]   = a * S[p,n] + (1 - lam) * delta * a * U_{t-1}[p,n] + lam * delta * U_t[p,n]
+ *     y[b,t,h,r,p] = sum_n C[b,t,g,r,n] * S[p,n] + D[h] * x[b,t,h,r,p],   out = y * silu(z)
+ * lam NULL is lam = 1 (the Mamba-2 rule, delta * U_t); rank 1 is
+ * mssm_ssd_trapezoidal_fwd (mssm_ssd_fwd without lam).  Layouts:
+ *   x, z, out : [batch, seqlen, nheads, rank, headdim]   (io_dtype; z nullable)
+ *   B, C      : [batch, seqlen, ngroups, rank, dstate]   (io_dtype)
+ *   delta, lam: [batch, seqlen, nheads] (io_dtype; lam nullable)
+ *   A, D, h0, final_state: as mssm_ssd_fwd.
+ * rank: 1..64 (MSSM_ERR_UNSUPPORTED above, MSSM_ERR_INVALID_ARG below 1).
+ * The matrix-core block kernel takes rank 1, 2, 4, 8 or 16 (besides the
+ * mssm_ssd_desc conditions): its 64-row blocks then hold 64 / rank steps, and
+ * the rows of a step share that step's decay.  Any other rank or shape runs
+ * token by token through the recurrent update kernel.  Before step 0 there is
+ * no input (U_{-1} = 0); to continue a sequence, pass final_state as h0 after
+ * adding (1 - lam) * delta * U of the boundary, or step on with
+ * mssm_ssd_mimo_state_update.  Other rules as mssm_ssd_fwd. */
+int mssm_ssd_mimo_fwd(const mssm_ssd_desc* desc, int32_t rank,
+                      const void* x, const void* delta, const void* lam, const float* A,
+                      const void* B, const void* C, const float* D, const void* z,
+                      const float* h0, void* out, float* final_state,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* Token-by-token state update (decode), Mamba-1 form.  At inference the layer
  * keeps only its fixed-size state and advances it one token at a time, at a
@@ -301,6 +334,24 @@ int mssm_mamba3_siso_update(const mssm_ssd_desc* desc, float* state,
                             const float* A, const float* omega,
                             const void* B, const void* C, const float* D, const void* z,
                             void* out, void* stream);
+
+/* The MIMO decode step (see mssm_ssd_mimo_fwd): desc->seqlen new tokens
+ * (normally 1) from `state`, written back in place.  The state is read and
+ * written once per call whatever the rank: the rank multiplies the work per
+ * byte of state, not the bytes ("Mamba-3" blog, "Resultados experimentales":
+ * MIMO does not raise decode latency).
+ *   x_prev : [batch, nheads, rank, headdim], B_prev : [batch, ngroups, rank, dstate]
+ *            (io_dtype, nullable: no previous token; read only, and ignored
+ *            when lam is NULL)
+ *   x, z, out, B, C, delta, lam: as mssm_ssd_mimo_fwd with seqlen tokens.
+ * Equals mssm_ssd_mimo_fwd with h0 = state + (1 - lam_0) * delta_0 * U_prev
+ * and final_state written to state, up to rounding.  Any headdim, dstate up
+ * to 256, fp32 or bf16; other rules as mssm_ssd_state_update. */
+int mssm_ssd_mimo_state_update(const mssm_ssd_desc* desc, int32_t rank, float* state,
+                               const void* x_prev, const void* B_prev,
+                               const void* x, const void* delta, const void* lam,
+                               const float* A, const void* B, const void* C,
+                               const float* D, const void* z, void* out, void* stream);
 
 /* Selective scan with the short causal convolution + SiLU that precedes it in
  * the Mamba-1/2 block fused in front ("Mamba-3" blog, "Arquitectura": the
@@ -410,6 +461,8 @@ int mssm_selective_scan_plan(const mssm_scan_desc* desc, int32_t* split_seq, int
 #define MSSM_SSD_ROUTE_BLOCK 0
 #define MSSM_SSD_ROUTE_RECURRENT 1
 int mssm_ssd_plan(const mssm_ssd_desc* desc, int32_t* route);
+/* The same for mssm_ssd_mimo_fwd with this rank. */
+int mssm_ssd_mimo_plan(const mssm_ssd_desc* desc, int32_t rank, int32_t* route);
 
 /* Static text for a status code (never NULL). */
 const char* mssm_status_string(int status);

@@ -48,6 +48,9 @@ SIGNATURES = {
     "mssm_ssd_fwd": (_I, [ctypes.POINTER(SSDDesc)] + [_P] * 10 + [_P, _SZ, _P]),
     "mssm_ssd_workspace_size": (_SZ, [ctypes.POINTER(SSDDesc)]),
     "mssm_ssd_plan": (_I, [ctypes.POINTER(SSDDesc), ctypes.POINTER(ctypes.c_int32)]),
+    "mssm_ssd_mimo_plan": (_I, [ctypes.POINTER(SSDDesc), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]),
+    "mssm_ssd_mimo_fwd": (_I, [ctypes.POINTER(SSDDesc), ctypes.c_int32] + [_P] * 11 + [_P, _SZ, _P]),
+    "mssm_ssd_mimo_state_update": (_I, [ctypes.POINTER(SSDDesc), ctypes.c_int32] + [_P] * 13),
     "mssm_ssd_trapezoidal_fwd": (_I, [ctypes.POINTER(SSDDesc)] + [_P] * 11 + [_P, _SZ, _P]),
     "mssm_selective_state_update": (_I, [ctypes.POINTER(ScanDesc)] + [_P] * 10),
     "mssm_ssd_state_update": (_I, [ctypes.POINTER(SSDDesc)] + [_P] * 10),
@@ -479,6 +482,86 @@ def ssd_trapezoidal_fwd(x, delta, lam, A, B, C, D=None, z=None, h0=None, chunk: 
     """
     return _ssd_call("mssm_ssd_trapezoidal_fwd", x, delta, lam, A, B, C, D, z, h0, chunk, return_final_state,
                      out, final_state, workspace, stream)
+
+
+def ssd_mimo_plan(batch, seqlen, nheads, headdim, dstate, ngroups, rank, chunk=0, io_dtype=MSSM_BF16) -> int:
+    """Which kernel mssm_ssd_mimo_fwd runs this problem on (SSD_ROUTE_BLOCK or SSD_ROUTE_RECURRENT)."""
+    d = ssd_desc(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, io_dtype)
+    r = ctypes.c_int32(-1)
+    st = lib.mssm_ssd_mimo_plan(ctypes.byref(d), rank, ctypes.byref(r))
+    if st != MSSM_OK:
+        raise MssmError(st, "mssm_ssd_mimo_plan")
+    return r.value
+
+
+def ssd_mimo_fwd(x, delta, lam, A, B, C, D=None, z=None, h0=None, chunk: int = 0, return_final_state: bool = False,
+                 out=None, final_state=None, workspace=None, stream=None):
+    """Mamba-3 MIMO (mssm_ssd_mimo_fwd): x, z [batch, seqlen, nheads, rank, headdim]; B, C [batch, seqlen,
+    ngroups, rank, dstate]; delta, lam [batch, seqlen, nheads] (lam None: the Mamba-2 rule); A, D [nheads];
+    h0 [batch, nheads, headdim, dstate].  Returns out (and the final state when asked)."""
+    torch = _torch()
+    if x.dim() != 5 or B.dim() != 5:
+        raise ValueError("x must be [batch, seqlen, nheads, rank, headdim] and B [batch, seqlen, ngroups, rank, dstate]")
+    bsz, L, H, R, P = x.shape
+    G, N = B.shape[2], B.shape[4]
+    io = _io_code(x.dtype)
+    cur = torch.cuda.current_device()
+    for name, t, shape in (("x", x, (bsz, L, H, R, P)), ("z", z, (bsz, L, H, R, P)), ("delta", delta, (bsz, L, H)),
+                           ("lam", lam, (bsz, L, H)), ("B", B, (bsz, L, G, R, N)), ("C", C, (bsz, L, G, R, N))):
+        _check_gpu(name, t, x.dtype, shape, cur)
+    _check_gpu("A", A, torch.float32, (H,), cur)
+    _check_gpu("D", D, torch.float32, (H,), cur)
+    _check_gpu("h0", h0, torch.float32, (bsz, H, P, N), cur)
+    if out is None:
+        out = torch.empty_like(x)
+    _check_gpu("out", out, x.dtype, (bsz, L, H, R, P), cur)
+    if return_final_state and final_state is None:
+        final_state = torch.empty((bsz, H, P, N), dtype=torch.float32, device=x.device)
+    _check_gpu("final_state", final_state, torch.float32, (bsz, H, P, N), cur)
+    d = ssd_desc(bsz, L, H, P, N, G, chunk, io)
+    ws_bytes = lib.mssm_ssd_workspace_size(ctypes.byref(d))
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    st = lib.mssm_ssd_mimo_fwd(ctypes.byref(d), R, _ptr(x), _ptr(delta), _ptr(lam), _ptr(A), _ptr(B), _ptr(C),
+                               _ptr(D), _ptr(z), _ptr(h0), _ptr(out), _ptr(final_state),
+                               _ptr(workspace) if ws_bytes else None,
+                               workspace.numel() if (ws_bytes and workspace is not None) else 0,
+                               _stream_handle(stream))
+    if st != MSSM_OK:
+        raise MssmError(st, "mssm_ssd_mimo_fwd")
+    return (out, final_state) if return_final_state else out
+
+
+def ssd_mimo_state_update(state, x, delta, lam, A, B, C, D=None, z=None, x_prev=None, B_prev=None, out=None,
+                          stream=None):
+    """Advance a multi-head state by seqlen tokens in place under Mamba-3 MIMO (mssm_ssd_mimo_state_update).
+    x, z [batch, seqlen, nheads, rank, headdim]; B, C [batch, seqlen, ngroups, rank, dstate]; lam None: the
+    Mamba-2 rule; x_prev [batch, nheads, rank, headdim], B_prev [batch, ngroups, rank, dstate] (None: no
+    previous token).  Returns out."""
+    torch = _torch()
+    if x.dim() != 5 or B.dim() != 5:
+        raise ValueError("x must be [batch, seqlen, nheads, rank, headdim] and B [batch, seqlen, ngroups, rank, dstate]")
+    bsz, L, H, R, P = x.shape
+    G, N = B.shape[2], B.shape[4]
+    io = _io_code(x.dtype)
+    cur = torch.cuda.current_device()
+    for name, t, shape in (("x", x, (bsz, L, H, R, P)), ("z", z, (bsz, L, H, R, P)), ("delta", delta, (bsz, L, H)),
+                           ("lam", lam, (bsz, L, H)), ("B", B, (bsz, L, G, R, N)), ("C", C, (bsz, L, G, R, N)),
+                           ("x_prev", x_prev, (bsz, H, R, P)), ("B_prev", B_prev, (bsz, G, R, N))):
+        _check_gpu(name, t, x.dtype, shape, cur)
+    _check_gpu("A", A, torch.float32, (H,), cur)
+    _check_gpu("D", D, torch.float32, (H,), cur)
+    _check_gpu("state", state, torch.float32, (bsz, H, P, N), cur)
+    if out is None:
+        out = torch.empty_like(x)
+    _check_gpu("out", out, x.dtype, (bsz, L, H, R, P), cur)
+    d = ssd_desc(bsz, L, H, P, N, G, 0, io)
+    st = lib.mssm_ssd_mimo_state_update(ctypes.byref(d), R, _ptr(state), _ptr(x_prev), _ptr(B_prev), _ptr(x),
+                                        _ptr(delta), _ptr(lam), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                        _ptr(out), _stream_handle(stream))
+    if st != MSSM_OK:
+        raise MssmError(st, "mssm_ssd_mimo_state_update")
+    return out
 
 
 def _ssd_call(fn, x, delta, lam, A, B, C, D, z, h0, chunk, return_final_state, out, final_state, workspace,

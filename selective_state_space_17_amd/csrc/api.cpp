@@ -265,31 +265,34 @@ int mssm_selective_scan_fwd_noalloc(const mssm_scan_desc* desc, const void* x, c
 // Mamba-2 scalar-A multi-head form
 // --------------------------------------------------------------------------
 // *matrix: the shape and dtype the matrix-core block kernel takes (bf16 I/O, headdim a multiple of 64,
-// dstate a multiple of 16 up to 128); any other valid problem runs through the recurrent update kernel
-static int validate_ssd_desc(const mssm_ssd_desc* d, int64_t* Q, bool* matrix) {
+// dstate a multiple of 16 up to 128, rank 1, 2, 4, 8 or 16); any other valid problem runs through the
+// recurrent update kernel.  R: inputs and outputs per channel (MIMO; 1 otherwise), 1..64.
+constexpr int64_t kMaxRank = 64;
+static int validate_ssd_desc(const mssm_ssd_desc* d, int64_t R, int64_t* Q, bool* matrix) {
   if (d == nullptr) return MSSM_ERR_INVALID_ARG;
   if (d->batch < 0 || d->seqlen < 0 || d->nheads <= 0 || d->headdim <= 0 || d->dstate <= 0 || d->ngroups <= 0)
     return MSSM_ERR_INVALID_ARG;
   if (d->flags != 0) return MSSM_ERR_INVALID_ARG;
+  if (R < 1) return MSSM_ERR_INVALID_ARG;
+  if (R > kMaxRank) return MSSM_ERR_UNSUPPORTED;
   if (d->io_dtype != MSSM_BF16 && d->io_dtype != MSSM_F32) return MSSM_ERR_UNSUPPORTED;
   if (d->nheads % d->ngroups != 0 || d->dstate > 256) return MSSM_ERR_UNSUPPORTED;
   const int64_t q = d->chunk == 0 ? 64 : d->chunk;
   if (q != 64 && q != 128 && q != 256) return MSSM_ERR_UNSUPPORTED;
-  // per-step row strides of the block kernel (nheads * headdim, ngroups * dstate) go through 24-bit
-  // multiplies, which read only the low 24 bits of an operand: both must stay below 2^24
-  *matrix = d->io_dtype == MSSM_BF16 && mssm::ssd_supported(d->headdim, d->dstate) &&
-            d->nheads <= ((1 << 24) - 1) / d->headdim && d->ngroups <= ((1 << 24) - 1) / d->dstate;
   const int64_t es = d->io_dtype == MSSM_BF16 ? 2 : 4;
   int64_t t = 0;
-  if (!mul_ok(d->batch, d->seqlen, &t) || !mul_ok(t, d->nheads, &t) || !mul_ok(t, d->headdim, &t) ||
-      !mul_ok(t, es, &t))
+  if (!mul_ok(d->batch, d->seqlen, &t) || !mul_ok(t, d->nheads, &t) || !mul_ok(t, R, &t) ||
+      !mul_ok(t, d->headdim, &t) || !mul_ok(t, es, &t))
     return MSSM_ERR_INVALID_ARG;
-  if (!mul_ok(d->batch, d->seqlen, &t) || !mul_ok(t, d->ngroups, &t) || !mul_ok(t, d->dstate, &t) ||
-      !mul_ok(t, es, &t))
+  if (!mul_ok(d->batch, d->seqlen, &t) || !mul_ok(t, d->ngroups, &t) || !mul_ok(t, R, &t) ||
+      !mul_ok(t, d->dstate, &t) || !mul_ok(t, es, &t))
     return MSSM_ERR_INVALID_ARG;
   if (!mul_ok(d->batch, d->nheads, &t) || !mul_ok(t, d->headdim, &t) || !mul_ok(t, d->dstate, &t) ||
       !mul_ok(t, 4, &t))
     return MSSM_ERR_INVALID_ARG;
+  // the block kernel's grid: one workgroup per (batch, head, 64-wide headdim slice) at most
+  *matrix = d->io_dtype == MSSM_BF16 && mssm::ssd_supported(d->headdim, d->dstate) && mssm::ssd_rank_supported(R) &&
+            d->batch * d->nheads * (d->headdim / 64) <= std::numeric_limits<int32_t>::max();
   *Q = q;
   return MSSM_OK;
 }
@@ -380,8 +383,8 @@ int mssm_selective_state_update_conv(const mssm_scan_desc* desc, int32_t conv_wi
 }  // extern "C"
 
 namespace {
-// both multi-head decode rules: lam == nullptr (want_lam false) is the Mamba-2 rule
-int ssd_update_impl(const mssm_ssd_desc* desc, float* state, const void* x_prev, const void* B_prev,
+// every multi-head decode rule: lam == nullptr (want_lam false) is the Mamba-2 rule; R > 1 is MIMO
+int ssd_update_impl(const mssm_ssd_desc* desc, int64_t R, float* state, const void* x_prev, const void* B_prev,
                     const void* x, const void* delta, const void* lam, bool want_lam, const float* A,
                     const float* omega, bool want_omega, const void* B, const void* C, const float* D,
                     const void* z, void* out, void* stream) {
@@ -390,16 +393,18 @@ int ssd_update_impl(const mssm_ssd_desc* desc, float* state, const void* x_prev,
   if (d->batch < 0 || d->seqlen < 0 || d->nheads <= 0 || d->headdim <= 0 || d->dstate <= 0 || d->ngroups <= 0)
     return MSSM_ERR_INVALID_ARG;
   if (d->flags != 0) return MSSM_ERR_INVALID_ARG;
+  if (R < 1) return MSSM_ERR_INVALID_ARG;
+  if (R > kMaxRank) return MSSM_ERR_UNSUPPORTED;
   if (d->io_dtype != MSSM_BF16 && d->io_dtype != MSSM_F32) return MSSM_ERR_UNSUPPORTED;
   if (d->nheads % d->ngroups != 0 || d->dstate > 256) return MSSM_ERR_UNSUPPORTED;
   if (want_omega && d->dstate % 2 != 0) return MSSM_ERR_UNSUPPORTED;   // complex state: whole pairs
   const int64_t es = d->io_dtype == MSSM_BF16 ? 2 : 4;
   int64_t n_x = 0, n_bc = 0, n_st = 0, n_d = 0, t = 0;
-  if (!mul_ok(d->batch, d->seqlen, &t) || !mul_ok(t, d->nheads, &n_d) || !mul_ok(n_d, d->headdim, &n_x) ||
-      !mul_ok(n_x, es, &t))
+  if (!mul_ok(d->batch, d->seqlen, &t) || !mul_ok(t, d->nheads, &n_d) || !mul_ok(n_d, R, &t) ||
+      !mul_ok(t, d->headdim, &n_x) || !mul_ok(n_x, es, &t))
     return MSSM_ERR_INVALID_ARG;
-  if (!mul_ok(d->batch, d->seqlen, &t) || !mul_ok(t, d->ngroups, &t) || !mul_ok(t, d->dstate, &n_bc) ||
-      !mul_ok(n_bc, es, &t))
+  if (!mul_ok(d->batch, d->seqlen, &t) || !mul_ok(t, d->ngroups, &t) || !mul_ok(t, R, &t) ||
+      !mul_ok(t, d->dstate, &n_bc) || !mul_ok(n_bc, es, &t))
     return MSSM_ERR_INVALID_ARG;
   if (!mul_ok(d->batch, d->nheads, &t) || !mul_ok(t, d->headdim, &t) || !mul_ok(t, d->dstate, &n_st) ||
       !mul_ok(n_st, 4 * 64, &t))
@@ -415,7 +420,7 @@ int ssd_update_impl(const mssm_ssd_desc* desc, float* state, const void* x_prev,
       !aligned(x_prev, es) || !aligned(B_prev, es) || !aligned(omega, 4))
     return MSSM_ERR_MISALIGNED;
   const int64_t b_io = n_x * es, b_st = n_st * 4;
-  const int64_t b_xp = d->batch * d->nheads * d->headdim * es, b_bp = d->batch * d->ngroups * d->dstate * es;
+  const int64_t b_xp = d->batch * d->nheads * R * d->headdim * es, b_bp = d->batch * d->ngroups * R * d->dstate * es;
   const void* ins[] = {x, delta, B, C, z, A, D, lam, x_prev, B_prev, omega};
   const int64_t inb[] = {b_io, n_d * es, n_bc * es, n_bc * es, b_io, d->nheads * 4, d->nheads * 4, n_d * es,
                          b_xp, b_bp, d->nheads * (d->dstate / 2) * 4};
@@ -429,7 +434,7 @@ int ssd_update_impl(const mssm_ssd_desc* desc, float* state, const void* x_prev,
   mssm::UpdateArgs a{};
   a.state = state; a.x = x; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.out = out;
   a.batch = d->batch; a.L = d->seqlen; a.N = d->dstate;
-  a.H = d->nheads; a.P = d->headdim; a.G = d->ngroups; a.io = d->io_dtype;
+  a.H = d->nheads; a.P = d->headdim; a.G = d->ngroups; a.io = d->io_dtype; a.rank = R;
   if (want_lam) {
     a.lam = lam; a.x_prev = x_prev; a.B_prev = B_prev;
     if (want_omega) a.omega = omega;
@@ -448,22 +453,31 @@ extern "C" {
 int mssm_ssd_state_update(const mssm_ssd_desc* desc, float* state, const void* x, const void* delta,
                           const float* A, const void* B, const void* C, const float* D, const void* z, void* out,
                           void* stream) {
-  return ssd_update_impl(desc, state, nullptr, nullptr, x, delta, nullptr, false, A, nullptr, false, B, C, D, z, out,
-                         stream);
+  return ssd_update_impl(desc, 1, state, nullptr, nullptr, x, delta, nullptr, false, A, nullptr, false, B, C, D, z,
+                         out, stream);
 }
 
 int mssm_ssd_trapezoidal_state_update(const mssm_ssd_desc* desc, float* state, const void* x_prev,
                                       const void* B_prev, const void* x, const void* delta, const void* lam,
                                       const float* A, const void* B, const void* C, const float* D, const void* z,
                                       void* out, void* stream) {
-  return ssd_update_impl(desc, state, x_prev, B_prev, x, delta, lam, true, A, nullptr, false, B, C, D, z, out,
+  return ssd_update_impl(desc, 1, state, x_prev, B_prev, x, delta, lam, true, A, nullptr, false, B, C, D, z, out,
                          stream);
 }
 
 int mssm_mamba3_siso_update(const mssm_ssd_desc* desc, float* state, const void* x_prev, const void* B_prev,
                             const void* x, const void* delta, const void* lam, const float* A, const float* omega,
                             const void* B, const void* C, const float* D, const void* z, void* out, void* stream) {
-  return ssd_update_impl(desc, state, x_prev, B_prev, x, delta, lam, true, A, omega, true, B, C, D, z, out, stream);
+  return ssd_update_impl(desc, 1, state, x_prev, B_prev, x, delta, lam, true, A, omega, true, B, C, D, z, out,
+                         stream);
+}
+
+int mssm_ssd_mimo_state_update(const mssm_ssd_desc* desc, int32_t rank, float* state, const void* x_prev,
+                               const void* B_prev, const void* x, const void* delta, const void* lam,
+                               const float* A, const void* B, const void* C, const float* D, const void* z,
+                               void* out, void* stream) {
+  return ssd_update_impl(desc, rank, state, x_prev, B_prev, x, delta, lam, lam != nullptr, A, nullptr, false, B, C,
+                         D, z, out, stream);
 }
 
 // --------------------------------------------------------------------------
@@ -752,10 +766,12 @@ int mssm_selective_scan_bwd(const mssm_scan_desc* desc, const void* x, const voi
   return MSSM_OK;
 }
 
-int mssm_ssd_plan(const mssm_ssd_desc* desc, int32_t* route) {
+int mssm_ssd_plan(const mssm_ssd_desc* desc, int32_t* route) { return mssm_ssd_mimo_plan(desc, 1, route); }
+
+int mssm_ssd_mimo_plan(const mssm_ssd_desc* desc, int32_t rank, int32_t* route) {
   int64_t Q = 0;
   bool matrix = false;
-  const int v = validate_ssd_desc(desc, &Q, &matrix);
+  const int v = validate_ssd_desc(desc, rank, &Q, &matrix);
   if (v != MSSM_OK) return v;
   if (route == nullptr) return MSSM_ERR_INVALID_ARG;
   *route = matrix ? MSSM_SSD_ROUTE_BLOCK : MSSM_SSD_ROUTE_RECURRENT;
@@ -765,7 +781,7 @@ int mssm_ssd_plan(const mssm_ssd_desc* desc, int32_t* route) {
 size_t mssm_ssd_workspace_size(const mssm_ssd_desc* desc) {
   int64_t Q = 0;
   bool matrix = false;
-  if (validate_ssd_desc(desc, &Q, &matrix) != MSSM_OK || !matrix) return 0;
+  if (validate_ssd_desc(desc, 1, &Q, &matrix) != MSSM_OK || !matrix) return 0;
   return mssm::ssd_workspace_bytes(desc->batch, desc->seqlen, desc->nheads, desc->headdim, desc->dstate,
                                    desc->ngroups, Q);
 }
@@ -775,13 +791,13 @@ size_t mssm_ssd_workspace_size(const mssm_ssd_desc* desc) {
 namespace {
 // A whole sequence through the recurrent update kernel, for the problems the block kernel does not take:
 // the state starts from h0 (or zero) and is written to final_state (if given); no previous token.
-int ssd_fwd_recurrent(const mssm_ssd_desc& d, const void* x, const void* delta, const void* lam, bool want_lam,
-                      const float* A, const void* B, const void* C, const float* D, const void* z, const float* h0,
-                      void* out, float* final_state, void* stream) {
+int ssd_fwd_recurrent(const mssm_ssd_desc& d, int64_t R, const void* x, const void* delta, const void* lam,
+                      bool want_lam, const float* A, const void* B, const void* C, const float* D, const void* z,
+                      const float* h0, void* out, float* final_state, void* stream) {
   const int64_t es = d.io_dtype == MSSM_BF16 ? 2 : 4;
   const int64_t n_d = d.batch * d.seqlen * d.nheads;
-  const int64_t n_x = n_d * d.headdim;
-  const int64_t n_bc = d.batch * d.seqlen * d.ngroups * d.dstate;
+  const int64_t n_x = n_d * R * d.headdim;
+  const int64_t n_bc = d.batch * d.seqlen * d.ngroups * R * d.dstate;
   // the descriptor check bounds batch * nheads * headdim * dstate * 4; the update kernel's lane count
   // is up to 64 times that many bytes' worth of states
   const int64_t n_st = d.batch * d.nheads * d.headdim * d.dstate;
@@ -797,7 +813,7 @@ int ssd_fwd_recurrent(const mssm_ssd_desc& d, const void* x, const void* delta, 
       !aligned(out, es) || !aligned(lam, es) || !aligned(A, 4) || !aligned(D, 4) || !aligned(h0, 4) ||
       !aligned(final_state, 4))
     return MSSM_ERR_MISALIGNED;
-  const int64_t b_io = n_x * es, b_d = d.batch * d.seqlen * d.nheads * es;
+  const int64_t b_io = n_x * es, b_d = n_d * es;
   const void* ins[] = {x, delta, B, C, z, A, D, h0, lam};
   const int64_t inb[] = {b_io, b_d, n_bc * es, n_bc * es, b_io, d.nheads * 4, d.nheads * 4, b_st, b_d};
   for (int i = 0; i < 9; ++i) {
@@ -813,7 +829,7 @@ int ssd_fwd_recurrent(const mssm_ssd_desc& d, const void* x, const void* delta, 
   a.x = x; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.out = out;
   a.lam = want_lam ? lam : nullptr;
   a.batch = d.batch; a.L = d.seqlen; a.N = d.dstate; a.H = d.nheads; a.P = d.headdim; a.G = d.ngroups;
-  a.io = d.io_dtype;
+  a.io = d.io_dtype; a.rank = R;
   const hipError_t e = mssm::ssd_update_launch(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     set_err(e);
@@ -822,22 +838,24 @@ int ssd_fwd_recurrent(const mssm_ssd_desc& d, const void* x, const void* delta, 
   return MSSM_OK;
 }
 
-// both SSD forms: lam == nullptr is the Mamba-2 rule, else lam is required
-int ssd_fwd_impl(const mssm_ssd_desc* desc, const void* x, const void* delta, const void* lam, bool want_lam,
-                 const float* A, const void* B, const void* C, const float* D, const void* z, const float* h0,
-                 void* out, float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
+// every multi-head sequence form: lam == nullptr (want_lam false) is the Mamba-2 rule, else lam is
+// required; R > 1 is MIMO
+int ssd_fwd_impl(const mssm_ssd_desc* desc, int64_t R, const void* x, const void* delta, const void* lam,
+                 bool want_lam, const float* A, const void* B, const void* C, const float* D, const void* z,
+                 const float* h0, void* out, float* final_state, void* workspace, size_t workspace_bytes,
+                 void* stream) {
   int64_t Q = 0;
   bool matrix = false;
-  const int v = validate_ssd_desc(desc, &Q, &matrix);
+  const int v = validate_ssd_desc(desc, R, &Q, &matrix);
   if (v != MSSM_OK) return v;
   const mssm_ssd_desc& d = *desc;
   if (d.batch == 0) return MSSM_OK;
   if (!matrix)
-    return ssd_fwd_recurrent(d, x, delta, want_lam ? lam : nullptr, want_lam, A, B, C, D, z, h0, out, final_state,
-                             stream);
-  const int64_t n_x = d.batch * d.seqlen * d.nheads * d.headdim;
+    return ssd_fwd_recurrent(d, R, x, delta, want_lam ? lam : nullptr, want_lam, A, B, C, D, z, h0, out,
+                             final_state, stream);
+  const int64_t n_x = d.batch * d.seqlen * d.nheads * R * d.headdim;
   const int64_t n_d = d.batch * d.seqlen * d.nheads;
-  const int64_t n_bc = d.batch * d.seqlen * d.ngroups * d.dstate;
+  const int64_t n_bc = d.batch * d.seqlen * d.ngroups * R * d.dstate;
   const int64_t b_st = d.batch * d.nheads * d.headdim * d.dstate * 4;
   const bool has_steps = n_x > 0;
   if (A == nullptr) return MSSM_ERR_INVALID_ARG;
@@ -864,6 +882,7 @@ int ssd_fwd_impl(const mssm_ssd_desc* desc, const void* x, const void* delta, co
   a.x = x; a.delta = delta; a.lam = want_lam ? lam : nullptr; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z;
   a.h0 = h0; a.out = out; a.final_state = final_state; a.workspace = workspace;
   a.batch = d.batch; a.L = d.seqlen; a.H = d.nheads; a.P = d.headdim; a.N = d.dstate; a.G = d.ngroups; a.Q = Q;
+  a.R = R;
   const hipError_t e = mssm::ssd_launch(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     set_err(e);
@@ -878,7 +897,7 @@ extern "C" {
 int mssm_ssd_fwd(const mssm_ssd_desc* desc, const void* x, const void* delta, const float* A, const void* B,
                  const void* C, const float* D, const void* z, const float* h0, void* out, float* final_state,
                  void* workspace, size_t workspace_bytes, void* stream) {
-  return ssd_fwd_impl(desc, x, delta, nullptr, false, A, B, C, D, z, h0, out, final_state, workspace,
+  return ssd_fwd_impl(desc, 1, x, delta, nullptr, false, A, B, C, D, z, h0, out, final_state, workspace,
                       workspace_bytes, stream);
 }
 
@@ -886,7 +905,14 @@ int mssm_ssd_trapezoidal_fwd(const mssm_ssd_desc* desc, const void* x, const voi
                              const float* A, const void* B, const void* C, const float* D, const void* z,
                              const float* h0, void* out, float* final_state, void* workspace,
                              size_t workspace_bytes, void* stream) {
-  return ssd_fwd_impl(desc, x, delta, lam, true, A, B, C, D, z, h0, out, final_state, workspace,
+  return ssd_fwd_impl(desc, 1, x, delta, lam, true, A, B, C, D, z, h0, out, final_state, workspace,
+                      workspace_bytes, stream);
+}
+
+int mssm_ssd_mimo_fwd(const mssm_ssd_desc* desc, int32_t rank, const void* x, const void* delta, const void* lam,
+                      const float* A, const void* B, const void* C, const float* D, const void* z, const float* h0,
+                      void* out, float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
+  return ssd_fwd_impl(desc, rank, x, delta, lam, lam != nullptr, A, B, C, D, z, h0, out, final_state, workspace,
                       workspace_bytes, stream);
 }
 

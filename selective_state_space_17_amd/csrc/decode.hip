@@ -157,6 +157,8 @@ struct UpdParams {
   const void* x_prev;      // [batch, H, P], nullable
   const void* B_prev;      // [batch, G, N], nullable
   const float* omega;      // [H, N/2] (ROT)
+  int64_t rank;            // MIMO: inputs and outputs per channel (x, z, out [batch, L, H, rank, P],
+                           // B, C [batch, L, G, rank, N]; x_prev [batch, H, rank, P], B_prev [batch, G, rank, N])
   // the state read before the first token (nullable: zero) and written after
   // the last (nullable: not written); both are `state` for an update in place,
   // h0 and final_state for a whole sequence
@@ -393,6 +395,94 @@ __global__ __launch_bounds__(kThreads) void ssd_update_kernel(UpdParams p) {
     if (live[k] && p.state_out != nullptr) storeS<S, VEC>(p.state_out + rr[k] * N, n0, N, h[k]);
 }
 
+// Mamba-3 MIMO ("Mamba-3" blog, "El modelo Mamba-3" item 3), row = (b, h, p): the rank inputs of the
+// row's channel drive its states through one transition, U = sum_r x_r B_r, and each rank reads them out
+// through its own C_r.  Mamba-2 rule, or with TRAP the exponential-trapezoidal rule, whose left-end term
+// uses the previous token's U.  The ranks are walked one at a time (S registers of B or C each).
+template <typename T, bool VEC, int S, bool TRAP>
+__global__ __launch_bounds__(kThreads) void ssdm_update_kernel(UpdParams p) {
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t row = gid / p.lpr;
+  const int n0 = S * static_cast<int>(gid % p.lpr);
+  const int64_t P = p.P, H = p.H, G = p.G, L = p.L, NR = p.rank;
+  const int N = static_cast<int>(p.N);
+  const T* x = static_cast<const T*>(p.x);
+  const T* delta = static_cast<const T*>(p.delta);
+  const T* Bm = static_cast<const T*>(p.B);
+  const T* Cm = static_cast<const T*>(p.C);
+  const T* z = static_cast<const T*>(p.z);
+  T* out = static_cast<T*>(p.out);
+  const bool live = row < p.rows;
+  const int64_t rr = live ? row : 0;
+  const int64_t pp = rr % P, bh = rr / P, hd = bh % H, bb = bh / H, gg = hd / (H / G);
+  float h[S], up[S];
+  if (p.state_in != nullptr) {
+    loadS<S, VEC>(p.state_in + rr * N, n0, N, h);
+  } else {
+#pragma unroll
+    for (int q = 0; q < S; ++q) h[q] = 0.f;
+  }
+  const float a2 = p.A[hd] * kLog2e;
+  const float Dh = p.D != nullptr ? p.D[hd] : 0.f;
+#pragma unroll
+  for (int q = 0; q < S; ++q) up[q] = 0.f;   // TRAP: the previous token's sum_r x_r B_r
+  if constexpr (TRAP) {
+    if (p.x_prev != nullptr && p.B_prev != nullptr) {
+      for (int64_t r = 0; r < NR; ++r) {
+        float bv[S];
+        const float u = to_f32(static_cast<const T*>(p.x_prev)[(bh * NR + r) * P + pp]);
+        loadSio<T, S, VEC>(static_cast<const T*>(p.B_prev) + ((bb * G + gg) * NR + r) * N, n0, N, bv);
+#pragma unroll
+        for (int q = 0; q < S; ++q) up[q] = __builtin_fmaf(u, bv[q], up[q]);
+      }
+    }
+  }
+  const T* lam = static_cast<const T*>(p.lam);
+  for (int64_t t = 0; t < L; ++t) {
+    const int64_t obh = (bb * L + t) * H + hd;
+    const int64_t bcr = ((bb * L + t) * G + gg) * NR;   // B, C row of rank 0
+    const float d = to_f32(delta[obh]);
+    const float dA = exp2_hw(d * a2);
+    float U[S];
+#pragma unroll
+    for (int q = 0; q < S; ++q) U[q] = 0.f;
+    for (int64_t r = 0; r < NR; ++r) {
+      float bv[S];
+      const float u = to_f32(x[(obh * NR + r) * P + pp]);
+      loadSio<T, S, VEC>(Bm + (bcr + r) * N, n0, N, bv);
+#pragma unroll
+      for (int q = 0; q < S; ++q) U[q] = __builtin_fmaf(u, bv[q], U[q]);
+    }
+    if constexpr (TRAP) {
+      const float lm = to_f32(lam[obh]);
+      const float wl = (1.f - lm) * d, wr = lm * d;
+#pragma unroll
+      for (int q = 0; q < S; ++q) {
+        h[q] = __builtin_fmaf(dA, __builtin_fmaf(wl, up[q], h[q]), wr * U[q]);
+        up[q] = U[q];
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < S; ++q) h[q] = __builtin_fmaf(dA, h[q], d * U[q]);
+    }
+    for (int64_t r = 0; r < NR; ++r) {
+      float cv[S];
+      loadSio<T, S, VEC>(Cm + (bcr + r) * N, n0, N, cv);
+      float acc = 0.f;
+#pragma unroll
+      for (int q = 0; q < S; ++q) acc = __builtin_fmaf(cv[q], h[q], acc);
+      acc = group_sum(acc, p.lpr);
+      if (live && n0 == 0) {
+        const int64_t o = (obh * NR + r) * P + pp;
+        float y = __builtin_fmaf(Dh, to_f32(x[o]), acc);
+        if (z != nullptr) y *= silu(to_f32(z[o]));
+        out[o] = from_f32<T>(y);
+      }
+    }
+  }
+  if (live && p.state_out != nullptr) storeS<S, VEC>(p.state_out + rr * N, n0, N, h);
+}
+
 int lanes_per_row(int64_t N, int S) {
   int l = 1;
   while (static_cast<int64_t>(S) * l < N) l *= 2;
@@ -444,6 +534,8 @@ template <typename T, bool VEC, int S> struct ScanUpdConv { static constexpr aut
 template <typename T, bool VEC, int S> struct SsdUpd { static constexpr auto fn = ssd_update_kernel<T, VEC, S, false, false>; };
 template <typename T, bool VEC, int S> struct SsdUpdTrap { static constexpr auto fn = ssd_update_kernel<T, VEC, S, true, false>; };
 template <typename T, bool VEC, int S> struct SsdUpdRot { static constexpr auto fn = ssd_update_kernel<T, VEC, S, true, true>; };
+template <typename T, bool VEC, int S> struct SsdmUpd { static constexpr auto fn = ssdm_update_kernel<T, VEC, S, false>; };
+template <typename T, bool VEC, int S> struct SsdmUpdTrap { static constexpr auto fn = ssdm_update_kernel<T, VEC, S, true>; };
 
 }  // namespace
 
@@ -466,6 +558,17 @@ hipError_t ssd_update_launch(const UpdateArgs& a, hipStream_t stream) {
   UpdParams p = common(a);
   p.H = a.H; p.P = a.P; p.G = a.G;
   p.rows = a.batch * a.H * a.P;
+  p.rank = a.rank;
+  if (a.rank > 1) {   // MIMO (no complex state)
+    if (a.omega != nullptr) return hipErrorInvalidValue;
+    if (a.lam != nullptr) {
+      p.lam = a.lam; p.x_prev = a.x_prev; p.B_prev = a.B_prev;
+      return a.io == 1 ? launch_update<SsdmUpdTrap, uint16_t>(p, a, false, stream)
+                       : launch_update<SsdmUpdTrap, float>(p, a, false, stream);
+    }
+    return a.io == 1 ? launch_update<SsdmUpd, uint16_t>(p, a, false, stream)
+                     : launch_update<SsdmUpd, float>(p, a, false, stream);
+  }
   if (a.lam != nullptr) {
     p.lam = a.lam; p.x_prev = a.x_prev; p.B_prev = a.B_prev;
     if (a.omega != nullptr) {   // dstate is even: lanes own whole pairs (groups of 4 or 8 from a multiple of 4)

@@ -76,11 +76,13 @@ struct SSDArgs {
   float* final_state;
   void* workspace;
   int64_t batch, L, H, P, N, G, Q;
+  int64_t R = 1;   // inputs and outputs per channel (MIMO); x, z, out [B, L, H, R, P], B, C [B, L, G, R, N]
 };
 
 size_t ssd_workspace_bytes(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q);
-// headdim and dstate the matrix-core block kernel takes (bf16 I/O)
+// headdim and dstate the matrix-core block kernel takes (bf16 I/O), and the MIMO ranks
 bool ssd_supported(int64_t P, int64_t N);
+bool ssd_rank_supported(int64_t R);
 hipError_t ssd_launch(const SSDArgs& a, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
@@ -112,6 +114,8 @@ struct UpdateArgs {
   const void* x_prev = nullptr;    // [batch, H, P], the token before the first one; nullable = none
   const void* B_prev = nullptr;    // [batch, G, N], likewise
   const float* omega = nullptr;    // [H, N/2] rotation rates of the state pairs (complex state); nullable
+  int64_t rank = 1;                // MIMO inputs and outputs per channel (x, z, out [.., H, rank, P],
+                                   // B, C [.., G, rank, N]); > 1 takes no omega
   // with state == nullptr: the state before the first token (nullable: zero) and the one written
   // after the last (nullable: not written), for a whole sequence run through the update kernel
   const float* state_in = nullptr;

@@ -168,7 +168,7 @@ def test_ssd_validation(kw, expect):
 # Shapes and dtypes the matrix-core block kernel does not take: accepted, and run through the recurrent
 # update kernel. A null x proves the descriptor passed (the pointer checks reject it) without launching.
 RECURRENT_SSD = [dict(io_dtype=M.MSSM_F32), dict(headdim=24), dict(headdim=96), dict(dstate=20), dict(dstate=256),
-                 dict(dstate=6), dict(nheads=(1 << 18) + 1, ngroups=1, headdim=64)]
+                 dict(dstate=6)]
 
 
 @pytest.mark.parametrize("kw", RECURRENT_SSD)
@@ -189,13 +189,21 @@ def test_ssd_route():
         a = dict(batch=2, seqlen=128, nheads=4, headdim=64, dstate=64, ngroups=1, chunk=64, io_dtype=M.MSSM_BF16)
         a.update(kw)
         assert M.ssd_plan(**a) == rec, kw
-    # per-step row strides go through 24-bit multiplies: nheads * headdim and ngroups * dstate below 2^24 only
-    assert M.ssd_plan(1, 8, (1 << 18) - 1, 64, 64, 1) == block          # nheads * headdim = 2^24 - 64
-    assert M.ssd_plan(1, 8, 1 << 18, 64, 64, 1) == rec                  # exactly 2^24: low 24 bits would be 0
-    assert M.ssd_plan(1, 8, 1 << 17, 128, 64, 1) == rec
-    assert M.ssd_plan(1, 8, 1 << 20, 64, 16, 1 << 20) == rec            # ngroups * dstate = 2^24
-    assert M.ssd_plan(1, 8, (1 << 20) - 1, 64, 16, (1 << 20) - 1) == rec   # nheads * headdim > 2^24
-    assert M.ssd_plan(1, 8, 1 << 16, 64, 16, 1 << 16) == block
+    # the block kernel forms every offset in 64 bits: strides of 2^24 elements and more stay on it
+    assert M.ssd_plan(1, 8, (1 << 18) - 1, 64, 64, 1) == block
+    assert M.ssd_plan(1, 8, 1 << 18, 64, 64, 1) == block                # nheads * headdim = 2^24
+    assert M.ssd_plan(1, 8, (1 << 18) + 1, 64, 64, 1) == block
+    assert M.ssd_plan(1, 8, 1 << 20, 64, 16, 1 << 20) == block          # ngroups * dstate = 2^24
+    # MIMO: the block kernel takes ranks 1, 2, 4, 8 and 16; others run through the update kernel
+    for r in (1, 2, 4, 8, 16):
+        assert M.ssd_mimo_plan(8, 4096, 32, 64, 128, 1, r) == block
+    for r in (3, 5, 32, 64):
+        assert M.ssd_mimo_plan(8, 4096, 32, 64, 128, 1, r) == rec
+    assert M.ssd_mimo_plan(1, 8, 4, 64, 64, 1, 4, io_dtype=M.MSSM_F32) == rec
+    for r, st in ((0, M.MSSM_ERR_INVALID_ARG), (-1, M.MSSM_ERR_INVALID_ARG), (65, M.MSSM_ERR_UNSUPPORTED)):
+        with pytest.raises(M.MssmError) as e:
+            M.ssd_mimo_plan(1, 8, 4, 64, 64, 1, r)
+        assert e.value.status == st
     with pytest.raises(M.MssmError):
         M.ssd_plan(1, 8, 6, 64, 64, 4)                                  # nheads % ngroups != 0
     d = M.ssd_desc(1, 8, 4, 64, 64, 1)

@@ -32,32 +32,49 @@
 // rank pair.  R = 1 is the single-input form.
 //
 // Mapping onto the chip.  A block is 64 rows.  One workgroup of 8 waves owns
-// one (b, head, 64-wide headdim slice) and walks its sequence.  Wave w holds
-// headdim columns 16 (w % 4).. of the transposed state S^T[n, p] for one half
-// of the states (w / 4), in MFMA accumulators for the whole sequence, so the
-// state never leaves the chip except as final_state.  Per block
-// (v_mfma_f32_16x16x32_bf16, base-2 exponents, A pre-scaled by log2 e):
-//   G^T = B . C^T   the 10 causal 16x16 tiles dealt out over the waves
-//   M   = G o exp2(s_t - s_s) o w_s  ->  LDS, bf16 hi/lo pair, [t][s]
-//   Y^T = exp2(s_t) (S . C^T) + X^T . M^T        (p x t; each wave of a pair reads
-//                   out its half of the states for all row tiles, keeps two and
-//                   hands the partner the other two through LDS)
-//   S^T = exp2(s_Q) S^T + B^T . Xw               (n x p, k = rows)
-// x, B and C enter the matrix cores exactly (bf16 inputs).  The three computed
-// operands -- the state, the mask and the weighted inputs -- are each split
-// into hi = bf16(v), lo = bf16(v - hi), about 16 significant bits.
+// one (b, head, 64-wide headdim slice) and walks its sequence; the waves take
+// two roles, one of each on every SIMD, so that the two waves sharing a SIMD
+// do different work at the same time:
+//  * state waves 0-3: wave w holds headdim columns 16 w .. 16 w + 15 of the
+//    transposed state S^T[n, p] for all states, in MFMA accumulators for the
+//    whole sequence (the state never leaves the chip except as final_state);
+//    they read out the carried state, update it, and finish the outputs;
+//  * mask waves 4-7: wave 4 + t forms the mask tiles of row tile t and the
+//    per-row arrays (decay sums and weights) of the next block.
+// Per block (v_mfma_f32_16x16x32_bf16, base-2 exponents, A pre-scaled by log2 e):
+//   G^T = B . C^T   (s x t) all 16 tiles, tiles past the diagonal come out 0
+//   M   = G o exp2(s_t - s_s) o w_s  ->  LDS as bf16 hi/lo, double-buffered
+//   Y^T = exp2(s_t) (S . C^T) + X^T . M^T   (p x t)
+//   S^T = exp2(s_Q) S^T + B^T . Xw          (n x p, k = rows)
+// The X^T . M^T term of a block, with D x, the gate and the store, is done in
+// the next block's pass of the state waves, once the barrier that starts it
+// has published the mask: one barrier per block.  x, B and C enter the matrix
+// cores exactly (bf16 inputs).  The three computed operands -- the state, the
+// mask and the weighted inputs -- are each split into hi = bf16(v),
+// lo = bf16(v - hi), about 16 significant bits: with one bf16 rounding the
+// outputs drift past a 2e-2 relative bound in rare elements (the mask enters
+// sums whose terms are much larger than the result).
 //
 // Data movement.  Every input reaches LDS by direct global->LDS loads
-// (global_load_lds), in natural row-major order with each row's 16-byte
-// chunks XOR-swizzled by the row index, so the reads below are free of bank
-// conflicts: x two blocks ahead, B and C one block ahead, delta and lam three
-// blocks ahead.  Fragments whose contraction index is the row index (B^T for
-// the state update, X^T for the intra-block product) come from transposing
-// LDS reads (ds_read_b64_tr_b16): in each 16-lane group, lane j receives
-// element j of each of the four 4-element pieces that lanes 4k..4k+3 point
-// at.  Each wave waits for its own loads (s_waitcnt vmcnt) and a barrier makes
-// them visible; the compiler sees no loads into registers inside the loop, so
-// nothing drains the prefetch.
+// (global_load_lds), shared out over all eight waves (a wave whose load finds
+// the memory pipeline full waits, so one wave issuing them all would stall):
+// x two blocks ahead, B and C one block ahead, delta and lam three blocks
+// ahead.  Each tile in LDS is a plane of 64 rows x 128 bytes with row r's
+// 16-byte chunk c kept at chunk c ^ (r % 8): 16-byte reads of one chunk from
+// 16 consecutive rows and transposing reads of 8 consecutive rows are then both
+// free of bank conflicts (B and C, 256-byte rows at 128 states, are split into
+// two planes).  Fragments whose contraction index is the row index (B^T for
+// the state update, X^T for the intra-block product) come from transposing LDS
+// reads (ds_read_b64_tr_b16): in each 16-lane group, lane j receives element j
+// of each of the four 4-element pieces that lanes 4k..4k+3 point at.  The
+// state's readout fragments are brought into natural k order by two cross-lane
+// swaps (v_permlane32_swap, v_permlane16_swap), so C is read 16 bytes at a
+// time; the mask is stored in the k order of the X^T fragments for the same
+// reason.  Each wave waits for its own loads (s_waitcnt vmcnt) and a barrier
+// makes them visible; the loops hold no other vector-memory operations than
+// these loads and the output stores, so the counts are exact and nothing
+// drains the prefetch.  Within a pass, each phase issues all of its LDS reads
+// before their first use.
 #include <type_traits>
 
 #include "internal.h"
@@ -69,10 +86,6 @@ constexpr float kLog2e = 1.44269504088896340736f;
 constexpr int kWave = 64;
 constexpr int QB = 64;          // rows per block
 constexpr int PB = 64;          // headdim slice per unit
-constexpr int XROW = PB * 2;    // bytes of an x row in LDS (8 chunks of 16 bytes)
-constexpr int XBLK = QB * XROW;
-constexpr int MROW = (QB + 4) * 2;   // bytes of a mask row (padded: 16 rows hit distinct banks)
-constexpr int MBLK = QB * MROW;
 constexpr int NXS = 3;          // x / z ring: two blocks ahead
 constexpr int NBS = 2;          // B / C ring: one block ahead
 constexpr int NDS = 4;          // delta / lam ring: three blocks ahead
@@ -87,7 +100,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 __device__ __forceinline__ float exp2_hw(float v) { return __builtin_amdgcn_exp2f(v); }
@@ -127,23 +139,24 @@ __device__ __forceinline__ bf16x8 cat(const u32x2 a, const u32x2 b) {
   return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
 }
 
-// global -> LDS: lane l's 16 bytes land at lds_base + 16 l; a 2-byte load lands zero-extended in the
-// dword at lds_base + 4 l.  lds_base is wave-uniform (it goes to M0).  Written as asm so that the
+// global -> LDS: lane l's 16 bytes land at LDS offset lds + 16 l; a 2-byte load lands zero-extended in the
+// dword at lds + 4 l.  lds is wave-uniform (it goes to M0); it is formed as an integer from each array's
+// base, since a pointer chosen at run time among LDS buffers would be cast with a null check.  Written as asm so that the
 // compiler does not track these loads: it would otherwise wait for all of them before the transposing
 // LDS reads of the same buffers, draining the prefetch; completion is waited for explicitly (wait_vm)
 // before the barrier that publishes a block.  The asm has no outputs (the data goes to LDS), so no
 // register can be overwritten while a load is in flight.
-__device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
-  return __builtin_amdgcn_readfirstlane(
-      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)const_cast<unsigned char*>(p))));
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  // the low half of a flat address into LDS is the LDS offset
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
 }
-__device__ __forceinline__ void dma16(const void* g, unsigned char* lds_base) {
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(g), "s"(lds_addr(lds_base)) : "memory", "m0");
+               :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
 }
-__device__ __forceinline__ void dma2(const void* g, unsigned char* lds_base) {
+__device__ __forceinline__ void dma2(const void* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_ushort %0, off"
-               :: "v"(g), "s"(lds_addr(lds_base)) : "memory", "m0");
+               :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
 }
 
 // Barrier without a memory fence: LDS writes of this wave are complete
@@ -154,11 +167,21 @@ __device__ __forceinline__ void block_barrier() {
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
-// wait until at most n (0, 1 or 2; wave-uniform) of this wave's vector-memory operations are outstanding
+// wait until at most n (0..8, wave-uniform) of this wave's vector-memory operations are outstanding.  Loads
+// and stores share the counter and retire in issue order, so n counts the stores issued after the load
+// waited for as well.
 __device__ __forceinline__ void wait_vm(int n) {
-  if (n >= 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-  else if (n == 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  switch (n) {
+    case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+    case 7: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
+    case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
 }
 
 // DPP-moved copy of v (lanes outside the row mask, or whose source lane is out
@@ -184,58 +207,54 @@ struct SSDParams {
   int nps;       // headdim slices per head (P / 64)
 };
 
-// Causal G^T tiles (s-tile jt, t-tile it) handled by each of the 8 waves, packed (jt << 2) | it, -1 when
-// none: waves 0 and 1 take two (a diagonal and an off-diagonal tile), the others one.  (A switch, so the
-// choice is made with immediates: a table in memory would be a load inside the block loop.)
-__device__ __forceinline__ int tile_of(int w, int k) {
-  switch (w * 2 + k) {
-    case 0: return 0x00; case 1: return 0x0b;
-    case 2: return 0x05; case 3: return 0x03;
-    case 4: return 0x0a;
-    case 6: return 0x0f;
-    case 8: return 0x01;
-    case 10: return 0x06;
-    case 12: return 0x02;
-    case 14: return 0x07;
-    default: return -1;
-  }
-}
-
 constexpr int kWaves = 8;
 constexpr int kThreads = kWave * kWaves;
+constexpr int PROW = 128;                // bytes of an LDS tile row: 64 bf16
+constexpr int PLANE = QB * PROW;         // one 64-row tile (8 KB)
+
+// Every tile in LDS is a plane of 64 rows x 128 bytes whose row r keeps its 16-byte chunk c at chunk
+// c ^ (r % 8).  Both access shapes used below are then free of bank conflicts: 16-byte reads of one chunk
+// from 16 consecutive rows, and transposing reads of 8 consecutive rows.
+__device__ __forceinline__ int swz(int r, int c) { return r * PROW + ((c ^ (r & 7)) << 4); }
+
+// What a state wave keeps from the main pass of a block for its finish in the next one: the carried-state
+// readout of the four row tiles, the X^T fragments, and x (z) at the output points.
+struct Carry {
+  f32x4 y[4];
+  bf16x8 xf0, xf1;
+  u32x2 xv[4], zv[4];
+};
 
 // MFMA 16x16x32 lane layout: A row / B column = lane % 16, k slots 8(lane/16)..+7;
 // accumulator element v of a lane is row 4 (lane / 16) + v, column lane % 16.
-template <int NP, bool TRAP>
+template <int NP, bool TRAP, bool EPI>
 __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
   static_assert(NP == 64 || NP == 128, "padded state count");
-  constexpr int NTH = NP / 32;          // 16-row state tiles per wave (its half of the states)
-  constexpr int NKH = NP / 64;          // 32-wide k blocks in a half
-  constexpr int NKB = NP / 32;          // 32-wide k blocks over all states (C . B^T)
-  constexpr int CPR = NP / 8;           // 16-byte chunks per B/C row
-  constexpr int BROW = NP * 2;
-  constexpr int BBLK = QB * BROW;
-  constexpr int BC_PER_WAVE = 2 * CPR / kWaves;   // B then C, 64 / CPR rows per load
-  static_assert(2 * CPR % kWaves == 0, "B/C loads split evenly over the waves");
+  constexpr int NT = NP / 16;               // 16-row state tiles of a state wave
+  constexpr int NKB = NP / 32;              // 32-wide k blocks over the states
+  constexpr int NPL = NP / 64;              // planes of a B or C block
+  constexpr int BBLK = NPL * PLANE;
+  constexpr int NBC = 2 * NPL * 8;          // 1 KB loads of a block's B and C (8 rows of one plane each)
+  constexpr int BC_PER = NBC / 8;           // per wave
+  static_assert(NBC % 8 == 0, "B/C loads split evenly over the waves");
 
-  __shared__ __attribute__((aligned(16))) unsigned char xs[NXS][XBLK];
-  __shared__ __attribute__((aligned(16))) unsigned char zs[NXS][XBLK];
+  __shared__ __attribute__((aligned(16))) unsigned char xs[NXS][PLANE];
+  __shared__ __attribute__((aligned(16))) unsigned char zs[EPI ? NXS : 1][EPI ? PLANE : 16];
   __shared__ __attribute__((aligned(16))) unsigned char bs[NBS][BBLK];
   __shared__ __attribute__((aligned(16))) unsigned char cs_[NBS][BBLK];
   __shared__ __attribute__((aligned(16))) uint32_t dls[NDS][QB];            // delta bits, one per row
   __shared__ __attribute__((aligned(16))) uint32_t lls[TRAP ? NDS : 1][QB];   // lam bits
-  __shared__ __attribute__((aligned(16))) unsigned char ms[2][MBLK];         // mask hi / lo, [t][s]
-  __shared__ __attribute__((aligned(16))) f32x4 xc[kWaves][2][kWave];        // partial readouts for the partner
+  __shared__ __attribute__((aligned(16))) unsigned char ms[2][2][PLANE];     // mask of even / odd blocks: hi, lo
   __shared__ __attribute__((aligned(16))) float arr[2][NARR][QB];
   static_assert(sizeof(xs) + sizeof(zs) + sizeof(bs) + sizeof(cs_) + sizeof(dls) + sizeof(lls) + sizeof(ms) +
-                    sizeof(xc) + sizeof(arr) <= 160 * 1024,
+                    sizeof(arr) <= 160 * 1024,
                 "LDS budget");
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform, in a scalar register
-  const int pt = w % 4;                // 16-wide headdim tile of this wave
-  const int nh = w / 4;                // half of the states it holds
+  const bool state_wave = w < 4;       // waves 0-3 hold the state; waves 4-7 form the mask and the arrays
+  const int pt = w & 3;                // state wave: 16-wide headdim tile; mask wave: 16-row t tile
   const int lc = lane % 16;
   const int q = lane / 16;
 
@@ -258,10 +277,9 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
   const int64_t nblocks = (L * R + QB - 1) / QB;
   const int last_nv = static_cast<int>(L * R - (nblocks - 1) * QB);   // rows of the last block
 
-  // ---- zero what a load may leave untouched: B/C columns past N, mask tiles above the diagonal, and
-  // whatever an earlier kernel left in the rings ----
+  // ---- zero what a load may leave untouched: B/C columns past N, and whatever an earlier kernel left ----
   {
-    unsigned char* regions[5] = {&xs[0][0], &zs[0][0], &bs[0][0], &cs_[0][0], &ms[0][0]};
+    unsigned char* regions[5] = {&xs[0][0], &zs[0][0], &bs[0][0], &cs_[0][0], &ms[0][0][0]};
     const int sizes[5] = {static_cast<int>(sizeof(xs)), static_cast<int>(sizeof(zs)), static_cast<int>(sizeof(bs)),
                           static_cast<int>(sizeof(cs_)), static_cast<int>(sizeof(ms))};
 #pragma unroll
@@ -270,9 +288,6 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
         *reinterpret_cast<u32x4*>(regions[r] + e) = u32x4{0, 0, 0, 0};
   }
 
-  // ---- per-lane offsets of the direct loads, fixed for the whole sequence (a block's are these plus the
-  // block's first step times the step stride; the last block, when partial, recomputes them with its rows
-  // clamped to its last valid row, whose weights are then 0) ----
   const int64_t xstep = H * R * P, bcstep = G * R * N;
   const uint16_t* const x0 = p.x + (b * L * H + h) * R * P + p0;         // step 0, rank 0 of this unit
   const uint16_t* const z0 = (has_z ? p.z : p.x) + (b * L * H + h) * R * P + p0;
@@ -281,143 +296,72 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
   const uint16_t* const d0 = p.delta + b * L * H + h;
   const uint16_t* const l0 = TRAP ? p.lam + b * L * H + h : nullptr;
   uint16_t* const o0 = p.out + (b * L * H + h) * R * P + p0;
-  auto x_off = [&](int nv) {   // this wave's x row group: rows 8w .. 8w + 7
-    const int i = 8 * w + lane / 8;
-    const int ic = i < nv ? i : nv - 1;
-    const int c = (lane % 8) ^ (i % 8);   // logical chunk stored at this lane's physical chunk
-    return static_cast<int64_t>(ic >> rs) * xstep + (ic & (R - 1)) * P + 8 * c;
-  };
-  int64_t bc_o[BC_PER_WAVE];
-  bool bc_ok[BC_PER_WAVE];
-  auto bc_off = [&](int nv) {
-#pragma unroll
-    for (int jj = 0; jj < BC_PER_WAVE; ++jj) {
-      const int j = (w * BC_PER_WAVE + jj) % CPR;   // row group within B (first half) or C (second half)
-      const int i = j * (kWave / CPR) + lane / CPR;
-      const int ic = i < nv ? i : nv - 1;
-      const int c = (lane % CPR) ^ (i % CPR);
-      bc_ok[jj] = 8 * c < Ni;
-      bc_o[jj] = static_cast<int64_t>(ic >> rs) * bcstep + (ic & (R - 1)) * N + 8 * c;
-    }
-  };
-  auto dl_off = [&](int nv) {
-    const int ic = lane < nv ? lane : nv - 1;
-    return static_cast<int64_t>(ic >> rs) * H;
-  };
-  const int64_t xo_full = x_off(QB);
-  const int64_t do_full = dl_off(QB);
-  bc_off(QB);
-  int64_t bo_full[BC_PER_WAVE];
-#pragma unroll
-  for (int jj = 0; jj < BC_PER_WAVE; ++jj) bo_full[jj] = bc_o[jj];
-
-  // x (and z): one 1 KB load per wave per block (8 rows)
-  auto issue_x = [&](int64_t k, int slot) {
-    const int64_t o = (k + 1 < nblocks ? xo_full : x_off(last_nv)) + k * spb * xstep;
-    dma16(x0 + o, &xs[slot][w * 1024]);
-    if (has_z) dma16(z0 + o, &zs[slot][w * 1024]);
-  };
-  auto issue_bc = [&](int64_t k, int slot) {
-    if (k + 1 == nblocks) bc_off(last_nv);
-    const int64_t ko = k * spb * bcstep;
-#pragma unroll
-    for (int jj = 0; jj < BC_PER_WAVE; ++jj) {
-      const int idx = w * BC_PER_WAVE + jj;
-      const bool isC = idx >= CPR;
-      const int j = idx % CPR;
-      const int64_t o = (k + 1 == nblocks ? bc_o[jj] : bo_full[jj]) + ko;
-      if (bc_ok[jj]) dma16((isC ? C0 : B0) + o, isC ? &cs_[slot][j * 1024] : &bs[slot][j * 1024]);
-    }
-  };
-  // delta (and lam): one element per row, 2-byte loads into dword slots, by waves 0 (and 1)
-  auto issue_dl = [&](int64_t k, int slot) {
-    const int64_t o = (k + 1 < nblocks ? do_full : dl_off(last_nv)) + k * spb * H;
-    if (w == 0) dma2(d0 + o, reinterpret_cast<unsigned char*>(&dls[slot][0]));
-    if constexpr (TRAP) {
-      if (w == 1) dma2(l0 + o, reinterpret_cast<unsigned char*>(&lls[slot][0]));
-    }
-  };
-
-  // ---- per-row arrays of block k (wave 0) ----
-  auto make_arrays = [&](int64_t k, int slot, int slot_next) {
-    const int nv = k + 1 < nblocks ? QB : last_nv;
-    const bool valid = lane < nv;
-    const float d = valid ? __uint_as_float(dls[slot][lane] << 16) : 0.f;
-    float v = (lane & (R - 1)) == 0 ? d * a2 : 0.f;   // the step's decay enters at its first row
-    v += dppf<0x111, 0xf>(v);   // row_shr:1
-    v += dppf<0x112, 0xf>(v);   // row_shr:2
-    v += dppf<0x114, 0xf>(v);   // row_shr:4
-    v += dppf<0x118, 0xf>(v);   // row_shr:8
-    v += dppf<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
-    v += dppf<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
-    const float cs_end = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), kWave - 1));
-    float wf = d, wd = d;
-    if constexpr (TRAP) {
-      const float lm = valid ? __uint_as_float(lls[slot][lane] << 16) : 0.f;
-      // the next step's first row: in this block, or row 0 of the next block
-      const int jn = (lane | (R - 1)) + 1;
-      float dn = 0.f, ln = 0.f;
-      if (jn < QB) {
-        if (jn < nv) {
-          dn = __uint_as_float(dls[slot][jn] << 16);
-          ln = __uint_as_float(lls[slot][jn] << 16);
-        }
-      } else if (k + 1 < nblocks) {
-        dn = __uint_as_float(dls[slot_next][0] << 16);
-        ln = __uint_as_float(lls[slot_next][0] << 16);
-      }
-      wd = lm * d;
-      wf = __builtin_fmaf(1.f - ln, dn, wd);
-    }
-    float* A_ = &arr[k & 1][0][0];
-    A_[A_CS * QB + lane] = v;
-    A_[A_ECS * QB + lane] = exp2_hw(v);
-    A_[A_WF * QB + lane] = wf;
-    A_[A_WD * QB + lane] = wd;
-    A_[A_WL * QB + lane] = exp2_hw(cs_end - v) * wf;
-  };
-
-  // ---- this wave's half of the state: S^T tiles, rows n = NP/2 nh + 16 i + 4 q + v, column p = p0 + 16 pt + lc
-  const int64_t prow = p0 + 16 * pt + lc;
-  const int nbase = (NP / 2) * nh;
-  f32x4 S[NTH];
-#pragma unroll
-  for (int i = 0; i < NTH; ++i) {
-    const int n0 = nbase + 16 * i + 4 * q;
-    if (p.h0 != nullptr && n0 < Ni) {
-      const float4 v = *reinterpret_cast<const float4*>(&p.h0[((b * H + h) * P + prow) * N + n0]);
-      S[i] = f32x4{v.x, v.y, v.z, v.w};
-    } else {
-      S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < NTH; ++i) asm volatile("" : "+v"(S[i]));   // h0 has arrived before any direct load is issued
-
-  // bit masks of the diagonal tile (fixed per lane): element v is row s = 4q + v, column t = lc of the
-  // tile; it is kept up to the diagonal (an earlier or the same step), and takes the own-step weight on
-  // it (the same step).  Bitwise selects: above the diagonal exp2(s_t - s_s) may overflow, and a
-  // multiply by 0 would turn that into NaN.
-  uint32_t keep[4], own[4];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int ss = (4 * q + v) >> rs, st = lc >> rs;
-    keep[v] = ss <= st ? 0xffffffffu : 0u;
-    own[v] = ss == st ? 0xffffffffu : 0u;
-    asm volatile("" : "+v"(keep[v]), "+v"(own[v]));
-  }
-
-  // row tiles this wave finishes (the partner finishes the other two): {0, 3} or {1, 2}, equal causal work
-  const int ja = nh == 0 ? 0 : 1, jb = nh == 0 ? 3 : 2;
-  const int partner = w ^ 4;
+  const uint32_t xs_a = lds_addr(&xs[0][0]), zs_a = lds_addr(&zs[0][0]), bs_a = lds_addr(&bs[0][0]),
+                 cs_a = lds_addr(&cs_[0][0]), dls_a = lds_addr(&dls[0][0]), lls_a = lds_addr(&lls[0][0]);
 
   // ring slots, advanced by counters (no division in the loop)
   int sx = 0, sb = 0, sd = 0;   // slots of block k in the x, B/C and delta rings
   auto nxt = [](int v, int n) { return v + 1 == n ? 0 : v + 1; };
+  auto advance = [&]() {
+    sx = nxt(sx, NXS);
+    sb = nxt(sb, NBS);
+    sd = nxt(sd, NDS);
+  };
 
-  // ---- prologue: loads of blocks 0..2 in the order of three earlier iterations ----
+  // ---- direct loads, shared out over all eight waves: wave w loads x (z) rows 8 w .. 8 w + 7, and B/C loads
+  // BC_PER w .. +BC_PER-1 (8 rows of one plane each); waves 4 and 5 load delta and lam ----
+  // a lane's row within its 8-row group and its logical 16-byte chunk (stored at chunk lane % 8 of the row);
+  // a block's offsets are formed at issue time, rows past the block's valid ones clamped to its last
+  const int lrow = lane / 8;
+  auto blk_off = [&](int64_t k, int row, int64_t step, int64_t rank_stride) {
+    const int nv = k + 1 < nblocks ? QB : last_nv;
+    const int ic = row < nv ? row : nv - 1;
+    return (k * spb + (ic >> rs)) * step + (ic & (R - 1)) * rank_stride + 8 * ((lane % 8) ^ (row % 8));
+  };
+  auto issue_x = [&](int64_t k, int slot) {
+    const int64_t o = blk_off(k, 8 * w + lrow, xstep, P);
+    dma16(x0 + o, xs_a + slot * PLANE + w * 1024);
+    if constexpr (EPI) {
+      if (has_z) dma16(z0 + o, zs_a + slot * PLANE + w * 1024);
+    }
+  };
+  auto issue_bc = [&](int64_t k, int slot) {
+#pragma unroll
+    for (int jj = 0; jj < BC_PER; ++jj) {
+      const int idx = w * BC_PER + jj;
+      const bool isC = idx >= NPL * 8;
+      const int rem = idx % (NPL * 8), pl = rem / 8, gr = rem % 8;
+      const int col = pl * 64 + 8 * ((lane % 8) ^ lrow);
+      if (col < Ni)
+        dma16((isC ? C0 : B0) + blk_off(k, 8 * gr + lrow, bcstep, N) + pl * 64,
+              (isC ? cs_a : bs_a) + slot * BBLK + pl * PLANE + gr * 1024);
+    }
+  };
+  auto issue_dl = [&](int64_t k, int slot) {
+    const int nv = k + 1 < nblocks ? QB : last_nv;
+    const int ic = lane < nv ? lane : nv - 1;
+    const int64_t o = static_cast<int64_t>(ic >> rs) * H + k * spb * H;
+    if (w == 4) dma2(d0 + o, dls_a + slot * QB * 4);
+    if constexpr (TRAP) {
+      if (w == 5) dma2(l0 + o, lls_a + slot * QB * 4);
+    }
+  };
+  const int nxl = (EPI && has_z) ? 2 : 1;   // x (z) loads of a wave per block
+  // loads of later blocks issued at the top of block k: delta (lam) of k + 3, B/C of k + 1, x (z) of k + 2;
+  // returns the x (z) loads issued (they may stay in flight at the next top)
+  auto issue_ahead = [&](int64_t k) {
+    if (k + 3 < nblocks) issue_dl(k + 3, nxt(nxt(nxt(sd, NDS), NDS), NDS));
+    if (k + 1 < nblocks) issue_bc(k + 1, nxt(sb, NBS));
+    if (k + 2 < nblocks) {
+      issue_x(k + 2, nxt(nxt(sx, NXS), NXS));
+      return nxl;
+    }
+    return 0;
+  };
+
+  // ---- prologue (all waves): loads of blocks 0..2 in the order of three earlier iterations ----
   block_barrier();   // the zeroing is done before any load lands
-  int nx_prev = 0;
+  int vm_keep = 0;
   if (nblocks > 0) {
     issue_dl(0, 0);
     if (nblocks > 1) issue_dl(1, 1);
@@ -426,197 +370,387 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
     issue_bc(0, 0);
     if (nblocks > 1) {
       issue_x(1, 1);
-      nx_prev = has_z ? 2 : 1;
+      vm_keep = nxl;
     }
-    wait_vm(nx_prev);
+    wait_vm(vm_keep);
     block_barrier();
-    if (w == 0) make_arrays(0, 0, 1);
   }
 
-  for (int64_t k = 0; k < nblocks; ++k) {
-    const int nv = k + 1 < nblocks ? QB : last_nv;
-    wait_vm(nx_prev);
-    block_barrier();   // block k's data and arrays are in LDS; every wave is done with block k - 1
-    {
-      int s3 = nxt(nxt(nxt(sd, NDS), NDS), NDS), s2 = nxt(nxt(sx, NXS), NXS);
-      if (k + 3 < nblocks) issue_dl(k + 3, s3);
-      if (k + 1 < nblocks) issue_bc(k + 1, nxt(sb, NBS));
-      nx_prev = 0;
-      if (k + 2 < nblocks) {
-        issue_x(k + 2, s2);
-        nx_prev = has_z ? 2 : 1;
+  if (!state_wave) {
+    // =========================== mask waves ===========================
+
+    // per-row arrays of block k (every loading wave computes them and writes the same values)
+    auto make_arrays = [&](int64_t k, int slot, int slot_next) {
+      const int nv = k + 1 < nblocks ? QB : last_nv;
+      const bool valid = lane < nv;
+      const float d = valid ? __uint_as_float(dls[slot][lane] << 16) : 0.f;
+      float v = (lane & (R - 1)) == 0 ? d * a2 : 0.f;   // the step's decay enters at its first row
+      v += dppf<0x111, 0xf>(v);   // row_shr:1
+      v += dppf<0x112, 0xf>(v);   // row_shr:2
+      v += dppf<0x114, 0xf>(v);   // row_shr:4
+      v += dppf<0x118, 0xf>(v);   // row_shr:8
+      v += dppf<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
+      v += dppf<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
+      const float cs_end = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), kWave - 1));
+      float wf = d, wd = d;
+      if constexpr (TRAP) {
+        const float lm = valid ? __uint_as_float(lls[slot][lane] << 16) : 0.f;
+        // the next step's first row: in this block, or row 0 of the next block
+        const int jn = (lane | (R - 1)) + 1;
+        float dn = 0.f, ln = 0.f;
+        if (jn < QB) {
+          if (jn < nv) {
+            dn = __uint_as_float(dls[slot][jn] << 16);
+            ln = __uint_as_float(lls[slot][jn] << 16);
+          }
+        } else if (k + 1 < nblocks) {
+          dn = __uint_as_float(dls[slot_next][0] << 16);
+          ln = __uint_as_float(lls[slot_next][0] << 16);
+        }
+        wd = lm * d;
+        wf = __builtin_fmaf(1.f - ln, dn, wd);
       }
+      float* A_ = &arr[k & 1][0][0];
+      A_[A_CS * QB + lane] = v;
+      A_[A_ECS * QB + lane] = exp2_hw(v);
+      A_[A_WF * QB + lane] = wf;
+      A_[A_WD * QB + lane] = wd;
+      A_[A_WL * QB + lane] = exp2_hw(cs_end - v) * wf;
+    };
+
+    // mask tiles: G^T = B . C^T for s tiles 0..3 and t tile pt, decayed and weighted; element v of s tile sj
+    // is row s = 16 sj + 4 q + v, column t = 16 pt + lc.  Kept up to the diagonal (an earlier or the same
+    // step), with the own-step weight on it (the same step); past the diagonal the exponent takes a bias
+    // of -inf, so the element comes out 0 (a multiply by 0 could meet exp2 = inf there).
+    float kbias[4][4];
+    uint32_t ownm[4][4];
+#pragma unroll
+    for (int sj = 0; sj < 4; ++sj)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int ss = (16 * sj + 4 * q + v) >> rs, st = (16 * pt + lc) >> rs;
+        kbias[sj][v] = ss <= st ? 0.f : -__builtin_inff();
+        ownm[sj][v] = ss == st ? 0xffffffffu : 0u;
+      }
+    // 16-byte chunk (4 kb + q) of row 16 j + lc: the row tile part (16 j rows) and the plane (kb / 2) are
+    // constants of each read
+    int rd[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) rd[hh] = swz(lc, 4 * hh + q);
+    // The mask is stored as M^T: row t, and within each 32-row k block the 8 s values a lane of group q
+    // contracts, in the order of the X^T fragments (s = 32 kb + 16 (e / 4) + 4 q + e % 4 in slot 8 q + e)
+    // G^T fragments of block k: C rows of t tile pt, B rows of s tiles 0..3 (all reads issued first)
+    struct GFrag { bf16x8 c[NKB], b[4][NKB]; };
+    auto g_reads = [&](const GFrag*, int64_t) {
+      GFrag f;
+      const unsigned char* Bk = &bs[sb][0];
+      const unsigned char* Ck = &cs_[sb][0] + 16 * pt * PROW;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int po = (kb / 2) * PLANE;
+        f.c[kb] = lds_ld<bf16x8>(Ck, po + rd[kb % 2]);
+#pragma unroll
+        for (int sj = 0; sj < 4; ++sj) f.b[sj][kb] = lds_ld<bf16x8>(Bk, po + 16 * sj * PROW + rd[kb % 2]);
+      }
+      return f;
+    };
+    auto mask = [&](int64_t k, const GFrag& f) {
+      const float* Au = &arr[k & 1][0][0];
+      unsigned char* Mw = &ms[k & 1][0][0] + 16 * pt * PROW;
+      f32x4 gacc[4];
+#pragma unroll
+      for (int sj = 0; sj < 4; ++sj) gacc[sj] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int sj = 0; sj < 4; ++sj) gacc[sj] = mfma16(f.b[sj][kb], f.c[kb], gacc[sj]);
+      const float ct = Au[A_CS * QB + 16 * pt + lc];
+#pragma unroll
+      for (int sj = 0; sj < 4; ++sj) {
+        const int s0 = 16 * sj + 4 * q;
+        const float4 c4 = *reinterpret_cast<const float4*>(&Au[A_CS * QB + s0]);
+        const float4 f4 = *reinterpret_cast<const float4*>(&Au[A_WF * QB + s0]);
+        const float4 d4 = *reinterpret_cast<const float4*>(&Au[A_WD * QB + s0]);
+        const float cc[4] = {c4.x, c4.y, c4.z, c4.w}, ff[4] = {f4.x, f4.y, f4.z, f4.w}, dd[4] = {d4.x, d4.y, d4.z, d4.w};
+        float m[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float e = exp2_hw((ct - cc[v]) + kbias[sj][v]);
+          const float wsel = __uint_as_float((ownm[sj][v] & __float_as_uint(dd[v])) | (~ownm[sj][v] & __float_as_uint(ff[v])));
+          m[v] = gacc[sj][v] * e * wsel;
+        }
+        // s tile sj = 2 kb + hh: chunk 4 kb + q of row t, bytes 8 hh .. +7; bf16 hi and lo parts
+        const uint32_t h01 = pack2(m[0], m[1]), h23 = pack2(m[2], m[3]);
+        const uint32_t l01 = pack2(m[0] - lo_f(h01), m[1] - hi_f(h01)), l23 = pack2(m[2] - lo_f(h23), m[3] - hi_f(h23));
+        *reinterpret_cast<u32x2*>(Mw + rd[sj / 2] + 8 * (sj % 2)) = u32x2{h01, h23};
+        *reinterpret_cast<u32x2*>(Mw + PLANE + rd[sj / 2] + 8 * (sj % 2)) = u32x2{l01, l23};
+      }
+    };
+
+    if (nblocks > 0) {
+      make_arrays(0, 0, 1);
+      for (int64_t k = 0; k < nblocks; ++k) {
+        // outstanding may stay: the x (z) loads of block k + 1, issued after the B/C loads of block k
+        wait_vm(vm_keep);
+        block_barrier();
+        // the mask's LDS reads first; this wave's loads of later blocks are issued while they are in flight
+        const GFrag gf = g_reads(nullptr, k);
+        __builtin_amdgcn_sched_barrier(0);
+        vm_keep = issue_ahead(k);
+        __builtin_amdgcn_sched_barrier(0);
+        mask(k, gf);
+        make_arrays(k + 1, nxt(sd, NDS), nxt(nxt(sd, NDS), NDS));   // harmless past the last block
+        advance();
+      }
+      block_barrier();   // pairs with the state waves' last barrier
     }
+    return;
+  }
+
+  // =========================== state waves ===========================
+  // the state S^T, rows n = 16 i + 4 q + v, column p = p0 + 16 pt + lc
+  const int64_t prow = p0 + 16 * pt + lc;
+  f32x4 S[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    const int n0 = 16 * i + 4 * q;
+    if (p.h0 != nullptr && n0 < Ni) {
+      const float4 v = *reinterpret_cast<const float4*>(&p.h0[((b * H + h) * P + prow) * N + n0]);
+      S[i] = f32x4{v.x, v.y, v.z, v.w};
+    } else {
+      S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+
+  // per-lane LDS offsets (the tile and plane parts of each read are constants)
+  int rd[2];                       // 16-byte chunk 4 hh + q of row lc (C readout, mask reads)
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) rd[hh] = swz(lc, 4 * hh + q);
+  // transposing reads: the lane points at row r4 = 4 q + lc / 4 (+ 16 u + 32 kb) and four columns from
+  // 4 (lc % 4); X^T for columns 16 pt .., B^T for state tile i (columns 16 i ..)
+  const int r4 = 4 * q + lc / 4;
+  const int xt = r4 * PROW + (((2 * pt + (lc % 4) / 2) ^ (r4 & 7)) << 4) + 8 * (lc % 2);
+  int bt[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) bt[i] = r4 * PROW + (((2 * i + (lc % 4) / 2) ^ (r4 & 7)) << 4) + 8 * (lc % 2);
+  const int xo = swz(lc, 2 * pt + q / 2) + 8 * (q % 2);   // x at row lc of a tile, columns 16 pt + 4 q ..
+  int64_t oo[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int t = 16 * j + lc;
+    oo[j] = static_cast<int64_t>(t >> rs) * xstep + (t & (R - 1)) * P + 16 * pt + 4 * q;
+  }
+
+  // one block on the state waves: the finish of block k - 1 (FIN), then block k's readout, X^T fragments and
+  // state update.  Each phase issues all of its LDS reads before its first use, so their latencies overlap.
+  auto step = [&](int64_t k, Carry& c, auto fin, int nv) {
+    constexpr bool FIN = decltype(fin)::value;
     const unsigned char* Bk = &bs[sb][0];
     const unsigned char* Ck = &cs_[sb][0];
     const unsigned char* Xk = &xs[sx][0];
     const float* Au = &arr[k & 1][0][0];
 
-    // -- mask tiles: G^T = B . C^T (once per head), decayed and weighted --
+    // -- reads: mask of block k - 1 (hi, lo) --
+    bf16x8 mf[4][2][2];   // [row tile][k block][hi, lo]
+    if constexpr (FIN) {
+      const unsigned char* Mr = &ms[(k - 1) & 1][0][0];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int tl = tile_of(w, kk);
-      if (tl < 0) break;
-      const int jt = tl >> 2, it = tl & 3;
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int sr = 16 * jt + lc, tr = 16 * it + lc;
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const bf16x8 af = lds_ld<bf16x8>(Bk, sr * BROW + (((4 * kb + q) ^ (sr % CPR)) << 4));
-        const bf16x8 bf = lds_ld<bf16x8>(Ck, tr * BROW + (((4 * kb + q) ^ (tr % CPR)) << 4));
-        acc = mfma16(af, bf, acc);
-      }
-      const int t = 16 * it + lc, s0 = 16 * jt + 4 * q;
-      const float ct = Au[A_CS * QB + t];
-      const float4 c4 = *reinterpret_cast<const float4*>(&Au[A_CS * QB + s0]);
-      const float4 f4 = *reinterpret_cast<const float4*>(&Au[A_WF * QB + s0]);
-      float m[4] = {acc[0] * exp2_hw(ct - c4.x) * f4.x, acc[1] * exp2_hw(ct - c4.y) * f4.y,
-                    acc[2] * exp2_hw(ct - c4.z) * f4.z, acc[3] * exp2_hw(ct - c4.w) * f4.w};
-      if (jt == it) {
-        const float4 d4 = *reinterpret_cast<const float4*>(&Au[A_WD * QB + s0]);
-        const float wd[4] = {d4.x, d4.y, d4.z, d4.w};
+        for (int kb = 0; kb < 2; ++kb)
+          if (kb == 0 || j >= 2)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {   // same step: decay 1 and the own-step weight; later step: 0
-          const uint32_t sel = (own[v] & __float_as_uint(acc[v] * wd[v])) | (~own[v] & __float_as_uint(m[v]));
-          m[v] = __uint_as_float(sel & keep[v]);
+            for (int hl = 0; hl < 2; ++hl) mf[j][kb][hl] = lds_ld<bf16x8>(Mr, hl * PLANE + 16 * j * PROW + rd[kb]);
+    }
+    float ecs[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ecs[j] = Au[A_ECS * QB + 16 * j + lc];
+    __builtin_amdgcn_sched_barrier(0);
+
+    // -- the state as A fragments in natural k order (slot e of lane group q is n = 32 kb + 8 q + e), split
+    // into bf16 hi and lo parts: the accumulators hold rows 4 q + v of each tile, so two cross-lane swaps
+    // regroup tiles 2 kb, 2 kb + 1 --
+    bf16x8 sh[NKB], sl[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      uint32_t hw[4], lw[4];   // tile 2 kb rows (v0 v1, v2 v3), tile 2 kb + 1 rows (v0 v1, v2 v3)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int hv = 0; hv < 2; ++hv) {
+          const float a = S[2 * kb + u][2 * hv], c2 = S[2 * kb + u][2 * hv + 1];
+          const uint32_t hh = pack2(a, c2);
+          hw[2 * u + hv] = hh;
+          lw[2 * u + hv] = pack2(a - lo_f(hh), c2 - hi_f(hh));
         }
-      }
-      const uint32_t h01 = pack2(m[0], m[1]), h23 = pack2(m[2], m[3]);
-      const uint32_t l01 = pack2(m[0] - lo_f(h01), m[1] - hi_f(h01));
-      const uint32_t l23 = pack2(m[2] - lo_f(h23), m[3] - hi_f(h23));
-      *reinterpret_cast<u32x2*>(&ms[0][t * MROW + 2 * s0]) = u32x2{h01, h23};
-      *reinterpret_cast<u32x2*>(&ms[1][t * MROW + 2 * s0]) = u32x2{l01, l23};
+      auto regroup = [](const uint32_t (&v)[4]) {
+        auto s0 = __builtin_amdgcn_permlane32_swap(v[0], v[2], false, false);
+        auto s1 = __builtin_amdgcn_permlane32_swap(v[1], v[3], false, false);
+        auto t0 = __builtin_amdgcn_permlane16_swap(s0[0], s0[1], false, false);
+        auto t1 = __builtin_amdgcn_permlane16_swap(s1[0], s1[1], false, false);
+        return __builtin_bit_cast(bf16x8, u32x4{t0[0], t1[0], t0[1], t1[1]});
+      };
+      sh[kb] = regroup(hw);
+      sl[kb] = regroup(lw);
     }
 
-    // -- readout of the carried-in state over this wave's half, for all four row tiles; the two the
-    // partner finishes go to it through LDS --
-    bf16x8 sh[NKH], sl[NKH];   // state fragments (A: rows p, k = n in the accumulators' order)
+    // -- finish of block k - 1: + X^T M^T, + D x, * silu(z), store --
+    if constexpr (FIN) {
+      uint16_t* const ob = o0 + (k - 1) * spb * xstep;
 #pragma unroll
-    for (int kb = 0; kb < NKH; ++kb) {
-      const float v[8] = {S[2 * kb][0], S[2 * kb][1], S[2 * kb][2], S[2 * kb][3],
-                          S[2 * kb + 1][0], S[2 * kb + 1][1], S[2 * kb + 1][2], S[2 * kb + 1][3]};
-      split8(v, sh[kb], sl[kb]);
+      for (int j = 0; j < 4; ++j) {
+        f32x4 acc = mfma16(c.xf0, mf[j][0][0], c.y[j]);
+        acc = mfma16(c.xf0, mf[j][0][1], acc);
+        if (j >= 2) {
+          acc = mfma16(c.xf1, mf[j][1][0], acc);
+          acc = mfma16(c.xf1, mf[j][1][1], acc);
+        }
+        float y[4] = {acc[0], acc[1], acc[2], acc[3]};
+        if constexpr (EPI) {
+          const u32x2 xv = c.xv[j];
+          y[0] = __builtin_fmaf(Dh, lo_f(xv[0]), y[0]);
+          y[1] = __builtin_fmaf(Dh, hi_f(xv[0]), y[1]);
+          y[2] = __builtin_fmaf(Dh, lo_f(xv[1]), y[2]);
+          y[3] = __builtin_fmaf(Dh, hi_f(xv[1]), y[3]);
+          if (has_z) {
+            const u32x2 zv = c.zv[j];
+            const float zz[4] = {lo_f(zv[0]), hi_f(zv[0]), lo_f(zv[1]), hi_f(zv[1])};
+#pragma unroll
+            for (int v = 0; v < 4; ++v) y[v] *= zz[v] * __builtin_amdgcn_rcpf(1.f + exp2_hw(-zz[v] * kLog2e));
+          }
+        }
+        *reinterpret_cast<u32x2*>(ob + oo[j]) = u32x2{pack2(y[0], y[1]), pack2(y[2], y[3])};
+      }
     }
-    f32x4 Ya, Yb;
+
+    // -- reads: C of block k --
+    bf16x8 cfr[4][NKB];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) cfr[j][kb] = lds_ld<bf16x8>(Ck, (kb / 2) * PLANE + 16 * j * PROW + rd[kb % 2]);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // -- readout of the carried-in state for the four row tiles --
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int t = 16 * j + lc;
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < NKH; ++kb) {
-        // C[t][n0 + 4q .. +3] and C[t][n0 + 16 + 4q .. +3] of this half's k block n0 = NP/2 nh + 32 kb
-        const int cb = 4 * (NKH * nh + kb);
-        const int c1 = cb + q / 2, c2 = cb + 2 + q / 2, off = 8 * (q % 2);
-        const u32x2 a = lds_ld<u32x2>(Ck, t * BROW + ((c1 ^ (t % CPR)) << 4) + off);
-        const u32x2 bb = lds_ld<u32x2>(Ck, t * BROW + ((c2 ^ (t % CPR)) << 4) + off);
-        const bf16x8 cf = cat(a, bb);
-        acc = mfma16(sh[kb], cf, acc);
-        acc = mfma16(sl[kb], cf, acc);
+      for (int kb = 0; kb < NKB; ++kb) {
+        acc = mfma16(sh[kb], cfr[j][kb], acc);
+        acc = mfma16(sl[kb], cfr[j][kb], acc);
       }
-      const float e = Au[A_ECS * QB + t];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) acc[v] *= e;
-      if (j == ja) Ya = acc;
-      else if (j == jb) Yb = acc;
-      else xc[w][(j == (nh == 0 ? 1 : 0)) ? 0 : 1][lane] = acc;   // the partner's tiles, in its order
+      for (int v = 0; v < 4; ++v) acc[v] *= ecs[j];
+      c.y[j] = acc;
     }
+    __builtin_amdgcn_sched_barrier(0);
 
-    // -- x^T fragments of this wave's columns (rows s = 32kb + 4q + k', +16): transposed reads --
-    bf16x8 xf[2];
-    {
-      const int pc = 16 * pt + 4 * (lc % 4);    // column this lane points at
-      const int off = 2 * (pc % 8);
+    // -- reads: X^T fragments (rows s = 32 kb + 16 (e / 4) + 4 q + e % 4 in slot e), x (z) at the output
+    // points, the update weights and B^T --
+    c.xf0 = cat(lds_tr(Xk, xt), lds_tr(Xk, xt + 16 * PROW));
+    c.xf1 = cat(lds_tr(Xk, xt + 32 * PROW), lds_tr(Xk, xt + 48 * PROW));
+    if constexpr (EPI) {
+      const unsigned char* Zk = &zs[sx][0];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int s1 = 32 * kb + 4 * q + lc / 4, s2 = s1 + 16;
-        const u32x2 a = lds_tr(Xk, s1 * XROW + (((pc / 8) ^ (s1 % 8)) << 4) + off);
-        const u32x2 bb = lds_tr(Xk, s2 * XROW + (((pc / 8) ^ (s2 % 8)) << 4) + off);
-        xf[kb] = cat(a, bb);
+      for (int j = 0; j < 4; ++j) {
+        c.xv[j] = lds_ld<u32x2>(Xk, 16 * j * PROW + xo);
+        c.zv[j] = lds_ld<u32x2>(Zk, 16 * j * PROW + xo);
       }
     }
-
-    // -- state update of this half: S^T = exp2(s_Q) S^T + B^T . Xw --
-    {
-      const float dec = exp2_hw(Au[A_CS * QB + QB - 1]);
+    float4 wl[2][2];
 #pragma unroll
-      for (int i = 0; i < NTH; ++i)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) S[i][v] *= dec;
+      for (int hf = 0; hf < 2; ++hf) wl[kb][hf] = *reinterpret_cast<const float4*>(&Au[A_WL * QB + 32 * kb + 16 * hf + 4 * q]);
+    const float dec = exp2_hw(Au[A_CS * QB + QB - 1]);
+    bf16x8 btf[NT][2];
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const float4 w0 = *reinterpret_cast<const float4*>(&Au[A_WL * QB + 32 * kb + 4 * q]);
-        const float4 w1 = *reinterpret_cast<const float4*>(&Au[A_WL * QB + 32 * kb + 16 + 4 * q]);
-        const u32x4 xr = __builtin_bit_cast(u32x4, xf[kb]);
-        const float xw[8] = {lo_f(xr[0]) * w0.x, hi_f(xr[0]) * w0.y, lo_f(xr[1]) * w0.z, hi_f(xr[1]) * w0.w,
-                             lo_f(xr[2]) * w1.x, hi_f(xr[2]) * w1.y, lo_f(xr[3]) * w1.z, hi_f(xr[3]) * w1.w};
-        bf16x8 xh, xl;
-        split8(xw, xh, xl);
-        const int s1 = 32 * kb + 4 * q + lc / 4, s2 = s1 + 16;
+        const int o = (i / 4) * PLANE + 32 * kb * PROW + bt[i % 4];
+        btf[i][kb] = cat(lds_tr(Bk, o), lds_tr(Bk, o + 16 * PROW));
+      }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // -- state update: S^T = exp2(s_Q) S^T + B^T . Xw (Xw in bf16 hi and lo parts) --
 #pragma unroll
-        for (int i = 0; i < NTH; ++i) {
-          const int nc = nbase + 16 * i + 4 * (lc % 4);   // state column this lane points at
-          const int off = 2 * (nc % 8);
-          const u32x2 a = lds_tr(Bk, s1 * BROW + (((nc / 8) ^ (s1 % CPR)) << 4) + off);
-          const u32x2 bb = lds_tr(Bk, s2 * BROW + (((nc / 8) ^ (s2 % CPR)) << 4) + off);
-          const bf16x8 bt = cat(a, bb);
-          S[i] = mfma16(bt, xh, S[i]);
-          S[i] = mfma16(bt, xl, S[i]);
-        }
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) S[i][v] *= dec;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const float4 w0 = wl[kb][0], w1 = wl[kb][1];
+      const u32x4 xr = __builtin_bit_cast(u32x4, kb == 0 ? c.xf0 : c.xf1);
+      const float xw[8] = {lo_f(xr[0]) * w0.x, hi_f(xr[0]) * w0.y, lo_f(xr[1]) * w0.z, hi_f(xr[1]) * w0.w,
+                           lo_f(xr[2]) * w1.x, hi_f(xr[2]) * w1.y, lo_f(xr[3]) * w1.z, hi_f(xr[3]) * w1.w};
+      bf16x8 xh, xl;
+      split8(xw, xh, xl);
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        S[i] = mfma16(btf[i][kb], xh, S[i]);
+        S[i] = mfma16(btf[i][kb], xl, S[i]);
       }
     }
+    (void)nv;
+  };
 
-    block_barrier();   // the mask and the partner's partial readouts are complete
-
-    // -- finish two row tiles: + X^T M^T, + the partner's partial, + D x, * silu(z), store --
-    const unsigned char* Mh = &ms[0][0];
-    const unsigned char* Ml = &ms[1][0];
-    const unsigned char* Zk = &zs[sx][0];
+  // finish of the last block (its mask published)
+  auto finish_last = [&](int64_t k, const Carry& c, int nv) {
+    const unsigned char* Mr = &ms[k & 1][0][0];
+    uint16_t* const ob = o0 + k * spb * xstep;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int j = kk == 0 ? ja : jb;
-      f32x4 acc = kk == 0 ? Ya : Yb;
-      const int t = 16 * j + lc;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        if (32 * kb <= 16 * j + 15) {
-          const int o1 = t * MROW + 2 * (32 * kb + 4 * q), o2 = o1 + 32;
-          const bf16x8 mh = cat(lds_ld<u32x2>(Mh, o1), lds_ld<u32x2>(Mh, o2));
-          const bf16x8 mlo = cat(lds_ld<u32x2>(Ml, o1), lds_ld<u32x2>(Ml, o2));
-          acc = mfma16(xf[kb], mh, acc);
-          acc = mfma16(xf[kb], mlo, acc);
-        }
+    for (int j = 0; j < 4; ++j) {
+      f32x4 acc = mfma16(c.xf0, lds_ld<bf16x8>(Mr, 16 * j * PROW + rd[0]), c.y[j]);
+      acc = mfma16(c.xf0, lds_ld<bf16x8>(Mr, PLANE + 16 * j * PROW + rd[0]), acc);
+      if (j >= 2) {
+        acc = mfma16(c.xf1, lds_ld<bf16x8>(Mr, 16 * j * PROW + rd[1]), acc);
+        acc = mfma16(c.xf1, lds_ld<bf16x8>(Mr, PLANE + 16 * j * PROW + rd[1]), acc);
       }
-      const f32x4 o = xc[partner][kk][lane];
-      if (t < nv) {
-        const int pl = 16 * pt + 4 * q;   // first of this lane's 4 columns
-        const int xo = t * XROW + (((pl / 8) ^ (t % 8)) << 4) + 2 * (pl % 8);
-        const u32x2 xv = lds_ld<u32x2>(Xk, xo);
-        float y[4] = {__builtin_fmaf(Dh, lo_f(xv[0]), acc[0] + o[0]), __builtin_fmaf(Dh, hi_f(xv[0]), acc[1] + o[1]),
-                      __builtin_fmaf(Dh, lo_f(xv[1]), acc[2] + o[2]), __builtin_fmaf(Dh, hi_f(xv[1]), acc[3] + o[3])};
+      float y[4] = {acc[0], acc[1], acc[2], acc[3]};
+      if constexpr (EPI) {
+        const u32x2 xv = c.xv[j];
+        y[0] = __builtin_fmaf(Dh, lo_f(xv[0]), y[0]);
+        y[1] = __builtin_fmaf(Dh, hi_f(xv[0]), y[1]);
+        y[2] = __builtin_fmaf(Dh, lo_f(xv[1]), y[2]);
+        y[3] = __builtin_fmaf(Dh, hi_f(xv[1]), y[3]);
         if (has_z) {
-          const u32x2 zv = lds_ld<u32x2>(Zk, xo);
+          const u32x2 zv = c.zv[j];
           const float zz[4] = {lo_f(zv[0]), hi_f(zv[0]), lo_f(zv[1]), hi_f(zv[1])};
 #pragma unroll
           for (int v = 0; v < 4; ++v) y[v] *= zz[v] * __builtin_amdgcn_rcpf(1.f + exp2_hw(-zz[v] * kLog2e));
         }
-        const int64_t tt = k * spb + (t >> rs);
-        const int r = t & (R - 1);
-        *reinterpret_cast<u32x2*>(o0 + tt * xstep + r * P + pl) = u32x2{pack2(y[0], y[1]), pack2(y[2], y[3])};
       }
+      if (16 * j + lc < nv)
+        *reinterpret_cast<u32x2*>(ob + oo[j]) = u32x2{pack2(y[0], y[1]), pack2(y[2], y[3])};
     }
+  };
 
-    // -- the next block's per-row arrays (its delta and lam, and the step after it, arrived with this block) --
-    const int sd1 = nxt(sd, NDS);
-    if (w == 0 && k + 1 < nblocks) make_arrays(k + 1, sd1, nxt(sd1, NDS));
-    sx = nxt(sx, NXS);
-    sb = nxt(sb, NBS);
-    sd = sd1;
+  if (nblocks > 0) {
+    wait_vm(vm_keep);
+    block_barrier();   // block 0's data and arrays: pairs with the top of the mask waves' block 0
+    Carry c;
+    vm_keep = issue_ahead(0);
+    step(0, c, std::false_type{}, QB);
+    advance();
+    for (int64_t k = 1; k < nblocks; ++k) {
+      // outstanding may stay: the x (z) loads of block k + 1 and the four output stores of block k - 2,
+      // issued after the B/C loads of block k
+      wait_vm(vm_keep + (k >= 2 ? 4 : 0));
+      block_barrier();   // block k's data and arrays, and block k - 1's mask, are in LDS
+      vm_keep = issue_ahead(k);
+      step(k, c, std::true_type{}, QB);
+      advance();
+    }
+    block_barrier();   // the last block's mask is complete
+    finish_last(nblocks - 1, c, last_nv);
   }
 
   if (p.final_state != nullptr) {
 #pragma unroll
-    for (int i = 0; i < NTH; ++i) {
-      const int n0 = nbase + 16 * i + 4 * q;
+    for (int i = 0; i < NT; ++i) {
+      const int n0 = 16 * i + 4 * q;
       if (n0 < Ni)
         *reinterpret_cast<float4*>(&p.final_state[((b * H + h) * P + prow) * N + n0]) =
             float4{S[i][0], S[i][1], S[i][2], S[i][3]};
@@ -624,11 +758,17 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
   }
 }
 
-template <int NP, bool TRAP>
+template <int NP, bool TRAP, bool EPI>
 hipError_t launch_np(const SSDParams& sp, hipStream_t stream) {
   const int64_t blocks = sp.batch * sp.H * sp.nps;
-  hipLaunchKernelGGL((ssd_kernel<NP, TRAP>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream, sp);
+  hipLaunchKernelGGL((ssd_kernel<NP, TRAP, EPI>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream, sp);
   return hipGetLastError();
+}
+
+template <int NP, bool TRAP>
+hipError_t launch_gate(const SSDParams& sp, hipStream_t stream) {
+  const bool epi = sp.z != nullptr || sp.D != nullptr;
+  return epi ? launch_np<NP, TRAP, true>(sp, stream) : launch_np<NP, TRAP, false>(sp, stream);
 }
 
 }  // namespace
@@ -657,11 +797,11 @@ hipError_t ssd_launch(const SSDArgs& a, hipStream_t stream) {
   while ((1 << sp.rs) < sp.R) ++sp.rs;
   sp.nps = static_cast<int>(a.P / PB);
   if (a.lam != nullptr) {
-    if (a.N <= 64) return launch_np<64, true>(sp, stream);
-    return launch_np<128, true>(sp, stream);
+    if (a.N <= 64) return launch_gate<64, true>(sp, stream);
+    return launch_gate<128, true>(sp, stream);
   }
-  if (a.N <= 64) return launch_np<64, false>(sp, stream);
-  return launch_np<128, false>(sp, stream);
+  if (a.N <= 64) return launch_gate<64, false>(sp, stream);
+  return launch_gate<128, false>(sp, stream);
 }
 
 }  // namespace mssm

@@ -1,0 +1,87 @@
+"""Properties of the compiled SSD block kernel that its hand-written waits rely on (no GPU needed).
+
+The kernel waits for its direct global->LDS loads with explicit `s_waitcnt vmcnt(n)`, n counting the
+vector-memory operations the wave issued after the load it needs.  That count is exact only if the loop
+bodies contain no vector-memory instruction other than those loads and the output stores: a register spill
+reload, or a load the compiler adds, would let a needed load still be in flight at the barrier.  This test
+compiles the kernel source to gfx950 assembly with the library's own flags and checks every loop block
+(by the compiler's loop annotations) of every instantiation.
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "selective_state_space_17_amd", "csrc")
+ALLOWED = re.compile(r"global_load_lds_(dwordx4|ushort)|global_store_dwordx2 ")
+VMEM = re.compile(r"(global_|buffer_|scratch_|flat_)")
+
+
+def _kernels(asm: str):
+    out, name = {}, None
+    for ln in asm.split("\n"):
+        m = re.match(r"^(_ZN4mssm12_GLOBAL__N_110ssd_kernel[^:]*):", ln)
+        if m:
+            name = m.group(1)
+            out[name] = []
+            continue
+        if name and ln.startswith(".Lfunc_end"):
+            name = None
+            continue
+        if name:
+            out[name].append(ln)
+    return out
+
+
+def _loop_vmem(body):
+    inloop, seen, bad = False, 0, []
+    for ln in body:
+        if re.match(r"^(\.LBB\d+_\d+:|; %bb\.\d+:)", ln):
+            inloop = ("Loop Header" in ln) or ("in Loop:" in ln)
+            continue
+        t = ln.strip()
+        if inloop and VMEM.match(t):
+            seen += 1
+            if not ALLOWED.match(t):
+                bad.append(t)
+    return seen, bad
+
+
+@pytest.fixture(scope="module")
+def ssd_asm(tmp_path_factory):
+    from selective_state_space_17_amd.build import FLAGS, HIPCC
+    if not shutil.which(HIPCC) and not os.path.exists(HIPCC):
+        pytest.skip("hipcc not available")
+    out = str(tmp_path_factory.mktemp("asm") / "ssd_m2.s")
+    flags = [f for f in FLAGS if f not in ("-shared", "-fPIC", "-Wall", "-Wno-unused-function")]
+    subprocess.check_call([HIPCC] + flags + ["--cuda-device-only", "-S", "-I", CSRC, "-o", out,
+                           os.path.join(CSRC, "ssd_m2.hip")], stderr=subprocess.DEVNULL)
+    return open(out).read()
+
+
+def test_ssd_loops_hold_only_the_counted_memory_operations(ssd_asm):
+    ks = _kernels(ssd_asm)
+    assert len(ks) == 8, sorted(ks)   # 64/128 states x two rules x with/without the D/z epilogue
+    for name, body in ks.items():
+        seen, bad = _loop_vmem(body)
+        assert seen > 0, name
+        assert not bad, (name, bad[:4])
+
+
+def test_ssd_no_vector_register_spills(ssd_asm):
+    spills = [int(v) for v in re.findall(r"\.vgpr_spill_count:\s+(\d+)", ssd_asm)]
+    assert spills and all(v == 0 for v in spills), spills
+
+
+def test_checker_flags_an_extra_load():
+    body = [".LBB0_1:                               ; =>This Inner Loop Header: Depth=1",
+            "\tglobal_load_lds_dwordx4 v[0:1], off",
+            "\tscratch_load_dwordx2 v[4:5], off, off ; 8-byte Folded Reload",
+            "\tglobal_store_dwordx2 v[2:3], v[6:7], off",
+            "; %bb.2:",
+            "\tglobal_load_dwordx4 v[8:11], v[0:1], off"]
+    seen, bad = _loop_vmem(body)
+    assert seen == 3 and bad == ["scratch_load_dwordx2 v[4:5], off, off ; 8-byte Folded Reload"]

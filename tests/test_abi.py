@@ -629,3 +629,57 @@ def test_noalloc_validation():
     d = small(batch=0)
     assert M.lib.mssm_selective_scan_fwd_noalloc(ctypes.byref(d), None, None, BASE, None, None, None, None, None,
                                                  None, None, None) == M.MSSM_OK
+
+
+def _mimo_call(desc, rank, x=BASE, delta=BASE + 100 * MB, lam=BASE + 150 * MB, A=BASE + 200 * MB, B=BASE + 300 * MB,
+               C=BASE + 400 * MB, D=None, z=None, h0=None, out=BASE + 500 * MB, fin=None):
+    return M.lib.mssm_ssd_mimo_fwd(ctypes.byref(desc), rank, x, delta, lam, A, B, C, D, z, h0, out, fin, None, 0,
+                                   None)
+
+
+def test_ssd_mimo_fwd_checks():
+    """Mamba-3 MIMO forward: the rank is checked, and every pointer rule of the SSD forward holds with x, z,
+    out spanning rank * headdim per head and B, C rank * dstate per group (nothing here reaches a kernel)."""
+    d = M.ssd_desc(2, 128, 4, 64, 64, 1, 64)
+    for r, st in ((0, M.MSSM_ERR_INVALID_ARG), (-3, M.MSSM_ERR_INVALID_ARG), (65, M.MSSM_ERR_UNSUPPORTED)):
+        assert _mimo_call(d, r) == st, r
+    assert _mimo_call(d, 4, x=None) == M.MSSM_ERR_INVALID_ARG
+    assert _mimo_call(d, 4, A=None) == M.MSSM_ERR_INVALID_ARG
+    assert _mimo_call(d, 4, x=BASE + 8) == M.MSSM_ERR_MISALIGNED
+    assert _mimo_call(d, 4, lam=BASE + 150 * MB + 1) == M.MSSM_ERR_MISALIGNED
+    assert _mimo_call(d, 4, h0=BASE + 600 * MB + 4) == M.MSSM_ERR_MISALIGNED
+    # x spans 2 * 128 * 4 * 4 * 64 bf16 = 512 KiB at rank 4: an output 256 KiB in overlaps it
+    assert _mimo_call(d, 4, out=BASE + 256 * 1024) == M.MSSM_ERR_INVALID_ARG
+    # B spans 2 * 128 * 1 * 4 * 64 bf16 = 128 KiB at rank 4: a final state 64 KiB in overlaps it
+    assert _mimo_call(d, 4, fin=BASE + 300 * MB + 64 * 1024) == M.MSSM_ERR_INVALID_ARG
+    for kw, st in ((dict(io_dtype=7), M.MSSM_ERR_UNSUPPORTED), (dict(dstate=300), M.MSSM_ERR_UNSUPPORTED),
+                   (dict(batch=-1), M.MSSM_ERR_INVALID_ARG), (dict(nheads=6, ngroups=4), M.MSSM_ERR_UNSUPPORTED)):
+        a = dict(batch=2, seqlen=128, nheads=4, headdim=64, dstate=64, ngroups=1, chunk=64, io_dtype=M.MSSM_BF16)
+        a.update(kw)
+        assert _mimo_call(M.ssd_desc(**a), 4) == st, kw
+    # no batch rows: nothing to do, null pointers allowed
+    assert _mimo_call(M.ssd_desc(0, 128, 4, 64, 64, 1, 64), 4, x=None, delta=None, lam=None, B=None, C=None,
+                      out=None) == M.MSSM_OK
+
+
+def test_ssd_mimo_state_update_checks():
+    """Mamba-3 MIMO decode step: rank, state and aliasing rules (nothing here reaches a kernel)."""
+    d = M.ssd_desc(2, 1, 4, 64, 64, 1, 0)
+    # state, x_prev, B_prev, x, delta, lam, A, B, C, D, z, out
+    args = [BASE + 600 * MB, BASE + 700 * MB, BASE + 800 * MB, BASE, BASE + 100 * MB, BASE + 150 * MB,
+            BASE + 200 * MB, BASE + 300 * MB, BASE + 400 * MB, None, None, BASE + 500 * MB]
+    call = lambda a, r=4, dd=d: M.lib.mssm_ssd_mimo_state_update(ctypes.byref(dd), r, *a, None)
+    for r, st in ((0, M.MSSM_ERR_INVALID_ARG), (-1, M.MSSM_ERR_INVALID_ARG), (65, M.MSSM_ERR_UNSUPPORTED)):
+        assert call(args, r) == st, r
+    bad = list(args); bad[0] = None
+    assert call(bad) == M.MSSM_ERR_INVALID_ARG              # state missing
+    bad = list(args); bad[0] = BASE + 600 * MB + 2
+    assert call(bad) == M.MSSM_ERR_MISALIGNED               # state misaligned
+    bad = list(args); bad[11] = BASE + 600 * MB
+    assert call(bad) == M.MSSM_ERR_INVALID_ARG              # out aliases the state
+    bad = list(args); bad[11] = BASE + 1024
+    assert call(bad) == M.MSSM_ERR_INVALID_ARG              # out overlaps x (rank-4 rows span 4 KiB)
+    bad = list(args); bad[2] = BASE + 800 * MB + 1
+    assert call(bad) == M.MSSM_ERR_MISALIGNED               # B_prev misaligned
+    # no tokens: nothing to do, null pointers allowed
+    assert call([None] * 12, 4, M.ssd_desc(2, 0, 4, 64, 64, 1, 0)) == M.MSSM_OK

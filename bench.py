@@ -30,7 +30,6 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0                      # MI355X HBM3E
-# VALU issue rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (packed fp32 is not used)
 PEAK_VALU_TSLOT = 256 * 4 * 32 * 2.4e9 / 1e12
 # VALU issue: each SIMD retires a full-rate fp32 instruction (mul, add, FMA) for 32 of a wave's 64 lanes per
 # cycle -- 256 CUs x 4 SIMDs x 32 lanes x 2.4 GHz = 78.6 T lane-slots/s, the published 157.3 TFLOP/s fp32 vector

@@ -66,7 +66,7 @@ def kernel_tags(is_ssd: bool, decode: bool = False, backward: bool = False):
         return ("scan_bwd_kernel", "bwd_reduce")
     if decode:
         return ("ssd_update_kernel", "ssdm_update_kernel") if is_ssd else ("scan_update_kernel",)
-    return ("ssd_kernel",) if is_ssd else ("wide_kernel", "scan_kernel", "carry_kernel")
+    return ("ssd_kernel",) if is_ssd else ("wide_kernel", "lane_kernel", "scan_kernel", "carry_kernel")
 
 
 def load_traffic(workload: str, is_ssd: bool, decode: bool = False, backward: bool = False):

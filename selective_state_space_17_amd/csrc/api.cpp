@@ -91,6 +91,19 @@ int validate_scan_desc(const mssm_scan_desc* d) {
   return MSSM_OK;
 }
 
+// Whether the launches of a plan fit a 1-D grid, whose size in work-items is a 32-bit count:
+// batch * K * channel-groups blocks of 256 threads (256 / G channels per block; the one-channel-per-lane
+// kernel's 64-thread blocks of 64 channels come to no more), and with a split the carry's one wave per
+// (b, c, n), four waves per block.
+bool plan_fits(const mssm_scan_desc& d, int G, int K) {
+  constexpr int64_t kMaxItems = std::numeric_limits<uint32_t>::max();
+  const int64_t cpb = 256 / G;
+  const int64_t groups = (d.dim + cpb - 1) / cpb;
+  if (d.batch > kMaxItems / 256 / K || groups > kMaxItems / 256 / K / std::max<int64_t>(d.batch, 1)) return false;
+  if (K > 1 && (d.batch * d.dim * d.dstate + 3) / 4 > kMaxItems / 256) return false;
+  return true;
+}
+
 int plan_scan(const mssm_scan_desc& d, int* K_out, int* G_out) {
   int bestK = 1, bestG = 0;
   double best = std::numeric_limits<double>::infinity();
@@ -101,23 +114,16 @@ int plan_scan(const mssm_scan_desc& d, int* K_out, int* G_out) {
     if (d.split_seq != 0) {
       const int K = static_cast<int>(std::min<int64_t>(d.split_seq, std::max<int64_t>(d.seqlen, 1)));
       const double c = scan_cost(d, G, K);
-      if (c < best) { best = c; bestK = K; bestG = G; }
+      if (c < best && plan_fits(d, G, K)) { best = c; bestK = K; bestG = G; }
       continue;
     }
     for (int K = 1; K <= 4096; K *= 2) {
       if (K > 1 && d.seqlen / K < 256) break;
       const double c = scan_cost(d, G, K);
-      if (c < best) { best = c; bestK = K; bestG = G; }
+      if (c < best && plan_fits(d, G, K)) { best = c; bestK = K; bestG = G; }
     }
   }
   if (bestG == 0) return MSSM_ERR_UNSUPPORTED;
-  // the grid is 1-D: batch * K * channel-groups blocks
-  const int64_t cpb = 256 / bestG;
-  const int64_t blocks = d.batch * bestK * ((d.dim + cpb - 1) / cpb);
-  if (blocks > std::numeric_limits<int32_t>::max()) return MSSM_ERR_UNSUPPORTED;
-  // with a split, the carry runs one wave per (b, c, n), four waves per block
-  if (bestK > 1 && (d.batch * d.dim * d.dstate + 3) / 4 > std::numeric_limits<int32_t>::max())
-    return MSSM_ERR_UNSUPPORTED;
   *K_out = bestK;
   *G_out = bestG;
   return MSSM_OK;

@@ -1019,6 +1019,250 @@ __global__ __launch_bounds__(kThreads) void wide_kernel(KernelParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// One channel per lane, every wave on its own ("lane" layout), dstate == 16.
+//
+// A workgroup is one wave.  It owns 64 consecutive channels of one batch row
+// and one sequence chunk, and lane c holds the 16 states of channel c in
+// VGPRs.  Waves share nothing, so there is no barrier: each wave copies its own
+// time tiles of x, delta, z and of B, C from HBM into its LDS with direct
+// global->LDS loads (one tile ahead, double-buffered) and lane c reads the
+// values of its channel at step s from there.  B_n and C_n reach the lanes as
+// in the one-lane-per-channel fast path above: lane n of each 16-lane row
+// reads state n's value and the update and readout take it through a DPP
+// row_newbcast operand.  Per step a lane does the 16 updates, the readout and
+// the per-(t, c) work of its own channel (widening, delta*x, the SiLU gate,
+// D*x); outputs collect in an LDS tile that is written back with 16-byte
+// stores at the start of the next tile.
+//
+// Ordering of the direct loads: a tile's loads are issued before the previous
+// tile is computed, and the wait before a tile is computed lets only the loads
+// issued after them (the next tile's) stay in flight.  Every vector-memory
+// operation issued earlier (the output stores of two tiles back) has then
+// completed as well, since the counter retires in issue order.
+// ---------------------------------------------------------------------------
+namespace lanek {
+constexpr int TT = 16;   // steps per tile
+}
+
+__device__ __forceinline__ uint32_t lds_off(const void* p) {
+  // the low half of a flat address into LDS is the LDS offset
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+// global -> LDS: lane l's 16 bytes land at LDS offset lds + 16 l (lds is wave-uniform and goes to M0).
+// Written as asm with no outputs, so the compiler neither tracks nor waits for these loads and no
+// register can be overwritten while one is in flight; completion is waited for with wait_vmcnt.
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
+}
+// wait until at most n (0..15, wave-uniform) of this wave's vector-memory operations are outstanding
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  switch (n) {
+    case 15: asm volatile("s_waitcnt vmcnt(15)" ::: "memory"); break;
+    case 14: asm volatile("s_waitcnt vmcnt(14)" ::: "memory"); break;
+    case 13: asm volatile("s_waitcnt vmcnt(13)" ::: "memory"); break;
+    case 12: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+    case 11: asm volatile("s_waitcnt vmcnt(11)" ::: "memory"); break;
+    case 10: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
+    case 9: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
+    case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+    case 7: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
+    case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
+}
+
+template <int IO, int MODE>
+__global__ __launch_bounds__(kWave) void lane_kernel(KernelParams p) {
+  using namespace lanek;
+  using T = typename IoType<IO>::T;
+  constexpr int ES = sizeof(T);
+  constexpr int EPC = 16 / ES;                    // elements per 16-byte piece
+  constexpr int RBY = kWave * ES;                 // bytes of one step of the wave's 64 channels
+  constexpr int TB = TT * RBY;                    // bytes of one tensor's tile
+  constexpr int NX = TB / 1024;                   // 16-byte loads per lane for one tensor's tile
+  constexpr int PPR = RBY / 16;                   // 16-byte pieces per step row
+  constexpr int RPI = kWave / PPR;                // step rows per load instruction
+  constexpr int BCB = TT * 16 * ES;               // bytes of B (or of C) per tile
+  constexpr int BCW = BCB / 16;                   // 16-byte pieces of B (or C) per tile
+  constexpr int NBC = (2 * BCB + 1023) / 1024;    // 16-byte loads per lane for B and C together
+  static_assert(TB % 1024 == 0 && BCB % 16 == 0, "tile geometry");
+
+  __shared__ __attribute__((aligned(16))) unsigned char xs[2][TB];
+  __shared__ __attribute__((aligned(16))) unsigned char dls[2][TB];
+  __shared__ __attribute__((aligned(16))) unsigned char zs[2][TB];
+  __shared__ __attribute__((aligned(16))) unsigned char bcs[2][NBC * 1024];   // B [t][n], then C [t][n]
+  __shared__ __attribute__((aligned(16))) T ys[TT * kWave];                   // outputs [t][c]
+
+  const int lane = threadIdx.x;
+  const int64_t bid = blockIdx.x;
+  const int cg = static_cast<int>(bid % p.ngroups);
+  const int64_t rest = bid / p.ngroups;
+  const int nchunks_here = (MODE == kFixup) ? p.K - 1 : p.K;
+  const int k = static_cast<int>(rest % nchunks_here) + p.chunk_offset;
+  const int64_t b = rest / nchunks_here;
+
+  const int64_t dim = p.dim, L = p.L;
+  const int64_t c0 = static_cast<int64_t>(cg) * kWave;
+  const int64_t c = c0 + lane;
+  const bool cvalid = c < dim;
+  const int64_t cl = cvalid ? c : dim - 1;
+  const int64_t t_begin = static_cast<int64_t>(k) * p.chunk_len;
+  const int64_t t_end = t_begin + p.chunk_len < L ? t_begin + p.chunk_len : L;
+
+  const T* __restrict__ xg = static_cast<const T*>(p.x);
+  const T* __restrict__ dg = static_cast<const T*>(p.delta);
+  const T* __restrict__ zg = static_cast<const T*>(p.z);
+  const T* __restrict__ Bg = static_cast<const T*>(p.B);
+  const T* __restrict__ Cg = static_cast<const T*>(p.C);
+  T* __restrict__ yg = static_cast<T*>(p.out);
+  const bool has_z = p.z != nullptr;
+
+  float A2[16], h[16];
+  float amax = -INFINITY;   // largest (least negative) exponent slope of the channel
+  float hmax = 0.f;         // largest |h_in| (fix-up)
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    A2[j] = cvalid ? p.A[c * 16 + j] * kLog2e : 0.f;
+    float h_init = 0.f;
+    if constexpr (MODE == kFixup) {
+      h_init = cvalid ? p.hin[((b * p.K + k) * dim + c) * 16 + j] : 0.f;
+    } else {
+      if (p.h0 != nullptr && cvalid && (MODE == kSingle || k == 0)) h_init = p.h0[(b * dim + c) * 16 + j];
+    }
+    h[j] = h_init;
+    if (cvalid) {
+      amax = fmaxf(amax, A2[j]);
+      hmax = fmaxf(hmax, fabsf(h_init));
+    }
+  }
+  bool never_exit = false;
+  if constexpr (MODE == kFixup) never_exit = cvalid && p.neg[(b * p.K + k) * dim + c] != 0;
+  const float Dv = p.D != nullptr ? p.D[cl] : 0.f;
+  float S = 0.f;
+  int negseen = 0;
+
+  // this lane's 16-byte piece of a step row: row lane / PPR of each load, channels from pc
+  const int lrow = lane / PPR;
+  int64_t pc = c0 + (lane % PPR) * EPC;
+  if (pc > dim - EPC) pc = dim - EPC;   // dim is a multiple of EPC; pieces past the end repeat the last one
+  const int nload = NX * (has_z ? 3 : 2) + NBC;
+
+  // all of a tile's loads, unconditionally (rows past the chunk end repeat its last step)
+  auto issue = [&](int64_t t0, int buf) {
+    const int64_t nv = (t_end - t0) < TT ? (t_end - t0) : TT;
+#pragma unroll
+    for (int j = 0; j < NX; ++j) {
+      const int64_t r = j * RPI + lrow;
+      const int64_t off = (b * L + t0 + (r < nv ? r : nv - 1)) * dim + pc;
+      lds_dma16(xg + off, lds_off(&xs[buf][0]) + j * 1024);
+      lds_dma16(dg + off, lds_off(&dls[buf][0]) + j * 1024);
+      if (has_z) lds_dma16(zg + off, lds_off(&zs[buf][0]) + j * 1024);
+    }
+#pragma unroll
+    for (int j = 0; j < NBC; ++j) {
+      int g = j * kWave + lane, tsr = g / BCW, w = g % BCW;
+      if (tsr > 1) {   // spare lanes of the last load: repeat C's last piece into the spare LDS space
+        tsr = 1;
+        w = BCW - 1;
+      }
+      const int64_t r = w / ES;   // ES pieces per step row of 16 states
+      const int64_t off = (b * L + t0 + (r < nv ? r : nv - 1)) * 16 + (w % ES) * EPC;
+      lds_dma16((tsr ? Cg : Bg) + off, lds_off(&bcs[buf][0]) + j * 1024);
+    }
+  };
+
+  // HZ: z is given (a compile-time copy of has_z, so that a tile is one straight block of code)
+  auto step = [&](auto hz, int buf, int s) {
+    constexpr bool HZ = decltype(hz)::value;
+    const float d = to_f32(*reinterpret_cast<const T*>(&dls[buf][s * RBY + lane * ES]));
+    const float u = to_f32(*reinterpret_cast<const T*>(&xs[buf][s * RBY + lane * ES]));
+    const float bv = to_f32(*reinterpret_cast<const T*>(&bcs[buf][(s * 16 + (lane & 15)) * ES]));
+    const float cv = to_f32(*reinterpret_cast<const T*>(&bcs[buf][BCB + (s * 16 + (lane & 15)) * ES]));
+    fast_updates<1, 0, 16>(h, A2, d, d * u, bv, bv);
+    float a0, a1;
+    FastReadout<1>::run(a0, a1, cv, h);
+    float y = a0 + a1;
+    if constexpr (HZ) {
+      const float gz = silu_gate(to_f32(*reinterpret_cast<const T*>(&zs[buf][s * RBY + lane * ES])));
+      y = __builtin_fmaf(y, gz, gz * (Dv * u));
+    } else {
+      y = __builtin_fmaf(Dv, u, y);
+    }
+    ys[s * kWave + lane] = from_f32<T>(y);
+    if constexpr (MODE != kSingle) {
+      S += d;
+      negseen |= (d < 0.f);
+    }
+  };
+
+  // the outputs of the tile at t0 from ys: 16-byte pieces, rows past the chunk end skipped
+  auto store_tile = [&](int64_t t0) {
+    const int64_t nv = (t_end - t0) < TT ? (t_end - t0) : TT;
+#pragma unroll
+    for (int j = 0; j < NX; ++j) {
+      const int r = j * RPI + lrow;
+      const int64_t cc = c0 + (lane % PPR) * EPC;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(&ys[r * kWave + (lane % PPR) * EPC]);
+      if (r < nv && cc < dim) *reinterpret_cast<u32x4*>(yg + (b * L + t0 + r) * dim + cc) = v;
+    }
+  };
+
+  auto run = [&](auto hz) {
+    int64_t prev_t0 = -1;
+    int i = 0;
+    if (t_begin < t_end) issue(t_begin, 0);
+    for (int64_t t0 = t_begin; t0 < t_end; t0 += TT, ++i) {
+      const int buf = i & 1;
+      int inflight = 0;
+      if (t0 + TT < t_end) {
+        issue(t0 + TT, buf ^ 1);
+        inflight = nload;
+      }
+      wait_vmcnt(inflight);
+      if (prev_t0 >= 0) store_tile(prev_t0);
+      const int64_t ns = (t_end - t0) < TT ? (t_end - t0) : TT;
+      if (ns == TT) {
+#pragma unroll
+        for (int s = 0; s < TT; ++s) step(hz, buf, s);
+      } else {
+        for (int s = 0; s < static_cast<int>(ns); ++s) step(hz, buf, s);
+      }
+      prev_t0 = t0;
+      if constexpr (MODE == kFixup) {
+        // carried-in part bounded by exp2(amax * S) * hmax; done once it would be 0 in fp32
+        const bool lane_done = !cvalid || hmax == 0.f ||
+                               (!never_exit && amax < 0.f && amax * S + __log2f(hmax) < -150.f);
+        if (__builtin_amdgcn_ballot_w64(!lane_done) == 0) break;
+      }
+    }
+    if (prev_t0 >= 0) store_tile(prev_t0);
+    wait_vmcnt(0);   // a fix-up wave can leave with the next tile's loads in flight
+  };
+  if (has_z) run(std::true_type{});
+  else run(std::false_type{});
+
+  if constexpr (MODE == kSingle) {
+    if (p.final_state != nullptr && cvalid) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) p.final_state[(b * dim + c) * 16 + j] = h[j];
+    }
+  } else if constexpr (MODE == kChunk) {
+    if (cvalid) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) p.hend[((b * p.K + k) * dim + c) * 16 + j] = h[j];
+      p.S[(b * p.K + k) * dim + c] = S;
+      p.neg[(b * p.K + k) * dim + c] = negseen;
+    }
+  }
+}
+
 // Carry across chunks, as a wave-level parallel scan over the chunks' affine maps.
 // Chunk k >= 1 takes the state entering it to the state leaving it by
 //   h -> a_k h + hend_k,   a_k = exp2(A' S_k)   (hend_k: its end state from a zero start),
@@ -1134,6 +1378,38 @@ hipError_t launch_wide(const KernelParams& kp, int64_t batch, hipStream_t stream
   }
 }
 
+// the same three launches for the one-channel-per-lane kernel: one wave per workgroup, 64 channels each
+template <int IO>
+hipError_t launch_lane(const KernelParams& kp0, int64_t batch, hipStream_t stream) {
+  KernelParams kp = kp0;
+  kp.ngroups = static_cast<int>((kp.dim + kWave - 1) / kWave);
+  const dim3 block(kWave);
+  if (kp.K == 1) {
+    const dim3 grid(static_cast<unsigned>(batch * kp.ngroups));
+    hipLaunchKernelGGL((lane_kernel<IO, kSingle>), grid, block, 0, stream, kp);
+    return hipGetLastError();
+  }
+  {
+    const dim3 grid(static_cast<unsigned>(batch * kp.K * kp.ngroups));
+    hipLaunchKernelGGL((lane_kernel<IO, kChunk>), grid, block, 0, stream, kp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    const dim3 grid(static_cast<unsigned>(carry_blocks(batch, kp.dim, kp.N)));
+    hipLaunchKernelGGL(carry_kernel, grid, dim3(256), 0, stream, kp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    KernelParams kf = kp;
+    kf.chunk_offset = 1;
+    const dim3 grid(static_cast<unsigned>(batch * (kp.K - 1) * kp.ngroups));
+    hipLaunchKernelGGL((lane_kernel<IO, kFixup>), grid, block, 0, stream, kf);
+    return hipGetLastError();
+  }
+}
+
 template <int IO, int G, int NPL, bool FAST>
 hipError_t launch_vec(const KernelParams& kp, bool vec, int64_t batch, hipStream_t stream) {
   if constexpr (Geometry<IO, G, NPL, true, FAST>::VEC_OK) {
@@ -1162,7 +1438,9 @@ hipError_t launch_io(const KernelParams& kp, int G, int npl, bool vec, int64_t b
   if (G == 16 && kp.N == 16 && vec) return launch_wide<IO, kPlain>(kp, batch, stream);
   if (kp.N <= 16) {
     switch (G) {
-      case 1: return launch_vec<IO, 1, 16, true>(kp, vec, batch, stream);
+      case 1:
+        if (kp.N == 16 && vec) return launch_lane<IO>(kp, batch, stream);
+        return launch_vec<IO, 1, 16, true>(kp, vec, batch, stream);
       case 2: return launch_vec<IO, 2, 8, true>(kp, vec, batch, stream);
       case 4: return launch_vec<IO, 4, 4, true>(kp, vec, batch, stream);
       case 8: return launch_vec<IO, 8, 4, false>(kp, vec, batch, stream);

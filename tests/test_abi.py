@@ -143,6 +143,12 @@ def test_plan_and_workspace():
     # forced plans are honoured
     assert M.selective_scan_plan(2, 1000, 64, 16, split_seq=3, split_state=4) == (3, 4)
     assert M.selective_scan_plan(1, 10, 64, 16, split_seq=64)[0] == 10   # never more chunks than steps
+    # a launch grid counts its work-items in 32 bits: 2048 x 2^20 channels fit only with one lane per
+    # channel and no split (2^31 items), 4096 x 2^20 (2^32 items) in no plan at all
+    assert M.selective_scan_plan(2048, 1, 1 << 20, 16) == (1, 1)
+    with pytest.raises(M.MssmError) as e:
+        M.selective_scan_plan(4096, 1, 1 << 20, 16)
+    assert e.value.status == M.MSSM_ERR_UNSUPPORTED
 
 
 def _ssd_call(desc, x=BASE, delta=BASE + 100 * MB, A=BASE + 200 * MB, B=BASE + 300 * MB, C=BASE + 400 * MB,

@@ -1,11 +1,13 @@
-"""Properties of the compiled SSD block kernel that its hand-written waits rely on (no GPU needed).
+"""Properties of the compiled kernels that wait for direct global->LDS loads by count (no GPU needed).
 
-The kernel waits for its direct global->LDS loads with explicit `s_waitcnt vmcnt(n)`, n counting the
-vector-memory operations the wave issued after the load it needs.  That count is exact only if the loop
-bodies contain no vector-memory instruction other than those loads and the output stores: a register spill
-reload, or a load the compiler adds, would let a needed load still be in flight at the barrier.  This test
-compiles the kernel source to gfx950 assembly with the library's own flags and checks every loop block
-(by the compiler's loop annotations) of every instantiation.
+The SSD block kernel and the one-channel-per-lane scan wait for their direct global->LDS loads with
+explicit `s_waitcnt vmcnt(n)`, n counting the vector-memory operations the wave issued after the load it
+needs.  In the SSD kernel that count must be exact: the loop bodies may contain no vector-memory instruction
+other than those loads and the output stores, since a register spill reload, or a load the compiler adds,
+would let a needed load still be in flight at the barrier.  (The scan's count covers only loads issued
+unconditionally, so an extra operation there would only make a wait stricter; a spill would still cost
+time.)  These tests compile the sources to gfx950 assembly with the library's own flags and check every
+loop block (by the compiler's loop annotations) of every instantiation.
 """
 import os
 import re
@@ -20,10 +22,10 @@ ALLOWED = re.compile(r"global_load_lds_(dwordx4|ushort)|global_store_dwordx2 ")
 VMEM = re.compile(r"(global_|buffer_|scratch_|flat_)")
 
 
-def _kernels(asm: str):
+def _kernels(asm: str, kernel: str = "10ssd_kernel"):
     out, name = {}, None
     for ln in asm.split("\n"):
-        m = re.match(r"^(_ZN4mssm12_GLOBAL__N_110ssd_kernel[^:]*):", ln)
+        m = re.match(r"^(_ZN4mssm12_GLOBAL__N_1" + kernel + r"[^:]*):", ln)
         if m:
             name = m.group(1)
             out[name] = []
@@ -50,16 +52,26 @@ def _loop_vmem(body):
     return seen, bad
 
 
-@pytest.fixture(scope="module")
-def ssd_asm(tmp_path_factory):
+def _device_asm(tmp_path_factory, src):
     from selective_state_space_17_amd.build import FLAGS, HIPCC
     if not shutil.which(HIPCC) and not os.path.exists(HIPCC):
         pytest.skip("hipcc not available")
-    out = str(tmp_path_factory.mktemp("asm") / "ssd_m2.s")
+    out = str(tmp_path_factory.mktemp("asm") / (os.path.splitext(src)[0] + ".s"))
     flags = [f for f in FLAGS if f not in ("-shared", "-fPIC", "-Wall", "-Wno-unused-function")]
-    subprocess.check_call([HIPCC] + flags + ["--cuda-device-only", "-S", "-I", CSRC, "-o", out,
-                           os.path.join(CSRC, "ssd_m2.hip")], stderr=subprocess.DEVNULL)
+    subprocess.check_call([HIPCC] + flags + ["--cuda-device-only", "-S", "-I", CSRC, "-I",
+                           os.path.join(ROOT, "include"), "-o", out, os.path.join(CSRC, src)],
+                          stderr=subprocess.DEVNULL)
     return open(out).read()
+
+
+@pytest.fixture(scope="module")
+def ssd_asm(tmp_path_factory):
+    return _device_asm(tmp_path_factory, "ssd_m2.hip")
+
+
+@pytest.fixture(scope="module")
+def scan_asm(tmp_path_factory):
+    return _device_asm(tmp_path_factory, "scan_m1.hip")
 
 
 def test_ssd_loops_hold_only_the_counted_memory_operations(ssd_asm):
@@ -74,6 +86,37 @@ def test_ssd_loops_hold_only_the_counted_memory_operations(ssd_asm):
 def test_ssd_no_vector_register_spills(ssd_asm):
     spills = [int(v) for v in re.findall(r"\.vgpr_spill_count:\s+(\d+)", ssd_asm)]
     assert spills and all(v == 0 for v in spills), spills
+
+
+LANE_ALLOWED = re.compile(r"global_load_lds_dwordx4|global_store_dwordx4 ")
+
+
+def test_lane_kernel_loops_and_spills(scan_asm):
+    # the one-channel-per-lane scan waits for its direct loads by count as well: its loops may hold only
+    # those loads and the output stores, and no instantiation may spill
+    ks = _kernels(scan_asm, "11lane_kernel")
+    assert len(ks) == 6, sorted(ks)   # fp32 / bf16 x single pass, chunk pass, fix-up pass
+    for name, body in ks.items():
+        ops = _loop_ops(body)
+        assert ops, name
+        assert all(LANE_ALLOWED.match(t) for t in ops), (name, [t for t in ops if not LANE_ALLOWED.match(t)][:4])
+    spills = {}
+    for name in ks:
+        md = scan_asm[scan_asm.index(".name:           " + name):]
+        spills[name] = int(re.search(r"\.vgpr_spill_count:\s+(\d+)", md).group(1))
+    assert all(v == 0 for v in spills.values()), spills
+
+
+def _loop_ops(body):
+    inloop, ops = False, []
+    for ln in body:
+        if re.match(r"^(\.LBB\d+_\d+:|; %bb\.\d+:)", ln):
+            inloop = ("Loop Header" in ln) or ("in Loop:" in ln)
+            continue
+        t = ln.strip()
+        if inloop and VMEM.match(t):
+            ops.append(t)
+    return ops
 
 
 def test_checker_flags_an_extra_load():

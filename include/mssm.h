@@ -425,13 +425,15 @@ size_t mssm_selective_scan_checkpoint_size(const mssm_scan_desc* desc);
  *   dB_t = sum_c lam_t delta_t x_t; dz = dout y silu'(z); dh0 = exp(delta_0 A) lam_0.
  * Without checkpoints (below) the states are recomputed from h0: nothing is
  * kept from the forward call.
- * dstate must be at most 16 (MSSM_ERR_UNSUPPORTED otherwise); split_seq and
+ * dstate up to 256 (the states are taken in slices of 16); split_seq and
  * split_state are ignored.  The result is deterministic: every sum is taken
  * in a fixed order.  workspace: at least
- * mssm_selective_scan_bwd_workspace_size(desc) bytes, 256-byte aligned (about
- * 64 * batch * ceil(seqlen / 16) * 16 * ceil(dim / 16) bytes of state
- * checkpoints, 16 states per channel whatever dstate is, plus
- * 128 * batch * seqlen * ceil(dim / 16) bytes of per-block partial sums).
+ * mssm_selective_scan_bwd_workspace_size(desc) bytes, 256-byte aligned.  With
+ * S = ceil(dstate / 16) that is about 4 * batch * ceil(seqlen / 16) * 16 *
+ * ceil(dim / 16) * 16 S bytes of state checkpoints, plus 8 * batch * seqlen *
+ * ceil(dim / 16) * 16 S bytes of per-block dB/dC partial sums, plus, when
+ * S > 1, 12 * S * batch * seqlen * dim bytes of the slices' partial sums
+ * (added by a finishing kernel).
  * checkpoints: nullable; the array mssm_selective_scan_fwd_ckpt wrote for
  * these inputs (dstate 16 only).  Given it, the kernel starts every tile from
  * the stored state instead of walking the sequence forward once more (the

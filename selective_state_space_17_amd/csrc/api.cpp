@@ -705,8 +705,8 @@ int mssm_selective_scan_conv_fwd(const mssm_scan_desc* desc, int32_t conv_width,
 // Gradients of the Mamba-1 selective scan
 // --------------------------------------------------------------------------
 size_t mssm_selective_scan_bwd_workspace_size(const mssm_scan_desc* desc) {
-  if (validate_scan_desc(desc) != MSSM_OK || desc->dstate > 16) return 0;
-  return mssm::scan_bwd_workspace_bytes(desc->batch, desc->seqlen, desc->dim);
+  if (validate_scan_desc(desc) != MSSM_OK) return 0;
+  return mssm::scan_bwd_workspace_bytes(desc->batch, desc->seqlen, desc->dim, desc->dstate);
 }
 
 int mssm_selective_scan_bwd(const mssm_scan_desc* desc, const void* x, const void* delta, const float* A,
@@ -717,7 +717,6 @@ int mssm_selective_scan_bwd(const mssm_scan_desc* desc, const void* x, const voi
   const int v = validate_scan_desc(desc);
   if (v != MSSM_OK) return v;
   const mssm_scan_desc& d = *desc;
-  if (d.dstate > 16) return MSSM_ERR_UNSUPPORTED;
   const int64_t es = d.io_dtype == MSSM_BF16 ? 2 : 4;
   const int64_t n_bld = d.batch * d.seqlen * d.dim;
   const bool has_steps = n_bld > 0;
@@ -733,10 +732,15 @@ int mssm_selective_scan_bwd(const mssm_scan_desc* desc, const void* x, const voi
       !aligned(dC, 4) || !aligned(dD, 4) || !aligned(dh0, 4) || !aligned(checkpoints, 4))
     return MSSM_ERR_MISALIGNED;
   if (checkpoints != nullptr && d.dstate != 16) return MSSM_ERR_UNSUPPORTED;   // written by the dstate-16 forward
+  // launch grids count their work-items in 32 bits: the gradient kernel's blocks of 256 threads, the dB/dC
+  // sums over (b, t, 4 states), and with more than 16 states the element-wise finish over (b, t, c)
+  constexpr int64_t kMaxItems = std::numeric_limits<uint32_t>::max();
   if ((d.seqlen + 15) / 16 > std::numeric_limits<int32_t>::max() ||
-      mssm::scan_bwd_grid_blocks(d.batch, d.dim) > std::numeric_limits<int32_t>::max())
+      mssm::scan_bwd_grid_blocks(d.batch, d.dim, d.dstate) > kMaxItems / 256 ||
+      d.batch * d.seqlen * ((d.dstate + 15) / 16 * 4) > kMaxItems - 255 ||
+      (d.dstate > 16 && n_bld > kMaxItems - 255))
     return MSSM_ERR_UNSUPPORTED;
-  const size_t need = mssm::scan_bwd_workspace_bytes(d.batch, d.seqlen, d.dim);
+  const size_t need = mssm::scan_bwd_workspace_bytes(d.batch, d.seqlen, d.dim, d.dstate);
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need) return MSSM_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return MSSM_ERR_MISALIGNED;

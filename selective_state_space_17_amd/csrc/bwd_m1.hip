@@ -15,10 +15,14 @@
 //   dA[c,n] = sum_{b,t} lam_t a_t h_{t-1} delta_t,  dD[c] = sum_{b,t} dy_t x_t
 //   dh0 = a_0 lam_0
 //
-// Mapping.  A block of 4 waves owns 16 channels of one batch row; lane
-// (row cl = tid/16, n = tid%16) holds state n of channel c0 + cl (dstate <=
-// 16; the other lanes carry zeros).  The reverse walk needs h_{t-1} at every
-// step, so:
+// Mapping.  A block of 4 waves owns 16 channels of one batch row and one
+// slice of 16 states; lane (row cl = tid/16, n = tid%16) holds state
+// 16 * slice + n of channel c0 + cl (states past dstate carry zeros).  The
+// slices of a channel are independent except in the three sums over all
+// states (y for dz, and the two sums that make ddelta and dx): with more than
+// one slice each block writes its partial sums, and a finishing kernel adds
+// them in slice order and forms dz, ddelta and dx.  The reverse walk needs
+// h_{t-1} at every step, so:
 //   phase A  walks the sequence forward once (the exp and FMA of the
 //            forward recurrence only) and writes the state entering every
 //            16-step tile to a checkpoint workspace;
@@ -141,14 +145,18 @@ struct BwdParams {
   void* ddelta;
   void* dz;            // written iff z != nullptr
   float* dh0;          // nullable
-  float* ckpt;         // [batch][ntiles][ncb*16][16]
-  const float* ckpt_in;   // nullable: the same array written by the training-mode forward
-  float* partB;        // [ncb][batch][L][16]
-  float* partC;        // [ncb][batch][L][16]
-  float* wsA;          // [batch][ncb*16][16]
+  float* ckpt;         // [batch][ntiles][ncb*16][np16]
+  const float* ckpt_in;   // nullable: the same array written by the training-mode forward (dstate 16)
+  float* partB;        // [ncb][batch][L][np16]
+  float* partC;        // [ncb][batch][L][np16]
+  float* wsA;          // [batch][ncb*16][np16]
   float* wsD;          // [batch][ncb*16]
+  float* part_y;       // [nsl][batch][L][dim]: with several slices, each slice's share of
+  float* part_s1;      //   sum_n C h, of sum_n lam a h A (ddelta) and of sum_n lam B (ddelta, dx)
+  float* part_s2;
   int64_t batch, L, dim, N;
   int ntiles, ncb;
+  int nsl, np16;       // state slices of 16, and 16 * nsl
 };
 
 // Step S of the forward recurrence for lane (cl, n): the per-(t, c) values
@@ -193,7 +201,8 @@ __device__ __forceinline__ void adj_step(float& lam, float& dA, const float (&av
 }
 
 // three waves per SIMD: what the grid of a typical layer provides (batch x dim / 16 blocks of 4 waves)
-template <typename T>
+// SPLIT: more than one state slice (partial sums out, finished by bwd_finish)
+template <typename T, bool SPLIT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void scan_bwd_kernel(BwdParams p) {
   using io = Io<T>;
   __shared__ __attribute__((aligned(16))) float BT[16 * kBT];      // B^T per tile
@@ -209,8 +218,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   // turn, so consecutive blocks are remapped to put 4 neighbouring channel
   // blocks (one 128-byte line of a bf16 row) on one XCD, whose L2 then serves
   // them all
-  const int64_t nb = gridDim.x;
-  const int64_t bid = blockIdx.x;
+  // (the slices of one channel block are consecutive blocks)
+  const int slice = SPLIT ? static_cast<int>(blockIdx.x % p.nsl) : 0;
+  const int64_t nb = SPLIT ? gridDim.x / p.nsl : gridDim.x;
+  const int64_t bid = SPLIT ? blockIdx.x / p.nsl : blockIdx.x;
   int64_t lin = bid;
   if (bid < (nb / 32) * 32) {
     const int64_t xcd = bid % 8, rr = bid / 8;
@@ -221,15 +232,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   const int64_t c0 = static_cast<int64_t>(cb) * kCPB;
   const int64_t c = c0 + cl;
   const int64_t L = p.L, dim = p.dim, N = p.N;
-  const bool lane_ok = c < dim && n < N;
+  const int s0 = 16 * slice;           // first state of the slice
+  const int64_t sn = s0 + n;           // this lane's state
+  const bool lane_ok = c < dim && sn < N;
   const int64_t D16 = static_cast<int64_t>(p.ncb) * kCPB;
-  const int bs = tid >> 4, bn = tid & 15;   // B/C staging: step, state
+  const int64_t NP = p.np16;
+  const int bs = tid >> 4, bn = tid & 15;   // B/C staging: step, state s0 + bn
 
-  const float Av = lane_ok ? p.A[c * N + n] : 0.f;
+  const float Av = lane_ok ? p.A[c * N + sn] : 0.f;
   const float A2 = Av * kLog2e;
-  float* ck = p.ckpt + (b * p.ntiles * D16 + c) * 16 + n;   // + k * D16 * 16
+  float* ck = p.ckpt + (b * p.ntiles * D16 + c) * NP + sn;   // + k * D16 * NP
   // the checkpoints phase B starts its tiles from: the forward's, or phase A's
-  const float* ckr = p.ckpt_in != nullptr ? p.ckpt_in + (b * p.ntiles * D16 + c) * 16 + n : ck;
+  const float* ckr = p.ckpt_in != nullptr ? p.ckpt_in + (b * p.ntiles * D16 + c) * NP + sn : ck;
 
   // -------------------------------------------------------------- phase A
   // Staged 64 steps at a time (one barrier per 64 steps, loads a whole
@@ -237,7 +251,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   // Skipped when the training-mode forward already stored them.
   if (p.ckpt_in == nullptr) {
     float* BA = Q1;   // B^T of a 64-step staging tile: [2 buffers][16 states][kBA]
-    float h = (lane_ok && p.h0 != nullptr) ? p.h0[(b * dim + c) * N + n] : 0.f;
+    float h = (lane_ok && p.h0 != nullptr) ? p.h0[(b * dim + c) * N + sn] : 0.f;
     // Loads are unconditional, from an in-range element when the step or
     // channel is past the end, and their raw values are left untouched until
     // the tile is staged (masking or widening them at once would make the
@@ -253,8 +267,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         rd[j] = io::raw(p.delta, i);
         rx[j] = io::raw(p.x, i);
         const int64_t tb = t0 + 16 * j + bs;
-        okb[j] = tb < L && bn < N;
-        rb[j] = io::raw(p.B, (b * L + (tb < L ? tb : L - 1)) * N + (bn < N ? bn : N - 1));
+        okb[j] = tb < L && s0 + bn < N;
+        rb[j] = io::raw(p.B, (b * L + (tb < L ? tb : L - 1)) * N + (s0 + bn < N ? s0 + bn : N - 1));
       }
     };
     // tiles 0 .. ntiles-2 are walked (their end states are checkpoints 1 .. ntiles-1)
@@ -277,7 +291,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         if (t0 + 16 * j < walk) {   // uniform
-          ck[static_cast<int64_t>(k0 + j) * D16 * 16] = h;   // padded lanes store their zero state too
+          ck[static_cast<int64_t>(k0 + j) * D16 * NP] = h;   // padded lanes store their zero state too
           fwd_group<0>(h, dl[j], du[j], A2, b4[4 * j + 0]);
           fwd_group<1>(h, dl[j], du[j], A2, b4[4 * j + 1]);
           fwd_group<2>(h, dl[j], du[j], A2, b4[4 * j + 2]);
@@ -285,13 +299,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         }
       }
     }
-    if (p.ntiles > 0) ck[static_cast<int64_t>(p.ntiles - 1) * D16 * 16] = h;
+    if (p.ntiles > 0) ck[static_cast<int64_t>(p.ntiles - 1) * D16 * NP] = h;
     __syncthreads();   // orders the checkpoint stores before phase B's loads; frees Q1
   }
 
   // -------------------------------------------------------------- phase B
   const float Dc = (c < dim && p.D != nullptr) ? p.D[c] : 0.f;
-  float lam = (lane_ok && p.dfinal != nullptr) ? p.dfinal[(b * dim + c) * N + n] : 0.f;
+  float lam = (lane_ok && p.dfinal != nullptr) ? p.dfinal[(b * dim + c) * N + sn] : 0.f;
   float dAacc = 0.f, dDacc = 0.f;
   // raw prefetched values of the next tile (unconditional in-range loads, see phase A)
   T rdl{}, rx{}, rg{}, rz{}, rb{}, rc{};
@@ -306,11 +320,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     rg = io::raw(p.dout, i);
     if (p.z != nullptr) rz = io::raw(p.z, i);
     const int64_t tb = static_cast<int64_t>(k) * kTT + bs;
-    okb = tb < L && bn < N;
-    const int64_t ib = (b * L + (tb < L ? tb : L - 1)) * N + (bn < N ? bn : N - 1);
+    okb = tb < L && s0 + bn < N;
+    const int64_t ib = (b * L + (tb < L ? tb : L - 1)) * N + (s0 + bn < N ? s0 + bn : N - 1);
     rb = io::raw(p.B, ib);
     rc = io::raw(p.C, ib);
-    rh = ckr[static_cast<int64_t>(k) * D16 * 16];   // channels past dim: masked at staging
+    rh = ckr[static_cast<int64_t>(k) * D16 * NP];   // channels past dim: masked at staging
   };
   // transposes through this wave's own rows of Q1/Q2 (no other wave touches
   // them before the barrier that ends the tile's compute); a wave's LDS
@@ -434,8 +448,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       adj_step<1>(lam, dAacc, av, hs, hin, ls, r1, dl, dy, Av, cv.y);
       adj_step<0>(lam, dAacc, av, hs, hin, ls, r1, dl, dy, Av, cv.x);
     }
-    const float y = __builtin_fmaf(Dc, u, sum8(ry));
-    if (p.z != nullptr && fvalid) io::put(p.dz, fi, sdz * y);
+    const float yp = sum8(ry);   // this slice's sum_n C h
+    if constexpr (!SPLIT) {
+      if (p.z != nullptr && fvalid) io::put(p.dz, fi, sdz * __builtin_fmaf(Dc, u, yp));
+    }
     // both sums over states in one LDS round trip (Q1's rows take q1 after)
     park_pairs(Q1, r1);
     {
@@ -456,8 +472,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     dDacc = __builtin_fmaf(dy, u, dDacc);
     const float s1 = sum8(ra), s2 = sum8(rb2);
     if (fvalid) {
-      io::put(p.ddelta, fi, __builtin_fmaf(u, s2, s1));
-      io::put(p.dx, fi, __builtin_fmaf(dl, s2, Dc * dy));
+      if constexpr (SPLIT) {
+        const int64_t pi = ((static_cast<int64_t>(slice) * p.batch + b) * L + tf) * dim + c;
+        p.part_y[pi] = yp;
+        p.part_s1[pi] = s1;
+        p.part_s2[pi] = s2;
+      } else {
+        io::put(p.ddelta, fi, __builtin_fmaf(u, s2, s1));
+        io::put(p.dx, fi, __builtin_fmaf(dl, s2, Dc * dy));
+      }
     }
     park(Q1, q1);
     {
@@ -486,7 +509,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       }
       const int64_t t = t0 + rs;
       if (t < L) {
-        const int64_t o = ((static_cast<int64_t>(cb) * p.batch + b) * L + t) * 16 + rn;
+        const int64_t o = ((static_cast<int64_t>(cb) * p.batch + b) * L + t) * NP + s0 + rn;
         p.partB[o] = sb;
         p.partC[o] = sc;
       }
@@ -496,21 +519,51 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     // the next tile's first barrier, which every wave reaches after its sums.
   }
 
-  if (lane_ok && p.dh0 != nullptr) p.dh0[(b * dim + c) * N + n] = lam;
-  p.wsA[(b * D16 + c) * 16 + n] = dAacc;   // zero for padded lanes
-  const float dDrow = row_sum(dDacc);
-  if (n == 0) p.wsD[b * D16 + c] = dDrow;
+  if (lane_ok && p.dh0 != nullptr) p.dh0[(b * dim + c) * N + sn] = lam;
+  p.wsA[(b * D16 + c) * NP + sn] = dAacc;   // zero for padded lanes
+  const float dDrow = row_sum(dDacc);     // the same in every slice: slice 0 stores it
+  if (n == 0 && slice == 0) p.wsD[b * D16 + c] = dDrow;
+}
+
+// With several state slices: y = sum of the slices' shares + D x, and the two
+// state sums, added in slice order, then dz, ddelta and dx as the gradient
+// kernel forms them with one slice.
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_finish(BwdParams p) {
+  using io = Io<T>;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;   // (b, t, c)
+  const int64_t n_bld = p.batch * p.L * p.dim;
+  if (i >= n_bld) return;
+  const int64_t c = i % p.dim;
+  float yp = 0.f, s1 = 0.f, s2 = 0.f;
+  for (int sl = 0; sl < p.nsl; ++sl) {
+    yp += p.part_y[sl * n_bld + i];
+    s1 += p.part_s1[sl * n_bld + i];
+    s2 += p.part_s2[sl * n_bld + i];
+  }
+  const float dl = io::get(p.delta, i), u = io::get(p.x, i), g = io::get(p.dout, i);
+  const float Dc = p.D != nullptr ? p.D[c] : 0.f;
+  float dy = g;
+  if (p.z != nullptr) {
+    const float zz = io::get(p.z, i);
+    const float sg = __builtin_amdgcn_rcpf(1.f + exp2_hw(-zz * kLog2e));
+    dy = g * zz * sg;
+    io::put(p.dz, i, g * sg * __builtin_fmaf(zz, 1.f - sg, 1.f) * __builtin_fmaf(Dc, u, yp));
+  }
+  io::put(p.ddelta, i, __builtin_fmaf(u, s2, s1));
+  io::put(p.dx, i, __builtin_fmaf(dl, s2, Dc * dy));
 }
 
 // dB, dC: sum of the per-block partials, in block order.  A thread owns four
 // consecutive (step, state) slots (16-byte loads) and keeps several blocks'
 // loads in flight; the order of the additions is fixed.
 __global__ __launch_bounds__(256) void bwd_reduce_bc(const float* partB, const float* partC, float* dB, float* dC,
-                                                     int64_t batch, int64_t L, int64_t N, int ncb) {
+                                                     int64_t batch, int64_t L, int64_t N, int ncb, int np16) {
   const int64_t rows = batch * L;
+  const int64_t g4 = np16 / 4;   // 4-state groups per row
   const int64_t q = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;   // (row, 4-state group)
-  if (q >= rows * 4) return;
-  const int64_t stride = rows * 4;   // float4 slots per block's partial
+  if (q >= rows * g4) return;
+  const int64_t stride = rows * g4;   // float4 slots per block's partial
   const float4* pb = reinterpret_cast<const float4*>(partB) + q;
   const float4* pc = reinterpret_cast<const float4*>(partC) + q;
   float4 sb = {0.f, 0.f, 0.f, 0.f}, sc = {0.f, 0.f, 0.f, 0.f};
@@ -533,8 +586,8 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc(const float* partB, const f
     sb.x += vb.x; sb.y += vb.y; sb.z += vb.z; sb.w += vb.w;
     sc.x += vc.x; sc.y += vc.y; sc.z += vc.z; sc.w += vc.w;
   }
-  const int64_t row = q >> 2;
-  const int n0 = static_cast<int>(q & 3) * 4;
+  const int64_t row = q / g4;
+  const int n0 = static_cast<int>(q % g4) * 4;
   const float b4[4] = {sb.x, sb.y, sb.z, sb.w}, c4[4] = {sc.x, sc.y, sc.z, sc.w};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -547,15 +600,15 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc(const float* partB, const f
 
 // dA, dD: sum over the batch rows, in order
 __global__ __launch_bounds__(256) void bwd_reduce_ad(const float* wsA, const float* wsD, float* dA, float* dD,
-                                                     int64_t batch, int64_t dim, int64_t N, int ncb) {
+                                                     int64_t batch, int64_t dim, int64_t N, int ncb, int np16) {
   const int64_t D16 = static_cast<int64_t>(ncb) * 16;
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;   // (c, n16)
-  if (i >= dim * 16) return;
-  const int64_t cc = i >> 4;
-  const int nn = static_cast<int>(i & 15);
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;   // (c, padded state)
+  if (i >= dim * np16) return;
+  const int64_t cc = i / np16;
+  const int nn = static_cast<int>(i % np16);
   if (nn < N) {
     float s = 0.f;
-    for (int64_t bb = 0; bb < batch; ++bb) s += wsA[(bb * D16 + cc) * 16 + nn];
+    for (int64_t bb = 0; bb < batch; ++bb) s += wsA[(bb * D16 + cc) * np16 + nn];
     dA[cc * N + nn] = s;
   }
   if (nn == 0 && dD != nullptr) {
@@ -566,31 +619,42 @@ __global__ __launch_bounds__(256) void bwd_reduce_ad(const float* wsA, const flo
 }
 
 struct Layout {
-  size_t ckpt, partB, partC, wsA, wsD, total;
+  size_t ckpt, partB, partC, wsA, wsD, py, ps1, ps2, total;
 };
 size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
-Layout layout(int64_t batch, int64_t L, int64_t dim) {
+int64_t slices(int64_t N) { return (N + 15) / 16; }
+Layout layout(int64_t batch, int64_t L, int64_t dim, int64_t N) {
   const int64_t ncb = (dim + kCPB - 1) / kCPB, D16 = ncb * kCPB, nt = (L + kTT - 1) / kTT;
+  const int64_t nsl = slices(N), NP = 16 * nsl;
   Layout l{};
   size_t off = 0;
-  l.ckpt = off;  off += align256(sizeof(float) * static_cast<size_t>(batch * nt * D16 * 16));
-  l.partB = off; off += align256(sizeof(float) * static_cast<size_t>(ncb * batch * L * 16));
-  l.partC = off; off += align256(sizeof(float) * static_cast<size_t>(ncb * batch * L * 16));
-  l.wsA = off;   off += align256(sizeof(float) * static_cast<size_t>(batch * D16 * 16));
+  l.ckpt = off;  off += align256(sizeof(float) * static_cast<size_t>(batch * nt * D16 * NP));
+  l.partB = off; off += align256(sizeof(float) * static_cast<size_t>(ncb * batch * L * NP));
+  l.partC = off; off += align256(sizeof(float) * static_cast<size_t>(ncb * batch * L * NP));
+  l.wsA = off;   off += align256(sizeof(float) * static_cast<size_t>(batch * D16 * NP));
   l.wsD = off;   off += align256(sizeof(float) * static_cast<size_t>(batch * D16));
+  const size_t part = nsl > 1 ? align256(sizeof(float) * static_cast<size_t>(nsl * batch * L * dim)) : 0;
+  l.py = off;    off += part;
+  l.ps1 = off;   off += part;
+  l.ps2 = off;   off += part;
   l.total = off;
   return l;
 }
 
 }  // namespace
 
-size_t scan_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t dim) { return layout(batch, L, dim).total; }
+size_t scan_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_t N) {
+  return layout(batch, L, dim, N).total;
+}
 
-int64_t scan_bwd_grid_blocks(int64_t batch, int64_t dim) { return batch * ((dim + kCPB - 1) / kCPB); }
+int64_t scan_bwd_grid_blocks(int64_t batch, int64_t dim, int64_t N) {
+  return batch * ((dim + kCPB - 1) / kCPB) * slices(N);
+}
 
 hipError_t scan_bwd_launch(const ScanBwdArgs& a, hipStream_t stream) {
   const int64_t ncb = (a.dim + kCPB - 1) / kCPB;
-  const Layout l = layout(a.batch, a.L, a.dim);
+  const Layout l = layout(a.batch, a.L, a.dim, a.N);
+  const int nsl = static_cast<int>(slices(a.N));
   char* ws = static_cast<char*>(a.workspace);
   BwdParams p{};
   p.x = a.x; p.delta = a.delta; p.B = a.B; p.C = a.C; p.z = a.z; p.dout = a.dout;
@@ -602,28 +666,47 @@ hipError_t scan_bwd_launch(const ScanBwdArgs& a, hipStream_t stream) {
   p.partC = reinterpret_cast<float*>(ws + l.partC);
   p.wsA = reinterpret_cast<float*>(ws + l.wsA);
   p.wsD = reinterpret_cast<float*>(ws + l.wsD);
+  if (nsl > 1) {
+    p.part_y = reinterpret_cast<float*>(ws + l.py);
+    p.part_s1 = reinterpret_cast<float*>(ws + l.ps1);
+    p.part_s2 = reinterpret_cast<float*>(ws + l.ps2);
+  }
   p.batch = a.batch; p.L = a.L; p.dim = a.dim; p.N = a.N;
   p.ntiles = static_cast<int>((a.L + kTT - 1) / kTT);
   p.ncb = static_cast<int>(ncb);
+  p.nsl = nsl;
+  p.np16 = 16 * nsl;
   if (a.batch > 0) {
-    const dim3 grid(static_cast<unsigned>(ncb * a.batch));
-    if (a.io == 1)
-      hipLaunchKernelGGL(scan_bwd_kernel<uint16_t>, grid, dim3(kThreads), 0, stream, p);
-    else
-      hipLaunchKernelGGL(scan_bwd_kernel<float>, grid, dim3(kThreads), 0, stream, p);
+    const dim3 grid(static_cast<unsigned>(ncb * a.batch * nsl));
+    if (a.io == 1) {
+      if (nsl > 1) hipLaunchKernelGGL((scan_bwd_kernel<uint16_t, true>), grid, dim3(kThreads), 0, stream, p);
+      else hipLaunchKernelGGL((scan_bwd_kernel<uint16_t, false>), grid, dim3(kThreads), 0, stream, p);
+    } else {
+      if (nsl > 1) hipLaunchKernelGGL((scan_bwd_kernel<float, true>), grid, dim3(kThreads), 0, stream, p);
+      else hipLaunchKernelGGL((scan_bwd_kernel<float, false>), grid, dim3(kThreads), 0, stream, p);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t nbc = (a.batch * a.L * 4 + 255) / 256;
+    const int64_t nbc = (a.batch * a.L * (p.np16 / 4) + 255) / 256;
     if (nbc > 0) {
       hipLaunchKernelGGL(bwd_reduce_bc, dim3(static_cast<unsigned>(nbc)), dim3(256), 0, stream, p.partB, p.partC,
-                         a.dB, a.dC, a.batch, a.L, a.N, p.ncb);
+                         a.dB, a.dC, a.batch, a.L, a.N, p.ncb, p.np16);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    const int64_t nfin = (a.batch * a.L * a.dim + 255) / 256;
+    if (nsl > 1 && nfin > 0) {
+      if (a.io == 1)
+        hipLaunchKernelGGL(bwd_finish<uint16_t>, dim3(static_cast<unsigned>(nfin)), dim3(256), 0, stream, p);
+      else
+        hipLaunchKernelGGL(bwd_finish<float>, dim3(static_cast<unsigned>(nfin)), dim3(256), 0, stream, p);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
   }
-  const int64_t nad = (a.dim * 16 + 255) / 256;
+  const int64_t nad = (a.dim * p.np16 + 255) / 256;
   hipLaunchKernelGGL(bwd_reduce_ad, dim3(static_cast<unsigned>(nad)), dim3(256), 0, stream, p.wsA, p.wsD, a.dA, a.dD,
-                     a.batch, a.dim, a.N, p.ncb);
+                     a.batch, a.dim, a.N, p.ncb, p.np16);
   return hipGetLastError();
 }
 

@@ -156,9 +156,9 @@ struct ScanBwdArgs {
 };
 
 // workspace: per-tile state checkpoints, per-block dB/dC partials, per-row dA/dD partials
-size_t scan_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t dim);
+size_t scan_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int64_t N);
 // blocks of the main gradient kernel
-int64_t scan_bwd_grid_blocks(int64_t batch, int64_t dim);
+int64_t scan_bwd_grid_blocks(int64_t batch, int64_t dim, int64_t N);
 hipError_t scan_bwd_launch(const ScanBwdArgs& a, hipStream_t stream);
 
 }  // namespace mssm

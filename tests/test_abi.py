@@ -400,7 +400,7 @@ def _bwd_call(desc, ws=BASE + 2000 * MB, ws_bytes=None, **kw):
 
 @pytest.mark.parametrize("case,expect", [
     ("null_desc", M.MSSM_ERR_INVALID_ARG),
-    ("dstate_17", M.MSSM_ERR_UNSUPPORTED),
+    ("dstate_257", M.MSSM_ERR_UNSUPPORTED),
     ("bad_dtype", M.MSSM_ERR_UNSUPPORTED),
     ("null_dout", M.MSSM_ERR_INVALID_ARG),
     ("null_dA", M.MSSM_ERR_INVALID_ARG),
@@ -422,8 +422,8 @@ def test_scan_bwd_validation(case, expect):
     kw = {}
     if case == "null_desc":
         d = None
-    elif case == "dstate_17":
-        d = small(dstate=17, split_state=0)
+    elif case == "dstate_257":
+        d = small(dstate=257, split_state=0)
     elif case == "bad_dtype":
         d = small(io_dtype=3)
     elif case == "null_dout":
@@ -464,7 +464,12 @@ def test_scan_bwd_workspace_size():
     al = lambda v: (v + 255) // 256 * 256
     want = al(4 * 2 * 4 * 32 * 16) + 2 * al(4 * 2 * 2 * 64 * 16) + al(4 * 2 * 32 * 16) + al(4 * 2 * 32)
     assert M.lib.mssm_selective_scan_bwd_workspace_size(ctypes.byref(d)) == want
-    assert M.lib.mssm_selective_scan_bwd_workspace_size(ctypes.byref(small(dstate=17, split_state=0))) == 0
+    # 40 states: three slices of 16, and the slices' partial sums of the three per-(b, t, c) state sums
+    d = small(batch=2, seqlen=64, dim=32, dstate=40, split_state=0)
+    want = al(4 * 2 * 4 * 32 * 48) + 2 * al(4 * 2 * 2 * 64 * 48) + al(4 * 2 * 32 * 48) + al(4 * 2 * 32) + \
+        3 * al(4 * 3 * 2 * 64 * 32)
+    assert M.lib.mssm_selective_scan_bwd_workspace_size(ctypes.byref(d)) == want
+    assert M.lib.mssm_selective_scan_bwd_workspace_size(ctypes.byref(small(dstate=257, split_state=0))) == 0
 
 
 def _conv_call(desc, width=4, ws=None, ws_bytes=0, **kw):

@@ -4,7 +4,9 @@ Every output (dx, ddelta, dz, dB, dC, dA, dD, dh0) is compared element by
 element with oracle.scan_bwd on the same seeded inputs and upstream
 gradients, under the tolerance rule of gpu_util (1e-4 for fp32 I/O, 2e-2 for
 bf16 I/O): small cases that span several 16-step tiles and 16-channel blocks
-with ragged tails, dstate below 16, and the full 8 x 2048 x 1536 layer."""
+with ragged tails, dstate below 16, dstate above 16 (several 16-state slices,
+ragged ones too, whose partial sums a finishing kernel adds), and the full
+8 x 2048 x 1536 layer."""
 import numpy as np
 import pytest
 
@@ -55,6 +57,12 @@ CASES = [
     (2, 257, 100, 16, "bf16", False, True, True, False),
     (1, 20000, 64, 16, "bf16", True, True, True, True),   # 1250 tiles: checkpoint indexing far along
     (1, 256, 5120, 16, "bf16", True, True, False, False), # the 2.8B layer's width: 320 channel blocks
+    (2, 40, 40, 17, "f32", True, True, True, True),      # two slices, the second with one state
+    (2, 33, 24, 32, "bf16", True, True, True, True),
+    (1, 50, 40, 64, "f32", False, True, False, True),
+    (2, 40, 48, 128, "bf16", True, True, True, True),
+    (1, 37, 20, 256, "f32", True, False, True, True),    # the largest dstate, no z
+    (1, 300, 32, 100, "bf16", True, True, True, False),  # a ragged last slice
 ]
 
 
@@ -102,9 +110,33 @@ def test_scan_bwd_deterministic(M):
             assert torch.equal(g1[k], g2[k]), f"{k} differs between identical calls"
 
 
+def test_scan_bwd_deterministic_slices(M):
+    """The same with 64 states: the slices' partial sums are added in slice order."""
+    import torch
+    cfg = W.scan_config(2, 70, 40, 64, io="bf16", cfg_id=853)
+    inp = W.make_scan_inputs(cfg, with_h0=True)
+    dout, dfin = W.make_scan_grads(cfg)
+    args = [dev(a) for a in (inp.x, inp.delta, inp.A, inp.B, inp.C, inp.D, inp.z, inp.h0, dout, dfin)]
+    say("scan bwd determinism, 4 slices")
+    g1 = M.selective_scan_bwd(*args)
+    g2 = M.selective_scan_bwd(*args)
+    torch.cuda.synchronize()
+    for k in g1:
+        if g1[k] is not None:
+            assert torch.equal(g1[k], g2[k]), f"{k} differs between identical calls"
+
+
 def test_scan_bwd_full_layer(M):
     """The 8 x 2048 x 1536 x 16 bf16 layer the backward benchmark times, every element checked."""
     cfg = W.CONFIGS[8]
+    say("scan bwd full layer", cfg.name)
+    g, ref = run_case(M, cfg, False, False, want_dh0=False)
+    compare(g, ref, cfg.io, cfg.name)
+
+
+def test_scan_bwd_full_layer_n128(M):
+    """The same layer with 128 states per channel (eight slices), every element checked."""
+    cfg = W.CONFIGS[16]
     say("scan bwd full layer", cfg.name)
     g, ref = run_case(M, cfg, False, False, want_dh0=False)
     compare(g, ref, cfg.io, cfg.name)

@@ -186,6 +186,9 @@ CONFIGS = {
     # its decode step at config 7's serving shape (the previous token's 4 inputs and B rows too)
     15: SSDConfig("mamba3_mimo_decode_bf16", 15, 64, 1, 32, 64, 128, 1, 64, BF16, True, True, True, decode=True,
                   trapezoidal=True, rank=4),
+    # gradients of config 2's layer with 128 states per channel (the larger state sizes of the d_state sweep)
+    16: ScanConfig("mamba1_130m_layer_bwd_n128_bf16", 16, 8, 2048, 1536, 128, BF16, "exp_log", return_final=False,
+                   backward=True),
 }
 
 

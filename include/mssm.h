@@ -121,8 +121,13 @@ typedef struct {
  * rounding differs).  The matrix-core block kernel takes io_dtype MSSM_BF16
  * (the matrix cores take bf16 operands), headdim a multiple of 64, dstate a
  * multiple of 16 up to 128 (and, for the MIMO calls below, a rank of 1, 2,
- * 4, 8 or 16); there the state never leaves the chip between blocks, and x,
- * z, out, B, C, h0 and final_state must be 16-byte aligned.  Any other problem with io_dtype
+ * 4, 8 or 16), or with one input per channel a multiple of 16 up to 256;
+ * there the state never leaves the chip between blocks, and x,
+ * z, out, B, C, h0 and final_state must be 16-byte aligned.  Above 128 states
+ * the kernel runs twice, on states 0-127 and on the rest, each writing its
+ * share of the output's state sum in fp32 to the workspace, and a third
+ * kernel adds the shares, D x and the gate (workspace: 8 * batch * seqlen *
+ * nheads * headdim bytes, see mssm_ssd_workspace_size).  Any other problem with io_dtype
  * MSSM_F32 or MSSM_BF16 and dstate up to 256 runs token by token through the
  * recurrent update kernel (state from h0, written to final_state; the chunk
  * is then unused), with element-aligned pointers.  The state update's

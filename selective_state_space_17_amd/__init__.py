@@ -465,9 +465,10 @@ def ssd_fwd(x, delta, A, B, C, D=None, z=None, h0=None, chunk: int = 0, return_f
 
     x, z: [batch, seqlen, nheads, headdim]; delta: [batch, seqlen, nheads]; B, C: [batch, seqlen,
     ngroups, dstate], all bfloat16 or all float32; A, D: [nheads] float32; h0: [batch, nheads, headdim,
-    dstate] float32.  bfloat16 with headdim a multiple of 64 and dstate a multiple of 16 up to 128 runs
-    on the matrix-core block kernel; anything else (float32, other headdims, dstate up to 256) on the
-    recurrent kernel, token by token.
+    dstate] float32.  bfloat16 with headdim a multiple of 64 and dstate a multiple of 16 up to 256 runs
+    on the matrix-core block kernel (above 128 states as two shares of the states, with a workspace);
+    anything else (float32, other headdims, other dstate up to 256) on the recurrent kernel, token by
+    token.
     """
     return _ssd_call("mssm_ssd_fwd", x, delta, None, A, B, C, D, z, h0, chunk, return_final_state, out,
                      final_state, workspace, stream)

@@ -297,7 +297,9 @@ static int validate_ssd_desc(const mssm_ssd_desc* d, int64_t R, int64_t* Q, bool
       !mul_ok(t, 4, &t))
     return MSSM_ERR_INVALID_ARG;
   // the block kernel's grid: one workgroup per (batch, head, 64-wide headdim slice) at most
+  // (more than 128 states: one input per channel only, as two shares of the states)
   *matrix = d->io_dtype == MSSM_BF16 && mssm::ssd_supported(d->headdim, d->dstate) && mssm::ssd_rank_supported(R) &&
+            (d->dstate <= 128 || R == 1) &&
             d->batch * d->nheads * (d->headdim / 64) <= std::numeric_limits<int32_t>::max();
   *Q = q;
   return MSSM_OK;
@@ -887,6 +889,13 @@ int ssd_fwd_impl(const mssm_ssd_desc* desc, int64_t R, const void* x, const void
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need) return MSSM_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return MSSM_ERR_MISALIGNED;
+    for (int i = 0; i < 9; ++i)
+      if (overlap(workspace, static_cast<int64_t>(need), ins[i], inb[i])) return MSSM_ERR_INVALID_ARG;
+    if (overlap(workspace, static_cast<int64_t>(need), out, n_x * 2) ||
+        overlap(workspace, static_cast<int64_t>(need), final_state, b_st))
+      return MSSM_ERR_INVALID_ARG;
+    // the elementwise kernel adding the two shares: four columns per work-item
+    if (n_x / 4 > static_cast<int64_t>(std::numeric_limits<uint32_t>::max()) - 255) return MSSM_ERR_UNSUPPORTED;
   }
   mssm::SSDArgs a{};
   a.x = x; a.delta = delta; a.lam = want_lam ? lam : nullptr; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z;

@@ -205,6 +205,11 @@ struct SSDParams {
   int64_t batch, L, H, P, N, G;
   int R, rs;     // inputs per channel (MIMO rank) and log2 R
   int nps;       // headdim slices per head (P / 64)
+  // states n0 .. n0 + N - 1 of rows of Nr states (B, C, h0, final_state); with part != nullptr the
+  // kernel writes this share of sum_n C S (+ the in-block term) in fp32 to part, [B, L, H, R, P], and
+  // leaves D x, the gate and out to the kernel that adds the shares
+  int64_t Nr, n0;
+  float* part;
 };
 
 constexpr int kWaves = 8;
@@ -227,9 +232,10 @@ struct Carry {
 
 // MFMA 16x16x32 lane layout: A row / B column = lane % 16, k slots 8(lane/16)..+7;
 // accumulator element v of a lane is row 4 (lane / 16) + v, column lane % 16.
-template <int NP, bool TRAP, bool EPI>
+template <int NP, bool TRAP, bool EPI, bool PART>
 __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
   static_assert(NP == 64 || NP == 128, "padded state count");
+  static_assert(!(EPI && PART), "a share of the states leaves D x and the gate to the kernel adding the shares");
   constexpr int NT = NP / 16;               // 16-row state tiles of a state wave
   constexpr int NKB = NP / 32;              // 32-wide k blocks over the states
   constexpr int NPL = NP / 64;              // planes of a B or C block
@@ -288,14 +294,16 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
         *reinterpret_cast<u32x4*>(regions[r] + e) = u32x4{0, 0, 0, 0};
   }
 
-  const int64_t xstep = H * R * P, bcstep = G * R * N;
+  const int64_t Nr = p.Nr;   // B / C row length (all states)
+  const int64_t xstep = H * R * P, bcstep = G * R * Nr;
   const uint16_t* const x0 = p.x + (b * L * H + h) * R * P + p0;         // step 0, rank 0 of this unit
   const uint16_t* const z0 = (has_z ? p.z : p.x) + (b * L * H + h) * R * P + p0;
-  const uint16_t* const B0 = p.B + (b * L * G + g) * R * N;
-  const uint16_t* const C0 = p.C + (b * L * G + g) * R * N;
+  const uint16_t* const B0 = p.B + (b * L * G + g) * R * Nr + p.n0;
+  const uint16_t* const C0 = p.C + (b * L * G + g) * R * Nr + p.n0;
   const uint16_t* const d0 = p.delta + b * L * H + h;
   const uint16_t* const l0 = TRAP ? p.lam + b * L * H + h : nullptr;
-  uint16_t* const o0 = p.out + (b * L * H + h) * R * P + p0;
+  uint16_t* const o0 = PART ? nullptr : p.out + (b * L * H + h) * R * P + p0;
+  float* const po0 = PART ? p.part + (b * L * H + h) * R * P + p0 : nullptr;
   const uint32_t xs_a = lds_addr(&xs[0][0]), zs_a = lds_addr(&zs[0][0]), bs_a = lds_addr(&bs[0][0]),
                  cs_a = lds_addr(&cs_[0][0]), dls_a = lds_addr(&dls[0][0]), lls_a = lds_addr(&lls[0][0]);
 
@@ -333,7 +341,7 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
       const int rem = idx % (NPL * 8), pl = rem / 8, gr = rem % 8;
       const int col = pl * 64 + 8 * ((lane % 8) ^ lrow);
       if (col < Ni)
-        dma16((isC ? C0 : B0) + blk_off(k, 8 * gr + lrow, bcstep, N) + pl * 64,
+        dma16((isC ? C0 : B0) + blk_off(k, 8 * gr + lrow, bcstep, Nr) + pl * 64,
               (isC ? cs_a : bs_a) + slot * BBLK + pl * PLANE + gr * 1024);
     }
   };
@@ -515,7 +523,7 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
   for (int i = 0; i < NT; ++i) {
     const int n0 = 16 * i + 4 * q;
     if (p.h0 != nullptr && n0 < Ni) {
-      const float4 v = *reinterpret_cast<const float4*>(&p.h0[((b * H + h) * P + prow) * N + n0]);
+      const float4 v = *reinterpret_cast<const float4*>(&p.h0[((b * H + h) * P + prow) * Nr + p.n0 + n0]);
       S[i] = f32x4{v.x, v.y, v.z, v.w};
     } else {
       S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -596,7 +604,8 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
 
     // -- finish of block k - 1: + X^T M^T, + D x, * silu(z), store --
     if constexpr (FIN) {
-      uint16_t* const ob = o0 + (k - 1) * spb * xstep;
+      uint16_t* const ob = PART ? nullptr : o0 + (k - 1) * spb * xstep;
+      float* const pb = PART ? po0 + (k - 1) * spb * xstep : nullptr;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         f32x4 acc = mfma16(c.xf0, mf[j][0][0], c.y[j]);
@@ -619,7 +628,8 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
             for (int v = 0; v < 4; ++v) y[v] *= zz[v] * __builtin_amdgcn_rcpf(1.f + exp2_hw(-zz[v] * kLog2e));
           }
         }
-        *reinterpret_cast<u32x2*>(ob + oo[j]) = u32x2{pack2(y[0], y[1]), pack2(y[2], y[3])};
+        if constexpr (PART) *reinterpret_cast<float4*>(pb + oo[j]) = float4{y[0], y[1], y[2], y[3]};
+        else *reinterpret_cast<u32x2*>(ob + oo[j]) = u32x2{pack2(y[0], y[1]), pack2(y[2], y[3])};
       }
     }
 
@@ -699,7 +709,8 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
   // finish of the last block (its mask published)
   auto finish_last = [&](int64_t k, const Carry& c, int nv) {
     const unsigned char* Mr = &ms[k & 1][0][0];
-    uint16_t* const ob = o0 + k * spb * xstep;
+    uint16_t* const ob = PART ? nullptr : o0 + k * spb * xstep;
+    float* const pb = PART ? po0 + k * spb * xstep : nullptr;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       f32x4 acc = mfma16(c.xf0, lds_ld<bf16x8>(Mr, 16 * j * PROW + rd[0]), c.y[j]);
@@ -722,8 +733,10 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
           for (int v = 0; v < 4; ++v) y[v] *= zz[v] * __builtin_amdgcn_rcpf(1.f + exp2_hw(-zz[v] * kLog2e));
         }
       }
-      if (16 * j + lc < nv)
-        *reinterpret_cast<u32x2*>(ob + oo[j]) = u32x2{pack2(y[0], y[1]), pack2(y[2], y[3])};
+      if (16 * j + lc < nv) {
+        if constexpr (PART) *reinterpret_cast<float4*>(pb + oo[j]) = float4{y[0], y[1], y[2], y[3]};
+        else *reinterpret_cast<u32x2*>(ob + oo[j]) = u32x2{pack2(y[0], y[1]), pack2(y[2], y[3])};
+      }
     }
   };
 
@@ -752,31 +765,71 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
     for (int i = 0; i < NT; ++i) {
       const int n0 = 16 * i + 4 * q;
       if (n0 < Ni)
-        *reinterpret_cast<float4*>(&p.final_state[((b * H + h) * P + prow) * N + n0]) =
+        *reinterpret_cast<float4*>(&p.final_state[((b * H + h) * P + prow) * Nr + p.n0 + n0]) =
             float4{S[i][0], S[i][1], S[i][2], S[i][3]};
     }
   }
 }
 
-template <int NP, bool TRAP, bool EPI>
+template <int NP, bool TRAP, bool EPI, bool PART>
 hipError_t launch_np(const SSDParams& sp, hipStream_t stream) {
   const int64_t blocks = sp.batch * sp.H * sp.nps;
-  hipLaunchKernelGGL((ssd_kernel<NP, TRAP, EPI>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream, sp);
+  hipLaunchKernelGGL((ssd_kernel<NP, TRAP, EPI, PART>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+                     stream, sp);
   return hipGetLastError();
 }
 
 template <int NP, bool TRAP>
 hipError_t launch_gate(const SSDParams& sp, hipStream_t stream) {
+  if (sp.part != nullptr) return launch_np<NP, TRAP, false, true>(sp, stream);
   const bool epi = sp.z != nullptr || sp.D != nullptr;
-  return epi ? launch_np<NP, TRAP, true>(sp, stream) : launch_np<NP, TRAP, false>(sp, stream);
+  return epi ? launch_np<NP, TRAP, true, false>(sp, stream) : launch_np<NP, TRAP, false, false>(sp, stream);
 }
+
+template <bool TRAP>
+hipError_t launch_rule(const SSDParams& sp, hipStream_t stream) {
+  return sp.N <= 64 ? launch_gate<64, TRAP>(sp, stream) : launch_gate<128, TRAP>(sp, stream);
+}
+
+// More than 128 states: the two shares of the state sum, then out = (share 0 + share 1 + D x) * silu(z).
+// Four consecutive headdim columns per thread (P is a multiple of 64).
+__global__ __launch_bounds__(256) void ssd_add_shares(const float* part, int64_t n_x, const uint16_t* x,
+                                                      const uint16_t* z, const float* D, uint16_t* out,
+                                                      int64_t RP, int64_t H) {
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (i >= n_x) return;
+  const float4 s0 = *reinterpret_cast<const float4*>(part + i);
+  const float4 s1 = *reinterpret_cast<const float4*>(part + n_x + i);
+  float y[4] = {s0.x + s1.x, s0.y + s1.y, s0.z + s1.z, s0.w + s1.w};
+  if (D != nullptr) {
+    const float Dh = D[(i / RP) % H];
+    const u32x2 xv = *reinterpret_cast<const u32x2*>(x + i);
+    y[0] = __builtin_fmaf(Dh, lo_f(xv[0]), y[0]);
+    y[1] = __builtin_fmaf(Dh, hi_f(xv[0]), y[1]);
+    y[2] = __builtin_fmaf(Dh, lo_f(xv[1]), y[2]);
+    y[3] = __builtin_fmaf(Dh, hi_f(xv[1]), y[3]);
+  }
+  if (z != nullptr) {
+    const u32x2 zv = *reinterpret_cast<const u32x2*>(z + i);
+    const float zz[4] = {lo_f(zv[0]), hi_f(zv[0]), lo_f(zv[1]), hi_f(zv[1])};
+#pragma unroll
+    for (int v = 0; v < 4; ++v) y[v] *= zz[v] * __builtin_amdgcn_rcpf(1.f + exp2_hw(-zz[v] * kLog2e));
+  }
+  *reinterpret_cast<u32x2*>(out + i) = u32x2{pack2(y[0], y[1]), pack2(y[2], y[3])};
+}
+
+size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
 }  // namespace
 
-bool ssd_supported(int64_t P, int64_t N) { return P % PB == 0 && P > 0 && N % 16 == 0 && N > 0 && N <= 128; }
+bool ssd_supported(int64_t P, int64_t N) { return P % PB == 0 && P > 0 && N % 16 == 0 && N > 0 && N <= 256; }
 bool ssd_rank_supported(int64_t R) { return R == 1 || R == 2 || R == 4 || R == 8 || R == 16; }
 
-size_t ssd_workspace_bytes(int64_t, int64_t, int64_t, int64_t, int64_t, int64_t, int64_t) { return 0; }
+// more than 128 states (one input per channel): the two shares of the state sum, fp32 [2][B, L, H, P]
+size_t ssd_workspace_bytes(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_t, int64_t) {
+  if (N <= 128) return 0;
+  return align256(sizeof(float) * 2 * static_cast<size_t>(batch * L * H * P));
+}
 
 hipError_t ssd_launch(const SSDArgs& a, hipStream_t stream) {
   SSDParams sp{};
@@ -796,12 +849,27 @@ hipError_t ssd_launch(const SSDArgs& a, hipStream_t stream) {
   sp.rs = 0;
   while ((1 << sp.rs) < sp.R) ++sp.rs;
   sp.nps = static_cast<int>(a.P / PB);
-  if (a.lam != nullptr) {
-    if (a.N <= 64) return launch_gate<64, true>(sp, stream);
-    return launch_gate<128, true>(sp, stream);
+  sp.Nr = a.N;
+  sp.n0 = 0;
+  sp.part = nullptr;
+  auto run = [&](const SSDParams& q) { return a.lam != nullptr ? launch_rule<true>(q, stream) : launch_rule<false>(q, stream); };
+  if (a.N <= 128) return run(sp);
+  // states 0..127 and 128..N-1 as two shares (the sum over states is linear in them up to D x and the gate)
+  const int64_t n_x = a.batch * a.L * a.H * a.P;
+  float* part = static_cast<float*>(a.workspace);
+  for (int s = 0; s < 2; ++s) {
+    SSDParams q = sp;
+    q.n0 = 128 * s;
+    q.N = s == 0 ? 128 : a.N - 128;
+    q.part = part + s * n_x;
+    const hipError_t e = run(q);
+    if (e != hipSuccess) return e;
   }
-  if (a.N <= 64) return launch_gate<64, false>(sp, stream);
-  return launch_gate<128, false>(sp, stream);
+  if (n_x == 0) return hipSuccess;
+  const int64_t blocks = (n_x / 4 + 255) / 256;
+  hipLaunchKernelGGL(ssd_add_shares, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, part, n_x, sp.x,
+                     sp.z, sp.D, sp.out, a.R * a.P, a.H);
+  return hipGetLastError();
 }
 
 }  // namespace mssm

@@ -173,7 +173,7 @@ def test_ssd_validation(kw, expect):
 
 # Shapes and dtypes the matrix-core block kernel does not take: accepted, and run through the recurrent
 # update kernel. A null x proves the descriptor passed (the pointer checks reject it) without launching.
-RECURRENT_SSD = [dict(io_dtype=M.MSSM_F32), dict(headdim=24), dict(headdim=96), dict(dstate=20), dict(dstate=256),
+RECURRENT_SSD = [dict(io_dtype=M.MSSM_F32), dict(headdim=24), dict(headdim=96), dict(dstate=20), dict(dstate=200),
                  dict(dstate=6)]
 
 
@@ -206,6 +206,15 @@ def test_ssd_route():
     for r in (3, 5, 32, 64):
         assert M.ssd_mimo_plan(8, 4096, 32, 64, 128, 1, r) == rec
     assert M.ssd_mimo_plan(1, 8, 4, 64, 64, 1, 4, io_dtype=M.MSSM_F32) == rec
+    # more than 128 states: the block kernel on two shares of the states, one input per channel only
+    for n in (144, 192, 256):
+        assert M.ssd_plan(8, 4096, 32, 64, n, 1, 256) == block
+        assert M.ssd_mimo_plan(8, 4096, 32, 64, n, 1, 1) == block
+        assert M.ssd_mimo_plan(8, 4096, 32, 64, n, 1, 2) == rec
+    # its workspace holds the two shares in fp32; up to 128 states none is needed
+    d = M.ssd_desc(2, 100, 3, 128, 256, 1)
+    assert M.lib.mssm_ssd_workspace_size(ctypes.byref(d)) == (2 * 4 * 2 * 100 * 3 * 128 + 255) // 256 * 256
+    assert M.lib.mssm_ssd_workspace_size(ctypes.byref(M.ssd_desc(2, 100, 3, 128, 128, 1))) == 0
     for r, st in ((0, M.MSSM_ERR_INVALID_ARG), (-1, M.MSSM_ERR_INVALID_ARG), (65, M.MSSM_ERR_UNSUPPORTED)):
         with pytest.raises(M.MssmError) as e:
             M.ssd_mimo_plan(1, 8, 4, 64, 64, 1, r)
@@ -221,6 +230,22 @@ def test_ssd_pointer_checks():
     assert _ssd_call(d, x=None) == M.MSSM_ERR_INVALID_ARG
     assert _ssd_call(d, x=BASE + 8) == M.MSSM_ERR_MISALIGNED
     assert _ssd_call(d, out=BASE + 16) == M.MSSM_ERR_INVALID_ARG
+
+
+def test_ssd_shares_workspace_checks():
+    # above 128 states the block kernel needs its workspace: missing, short, misaligned, or overlapping
+    d = M.ssd_desc(2, 128, 4, 64, 256, 1, 64)
+    need = M.lib.mssm_ssd_workspace_size(ctypes.byref(d))
+    assert need == 2 * 4 * 2 * 128 * 4 * 64
+
+    def call(ws, nbytes, out=BASE + 500 * MB):
+        return M.lib.mssm_ssd_fwd(ctypes.byref(d), BASE, BASE + 100 * MB, BASE + 200 * MB, BASE + 300 * MB,
+                                  BASE + 400 * MB, None, None, None, out, None, ws, nbytes, None)
+    assert call(None, 0) == M.MSSM_ERR_WORKSPACE
+    assert call(BASE + 600 * MB, need - 1) == M.MSSM_ERR_WORKSPACE
+    assert call(BASE + 600 * MB + 16, need) == M.MSSM_ERR_MISALIGNED
+    assert call(BASE + 400 * MB, need) == M.MSSM_ERR_INVALID_ARG       # overlaps C
+    assert call(BASE + 600 * MB, need, out=BASE + 600 * MB + need - 64) == M.MSSM_ERR_INVALID_ARG
 
 
 def _ssd3_call(desc, x=BASE, delta=BASE + 100 * MB, lam=BASE + 150 * MB, A=BASE + 200 * MB, B=BASE + 300 * MB,

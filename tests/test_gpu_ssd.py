@@ -45,6 +45,11 @@ CASES = [
     (2, 1000, 4, 64, 48, 1, True, True, True),
     (1, 777, 2, 192, 80, 2, False, False, True),
     (2, 300, 4, 64, 112, 2, True, True, False),
+    # more than 128 states: two shares of the states, added with D x and the gate by a third kernel
+    (2, 200, 4, 64, 256, 1, True, True, True),
+    (1, 130, 2, 128, 144, 2, False, True, False),   # a second share of 16 states
+    (2, 65, 3, 64, 192, 3, True, False, True),
+    (1, 1, 2, 64, 256, 1, True, True, True),
 ]
 
 
@@ -64,8 +69,9 @@ def test_ssd_chunk_argument(M, chunk):
     compare(M, s, f"chunk={chunk}", chunk=chunk)
 
 
-def test_ssd_delta_zero_keeps_state(M):
-    cfg = W.ssd_config(1, 300, 2, 64, 64, 1, cfg_id=602)
+@pytest.mark.parametrize("dstate", [64, 256])
+def test_ssd_delta_zero_keeps_state(M, dstate):
+    cfg = W.ssd_config(1, 300, 2, 64, dstate, 1, cfg_id=602 + dstate)
     s = W.make_ssd_inputs(cfg, with_h0=True)
     s.delta[:] = 0
     _, fin = run_gpu(M, s)
@@ -118,10 +124,11 @@ def test_config4_full(M):
     say("config4", st)
 
 
-@pytest.mark.parametrize("dstate", [48, 80])
+@pytest.mark.parametrize("dstate", [48, 80, 208])
 def test_ssd_padded_states_ignore_stale_lds(M, dstate):
-    """dstate 48 or 80 (padded to 64 or 128 inside): state rows past dstate must not pick up whatever an
-    earlier kernel left in LDS.  A forward scan over NaN inputs first leaves NaNs in the LDS of every CU."""
+    """dstate 48, 80 or 208 (padded to 64 or 128 inside, 208 as shares of 128 and 80): state rows past
+    dstate must not pick up whatever an earlier kernel left in LDS.  A forward scan over NaN inputs first
+    leaves NaNs in the LDS of every CU."""
     import torch
     big = W.scan_config(8, 512, 1536, 16, io="bf16", cfg_id=610)
     poison = W.make_scan_inputs(big)
@@ -132,3 +139,16 @@ def test_ssd_padded_states_ignore_stale_lds(M, dstate):
     cfg = W.ssd_config(2, 1000, 4, 64, dstate, 1, cfg_id=611 + dstate)
     s = W.make_ssd_inputs(cfg, with_D=True, with_z=True, with_h0=True)
     compare(M, s, f"ssd dstate {dstate} after NaN in LDS")
+
+
+def test_config17_full(M):
+    """Config 4's shape with 256 states (two shares of the states): every output and final-state element
+    against the oracle."""
+    cfg = W.CONFIGS[17]
+    say("config", cfg.name)
+    s = W.make_ssd_inputs(cfg)
+    out, fin = run_gpu(M, s, chunk=cfg.chunk)
+    ref, ref_fin = oracle.ssd_fwd(s.x, s.delta, s.A, s.B, s.C, None, None, None)
+    st = check(host64(out), ref, RTOL["bf16"], "config17 out")
+    check(host64(fin), ref_fin, RTOL["bf16"], "config17 final")
+    say("config17", st)

@@ -48,6 +48,8 @@ CASES = [
     (2, 1000, 4, 64, 48, 1, True, True, True),     # padded states, many block boundaries
     (1, 777, 2, 192, 80, 2, False, False, True),
     (2, 300, 4, 64, 112, 2, True, True, False),
+    (2, 300, 4, 64, 256, 2, True, True, True),     # two shares of the states
+    (1, 100, 2, 64, 176, 1, False, True, True),
 ]
 
 

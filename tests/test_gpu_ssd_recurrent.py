@@ -1,6 +1,6 @@
 """The SSD entry points on problems the matrix-core block kernel does not take (float32 I/O, headdim not a
-multiple of 64, dstate not a multiple of 16 or above 128): the library runs them through the recurrent
-update kernel, h0 in and final_state out, and the results must meet the same bar against the fp64 oracle."""
+multiple of 64, dstate not a multiple of 16): the library runs them through the recurrent update kernel, h0
+in and final_state out, and the results must meet the same bar against the fp64 oracle."""
 import numpy as np
 import pytest
 
@@ -24,7 +24,7 @@ def M():
 CASES = [
     (2, 150, 4, 32, 64, 1, "bf16", True, True, True, True),      # headdim 32
     (1, 70, 2, 96, 128, 2, "bf16", False, True, False, True),    # headdim 96
-    (2, 40, 2, 64, 256, 1, "bf16", True, False, True, True),     # dstate 256
+    (2, 40, 2, 48, 256, 1, "bf16", True, False, True, True),     # dstate 256 (headdim 48)
     (1, 65, 3, 64, 20, 3, "bf16", True, True, True, False),      # dstate 20, no final state
     (2, 100, 4, 64, 128, 2, "f32", True, True, True, True),      # float32 I/O at the block kernel's shape
     (1, 33, 2, 7, 5, 1, "f32", False, False, False, True),       # odd sizes: the scalar state path
@@ -36,6 +36,8 @@ CASES = [
 def _run(M, case, trap):
     import torch
     b, l, h, p, n, g, io, hd, hz, hh, hf = case
+    iod = M.MSSM_BF16 if io == "bf16" else M.MSSM_F32
+    assert M.ssd_plan(b, l, h, p, n, g, io_dtype=iod) == M.SSD_ROUTE_RECURRENT, case
     cfg = W.ssd_config(b, l, h, p, n, g, io=io, cfg_id=7800 + l + p + n + (50 if trap else 0))
     s = W.make_ssd_inputs(cfg, with_D=hd, with_z=hz, with_h0=hh)
     lam = W.make_ssd_lam(cfg) if trap else None

@@ -18,7 +18,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "selective_state_space_17_amd", "csrc")
-ALLOWED = re.compile(r"global_load_lds_(dwordx4|ushort)|global_store_dwordx2 ")
+ALLOWED = re.compile(r"global_load_lds_(dwordx4|ushort)|global_store_dwordx[24] ")
 VMEM = re.compile(r"(global_|buffer_|scratch_|flat_)")
 
 
@@ -76,7 +76,8 @@ def scan_asm(tmp_path_factory):
 
 def test_ssd_loops_hold_only_the_counted_memory_operations(ssd_asm):
     ks = _kernels(ssd_asm)
-    assert len(ks) == 8, sorted(ks)   # 64/128 states x two rules x with/without the D/z epilogue
+    # 64/128 states x two rules x (with / without the D, z epilogue, or a share of the states in fp32)
+    assert len(ks) == 12, sorted(ks)
     for name, body in ks.items():
         seen, bad = _loop_vmem(body)
         assert seen > 0, name

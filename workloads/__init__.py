@@ -189,6 +189,8 @@ CONFIGS = {
     # gradients of config 2's layer with 128 states per channel (the larger state sizes of the d_state sweep)
     16: ScanConfig("mamba1_130m_layer_bwd_n128_bf16", 16, 8, 2048, 1536, 128, BF16, "exp_log", return_final=False,
                    backward=True),
+    # config 4's shape with 256 states per head (the largest state size of the d_state sweep)
+    17: SSDConfig("mamba2_ssd_n256_bf16", 17, 8, 4096, 32, 64, 256, 1, 256),
 }
 
 

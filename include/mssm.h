@@ -119,7 +119,8 @@ typedef struct {
  * or 256; a chunk longer than 64 steps is evaluated as consecutive 64-step
  * blocks with the state carried between them (the same algebra, so only
  * rounding differs).  The matrix-core block kernel takes io_dtype MSSM_BF16
- * (the matrix cores take bf16 operands), headdim a multiple of 64, dstate a
+ * (the matrix cores take bf16 operands), headdim a multiple of 8 (it works in
+ * 64-wide slices, the last one cut at headdim), dstate a
  * multiple of 16 up to 128 (and, for the MIMO calls below, a rank of 1, 2,
  * 4, 8 or 16), or with one input per channel a multiple of 16 up to 256;
  * there the state never leaves the chip between blocks, and x,

@@ -465,7 +465,7 @@ def ssd_fwd(x, delta, A, B, C, D=None, z=None, h0=None, chunk: int = 0, return_f
 
     x, z: [batch, seqlen, nheads, headdim]; delta: [batch, seqlen, nheads]; B, C: [batch, seqlen,
     ngroups, dstate], all bfloat16 or all float32; A, D: [nheads] float32; h0: [batch, nheads, headdim,
-    dstate] float32.  bfloat16 with headdim a multiple of 64 and dstate a multiple of 16 up to 256 runs
+    dstate] float32.  bfloat16 with headdim a multiple of 8 and dstate a multiple of 16 up to 256 runs
     on the matrix-core block kernel (above 128 states as two shares of the states, with a workspace);
     anything else (float32, other headdims, other dstate up to 256) on the recurrent kernel, token by
     token.

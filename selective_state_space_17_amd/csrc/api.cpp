@@ -270,9 +270,9 @@ int mssm_selective_scan_fwd_noalloc(const mssm_scan_desc* desc, const void* x, c
 // --------------------------------------------------------------------------
 // Mamba-2 scalar-A multi-head form
 // --------------------------------------------------------------------------
-// *matrix: the shape and dtype the matrix-core block kernel takes (bf16 I/O, headdim a multiple of 64,
-// dstate a multiple of 16 up to 128, rank 1, 2, 4, 8 or 16); any other valid problem runs through the
-// recurrent update kernel.  R: inputs and outputs per channel (MIMO; 1 otherwise), 1..64.
+// *matrix: the shape and dtype the matrix-core block kernel takes (bf16 I/O, headdim a multiple of 8,
+// dstate a multiple of 16 up to 256 -- above 128 with one input per channel --, rank 1, 2, 4, 8 or 16);
+// any other valid problem runs through the recurrent update kernel.  R: inputs and outputs per channel (MIMO; 1 otherwise), 1..64.
 constexpr int64_t kMaxRank = 64;
 static int validate_ssd_desc(const mssm_ssd_desc* d, int64_t R, int64_t* Q, bool* matrix) {
   if (d == nullptr) return MSSM_ERR_INVALID_ARG;
@@ -300,7 +300,7 @@ static int validate_ssd_desc(const mssm_ssd_desc* d, int64_t R, int64_t* Q, bool
   // (more than 128 states: one input per channel only, as two shares of the states)
   *matrix = d->io_dtype == MSSM_BF16 && mssm::ssd_supported(d->headdim, d->dstate) && mssm::ssd_rank_supported(R) &&
             (d->dstate <= 128 || R == 1) &&
-            d->batch * d->nheads * (d->headdim / 64) <= std::numeric_limits<int32_t>::max();
+            d->batch * d->nheads * ((d->headdim + 63) / 64) <= std::numeric_limits<int32_t>::max();
   *Q = q;
   return MSSM_OK;
 }

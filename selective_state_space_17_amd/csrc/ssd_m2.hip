@@ -204,7 +204,7 @@ struct SSDParams {
   float* final_state;
   int64_t batch, L, H, P, N, G;
   int R, rs;     // inputs per channel (MIMO rank) and log2 R
-  int nps;       // headdim slices per head (P / 64)
+  int nps;       // headdim slices per head (P / 64, rounded up; the last one is cut at P)
   // states n0 .. n0 + N - 1 of rows of Nr states (B, C, h0, final_state); with part != nullptr the
   // kernel writes this share of sum_n C S (+ the in-block term) in fp32 to part, [B, L, H, R, P], and
   // leaves D x, the gate and out to the kernel that adds the shares
@@ -273,6 +273,7 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
   const int64_t hpg = p.H / p.G;
   const int64_t h = g * hpg + member / p.nps;
   const int64_t p0 = (member % p.nps) * PB;
+  const int ncol = static_cast<int>(p.P - p0 < PB ? p.P - p0 : PB);   // columns of this slice (a multiple of 8)
   const int64_t L = p.L, H = p.H, P = p.P, N = p.N, G = p.G;
   const int R = p.R, rs = p.rs;
   const int Ni = static_cast<int>(N);
@@ -321,13 +322,15 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
   // a lane's row within its 8-row group and its logical 16-byte chunk (stored at chunk lane % 8 of the row);
   // a block's offsets are formed at issue time, rows past the block's valid ones clamped to its last
   const int lrow = lane / 8;
-  auto blk_off = [&](int64_t k, int row, int64_t step, int64_t rank_stride) {
+  // (cols: the row's valid columns; a chunk past them loads chunk 0 again, so every lane still loads)
+  auto blk_off = [&](int64_t k, int row, int64_t step, int64_t rank_stride, int cols) {
     const int nv = k + 1 < nblocks ? QB : last_nv;
     const int ic = row < nv ? row : nv - 1;
-    return (k * spb + (ic >> rs)) * step + (ic & (R - 1)) * rank_stride + 8 * ((lane % 8) ^ (row % 8));
+    const int cc = 8 * ((lane % 8) ^ (row % 8));
+    return (k * spb + (ic >> rs)) * step + (ic & (R - 1)) * rank_stride + (cc < cols ? cc : 0);
   };
   auto issue_x = [&](int64_t k, int slot) {
-    const int64_t o = blk_off(k, 8 * w + lrow, xstep, P);
+    const int64_t o = blk_off(k, 8 * w + lrow, xstep, P, ncol);
     dma16(x0 + o, xs_a + slot * PLANE + w * 1024);
     if constexpr (EPI) {
       if (has_z) dma16(z0 + o, zs_a + slot * PLANE + w * 1024);
@@ -341,7 +344,7 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
       const int rem = idx % (NPL * 8), pl = rem / 8, gr = rem % 8;
       const int col = pl * 64 + 8 * ((lane % 8) ^ lrow);
       if (col < Ni)
-        dma16((isC ? C0 : B0) + blk_off(k, 8 * gr + lrow, bcstep, Nr) + pl * 64,
+        dma16((isC ? C0 : B0) + blk_off(k, 8 * gr + lrow, bcstep, Nr, PB) + pl * 64,
               (isC ? cs_a : bs_a) + slot * BBLK + pl * PLANE + gr * 1024);
     }
   };
@@ -518,11 +521,16 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
   // =========================== state waves ===========================
   // the state S^T, rows n = 16 i + 4 q + v, column p = p0 + 16 pt + lc
   const int64_t prow = p0 + 16 * pt + lc;
+  const bool prow_ok = prow < P;                      // this lane's state column exists
+  const bool scol_ok = p0 + 16 * pt + 4 * q < P;      // the four output columns this lane stores exist
+  // output stores this wave issues per block: every lane's four columns lie past P in a wave whose first
+  // column does (the slice is cut at a multiple of 8), and then the wave issues none
+  const int nst = 16 * pt < ncol ? 4 : 0;
   f32x4 S[NT];
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
     const int n0 = 16 * i + 4 * q;
-    if (p.h0 != nullptr && n0 < Ni) {
+    if (p.h0 != nullptr && n0 < Ni && prow_ok) {
       const float4 v = *reinterpret_cast<const float4*>(&p.h0[((b * H + h) * P + prow) * Nr + p.n0 + n0]);
       S[i] = f32x4{v.x, v.y, v.z, v.w};
     } else {
@@ -628,8 +636,10 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
             for (int v = 0; v < 4; ++v) y[v] *= zz[v] * __builtin_amdgcn_rcpf(1.f + exp2_hw(-zz[v] * kLog2e));
           }
         }
-        if constexpr (PART) *reinterpret_cast<float4*>(pb + oo[j]) = float4{y[0], y[1], y[2], y[3]};
-        else *reinterpret_cast<u32x2*>(ob + oo[j]) = u32x2{pack2(y[0], y[1]), pack2(y[2], y[3])};
+        if (scol_ok) {
+          if constexpr (PART) *reinterpret_cast<float4*>(pb + oo[j]) = float4{y[0], y[1], y[2], y[3]};
+          else *reinterpret_cast<u32x2*>(ob + oo[j]) = u32x2{pack2(y[0], y[1]), pack2(y[2], y[3])};
+        }
       }
     }
 
@@ -733,7 +743,7 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
           for (int v = 0; v < 4; ++v) y[v] *= zz[v] * __builtin_amdgcn_rcpf(1.f + exp2_hw(-zz[v] * kLog2e));
         }
       }
-      if (16 * j + lc < nv) {
+      if (16 * j + lc < nv && scol_ok) {
         if constexpr (PART) *reinterpret_cast<float4*>(pb + oo[j]) = float4{y[0], y[1], y[2], y[3]};
         else *reinterpret_cast<u32x2*>(ob + oo[j]) = u32x2{pack2(y[0], y[1]), pack2(y[2], y[3])};
       }
@@ -748,9 +758,9 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
     step(0, c, std::false_type{}, QB);
     advance();
     for (int64_t k = 1; k < nblocks; ++k) {
-      // outstanding may stay: the x (z) loads of block k + 1 and the four output stores of block k - 2,
-      // issued after the B/C loads of block k
-      wait_vm(vm_keep + (k >= 2 ? 4 : 0));
+      // outstanding may stay: the x (z) loads of block k + 1 and the output stores of block k - 2 (four,
+      // or none in a wave whose columns lie past the headdim), issued after the B/C loads of block k
+      wait_vm(vm_keep + (k >= 2 ? nst : 0));
       block_barrier();   // block k's data and arrays, and block k - 1's mask, are in LDS
       vm_keep = issue_ahead(k);
       step(k, c, std::true_type{}, QB);
@@ -764,7 +774,7 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
       const int n0 = 16 * i + 4 * q;
-      if (n0 < Ni)
+      if (n0 < Ni && prow_ok)
         *reinterpret_cast<float4*>(&p.final_state[((b * H + h) * P + prow) * Nr + p.n0 + n0]) =
             float4{S[i][0], S[i][1], S[i][2], S[i][3]};
     }
@@ -822,7 +832,7 @@ size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
 }  // namespace
 
-bool ssd_supported(int64_t P, int64_t N) { return P % PB == 0 && P > 0 && N % 16 == 0 && N > 0 && N <= 256; }
+bool ssd_supported(int64_t P, int64_t N) { return P % 8 == 0 && P > 0 && N % 16 == 0 && N > 0 && N <= 256; }
 bool ssd_rank_supported(int64_t R) { return R == 1 || R == 2 || R == 4 || R == 8 || R == 16; }
 
 // more than 128 states (one input per channel): the two shares of the state sum, fp32 [2][B, L, H, P]
@@ -848,7 +858,7 @@ hipError_t ssd_launch(const SSDArgs& a, hipStream_t stream) {
   sp.R = static_cast<int>(a.R);
   sp.rs = 0;
   while ((1 << sp.rs) < sp.R) ++sp.rs;
-  sp.nps = static_cast<int>(a.P / PB);
+  sp.nps = static_cast<int>((a.P + PB - 1) / PB);
   sp.Nr = a.N;
   sp.n0 = 0;
   sp.part = nullptr;

@@ -173,7 +173,7 @@ def test_ssd_validation(kw, expect):
 
 # Shapes and dtypes the matrix-core block kernel does not take: accepted, and run through the recurrent
 # update kernel. A null x proves the descriptor passed (the pointer checks reject it) without launching.
-RECURRENT_SSD = [dict(io_dtype=M.MSSM_F32), dict(headdim=24), dict(headdim=96), dict(dstate=20), dict(dstate=200),
+RECURRENT_SSD = [dict(io_dtype=M.MSSM_F32), dict(headdim=20), dict(headdim=100), dict(dstate=20), dict(dstate=200),
                  dict(dstate=6)]
 
 
@@ -206,6 +206,10 @@ def test_ssd_route():
     for r in (3, 5, 32, 64):
         assert M.ssd_mimo_plan(8, 4096, 32, 64, 128, 1, r) == rec
     assert M.ssd_mimo_plan(1, 8, 4, 64, 64, 1, 4, io_dtype=M.MSSM_F32) == rec
+    # headdims that are multiples of 8: 64-wide slices, the last one cut at headdim
+    for pd in (8, 24, 48, 96, 136):
+        assert M.ssd_plan(2, 100, 4, pd, 64, 1) == block
+        assert M.ssd_mimo_plan(2, 100, 4, pd, 64, 1, 4) == block
     # more than 128 states: the block kernel on two shares of the states, one input per channel only
     for n in (144, 192, 256):
         assert M.ssd_plan(8, 4096, 32, 64, n, 1, 256) == block

@@ -45,8 +45,8 @@ def compare(M, cfg, s, lam, what, chunk=0):
 
 
 # (batch, seqlen, nheads, headdim, dstate, ngroups, rank, lam, D, z, h0): the block kernel (bf16, headdim a
-# multiple of 64, dstate a multiple of 16 up to 128, rank a power of two up to 16) -- ragged lengths, one step
-# across several blocks, padded states, groups, an odd unit count
+# multiple of 8, dstate a multiple of 16 up to 128, rank a power of two up to 16) -- ragged lengths, one step
+# across several blocks, padded states, groups, an odd unit count, headdim slices cut short
 BLOCK = [
     (1, 16, 2, 64, 64, 1, 4, True, False, False, True),
     (2, 100, 4, 64, 128, 1, 4, True, True, True, True),
@@ -56,6 +56,8 @@ BLOCK = [
     (1, 200, 3, 64, 32, 1, 4, True, True, False, True),
     (2, 130, 2, 64, 128, 1, 1, True, False, False, True),
     (1, 257, 4, 64, 128, 4, 2, False, False, False, False),
+    (1, 60, 2, 48, 64, 1, 4, True, True, True, True),
+    (2, 40, 3, 96, 32, 1, 2, False, True, False, True),
 ]
 
 

@@ -50,6 +50,13 @@ CASES = [
     (1, 130, 2, 128, 144, 2, False, True, False),   # a second share of 16 states
     (2, 65, 3, 64, 192, 3, True, False, True),
     (1, 1, 2, 64, 256, 1, True, True, True),
+    # headdims that are multiples of 8: the last 64-wide slice is cut at headdim
+    (2, 150, 4, 96, 64, 2, True, True, True),      # second slice of 32 columns
+    (1, 70, 3, 24, 128, 1, True, True, True),      # one slice of 24: a state wave with half its lanes
+    (2, 65, 2, 8, 32, 1, False, True, True),       # 8 columns
+    (1, 300, 2, 136, 48, 2, True, False, True),    # third slice of 8 columns
+    (2, 100, 2, 40, 256, 1, True, True, True),     # a cut slice with two shares of the states
+    (2, 0, 2, 16, 32, 1, True, True, True),        # no steps: the final state is h0
 ]
 
 

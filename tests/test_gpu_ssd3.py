@@ -50,6 +50,7 @@ CASES = [
     (2, 300, 4, 64, 112, 2, True, True, False),
     (2, 300, 4, 64, 256, 2, True, True, True),     # two shares of the states
     (1, 100, 2, 64, 176, 1, False, True, True),
+    (2, 130, 3, 80, 64, 1, True, True, True),      # headdim 80: a second slice of 16 columns
 ]
 
 

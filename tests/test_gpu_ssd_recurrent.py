@@ -1,5 +1,5 @@
 """The SSD entry points on problems the matrix-core block kernel does not take (float32 I/O, headdim not a
-multiple of 64, dstate not a multiple of 16): the library runs them through the recurrent update kernel, h0
+multiple of 8, dstate not a multiple of 16): the library runs them through the recurrent update kernel, h0
 in and final_state out, and the results must meet the same bar against the fp64 oracle."""
 import numpy as np
 import pytest
@@ -22,14 +22,14 @@ def M():
 
 # (batch, seqlen, nheads, headdim, dstate, ngroups, io, D, z, h0, final_state)
 CASES = [
-    (2, 150, 4, 32, 64, 1, "bf16", True, True, True, True),      # headdim 32
-    (1, 70, 2, 96, 128, 2, "bf16", False, True, False, True),    # headdim 96
-    (2, 40, 2, 48, 256, 1, "bf16", True, False, True, True),     # dstate 256 (headdim 48)
+    (2, 150, 4, 36, 64, 1, "bf16", True, True, True, True),      # headdim 36
+    (1, 70, 2, 100, 128, 2, "bf16", False, True, False, True),   # headdim 100
+    (2, 40, 2, 44, 256, 1, "bf16", True, False, True, True),     # dstate 256 (headdim 44)
     (1, 65, 3, 64, 20, 3, "bf16", True, True, True, False),      # dstate 20, no final state
     (2, 100, 4, 64, 128, 2, "f32", True, True, True, True),      # float32 I/O at the block kernel's shape
     (1, 33, 2, 7, 5, 1, "f32", False, False, False, True),       # odd sizes: the scalar state path
     (2, 0, 2, 16, 16, 1, "f32", True, True, True, True),         # no steps: final state = h0
-    (1, 0, 2, 16, 16, 1, "bf16", False, False, False, True),     # no steps, no h0: final state = 0
+    (1, 0, 2, 12, 16, 1, "bf16", False, False, False, True),     # no steps, no h0: final state = 0
 ]
 
 
@@ -76,7 +76,8 @@ def test_ssd_trapezoidal_recurrent_route(M, case):
 def test_ssd_recurrent_route_matches_update(M):
     """The routed sequence is the update entry point from h0, bit for bit (same kernel, same order)."""
     import torch
-    cfg = W.ssd_config(2, 50, 4, 32, 64, 2, io="bf16", cfg_id=7890)
+    assert M.ssd_plan(2, 50, 4, 36, 64, 2) == M.SSD_ROUTE_RECURRENT
+    cfg = W.ssd_config(2, 50, 4, 36, 64, 2, io="bf16", cfg_id=7890)
     s = W.make_ssd_inputs(cfg, with_D=True, with_z=True, with_h0=True)
     ins = [dev(a) for a in (s.x, s.delta, s.A, s.B, s.C, s.D, s.z)]
     out, fin = M.ssd_fwd(*ins[:2], *ins[2:], dev(s.h0), return_final_state=True)

@@ -51,32 +51,34 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_digest(is_ssd: bool, decode: bool = False, backward: bool = False) -> str:
-    """Hash of the sources that make the workload's kernels (counters go stale when it changes)."""
+def source_digest(is_ssd: bool, decode: bool = False, backward: bool = False, train: bool = False) -> str:
+    """Hash of the sources that make the workload's kernels (counters go stale when they change)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "selective_state_space_17_amd", "csrc")
     kern = "bwd_m1.hip" if backward else ("decode.hip" if decode else ("ssd_m2.hip" if is_ssd else "scan_m1.hip"))
     h.update(open(os.path.join(csrc, kern), "rb").read())
+    if train:   # a training step runs the checkpointing forward too
+        h.update(open(os.path.join(csrc, "scan_m1.hip"), "rb").read())
     return h.hexdigest()[:16]
 
 
-def kernel_tags(is_ssd: bool, decode: bool = False, backward: bool = False):
+def kernel_tags(is_ssd: bool, decode: bool = False, backward: bool = False, train: bool = False):
     """Name fragments of every kernel one call of the workload launches (the first names the dominant one)."""
     if backward:
-        return ("scan_bwd_kernel", "bwd_reduce", "bwd_finish")
+        return ("scan_bwd_kernel", "bwd_reduce", "bwd_finish") + (("wide_kernel",) if train else ())
     if decode:
         return ("ssd_update_kernel", "ssdm_update_kernel") if is_ssd else ("scan_update_kernel",)
     return ("ssd_kernel", "ssd_add_shares") if is_ssd else ("wide_kernel", "lane_kernel", "scan_kernel", "carry_kernel")
 
 
-def load_traffic(workload: str, is_ssd: bool, decode: bool = False, backward: bool = False):
+def load_traffic(workload: str, is_ssd: bool, decode: bool = False, backward: bool = False, train: bool = False):
     """HBM bytes per launch of the dominant kernel from committed rocprofv3 counters, if they were
     taken on the current kernel sources (else None)."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     t = json.load(open(path))
-    if t.get("source_digest") != source_digest(is_ssd, decode, backward):
+    if t.get("source_digest") != source_digest(is_ssd, decode, backward, train):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -90,12 +92,13 @@ def _counter_rows(d, counter):
 def summarize_counters(cfg, is_ssd, d, copy_mib):
     """Turn the four rocprofv3 --pmc runs under d (workload FETCH_SIZE / WRITE_SIZE, copy FETCH_SIZE /
     WRITE_SIZE) into HBM bytes per call of the workload (every kernel the call launches, summed; the
-    calls are counted by the dominant kernel's dispatches), each counter scaled by what it reads for a
-    device copy of copy_mib MiB, and write profiles/traffic_<workload>.json."""
-    bwd = getattr(cfg, "backward", False) or getattr(cfg, "train", False)   # the gradient kernel dominates
-    tags = kernel_tags(is_ssd, cfg.decode, bwd)
+    calls are counted by the dispatches of the kernel a call launches least often), each counter scaled by
+    what it reads for a device copy of copy_mib MiB, and write profiles/traffic_<workload>.json."""
+    train = getattr(cfg, "train", False)
+    bwd = getattr(cfg, "backward", False) or train   # the gradient kernel dominates
+    tags = kernel_tags(is_ssd, cfg.decode, bwd, train)
     copy_bytes = copy_mib << 20
-    res = {"workload": cfg.name, "source_digest": source_digest(is_ssd, cfg.decode, bwd),
+    res = {"workload": cfg.name, "source_digest": source_digest(is_ssd, cfg.decode, bwd, train),
            "copy_bytes": copy_bytes, "algorithmic_bytes_per_launch": cfg.algorithmic_bytes()}
     total = 0.0
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
@@ -109,13 +112,17 @@ def summarize_counters(cfg, is_ssd, d, copy_mib):
         if not rows:
             raise SystemExit(f"no {tags} dispatches with {counter} under {d}")
         names = sorted(set(n for n, _ in rows))
-        # the dominant kernel: the one moving the most bytes; the calls: the dispatches of the kernel a call
-        # launches least often (once; the SSD kernel runs twice per call above 128 states)
+        # the dominant kernel: the one moving the most bytes.  Per call, each kernel's average bytes per
+        # dispatch times the dispatches a call makes of it: a whole multiple of the fewest dispatches of any
+        # of the call's kernels (the SSD kernel runs twice per call above 128 states), else once (the set-up
+        # of a training-step run launches the gradient kernels alone as well)
         name = max(names, key=lambda k: sum(v for n, v in rows if n == k))
-        calls = min(sum(1 for n, _ in rows if n == k) for k in names)
-        kib = sum(v for _, v in rows) / calls
+        count = {k: sum(1 for n, _ in rows if n == k) for k in names}
+        calls = min(count.values())
+        mult = {k: (count[k] // calls if count[k] % calls == 0 else 1) for k in names}
+        kib = sum(sum(v for n, v in rows if n == k) / count[k] * mult[k] for k in names)
         res["kernel"] = name
-        res["kernels_per_call"] = {k: sum(1 for n, _ in rows if n == k) / calls for k in names}
+        res["kernels_per_call"] = mult
         res[counter] = {"kib_per_call": kib, "calls": calls, "copy_kib": copy_kib,
                         "scale": factor, "bytes_per_launch": kib * 1024.0 * factor}
         total += kib * 1024.0 * factor
@@ -463,7 +470,7 @@ def main():
 
     upd_s = cfg.updates / (wall / args.steps)
     kern_s = ms * 1e-3
-    traffic = load_traffic(cfg.name, is_ssd, decode, backward or train)
+    traffic = load_traffic(cfg.name, is_ssd, decode, backward or train, train)
     # the headline roofline is HBM: algorithmic bytes over the event-timed call
     roof = {"bound": "hbm", "achieved": alg_bytes / kern_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / PEAK_HBM_GBS

@@ -45,6 +45,20 @@ def _ssd_case(seed):
     return b, l, h, p, n, g, bool(r.integers(2)), bool(r.integers(2)), bool(r.integers(2))
 
 
+def _ssd_case_any(seed):
+    """Shapes off the 64/128 grid: either I/O type, headdims that are or are not a multiple of 8 and dstate
+    up to 256, so that random cases reach the recurrent route, the cut headdim slices and the two-share
+    block route as well."""
+    r = np.random.default_rng(seed)
+    g = int(r.choice([1, 1, 2, 4]))
+    h = g * int(r.integers(1, 4))
+    p = int(8 * r.integers(1, 21)) if r.integers(2) else int(r.integers(1, 161))
+    n = int(r.integers(1, 257))
+    io = str(r.choice(["f32", "bf16", "bf16"]))
+    b, l = int(r.integers(1, 3)), int(r.integers(1, 300))
+    return b, l, h, p, n, g, io, bool(r.integers(2)), bool(r.integers(2)), bool(r.integers(2))
+
+
 SCAN_SEEDS = list(range(7100, 7114))
 SSD_SEEDS = list(range(7200, 7210))
 
@@ -99,6 +113,21 @@ def test_fuzz_ssd_fwd(M, seed):
     ref, ref_fin = oracle.ssd_fwd(s.x, s.delta, s.A, s.B, s.C, s.D, s.z, s.h0)
     check(host64(out), ref, RTOL["bf16"], f"{case} out")
     check(host64(fin), ref_fin, RTOL["bf16"], f"{case} final_state")
+
+
+@pytest.mark.parametrize("seed", list(range(7220, 7232)))
+def test_fuzz_ssd_fwd_any_shape(M, seed):
+    import torch
+    b, l, h, p, n, g, io, hd, hz, hh = case = _ssd_case_any(seed)
+    say("fuzz ssd fwd any shape", seed, case)
+    cfg = W.ssd_config(b, l, h, p, n, g, io=io, cfg_id=seed)
+    s = W.make_ssd_inputs(cfg, with_D=hd, with_z=hz, with_h0=hh)
+    out, fin = M.ssd_fwd(dev(s.x), dev(s.delta), dev(s.A), dev(s.B), dev(s.C), dev(s.D), dev(s.z), dev(s.h0),
+                         return_final_state=True)
+    torch.cuda.synchronize()
+    ref, ref_fin = oracle.ssd_fwd(s.x, s.delta, s.A, s.B, s.C, s.D, s.z, s.h0)
+    check(host64(out), ref, RTOL[io], f"{case} out")
+    check(host64(fin), ref_fin, RTOL[io], f"{case} final_state")
 
 
 @pytest.mark.parametrize("seed", SSD_SEEDS[:6])
@@ -202,6 +231,27 @@ def test_fuzz_scan_bwd(M, seed):
         g = M.selective_scan_bwd(*args, dev(dout), dev(dfin), checkpoints=ck)
         torch.cuda.synchronize()
         _compare_grads(g, ref, io, f"{case} from checkpoints")
+
+
+@pytest.mark.parametrize("seed", list(range(7310, 7316)))
+def test_fuzz_scan_bwd_wide_state(M, seed):
+    """Gradients with dstate above 16 (one to sixteen slices of 16 states, the last one ragged)."""
+    import torch
+    r = np.random.default_rng(seed)
+    io = str(r.choice(["f32", "bf16"]))
+    b, l, d = int(r.integers(1, 3)), int(r.integers(1, 300)), int(r.integers(1, 100))
+    n = int(r.integers(17, 257))
+    hd, hz, hh, hf = (bool(v) for v in r.integers(2, size=4))
+    case = (b, l, d, n, io, hd, hz, hh, hf)
+    say("fuzz scan bwd wide state", seed, case)
+    cfg = W.scan_config(b, l, d, n, io=io, has_D=hd, has_z=hz, cfg_id=seed)
+    inp = W.make_scan_inputs(cfg, with_h0=hh)
+    dout, dfin = W.make_scan_grads(cfg, with_dfinal=hf)
+    ref = oracle.scan_bwd(inp.x, inp.delta, inp.A, inp.B, inp.C, inp.D, inp.z, inp.h0, dout, dfin)
+    g = M.selective_scan_bwd(*[dev(a) for a in (inp.x, inp.delta, inp.A, inp.B, inp.C, inp.D, inp.z, inp.h0)],
+                             dev(dout), dev(dfin))
+    torch.cuda.synchronize()
+    _compare_grads(g, ref, io, f"{case}")
 
 
 @pytest.mark.parametrize("seed", list(range(7400, 7406)))

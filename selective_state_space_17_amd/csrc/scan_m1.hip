@@ -1078,6 +1078,14 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
   }
 }
 
+// 8 bytes of a transposing LDS read (ds_read_b64_tr_b16); the element layout is at its use
+__device__ __forceinline__ u32x2 tr_read(const unsigned char* p) {
+  typedef short i16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(const_cast<unsigned char*>(p)));
+  return __builtin_bit_cast(u32x2, v);
+}
+
 template <int IO, int MODE>
 __global__ __launch_bounds__(kWave) void lane_kernel(KernelParams p) {
   using namespace lanek;
@@ -1178,19 +1186,15 @@ __global__ __launch_bounds__(kWave) void lane_kernel(KernelParams p) {
     }
   };
 
-  // HZ: z is given (a compile-time copy of has_z, so that a tile is one straight block of code)
-  auto step = [&](auto hz, int buf, int s) {
+  // one step from its widened values (zv: z, read only when HZ)
+  auto step_v = [&](auto hz, int s, float d, float u, float zv, float bv, float cv) {
     constexpr bool HZ = decltype(hz)::value;
-    const float d = to_f32(*reinterpret_cast<const T*>(&dls[buf][s * RBY + lane * ES]));
-    const float u = to_f32(*reinterpret_cast<const T*>(&xs[buf][s * RBY + lane * ES]));
-    const float bv = to_f32(*reinterpret_cast<const T*>(&bcs[buf][(s * 16 + (lane & 15)) * ES]));
-    const float cv = to_f32(*reinterpret_cast<const T*>(&bcs[buf][BCB + (s * 16 + (lane & 15)) * ES]));
     fast_updates<1, 0, 16>(h, A2, d, d * u, bv, bv);
     float a0, a1;
     FastReadout<1>::run(a0, a1, cv, h);
     float y = a0 + a1;
     if constexpr (HZ) {
-      const float gz = silu_gate(to_f32(*reinterpret_cast<const T*>(&zs[buf][s * RBY + lane * ES])));
+      const float gz = silu_gate(zv);
       y = __builtin_fmaf(y, gz, gz * (Dv * u));
     } else {
       y = __builtin_fmaf(Dv, u, y);
@@ -1199,6 +1203,40 @@ __global__ __launch_bounds__(kWave) void lane_kernel(KernelParams p) {
     if constexpr (MODE != kSingle) {
       S += d;
       negseen |= (d < 0.f);
+    }
+  };
+  // HZ: z is given (a compile-time copy of has_z, so that a tile is one straight block of code)
+  auto step = [&](auto hz, int buf, int s) {
+    constexpr bool HZ = decltype(hz)::value;
+    const float d = to_f32(*reinterpret_cast<const T*>(&dls[buf][s * RBY + lane * ES]));
+    const float u = to_f32(*reinterpret_cast<const T*>(&xs[buf][s * RBY + lane * ES]));
+    const float bv = to_f32(*reinterpret_cast<const T*>(&bcs[buf][(s * 16 + (lane & 15)) * ES]));
+    const float cv = to_f32(*reinterpret_cast<const T*>(&bcs[buf][BCB + (s * 16 + (lane & 15)) * ES]));
+    const float zv = HZ ? to_f32(*reinterpret_cast<const T*>(&zs[buf][s * RBY + lane * ES])) : 0.f;
+    step_v(hz, s, d, u, zv, bv, cv);
+  };
+  // Four steps from five transposing LDS reads (bf16 only).  In each 16-lane group, lanes 4k..4k+3
+  // point at four consecutive 2-byte elements of row s0 + k and lane j receives element j of each
+  // row k = 0..3.  For x, delta and z the group's 16 elements are its 16 channels, so lane c gets its
+  // channel's values of steps s0..s0+3; for B and C they are the 16 states, so lane n of every row gets
+  // B_n and C_n of those steps, where the DPP operands of the updates and the readout take them from.
+  const int tr_k = (lane & 15) >> 2, tr_i = lane & 3;
+  const int tr_x = tr_k * RBY + 32 * (lane >> 4) + 8 * tr_i;   // + s0 * RBY
+  const int tr_b = tr_k * 32 + 8 * tr_i;                        // + s0 * 32 (B), + BCB (C)
+  auto quad = [&](auto hz, int buf, int s0) {
+    constexpr bool HZ = decltype(hz)::value;
+    const u32x2 dq = tr_read(&dls[buf][s0 * RBY + tr_x]);
+    const u32x2 xq = tr_read(&xs[buf][s0 * RBY + tr_x]);
+    const u32x2 bq = tr_read(&bcs[buf][s0 * 32 + tr_b]);
+    const u32x2 cq = tr_read(&bcs[buf][BCB + s0 * 32 + tr_b]);
+    u32x2 zq = u32x2{0u, 0u};
+    if constexpr (HZ) zq = tr_read(&zs[buf][s0 * RBY + tr_x]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t sh = (k & 1) ? 0u : 16u;
+      const uint32_t mk = (k & 1) ? 0xffff0000u : 0xffffffffu;
+      auto wid = [&](const u32x2& q) { return __uint_as_float((q[k >> 1] << sh) & mk); };
+      step_v(hz, s0 + k, wid(dq), wid(xq), HZ ? wid(zq) : 0.f, wid(bq), wid(cq));
     }
   };
 
@@ -1229,8 +1267,13 @@ __global__ __launch_bounds__(kWave) void lane_kernel(KernelParams p) {
       if (prev_t0 >= 0) store_tile(prev_t0);
       const int64_t ns = (t_end - t0) < TT ? (t_end - t0) : TT;
       if (ns == TT) {
+        if constexpr (ES == 2) {
 #pragma unroll
-        for (int s = 0; s < TT; ++s) step(hz, buf, s);
+          for (int s0 = 0; s0 < TT; s0 += 4) quad(hz, buf, s0);
+        } else {
+#pragma unroll
+          for (int s = 0; s < TT; ++s) step(hz, buf, s);
+        }
       } else {
         for (int s = 0; s < static_cast<int>(ns); ++s) step(hz, buf, s);
       }

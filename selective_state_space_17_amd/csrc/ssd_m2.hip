@@ -387,62 +387,76 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
     block_barrier();
   }
 
+// per-row arrays of block k, formed by state wave 0 during block k - 1 (the mask waves are the longer
+// path through a block) and published by the barrier at the top of block k
+  auto make_arrays = [&](int64_t k, int slot, int slot_next) {
+    const int nv = k + 1 < nblocks ? QB : last_nv;
+    const bool valid = lane < nv;
+    const float d = valid ? __uint_as_float(dls[slot][lane] << 16) : 0.f;
+    float v = (lane & (R - 1)) == 0 ? d * a2 : 0.f;   // the step's decay enters at its first row
+    v += dppf<0x111, 0xf>(v);   // row_shr:1
+    v += dppf<0x112, 0xf>(v);   // row_shr:2
+    v += dppf<0x114, 0xf>(v);   // row_shr:4
+    v += dppf<0x118, 0xf>(v);   // row_shr:8
+    v += dppf<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
+    v += dppf<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
+    const float cs_end = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), kWave - 1));
+    float wf = d, wd = d;
+    if constexpr (TRAP) {
+      const float lm = valid ? __uint_as_float(lls[slot][lane] << 16) : 0.f;
+      // the next step's first row: in this block, or row 0 of the next block
+      const int jn = (lane | (R - 1)) + 1;
+      float dn = 0.f, ln = 0.f;
+      if (jn < QB) {
+        if (jn < nv) {
+          dn = __uint_as_float(dls[slot][jn] << 16);
+          ln = __uint_as_float(lls[slot][jn] << 16);
+        }
+      } else if (k + 1 < nblocks) {
+        dn = __uint_as_float(dls[slot_next][0] << 16);
+        ln = __uint_as_float(lls[slot_next][0] << 16);
+      }
+      wd = lm * d;
+      wf = __builtin_fmaf(1.f - ln, dn, wd);
+    }
+    float* A_ = &arr[k & 1][0][0];
+    A_[A_CS * QB + lane] = v;
+    A_[A_ECS * QB + lane] = exp2_hw(v);
+    A_[A_WF * QB + lane] = wf;
+    A_[A_WD * QB + lane] = wd;
+    A_[A_WL * QB + lane] = exp2_hw(cs_end - v) * wf;
+  };
+
   if (!state_wave) {
     // =========================== mask waves ===========================
-
-    // per-row arrays of block k (every loading wave computes them and writes the same values)
-    auto make_arrays = [&](int64_t k, int slot, int slot_next) {
-      const int nv = k + 1 < nblocks ? QB : last_nv;
-      const bool valid = lane < nv;
-      const float d = valid ? __uint_as_float(dls[slot][lane] << 16) : 0.f;
-      float v = (lane & (R - 1)) == 0 ? d * a2 : 0.f;   // the step's decay enters at its first row
-      v += dppf<0x111, 0xf>(v);   // row_shr:1
-      v += dppf<0x112, 0xf>(v);   // row_shr:2
-      v += dppf<0x114, 0xf>(v);   // row_shr:4
-      v += dppf<0x118, 0xf>(v);   // row_shr:8
-      v += dppf<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
-      v += dppf<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
-      const float cs_end = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), kWave - 1));
-      float wf = d, wd = d;
-      if constexpr (TRAP) {
-        const float lm = valid ? __uint_as_float(lls[slot][lane] << 16) : 0.f;
-        // the next step's first row: in this block, or row 0 of the next block
-        const int jn = (lane | (R - 1)) + 1;
-        float dn = 0.f, ln = 0.f;
-        if (jn < QB) {
-          if (jn < nv) {
-            dn = __uint_as_float(dls[slot][jn] << 16);
-            ln = __uint_as_float(lls[slot][jn] << 16);
-          }
-        } else if (k + 1 < nblocks) {
-          dn = __uint_as_float(dls[slot_next][0] << 16);
-          ln = __uint_as_float(lls[slot_next][0] << 16);
-        }
-        wd = lm * d;
-        wf = __builtin_fmaf(1.f - ln, dn, wd);
-      }
-      float* A_ = &arr[k & 1][0][0];
-      A_[A_CS * QB + lane] = v;
-      A_[A_ECS * QB + lane] = exp2_hw(v);
-      A_[A_WF * QB + lane] = wf;
-      A_[A_WD * QB + lane] = wd;
-      A_[A_WL * QB + lane] = exp2_hw(cs_end - v) * wf;
-    };
 
     // mask tiles: G^T = B . C^T for s tiles 0..3 and t tile pt, decayed and weighted; element v of s tile sj
     // is row s = 16 sj + 4 q + v, column t = 16 pt + lc.  Kept up to the diagonal (an earlier or the same
     // step), with the own-step weight on it (the same step); past the diagonal the exponent takes a bias
     // of -inf, so the element comes out 0 (a multiply by 0 could meet exp2 = inf there).
-    float kbias[4][4];
-    uint32_t ownm[4][4];
+    // Only the ten tile pairs (t tile, s tile) with s <= t are nonzero (the rows of an s tile past t are
+    // later steps); the other six stay at the zeros the set-up wrote.  They are shared out three per
+    // mask wave, the last two waves repeating one of theirs (the same values written twice), so no wave
+    // has more than three: wave pt takes pairs (tp[i], sp[i]).
+    int tp[3], sp[3];
+    switch (pt) {
+      case 0: tp[0] = 3; sp[0] = 3; tp[1] = 3; sp[1] = 2; tp[2] = 3; sp[2] = 1; break;
+      case 1: tp[0] = 3; sp[0] = 0; tp[1] = 2; sp[1] = 2; tp[2] = 2; sp[2] = 1; break;
+      case 2: tp[0] = 2; sp[0] = 0; tp[1] = 1; sp[1] = 1; tp[2] = 1; sp[2] = 1; break;
+      default: tp[0] = 1; sp[0] = 0; tp[1] = 0; sp[1] = 0; tp[2] = 0; sp[2] = 0; break;
+    }
+    // On a diagonal pair element v of a lane is kept where its s row's step is at most its t row's
+    // (16 t is a multiple of R, so the test does not depend on the tile), with the own-step weight where
+    // the two are the same step; past the diagonal the exponent takes a bias of -inf, so the element
+    // comes out 0 (a multiply by 0 could meet exp2 = inf there).  Off the diagonal every element is kept.
+    float dbias[4];
+    uint32_t downm[4];
 #pragma unroll
-    for (int sj = 0; sj < 4; ++sj)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int ss = (16 * sj + 4 * q + v) >> rs, st = (16 * pt + lc) >> rs;
-        kbias[sj][v] = ss <= st ? 0.f : -__builtin_inff();
-        ownm[sj][v] = ss == st ? 0xffffffffu : 0u;
-      }
+    for (int v = 0; v < 4; ++v) {
+      const int ss = (4 * q + v) >> rs, st = lc >> rs;
+      dbias[v] = ss <= st ? 0.f : -__builtin_inff();
+      downm[v] = ss == st ? 0xffffffffu : 0u;
+    }
     // 16-byte chunk (4 kb + q) of row 16 j + lc: the row tile part (16 j rows) and the plane (kb / 2) are
     // constants of each read
     int rd[2];
@@ -450,35 +464,37 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
     for (int hh = 0; hh < 2; ++hh) rd[hh] = swz(lc, 4 * hh + q);
     // The mask is stored as M^T: row t, and within each 32-row k block the 8 s values a lane of group q
     // contracts, in the order of the X^T fragments (s = 32 kb + 16 (e / 4) + 4 q + e % 4 in slot 8 q + e)
-    // G^T fragments of block k: C rows of t tile pt, B rows of s tiles 0..3 (all reads issued first)
-    struct GFrag { bf16x8 c[NKB], b[4][NKB]; };
+    // G^T fragments of block k: C rows of t tile tp[i], B rows of s tile sp[i] (all reads issued first)
+    struct GFrag { bf16x8 c[3][NKB], b[3][NKB]; };
     auto g_reads = [&](const GFrag*, int64_t) {
       GFrag f;
       const unsigned char* Bk = &bs[sb][0];
-      const unsigned char* Ck = &cs_[sb][0] + 16 * pt * PROW;
+      const unsigned char* Ck = &cs_[sb][0];
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const int po = (kb / 2) * PLANE;
-        f.c[kb] = lds_ld<bf16x8>(Ck, po + rd[kb % 2]);
+      for (int i = 0; i < 3; ++i)
 #pragma unroll
-        for (int sj = 0; sj < 4; ++sj) f.b[sj][kb] = lds_ld<bf16x8>(Bk, po + 16 * sj * PROW + rd[kb % 2]);
-      }
+        for (int kb = 0; kb < NKB; ++kb) {
+          const int po = (kb / 2) * PLANE;
+          f.c[i][kb] = lds_ld<bf16x8>(Ck, po + 16 * tp[i] * PROW + rd[kb % 2]);
+          f.b[i][kb] = lds_ld<bf16x8>(Bk, po + 16 * sp[i] * PROW + rd[kb % 2]);
+        }
       return f;
     };
     auto mask = [&](int64_t k, const GFrag& f) {
       const float* Au = &arr[k & 1][0][0];
-      unsigned char* Mw = &ms[k & 1][0][0] + 16 * pt * PROW;
-      f32x4 gacc[4];
+      unsigned char* Mw = &ms[k & 1][0][0];
+      f32x4 gacc[3];
 #pragma unroll
-      for (int sj = 0; sj < 4; ++sj) gacc[sj] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < 3; ++i) gacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int sj = 0; sj < 4; ++sj) gacc[sj] = mfma16(f.b[sj][kb], f.c[kb], gacc[sj]);
-      const float ct = Au[A_CS * QB + 16 * pt + lc];
+        for (int i = 0; i < 3; ++i) gacc[i] = mfma16(f.b[i][kb], f.c[i][kb], gacc[i]);
 #pragma unroll
-      for (int sj = 0; sj < 4; ++sj) {
-        const int s0 = 16 * sj + 4 * q;
+      for (int i = 0; i < 3; ++i) {
+        const bool diag = tp[i] == sp[i];
+        const float ct = Au[A_CS * QB + 16 * tp[i] + lc];
+        const int s0 = 16 * sp[i] + 4 * q;
         const float4 c4 = *reinterpret_cast<const float4*>(&Au[A_CS * QB + s0]);
         const float4 f4 = *reinterpret_cast<const float4*>(&Au[A_WF * QB + s0]);
         const float4 d4 = *reinterpret_cast<const float4*>(&Au[A_WD * QB + s0]);
@@ -486,20 +502,21 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
         float m[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float e = exp2_hw((ct - cc[v]) + kbias[sj][v]);
-          const float wsel = __uint_as_float((ownm[sj][v] & __float_as_uint(dd[v])) | (~ownm[sj][v] & __float_as_uint(ff[v])));
-          m[v] = gacc[sj][v] * e * wsel;
+          const uint32_t own = diag ? downm[v] : 0u;
+          const float e = exp2_hw((ct - cc[v]) + (diag ? dbias[v] : 0.f));
+          const float wsel = __uint_as_float((own & __float_as_uint(dd[v])) | (~own & __float_as_uint(ff[v])));
+          m[v] = gacc[i][v] * e * wsel;
         }
-        // s tile sj = 2 kb + hh: chunk 4 kb + q of row t, bytes 8 hh .. +7; bf16 hi and lo parts
+        // s tile sp = 2 kb + hh: chunk 4 kb + q of row t, bytes 8 hh .. +7; bf16 hi and lo parts
         const uint32_t h01 = pack2(m[0], m[1]), h23 = pack2(m[2], m[3]);
         const uint32_t l01 = pack2(m[0] - lo_f(h01), m[1] - hi_f(h01)), l23 = pack2(m[2] - lo_f(h23), m[3] - hi_f(h23));
-        *reinterpret_cast<u32x2*>(Mw + rd[sj / 2] + 8 * (sj % 2)) = u32x2{h01, h23};
-        *reinterpret_cast<u32x2*>(Mw + PLANE + rd[sj / 2] + 8 * (sj % 2)) = u32x2{l01, l23};
+        const int wo = 16 * tp[i] * PROW + (sp[i] >= 2 ? rd[1] : rd[0]) + 8 * (sp[i] & 1);
+        *reinterpret_cast<u32x2*>(Mw + wo) = u32x2{h01, h23};
+        *reinterpret_cast<u32x2*>(Mw + PLANE + wo) = u32x2{l01, l23};
       }
     };
 
     if (nblocks > 0) {
-      make_arrays(0, 0, 1);
       for (int64_t k = 0; k < nblocks; ++k) {
         // outstanding may stay: the x (z) loads of block k + 1, issued after the B/C loads of block k
         wait_vm(vm_keep);
@@ -510,7 +527,6 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
         vm_keep = issue_ahead(k);
         __builtin_amdgcn_sched_barrier(0);
         mask(k, gf);
-        make_arrays(k + 1, nxt(sd, NDS), nxt(nxt(sd, NDS), NDS));   // harmless past the last block
         advance();
       }
       block_barrier();   // pairs with the state waves' last barrier
@@ -751,11 +767,13 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
   };
 
   if (nblocks > 0) {
+    if (w == 0) make_arrays(0, 0, 1);
     wait_vm(vm_keep);
     block_barrier();   // block 0's data and arrays: pairs with the top of the mask waves' block 0
     Carry c;
     vm_keep = issue_ahead(0);
     step(0, c, std::false_type{}, QB);
+    if (w == 0) make_arrays(1, nxt(sd, NDS), nxt(nxt(sd, NDS), NDS));   // harmless past the last block
     advance();
     for (int64_t k = 1; k < nblocks; ++k) {
       // outstanding may stay: the x (z) loads of block k + 1 and the output stores of block k - 2 (four,
@@ -764,6 +782,7 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(SSDParams p) {
       block_barrier();   // block k's data and arrays, and block k - 1's mask, are in LDS
       vm_keep = issue_ahead(k);
       step(k, c, std::true_type{}, QB);
+      if (w == 0) make_arrays(k + 1, nxt(sd, NDS), nxt(nxt(sd, NDS), NDS));   // harmless past the last block
       advance();
     }
     block_barrier();   // the last block's mask is complete

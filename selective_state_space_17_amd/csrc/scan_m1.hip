@@ -1043,6 +1043,9 @@ __global__ __launch_bounds__(kThreads) void wide_kernel(KernelParams p) {
 // ---------------------------------------------------------------------------
 namespace lanek {
 constexpr int TT = 16;   // steps per tile
+// waves per workgroup: with bf16 eight (16 KB of LDS each, 128 KB, two waves on every SIMD of the CU);
+// fp32 tiles take 32 KB a wave, so one wave per workgroup
+constexpr int wpb(int io) { return io == 1 ? 8 : 1; }
 }
 
 __device__ __forceinline__ uint32_t lds_off(const void* p) {
@@ -1087,7 +1090,7 @@ __device__ __forceinline__ u32x2 tr_read(const unsigned char* p) {
 }
 
 template <int IO, int MODE>
-__global__ __launch_bounds__(kWave) void lane_kernel(KernelParams p) {
+__global__ __launch_bounds__(kWave * lanek::wpb(IO)) void lane_kernel(KernelParams p) {
   using namespace lanek;
   using T = typename IoType<IO>::T;
   constexpr int ES = sizeof(T);
@@ -1102,14 +1105,29 @@ __global__ __launch_bounds__(kWave) void lane_kernel(KernelParams p) {
   constexpr int NBC = (2 * BCB + 1023) / 1024;    // 16-byte loads per lane for B and C together
   static_assert(TB % 1024 == 0 && BCB % 16 == 0, "tile geometry");
 
-  __shared__ __attribute__((aligned(16))) unsigned char xs[2][TB];
-  __shared__ __attribute__((aligned(16))) unsigned char dls[2][TB];
-  __shared__ __attribute__((aligned(16))) unsigned char zs[2][TB];
-  __shared__ __attribute__((aligned(16))) unsigned char bcs[2][NBC * 1024];   // B [t][n], then C [t][n]
-  __shared__ __attribute__((aligned(16))) T ys[TT * kWave];                   // outputs [t][c]
+  constexpr int WPB = wpb(IO);
+  __shared__ __attribute__((aligned(16))) unsigned char xs_[WPB][2][TB];
+  __shared__ __attribute__((aligned(16))) unsigned char dls_[WPB][2][TB];
+  __shared__ __attribute__((aligned(16))) unsigned char zs_[WPB][2][TB];
+  __shared__ __attribute__((aligned(16))) unsigned char bcs_[WPB][2][NBC * 1024];   // B [t][n], then C [t][n]
+  __shared__ __attribute__((aligned(16))) T ys_[WPB][TT * kWave];                   // outputs [t][c]
+  __shared__ int prog[WPB];   // tiles each wave has finished (INT_MAX: no more work)
 
-  const int lane = threadIdx.x;
-  const int64_t bid = blockIdx.x;
+  const int lane = threadIdx.x % kWave;
+  const int w = WPB > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x / kWave) : 0;
+  auto& xs = xs_[w];
+  auto& dls = dls_[w];
+  auto& zs = zs_[w];
+  auto& bcs = bcs_[w];
+  T* const ys = &ys_[w][0];
+  const int64_t bid = static_cast<int64_t>(blockIdx.x) * WPB + w;   // this wave's unit
+  const int nunits_k = (MODE == kFixup) ? p.K - 1 : p.K;
+  const bool idle = bid >= p.batch * nunits_k * p.ngroups;   // a wave past the last unit of the grid
+  if constexpr (WPB > 1) {
+    if (lane == 0) prog[w] = idle ? INT_MAX : 0;
+    __syncthreads();
+  }
+  if (idle) return;
   const int cg = static_cast<int>(bid % p.ngroups);
   const int64_t rest = bid / p.ngroups;
   const int nchunks_here = (MODE == kFixup) ? p.K - 1 : p.K;
@@ -1252,6 +1270,16 @@ __global__ __launch_bounds__(kWave) void lane_kernel(KernelParams p) {
     }
   };
 
+  // Two waves of a workgroup share each SIMD (w and w ^ 4).  The SIMD issues from the older of two ready
+  // waves, so left alone one wave of a pair runs ahead and the other finishes its chunk alone, at the
+  // lower issue rate of a single wave.  At each tile a wave that has finished more tiles than its partner
+  // drops its priority, which keeps the pair within about a tile of each other.
+  auto pace = [&](int i) {
+    const int other = __hip_atomic_load(&prog[w ^ 4], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_store(&prog[w], i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (i > other) __builtin_amdgcn_s_setprio(0);
+    else __builtin_amdgcn_s_setprio(1);
+  };
   auto run = [&](auto hz) {
     int64_t prev_t0 = -1;
     int i = 0;
@@ -1264,6 +1292,7 @@ __global__ __launch_bounds__(kWave) void lane_kernel(KernelParams p) {
         inflight = nload;
       }
       wait_vmcnt(inflight);
+      if constexpr (WPB > 1) pace(i);
       if (prev_t0 >= 0) store_tile(prev_t0);
       const int64_t ns = (t_end - t0) < TT ? (t_end - t0) : TT;
       if (ns == TT) {
@@ -1287,6 +1316,10 @@ __global__ __launch_bounds__(kWave) void lane_kernel(KernelParams p) {
     }
     if (prev_t0 >= 0) store_tile(prev_t0);
     wait_vmcnt(0);   // a fix-up wave can leave with the next tile's loads in flight
+    if constexpr (WPB > 1) {
+      __hip_atomic_store(&prog[w], INT_MAX, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);   // never hold the partner back
+      __builtin_amdgcn_s_setprio(0);
+    }
   };
   if (has_z) run(std::true_type{});
   else run(std::false_type{});
@@ -1426,15 +1459,15 @@ template <int IO>
 hipError_t launch_lane(const KernelParams& kp0, int64_t batch, hipStream_t stream) {
   KernelParams kp = kp0;
   kp.ngroups = static_cast<int>((kp.dim + kWave - 1) / kWave);
-  const dim3 block(kWave);
+  constexpr int WPB = lanek::wpb(IO);
+  const dim3 block(kWave * WPB);
+  auto blocks = [](int64_t units) { return dim3(static_cast<unsigned>((units + WPB - 1) / WPB)); };
   if (kp.K == 1) {
-    const dim3 grid(static_cast<unsigned>(batch * kp.ngroups));
-    hipLaunchKernelGGL((lane_kernel<IO, kSingle>), grid, block, 0, stream, kp);
+    hipLaunchKernelGGL((lane_kernel<IO, kSingle>), blocks(batch * kp.ngroups), block, 0, stream, kp);
     return hipGetLastError();
   }
   {
-    const dim3 grid(static_cast<unsigned>(batch * kp.K * kp.ngroups));
-    hipLaunchKernelGGL((lane_kernel<IO, kChunk>), grid, block, 0, stream, kp);
+    hipLaunchKernelGGL((lane_kernel<IO, kChunk>), blocks(batch * kp.K * kp.ngroups), block, 0, stream, kp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1447,8 +1480,7 @@ hipError_t launch_lane(const KernelParams& kp0, int64_t batch, hipStream_t strea
   {
     KernelParams kf = kp;
     kf.chunk_offset = 1;
-    const dim3 grid(static_cast<unsigned>(batch * (kp.K - 1) * kp.ngroups));
-    hipLaunchKernelGGL((lane_kernel<IO, kFixup>), grid, block, 0, stream, kf);
+    hipLaunchKernelGGL((lane_kernel<IO, kFixup>), blocks(batch * (kp.K - 1) * kp.ngroups), block, 0, stream, kf);
     return hipGetLastError();
   }
 }

@@ -1270,12 +1270,15 @@ __global__ __launch_bounds__(kWave * lanek::wpb(IO)) void lane_kernel(KernelPara
     }
   };
 
-  // Two waves of a workgroup share each SIMD (w and w ^ 4).  The SIMD issues from the older of two ready
+  // The waves of a workgroup with the same w % 4 share a SIMD.  The SIMD issues from the older of two ready
   // waves, so left alone one wave of a pair runs ahead and the other finishes its chunk alone, at the
   // lower issue rate of a single wave.  At each tile a wave that has finished more tiles than its partner
   // drops its priority, which keeps the pair within about a tile of each other.
   auto pace = [&](int i) {
-    const int other = __hip_atomic_load(&prog[w ^ 4], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    int other = INT_MAX;
+#pragma unroll
+    for (int m = 1; m < WPB / 4; ++m)
+      other = min(other, __hip_atomic_load(&prog[(w + 4 * m) % WPB], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
     __hip_atomic_store(&prog[w], i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     if (i > other) __builtin_amdgcn_s_setprio(0);
     else __builtin_amdgcn_s_setprio(1);

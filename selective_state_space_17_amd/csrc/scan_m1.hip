@@ -1272,8 +1272,8 @@ __global__ __launch_bounds__(kWave * lanek::wpb(IO)) void lane_kernel(KernelPara
 
   // The waves of a workgroup with the same w % 4 share a SIMD.  The SIMD issues from the older of two ready
   // waves, so left alone one wave of a pair runs ahead and the other finishes its chunk alone, at the
-  // lower issue rate of a single wave.  At each tile a wave that has finished more tiles than its partner
-  // drops its priority, which keeps the pair within about a tile of each other.
+  // lower issue rate of a single wave.  At each tile a wave takes priority 0 when it has finished more
+  // tiles than its partner, 2 when fewer and 1 when as many, which keeps the pair within about a tile.
   auto pace = [&](int i) {
     int other = INT_MAX;
 #pragma unroll
@@ -1281,7 +1281,8 @@ __global__ __launch_bounds__(kWave * lanek::wpb(IO)) void lane_kernel(KernelPara
       other = min(other, __hip_atomic_load(&prog[(w + 4 * m) % WPB], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
     __hip_atomic_store(&prog[w], i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     if (i > other) __builtin_amdgcn_s_setprio(0);
-    else __builtin_amdgcn_s_setprio(1);
+    else if (i == other) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(2);
   };
   auto run = [&](auto hz) {
     int64_t prev_t0 = -1;

@@ -1022,9 +1022,10 @@ __global__ __launch_bounds__(kThreads) void wide_kernel(KernelParams p) {
 // ---------------------------------------------------------------------------
 // One channel per lane, every wave on its own ("lane" layout), dstate == 16.
 //
-// A workgroup is one wave.  It owns 64 consecutive channels of one batch row
-// and one sequence chunk, and lane c holds the 16 states of channel c in
-// VGPRs.  Waves share nothing, so there is no barrier: each wave copies its own
+// A wave owns 64 consecutive channels of one batch row and one sequence chunk,
+// and lane c holds the 16 states of channel c in VGPRs; with bf16 I/O a
+// workgroup is eight such waves (two on every SIMD), with fp32 one.  Waves
+// share no data, so there is no barrier: each wave copies its own
 // time tiles of x, delta, z and of B, C from HBM into its LDS with direct
 // global->LDS loads (one tile ahead, double-buffered) and lane c reads the
 // values of its channel at step s from there.  B_n and C_n reach the lanes as
@@ -1212,8 +1213,7 @@ __global__ __launch_bounds__(kWave * lanek::wpb(IO)) void lane_kernel(KernelPara
     FastReadout<1>::run(a0, a1, cv, h);
     float y = a0 + a1;
     if constexpr (HZ) {
-      const float gz = silu_gate(zv);
-      y = __builtin_fmaf(y, gz, gz * (Dv * u));
+      y = __builtin_fmaf(Dv, u, y) * silu_gate(zv);
     } else {
       y = __builtin_fmaf(Dv, u, y);
     }
@@ -1458,7 +1458,7 @@ hipError_t launch_wide(const KernelParams& kp, int64_t batch, hipStream_t stream
   }
 }
 
-// the same three launches for the one-channel-per-lane kernel: one wave per workgroup, 64 channels each
+// the same three launches for the one-channel-per-lane kernel: a wave per 64 channels, wpb(IO) waves a workgroup
 template <int IO>
 hipError_t launch_lane(const KernelParams& kp0, int64_t batch, hipStream_t stream) {
   KernelParams kp = kp0;

@@ -1312,9 +1312,14 @@ __global__ __launch_bounds__(kWave * lanek::wpb(IO)) void lane_kernel(KernelPara
       }
       prev_t0 = t0;
       if constexpr (MODE == kFixup) {
-        // carried-in part bounded by exp2(amax * S) * hmax; done once it would be 0 in fp32
+        // The carried-in part of state j is bounded by exp2(A2[j] S) hmax.  Done once it would be 0 in
+        // fp32, or once it is below 2^-26 of every state it is part of: from there on the zero-start
+        // values the chunk pass stored differ from the rescanned ones only by fp32 rounding of the states.
+        bool below = true;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) below = below && exp2_hw(A2[j] * S) * hmax < 0x1p-26f * fabsf(h[j]);
         const bool lane_done = !cvalid || hmax == 0.f ||
-                               (!never_exit && amax < 0.f && amax * S + __log2f(hmax) < -150.f);
+                               (!never_exit && amax < 0.f && (amax * S + __log2f(hmax) < -150.f || below));
         if (__builtin_amdgcn_ballot_w64(!lane_done) == 0) break;
       }
     }

@@ -68,7 +68,8 @@ def kernel_tags(is_ssd: bool, decode: bool = False, backward: bool = False, trai
         return ("scan_bwd_kernel", "bwd_reduce", "bwd_finish") + (("wide_kernel",) if train else ())
     if decode:
         return ("ssd_update_kernel", "ssdm_update_kernel") if is_ssd else ("scan_update_kernel",)
-    return ("ssd_kernel", "ssd_add_shares") if is_ssd else ("wide_kernel", "lane_kernel", "scan_kernel", "carry_kernel")
+    return ("ssd_kernel", "ssd_add_shares") if is_ssd else ("wide_kernel", "lane_kernel", "scan_kernel", "carry_kernel",
+                                                             "carry_serial_kernel")
 
 
 def load_traffic(workload: str, is_ssd: bool, decode: bool = False, backward: bool = False, train: bool = False):

@@ -70,6 +70,14 @@ double scan_cost(const mssm_scan_desc& d, int G, int K) {
   // softplus-distributed deltas and |A| >= 1); bounded by the chunk length
   const double steps = static_cast<double>(chunk) + (K > 1 ? std::min<double>(chunk, 800.0) : 0.0);
   const int64_t waves = groups * K;
+  if (G == 1 && d.dstate == 16 && d.io_dtype == MSSM_BF16) {
+    // the one-channel-per-lane kernel: workgroups of eight waves, one per CU, two waves on every SIMD of
+    // it (2048 resident over the chip), and its rescan stops once the carried-in part is below the
+    // states' rounding (about 250 steps for those deltas)
+    const double lane_steps = static_cast<double>(chunk) + (K > 1 ? std::min<double>(chunk, 250.0) : 0.0);
+    const int64_t rounds = (waves + 2 * kSimds - 1) / (2 * kSimds);
+    return static_cast<double>(rounds) * lane_steps * slots_step * 2.0 / 0.93 + (K > 1 ? 2e4 : 0.0);
+  }
   const int64_t per_simd = (waves + kSimds - 1) / kSimds;
   const double eff = per_simd <= 1 ? 0.85 : (per_simd == 2 ? 0.93 : 0.97);
   return steps * slots_step * static_cast<double>(per_simd) / eff + (K > 1 ? 2e4 : 0.0);
@@ -117,10 +125,17 @@ int plan_scan(const mssm_scan_desc& d, int* K_out, int* G_out) {
       if (c < best && plan_fits(d, G, K)) { best = c; bestK = K; bestG = G; }
       continue;
     }
+    // powers of two, and the chunk count that fills the chip's resident waves exactly
+    const int64_t cpb = 256 / G;
+    const int64_t per_chunk = std::max<int64_t>(1, d.batch * ((d.dim + cpb - 1) / cpb) * 4);
+    const int fill = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(4096, 2 * kSimds / per_chunk)));
     for (int K = 1; K <= 4096; K *= 2) {
+      for (int Kc : {K, K == 1 ? fill : 0}) {
+        if (Kc == 0 || (Kc > 1 && d.seqlen / Kc < 256)) continue;
+        const double c = scan_cost(d, G, Kc);
+        if (c < best && plan_fits(d, G, Kc)) { best = c; bestK = Kc; bestG = G; }
+      }
       if (K > 1 && d.seqlen / K < 256) break;
-      const double c = scan_cost(d, G, K);
-      if (c < best && plan_fits(d, G, K)) { best = c; bestK = K; bestG = G; }
     }
   }
   if (bestG == 0) return MSSM_ERR_UNSUPPORTED;

@@ -1399,8 +1399,42 @@ __global__ __launch_bounds__(256) void carry_kernel(KernelParams p) {
   if (p.final_state != nullptr && k_lo < K && k_hi == K) p.final_state[(b * p.dim + c) * p.N + n] = h;
 }
 
+// The same carry for few chunks, one lane per (b, c, n) walking the chunks in order: with K - 1 <= 16 the
+// wave-level scan would leave most lanes of its waves idle.
+__global__ __launch_bounds__(256) void carry_serial_kernel(KernelParams p) {
+  const int64_t col = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (col >= p.batch * p.dim * p.N) return;
+  const int64_t n = col % p.N;
+  const int64_t c = (col / p.N) % p.dim;
+  const int64_t b = col / (p.N * p.dim);
+  const float a2 = p.A[c * p.N + n] * kLog2e;
+  const int K = p.K;
+  const float* __restrict__ S = p.S + b * K * p.dim + c;
+  const float* __restrict__ he = p.hend + (b * K * p.dim + c) * p.N + n;
+  float* __restrict__ hi = p.hin + (b * K * p.dim + c) * p.N + n;
+  const int64_t ss = p.dim, hs = p.dim * p.N;
+  float h = he[0];   // chunk 0 starts from the true state: its end state enters chunk 1
+  for (int k = 1; k < K; ++k) {
+    hi[k * hs] = h;
+    h = __builtin_fmaf(exp2_hw(a2 * S[k * ss]), h, he[k * hs]);
+  }
+  if (p.final_state != nullptr) p.final_state[(b * p.dim + c) * p.N + n] = h;
+}
+
 // blocks of the carry kernel: one wave per (b, c, n), 4 waves per block
 int64_t carry_blocks(int64_t batch, int64_t dim, int64_t N) { return (batch * dim * N + 3) / 4; }
+
+// the carry of a split: few chunks one lane per (b, c, n), else one wave per (b, c, n)
+hipError_t launch_carry(const KernelParams& kp, int64_t batch, hipStream_t stream) {
+  if (kp.K - 1 <= 16) {
+    const int64_t cols = batch * kp.dim * kp.N;
+    hipLaunchKernelGGL(carry_serial_kernel, dim3(static_cast<unsigned>((cols + 255) / 256)), dim3(256), 0, stream, kp);
+  } else {
+    hipLaunchKernelGGL(carry_kernel, dim3(static_cast<unsigned>(carry_blocks(batch, kp.dim, kp.N))), dim3(256), 0,
+                       stream, kp);
+  }
+  return hipGetLastError();
+}
 
 size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
@@ -1419,9 +1453,7 @@ hipError_t launch_cfg(const KernelParams& kp, int64_t batch, hipStream_t stream)
     if (e != hipSuccess) return e;
   }
   {
-    const dim3 grid(static_cast<unsigned>(carry_blocks(batch, kp.dim, kp.N)));
-    hipLaunchKernelGGL(carry_kernel, grid, dim3(256), 0, stream, kp);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_carry(kp, batch, stream);
     if (e != hipSuccess) return e;
   }
   {
@@ -1449,9 +1481,7 @@ hipError_t launch_wide(const KernelParams& kp, int64_t batch, hipStream_t stream
     if (e != hipSuccess) return e;
   }
   {
-    const dim3 grid(static_cast<unsigned>(carry_blocks(batch, kp.dim, kp.N)));
-    hipLaunchKernelGGL(carry_kernel, grid, dim3(256), 0, stream, kp);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_carry(kp, batch, stream);
     if (e != hipSuccess) return e;
   }
   {
@@ -1481,9 +1511,7 @@ hipError_t launch_lane(const KernelParams& kp0, int64_t batch, hipStream_t strea
     if (e != hipSuccess) return e;
   }
   {
-    const dim3 grid(static_cast<unsigned>(carry_blocks(batch, kp.dim, kp.N)));
-    hipLaunchKernelGGL(carry_kernel, grid, dim3(256), 0, stream, kp);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_carry(kp, batch, stream);
     if (e != hipSuccess) return e;
   }
   {

@@ -140,6 +140,11 @@ def test_plan_and_workspace():
         assert (ws == 0) == (k == 1)
     # the long sequence must be split to fill the chip
     assert M.selective_scan_plan(1, 1 << 20, 2048, 16)[0] > 1
+    # bf16 at dstate 16: one lane per channel, the chunk count that fills the resident waves (2048 / 32 and
+    # 2048 / 320 chunks of 64 channels), and the 130M layer unsplit on one state per lane
+    assert M.selective_scan_plan(1, 1 << 20, 2048, 16, M.MSSM_BF16) == (64, 1)
+    assert M.selective_scan_plan(4, 8192, 5120, 16, M.MSSM_BF16) == (6, 1)
+    assert M.selective_scan_plan(8, 2048, 1536, 16, M.MSSM_BF16) == (1, 16)
     # forced plans are honoured
     assert M.selective_scan_plan(2, 1000, 64, 16, split_seq=3, split_state=4) == (3, 4)
     assert M.selective_scan_plan(1, 10, 64, 16, split_seq=64)[0] == 10   # never more chunks than steps
